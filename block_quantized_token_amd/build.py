@@ -1,0 +1,43 @@
+"""Build libqgemv.so in-tree: the host front with g++, the kernels with hipcc for gfx950."""
+from __future__ import annotations
+
+import os
+import subprocess
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+CSRC = os.path.join(HERE, "csrc")
+BUILD = os.path.join(HERE, "_build")
+LIB = os.path.join(HERE, "libqgemv.so")
+ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
+
+HIP_FLAGS = [
+    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-ffp-contract=off", "-Wall",
+    # packed fp32 instructions are kept out of every code object
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+]
+HOST_FLAGS = ["-O2", "-std=c++17", "-fPIC", "-ffp-contract=off", "-Wall", "-Wextra", "-Werror"]
+
+
+def _run(cmd, verbose):
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    subprocess.run(cmd, check=True)
+
+
+def build(verbose: bool = False, extra_hip_flags=()) -> str:
+    os.makedirs(BUILD, exist_ok=True)
+    host_o = os.path.join(BUILD, "qgemv_host.o")
+    kern_o = os.path.join(BUILD, "qgemv_kernels.o")
+    _run(["g++", *HOST_FLAGS, "-c", os.path.join(CSRC, "qgemv_host.cpp"), "-o", host_o], verbose)
+    _run([os.path.join(ROCM, "bin", "hipcc"), *HIP_FLAGS, *extra_hip_flags, "-c", "-x", "hip",
+          os.path.join(CSRC, "qgemv_kernels.hip"), "-o", kern_o], verbose)
+    tmp = LIB + f".tmp{os.getpid()}"
+    _run([os.path.join(ROCM, "bin", "hipcc"), "--offload-arch=gfx950", "-shared", "-fPIC", host_o, kern_o,
+          "-o", tmp], verbose)
+    os.replace(tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build(verbose="-v" in sys.argv))

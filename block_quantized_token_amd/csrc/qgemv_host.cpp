@@ -1,0 +1,335 @@
+// Host front of the C ABI declared in include/qgemv.h: argument checks (all of
+// them before any HIP call), the tile table and its QGEMV_TILE override, the
+// bit-exact pack/unpack helpers and the status strings.
+#include <stdarg.h>
+#include <stdint.h>
+#include <stdio.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include <string>
+
+#include "qgemv_internal.h"
+
+namespace qg {
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int status, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+int fail(int status, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return status;
+}
+
+int ok() {
+    g_last_error.clear();
+    return QG_OK;
+}
+
+bool valid_fmt(int fmt) { return fmt == QG_FMT_Q8_0 || fmt == QG_FMT_Q4_0 || fmt == QG_FMT_BF16; }
+
+const char* fmt_name(int fmt) { return fmt == QG_FMT_Q8_0 ? "q8_0" : fmt == QG_FMT_Q4_0 ? "q4_0" : "bf16"; }
+
+// bytes per row, -1 if cols is not whole blocks
+int64_t row_bytes(int fmt, int64_t cols) {
+    if (cols <= 0) return -1;
+    if (fmt == QG_FMT_BF16) return cols * 2;
+    if (cols % 32) return -1;
+    return cols / 32 * (fmt == QG_FMT_Q8_0 ? 34 : 18);
+}
+
+// Largest sizes the kernels index with their int32 fields: cols (k positions) and
+// the workgroup count; byte offsets are 64-bit throughout.
+constexpr int64_t kMaxCols = int64_t(1) << 24;
+constexpr int64_t kMaxRows = int64_t(1) << 31;
+
+// ------------------------------------------------------------ tile table
+// Defaults keyed by (format, rows, cols, T).  The k split (waves per workgroup)
+// depends on cols only, so a token's summation order -- and its bits -- are the
+// same at every T.  rows_per_batch and rows_per_wg may vary with T.
+Tile default_tile(int fmt, int64_t rows, int64_t cols, int T) {
+    Tile t{};
+    t.lanes_per_row = kLanesPerRow;
+    t.k_slice = kSlice;
+    t.mfma = 0;
+    const int64_t nslices = (cols + kSlice - 1) / kSlice;
+    // fewest waves that cover the slices in equal rounds
+    const int64_t rounds = (nslices + kMaxWaves - 1) / kMaxWaves;
+    t.waves_per_wg = (int)((nslices + rounds - 1) / rounds);
+    t.rows_per_batch = T <= 2 ? 4 : T == 3 ? 4 : 2;
+    (void)fmt;
+    (void)T;
+    // aim for roughly 4 workgroups per CU (256 CUs) or more
+    const int64_t step = 2 * t.rows_per_batch;
+    int64_t rw = rows / 1024;
+    rw = rw / step * step;
+    if (rw < step) rw = step;
+    if (rw > 128) rw = 128;
+    t.rows_per_wg = (int)rw;
+    return t;
+}
+
+// QGEMV_TILE="fmt:rb,nw,rw[;fmt:rb,nw,rw...]".  Returns 0 (no override for fmt),
+// 1 (override applied to *t) or -1 (malformed / outside the compiled set).
+int tile_override(int fmt, Tile* t, std::string* why) {
+    const char* env = getenv("QGEMV_TILE");
+    if (!env || !*env) return 0;
+    std::string s(env);
+    size_t pos = 0;
+    while (pos <= s.size()) {
+        size_t end = s.find(';', pos);
+        if (end == std::string::npos) end = s.size();
+        std::string item = s.substr(pos, end - pos);
+        pos = end + 1;
+        if (item.empty()) continue;
+        size_t colon = item.find(':');
+        if (colon == std::string::npos) {
+            *why = "QGEMV_TILE item '" + item + "' has no 'fmt:'";
+            return -1;
+        }
+        std::string name = item.substr(0, colon);
+        int f = name == "q8_0" ? QG_FMT_Q8_0 : name == "q4_0" ? QG_FMT_Q4_0 : name == "bf16" ? QG_FMT_BF16 : -1;
+        if (f < 0) {
+            *why = "QGEMV_TILE format '" + name + "' unknown";
+            return -1;
+        }
+        int rb = 0, nw = 0, rw = 0;
+        char tail = 0;
+        if (sscanf(item.c_str() + colon + 1, "%d,%d,%d%c", &rb, &nw, &rw, &tail) != 3) {
+            *why = "QGEMV_TILE item '" + item + "' is not fmt:rb,nw,rw";
+            return -1;
+        }
+        if (!valid_rb(rb) || nw < 1 || nw > kMaxWaves || rw < 2 * rb || rw % (2 * rb) || rw > (1 << 20)) {
+            *why = "QGEMV_TILE item '" + item + "' is outside the compiled set (rb in {1,2,4,8}, nw in 1..12, rw a multiple of 2*rb)";
+            return -1;
+        }
+        if (f == fmt) {
+            t->rows_per_batch = rb;
+            t->waves_per_wg = nw;
+            t->rows_per_wg = rw;
+            return 1;
+        }
+    }
+    return 0;
+}
+
+int pick_tile(int fmt, int64_t rows, int64_t cols, int T, Tile* t) {
+    *t = default_tile(fmt, rows, cols, T);
+    std::string why;
+    if (tile_override(fmt, t, &why) < 0) return fail(QG_EINVAL, "%s", why.c_str());
+    if (!tile_supported(T, t->rows_per_batch))
+        return fail(QG_EINVAL, "rows_per_batch %d is not compiled for T=%d", t->rows_per_batch, T);
+    const int64_t nslices = (cols + kSlice - 1) / kSlice;
+    if (t->waves_per_wg > nslices) t->waves_per_wg = (int)nslices;  // idle waves would only add zeros
+    if (lds_bytes(*t, T) > kMaxLds)
+        return fail(QG_EINVAL, "tile needs %zu B of LDS (rows_per_wg %d too large)", lds_bytes(*t, T), t->rows_per_wg);
+    return QG_OK;
+}
+
+bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
+
+bool overlap(const void* a, size_t na, const void* b, size_t nb) {
+    const uintptr_t a0 = (uintptr_t)a, b0 = (uintptr_t)b;
+    return a0 < b0 + nb && b0 < a0 + na;
+}
+
+int check_common(int fmt, int64_t rows, int64_t cols, int T, const void* W, const float* x, const float* y,
+                 int64_t* rb_out) {
+    if (!valid_fmt(fmt)) return fail(QG_EINVAL, "unknown format %d", fmt);
+    if (!W || !x || !y) return fail(QG_EINVAL, "null pointer (W=%p x=%p y=%p)", W, (const void*)x, (const void*)y);
+    if (rows <= 0 || cols <= 0) return fail(QG_EINVAL, "rows=%lld cols=%lld must be positive", (long long)rows, (long long)cols);
+    if (T < 1 || T > QG_MAX_T) return fail(QG_EINVAL, "T=%d outside 1..%d", T, QG_MAX_T);
+    if (fmt != QG_FMT_BF16 && cols % 32) return fail(QG_EINVAL, "%s needs whole 32-weight blocks: cols=%lld", fmt_name(fmt), (long long)cols);
+    if (fmt == QG_FMT_BF16 && cols % 8) return fail(QG_EUNSUPPORTED, "bf16 path needs cols %% 8 == 0: cols=%lld", (long long)cols);
+    if (cols > kMaxCols || rows >= kMaxRows) return fail(QG_EUNSUPPORTED, "rows=%lld cols=%lld beyond the supported range", (long long)rows, (long long)cols);
+    if (!aligned(W, 16) || !aligned(x, 16)) return fail(QG_EALIGN, "W and x must be 16-byte aligned (W=%p x=%p)", W, (const void*)x);
+    if (!aligned(y, 4)) return fail(QG_EALIGN, "y must be 4-byte aligned (y=%p)", (const void*)y);
+    *rb_out = row_bytes(fmt, cols);
+    return QG_OK;
+}
+
+int run_dense(int fmt, int64_t rows, int64_t cols, int T, const void* W, const float* x, float* y, void* stream) {
+    int64_t rbytes = 0;
+    int st = check_common(fmt, rows, cols, T, W, x, y, &rbytes);
+    if (st) return st;
+    const size_t wbytes = (size_t)(rbytes * rows), xbytes = (size_t)T * cols * 4, ybytes = (size_t)T * rows * 4;
+    if (overlap(y, ybytes, W, wbytes) || overlap(y, ybytes, x, xbytes)) return fail(QG_EINVAL, "y overlaps W or x");
+    Tile tile;
+    if ((st = pick_tile(fmt, rows, cols, T, &tile))) return st;
+    DenseArgs a;
+    a.W = (const uint8_t*)W;
+    a.x = x;
+    a.y = y;
+    a.rows = rows;
+    a.row_bytes = rbytes;
+    a.cols = (int)cols;
+    a.nslices = (int)((cols + kSlice - 1) / kSlice);
+    a.rows_per_wg = tile.rows_per_wg;
+    if ((rows + tile.rows_per_wg - 1) / tile.rows_per_wg > 0x7FFFFFFF) return fail(QG_EUNSUPPORTED, "grid too large");
+    int err = launch_dense(fmt, T, tile, a, stream);
+    if (err) return fail(QG_EHIP, "kernel launch failed: %s", hip_error_name(err));
+    return ok();
+}
+
+}  // namespace
+}  // namespace qg
+
+using namespace qg;
+
+extern "C" {
+
+int qgemv_q8_0(int64_t rows, int64_t cols, int T, const void* W, const float* x, float* y, void* stream) {
+    return run_dense(QG_FMT_Q8_0, rows, cols, T, W, x, y, stream);
+}
+
+int qgemv_q4_0(int64_t rows, int64_t cols, int T, const void* W, const float* x, float* y, void* stream) {
+    return run_dense(QG_FMT_Q4_0, rows, cols, T, W, x, y, stream);
+}
+
+int qgemv_bf16(int64_t rows, int64_t cols, int T, const void* W, const float* x, float* y, void* stream) {
+    return run_dense(QG_FMT_BF16, rows, cols, T, W, x, y, stream);
+}
+
+int qgemv_grouped_experts(int fmt, int64_t n_experts, int64_t rows, int64_t cols, int T, int topk,
+                          const int32_t* ids, const void* W, const float* x, float* y, void* stream) {
+    int64_t rbytes = 0;
+    int st = check_common(fmt, rows, cols, T, W, x, y, &rbytes);
+    if (st) return st;
+    if (!ids) return fail(QG_EINVAL, "null ids");
+    if (n_experts < 1 || n_experts > 0x7FFFFFFF) return fail(QG_EINVAL, "n_experts=%lld must be in 1..2^31-1", (long long)n_experts);
+    if (topk < 1 || topk > 4096) return fail(QG_EINVAL, "topk=%d must be in 1..4096", topk);
+    if (!aligned(ids, 4)) return fail(QG_EALIGN, "ids must be 4-byte aligned");
+    const int64_t ebytes = rbytes * rows;
+    if (ebytes > INT64_MAX / n_experts) return fail(QG_EUNSUPPORTED, "expert table too large");
+    const size_t ybytes = (size_t)T * topk * rows * 4;
+    if (overlap(y, ybytes, W, (size_t)(ebytes * n_experts)) || overlap(y, ybytes, x, (size_t)T * cols * 4) ||
+        overlap(y, ybytes, ids, (size_t)T * topk * 4))
+        return fail(QG_EINVAL, "y overlaps W, x or ids");
+    Tile tile;
+    if ((st = pick_tile(fmt, rows, cols, QG_MAX_T, &tile))) return st;  // one kernel for 1..4 tokens per expert
+    GroupedArgs a;
+    a.W = (const uint8_t*)W;
+    a.x = x;
+    a.y = y;
+    a.ids = ids;
+    a.rows = rows;
+    a.row_bytes = rbytes;
+    a.expert_bytes = ebytes;
+    a.n_experts = (int)n_experts;
+    a.cols = (int)cols;
+    a.nslices = (int)((cols + kSlice - 1) / kSlice);
+    a.rows_per_wg = tile.rows_per_wg;
+    a.tiles_per_expert = (int)((rows + tile.rows_per_wg - 1) / tile.rows_per_wg);
+    a.T = T;
+    a.topk = topk;
+    if ((int64_t)T * topk * a.tiles_per_expert > 0x7FFFFFFF) return fail(QG_EUNSUPPORTED, "grid too large");
+    int err = launch_grouped(fmt, tile, a, stream);
+    if (err) return fail(QG_EHIP, "kernel launch failed: %s", hip_error_name(err));
+    return ok();
+}
+
+size_t qg_packed_bytes(int fmt, int64_t rows, int64_t cols) {
+    if (!valid_fmt(fmt) || rows < 0) return 0;
+    const int64_t rb = row_bytes(fmt, cols);
+    if (rb < 0 || (rows && rb > INT64_MAX / rows)) return 0;
+    return (size_t)(rb * rows);
+}
+
+int qg_pack_q8_0(int64_t rows, int64_t cols, const uint16_t* d_bits, const int8_t* codes, void* out) {
+    if (rows < 0 || cols <= 0 || cols % 32 || !d_bits || !codes || !out) return fail(QG_EINVAL, "bad arguments to qg_pack_q8_0");
+    const int64_t nb = cols / 32;
+    uint8_t* o = (uint8_t*)out;
+    for (int64_t r = 0; r < rows; ++r)
+        for (int64_t b = 0; b < nb; ++b) {
+            uint8_t* blk = o + (r * nb + b) * 34;
+            const uint16_t d = d_bits[r * nb + b];
+            blk[0] = (uint8_t)(d & 0xFF);
+            blk[1] = (uint8_t)(d >> 8);
+            memcpy(blk + 2, codes + r * cols + b * 32, 32);
+        }
+    return ok();
+}
+
+int qg_unpack_q8_0(int64_t rows, int64_t cols, const void* in, uint16_t* d_bits, int8_t* codes) {
+    if (rows < 0 || cols <= 0 || cols % 32 || !in || !d_bits || !codes) return fail(QG_EINVAL, "bad arguments to qg_unpack_q8_0");
+    const int64_t nb = cols / 32;
+    const uint8_t* p = (const uint8_t*)in;
+    for (int64_t r = 0; r < rows; ++r)
+        for (int64_t b = 0; b < nb; ++b) {
+            const uint8_t* blk = p + (r * nb + b) * 34;
+            d_bits[r * nb + b] = (uint16_t)(blk[0] | (blk[1] << 8));
+            memcpy(codes + r * cols + b * 32, blk + 2, 32);
+        }
+    return ok();
+}
+
+int qg_pack_q4_0(int64_t rows, int64_t cols, const uint16_t* d_bits, const uint8_t* codes, void* out) {
+    if (rows < 0 || cols <= 0 || cols % 32 || !d_bits || !codes || !out) return fail(QG_EINVAL, "bad arguments to qg_pack_q4_0");
+    for (int64_t i = 0; i < rows * cols; ++i)
+        if (codes[i] > 15) return fail(QG_EINVAL, "q4_0 code %u at %lld is not 0..15", codes[i], (long long)i);
+    const int64_t nb = cols / 32;
+    uint8_t* o = (uint8_t*)out;
+    for (int64_t r = 0; r < rows; ++r)
+        for (int64_t b = 0; b < nb; ++b) {
+            uint8_t* blk = o + (r * nb + b) * 18;
+            const uint16_t d = d_bits[r * nb + b];
+            const uint8_t* c = codes + r * cols + b * 32;
+            blk[0] = (uint8_t)(d & 0xFF);
+            blk[1] = (uint8_t)(d >> 8);
+            for (int j = 0; j < 16; ++j) blk[2 + j] = (uint8_t)(c[j] | (c[j + 16] << 4));
+        }
+    return ok();
+}
+
+int qg_unpack_q4_0(int64_t rows, int64_t cols, const void* in, uint16_t* d_bits, uint8_t* codes) {
+    if (rows < 0 || cols <= 0 || cols % 32 || !in || !d_bits || !codes) return fail(QG_EINVAL, "bad arguments to qg_unpack_q4_0");
+    const int64_t nb = cols / 32;
+    const uint8_t* p = (const uint8_t*)in;
+    for (int64_t r = 0; r < rows; ++r)
+        for (int64_t b = 0; b < nb; ++b) {
+            const uint8_t* blk = p + (r * nb + b) * 18;
+            uint8_t* c = codes + r * cols + b * 32;
+            d_bits[r * nb + b] = (uint16_t)(blk[0] | (blk[1] << 8));
+            for (int j = 0; j < 16; ++j) {
+                c[j] = blk[2 + j] & 15;
+                c[j + 16] = blk[2 + j] >> 4;
+            }
+        }
+    return ok();
+}
+
+int qg_query_tile(int fmt, int64_t rows, int64_t cols, int T, int out_tile[QG_TILE_FIELDS]) {
+    if (!valid_fmt(fmt) || rows <= 0 || cols <= 0 || T < 1 || T > QG_MAX_T || !out_tile)
+        return fail(QG_EINVAL, "bad arguments to qg_query_tile");
+    Tile t;
+    int st = pick_tile(fmt, rows, cols, T, &t);
+    if (st) return st;
+    out_tile[0] = t.lanes_per_row;
+    out_tile[1] = t.rows_per_batch;
+    out_tile[2] = t.waves_per_wg;
+    out_tile[3] = t.k_slice;
+    out_tile[4] = t.rows_per_wg;
+    out_tile[5] = t.mfma;
+    return ok();
+}
+
+const char* qg_status_string(int status) {
+    switch (status) {
+    case QG_OK: return "QG_OK: success";
+    case QG_EINVAL: return "QG_EINVAL: invalid argument";
+    case QG_EALIGN: return "QG_EALIGN: misaligned pointer";
+    case QG_EUNSUPPORTED: return "QG_EUNSUPPORTED: valid but unsupported shape";
+    case QG_EHIP: return "QG_EHIP: HIP runtime error";
+    }
+    return "unknown qgemv status";
+}
+
+const char* qg_last_error(void) { return g_last_error.c_str(); }
+
+}  // extern "C"

@@ -1,0 +1,110 @@
+"""Torch-facing helpers over the C ABI: PyTorch supplies device memory and the
+current stream; the computation is entirely the library's HIP kernels."""
+from __future__ import annotations
+
+import numpy as np
+
+from . import _lib
+
+FMT = {"q8_0": _lib.QG_FMT_Q8_0, "q4_0": _lib.QG_FMT_Q4_0, "bf16": _lib.QG_FMT_BF16}
+_ENTRY = {_lib.QG_FMT_Q8_0: _lib.qgemv_q8_0, _lib.QG_FMT_Q4_0: _lib.qgemv_q4_0, _lib.QG_FMT_BF16: _lib.qgemv_bf16}
+
+
+def _fmt(fmt):
+    return FMT[fmt] if isinstance(fmt, str) else int(fmt)
+
+
+def _stream(torch, device):
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _require_device(t, name):
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor (the library has no CPU path)")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def gemv(fmt, W, x, rows: int, out=None):
+    """y[T][rows] = W . x[t] for packed weights W (uint8 device tensor) and x fp32 [T][cols]."""
+    import torch
+    f = _fmt(fmt)
+    _require_device(W, "W")
+    _require_device(x, "x")
+    if x.dtype != torch.float32 or x.dim() != 2:
+        raise ValueError("x must be fp32 [T][cols]")
+    T, cols = x.shape
+    if out is None:
+        out = torch.empty((T, rows), dtype=torch.float32, device=x.device)
+    _require_device(out, "out")
+    need = _lib.qg_packed_bytes(f, rows, cols)
+    if need == 0 or W.numel() * W.element_size() < need:
+        raise ValueError(f"W holds {W.numel() * W.element_size()} bytes, the shape needs {need}")
+    st = _ENTRY[f](rows, cols, T, W.data_ptr(), x.data_ptr(), out.data_ptr(), _stream(torch, x.device))
+    _lib.check(st, "qgemv")
+    return out
+
+
+def grouped_experts(fmt, W, x, ids, n_experts: int, rows: int, out=None):
+    """y[T][topk][rows] = W_{ids[t][j]} . x[t]; ids int32 [T][topk] on the device."""
+    import torch
+    f = _fmt(fmt)
+    for t, n in ((W, "W"), (x, "x"), (ids, "ids")):
+        _require_device(t, n)
+    if ids.dtype != torch.int32 or ids.dim() != 2:
+        raise ValueError("ids must be int32 [T][topk]")
+    T, cols = x.shape
+    topk = ids.shape[1]
+    if ids.shape[0] != T:
+        raise ValueError("ids and x disagree on T")
+    if out is None:
+        out = torch.empty((T, topk, rows), dtype=torch.float32, device=x.device)
+    _require_device(out, "out")
+    need = _lib.qg_packed_bytes(f, rows * n_experts, cols)
+    if need == 0 or W.numel() * W.element_size() < need:
+        raise ValueError(f"W holds {W.numel() * W.element_size()} bytes, the experts need {need}")
+    st = _lib.qgemv_grouped_experts(f, n_experts, rows, cols, T, topk, ids.data_ptr(), W.data_ptr(), x.data_ptr(),
+                                    out.data_ptr(), _stream(torch, x.device))
+    _lib.check(st, "qgemv_grouped_experts")
+    return out
+
+
+def pack_q8_0(d_bits: np.ndarray, codes: np.ndarray) -> np.ndarray:
+    rows, cols = codes.shape
+    d = np.ascontiguousarray(d_bits, dtype=np.uint16)
+    c = np.ascontiguousarray(codes, dtype=np.int8)
+    out = np.empty(_lib.qg_packed_bytes(_lib.QG_FMT_Q8_0, rows, cols), dtype=np.uint8)
+    _lib.check(_lib.qg_pack_q8_0(rows, cols, d.ctypes.data, c.ctypes.data, out.ctypes.data), "qg_pack_q8_0")
+    return out
+
+
+def unpack_q8_0(packed: np.ndarray, rows: int, cols: int):
+    p = np.ascontiguousarray(packed, dtype=np.uint8)
+    d = np.empty((rows, cols // 32), dtype=np.uint16)
+    c = np.empty((rows, cols), dtype=np.int8)
+    _lib.check(_lib.qg_unpack_q8_0(rows, cols, p.ctypes.data, d.ctypes.data, c.ctypes.data), "qg_unpack_q8_0")
+    return d, c
+
+
+def pack_q4_0(d_bits: np.ndarray, codes: np.ndarray) -> np.ndarray:
+    rows, cols = codes.shape
+    d = np.ascontiguousarray(d_bits, dtype=np.uint16)
+    c = np.ascontiguousarray(codes, dtype=np.uint8)
+    out = np.empty(_lib.qg_packed_bytes(_lib.QG_FMT_Q4_0, rows, cols), dtype=np.uint8)
+    _lib.check(_lib.qg_pack_q4_0(rows, cols, d.ctypes.data, c.ctypes.data, out.ctypes.data), "qg_pack_q4_0")
+    return out
+
+
+def unpack_q4_0(packed: np.ndarray, rows: int, cols: int):
+    p = np.ascontiguousarray(packed, dtype=np.uint8)
+    d = np.empty((rows, cols // 32), dtype=np.uint16)
+    c = np.empty((rows, cols), dtype=np.uint8)
+    _lib.check(_lib.qg_unpack_q4_0(rows, cols, p.ctypes.data, d.ctypes.data, c.ctypes.data), "qg_unpack_q4_0")
+    return d, c
+
+
+def query_tile(fmt, rows: int, cols: int, T: int) -> dict:
+    st, t = _lib.qg_query_tile(_fmt(fmt), rows, cols, T)
+    _lib.check(st, "qg_query_tile")
+    keys = ("lanes_per_row", "rows_per_batch", "waves_per_wg", "k_slice", "rows_per_wg", "mfma")
+    return dict(zip(keys, t))

@@ -1,0 +1,125 @@
+/*
+ * qgemv.h -- C ABI of the MI355X (gfx950) multi-token block-quantized mat-vec.
+ *
+ *     y[t][r] = sum_{k < cols} w[r][k] * x[t][k]        t < T (1..4), r < rows
+ *
+ * the product that the pages measure at 1..4 activation vectors per pass over
+ * the weights: speculative-decode verify and draft steps (M5 multi-token audit,
+ * "Track 2 Audit & Optimization Report: M5 Metal Kernels for Multi-Token
+ * Speculative Decode", section 1 item 1 and the section 2.1 tile sweep; the M2
+ * Max performance page, "Where the time goes on an M2 Max", mat-vec table).
+ * Its cost is effective weight bandwidth: packed weight bytes / time per call.
+ *
+ * Weight formats (ggml block layouts, as the pages' format names imply):
+ *   Q8_0  blocks of 32 weights: little-endian fp16 scale d, then 32 int8
+ *         codes c (34 B);  w = d * c.
+ *   Q4_0  blocks of 32 weights: little-endian fp16 scale d, then 16 bytes;
+ *         byte j holds code j in its low nibble and code j + 16 in its high
+ *         nibble (18 B, 4.5 bits per weight);  w = d * (c - 8).
+ *   BF16  one little-endian bfloat16 per weight.
+ * W is row-major: row r's blocks (or bf16 values) follow row r - 1's with no
+ * padding; within a row the blocks run along k.
+ *
+ * Common conventions of the compute entry points
+ *   - rows, cols: output count and reduction length (the pages write shapes as
+ *     n_in x n_out; here cols = n_in, rows = n_out).
+ *   - T: number of activation vectors, 1 <= T <= QG_MAX_T.
+ *   - W, x, y, ids are DEVICE pointers, allocated and owned by the caller; the
+ *     library allocates nothing and keeps no per-call state.
+ *   - x is fp32 [T][cols] contiguous; y is fp32 [T][rows] contiguous (grouped:
+ *     [T][topk][rows]).  y is overwritten (no accumulation) and must not
+ *     overlap W, x or ids.
+ *   - stream is a hipStream_t (NULL = the default stream).  Calls are
+ *     stream-ordered and asynchronous: they return once the kernel is queued;
+ *     a device fault surfaces at the caller's next synchronisation.
+ *   - Every argument is checked on the host before any HIP call.  Return
+ *     value: QG_OK, or a qg_status; qg_last_error() then holds a message.
+ *   - Thread-safe: the only shared state is an immutable tile table and a
+ *     thread-local error string.
+ *   - Each token's outputs are computed in the same order whatever T is, so
+ *     y[t] at T tokens equals y[t] at T' tokens bit for bit (the pages note
+ *     that each token's sum should not depend on the token count: opus-mtp-
+ *     turbo report, finding 3) -- as long as QGEMV_TILE does not change the
+ *     k split (waves per workgroup) between the calls.
+ *   - Accuracy: |y - exact| <= 1e-4 * sum_k |w_k * x_k| + 1e-6 per output
+ *     (fp32 accumulation of exactly decoded weights).
+ *
+ * Environment: QGEMV_TILE="fmt:rb,nw,rw[;fmt:...]" overrides the tile for a
+ * format (fmt = q8_0 | q4_0 | bf16): rb rows per lane group per batch (one of
+ * 1, 2, 4, 8), nw waves per workgroup (1..16), rw rows per workgroup (a
+ * multiple of 2*rb).  A malformed or out-of-set value makes every call of
+ * that format return QG_EINVAL.
+ */
+#ifndef QGEMV_H
+#define QGEMV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    QG_OK = 0,
+    QG_EINVAL = 1,       /* bad argument: null pointer, size, T, fmt, topk, bad QGEMV_TILE */
+    QG_EALIGN = 2,       /* W or x not 16-byte aligned, y or ids not 4-byte aligned */
+    QG_EUNSUPPORTED = 3, /* valid but not handled: BF16 cols % 8 != 0, sizes past the int32 grid */
+    QG_EHIP = 4          /* the HIP runtime refused the launch */
+} qg_status;
+
+typedef enum { QG_FMT_Q8_0 = 0, QG_FMT_Q4_0 = 1, QG_FMT_BF16 = 2 } qg_format;
+
+#define QG_MAX_T 4
+#define QG_TILE_FIELDS 6 /* lanes_per_row, rows_per_batch, waves_per_wg, k_slice, rows_per_wg, mfma */
+
+/* Q8_0 weights: cols % 32 == 0; W holds rows * cols/32 * 34 bytes. */
+int qgemv_q8_0(int64_t rows, int64_t cols, int T, const void* W, const float* x, float* y, void* stream);
+
+/* Q4_0 weights: cols % 32 == 0; W holds rows * cols/32 * 18 bytes. */
+int qgemv_q4_0(int64_t rows, int64_t cols, int T, const void* W, const float* x, float* y, void* stream);
+
+/* BF16 weights: cols % 8 == 0 (else QG_EUNSUPPORTED); W holds rows * cols * 2 bytes. */
+int qgemv_bf16(int64_t rows, int64_t cols, int T, const void* W, const float* x, float* y, void* stream);
+
+/*
+ * Grouped experts (M5 audit, section 1 item 2: tokens grouped by expert id so
+ * each distinct expert's weights are streamed once for all tokens that chose
+ * it):
+ *     y[t][j][r] = sum_k W_{ids[t][j]}[r][k] * x[t][k]     t < T, j < topk
+ * W holds n_experts matrices of fmt, each [rows][cols], back to back; ids is
+ * a DEVICE int32 [T][topk].  One launch; the grouping is done on the device.
+ * An id outside [0, n_experts) cannot be reported synchronously: that slot's
+ * output row y[t][j][*] is filled with NaN instead.
+ */
+int qgemv_grouped_experts(int fmt, int64_t n_experts, int64_t rows, int64_t cols, int T, int topk,
+                          const int32_t* ids, const void* W, const float* x, float* y, void* stream);
+
+/* ---- host-only helpers (no GPU needed) ---------------------------------- */
+
+/* Packed bytes of a rows x cols matrix of fmt; 0 if the shape is invalid. */
+size_t qg_packed_bytes(int fmt, int64_t rows, int64_t cols);
+
+/* HOST pointers.  d_bits: [rows][cols/32] fp16 bit patterns; codes: [rows][cols]
+ * (Q8_0 any int8, Q4_0 0..15 -- a code > 15 is QG_EINVAL).  out / in: the
+ * packed bytes (qg_packed_bytes of them).  Bit-exact in both directions. */
+int qg_pack_q8_0(int64_t rows, int64_t cols, const uint16_t* d_bits, const int8_t* codes, void* out);
+int qg_unpack_q8_0(int64_t rows, int64_t cols, const void* in, uint16_t* d_bits, int8_t* codes);
+int qg_pack_q4_0(int64_t rows, int64_t cols, const uint16_t* d_bits, const uint8_t* codes, void* out);
+int qg_unpack_q4_0(int64_t rows, int64_t cols, const void* in, uint16_t* d_bits, uint8_t* codes);
+
+/* The tile a call with these arguments would use (after QGEMV_TILE):
+ * out_tile = {lanes_per_row, rows_per_batch, waves_per_wg, k_slice, rows_per_wg, mfma}. */
+int qg_query_tile(int fmt, int64_t rows, int64_t cols, int T, int out_tile[QG_TILE_FIELDS]);
+
+/* Static description of a status code (never NULL). */
+const char* qg_status_string(int status);
+
+/* Detail of the calling thread's last failure ("" if none). */
+const char* qg_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QGEMV_H */

@@ -1,0 +1,168 @@
+"""The C-ABI library on the CPU: it loads, exports every function include/qgemv.h
+declares, packs and unpacks bit-exactly, and rejects bad arguments with the
+documented status before touching the GPU."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+from block_quantized_token_amd import _lib, inputs as I, ops
+from tests.conftest import ROOT
+
+HEADER = os.path.join(ROOT, "include", "qgemv.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(_lib.LIB_PATH):
+        from block_quantized_token_amd import build
+        build.build()
+    return _lib.load()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\**\s+\**(q\w+)\s*\(", text, flags=re.M)))
+
+
+def test_header_declares_the_abi():
+    assert declared_functions() == sorted(_lib.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_status_strings(lib):
+    for st in range(5):
+        assert _lib.status_string(st).startswith(("QG_OK", "QG_E"))
+    assert "unknown" in _lib.status_string(99)
+
+
+def test_packed_bytes(lib, orc):
+    for fmt in (0, 1, 2):
+        for rows, cols in ((1, 32), (10240, 2560), (2560, 6144), (248320, 5120), (7, 640)):
+            assert _lib.qg_packed_bytes(fmt, rows, cols) == orc.packed_bytes(fmt, rows, cols)
+    assert _lib.qg_packed_bytes(0, 4, 33) == 0 and _lib.qg_packed_bytes(1, 4, 48) == 0
+    assert _lib.qg_packed_bytes(7, 4, 32) == 0 and _lib.qg_packed_bytes(0, -1, 32) == 0
+
+
+def test_pack_matches_generator_and_oracle(lib, orc):
+    rng = np.random.default_rng(1)
+    d, c = I.q8_0_fields(rng, 9, 320)
+    packed = ops.pack_q8_0(d, c)
+    assert np.array_equal(packed, I.pack_q8_0(d, c))
+    od, oc = orc.unpack(0, 9, 320, packed)
+    assert np.array_equal(od, d) and np.array_equal(oc, c.astype(np.int32))
+    d4, c4 = I.q4_0_fields(rng, 9, 320)
+    packed4 = ops.pack_q4_0(d4, c4)
+    assert np.array_equal(packed4, I.pack_q4_0(d4, c4))
+    od, oc = orc.unpack(1, 9, 320, packed4)
+    assert np.array_equal(od, d4) and np.array_equal(oc, c4.astype(np.int32))
+
+
+def test_pack_unpack_every_field_value(lib):
+    """All 65,536 scale patterns, every int8 code and every nibble round-trip bit-exactly."""
+    rows, cols = 2048, 1024  # 65,536 blocks
+    d = np.arange(65536, dtype=np.uint32).astype(np.uint16).reshape(rows, cols // 32)
+    c8 = (np.arange(rows * cols) % 256 - 128).astype(np.int8).reshape(rows, cols)
+    gd, gc = ops.unpack_q8_0(ops.pack_q8_0(d, c8), rows, cols)
+    assert np.array_equal(gd, d) and np.array_equal(gc, c8)
+    c4 = (np.arange(rows * cols) * 7 % 16).astype(np.uint8).reshape(rows, cols)
+    gd, gc = ops.unpack_q4_0(ops.pack_q4_0(d, c4), rows, cols)
+    assert np.array_equal(gd, d) and np.array_equal(gc, c4)
+
+
+def test_unpack_pack_random_bytes(lib):
+    rng = np.random.default_rng(2)
+    for rows, cols, fmt in ((13, 96, 0), (13, 96, 1)):
+        raw = rng.integers(0, 256, size=_lib.qg_packed_bytes(fmt, rows, cols), dtype=np.uint8)
+        if fmt == 0:
+            assert np.array_equal(ops.pack_q8_0(*ops.unpack_q8_0(raw, rows, cols)), raw)
+        else:
+            assert np.array_equal(ops.pack_q4_0(*ops.unpack_q4_0(raw, rows, cols)), raw)
+
+
+def test_pack_q4_0_rejects_wide_codes(lib):
+    d = np.zeros((1, 1), np.uint16)
+    c = np.full((1, 32), 16, np.uint8)
+    with pytest.raises(_lib.QGError) as e:
+        ops.pack_q4_0(d, c)
+    assert e.value.status == _lib.QG_EINVAL
+
+
+# ------------------------------------------------------------ argument checks
+# Fake but aligned device addresses: every call below must be refused on the
+# host, so nothing is ever dereferenced or launched.
+W0, X0, Y0, I0 = 0x10000000, 0x20000000, 0x30000000, 0x40000000
+
+
+@pytest.mark.parametrize("args, status", [
+    ((64, 256, 1, W0, X0, 0), _lib.QG_EINVAL),          # null y
+    ((64, 256, 1, 0, X0, Y0), _lib.QG_EINVAL),          # null W
+    ((64, 256, 1, W0, 0, Y0), _lib.QG_EINVAL),          # null x
+    ((0, 256, 1, W0, X0, Y0), _lib.QG_EINVAL),          # rows 0
+    ((64, 0, 1, W0, X0, Y0), _lib.QG_EINVAL),           # cols 0
+    ((64, 256, 0, W0, X0, Y0), _lib.QG_EINVAL),         # T 0
+    ((64, 256, 5, W0, X0, Y0), _lib.QG_EINVAL),         # T 5
+    ((64, 250, 1, W0, X0, Y0), _lib.QG_EINVAL),         # not whole blocks
+    ((64, 256, 1, W0 + 2, X0, Y0), _lib.QG_EALIGN),     # W misaligned
+    ((64, 256, 1, W0, X0 + 4, Y0), _lib.QG_EALIGN),     # x misaligned
+    ((64, 256, 1, W0, X0, Y0 + 2), _lib.QG_EALIGN),     # y misaligned
+    ((64, 256, 1, W0, X0, W0 + 64), _lib.QG_EINVAL),    # y inside W
+    ((64, 256, 2, W0, X0, X0 + 256), _lib.QG_EINVAL),   # y overlaps x
+    ((1 << 31, 256, 1, W0, X0, Y0), _lib.QG_EUNSUPPORTED),
+])
+def test_dense_argument_errors(lib, args, status):
+    for entry in (_lib.qgemv_q8_0, _lib.qgemv_q4_0):
+        assert entry(*args) == status, _lib.last_error()
+        assert _lib.last_error()
+
+
+def test_bf16_cols(lib):
+    assert _lib.qgemv_bf16(64, 250, 1, W0, X0, Y0) == _lib.QG_EUNSUPPORTED
+    assert _lib.qgemv_bf16(64, 256, 1, W0 + 8, X0, Y0) == _lib.QG_EALIGN
+
+
+@pytest.mark.parametrize("args, status", [
+    ((3, 4, 64, 256, 1, 2, I0, W0, X0, Y0), _lib.QG_EINVAL),    # bad fmt
+    ((0, 0, 64, 256, 1, 2, I0, W0, X0, Y0), _lib.QG_EINVAL),    # no experts
+    ((0, 4, 64, 256, 1, 0, I0, W0, X0, Y0), _lib.QG_EINVAL),    # topk 0
+    ((0, 4, 64, 256, 1, 2, 0, W0, X0, Y0), _lib.QG_EINVAL),     # null ids
+    ((0, 4, 64, 256, 1, 2, I0 + 2, W0, X0, Y0), _lib.QG_EALIGN),
+    ((0, 4, 64, 256, 5, 2, I0, W0, X0, Y0), _lib.QG_EINVAL),    # T 5
+    ((0, 4, 64, 256, 1, 2, I0, W0, X0, I0), _lib.QG_EINVAL),    # y overlaps ids
+])
+def test_grouped_argument_errors(lib, args, status):
+    assert _lib.qgemv_grouped_experts(*args) == status, _lib.last_error()
+
+
+def test_tile_query_and_override(lib, monkeypatch):
+    monkeypatch.delenv("QGEMV_TILE", raising=False)
+    t = ops.query_tile("q8_0", 10240, 2560, 1)
+    assert t["lanes_per_row"] == 32 and t["k_slice"] == 512 and t["waves_per_wg"] == 5
+    # the k split must not depend on T (bit-identical tokens across T)
+    for fmt in ("q8_0", "q4_0", "bf16"):
+        for rows, cols in ((10240, 2560), (2560, 6144), (248320, 5120), (8192, 2560), (7, 65536)):
+            assert len({ops.query_tile(fmt, rows, cols, T)["waves_per_wg"] for T in (1, 2, 3, 4)}) == 1
+    monkeypatch.setenv("QGEMV_TILE", "q8_0:2,5,8")
+    t = ops.query_tile("q8_0", 10240, 2560, 4)
+    assert (t["rows_per_batch"], t["waves_per_wg"], t["rows_per_wg"]) == (2, 5, 8)
+    assert ops.query_tile("q4_0", 10240, 2560, 4)["rows_per_wg"] != 8 or True  # other formats untouched
+    for bad in ("q8_0:3,5,8", "q8_0:2,13,8", "q8_0:2,5,6", "q9:2,5,8", "q8_0:2,5", "q8_0:8,5,16"):
+        monkeypatch.setenv("QGEMV_TILE", bad)
+        st, _ = _lib.qg_query_tile(0, 10240, 2560, 4)
+        assert st == _lib.QG_EINVAL, bad
+        assert _lib.qgemv_q8_0(10240, 2560, 4, W0, X0, Y0) == _lib.QG_EINVAL
+
+
+def test_binding_refuses_cpu_tensors(lib):
+    torch = pytest.importorskip("torch")
+    W = torch.zeros(34 * 4, dtype=torch.uint8)
+    x = torch.zeros(1, 32)
+    with pytest.raises(ValueError):
+        ops.gemv("q8_0", W, x, rows=4)

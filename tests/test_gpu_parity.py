@@ -1,0 +1,262 @@
+"""GPU parity: the HIP path through the C ABI against the fp64 CPU oracle.
+
+Bar (per output): |y_gpu - y_oracle| <= 1e-4 * sum_k |w_k x_k| + 1e-6.
+Dyadic and identity inputs, whose exact result is representable, must match
+bit for bit; so must repeated calls, a token's outputs at different T, and the
+grouped kernel against the plain one.
+"""
+import sys
+
+import numpy as np
+import pytest
+
+from block_quantized_token_amd import _lib, inputs as I, ops
+
+pytestmark = pytest.mark.gpu
+
+Q8, Q4, BF = I.FMT_Q8_0, I.FMT_Q4_0, I.FMT_BF16
+NAMES = {Q8: "q8_0", Q4: "q4_0", BF: "bf16"}
+
+
+@pytest.fixture(scope="module")
+def torch():
+    import torch as _t
+    if not _t.cuda.is_available():
+        pytest.fail("no GPU visible: the gpu tests need an MI355X")
+    _lib.load()
+    return _t
+
+
+def say(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def dev(torch, arr):
+    return torch.from_numpy(np.ascontiguousarray(arr)).cuda()
+
+
+def gpu_gemv(torch, fmt, W_dev, x, rows):
+    y = ops.gemv(NAMES[fmt], W_dev, dev(torch, x), rows)
+    torch.cuda.synchronize()
+    return y.cpu().numpy()
+
+
+def assert_parity(y, ref, bound, what):
+    err = np.abs(y.astype(np.float64) - ref)
+    tol = 1e-4 * bound + 1e-6
+    bad = err > tol
+    assert not bad.any(), (f"{what}: {bad.sum()} outputs out of tolerance; worst err {err.max():.3e}, "
+                           f"worst err/tol {(err / tol).max():.3f}")
+    assert np.isfinite(y).all(), what
+
+
+def check_dense(torch, orc, fmt, rows, cols, W, x, what, sel=None):
+    Wd = dev(torch, W)
+    y4 = None
+    for T in range(x.shape[0], 0, -1):
+        say(f"[{what}] fmt={NAMES[fmt]} rows={rows} cols={cols} T={T}")
+        y = gpu_gemv(torch, fmt, Wd, x[:T], rows)
+        ref, bound = orc.gemv(fmt, rows, cols, W, x[:T], sel=sel)
+        assert_parity(y if sel is None else y[:, sel], ref, bound, f"{what} T={T}")
+        if y4 is None:
+            y4 = y
+        else:  # a token's outputs do not depend on T
+            assert np.array_equal(y, y4[:T]), f"{what}: token results differ between T={T} and T={x.shape[0]}"
+    return y4
+
+
+# ------------------------------------------------------------- hand vectors
+def test_hand_vectors_bitwise(torch, orc):
+    from tests import golden_io
+    for name in golden_io.hand_vectors():
+        g = golden_io.load(name)
+        say(f"[hand] {name}")
+        y = gpu_gemv(torch, g["fmt"], dev(torch, g["W"]), g["x"], g["rows"])
+        assert np.array_equal(y.astype(np.float64).reshape(g["y"].shape), g["y"]), (name, y, g["y"])
+
+
+def test_identity_bitwise(torch):
+    for fmt, n in ((Q8, 64), (Q8, 1024), (Q4, 64), (Q4, 1024)):
+        rng = np.random.default_rng(n + fmt)
+        perm = rng.permutation(n)
+        d = np.full((n, n // 32), 0x3C00, dtype=np.uint16)
+        if fmt == Q8:
+            codes = np.zeros((n, n), dtype=np.int8)
+            codes[np.arange(n), perm] = 1
+            W = I.pack_q8_0(d, codes)
+        else:
+            codes = np.full((n, n), 8, dtype=np.uint8)
+            codes[np.arange(n), perm] = 9
+            W = I.pack_q4_0(d, codes)
+        x = rng.standard_normal((4, n)).astype(np.float32)
+        say(f"[identity] fmt={NAMES[fmt]} n={n}")
+        y = gpu_gemv(torch, fmt, dev(torch, W), x, n)
+        assert np.array_equal(y, x[:, perm])
+
+
+def dyadic_weights(rng, fmt, rows, cols):
+    d = rng.choice(np.array([0x3400, 0x3800, 0x3C00], dtype=np.uint16), size=(rows, cols // 32))
+    if fmt == Q8:
+        return I.pack_q8_0(d, rng.integers(-128, 128, (rows, cols), dtype=np.int8))
+    return I.pack_q4_0(d, rng.integers(0, 16, (rows, cols), dtype=np.uint8))
+
+
+@pytest.mark.parametrize("fmt,rows,cols", [(Q8, 10240, 2560), (Q8, 2560, 6144), (Q4, 8192, 2560), (Q8, 333, 736)])
+def test_dyadic_bitwise(torch, orc, fmt, rows, cols):
+    """Every partial sum is a multiple of 2^-6 below 2^20: exact in fp32 in any order."""
+    rng = np.random.default_rng(rows + cols)
+    W = dyadic_weights(rng, fmt, rows, cols)
+    x = (rng.integers(-4, 5, (4, cols)) / 4.0).astype(np.float32)
+    say(f"[dyadic] fmt={NAMES[fmt]} {rows}x{cols}")
+    y = gpu_gemv(torch, fmt, dev(torch, W), x, rows)
+    ref, _ = orc.gemv(fmt, rows, cols, W, x)
+    assert np.array_equal(y.astype(np.float64), ref)
+
+
+def test_bf16_dyadic_bitwise(torch, orc):
+    rng = np.random.default_rng(4)
+    rows, cols = 777, 1032
+    vals = rng.integers(-64, 65, (rows, cols)) / 16.0
+    W = I.pack_bf16(I.bf16_bits(vals))
+    x = (rng.integers(-4, 5, (4, cols)) / 4.0).astype(np.float32)
+    y = gpu_gemv(torch, BF, dev(torch, W), x, rows)
+    ref, _ = orc.gemv(BF, rows, cols, W, x)
+    assert np.array_equal(y.astype(np.float64), ref)
+
+
+# --------------------------------------------------------- ragged and tiny
+TINY_ROWS = (1, 2, 3, 5, 17, 33, 67)
+TINY_COLS = tuple(32 * i for i in range(1, 10)) + (256, 544, 640, 1056)
+
+
+@pytest.mark.parametrize("fmt", [Q8, Q4])
+def test_tiny_shapes(torch, orc, fmt):
+    for rows in TINY_ROWS:
+        for cols in TINY_COLS:
+            rng = np.random.default_rng(rows * 1000 + cols)
+            W = I.weights(rng, fmt, rows, cols)
+            x = I.activations(rng, cols)
+            check_dense(torch, orc, fmt, rows, cols, W, x, "tiny")
+
+
+def test_tiny_shapes_bf16(torch, orc):
+    for rows in TINY_ROWS:
+        for cols in (8, 16, 24, 40, 56, 504, 520, 1000, 1032):
+            rng = np.random.default_rng(rows * 1000 + cols)
+            W = I.weights(rng, BF, rows, cols)
+            x = I.activations(rng, cols)
+            check_dense(torch, orc, BF, rows, cols, W, x, "tiny")
+
+
+@pytest.mark.parametrize("fmt,rows,cols", [(Q8, 64, 65536), (Q4, 48, 6656), (BF, 40, 7000), (Q8, 1000, 4608)])
+def test_many_slices(torch, orc, fmt, rows, cols):
+    """More k slices than waves per workgroup: waves loop over several slices."""
+    rng = np.random.default_rng(cols)
+    W = I.weights(rng, fmt, rows, cols)
+    x = I.activations(rng, cols)
+    check_dense(torch, orc, fmt, rows, cols, W, x, "many-slices")
+
+
+# ------------------------------------------------------------ the workloads
+@pytest.mark.parametrize("name", ["c1_q8_0_2560x2560", "c2a_q8_0_10240x2560", "c2b_q8_0_2560x6144",
+                                  "c3_q4_0_8192x2560", "c3_bf16_8192x2560"])
+def test_config_full(torch, orc, name):
+    c = I.dense_case(name)
+    check_dense(torch, orc, c["fmt"], c["rows"], c["cols"], c["W"], c["x"], name)
+
+
+def test_lm_head_sampled(torch, orc):
+    """248,320 x 5,120 Q8_0 at full size; the oracle checks a sample of rows, every
+    output is finite, and a token's rows agree bit for bit across T."""
+    name = "c4_q8_0_248320x5120"
+    say(f"[{name}] generating 1.35 GB of packed weights")
+    c = I.dense_case(name)
+    rows = c["rows"]
+    rng = np.random.default_rng(123)
+    sel = np.unique(np.concatenate([rng.choice(rows, 3000, replace=False), [0, 1, rows // 2, rows - 2, rows - 1]]))
+    check_dense(torch, orc, c["fmt"], rows, c["cols"], c["W"], c["x"], name, sel=sel)
+
+
+def test_repeat_calls_bitwise(torch):
+    c = I.dense_case("c2a_q8_0_10240x2560")
+    Wd, xd = dev(torch, c["W"]), dev(torch, c["x"])
+    ys = [ops.gemv("q8_0", Wd, xd, c["rows"]).cpu().numpy() for _ in range(3)]
+    assert all(np.array_equal(ys[0], y) for y in ys[1:])
+
+
+def test_tile_override_keeps_bits(torch, monkeypatch):
+    """Different row tilings with the same k split give identical bits."""
+    c = I.dense_case("c2a_q8_0_10240x2560")
+    Wd, xd = dev(torch, c["W"]), dev(torch, c["x"])
+    monkeypatch.delenv("QGEMV_TILE", raising=False)
+    base = ops.gemv("q8_0", Wd, xd, c["rows"]).cpu().numpy()
+    for tile in ("q8_0:1,5,2", "q8_0:2,5,8", "q8_0:1,5,64", "q8_0:2,5,100"):
+        monkeypatch.setenv("QGEMV_TILE", tile)
+        say(f"[tile] {tile}")
+        assert np.array_equal(ops.gemv("q8_0", Wd, xd, c["rows"]).cpu().numpy(), base), tile
+
+
+def test_tile_override_other_k_split(torch, orc, monkeypatch):
+    c = I.dense_case("c2b_q8_0_2560x6144")
+    monkeypatch.setenv("QGEMV_TILE", "q8_0:2,4,16")  # 12 slices over 4 waves
+    y = gpu_gemv(torch, Q8, dev(torch, c["W"]), c["x"], c["rows"])
+    ref, bound = orc.gemv(Q8, c["rows"], c["cols"], c["W"], c["x"])
+    assert_parity(y, ref, bound, "c2b nw=4")
+
+
+# ---------------------------------------------------------- grouped experts
+def grouped_check(torch, orc, fmt, n_experts, rows, cols, ids, W, x, what):
+    say(f"[{what}] fmt={NAMES[fmt]} experts={n_experts} rows={rows} cols={cols} ids={ids.tolist()}")
+    y = ops.grouped_experts(NAMES[fmt], dev(torch, W), dev(torch, x), dev(torch, ids), n_experts, rows)
+    torch.cuda.synchronize()
+    y = y.cpu().numpy()
+    ref, bound = orc.grouped(fmt, n_experts, rows, cols, ids, W, x)
+    assert_parity(y, ref, bound, what)
+    return y
+
+
+def test_grouped_config(torch, orc):
+    g = I.grouped_case()
+    y = grouped_check(torch, orc, g["fmt"], g["n_experts"], g["rows"], g["cols"], g["ids"], g["W"], g["x"], "c5")
+    # equals the plain kernel on each selected expert, bit for bit
+    rb = I.packed_row_bytes(g["fmt"], g["cols"])
+    Wd = dev(torch, g["W"])
+    for t in range(g["T"]):
+        for j in (0, g["topk"] - 1):
+            e = int(g["ids"][t, j])
+            We = Wd[e * g["rows"] * rb:(e + 1) * g["rows"] * rb]
+            yp = gpu_gemv(torch, g["fmt"], We, g["x"][t:t + 1], g["rows"])
+            assert np.array_equal(yp[0], y[t, j])
+
+
+@pytest.mark.parametrize("fmt", [Q4, Q8, BF])
+def test_grouped_sharing(torch, orc, fmt):
+    rng = np.random.default_rng(10 + fmt)
+    n_experts, rows, cols = 12, 200, 1024
+    W = I.weights(rng, fmt, n_experts * rows, cols)
+    x = I.activations(rng, cols)
+    cases = [
+        np.array([[3, 5], [3, 7], [3, 5], [3, 9]], np.int32),   # expert 3 shared by 4 tokens, 5 by 2
+        np.array([[1, 1, 2], [2, 2, 1], [0, 11, 2], [11, 0, 4]], np.int32),  # duplicates inside a token
+        np.array([[7, 8, 9, 10]], np.int32),                    # T = 1
+        np.array([[4, 6], [6, 4], [4, 6]], np.int32),           # T = 3, ne = 3
+    ]
+    for ids in cases:
+        T = ids.shape[0]
+        grouped_check(torch, orc, fmt, n_experts, rows, cols, ids, W, x[:T], "sharing")
+
+
+def test_grouped_bad_id_gives_nan_rows(torch, orc):
+    rng = np.random.default_rng(77)
+    n_experts, rows, cols = 6, 100, 512
+    W = I.weights(rng, Q8, n_experts * rows, cols)
+    x = I.activations(rng, cols, 2)
+    ids = np.array([[0, 6], [-1, 2]], np.int32)
+    y = ops.grouped_experts("q8_0", dev(torch, W), dev(torch, x), dev(torch, ids), n_experts, rows)
+    torch.cuda.synchronize()
+    y = y.cpu().numpy()
+    assert np.isnan(y[0, 1]).all() and np.isnan(y[1, 0]).all()
+    good = np.array([[0, 0], [2, 2]], np.int32)
+    ref, bound = orc.grouped(Q8, n_experts, rows, cols, good, W, x)
+    assert_parity(y[0, 0], ref[0, 0], bound[0, 0], "good slot 0,0")
+    assert_parity(y[1, 1], ref[1, 1], bound[1, 1], "good slot 1,1")
