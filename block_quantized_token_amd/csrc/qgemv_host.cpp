@@ -54,6 +54,7 @@ constexpr int64_t kMaxRows = int64_t(1) << 31;
 // depends on cols only, so a token's summation order -- and its bits -- are the
 // same at every T.  rows_per_batch and rows_per_wg may vary with T.
 Tile default_tile(int fmt, int64_t rows, int64_t cols, int T) {
+    (void)rows;
     Tile t{};
     t.lanes_per_row = kLanesPerRow;
     t.k_slice = kSlice;
@@ -62,20 +63,38 @@ Tile default_tile(int fmt, int64_t rows, int64_t cols, int T) {
     // fewest waves that cover the slices in equal rounds
     const int64_t rounds = (nslices + kMaxWaves - 1) / kMaxWaves;
     t.waves_per_wg = (int)((nslices + rounds - 1) / rounds);
-    t.rows_per_batch = T <= 2 ? 4 : T == 3 ? 4 : 2;
-    (void)fmt;
-    (void)T;
-    // aim for roughly 4 workgroups per CU (256 CUs) or more
-    const int64_t step = 2 * t.rows_per_batch;
-    int64_t rw = rows / 1024;
-    rw = rw / step * step;
-    if (rw < step) rw = step;
-    if (rw > 128) rw = 128;
-    t.rows_per_wg = (int)rw;
+    // one batch per workgroup (every load of a wave in flight at once) when each
+    // wave has one slice; otherwise the pipelined kernel with its largest batch
+    const bool os = nslices <= t.waves_per_wg;
+    t.kind = 0;
+    if (os && row_bytes(fmt, cols) % 16 == 0 && stream_supported(fmt, T, 4)) {
+        // streamed through LDS in 8-row tiles.  Large matrices: long workgroups
+        // (rows per workgroup grows with the matrix, shrinks with T); small
+        // ones: enough workgroups to give every CU work.
+        t.kind = 1;
+        t.rows_per_batch = 4;
+        const int64_t per_cu = rows / 256;  // rows each CU gets with one workgroup per CU
+        int64_t rw = T == 1 ? 256 : T == 2 ? 128 : 80;
+        if (per_cu < rw) rw = per_cu < 8 ? 8 : per_cu / 8 * 8;
+        // two row groups per slice when a workgroup would otherwise hold few waves
+        if (2 * nslices <= kMaxWaves && rows <= 65536) t.waves_per_wg = (int)(2 * nslices);
+        t.rows_per_wg = (int)rw;
+        if (stream_lds_bytes(fmt, t, T, (int)nslices) <= kMaxLds) return t;
+        t.waves_per_wg = (int)nslices;
+        t.rows_per_wg = 16;
+        if (stream_lds_bytes(fmt, t, T, (int)nslices) <= kMaxLds) return t;
+        t.kind = 0;
+        t.waves_per_wg = (int)nslices;
+    }
+    t.rows_per_batch = 1;
+    for (int rb : {2, 4, 8, os ? (T <= 2 ? 8 : 4) : 8})
+        if (rb <= (os ? (T <= 2 ? 8 : 4) : 8) && tile_supported(fmt, T, rb, os)) t.rows_per_batch = rb;
+    t.rows_per_wg = os ? 2 * t.rows_per_batch : 8 * t.rows_per_batch;
     return t;
 }
 
-// QGEMV_TILE="fmt:rb,nw,rw[;fmt:rb,nw,rw...]".  Returns 0 (no override for fmt),
+// QGEMV_TILE="fmt:rb,nw,rw[,k][;...]" with k = d (direct) or s (streamed through
+// LDS; the default when the shape allows it).  Returns 0 (no override for fmt),
 // 1 (override applied to *t) or -1 (malformed / outside the compiled set).
 int tile_override(int fmt, Tile* t, std::string* why) {
     const char* env = getenv("QGEMV_TILE");
@@ -100,19 +119,21 @@ int tile_override(int fmt, Tile* t, std::string* why) {
             return -1;
         }
         int rb = 0, nw = 0, rw = 0;
-        char tail = 0;
-        if (sscanf(item.c_str() + colon + 1, "%d,%d,%d%c", &rb, &nw, &rw, &tail) != 3) {
-            *why = "QGEMV_TILE item '" + item + "' is not fmt:rb,nw,rw";
+        char kind = 0, tail = 0;
+        const int got = sscanf(item.c_str() + colon + 1, "%d,%d,%d,%c%c", &rb, &nw, &rw, &kind, &tail);
+        if (!(got == 3 || (got == 4 && (kind == 'd' || kind == 's')))) {
+            *why = "QGEMV_TILE item '" + item + "' is not fmt:rb,nw,rw[,d|s]";
             return -1;
         }
         if (!valid_rb(rb) || nw < 1 || nw > kMaxWaves || rw < 2 * rb || rw % (2 * rb) || rw > (1 << 20)) {
-            *why = "QGEMV_TILE item '" + item + "' is outside the compiled set (rb in {1,2,4,8}, nw in 1..12, rw a multiple of 2*rb)";
+            *why = "QGEMV_TILE item '" + item + "' is outside the compiled set (rb in {1,2,4,8,16}, nw in 1..12, rw a multiple of 2*rb)";
             return -1;
         }
         if (f == fmt) {
             t->rows_per_batch = rb;
             t->waves_per_wg = nw;
             t->rows_per_wg = rw;
+            t->kind = got == 4 ? (kind == 's') : -1;  // -1: choose below
             return 1;
         }
     }
@@ -123,10 +144,27 @@ int pick_tile(int fmt, int64_t rows, int64_t cols, int T, Tile* t) {
     *t = default_tile(fmt, rows, cols, T);
     std::string why;
     if (tile_override(fmt, t, &why) < 0) return fail(QG_EINVAL, "%s", why.c_str());
-    if (!tile_supported(T, t->rows_per_batch))
-        return fail(QG_EINVAL, "rows_per_batch %d is not compiled for T=%d", t->rows_per_batch, T);
     const int64_t nslices = (cols + kSlice - 1) / kSlice;
+    const bool stream_shape = row_bytes(fmt, cols) % 16 == 0 && t->waves_per_wg >= nslices &&
+                              t->waves_per_wg % nslices == 0;
+    if (t->kind < 0)  // override without a kind: streamed when the shape and tile allow it
+        t->kind = stream_shape && stream_supported(fmt, T, t->rows_per_batch) &&
+                  stream_lds_bytes(fmt, *t, T, (int)nslices) <= kMaxLds;
+    if (t->kind == 1) {
+        // waves = slices x row groups
+        if (!stream_shape)
+            return fail(QG_EINVAL, "streamed tile needs rows of a multiple of 16 bytes and waves_per_wg a multiple of "
+                                   "the %lld k slices", (long long)nslices);
+        if (!stream_supported(fmt, T, t->rows_per_batch))
+            return fail(QG_EINVAL, "streamed rows_per_batch %d is not compiled for T=%d", t->rows_per_batch, T);
+        if (stream_lds_bytes(fmt, *t, T, (int)nslices) > kMaxLds)
+            return fail(QG_EINVAL, "tile needs %zu B of LDS (rows_per_wg %d too large)",
+                        stream_lds_bytes(fmt, *t, T, (int)nslices), t->rows_per_wg);
+        return QG_OK;
+    }
     if (t->waves_per_wg > nslices) t->waves_per_wg = (int)nslices;  // idle waves would only add zeros
+    if (!tile_supported(fmt, T, t->rows_per_batch, one_shot(*t, (int)nslices)))
+        return fail(QG_EINVAL, "rows_per_batch %d is not compiled for T=%d with this tile", t->rows_per_batch, T);
     if (lds_bytes(*t, T) > kMaxLds)
         return fail(QG_EINVAL, "tile needs %zu B of LDS (rows_per_wg %d too large)", lds_bytes(*t, T), t->rows_per_wg);
     return QG_OK;
@@ -172,7 +210,7 @@ int run_dense(int fmt, int64_t rows, int64_t cols, int T, const void* W, const f
     a.nslices = (int)((cols + kSlice - 1) / kSlice);
     a.rows_per_wg = tile.rows_per_wg;
     if ((rows + tile.rows_per_wg - 1) / tile.rows_per_wg > 0x7FFFFFFF) return fail(QG_EUNSUPPORTED, "grid too large");
-    int err = launch_dense(fmt, T, tile, a, stream);
+    int err = tile.kind == 1 ? launch_stream(fmt, T, tile, a, stream) : launch_dense(fmt, T, tile, a, stream);
     if (err) return fail(QG_EHIP, "kernel launch failed: %s", hip_error_name(err));
     return ok();
 }
@@ -213,6 +251,14 @@ int qgemv_grouped_experts(int fmt, int64_t n_experts, int64_t rows, int64_t cols
         return fail(QG_EINVAL, "y overlaps W, x or ids");
     Tile tile;
     if ((st = pick_tile(fmt, rows, cols, QG_MAX_T, &tile))) return st;  // one kernel for 1..4 tokens per expert
+    if (tile.kind != 0) {  // the grouped kernel runs the direct path: one wave per slice
+        tile.kind = 0;
+        const int64_t nsl = (cols + kSlice - 1) / kSlice;
+        if (tile.waves_per_wg > nsl) tile.waves_per_wg = (int)nsl;
+        tile.rows_per_wg = 2 * tile.rows_per_batch;
+        if (!tile_supported(fmt, QG_MAX_T, tile.rows_per_batch, one_shot(tile, (int)((cols + kSlice - 1) / kSlice))))
+            tile.rows_per_batch = 2, tile.rows_per_wg = 4;
+    }
     GroupedArgs a;
     a.W = (const uint8_t*)W;
     a.x = x;
@@ -316,6 +362,7 @@ int qg_query_tile(int fmt, int64_t rows, int64_t cols, int T, int out_tile[QG_TI
     out_tile[3] = t.k_slice;
     out_tile[4] = t.rows_per_wg;
     out_tile[5] = t.mfma;
+    out_tile[6] = t.kind;
     return ok();
 }
 

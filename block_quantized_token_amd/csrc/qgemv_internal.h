@@ -17,6 +17,7 @@ struct Tile {
     int k_slice;         // 512 (fixed by the kernels)
     int rows_per_wg;     // RW: rows per workgroup (multiple of 2*RB)
     int mfma;            // 0: VALU path
+    int kind;            // 0: direct (lanes load their own bytes); 1: streamed through LDS
 };
 
 constexpr int kLanesPerRow = 32;
@@ -32,17 +33,45 @@ inline size_t lds_bytes(const Tile& t, int T) {
     const size_t nbatch = (size_t)(t.rows_per_wg + 2 * t.rows_per_batch - 1) / (2 * t.rows_per_batch);
     return nbatch * t.waves_per_wg * 2 * t.rows_per_batch * pad_tokens(T) * 4 + nbatch * 4;
 }
+// (a workgroup of a single batch uses only the first nw * 2 * N floats)
 constexpr size_t kMaxLds = 64 * 1024;
 
-inline bool valid_rb(int rb) { return rb == 1 || rb == 2 || rb == 4 || rb == 8; }
+inline bool valid_rb(int rb) { return rb == 1 || rb == 2 || rb == 4 || rb == 8 || rb == 16; }
 
 // The compiled set: rows_per_batch values instantiated for T tokens (the ones
 // whose registers fit the 768-thread budget without spilling).  The grouped
 // kernel serves up to 4 tokens per expert, so it uses the T = 4 row.
-inline bool tile_supported(int T, int rb) {
+// A workgroup of one batch whose waves have one k slice each runs the one-shot
+// kernel (every load of a wave in flight at once, one reduction); otherwise the
+// pipelined kernel (ping-pong batches) runs.
+inline bool one_shot(const Tile& t, int nslices) {
+    return t.rows_per_wg == 2 * t.rows_per_batch && nslices <= t.waves_per_wg;
+}
+
+// Streamed kernel: a tile is 2 * RB rows; RB in {4, 8}.  Chunks (16 B) per full
+// row slice and the per-wave LDS buffer it needs.
+inline int stream_chunks(int fmt) { return fmt == QG_FMT_Q8_0 ? 34 : fmt == QG_FMT_Q4_0 ? 18 : 64; }
+inline size_t stream_buf_bytes(int fmt, int rb) { return (size_t)((2 * rb * stream_chunks(fmt) + 63) / 64) * 1024; }
+// waves_per_wg = nslices * row groups; each row group walks its tiles in pairs.
+inline size_t stream_lds_bytes(int fmt, const Tile& t, int T, int nslices) {
+    const size_t rg = (size_t)(t.waves_per_wg / nslices);
+    size_t ntiles = (size_t)(t.rows_per_wg + 2 * t.rows_per_batch - 1) / (2 * t.rows_per_batch);
+    ntiles = (ntiles + 2 * rg - 1) / (2 * rg) * (2 * rg);
+    return t.waves_per_wg * stream_buf_bytes(fmt, t.rows_per_batch) +
+           ntiles * nslices * 2 * t.rows_per_batch * pad_tokens(T) * 4;
+}
+inline bool stream_supported(int fmt, int T, int rb) {
+    if (rb == 4) return fmt != QG_FMT_BF16 || T <= 2;
+    if (rb == 8) return (fmt == QG_FMT_Q8_0 && T == 1) || (fmt == QG_FMT_Q4_0 && T <= 2);
+    return false;
+}
+
+inline bool tile_supported(int fmt, int T, int rb, bool oneshot) {
+    if (!valid_rb(rb) || rb * pad_tokens(T) > 32) return false;
+    if (oneshot) return true;
     if (rb == 1 || rb == 2) return true;
     if (rb == 4) return T <= 3;
-    if (rb == 8) return T == 1;
+    if (rb == 8) return T == 1 && fmt != QG_FMT_BF16;
     return false;
 }
 
@@ -76,6 +105,7 @@ struct GroupedArgs {
 
 // Launchers (qgemv_kernels.hip).  Return a hipError_t value as int.
 int launch_dense(int fmt, int T, const Tile& tile, const DenseArgs& a, void* stream);
+int launch_stream(int fmt, int T, const Tile& tile, const DenseArgs& a, void* stream);
 int launch_grouped(int fmt, const Tile& tile, const GroupedArgs& a, void* stream);
 const char* hip_error_name(int err);
 

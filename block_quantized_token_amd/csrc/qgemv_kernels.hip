@@ -38,15 +38,18 @@ namespace {
 struct __attribute__((packed, aligned(2))) U4u { uint32_t v[4]; };  // 16 B at 2-byte alignment
 struct __attribute__((packed, aligned(2))) U2u { uint32_t v[2]; };  // 8 B at 2-byte alignment
 struct __attribute__((aligned(16))) U4a { uint32_t v[4]; };
+typedef uint32_t V4 __attribute__((ext_vector_type(4)));  // 16 B in four VGPRs
 
 __device__ __forceinline__ float half_bits_to_float(uint32_t bits) {
     return (float)__builtin_bit_cast(_Float16, (uint16_t)bits);
 }
 
 // ---------------------------------------------------------------- formats
-// Each format says which k positions lane li owns inside a 512-wide slice, how
-// to fetch the lane's bytes for one row, and how to turn them into 16 fp32
-// weights (up to a per-block scale).
+// Each format says which k positions lane li owns inside a 512-wide slice, where
+// the lane's bytes of one row sit, and how to turn them into 16 fp32 weights (up
+// to a per-block scale).  Loads are never predicated: a lane with no weights in
+// range reads lane 0's bytes of the same row (always in range) and its result
+// is dropped by a select, so every load of a batch can be in flight at once.
 template <int FMT> struct Fmt;
 
 template <> struct Fmt<QG_FMT_Q8_0> {
@@ -54,9 +57,10 @@ template <> struct Fmt<QG_FMT_Q8_0> {
     static constexpr bool kScaled = true;
     struct Raw { uint32_t c[4]; uint32_t d; };
     // block q = li / 2 of the slice, codes [16 h, 16 h + 16) with h = li % 2
-    __device__ static int kpos(int li, int i) { return 32 * (li >> 1) + 16 * (li & 1) + i; }
+    __device__ static int kbase(int li, int half) { return 32 * (li >> 1) + 16 * (li & 1) + 8 * half; }
     __device__ static int64_t slice_offset(int s) { return (int64_t)s * 16 * kBlockBytes; }
-    __device__ static bool lane_valid(int li, int kslice0, int cols) { return kslice0 + 32 * (li >> 1) < cols; }
+    __device__ static bool lane_valid(int li, int k0, int cols) { return k0 + 32 * (li >> 1) < cols; }
+    __device__ static bool upper_valid(int, int, int) { return true; }
     __device__ static Raw load(const uint8_t* slice, int li) {
         const uint8_t* blk = slice + (li >> 1) * kBlockBytes;
         const U4u q = *reinterpret_cast<const U4u*>(blk + 2 + 16 * (li & 1));
@@ -65,7 +69,6 @@ template <> struct Fmt<QG_FMT_Q8_0> {
         r.d = *reinterpret_cast<const uint16_t*>(blk);
         return r;
     }
-    __device__ static Raw zero() { Raw r; r.c[0] = r.c[1] = r.c[2] = r.c[3] = 0; r.d = 0; return r; }
     __device__ static float scale(const Raw& r) { return half_bits_to_float(r.d); }
     __device__ static float weight(const Raw& r, int i) {
         return (float)(int32_t)(int8_t)(r.c[i >> 2] >> (8 * (i & 3)));
@@ -77,12 +80,11 @@ template <> struct Fmt<QG_FMT_Q4_0> {
     static constexpr bool kScaled = true;
     struct Raw { uint32_t c[2]; uint32_t d; };
     // block q = li / 2, bytes [8 h, 8 h + 8) of its 16 code bytes: low nibbles are
-    // codes 8h .. 8h+7 (i < 8), high nibbles codes 16 + 8h .. 16 + 8h + 7 (i >= 8)
-    __device__ static int kpos(int li, int i) {
-        return 32 * (li >> 1) + (i < 8 ? 8 * (li & 1) + i : 16 + 8 * (li & 1) + (i - 8));
-    }
+    // codes 8h .. 8h+7 (weights 0..7), high nibbles codes 16 + 8h .. (weights 8..15)
+    __device__ static int kbase(int li, int half) { return 32 * (li >> 1) + 8 * (li & 1) + 16 * half; }
     __device__ static int64_t slice_offset(int s) { return (int64_t)s * 16 * kBlockBytes; }
-    __device__ static bool lane_valid(int li, int kslice0, int cols) { return kslice0 + 32 * (li >> 1) < cols; }
+    __device__ static bool lane_valid(int li, int k0, int cols) { return k0 + 32 * (li >> 1) < cols; }
+    __device__ static bool upper_valid(int, int, int) { return true; }
     __device__ static Raw load(const uint8_t* slice, int li) {
         const uint8_t* blk = slice + (li >> 1) * kBlockBytes;
         const U2u q = *reinterpret_cast<const U2u*>(blk + 2 + 8 * (li & 1));
@@ -91,7 +93,6 @@ template <> struct Fmt<QG_FMT_Q4_0> {
         r.d = *reinterpret_cast<const uint16_t*>(blk);
         return r;
     }
-    __device__ static Raw zero() { Raw r; r.c[0] = r.c[1] = 0; r.d = 0; return r; }
     // codes are returned as 16 * (c - 8): flipping bit 3 of a nibble gives the
     // 4-bit two's complement of c - 8, and shifting it to the top of a byte makes
     // a signed byte; the 16 is taken back out of the scale (exact: a power of 2).
@@ -99,7 +100,7 @@ template <> struct Fmt<QG_FMT_Q4_0> {
     __device__ static float weight(const Raw& r, int i) {
         const uint32_t w = r.c[(i & 7) >> 2] ^ 0x88888888u;
         const uint32_t b = (i < 8) ? (w << 4) : w;  // nibble to the top of its byte
-        return (float)(int32_t)(int8_t)((b >> (8 * (i & 3) + 0)) & 0xF0u);
+        return (float)(int32_t)(int8_t)((b >> (8 * (i & 3))) & 0xF0u);
     }
 };
 
@@ -107,23 +108,20 @@ template <> struct Fmt<QG_FMT_BF16> {
     static constexpr bool kScaled = false;
     struct Raw { uint32_t c[8]; };
     // values [16 li, 16 li + 16) of the slice
-    __device__ static int kpos(int li, int i) { return 16 * li + i; }
+    __device__ static int kbase(int li, int half) { return 16 * li + 8 * half; }
     __device__ static int64_t slice_offset(int s) { return (int64_t)s * kSlice * 2; }
-    __device__ static bool lane_valid(int li, int kslice0, int cols) { return kslice0 + 16 * li < cols; }
-    __device__ static Raw load_masked(const uint8_t* slice, int li, int kslice0, int cols) {
+    __device__ static bool lane_valid(int li, int k0, int cols) { return k0 + 16 * li < cols; }
+    // cols % 8 == 0: the lane's second 8 values may lie past the end of the row
+    __device__ static bool upper_valid(int li, int k0, int cols) { return k0 + 16 * li + 8 < cols; }
+    __device__ static Raw load(const uint8_t* slice, int li, bool upper_ok) {
         const U4a* p = reinterpret_cast<const U4a*>(slice + 32 * li);
         const U4a a = p[0];
+        const U4a b = p[upper_ok ? 1 : 0];
         Raw r;
         r.c[0] = a.v[0]; r.c[1] = a.v[1]; r.c[2] = a.v[2]; r.c[3] = a.v[3];
-        if (kslice0 + 16 * li + 8 < cols) {
-            const U4a b = p[1];
-            r.c[4] = b.v[0]; r.c[5] = b.v[1]; r.c[6] = b.v[2]; r.c[7] = b.v[3];
-        } else {
-            r.c[4] = r.c[5] = r.c[6] = r.c[7] = 0;
-        }
+        r.c[4] = b.v[0]; r.c[5] = b.v[1]; r.c[6] = b.v[2]; r.c[7] = b.v[3];
         return r;
     }
-    __device__ static Raw zero() { Raw r; for (int i = 0; i < 8; ++i) r.c[i] = 0; return r; }
     __device__ static float scale(const Raw&) { return 1.0f; }
     __device__ static float weight(const Raw& r, int i) {
         const uint32_t w = r.c[i >> 1];
@@ -132,37 +130,72 @@ template <> struct Fmt<QG_FMT_BF16> {
 };
 
 template <int FMT>
-__device__ __forceinline__ typename Fmt<FMT>::Raw load_lane(const uint8_t* slice, int li, int kslice0, int cols,
-                                                            bool row_ok) {
-    using F = Fmt<FMT>;
-    if (!row_ok || !F::lane_valid(li, kslice0, cols)) return F::zero();
-    if constexpr (FMT == QG_FMT_BF16) return F::load_masked(slice, li, kslice0, cols);
-    else return F::load(slice, li);
+__device__ __forceinline__ typename Fmt<FMT>::Raw load_lane(const uint8_t* slice, int li_eff, bool upper_ok) {
+    if constexpr (FMT == QG_FMT_BF16) return Fmt<FMT>::load(slice, li_eff, upper_ok);
+    else return Fmt<FMT>::load(slice, li_eff);
 }
 
 // ------------------------------------------------------------- reduction
 // Halving butterfly over the 32 lanes of a row: with N values per lane, stage m
-// (16, 8, 4, 2, 1) pairs lane li with li ^ m; the lane with bit m set keeps the
-// upper half of its values and adds its partner's upper half, the other keeps
-// the lower half.  After 5 stages value v's sum over all 32 lanes sits in the
-// lanes whose index() is v.  The pairing of lanes at each stage -- hence every
-// value's addition tree -- does not depend on N.
+// (16, 8, 4, 2, 1) pairs each lane with a partner whose lane bit m differs; the
+// lane with bit m set keeps the upper half of its values and adds its partner's
+// upper half, the other keeps the lower half.  After 5 stages value v's sum
+// over all 32 lanes sits in the lanes whose index() is v.
+//   stage 16: v_permlane16_swap (rows of 16 lanes swap halves; one add finishes)
+//   stage  8: DPP row_mirror      (lane i <-> 15 - i)
+//   stage  4: DPP row_half_mirror (lane i <-> 7 - i)
+//   stage  2: DPP quad_perm [2,3,0,1]
+//   stage  1: DPP quad_perm [1,0,3,2]
+// The partner of a lane at each stage -- hence every value's addition tree --
+// does not depend on N, so a token's sum does not depend on T.
+__device__ __forceinline__ float dpp_f(float v, int ctrl) {
+    switch (ctrl) {  // the control must be an immediate
+    case 0x140: return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x140, 0xF, 0xF, true));
+    case 0x141: return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x141, 0xF, 0xF, true));
+    case 0x4E: return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x4E, 0xF, 0xF, true));
+    default: return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0xB1, 0xF, 0xF, true));
+    }
+}
+
+// v_permlane16_swap a, b: lanes 16..31 of a trade places with lanes 0..15 of b
+// (and 48..63 of a with 32..47 of b).  Written as inline asm with both operands
+// read-write: the clang builtin of this ROCm release returns the first result
+// twice (r[0] + r[1] compiles to v + v), so its second result cannot be used.
+__device__ __forceinline__ void permlane16_swap(float& a, float& b) {
+    asm volatile("s_nop 1\n\tv_permlane16_swap_b32 %0, %1" : "+v"(a), "+v"(b));
+}
+
 template <int N>
 __device__ __forceinline__ void butterfly32(float (&v)[N], int li) {
+    // stage 16: after the swap, a lane of row 0 holds (its a, row 1's a) and a lane
+    // of row 1 holds (row 0's b, its b): one add gives the lower / upper half sums
+    if constexpr (N >= 2) {
 #pragma unroll
-    for (int st = 0; st < 5; ++st) {
+        for (int i = 0; i < N / 2; ++i) {
+            float a = v[i], b = v[i + N / 2];
+            permlane16_swap(a, b);
+            v[i] = a + b;
+        }
+    } else {
+        float a = v[0], b = v[0];
+        permlane16_swap(a, b);
+        v[0] = a + b;
+    }
+    constexpr int ctrls[4] = {0x140, 0x141, 0x4E, 0xB1};
+#pragma unroll
+    for (int st = 1; st < 5; ++st) {
         const int m = 16 >> st;
         const int cnt = N >> st;
         if (cnt >= 2) {
             const bool up = (li & m) != 0;
 #pragma unroll
             for (int i = 0; i < cnt / 2; ++i) {
-                const float send = up ? v[i] : v[i + cnt / 2];
-                const float keep = up ? v[i + cnt / 2] : v[i];
-                v[i] = keep + __shfl_xor(send, m, 64);
+                const float lo = v[i] + dpp_f(v[i], ctrls[st - 1]);
+                const float hi = v[i + cnt / 2] + dpp_f(v[i + cnt / 2], ctrls[st - 1]);
+                v[i] = up ? hi : lo;
             }
         } else {
-            v[0] = v[0] + __shfl_xor(v[0], m, 64);
+            v[0] = v[0] + dpp_f(v[0], ctrls[st - 1]);
         }
     }
 }
@@ -190,18 +223,136 @@ constexpr int pad_pow2(int t) { return t <= 1 ? 1 : t <= 2 ? 2 : 4; }
 // One workgroup: rows [row_begin, row_end) of one matrix, all of k.  NT tokens;
 // token n reads x + xoff[n] and its outputs go through out(n, row, value).
 //
-// Cross-wave reduction without barriers: every batch of 2*RB rows has its own
-// LDS slots [wave][row group][value] and an arrival counter.  A wave writes its
-// butterfly results, then bumps the counter; the wave that arrives last adds the
-// NW partial sets in wave order and stores the outputs.  No wave ever waits for
+// A batch is 2*RB rows: each 32-lane half of a wave takes every other row.  The
+// loads of batch b+1 are issued before batch b is computed (ping-pong register
+// sets), so a wave always has a batch of weights in flight.
+//
+// Cross-wave reduction without barriers: every batch has its own LDS slots
+// [wave][row group][value] and an arrival counter.  A wave writes its butterfly
+// results, then bumps the counter; the wave that arrives last adds the NW
+// partial sets in wave order and stores the outputs.  No wave ever waits for
 // another, and no slot is reused within a launch.
+template <int FMT, int NT, int RB>
+struct RowsCtx {
+    using F = Fmt<FMT>;
+    static constexpr int TP = pad_pow2(NT);
+    static constexpr int N = RB * TP;  // values per lane entering the butterfly
+    const uint8_t* W;
+    int64_t row_bytes, row_begin, row_end;
+    int g, li;
+};
+
+template <int FMT, int NT, int RB>
+__device__ __forceinline__ void issue_batch(const RowsCtx<FMT, NT, RB>& c, int64_t rb0, int64_t slice_off, int li_eff,
+                                            bool upper_ok, typename Fmt<FMT>::Raw (&raw)[RB]) {
+#pragma unroll
+    for (int r = 0; r < RB; ++r) {
+        int64_t row = rb0 + 2 * r + c.g;
+        row = row < c.row_end ? row : c.row_begin;  // out-of-range rows reread a valid row; never stored
+        raw[r] = load_lane<FMT>(c.W + row * c.row_bytes + slice_off, li_eff, upper_ok);
+    }
+}
+
+template <int FMT, int NT, int RB>
+__device__ __forceinline__ void accumulate_batch(const typename Fmt<FMT>::Raw (&raw)[RB], const float (&xr)[NT][kWeightsPerLane],
+                                                 bool lane_ok, bool upper_ok, float (&acc)[RB][pad_pow2(NT)]) {
+    using F = Fmt<FMT>;
+#pragma unroll
+    for (int r = 0; r < RB; ++r) {
+        float p[NT];
+#pragma unroll
+        for (int n = 0; n < NT; ++n) p[n] = 0.0f;
+        float ph[NT];
+#pragma unroll
+        for (int i = 0; i < kWeightsPerLane; ++i) {
+            if (i == kWeightsPerLane / 2) {
+#pragma unroll
+                for (int n = 0; n < NT; ++n) ph[n] = p[n];
+            }
+            const float w = F::weight(raw[r], i);
+#pragma unroll
+            for (int n = 0; n < NT; ++n) p[n] = __builtin_fmaf(w, xr[n][i], p[n]);
+        }
+        if constexpr (F::kScaled) {
+            // a lane with nothing in range decoded finite codes from in-range bytes and
+            // read in-range x, so its p is finite and 0 * p adds exactly nothing
+            const float d = lane_ok ? F::scale(raw[r]) : 0.0f;
+#pragma unroll
+            for (int n = 0; n < NT; ++n) acc[r][n] = __builtin_fmaf(d, p[n], acc[r][n]);
+        } else {
+#pragma unroll
+            for (int n = 0; n < NT; ++n) {
+                const float q = upper_ok ? p[n] : ph[n];  // drop values past the end of the row
+                acc[r][n] = acc[r][n] + (lane_ok ? q : 0.0f);
+            }
+        }
+    }
+}
+
+template <int FMT, int NT>
+__device__ __forceinline__ void load_x(const float* __restrict__ x, const int64_t (&xoff)[NT], int k0, int li, bool lane_ok,
+                                       int cols, float (&xr)[NT][kWeightsPerLane]) {
+    using F = Fmt<FMT>;
+    // two runs of 8 consecutive k per lane; a lane with nothing in range reads the
+    // token's first 8 values (cols >= 8 always), and its products are discarded
+    const int b0 = lane_ok ? k0 + F::kbase(li, 0) : 0;
+    const int b1 = lane_ok ? k0 + F::kbase(li, 1) : 0;
+    const int b1c = b1 + 8 <= cols ? b1 : b0;  // BF16 tail: the upper run may not exist
+#pragma unroll
+    for (int n = 0; n < NT; ++n) {
+        const float4* p0 = reinterpret_cast<const float4*>(x + xoff[n] + b0);
+        const float4* p1 = reinterpret_cast<const float4*>(x + xoff[n] + b1c);
+        const float4 a = p0[0], b = p0[1], c = p1[0], d = p1[1];
+        xr[n][0] = a.x; xr[n][1] = a.y; xr[n][2] = a.z; xr[n][3] = a.w;
+        xr[n][4] = b.x; xr[n][5] = b.y; xr[n][6] = b.z; xr[n][7] = b.w;
+        xr[n][8] = c.x; xr[n][9] = c.y; xr[n][10] = c.z; xr[n][11] = c.w;
+        xr[n][12] = d.x; xr[n][13] = d.y; xr[n][14] = d.z; xr[n][15] = d.w;
+    }
+}
+
 template <int FMT, int NT, int RB, class Out>
+__device__ __forceinline__ void reduce_batch(float (&acc)[RB][pad_pow2(NT)], int b, int64_t rb0, float* part,
+                                             int* arrivals, int nw, int wave, int lane, int li, int g, int my_idx,
+                                             bool writer, int64_t row_end, Out& out) {
+    constexpr int TP = pad_pow2(NT);
+    constexpr int N = RB * TP;
+    float v[N];
+#pragma unroll
+    for (int r = 0; r < RB; ++r)
+#pragma unroll
+        for (int t = 0; t < TP; ++t) v[r * TP + t] = acc[r][t];
+    butterfly32<N>(v, li);
+    float* mine = part + (((size_t)b * nw + wave) * 2 + g) * N;
+    if (writer) mine[my_idx] = v[0];
+    // publish this wave's slots, then count the arrival (one atomic per wave)
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+    int prev = 0;
+    if (lane == 0) prev = __hip_atomic_fetch_add(&arrivals[b], 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_WORKGROUP);
+    prev = __shfl(prev, 0, 64);
+    if (prev == nw - 1) {  // last arrival: all nw partial sets of batch b are in LDS
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+        if (lane < 2 * N) {
+            const int gg = lane / N, idx = lane % N;
+            const int t = idx % TP, r = idx / TP;
+            const int64_t row = rb0 + 2 * r + gg;
+            if (t < NT && row < row_end) {
+                const float* base = part + (size_t)b * nw * 2 * N + gg * N + idx;
+                float sum = base[0];
+                for (int w = 1; w < nw; ++w) sum = sum + base[(size_t)w * 2 * N];
+                out(t, row, sum);
+            }
+        }
+    }
+}
+
+template <int FMT, int NT, int RB, bool ONE_SHOT, class Out>
 __device__ __forceinline__ void gemv_rows(const uint8_t* __restrict__ W, int64_t row_bytes, int cols, int nslices,
                                           const float* __restrict__ x, const int64_t (&xoff)[NT], int64_t row_begin,
                                           int64_t row_end, Out out) {
     using F = Fmt<FMT>;
+    using Raw = typename F::Raw;
     constexpr int TP = pad_pow2(NT);
-    constexpr int N = RB * TP;  // values per lane entering the butterfly
+    constexpr int N = RB * TP;
     static_assert(N <= 32, "rows_per_batch * tokens too large");
     extern __shared__ float lds[];
 
@@ -212,100 +363,299 @@ __device__ __forceinline__ void gemv_rows(const uint8_t* __restrict__ W, int64_t
     const int g = lane >> 5;   // which of the two rows of a step
     const int li = lane & 31;  // lane within the row
     const int nbatch = (int)((row_end - row_begin + 2 * RB - 1) / (2 * RB));
-    float* part = lds;                                             // [nbatch][nw][2][N]
-    int* arrivals = reinterpret_cast<int*>(lds + (size_t)nbatch * nw * 2 * N);  // [nbatch]
-    for (int i = tid; i < nbatch; i += blockDim.x) arrivals[i] = 0;
-    __syncthreads();
 
     bool writer;
     const int my_idx = butterfly_index<N>(li, writer);
-
+    const RowsCtx<FMT, NT, RB> c{W, row_bytes, row_begin, row_end, g, li};
     float xr[NT][kWeightsPerLane];
-    int loaded_slice = -1;
+    float acc[RB][TP];
+#pragma unroll
+    for (int r = 0; r < RB; ++r)
+#pragma unroll
+        for (int t = 0; t < TP; ++t) acc[r][t] = 0.0f;
 
-    for (int b = 0; b < nbatch; ++b) {
-        const int64_t rb0 = row_begin + (int64_t)b * 2 * RB;
-        float acc[RB][TP];
-#pragma unroll
-        for (int r = 0; r < RB; ++r)
-#pragma unroll
-            for (int t = 0; t < TP; ++t) acc[r][t] = 0.0f;
-
-        for (int s = wave; s < nslices; s += nw) {
-            const int k0 = s * kSlice;
-            if (s != loaded_slice) {
-                const bool ok = F::lane_valid(li, k0, cols);
-#pragma unroll
-                for (int n = 0; n < NT; ++n)
-#pragma unroll
-                    for (int i = 0; i < kWeightsPerLane; ++i) {
-                        const int k = k0 + F::kpos(li, i);
-                        xr[n][i] = (ok && k < cols) ? x[xoff[n] + k] : 0.0f;
-                    }
-                loaded_slice = s;
-            }
-            typename F::Raw raw[RB];
-#pragma unroll
-            for (int r = 0; r < RB; ++r) {
-                const int64_t row = rb0 + 2 * r + g;
-                const bool row_ok = row < row_end;
-                raw[r] = load_lane<FMT>(W + (row_ok ? row : row_begin) * row_bytes + F::slice_offset(s), li, k0, cols,
-                                        row_ok);
-            }
-#pragma unroll
-            for (int r = 0; r < RB; ++r) {
-                float p[NT];
-#pragma unroll
-                for (int n = 0; n < NT; ++n) p[n] = 0.0f;
-#pragma unroll
-                for (int i = 0; i < kWeightsPerLane; ++i) {
-                    const float w = F::weight(raw[r], i);
-#pragma unroll
-                    for (int n = 0; n < NT; ++n) p[n] = __builtin_fmaf(w, xr[n][i], p[n]);
-                }
-                if constexpr (F::kScaled) {
-                    const float d = F::scale(raw[r]);
-#pragma unroll
-                    for (int n = 0; n < NT; ++n) acc[r][n] = __builtin_fmaf(d, p[n], acc[r][n]);
-                } else {
-#pragma unroll
-                    for (int n = 0; n < NT; ++n) acc[r][n] = acc[r][n] + p[n];
-                }
-            }
-        }
-
+    if constexpr (ONE_SHOT) {
+        // One shot (the host guarantees one batch per workgroup and one slice
+        // per wave): all of the wave's loads go out together, then one reduction
+        // through LDS.  (A wave past the last slice would read slice 0 with
+        // every lane invalid: it only adds zeros.)
+        (void)nbatch;
+        const int s = wave < nslices ? wave : 0;
+        const int k0 = s * kSlice;
+        const bool lane_ok = wave < nslices && F::lane_valid(li, k0, cols);
+        const bool upper_ok = lane_ok && F::upper_valid(li, k0, cols);
+        Raw ra[RB];
+        issue_batch(c, row_begin, F::slice_offset(s), lane_ok ? li : 0, upper_ok, ra);
+        load_x<FMT, NT>(x, xoff, k0, li, lane_ok, cols, xr);
+        accumulate_batch<FMT, NT, RB>(ra, xr, lane_ok, upper_ok, acc);
         float v[N];
 #pragma unroll
         for (int r = 0; r < RB; ++r)
 #pragma unroll
             for (int t = 0; t < TP; ++t) v[r * TP + t] = acc[r][t];
         butterfly32<N>(v, li);
-        float* mine = part + (((size_t)b * nw + wave) * 2 + g) * N;
-        if (writer) mine[my_idx] = v[0];
-        // publish this wave's slots, then count the arrival (one atomic per wave)
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-        int prev = 0;
-        if (lane == 0) prev = __hip_atomic_fetch_add(&arrivals[b], 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_WORKGROUP);
-        prev = __shfl(prev, 0, 64);
-        if (prev == nw - 1) {  // last arrival: all nw partial sets of batch b are in LDS
-            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
-            if (lane < 2 * N) {
-                const int gg = lane / N, idx = lane % N;
-                const int t = idx % TP, r = idx / TP;
-                const int64_t row = rb0 + 2 * r + gg;
-                if (t < NT && row < row_end) {
-                    const float* base = part + (size_t)b * nw * 2 * N + gg * N + idx;
-                    float sum = base[0];
-                    for (int w = 1; w < nw; ++w) sum = sum + base[(size_t)w * 2 * N];
-                    out(t, row, sum);
-                }
+        float* part = lds;  // [nw][2][N]
+        if (writer) part[(wave * 2 + g) * N + my_idx] = v[0];
+        __syncthreads();
+        if (tid < 2 * N) {
+            const int gg = tid / N, idx = tid % N;
+            const int t = idx % TP, r = idx / TP;
+            const int64_t row = row_begin + 2 * r + gg;
+            if (t < NT && row < row_end) {
+                const float* base = part + gg * N + idx;
+                float sum = base[0];
+                for (int w = 1; w < nw; ++w) sum = sum + base[w * 2 * N];
+                out(t, row, sum);
             }
         }
+        return;
+    } else {
+
+    float* part = lds;                                                           // [nbatch][nw][2][N]
+    int* arrivals = reinterpret_cast<int*>(lds + (size_t)nbatch * nw * 2 * N);  // [nbatch]
+    for (int i = tid; i < nbatch; i += blockDim.x) arrivals[i] = 0;
+    __syncthreads();
+
+    if (nslices <= nw) {
+        // one slice per wave: x stays in registers; batch b+1 loads while b computes
+        const int s = wave < nslices ? wave : 0;  // (a wave past the last slice only adds zeros)
+        const int k0 = s * kSlice;
+        const bool lane_ok = wave < nslices && F::lane_valid(li, k0, cols);
+        const bool upper_ok = lane_ok && F::upper_valid(li, k0, cols);
+        const int li_eff = lane_ok ? li : 0;
+        const int64_t soff = F::slice_offset(s);
+        Raw ra[RB], rb[RB];
+        issue_batch(c, row_begin, soff, li_eff, upper_ok, ra);
+        load_x<FMT, NT>(x, xoff, k0, li, lane_ok, cols, xr);
+        for (int b = 0; b < nbatch; b += 2) {
+            const int64_t r0 = row_begin + (int64_t)b * 2 * RB;
+            // next batch (past the end: rows clamp to valid ones and nothing is stored)
+            issue_batch(c, r0 + 2 * RB, soff, li_eff, upper_ok, rb);
+#pragma unroll
+            for (int r = 0; r < RB; ++r)
+#pragma unroll
+                for (int t = 0; t < TP; ++t) acc[r][t] = 0.0f;
+            accumulate_batch<FMT, NT, RB>(ra, xr, lane_ok, upper_ok, acc);
+            reduce_batch<FMT, NT, RB>(acc, b, r0, part, arrivals, nw, wave, lane, li, g, my_idx, writer, row_end, out);
+            if (b + 1 >= nbatch) break;
+            issue_batch(c, r0 + 4 * RB, soff, li_eff, upper_ok, ra);
+#pragma unroll
+            for (int r = 0; r < RB; ++r)
+#pragma unroll
+                for (int t = 0; t < TP; ++t) acc[r][t] = 0.0f;
+            accumulate_batch<FMT, NT, RB>(rb, xr, lane_ok, upper_ok, acc);
+            reduce_batch<FMT, NT, RB>(acc, b + 1, r0 + 2 * RB, part, arrivals, nw, wave, lane, li, g, my_idx, writer,
+                                      row_end, out);
+        }
+        return;
+    }
+
+    // several slices per wave (cols > 512 * nw): x is reloaded per slice visit
+    int loaded_slice = -1;
+    bool lane_ok = false, upper_ok = false;
+    for (int b = 0; b < nbatch; ++b) {
+        const int64_t r0 = row_begin + (int64_t)b * 2 * RB;
+#pragma unroll
+        for (int r = 0; r < RB; ++r)
+#pragma unroll
+            for (int t = 0; t < TP; ++t) acc[r][t] = 0.0f;
+        for (int s = wave; s < nslices; s += nw) {
+            const int k0 = s * kSlice;
+            lane_ok = F::lane_valid(li, k0, cols);
+            upper_ok = lane_ok && F::upper_valid(li, k0, cols);
+            Raw ra[RB];
+            issue_batch(c, r0, F::slice_offset(s), lane_ok ? li : 0, upper_ok, ra);
+            if (s != loaded_slice) {
+                load_x<FMT, NT>(x, xoff, k0, li, lane_ok, cols, xr);
+                loaded_slice = s;
+            }
+            accumulate_batch<FMT, NT, RB>(ra, xr, lane_ok, upper_ok, acc);
+        }
+        reduce_batch<FMT, NT, RB>(acc, b, r0, part, arrivals, nw, wave, lane, li, g, my_idx, writer, row_end, out);
+    }
+    }
+}
+
+// ------------------------------------------------------- streamed variant
+// For rows whose byte length is a multiple of 16 (Q8_0/Q4_0: cols % 256 == 0;
+// BF16: cols % 8 == 0) and one k slice per wave.  Each wave streams its own
+// slice of a tile of ST rows: the slice bytes of the tile are cut into aligned
+// 16-byte chunks, lane l of load k fetching chunk 64k + l -- so every load
+// instruction reads ~1 KB of contiguous row bytes -- into registers; the wave
+// then writes them to its private LDS buffer in the same order and reads back
+// its own lane's bytes (a block-aligned 16 / 8 / 32 bytes at an arbitrary LDS
+// offset).  Two tiles are in flight per wave (ping-pong register sets); waves
+// never wait for each other until one barrier before the final cross-wave sum.
+template <int FMT> struct StreamFmt;
+template <> struct StreamFmt<QG_FMT_Q8_0> { static constexpr int kChunks = 34; };  // 16 blocks x 34 B
+template <> struct StreamFmt<QG_FMT_Q4_0> { static constexpr int kChunks = 18; };  // 16 blocks x 18 B
+template <> struct StreamFmt<QG_FMT_BF16> { static constexpr int kChunks = 64; };  // 512 x 2 B
+
+template <int FMT, int ST>
+struct StreamShape {
+    static constexpr int kChunks = StreamFmt<FMT>::kChunks;   // chunks per full row slice
+    static constexpr int kLoads = (ST * kChunks + 63) / 64;   // loads per lane per tile
+    static constexpr int kBufBytes = kLoads * 64 * 16;        // per-wave LDS buffer
+};
+
+template <int FMT>
+__device__ __forceinline__ typename Fmt<FMT>::Raw lds_lane(const uint8_t* row_slice, int li) {
+    using F = Fmt<FMT>;
+    typename F::Raw r;
+    if constexpr (FMT == QG_FMT_Q8_0) {
+        const uint8_t* blk = row_slice + (li >> 1) * 34;
+        const U4u q = *reinterpret_cast<const U4u*>(blk + 2 + 16 * (li & 1));
+        r.c[0] = q.v[0]; r.c[1] = q.v[1]; r.c[2] = q.v[2]; r.c[3] = q.v[3];
+        r.d = *reinterpret_cast<const uint16_t*>(blk);
+    } else if constexpr (FMT == QG_FMT_Q4_0) {
+        const uint8_t* blk = row_slice + (li >> 1) * 18;
+        const U2u q = *reinterpret_cast<const U2u*>(blk + 2 + 8 * (li & 1));
+        r.c[0] = q.v[0]; r.c[1] = q.v[1];
+        r.d = *reinterpret_cast<const uint16_t*>(blk);
+    } else {
+        const U4a* p = reinterpret_cast<const U4a*>(row_slice + 32 * li);
+        const U4a a = p[0], b = p[1];
+        r.c[0] = a.v[0]; r.c[1] = a.v[1]; r.c[2] = a.v[2]; r.c[3] = a.v[3];
+        r.c[4] = b.v[0]; r.c[5] = b.v[1]; r.c[6] = b.v[2]; r.c[7] = b.v[3];
+    }
+    return r;
+}
+
+// Buffer-resource word 3 for gfx9-family (CDNA) raw buffer loads.
+constexpr int kBufferRsrcWord3 = 0x00020000;
+// Byte offset no tile reaches: a lane loading from it gets zeros, no memory access.
+constexpr int kNoLoad = 0x7FFFFFF0;
+
+// Tile t of the workgroup's rows, one 16-byte chunk per lane per load, through a
+// buffer descriptor that covers exactly the tile's rows: padding lanes (offset
+// kNoLoad) and rows past the end fall outside it and are skipped by the
+// hardware; a tile past the last gets an empty descriptor.  Every load is
+// issued unconditionally, so wait counts stay exact.
+template <int FMT, int ST>
+__device__ __forceinline__ void stream_issue(const uint8_t* __restrict__ W, int64_t row_bytes, int64_t row_begin,
+                                             int64_t row_end, int ntiles, int t,
+                                             const int (&off)[StreamShape<FMT, ST>::kLoads],
+                                             V4 (&R)[StreamShape<FMT, ST>::kLoads]) {
+    constexpr int L = StreamShape<FMT, ST>::kLoads;
+    const bool live = t < ntiles;
+    const int64_t r0 = row_begin + (int64_t)(live ? t : 0) * ST;
+    const int64_t rows_here = row_end - r0 < ST ? row_end - r0 : ST;
+    const int num = live ? (int)(rows_here * row_bytes) : 0;
+    const __amdgpu_buffer_rsrc_t rsrc =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(W + r0 * row_bytes), (short)0, num, kBufferRsrcWord3);
+#pragma unroll
+    for (int k = 0; k < L; ++k) R[k] = __builtin_amdgcn_raw_buffer_load_b128(rsrc, off[k], 0, 0);
+}
+
+template <int FMT, int NT, int ST>
+__device__ __forceinline__ void stream_tile(const uint8_t* __restrict__ W, int64_t row_bytes, int64_t row_begin,
+                                            int64_t row_end, int ntiles, int t, int ahead,
+                                            const int (&off)[StreamShape<FMT, ST>::kLoads],
+                                            V4 (&R)[StreamShape<FMT, ST>::kLoads], uint8_t* buf, float* part,
+                                            const float (&xr)[NT][kWeightsPerLane], int lane, int li, int g, int s,
+                                            int nsl, bool lane_ok, bool upper_ok, int my_idx, bool writer) {
+    using F = Fmt<FMT>;
+    using S = StreamShape<FMT, ST>;
+    constexpr int TP = pad_pow2(NT);
+    constexpr int RB = ST / 2;
+    constexpr int N = RB * TP;
+    constexpr int L = S::kLoads;
+    // registers -> LDS (chunk order), then the next-but-one tile into R
+#pragma unroll
+    for (int k = 0; k < L; ++k) *reinterpret_cast<V4*>(buf + (64 * k + lane) * 16) = R[k];
+    stream_issue<FMT, ST>(W, row_bytes, row_begin, row_end, ntiles, t + ahead, off, R);
+    typename F::Raw raw[RB];
+#pragma unroll
+    for (int i = 0; i < RB; ++i) raw[i] = lds_lane<FMT>(buf + (2 * i + g) * (S::kChunks * 16), li);
+    float acc[RB][TP];
+#pragma unroll
+    for (int i = 0; i < RB; ++i)
+#pragma unroll
+        for (int n = 0; n < TP; ++n) acc[i][n] = 0.0f;
+    accumulate_batch<FMT, NT, RB>(raw, xr, lane_ok, upper_ok, acc);
+    float v[N];
+#pragma unroll
+    for (int i = 0; i < RB; ++i)
+#pragma unroll
+        for (int n = 0; n < TP; ++n) v[i * TP + n] = acc[i][n];
+    butterfly32<N>(v, li);
+    if (writer) part[(((size_t)t * nsl + s) * 2 + g) * N + my_idx] = v[0];
+}
+
+template <int FMT, int NT, int ST, class Out>
+__device__ __forceinline__ void stream_rows(const uint8_t* __restrict__ W, int64_t row_bytes, int cols, int nsl,
+                                            const float* __restrict__ x, const int64_t (&xoff)[NT], int64_t row_begin,
+                                            int64_t row_end, Out out) {
+    using F = Fmt<FMT>;
+    using S = StreamShape<FMT, ST>;
+    constexpr int TP = pad_pow2(NT);
+    constexpr int RB = ST / 2;      // rows per 32-lane group per tile
+    constexpr int N = RB * TP;      // values per lane entering the butterfly
+    constexpr int L = S::kLoads;
+    static_assert(N <= 32, "tile rows * tokens too large");
+    extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int nw = blockDim.x >> 6;
+    const int g = lane >> 5;
+    const int li = lane & 31;
+    // waves = slices x row groups: wave (s, rg) takes k slice s of tiles rg, rg + RG, ...
+    const int s = wave % nsl;
+    const int rg = wave / nsl;
+    const int RG = nw / nsl;
+    const int k0 = s * kSlice;
+    const int ntiles = (int)((row_end - row_begin + ST - 1) / ST);
+    uint8_t* buf = smem + wave * S::kBufBytes;
+    float* part = reinterpret_cast<float*>(smem + nw * S::kBufBytes);  // [tiles, rounded up to 2*RG][nsl][2][N]
+
+    // chunks of this wave's slice that exist (the last slice of a row may be short)
+    const int64_t rest = row_bytes - (int64_t)s * S::kChunks * 16;
+    const int cs = rest / 16 < S::kChunks ? (int)(rest / 16) : S::kChunks;
+    // lane's chunk of load k: byte offset inside the tile (the same for every tile)
+    int off[L];
+#pragma unroll
+    for (int k = 0; k < L; ++k) {
+        const int j = 64 * k + lane;
+        const int r = j / S::kChunks, c = j % S::kChunks;
+        off[k] = (r < ST && c < cs) ? (int)(r * row_bytes) + s * S::kChunks * 16 + 16 * c : kNoLoad;
+    }
+
+    const bool lane_ok = F::lane_valid(li, k0, cols);
+    const bool upper_ok = lane_ok && F::upper_valid(li, k0, cols);
+    bool writer;
+    const int my_idx = butterfly_index<N>(li, writer);
+    float xr[NT][kWeightsPerLane];
+
+    V4 ra[L], rb[L];
+    load_x<FMT, NT>(x, xoff, k0, li, lane_ok, cols, xr);  // oldest loads first: waits inside the loop stay tight
+    stream_issue<FMT, ST>(W, row_bytes, row_begin, row_end, ntiles, rg, off, ra);
+    stream_issue<FMT, ST>(W, row_bytes, row_begin, row_end, ntiles, rg + RG, off, rb);
+    for (int t = rg; t < ntiles; t += 2 * RG) {
+        // both halves always run (a tile past the end loads nothing and its partial
+        // slots are never read), so every iteration has the same wait pattern
+        stream_tile<FMT, NT, ST>(W, row_bytes, row_begin, row_end, ntiles, t, 2 * RG, off, ra, buf, part, xr, lane, li,
+                                 g, s, nsl, lane_ok, upper_ok, my_idx, writer);
+        stream_tile<FMT, NT, ST>(W, row_bytes, row_begin, row_end, ntiles, t + RG, 2 * RG, off, rb, buf, part, xr, lane,
+                                 li, g, s, nsl, lane_ok, upper_ok, my_idx, writer);
+    }
+    __syncthreads();
+    // every output of the workgroup: sum the slices' partials in slice order
+    const int nrows = (int)(row_end - row_begin);
+    for (int o = tid; o < nrows * NT; o += blockDim.x) {
+        const int rr = o / NT, t = o % NT;
+        const int tl = rr / ST, rin = rr % ST;
+        const int gg = rin & 1, i = rin >> 1;
+        const float* base = part + ((size_t)tl * nsl * 2 + gg) * N + i * TP + t;
+        float sum = base[0];
+        for (int w = 1; w < nsl; ++w) sum = sum + base[(size_t)w * 2 * N];
+        out(t, row_begin + rr, sum);
     }
 }
 
 // ---------------------------------------------------------------- kernels
-template <int FMT, int T, int RB>
+template <int FMT, int T, int RB, bool ONE_SHOT>
 __global__ void __launch_bounds__(64 * kMaxWaves) qgemv_dense_kernel(DenseArgs a) {
     const int64_t row_begin = (int64_t)blockIdx.x * a.rows_per_wg;
     const int64_t row_end = row_begin + a.rows_per_wg < a.rows ? row_begin + a.rows_per_wg : a.rows;
@@ -314,8 +664,21 @@ __global__ void __launch_bounds__(64 * kMaxWaves) qgemv_dense_kernel(DenseArgs a
     for (int t = 0; t < T; ++t) xoff[t] = (int64_t)t * a.cols;
     float* __restrict__ y = a.y;
     const int64_t rows = a.rows;
-    gemv_rows<FMT, T, RB>(a.W, a.row_bytes, a.cols, a.nslices, a.x, xoff, row_begin, row_end,
+    gemv_rows<FMT, T, RB, ONE_SHOT>(a.W, a.row_bytes, a.cols, a.nslices, a.x, xoff, row_begin, row_end,
                           [=](int t, int64_t row, float v) { y[t * rows + row] = v; });
+}
+
+template <int FMT, int T, int ST>
+__global__ void __launch_bounds__(64 * kMaxWaves) qgemv_stream_kernel(DenseArgs a) {
+    const int64_t row_begin = (int64_t)blockIdx.x * a.rows_per_wg;
+    const int64_t row_end = row_begin + a.rows_per_wg < a.rows ? row_begin + a.rows_per_wg : a.rows;
+    int64_t xoff[T];
+#pragma unroll
+    for (int t = 0; t < T; ++t) xoff[t] = (int64_t)t * a.cols;
+    float* __restrict__ y = a.y;
+    const int64_t rows = a.rows;
+    stream_rows<FMT, T, ST>(a.W, a.row_bytes, a.cols, a.nslices, a.x, xoff, row_begin, row_end,
+                            [=](int t, int64_t row, float v) { y[t * rows + row] = v; });
 }
 
 // Grouped experts: workgroup (slot, tile) with slot = (t, j).  The workgroup of
@@ -323,7 +686,7 @@ __global__ void __launch_bounds__(64 * kMaxWaves) qgemv_dense_kernel(DenseArgs a
 // chose e (the M5 audit's expert grouping, section 1 item 2, done here inside
 // each workgroup from the tiny ids array instead of a separate plan pass);
 // workgroups of later slots with the same e exit at once.
-template <int FMT, int NE, int RB>
+template <int FMT, int NE, int RB, bool ONE_SHOT>
 __device__ __forceinline__ void grouped_run(const GroupedArgs& a, int e, uint32_t tokmask, int64_t row_begin, int64_t row_end) {
     const uint32_t tokmask0 = tokmask;
     int tk[NE];  // the NE tokens that chose e, ascending
@@ -339,7 +702,7 @@ __device__ __forceinline__ void grouped_run(const GroupedArgs& a, int e, uint32_
     float* __restrict__ y = a.y;
     const int topk = a.topk;
     const int64_t rows = a.rows;
-    gemv_rows<FMT, NE, RB>(a.W + (int64_t)e * a.expert_bytes, a.row_bytes, a.cols, a.nslices, a.x, xoff, row_begin,
+    gemv_rows<FMT, NE, RB, ONE_SHOT>(a.W + (int64_t)e * a.expert_bytes, a.row_bytes, a.cols, a.nslices, a.x, xoff, row_begin,
                            row_end, [=](int n, int64_t row, float v) {
                                // token of output n: the n-th set bit of tokmask (n varies
                                // across lanes, so no array indexing here)
@@ -351,7 +714,7 @@ __device__ __forceinline__ void grouped_run(const GroupedArgs& a, int e, uint32_
                            });
 }
 
-template <int FMT, int RB>
+template <int FMT, int RB, bool ONE_SHOT>
 __global__ void __launch_bounds__(64 * kMaxWaves) qgemv_grouped_kernel(GroupedArgs a) {
     const int slot = blockIdx.x / a.tiles_per_expert;
     const int tile = blockIdx.x % a.tiles_per_expert;
@@ -372,10 +735,10 @@ __global__ void __launch_bounds__(64 * kMaxWaves) qgemv_grouped_kernel(GroupedAr
         if (uses) tokmask |= 1u << t;
     }
     switch (__builtin_popcount(tokmask)) {
-    case 1: grouped_run<FMT, 1, RB>(a, e, tokmask, row_begin, row_end); break;
-    case 2: grouped_run<FMT, 2, RB>(a, e, tokmask, row_begin, row_end); break;
-    case 3: grouped_run<FMT, 3, RB>(a, e, tokmask, row_begin, row_end); break;
-    default: grouped_run<FMT, 4, RB>(a, e, tokmask, row_begin, row_end); break;
+    case 1: grouped_run<FMT, 1, RB, ONE_SHOT>(a, e, tokmask, row_begin, row_end); break;
+    case 2: grouped_run<FMT, 2, RB, ONE_SHOT>(a, e, tokmask, row_begin, row_end); break;
+    case 3: grouped_run<FMT, 3, RB, ONE_SHOT>(a, e, tokmask, row_begin, row_end); break;
+    default: grouped_run<FMT, 4, RB, ONE_SHOT>(a, e, tokmask, row_begin, row_end); break;
     }
 }
 
@@ -383,47 +746,85 @@ __global__ void __launch_bounds__(64 * kMaxWaves) qgemv_grouped_kernel(GroupedAr
 using DenseFn = void (*)(DenseArgs);
 using GroupedFn = void (*)(GroupedArgs);
 
-int rb_index(int rb) { return rb == 1 ? 0 : rb == 2 ? 1 : rb == 4 ? 2 : 3; }
+int rb_index(int rb) { return rb == 1 ? 0 : rb == 2 ? 1 : rb == 4 ? 2 : rb == 8 ? 3 : 4; }
 
-// Only the (T, RB) pairs of the compiled set (tile_supported) are instantiated.
-template <int FMT, int T>
+// Only the (format, T, RB, mode) combinations of the compiled set (tile_supported)
+// are instantiated.
+template <int FMT, int T, bool OS>
 DenseFn dense_entry(int rbi) {
-    if (rbi == 0) return qgemv_dense_kernel<FMT, T, 1>;
-    if (rbi == 1) return qgemv_dense_kernel<FMT, T, 2>;
-    if constexpr (T <= 3) {
-        if (rbi == 2) return qgemv_dense_kernel<FMT, T, 4>;
+    constexpr int TP = pad_pow2(T);
+    if (rbi == 0) return qgemv_dense_kernel<FMT, T, 1, OS>;
+    if (rbi == 1) return qgemv_dense_kernel<FMT, T, 2, OS>;
+    if constexpr (OS || T <= 3) {
+        if (rbi == 2) return qgemv_dense_kernel<FMT, T, 4, OS>;
     }
-    if constexpr (T == 1) {
-        if (rbi == 3) return qgemv_dense_kernel<FMT, T, 8>;
+    if constexpr ((OS && 8 * TP <= 32) || (!OS && T == 1 && FMT != QG_FMT_BF16)) {
+        if (rbi == 3) return qgemv_dense_kernel<FMT, T, 8, OS>;
+    }
+    if constexpr (OS && 16 * TP <= 32) {
+        if (rbi == 4) return qgemv_dense_kernel<FMT, T, 16, OS>;
     }
     return nullptr;
 }
 
-template <int FMT>
+template <int FMT, bool OS>
 DenseFn dense_for(int T, int rbi) {
     switch (T) {
-    case 1: return dense_entry<FMT, 1>(rbi);
-    case 2: return dense_entry<FMT, 2>(rbi);
-    case 3: return dense_entry<FMT, 3>(rbi);
-    default: return dense_entry<FMT, 4>(rbi);
+    case 1: return dense_entry<FMT, 1, OS>(rbi);
+    case 2: return dense_entry<FMT, 2, OS>(rbi);
+    case 3: return dense_entry<FMT, 3, OS>(rbi);
+    default: return dense_entry<FMT, 4, OS>(rbi);
     }
 }
 
-template <int FMT>
+template <int FMT, bool OS>
 GroupedFn grouped_for(int rbi) {
-    // one kernel serves 1..4 tokens per expert, so it takes the T = 4 limit on RB
-    if (rbi == 0) return qgemv_grouped_kernel<FMT, 1>;
-    if (rbi == 1) return qgemv_grouped_kernel<FMT, 2>;
+    // one kernel serves 1..4 tokens per expert, so it follows the T = 4 row of the set
+    if (rbi == 0) return qgemv_grouped_kernel<FMT, 1, OS>;
+    if (rbi == 1) return qgemv_grouped_kernel<FMT, 2, OS>;
+    if constexpr (OS) {
+        if (rbi == 2) return qgemv_grouped_kernel<FMT, 4, OS>;
+        if (rbi == 3) return qgemv_grouped_kernel<FMT, 8, OS>;
+    }
     return nullptr;
+}
+
+// the (format, T, tile) combinations of stream_supported: the ones that fit the
+// register budget without spilling
+template <int FMT, int T>
+DenseFn stream_entry(int rb) {
+    if constexpr (FMT != QG_FMT_BF16 || T <= 2) {
+        if (rb == 4) return qgemv_stream_kernel<FMT, T, 8>;
+    }
+    if constexpr ((FMT == QG_FMT_Q8_0 && T == 1) || (FMT == QG_FMT_Q4_0 && T <= 2)) {
+        if (rb == 8) return qgemv_stream_kernel<FMT, T, 16>;
+    }
+    return nullptr;
+}
+
+template <int FMT>
+DenseFn stream_for(int T, int rb) {
+    switch (T) {
+    case 1: return stream_entry<FMT, 1>(rb);
+    case 2: return stream_entry<FMT, 2>(rb);
+    case 3: return stream_entry<FMT, 3>(rb);
+    default: return stream_entry<FMT, 4>(rb);
+    }
 }
 
 }  // namespace
 
 int launch_dense(int fmt, int T, const Tile& tile, const DenseArgs& a, void* stream) {
     const int rbi = rb_index(tile.rows_per_batch);
-    DenseFn fn = fmt == QG_FMT_Q8_0 ? dense_for<QG_FMT_Q8_0>(T, rbi)
-               : fmt == QG_FMT_Q4_0 ? dense_for<QG_FMT_Q4_0>(T, rbi)
-                                    : dense_for<QG_FMT_BF16>(T, rbi);
+    DenseFn fn;
+    if (one_shot(tile, a.nslices))
+        fn = fmt == QG_FMT_Q8_0 ? dense_for<QG_FMT_Q8_0, true>(T, rbi)
+           : fmt == QG_FMT_Q4_0 ? dense_for<QG_FMT_Q4_0, true>(T, rbi)
+                                : dense_for<QG_FMT_BF16, true>(T, rbi);
+    else
+        fn = fmt == QG_FMT_Q8_0 ? dense_for<QG_FMT_Q8_0, false>(T, rbi)
+           : fmt == QG_FMT_Q4_0 ? dense_for<QG_FMT_Q4_0, false>(T, rbi)
+                                : dense_for<QG_FMT_BF16, false>(T, rbi);
     if (!fn) return (int)hipErrorInvalidValue;
     const int64_t nwg = (a.rows + tile.rows_per_wg - 1) / tile.rows_per_wg;
     hipLaunchKernelGGL(fn, dim3((unsigned)nwg), dim3(64 * tile.waves_per_wg), lds_bytes(tile, T), (hipStream_t)stream,
@@ -431,11 +832,28 @@ int launch_dense(int fmt, int T, const Tile& tile, const DenseArgs& a, void* str
     return (int)hipGetLastError();
 }
 
+int launch_stream(int fmt, int T, const Tile& tile, const DenseArgs& a, void* stream) {
+    DenseFn fn = fmt == QG_FMT_Q8_0 ? stream_for<QG_FMT_Q8_0>(T, tile.rows_per_batch)
+               : fmt == QG_FMT_Q4_0 ? stream_for<QG_FMT_Q4_0>(T, tile.rows_per_batch)
+                                    : stream_for<QG_FMT_BF16>(T, tile.rows_per_batch);
+    if (!fn) return (int)hipErrorInvalidValue;
+    const int64_t nwg = (a.rows + tile.rows_per_wg - 1) / tile.rows_per_wg;
+    hipLaunchKernelGGL(fn, dim3((unsigned)nwg), dim3(64 * tile.waves_per_wg),
+                       stream_lds_bytes(fmt, tile, T, a.nslices), (hipStream_t)stream, a);
+    return (int)hipGetLastError();
+}
+
 int launch_grouped(int fmt, const Tile& tile, const GroupedArgs& a, void* stream) {
     const int rbi = rb_index(tile.rows_per_batch);
-    GroupedFn fn = fmt == QG_FMT_Q8_0 ? grouped_for<QG_FMT_Q8_0>(rbi)
-                 : fmt == QG_FMT_Q4_0 ? grouped_for<QG_FMT_Q4_0>(rbi)
-                                      : grouped_for<QG_FMT_BF16>(rbi);
+    GroupedFn fn;
+    if (one_shot(tile, a.nslices))
+        fn = fmt == QG_FMT_Q8_0 ? grouped_for<QG_FMT_Q8_0, true>(rbi)
+           : fmt == QG_FMT_Q4_0 ? grouped_for<QG_FMT_Q4_0, true>(rbi)
+                                : grouped_for<QG_FMT_BF16, true>(rbi);
+    else
+        fn = fmt == QG_FMT_Q8_0 ? grouped_for<QG_FMT_Q8_0, false>(rbi)
+           : fmt == QG_FMT_Q4_0 ? grouped_for<QG_FMT_Q4_0, false>(rbi)
+                                : grouped_for<QG_FMT_BF16, false>(rbi);
     if (!fn) return (int)hipErrorInvalidValue;
     const int64_t nwg = (int64_t)a.T * a.topk * a.tiles_per_expert;
     hipLaunchKernelGGL(fn, dim3((unsigned)nwg), dim3(64 * tile.waves_per_wg), lds_bytes(tile, a.T), (hipStream_t)stream,

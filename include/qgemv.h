@@ -44,11 +44,13 @@
  *   - Accuracy: |y - exact| <= 1e-4 * sum_k |w_k * x_k| + 1e-6 per output
  *     (fp32 accumulation of exactly decoded weights).
  *
- * Environment: QGEMV_TILE="fmt:rb,nw,rw[;fmt:...]" overrides the tile for a
- * format (fmt = q8_0 | q4_0 | bf16): rb rows per lane group per batch (one of
- * 1, 2, 4, 8), nw waves per workgroup (1..16), rw rows per workgroup (a
- * multiple of 2*rb).  A malformed or out-of-set value makes every call of
- * that format return QG_EINVAL.
+ * Environment: QGEMV_TILE="fmt:rb,nw,rw[,k][;fmt:...]" overrides the tile for a
+ * format (fmt = q8_0 | q4_0 | bf16): rb rows per lane group per batch or tile
+ * (1, 2, 4, 8 or 16), nw waves per workgroup (1..12), rw rows per workgroup (a
+ * multiple of 2*rb), k the kernel kind: d (each lane loads its own bytes) or s
+ * (rows streamed through LDS; needs rows of a multiple of 16 bytes).  A
+ * malformed or out-of-set value makes every call of that format return
+ * QG_EINVAL.
  */
 #ifndef QGEMV_H
 #define QGEMV_H
@@ -71,7 +73,7 @@ typedef enum {
 typedef enum { QG_FMT_Q8_0 = 0, QG_FMT_Q4_0 = 1, QG_FMT_BF16 = 2 } qg_format;
 
 #define QG_MAX_T 4
-#define QG_TILE_FIELDS 6 /* lanes_per_row, rows_per_batch, waves_per_wg, k_slice, rows_per_wg, mfma */
+#define QG_TILE_FIELDS 7 /* lanes_per_row, rows_per_batch, waves_per_wg, k_slice, rows_per_wg, mfma, kind */
 
 /* Q8_0 weights: cols % 32 == 0; W holds rows * cols/32 * 34 bytes. */
 int qgemv_q8_0(int64_t rows, int64_t cols, int T, const void* W, const float* x, float* y, void* stream);
@@ -109,7 +111,8 @@ int qg_pack_q4_0(int64_t rows, int64_t cols, const uint16_t* d_bits, const uint8
 int qg_unpack_q4_0(int64_t rows, int64_t cols, const void* in, uint16_t* d_bits, uint8_t* codes);
 
 /* The tile a call with these arguments would use (after QGEMV_TILE):
- * out_tile = {lanes_per_row, rows_per_batch, waves_per_wg, k_slice, rows_per_wg, mfma}. */
+ * out_tile = {lanes_per_row, rows_per_batch, waves_per_wg, k_slice, rows_per_wg, mfma, kind}
+ * (kind 0: direct loads, 1: streamed through LDS). */
 int qg_query_tile(int fmt, int64_t rows, int64_t cols, int T, int out_tile[QG_TILE_FIELDS]);
 
 /* Static description of a status code (never NULL). */

@@ -126,7 +126,7 @@ def test_bf16_dyadic_bitwise(torch, orc):
 
 # --------------------------------------------------------- ragged and tiny
 TINY_ROWS = (1, 2, 3, 5, 17, 33, 67)
-TINY_COLS = tuple(32 * i for i in range(1, 10)) + (256, 544, 640, 1056)
+TINY_COLS = tuple(32 * i for i in range(1, 10)) + (256, 544, 640, 768, 1056, 1280, 4096, 6144)
 
 
 @pytest.mark.parametrize("fmt", [Q8, Q4])
@@ -148,7 +148,8 @@ def test_tiny_shapes_bf16(torch, orc):
             check_dense(torch, orc, BF, rows, cols, W, x, "tiny")
 
 
-@pytest.mark.parametrize("fmt,rows,cols", [(Q8, 64, 65536), (Q4, 48, 6656), (BF, 40, 7000), (Q8, 1000, 4608)])
+@pytest.mark.parametrize("fmt,rows,cols", [(Q8, 64, 65536), (Q4, 48, 6656), (BF, 40, 7000), (Q8, 1000, 4608),
+                                           (BF, 37, 6152)])
 def test_many_slices(torch, orc, fmt, rows, cols):
     """More k slices than waves per workgroup: waves loop over several slices."""
     rng = np.random.default_rng(cols)
@@ -194,6 +195,32 @@ def test_tile_override_keeps_bits(torch, monkeypatch):
         monkeypatch.setenv("QGEMV_TILE", tile)
         say(f"[tile] {tile}")
         assert np.array_equal(ops.gemv("q8_0", Wd, xd, c["rows"]).cpu().numpy(), base), tile
+
+
+@pytest.mark.parametrize("name", ["c2a_q8_0_10240x2560", "c2b_q8_0_2560x6144", "c3_q4_0_8192x2560",
+                                  "c3_bf16_8192x2560"])
+def test_direct_and_streamed_kernels_agree_bitwise(torch, monkeypatch, name):
+    """Both kernel kinds split k the same way, so their outputs must be identical."""
+    c = I.dense_case(name)
+    fmt = NAMES[c["fmt"]]
+    Wd = dev(torch, c["W"])
+    nw = min(12, -(-c["cols"] // 512))
+    for T in (1, 2, 3, 4):
+        xd = dev(torch, c["x"][:T])
+        outs = {}
+        for tile in (f"{fmt}:2,{nw},4,d", f"{fmt}:4,{nw},8,d", f"{fmt}:4,{nw},16,s", f"{fmt}:4,{nw},40,s",
+                     f"{fmt}:8,{nw},32,s"):
+            monkeypatch.setenv("QGEMV_TILE", tile)
+            st, t = _lib.qg_query_tile(c["fmt"], c["rows"], c["cols"], T)
+            if st != 0:
+                continue  # not in the compiled set for this T
+            say(f"[kinds] {name} T={T} tile={tile}")
+            outs[tile] = ops.gemv(fmt, Wd, xd, c["rows"]).cpu().numpy()
+        ref = next(iter(outs.values()))
+        for tile, y in outs.items():
+            assert np.array_equal(y, ref), (name, T, tile)
+        assert any(t.endswith(",d") for t in outs)
+        assert any(t.endswith(",s") for t in outs) or (fmt == "bf16" and T >= 3)  # no streamed bf16 at T>=3
 
 
 def test_tile_override_other_k_split(torch, orc, monkeypatch):
