@@ -31,6 +31,8 @@ sys.path.insert(0, ROOT)
 from block_quantized_token_amd import _lib, inputs as I, ops  # noqa: E402
 
 HBM_PEAK_GBS = 8000.0
+KERNEL_SRC = os.path.join(ROOT, "block_quantized_token_amd", "csrc", "qgemv_kernels.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "qgemv_q8_0_10240x2560_hbm_traffic.txt")
 METRIC = "effective weight GB/s (and % of HBM peak) at T=1..4, Q8_0 2560x10240"
 WORKLOAD = "c2a_q8_0_10240x2560"
 ALSO = "c2b_q8_0_2560x6144"
@@ -63,6 +65,85 @@ def time_calls(torch, fmt, ring, x_dev, rows, T, calls, stream, y_dev):
     return start, end
 
 
+def kernel_name(tile, T):
+    """Device symbol of the kernel a call with ``tile`` launches (Q8_0)."""
+    if tile["kind"] == 1 and tile["mfma"]:
+        return f"qgemv_mfma_q8_kernel<{T}>"
+    if tile["kind"] == 1:
+        return f"qgemv_stream_kernel<0, {T}, {2 * tile['rows_per_batch']}>"
+    one_shot = str(tile["rows_per_wg"] == 2 * tile["rows_per_batch"]).lower()
+    return f"qgemv_dense_kernel<0, {T}, {tile['rows_per_batch']}, {one_shot}>"
+
+
+def source_digest():
+    import hashlib
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def measured_traffic(kernel):
+    """HBM bytes per launch of ``kernel`` from the committed PMC summary, or None
+    when there is none or the kernel source changed since it was taken."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    fields, rows = {}, {}
+    for line in open(TRAFFIC_FILE):
+        line = line.strip()
+        if line.startswith("kernel_source_sha256:"):
+            fields["digest"] = line.split(":", 1)[1].strip()
+        elif line.startswith("| ") and "|" in line[2:]:
+            cells = [c.strip() for c in line.strip("|").split("|")]
+            if len(cells) >= 5 and cells[0] != "kernel" and not cells[0].startswith("-"):
+                rows[cells[0]] = cells
+    if fields.get("digest") != source_digest() or kernel not in rows:
+        return None
+    return int(float(rows[kernel][4]))
+
+
+def summarize_pmc(fetch_dir, write_dir, nbytes):
+    """Per-kernel HBM traffic from two rocprofv3 --pmc runs of this script
+    (FETCH_SIZE, then WRITE_SIZE; KiB per dispatch), each scaled by what the same
+    counter reads for the calibration copy (nbytes read, nbytes written)."""
+    import csv
+    import glob
+
+    def per_kernel(d, counter):
+        files = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
+        if not files:
+            sys.exit(f"no counter_collection.csv under {d}")
+        acc = {}
+        for f in files:
+            for r in csv.DictReader(open(f)):
+                if r["Counter_Name"] != counter:
+                    continue
+                name = r["Kernel_Name"].replace("void ", "").replace("qg::(anonymous namespace)::", "")
+                name = name.split("(")[0]
+                acc.setdefault(name, {}).setdefault(r["Dispatch_Id"], 0.0)
+                acc[name][r["Dispatch_Id"]] += float(r["Counter_Value"])
+        return {k: sorted(v.values())[len(v) // 2] for k, v in acc.items()}  # median over dispatches
+
+    fetch, write = per_kernel(fetch_dir, "FETCH_SIZE"), per_kernel(write_dir, "WRITE_SIZE")
+    cal = [k for k in fetch if "MulFunctor" in k]  # torch.mul(src, 1.0, out=dst): reads and writes nbytes
+    if not cal:
+        sys.exit("calibration copy kernel not found in the FETCH_SIZE run")
+    cal = cal[0]
+    f_scale = nbytes / (fetch[cal] * 1024.0)
+    w_scale = nbytes / (write[cal] * 1024.0)
+    print(f"kernel_source_sha256: {source_digest()}")
+    print(f"calibration: {cal} moves {nbytes} B each way; FETCH_SIZE reads {fetch[cal]:.1f} KiB "
+          f"(scale {f_scale:.4f}), WRITE_SIZE reads {write[cal]:.1f} KiB (scale {w_scale:.4f})")
+    print(f"algorithmic bytes per launch: {nbytes} weight bytes (+ x and y, under 0.3%)")
+    print()
+    print("| kernel | FETCH_SIZE KiB | WRITE_SIZE KiB | scaled read B | scaled read + write B | vs algorithmic |")
+    print("|---|---|---|---|---|---|")
+    for k in sorted(fetch):
+        if k == cal or not k.startswith("qgemv"):
+            continue
+        rb = fetch[k] * 1024.0 * f_scale
+        wb = write.get(k, 0.0) * 1024.0 * w_scale
+        print(f"| {k} | {fetch[k]:.1f} | {write.get(k, 0.0):.1f} | {rb:.0f} | {rb + wb:.0f} | {(rb + wb) / nbytes:.3f} |")
+
+
 def cpu_baseline(case, budget_s: float):
     """The oracle, untuned, on the host cores: whole steps (T = 1..4) of the same
     workload repeated until about ``budget_s`` seconds have passed."""
@@ -90,7 +171,16 @@ def main():
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="oracle time budget; 0 skips the CPU leg")
     ap.add_argument("--no-extra", action="store_true", help="skip the 2560x6144 detail timing")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="N",
+                    help="after the timed region, run N plain copies of the weight size (PMC calibration)")
+    ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="print the HBM traffic table from two rocprofv3 --pmc runs of this script and exit")
     args = ap.parse_args()
+
+    if args.summarize_pmc:
+        fmt, rows, cols, _ = I.CONFIGS[WORKLOAD]
+        summarize_pmc(*args.summarize_pmc, _lib.qg_packed_bytes(fmt, rows, cols))
+        return
 
     if args.gpus != 1:
         print(f"bench.py: --gpus {args.gpus} refused: this build measures one GPU only "
@@ -138,6 +228,16 @@ def main():
     dom = max(Ts, key=lambda T: ms[T])
     dom_us = ms[dom] * 1e3 / args.steps
     achieved = nbytes / dom_us / 1e3
+    dom_kernel = kernel_name(ops.query_tile("q8_0", rows, cols, dom), dom)
+    traffic = measured_traffic(dom_kernel)
+
+    if args.copy_calibration:
+        src = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda").fill_(1.0)
+        dst = torch.empty_like(src)
+        for _ in range(args.copy_calibration):
+            torch.mul(src, 1.0, out=dst)
+        torch.cuda.synchronize()
+        del src, dst
 
     detail = {}
     if not args.no_extra:
@@ -178,8 +278,8 @@ def main():
         "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBS, 1),
         "per_T": per_T,
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
-                     "kernel": f"qgemv_dense_kernel<Q8_0, T={dom}>", "us_per_launch": round(dom_us, 3),
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+                     "kernel": dom_kernel, "T": dom, "us_per_launch": round(dom_us, 3),
                      "bytes_per_launch": nbytes},
         "cpu_baseline": cpu,
         "detail": detail,

@@ -54,7 +54,6 @@ constexpr int64_t kMaxRows = int64_t(1) << 31;
 // depends on cols only, so a token's summation order -- and its bits -- are the
 // same at every T.  rows_per_batch and rows_per_wg may vary with T.
 Tile default_tile(int fmt, int64_t rows, int64_t cols, int T) {
-    (void)rows;
     Tile t{};
     t.lanes_per_row = kLanesPerRow;
     t.k_slice = kSlice;
@@ -68,19 +67,16 @@ Tile default_tile(int fmt, int64_t rows, int64_t cols, int T) {
     const bool os = nslices <= t.waves_per_wg;
     t.kind = 0;
     if (os && row_bytes(fmt, cols) % 16 == 0 && stream_supported(fmt, T, 4)) {
-        // streamed through LDS in 8-row tiles.  Large matrices: long workgroups
-        // (rows per workgroup grows with the matrix, shrinks with T); small
-        // ones: enough workgroups to give every CU work.
+        // streamed through LDS in 8-row tiles, one wave per k slice.  Rows per
+        // workgroup follow the matrix: about one workgroup per CU, in whole
+        // 16-row steps, between 16 (small matrices: fewer, fuller workgroups
+        // beat one per CU) and 256 (large ones: long pipelined workgroups).
         t.kind = 1;
         t.rows_per_batch = 4;
-        const int64_t per_cu = rows / 256;  // rows each CU gets with one workgroup per CU
-        int64_t rw = T == 1 ? 256 : T == 2 ? 128 : 80;
-        if (per_cu < rw) rw = per_cu < 8 ? 8 : per_cu / 8 * 8;
-        // two row groups per slice when a workgroup would otherwise hold few waves
-        if (2 * nslices <= kMaxWaves && rows <= 65536) t.waves_per_wg = (int)(2 * nslices);
+        int64_t rw = (rows / 256 + 15) / 16 * 16;
+        rw = rw < 16 ? 16 : rw > 256 ? 256 : rw;
         t.rows_per_wg = (int)rw;
         if (stream_lds_bytes(fmt, t, T, (int)nslices) <= kMaxLds) return t;
-        t.waves_per_wg = (int)nslices;
         t.rows_per_wg = 16;
         if (stream_lds_bytes(fmt, t, T, (int)nslices) <= kMaxLds) return t;
         t.kind = 0;
@@ -121,8 +117,8 @@ int tile_override(int fmt, Tile* t, std::string* why) {
         int rb = 0, nw = 0, rw = 0;
         char kind = 0, tail = 0;
         const int got = sscanf(item.c_str() + colon + 1, "%d,%d,%d,%c%c", &rb, &nw, &rw, &kind, &tail);
-        if (!(got == 3 || (got == 4 && (kind == 'd' || kind == 's')))) {
-            *why = "QGEMV_TILE item '" + item + "' is not fmt:rb,nw,rw[,d|s]";
+        if (!(got == 3 || (got == 4 && (kind == 'd' || kind == 's' || kind == 'm')))) {
+            *why = "QGEMV_TILE item '" + item + "' is not fmt:rb,nw,rw[,d|s|m]";
             return -1;
         }
         if (!valid_rb(rb) || nw < 1 || nw > kMaxWaves || rw < 2 * rb || rw % (2 * rb) || rw > (1 << 20)) {
@@ -133,7 +129,8 @@ int tile_override(int fmt, Tile* t, std::string* why) {
             t->rows_per_batch = rb;
             t->waves_per_wg = nw;
             t->rows_per_wg = rw;
-            t->kind = got == 4 ? (kind == 's') : -1;  // -1: choose below
+            t->kind = got == 4 ? (kind != 'd') : -1;  // -1: choose below
+            t->mfma = got == 4 && kind == 'm';
             return 1;
         }
     }
@@ -155,8 +152,9 @@ int pick_tile(int fmt, int64_t rows, int64_t cols, int T, Tile* t) {
         if (!stream_shape)
             return fail(QG_EINVAL, "streamed tile needs rows of a multiple of 16 bytes and waves_per_wg a multiple of "
                                    "the %lld k slices", (long long)nslices);
-        if (!stream_supported(fmt, T, t->rows_per_batch))
-            return fail(QG_EINVAL, "streamed rows_per_batch %d is not compiled for T=%d", t->rows_per_batch, T);
+        if (t->mfma ? !mfma_supported(fmt, t->rows_per_batch) : !stream_supported(fmt, T, t->rows_per_batch))
+            return fail(QG_EINVAL, "streamed%s rows_per_batch %d is not compiled for this format and T=%d",
+                        t->mfma ? " matrix-core" : "", t->rows_per_batch, T);
         if (stream_lds_bytes(fmt, *t, T, (int)nslices) > kMaxLds)
             return fail(QG_EINVAL, "tile needs %zu B of LDS (rows_per_wg %d too large)",
                         stream_lds_bytes(fmt, *t, T, (int)nslices), t->rows_per_wg);
@@ -253,6 +251,7 @@ int qgemv_grouped_experts(int fmt, int64_t n_experts, int64_t rows, int64_t cols
     if ((st = pick_tile(fmt, rows, cols, QG_MAX_T, &tile))) return st;  // one kernel for 1..4 tokens per expert
     if (tile.kind != 0) {  // the grouped kernel runs the direct path: one wave per slice
         tile.kind = 0;
+        tile.mfma = 0;
         const int64_t nsl = (cols + kSlice - 1) / kSlice;
         if (tile.waves_per_wg > nsl) tile.waves_per_wg = (int)nsl;
         tile.rows_per_wg = 2 * tile.rows_per_batch;

@@ -16,7 +16,7 @@ struct Tile {
     int waves_per_wg;    // NW: waves per workgroup; wave w takes k slices w, w+NW, ...
     int k_slice;         // 512 (fixed by the kernels)
     int rows_per_wg;     // RW: rows per workgroup (multiple of 2*RB)
-    int mfma;            // 0: VALU path
+    int mfma;            // 1: streamed tiles contracted on the matrix cores (kind 1 only)
     int kind;            // 0: direct (lanes load their own bytes); 1: streamed through LDS
 };
 
@@ -34,7 +34,8 @@ inline size_t lds_bytes(const Tile& t, int T) {
     return nbatch * t.waves_per_wg * 2 * t.rows_per_batch * pad_tokens(T) * 4 + nbatch * 4;
 }
 // (a workgroup of a single batch uses only the first nw * 2 * N floats)
-constexpr size_t kMaxLds = 64 * 1024;
+// gfx950 gives one workgroup up to the CU's whole 160 KB of LDS.
+constexpr size_t kMaxLds = 160 * 1024;
 
 inline bool valid_rb(int rb) { return rb == 1 || rb == 2 || rb == 4 || rb == 8 || rb == 16; }
 
@@ -65,6 +66,9 @@ inline bool stream_supported(int fmt, int T, int rb) {
     if (rb == 8) return (fmt == QG_FMT_Q8_0 && T == 1) || (fmt == QG_FMT_Q4_0 && T <= 2);
     return false;
 }
+
+// Matrix-core streamed kernel: 16-row tiles (rb 8), Q8_0, any T.
+inline bool mfma_supported(int fmt, int rb) { return fmt == QG_FMT_Q8_0 && rb == 8; }
 
 inline bool tile_supported(int fmt, int T, int rb, bool oneshot) {
     if (!valid_rb(rb) || rb * pad_tokens(T) > 32) return false;

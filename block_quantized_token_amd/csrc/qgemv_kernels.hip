@@ -358,7 +358,7 @@ __device__ __forceinline__ void gemv_rows(const uint8_t* __restrict__ W, int64_t
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: keeps buffer descriptors scalar
     const int nw = blockDim.x >> 6;
     const int g = lane >> 5;   // which of the two rows of a step
     const int li = lane & 31;  // lane within the row
@@ -597,7 +597,7 @@ __device__ __forceinline__ void stream_rows(const uint8_t* __restrict__ W, int64
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: keeps buffer descriptors scalar
     const int nw = blockDim.x >> 6;
     const int g = lane >> 5;
     const int li = lane & 31;
@@ -654,6 +654,166 @@ __device__ __forceinline__ void stream_rows(const uint8_t* __restrict__ W, int64
     }
 }
 
+// ------------------------------------------------------ matrix-core variant
+// The same streamed tiles (16 rows), contracted on the matrix cores with
+// v_mfma_f32_16x16x32_bf16: D[16 x 16] = A[16 x 32] . B[32 x 16] per block.
+//   A: activations.  Row m = 4p + t holds piece p (< 3) of token t (< 4); every
+//      fp32 x is split exactly into three bf16 pieces, x = hi + mid + lo (each
+//      residual is exact in fp32 and fits 8 significant bits by the third).
+//   B: one block of 16 weight rows; column n = weight row, the 32 codes as bf16
+//      (exact: |code| <= 128).
+//   Products are exact in fp32; per block, lane l gets D rows 4(l/16)..+3 of
+//   column l%16 -- one weight row, so one scale: acc += d * D.  At the end the
+//   three pieces of a token are added in a fixed order.  A token's outputs never
+//   depend on the other tokens' rows of A, so its bits do not depend on T.
+typedef __bf16 BF8 __attribute__((ext_vector_type(8)));
+typedef float F4 __attribute__((ext_vector_type(4)));
+
+// 8 int8 codes (two dwords) -> 8 bf16 (the high half of each exact fp32)
+__device__ __forceinline__ V4 codes_to_bf16(uint32_t c0, uint32_t c1) {
+    V4 r;
+    const uint32_t w[2] = {c0, c1};
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const uint32_t f0 = __builtin_bit_cast(uint32_t, (float)(int32_t)(int8_t)(w[h]));
+        const uint32_t f1 = __builtin_bit_cast(uint32_t, (float)(int32_t)(int8_t)(w[h] >> 8));
+        const uint32_t f2 = __builtin_bit_cast(uint32_t, (float)(int32_t)(int8_t)(w[h] >> 16));
+        const uint32_t f3 = __builtin_bit_cast(uint32_t, (float)(int32_t)(int8_t)(w[h] >> 24));
+        r[2 * h] = __builtin_amdgcn_perm(f1, f0, 0x07060302u);      // (hi16(f1) << 16) | hi16(f0)
+        r[2 * h + 1] = __builtin_amdgcn_perm(f3, f2, 0x07060302u);
+    }
+    return r;
+}
+
+// piece p of x as bf16 bits: p = 0 -> RNE(x); 1 -> RNE(x - hi); 2 -> the rest
+__device__ __forceinline__ uint32_t x_piece(float x, int p) {
+    const __bf16 hi = (__bf16)x;
+    const float r1 = x - (float)hi;
+    const __bf16 mid = (__bf16)r1;
+    const __bf16 lo = (__bf16)(r1 - (float)mid);
+    const __bf16 v = p == 0 ? hi : p == 1 ? mid : lo;
+    return (uint32_t)__builtin_bit_cast(uint16_t, v);
+}
+
+// One 16-row tile of one k slice: registers -> LDS, the next-but-one tile into R,
+// then one MFMA per block; the three pieces of each token are added at the end.
+template <int NT>
+__device__ __forceinline__ void mfma_tile_q8(const uint8_t* __restrict__ W, int64_t row_bytes, int64_t row_begin,
+                                             int64_t row_end, int ntiles, int t, int ahead,
+                                             const int (&off)[StreamShape<QG_FMT_Q8_0, 16>::kLoads],
+                                             V4 (&R)[StreamShape<QG_FMT_Q8_0, 16>::kLoads], uint8_t* buf, float* part,
+                                             const V4 (&afrag)[16], int lane, int n, int g, int s, int nsl, int nblk) {
+    using S = StreamShape<QG_FMT_Q8_0, 16>;
+    constexpr int L = S::kLoads;
+    constexpr int TP = pad_pow2(NT);
+#pragma unroll
+    for (int k = 0; k < L; ++k) *reinterpret_cast<V4*>(buf + (64 * k + lane) * 16) = R[k];
+    stream_issue<QG_FMT_Q8_0, 16>(W, row_bytes, row_begin, row_end, ntiles, t + ahead, off, R);
+    const uint8_t* rowp = buf + n * (S::kChunks * 16);
+    F4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+    // Blocks past a short last slice read stale (finite) codes against zero A
+    // fragments; their scale is forced to 0 so a stale Inf/NaN cannot leak in.
+#pragma unroll
+    for (int b = 0; b < 16; ++b) {
+        const uint8_t* blk = rowp + 34 * b;
+        const U2u q = *reinterpret_cast<const U2u*>(blk + 2 + 8 * g);
+        const float dv = half_bits_to_float(*reinterpret_cast<const uint16_t*>(blk));
+        const float d = b < nblk ? dv : 0.0f;
+        const V4 bq = codes_to_bf16(q.v[0], q.v[1]);
+        const F4 z = {0.0f, 0.0f, 0.0f, 0.0f};
+        const F4 dd = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(BF8, afrag[b]),
+                                                               __builtin_bit_cast(BF8, bq), z, 0, 0, 0);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[j] = __builtin_fmaf(d, dd[j], acc[j]);
+    }
+    // pieces of token j sit in lanes n (hi), n + 16 (mid), n + 32 (lo): added in that order
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const float mid = __shfl_down(acc[j], 16, 64);
+        const float lo = __shfl_down(acc[j], 32, 64);
+        acc[j] = (acc[j] + mid) + lo;
+    }
+    if (g == 0) {
+#pragma unroll
+        for (int j = 0; j < NT; ++j) part[(((size_t)t * nsl + s) * 16 + n) * TP + j] = acc[j];
+    }
+}
+
+template <int NT, class Out>
+__device__ __forceinline__ void mfma_rows_q8(const uint8_t* __restrict__ W, int64_t row_bytes, int cols, int nsl,
+                                             const float* __restrict__ x, const int64_t (&xoff)[NT], int64_t row_begin,
+                                             int64_t row_end, Out out) {
+    constexpr int FMT = QG_FMT_Q8_0;
+    constexpr int ST = 16;
+    using S = StreamShape<FMT, ST>;
+    constexpr int L = S::kLoads;
+    constexpr int TP = pad_pow2(NT);
+    extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: keeps buffer descriptors scalar
+    const int nw = blockDim.x >> 6;
+    const int n = lane & 15;   // B / D column: weight row in the tile
+    const int g = lane >> 4;   // k group of A / B; D row group
+    const int s = wave % nsl;
+    const int rg = wave / nsl;
+    const int RG = nw / nsl;
+    const int k0 = s * kSlice;
+    const int ntiles = (int)((row_end - row_begin + ST - 1) / ST);
+    uint8_t* buf = smem + wave * S::kBufBytes;
+    float* part = reinterpret_cast<float*>(smem + nw * S::kBufBytes);  // [tiles][nsl][16][TP]
+
+    const int64_t rest = row_bytes - (int64_t)s * S::kChunks * 16;
+    const int cs = rest / 16 < S::kChunks ? (int)(rest / 16) : S::kChunks;
+    const int nblk = (int)(rest / 34) < 16 ? (int)(rest / 34) : 16;  // blocks of this slice
+    int off[L];
+#pragma unroll
+    for (int k = 0; k < L; ++k) {
+        const int j = 64 * k + lane;
+        const int r = j / S::kChunks, c = j % S::kChunks;
+        off[k] = (r < ST && c < cs) ? (int)(r * row_bytes) + s * S::kChunks * 16 + 16 * c : kNoLoad;
+    }
+
+    // A fragments of the slice's 16 blocks (x is small and shared: its loads hit in L2)
+    const int am = lane & 15, ap = am >> 2, at = am & 3;
+    const bool arow = ap < 3 && at < NT;
+    int64_t xo = 0;
+#pragma unroll
+    for (int t = 0; t < NT; ++t) xo = at == t ? xoff[t] : xo;
+    V4 afrag[16];
+#pragma unroll
+    for (int b = 0; b < 16; ++b) {
+        const int kb = k0 + 32 * b + 8 * g;
+        const bool ok = arow && kb < cols;
+        const float4* px = reinterpret_cast<const float4*>(x + (ok ? xo + kb : 0));
+        const float4 u = px[0], v = px[1];
+        afrag[b][0] = ok ? x_piece(u.x, ap) | (x_piece(u.y, ap) << 16) : 0u;
+        afrag[b][1] = ok ? x_piece(u.z, ap) | (x_piece(u.w, ap) << 16) : 0u;
+        afrag[b][2] = ok ? x_piece(v.x, ap) | (x_piece(v.y, ap) << 16) : 0u;
+        afrag[b][3] = ok ? x_piece(v.z, ap) | (x_piece(v.w, ap) << 16) : 0u;
+        if (b == 7) __builtin_amdgcn_sched_barrier(0);  // two rounds of x loads: bounds live registers
+    }
+
+    // one tile in flight per wave (the A fragments hold the registers a second
+    // would need; a CU's waves together still keep enough bytes in flight)
+    V4 ra[L];
+    stream_issue<FMT, ST>(W, row_bytes, row_begin, row_end, ntiles, rg, off, ra);
+    for (int t = rg; t < ntiles; t += RG)
+        mfma_tile_q8<NT>(W, row_bytes, row_begin, row_end, ntiles, t, RG, off, ra, buf, part, afrag, lane, n, g, s, nsl,
+                         nblk);
+    __syncthreads();
+    const int nrows = (int)(row_end - row_begin);
+    for (int o = tid; o < nrows * NT; o += blockDim.x) {
+        const int rr = o / NT, t = o % NT;
+        const int tl = rr / ST, nn = rr % ST;
+        const float* base = part + (((size_t)tl * nsl) * 16 + nn) * TP + t;
+        float sum = base[0];
+        for (int w = 1; w < nsl; ++w) sum = sum + base[(size_t)w * 16 * TP];
+        out(t, row_begin + rr, sum);
+    }
+}
+
 // ---------------------------------------------------------------- kernels
 template <int FMT, int T, int RB, bool ONE_SHOT>
 __global__ void __launch_bounds__(64 * kMaxWaves) qgemv_dense_kernel(DenseArgs a) {
@@ -679,6 +839,19 @@ __global__ void __launch_bounds__(64 * kMaxWaves) qgemv_stream_kernel(DenseArgs 
     const int64_t rows = a.rows;
     stream_rows<FMT, T, ST>(a.W, a.row_bytes, a.cols, a.nslices, a.x, xoff, row_begin, row_end,
                             [=](int t, int64_t row, float v) { y[t * rows + row] = v; });
+}
+
+template <int T>
+__global__ void __launch_bounds__(64 * kMaxWaves) qgemv_mfma_q8_kernel(DenseArgs a) {
+    const int64_t row_begin = (int64_t)blockIdx.x * a.rows_per_wg;
+    const int64_t row_end = row_begin + a.rows_per_wg < a.rows ? row_begin + a.rows_per_wg : a.rows;
+    int64_t xoff[T];
+#pragma unroll
+    for (int t = 0; t < T; ++t) xoff[t] = (int64_t)t * a.cols;
+    float* __restrict__ y = a.y;
+    const int64_t rows = a.rows;
+    mfma_rows_q8<T>(a.W, a.row_bytes, a.cols, a.nslices, a.x, xoff, row_begin, row_end,
+                    [=](int t, int64_t row, float v) { y[t * rows + row] = v; });
 }
 
 // Grouped experts: workgroup (slot, tile) with slot = (t, j).  The workgroup of
@@ -812,6 +985,19 @@ DenseFn stream_for(int T, int rb) {
     }
 }
 
+template <int FMT>
+DenseFn mfma_for(int T) {
+    if constexpr (FMT == QG_FMT_Q8_0) {
+        switch (T) {
+        case 1: return qgemv_mfma_q8_kernel<1>;
+        case 2: return qgemv_mfma_q8_kernel<2>;
+        case 3: return qgemv_mfma_q8_kernel<3>;
+        default: return qgemv_mfma_q8_kernel<4>;
+        }
+    }
+    return nullptr;
+}
+
 }  // namespace
 
 int launch_dense(int fmt, int T, const Tile& tile, const DenseArgs& a, void* stream) {
@@ -833,9 +1019,16 @@ int launch_dense(int fmt, int T, const Tile& tile, const DenseArgs& a, void* str
 }
 
 int launch_stream(int fmt, int T, const Tile& tile, const DenseArgs& a, void* stream) {
-    DenseFn fn = fmt == QG_FMT_Q8_0 ? stream_for<QG_FMT_Q8_0>(T, tile.rows_per_batch)
-               : fmt == QG_FMT_Q4_0 ? stream_for<QG_FMT_Q4_0>(T, tile.rows_per_batch)
-                                    : stream_for<QG_FMT_BF16>(T, tile.rows_per_batch);
+    DenseFn fn;
+    if (tile.mfma)
+        fn = tile.rows_per_batch != 8 ? nullptr
+           : fmt == QG_FMT_Q8_0 ? mfma_for<QG_FMT_Q8_0>(T)
+           : fmt == QG_FMT_Q4_0 ? mfma_for<QG_FMT_Q4_0>(T)
+                                : mfma_for<QG_FMT_BF16>(T);
+    else
+        fn = fmt == QG_FMT_Q8_0 ? stream_for<QG_FMT_Q8_0>(T, tile.rows_per_batch)
+           : fmt == QG_FMT_Q4_0 ? stream_for<QG_FMT_Q4_0>(T, tile.rows_per_batch)
+                                : stream_for<QG_FMT_BF16>(T, tile.rows_per_batch);
     if (!fn) return (int)hipErrorInvalidValue;
     const int64_t nwg = (a.rows + tile.rows_per_wg - 1) / tile.rows_per_wg;
     hipLaunchKernelGGL(fn, dim3((unsigned)nwg), dim3(64 * tile.waves_per_wg),

@@ -47,10 +47,10 @@
  * Environment: QGEMV_TILE="fmt:rb,nw,rw[,k][;fmt:...]" overrides the tile for a
  * format (fmt = q8_0 | q4_0 | bf16): rb rows per lane group per batch or tile
  * (1, 2, 4, 8 or 16), nw waves per workgroup (1..12), rw rows per workgroup (a
- * multiple of 2*rb), k the kernel kind: d (each lane loads its own bytes) or s
- * (rows streamed through LDS; needs rows of a multiple of 16 bytes).  A
- * malformed or out-of-set value makes every call of that format return
- * QG_EINVAL.
+ * multiple of 2*rb), k the kernel kind: d (each lane loads its own bytes), s
+ * (rows streamed through LDS; needs rows of a multiple of 16 bytes) or m (as s,
+ * contracted on the matrix cores; Q8_0 with rb 8 only).  A malformed or
+ * out-of-set value makes every call of that format return QG_EINVAL.
  */
 #ifndef QGEMV_H
 #define QGEMV_H
@@ -112,7 +112,7 @@ int qg_unpack_q4_0(int64_t rows, int64_t cols, const void* in, uint16_t* d_bits,
 
 /* The tile a call with these arguments would use (after QGEMV_TILE):
  * out_tile = {lanes_per_row, rows_per_batch, waves_per_wg, k_slice, rows_per_wg, mfma, kind}
- * (kind 0: direct loads, 1: streamed through LDS). */
+ * (kind 0: direct loads, 1: streamed through LDS; mfma 1: matrix-core contraction). */
 int qg_query_tile(int fmt, int64_t rows, int64_t cols, int T, int out_tile[QG_TILE_FIELDS]);
 
 /* Static description of a status code (never NULL). */

@@ -145,10 +145,17 @@ def test_tile_query_and_override(lib, monkeypatch):
     monkeypatch.delenv("QGEMV_TILE", raising=False)
     t = ops.query_tile("q8_0", 10240, 2560, 1)
     assert t["lanes_per_row"] == 32 and t["k_slice"] == 512 and t["waves_per_wg"] % 5 == 0  # 5 k slices
-    # the k split must not depend on T (bit-identical tokens across T)
+    # the k split must not depend on T (bit-identical tokens across T): waves
+    # that each reduce one slice (streamed kinds; direct with waves >= slices)
+    # or the same number of slice-looping waves
+    def k_split(t, cols):
+        nsl = -(-cols // 512)
+        return nsl if t["kind"] == 1 else min(t["waves_per_wg"], nsl)
     for fmt in ("q8_0", "q4_0", "bf16"):
         for rows, cols in ((10240, 2560), (2560, 6144), (248320, 5120), (8192, 2560), (7, 65536)):
-            assert len({ops.query_tile(fmt, rows, cols, T)["waves_per_wg"] for T in (1, 2, 3, 4)}) == 1
+            tiles = [ops.query_tile(fmt, rows, cols, T) for T in (1, 2, 3, 4)]
+            assert len({k_split(t, cols) for t in tiles}) == 1, (fmt, rows, cols, tiles)
+            assert len({t["mfma"] for t in tiles}) == 1, (fmt, rows, cols, tiles)
     monkeypatch.setenv("QGEMV_TILE", "q8_0:2,5,8")
     t = ops.query_tile("q8_0", 10240, 2560, 4)
     assert (t["rows_per_batch"], t["waves_per_wg"], t["rows_per_wg"]) == (2, 5, 8)

@@ -231,6 +231,71 @@ def test_tile_override_other_k_split(torch, orc, monkeypatch):
     assert_parity(y, ref, bound, "c2b nw=4")
 
 
+# ------------------------------------------------- matrix-core (MFMA) kernel
+def mfma_tile(cols, rw=32, rg=1):
+    nsl = -(-cols // 512)
+    return f"q8_0:8,{nsl * rg},{rw},m"
+
+
+@pytest.mark.parametrize("name,rw,rg", [("c1_q8_0_2560x2560", 16, 1), ("c2a_q8_0_10240x2560", 32, 2),
+                                        ("c2b_q8_0_2560x6144", 16, 1), ("c2a_q8_0_10240x2560", 48, 1)])
+def test_mfma_config_full(torch, orc, monkeypatch, name, rw, rg):
+    """The matrix-core kernel on the workloads: parity, and a token's bits do not depend on T."""
+    c = I.dense_case(name)
+    monkeypatch.setenv("QGEMV_TILE", mfma_tile(c["cols"], rw, rg))
+    st, t = _lib.qg_query_tile(c["fmt"], c["rows"], c["cols"], 4)
+    assert st == 0 and t[5] == 1 and t[6] == 1, (st, t)
+    check_dense(torch, orc, c["fmt"], c["rows"], c["cols"], c["W"], c["x"], f"mfma {name}")
+
+
+def test_mfma_tiny_shapes(torch, orc, monkeypatch):
+    """Ragged rows (partial 16-row tiles) and short last k slices (streamed rows
+    must be a multiple of 16 bytes: cols a multiple of 256)."""
+    for rows in TINY_ROWS:
+        for cols in (256, 512, 768, 1280, 1792, 2304, 4096, 6144):
+            monkeypatch.setenv("QGEMV_TILE", mfma_tile(cols, 16 if rows < 40 else 48))
+            rng = np.random.default_rng(rows * 1000 + cols)
+            W = I.weights(rng, Q8, rows, cols)
+            x = I.activations(rng, cols)
+            check_dense(torch, orc, Q8, rows, cols, W, x, "mfma tiny")
+
+
+def test_mfma_dyadic_bitwise(torch, orc, monkeypatch):
+    """Dyadic x splits into one exact bf16 piece and every partial sum is exact: bitwise."""
+    rng = np.random.default_rng(99)
+    rows, cols = 1000, 2816
+    W = dyadic_weights(rng, Q8, rows, cols)
+    x = (rng.integers(-4, 5, (4, cols)) / 4.0).astype(np.float32)
+    monkeypatch.setenv("QGEMV_TILE", mfma_tile(cols, 32))
+    y = gpu_gemv(torch, Q8, dev(torch, W), x, rows)
+    ref, _ = orc.gemv(Q8, rows, cols, W, x)
+    assert np.array_equal(y.astype(np.float64), ref)
+
+
+def test_mfma_lm_head_sampled(torch, orc, monkeypatch):
+    name = "c4_q8_0_248320x5120"
+    c = I.dense_case(name)
+    rows = c["rows"]
+    monkeypatch.setenv("QGEMV_TILE", mfma_tile(c["cols"], 192))
+    rng = np.random.default_rng(321)
+    sel = np.unique(np.concatenate([rng.choice(rows, 2000, replace=False), [0, 15, 16, rows - 17, rows - 1]]))
+    check_dense(torch, orc, c["fmt"], rows, c["cols"], c["W"], c["x"], f"mfma {name}", sel=sel)
+
+
+def test_mfma_x_pieces_full_range(torch, orc, monkeypatch):
+    """x with full 24-bit significands over a wide exponent range (the kernel
+    splits each x into three bf16 pieces)."""
+    rng = np.random.default_rng(5)
+    rows, cols = 96, 1024
+    W = I.weights(rng, Q8, rows, cols)
+    mant = rng.integers(1 << 23, 1 << 24, (4, cols)).astype(np.float64)
+    x = (mant * 2.0 ** rng.integers(-40, -10, (4, cols)) * rng.choice([-1, 1], (4, cols))).astype(np.float32)
+    monkeypatch.setenv("QGEMV_TILE", mfma_tile(cols, 32))
+    y = gpu_gemv(torch, Q8, dev(torch, W), x, rows)
+    ref, bound = orc.gemv(Q8, rows, cols, W, x)
+    assert_parity(y, ref, bound, "mfma x pieces")
+
+
 # ---------------------------------------------------------- grouped experts
 def grouped_check(torch, orc, fmt, n_experts, rows, cols, ids, W, x, what):
     say(f"[{what}] fmt={NAMES[fmt]} experts={n_experts} rows={rows} cols={cols} ids={ids.tolist()}")
