@@ -14,7 +14,7 @@ LIB_PATH = os.path.join(HERE, "libqgemv.so")
 QG_OK, QG_EINVAL, QG_EALIGN, QG_EUNSUPPORTED, QG_EHIP = 0, 1, 2, 3, 4
 QG_FMT_Q8_0, QG_FMT_Q4_0, QG_FMT_BF16 = 0, 1, 2
 QG_MAX_T = 4
-QG_TILE_FIELDS = 7
+QG_TILE_FIELDS = 8
 
 EXPORTS = (
     "qgemv_q8_0", "qgemv_q4_0", "qgemv_bf16", "qgemv_grouped_experts", "qg_packed_bytes",

@@ -49,16 +49,67 @@ int64_t row_bytes(int fmt, int64_t cols) {
 constexpr int64_t kMaxCols = int64_t(1) << 24;
 constexpr int64_t kMaxRows = int64_t(1) << 31;
 
+// "rb,nw,rw[,k]" with k = d, s, m, l<depth> or L<depth>.  Returns false (and
+// the reason) when malformed or outside the compiled set.
+bool parse_tile_spec(const std::string& spec, Tile* t, std::string* why) {
+    int rb = 0, nw = 0, rw = 0, depth = 0;
+    char kind = 0, tail = 0;
+    int got = sscanf(spec.c_str(), "%d,%d,%d,%c%c", &rb, &nw, &rw, &kind, &tail);
+    if (got == 5 && (kind == 'l' || kind == 'L')) {  // l<depth> or L<depth>
+        char tail2 = 0;
+        const char* f = kind == 'l' ? "%d,%d,%d,l%d%c" : "%d,%d,%d,L%d%c";
+        got = sscanf(spec.c_str(), f, &rb, &nw, &rw, &depth, &tail2) == 4 ? 4 : -1;
+    }
+    const bool dma = kind == 'l' || kind == 'L';
+    if (!(got == 3 || (got == 4 && (kind == 'd' || kind == 's' || kind == 'm' || (dma && depth > 0))))) {
+        *why = "tile '" + spec + "' is not rb,nw,rw[,d|s|m|l<depth>|L<depth>]";
+        return false;
+    }
+    if (!valid_rb(rb) || nw < 1 || nw > kMaxWaves || rw < 2 * rb || rw % (2 * rb) || rw > (1 << 20)) {
+        *why = "tile '" + spec + "' is outside the compiled set (rb in {1,2,4,8,16}, nw in 1..12, rw a multiple of 2*rb)";
+        return false;
+    }
+    t->rows_per_batch = rb;
+    t->waves_per_wg = nw;
+    t->rows_per_wg = rw;
+    t->kind = got == 4 ? (kind == 'd' ? 0 : kind == 'l' ? 2 : kind == 'L' ? 3 : 1) : -1;  // -1: choose later
+    t->mfma = got == 4 && kind == 'm';
+    t->depth = got == 4 && dma ? depth : 0;
+    return true;
+}
+
 // ------------------------------------------------------------ tile table
-// Defaults keyed by (format, rows, cols, T).  The k split (waves per workgroup)
-// depends on cols only, so a token's summation order -- and its bits -- are the
-// same at every T.  rows_per_batch and rows_per_wg may vary with T.
+// Defaults keyed by (format, rows, cols, T): measured winners for the shapes
+// the pages time, then a rule for every other shape.  Every default gives each
+// k slice to one wave and sums the slices in slice order, so a token's
+// summation order -- and its bits -- are the same at every T.
+struct TuneEntry {
+    int fmt;
+    int64_t rows, cols;
+    int T;  // 0: every T
+    const char* tile;
+};
+// MI355X, µs per call at T = 1..4 from sweeps over (kind, rows per workgroup,
+// ring depth) where the rule's pick loses by more than a few percent.
+const TuneEntry kTuned[] = {
+    {QG_FMT_Q8_0, 2560, 6144, 0, "4,12,16,s"},     // register-streamed beats DMA at 12 slices
+    {QG_FMT_Q8_0, 248320, 5120, 1, "4,10,64,l2"},  // LM head, one token
+    {QG_FMT_Q4_0, 8192, 2560, 1, "4,5,8,d"},       // direct: 6.5 vs 7.8 µs
+    {QG_FMT_Q4_0, 8192, 2560, 4, "4,10,32,s"},     // two row groups per slice: 9.8 vs 11.3 µs
+};
+
 Tile default_tile(int fmt, int64_t rows, int64_t cols, int T) {
     Tile t{};
     t.lanes_per_row = kLanesPerRow;
     t.k_slice = kSlice;
     t.mfma = 0;
+    t.depth = 0;
     const int64_t nslices = (cols + kSlice - 1) / kSlice;
+    for (const TuneEntry& e : kTuned) {
+        std::string why;
+        if (e.fmt == fmt && e.rows == rows && e.cols == cols && (e.T == 0 || e.T == T) && parse_tile_spec(e.tile, &t, &why))
+            return t;
+    }
     // fewest waves that cover the slices in equal rounds
     const int64_t rounds = (nslices + kMaxWaves - 1) / kMaxWaves;
     t.waves_per_wg = (int)((nslices + rounds - 1) / rounds);
@@ -66,16 +117,33 @@ Tile default_tile(int fmt, int64_t rows, int64_t cols, int T) {
     // wave has one slice; otherwise the pipelined kernel with its largest batch
     const bool os = nslices <= t.waves_per_wg;
     t.kind = 0;
-    if (os && row_bytes(fmt, cols) % 16 == 0 && stream_supported(fmt, T, 4)) {
-        // streamed through LDS in 8-row tiles, one wave per k slice.  Rows per
-        // workgroup follow the matrix: about one workgroup per CU, in whole
-        // 16-row steps, between 16 (small matrices: fewer, fuller workgroups
-        // beat one per CU) and 256 (large ones: long pipelined workgroups).
+    const bool rows16 = row_bytes(fmt, cols) % 16 == 0;
+    // rows per workgroup follow the matrix: about one workgroup per CU, in whole
+    // 8-row tiles, between 16 (small matrices: fewer, fuller workgroups beat one
+    // per CU) and 256 (large ones: long pipelined workgroups)
+    int64_t rw = (rows / 256 + 7) / 8 * 8;
+    rw = rw < 16 ? 16 : rw > 256 ? 256 : rw;
+    if (os && rows16) {
+        // streamed by LDS-DMA loads in 8-row tiles, one wave per k slice; the
+        // ring is the smallest that leaves x its slots plus one tile (deeper
+        // rings measured slower: they cost occupancy and buy nothing)
+        t.kind = 2;
+        t.rows_per_batch = 4;
+        t.rows_per_wg = (int)rw;
+        const int x_slots = dma_x_slots(fmt, T);
+        for (int d : {2, 3, 4, 6}) {
+            t.depth = d;
+            if (d > x_slots) break;
+        }
+        if (dma_supported(fmt, T, 4, t.depth, false) && dma_lds_bytes(fmt, t, T, (int)nslices) <= kMaxLds) return t;
+        t.depth = 0;
+        t.kind = 0;
+    }
+    if (os && rows16 && stream_supported(fmt, T, 4)) {
+        // streamed through LDS via registers, two 8-row tiles in flight
         t.kind = 1;
         t.rows_per_batch = 4;
-        int64_t rw = (rows / 256 + 15) / 16 * 16;
-        rw = rw < 16 ? 16 : rw > 256 ? 256 : rw;
-        t.rows_per_wg = (int)rw;
+        t.rows_per_wg = (int)(rw + 15) / 16 * 16;
         if (stream_lds_bytes(fmt, t, T, (int)nslices) <= kMaxLds) return t;
         t.rows_per_wg = 16;
         if (stream_lds_bytes(fmt, t, T, (int)nslices) <= kMaxLds) return t;
@@ -89,9 +157,8 @@ Tile default_tile(int fmt, int64_t rows, int64_t cols, int T) {
     return t;
 }
 
-// QGEMV_TILE="fmt:rb,nw,rw[,k][;...]" with k = d (direct) or s (streamed through
-// LDS; the default when the shape allows it).  Returns 0 (no override for fmt),
-// 1 (override applied to *t) or -1 (malformed / outside the compiled set).
+// QGEMV_TILE="fmt:rb,nw,rw[,k][;...]".  Returns 0 (no override for fmt), 1
+// (override applied to *t) or -1 (malformed / outside the compiled set).
 int tile_override(int fmt, Tile* t, std::string* why) {
     const char* env = getenv("QGEMV_TILE");
     if (!env || !*env) return 0;
@@ -114,23 +181,13 @@ int tile_override(int fmt, Tile* t, std::string* why) {
             *why = "QGEMV_TILE format '" + name + "' unknown";
             return -1;
         }
-        int rb = 0, nw = 0, rw = 0;
-        char kind = 0, tail = 0;
-        const int got = sscanf(item.c_str() + colon + 1, "%d,%d,%d,%c%c", &rb, &nw, &rw, &kind, &tail);
-        if (!(got == 3 || (got == 4 && (kind == 'd' || kind == 's' || kind == 'm')))) {
-            *why = "QGEMV_TILE item '" + item + "' is not fmt:rb,nw,rw[,d|s|m]";
-            return -1;
-        }
-        if (!valid_rb(rb) || nw < 1 || nw > kMaxWaves || rw < 2 * rb || rw % (2 * rb) || rw > (1 << 20)) {
-            *why = "QGEMV_TILE item '" + item + "' is outside the compiled set (rb in {1,2,4,8,16}, nw in 1..12, rw a multiple of 2*rb)";
+        Tile parsed = *t;
+        if (!parse_tile_spec(item.substr(colon + 1), &parsed, why)) {
+            *why = "QGEMV_TILE: " + *why;
             return -1;
         }
         if (f == fmt) {
-            t->rows_per_batch = rb;
-            t->waves_per_wg = nw;
-            t->rows_per_wg = rw;
-            t->kind = got == 4 ? (kind != 'd') : -1;  // -1: choose below
-            t->mfma = got == 4 && kind == 'm';
+            *t = parsed;
             return 1;
         }
     }
@@ -147,6 +204,19 @@ int pick_tile(int fmt, int64_t rows, int64_t cols, int T, Tile* t) {
     if (t->kind < 0)  // override without a kind: streamed when the shape and tile allow it
         t->kind = stream_shape && stream_supported(fmt, T, t->rows_per_batch) &&
                   stream_lds_bytes(fmt, *t, T, (int)nslices) <= kMaxLds;
+    if (t->kind == 2 || t->kind == 3) {
+        if (!stream_shape)
+            return fail(QG_EINVAL, "streamed tile needs rows of a multiple of 16 bytes and waves_per_wg a multiple of "
+                                   "the %lld k slices", (long long)nslices);
+        if (!dma_supported(fmt, T, t->rows_per_batch, t->depth, t->kind == 3))
+            return fail(QG_EINVAL, "LDS-DMA tile rb=%d depth=%d is not compiled for this format and T=%d "
+                                   "(rb 4; depth 2, 3, 4 or 6, above the %d slots x takes)",
+                        t->rows_per_batch, t->depth, T, dma_x_slots(fmt, T));
+        if (dma_lds_bytes(fmt, *t, T, (int)nslices) > kMaxLds)
+            return fail(QG_EINVAL, "tile needs %zu B of LDS (rows_per_wg %d or depth %d too large)",
+                        dma_lds_bytes(fmt, *t, T, (int)nslices), t->rows_per_wg, t->depth);
+        return QG_OK;
+    }
     if (t->kind == 1) {
         // waves = slices x row groups
         if (!stream_shape)
@@ -208,7 +278,9 @@ int run_dense(int fmt, int64_t rows, int64_t cols, int T, const void* W, const f
     a.nslices = (int)((cols + kSlice - 1) / kSlice);
     a.rows_per_wg = tile.rows_per_wg;
     if ((rows + tile.rows_per_wg - 1) / tile.rows_per_wg > 0x7FFFFFFF) return fail(QG_EUNSUPPORTED, "grid too large");
-    int err = tile.kind == 1 ? launch_stream(fmt, T, tile, a, stream) : launch_dense(fmt, T, tile, a, stream);
+    int err = tile.kind >= 2   ? launch_dma(fmt, T, tile, a, stream)
+              : tile.kind == 1 ? launch_stream(fmt, T, tile, a, stream)
+                               : launch_dense(fmt, T, tile, a, stream);
     if (err) return fail(QG_EHIP, "kernel launch failed: %s", hip_error_name(err));
     return ok();
 }
@@ -251,6 +323,7 @@ int qgemv_grouped_experts(int fmt, int64_t n_experts, int64_t rows, int64_t cols
     if ((st = pick_tile(fmt, rows, cols, QG_MAX_T, &tile))) return st;  // one kernel for 1..4 tokens per expert
     if (tile.kind != 0) {  // the grouped kernel runs the direct path: one wave per slice
         tile.kind = 0;
+        tile.depth = 0;
         tile.mfma = 0;
         const int64_t nsl = (cols + kSlice - 1) / kSlice;
         if (tile.waves_per_wg > nsl) tile.waves_per_wg = (int)nsl;
@@ -362,6 +435,7 @@ int qg_query_tile(int fmt, int64_t rows, int64_t cols, int T, int out_tile[QG_TI
     out_tile[4] = t.rows_per_wg;
     out_tile[5] = t.mfma;
     out_tile[6] = t.kind;
+    out_tile[7] = t.depth;
     return ok();
 }
 

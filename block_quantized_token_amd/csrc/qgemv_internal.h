@@ -17,7 +17,10 @@ struct Tile {
     int k_slice;         // 512 (fixed by the kernels)
     int rows_per_wg;     // RW: rows per workgroup (multiple of 2*RB)
     int mfma;            // 1: streamed tiles contracted on the matrix cores (kind 1 only)
-    int kind;            // 0: direct (lanes load their own bytes); 1: streamed through LDS
+    int kind;            // 0: direct (lanes load their own bytes); 1: streamed through LDS via
+                         // registers; 2: streamed by LDS-DMA loads into a ring of `depth` buffers,
+                         // x staged in the ring's last slots; 3: as 2, x staged in its own region
+    int depth;           // kinds 2, 3: tiles in flight per wave (2, 3, 4 or 6); 0 otherwise
 };
 
 constexpr int kLanesPerRow = 32;
@@ -67,6 +70,24 @@ inline bool stream_supported(int fmt, int T, int rb) {
     return false;
 }
 
+// LDS-DMA streamed kernel: 8-row tiles (rb 4), a ring of `depth` tile buffers per
+// wave, partial sums [tiles][slices][2][rb * pad(T)] after the rings.
+// x of the slice (T x 512 fp32) is staged in the last ring slots, so the depth
+// must exceed the slots it takes.
+inline int dma_x_slots(int fmt, int T) {
+    const size_t buf = stream_buf_bytes(fmt, 4);
+    return (int)((T * kSlice * 4 + buf - 1) / buf);
+}
+inline bool dma_supported(int fmt, int T, int rb, int depth, bool xsep) {
+    return rb == 4 && (depth == 2 || depth == 3 || depth == 4 || depth == 6) && (xsep || dma_x_slots(fmt, T) < depth);
+}
+// rings, then (kind 3) x regions [waves][T][2 KB], then partial sums
+inline size_t dma_lds_bytes(int fmt, const Tile& t, int T, int nslices) {
+    const size_t ntiles = (size_t)(t.rows_per_wg + 2 * t.rows_per_batch - 1) / (2 * t.rows_per_batch);
+    return (size_t)t.waves_per_wg * (t.depth * stream_buf_bytes(fmt, t.rows_per_batch) + (t.kind == 3 ? T * 2048 : 0)) +
+           ntiles * nslices * 2 * t.rows_per_batch * pad_tokens(T) * 4;
+}
+
 // Matrix-core streamed kernel: 16-row tiles (rb 8), Q8_0, any T.
 inline bool mfma_supported(int fmt, int rb) { return fmt == QG_FMT_Q8_0 && rb == 8; }
 
@@ -110,6 +131,7 @@ struct GroupedArgs {
 // Launchers (qgemv_kernels.hip).  Return a hipError_t value as int.
 int launch_dense(int fmt, int T, const Tile& tile, const DenseArgs& a, void* stream);
 int launch_stream(int fmt, int T, const Tile& tile, const DenseArgs& a, void* stream);
+int launch_dma(int fmt, int T, const Tile& tile, const DenseArgs& a, void* stream);
 int launch_grouped(int fmt, const Tile& tile, const GroupedArgs& a, void* stream);
 const char* hip_error_name(int err);
 

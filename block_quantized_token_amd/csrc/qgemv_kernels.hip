@@ -547,23 +547,17 @@ __device__ __forceinline__ void stream_issue(const uint8_t* __restrict__ W, int6
     for (int k = 0; k < L; ++k) R[k] = __builtin_amdgcn_raw_buffer_load_b128(rsrc, off[k], 0, 0);
 }
 
+// Decode, multiply and reduce one tile that sits in the wave's LDS buffer (chunk
+// order), and write the wave's partial sums for it.
 template <int FMT, int NT, int ST>
-__device__ __forceinline__ void stream_tile(const uint8_t* __restrict__ W, int64_t row_bytes, int64_t row_begin,
-                                            int64_t row_end, int ntiles, int t, int ahead,
-                                            const int (&off)[StreamShape<FMT, ST>::kLoads],
-                                            V4 (&R)[StreamShape<FMT, ST>::kLoads], uint8_t* buf, float* part,
-                                            const float (&xr)[NT][kWeightsPerLane], int lane, int li, int g, int s,
-                                            int nsl, bool lane_ok, bool upper_ok, int my_idx, bool writer) {
+__device__ __forceinline__ void tile_compute(const uint8_t* buf, float* part, const float (&xr)[NT][kWeightsPerLane],
+                                             int li, int g, int s, int nsl, int t, bool lane_ok, bool upper_ok,
+                                             int my_idx, bool writer) {
     using F = Fmt<FMT>;
     using S = StreamShape<FMT, ST>;
     constexpr int TP = pad_pow2(NT);
     constexpr int RB = ST / 2;
     constexpr int N = RB * TP;
-    constexpr int L = S::kLoads;
-    // registers -> LDS (chunk order), then the next-but-one tile into R
-#pragma unroll
-    for (int k = 0; k < L; ++k) *reinterpret_cast<V4*>(buf + (64 * k + lane) * 16) = R[k];
-    stream_issue<FMT, ST>(W, row_bytes, row_begin, row_end, ntiles, t + ahead, off, R);
     typename F::Raw raw[RB];
 #pragma unroll
     for (int i = 0; i < RB; ++i) raw[i] = lds_lane<FMT>(buf + (2 * i + g) * (S::kChunks * 16), li);
@@ -580,6 +574,21 @@ __device__ __forceinline__ void stream_tile(const uint8_t* __restrict__ W, int64
         for (int n = 0; n < TP; ++n) v[i * TP + n] = acc[i][n];
     butterfly32<N>(v, li);
     if (writer) part[(((size_t)t * nsl + s) * 2 + g) * N + my_idx] = v[0];
+}
+
+template <int FMT, int NT, int ST>
+__device__ __forceinline__ void stream_tile(const uint8_t* __restrict__ W, int64_t row_bytes, int64_t row_begin,
+                                            int64_t row_end, int ntiles, int t, int ahead,
+                                            const int (&off)[StreamShape<FMT, ST>::kLoads],
+                                            V4 (&R)[StreamShape<FMT, ST>::kLoads], uint8_t* buf, float* part,
+                                            const float (&xr)[NT][kWeightsPerLane], int lane, int li, int g, int s,
+                                            int nsl, bool lane_ok, bool upper_ok, int my_idx, bool writer) {
+    constexpr int L = StreamShape<FMT, ST>::kLoads;
+    // registers -> LDS (chunk order), then the next-but-one tile into R
+#pragma unroll
+    for (int k = 0; k < L; ++k) *reinterpret_cast<V4*>(buf + (64 * k + lane) * 16) = R[k];
+    stream_issue<FMT, ST>(W, row_bytes, row_begin, row_end, ntiles, t + ahead, off, R);
+    tile_compute<FMT, NT, ST>(buf, part, xr, li, g, s, nsl, t, lane_ok, upper_ok, my_idx, writer);
 }
 
 template <int FMT, int NT, int ST, class Out>
@@ -654,6 +663,169 @@ __device__ __forceinline__ void stream_rows(const uint8_t* __restrict__ W, int64
     }
 }
 
+// ------------------------------------------------- LDS-DMA streamed variant
+// The same tiles and arithmetic as stream_rows, but the loads go straight into
+// LDS (buffer_load ... lds: one 1 KB row of the wave's buffer per instruction,
+// lane l's 16 bytes at offset 16 l, out-of-range lanes write zeros).  No
+// registers hold tiles in flight, so a wave keeps D tiles in flight in a ring of
+// D LDS slots -- for small matrices all of its tiles at once.
+//
+// The compiler does not order these loads against LDS reads, so the waits are
+// explicit.  x comes in the same way (into the last slots of the ring, read into
+// registers once, after which those slots take tiles), so no load of the kernel
+// writes registers and the compiler adds no vmcnt waits of its own.  The wave
+// always has exactly D tiles issued after the start (tiles past its last get an
+// empty descriptor: every lane out of range), so before tile i is read at most
+// (D - 1) * L newer loads may be outstanding; a slot is refilled only after its
+// reads have returned (lgkmcnt(0)); all loads are drained before the workgroup
+// ends, since an empty load still writes its zeros.
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+// One direct-to-LDS load (16 bytes per lane).  The builtin only exists for the
+// device; the host pass compiles an empty body it never runs.
+__device__ __forceinline__ void load_lds16(__amdgpu_buffer_rsrc_t rsrc, uint8_t* lds, int voffset) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void_t*)lds, 16, voffset, 0, 0, 0);
+#else
+    (void)rsrc, (void)lds, (void)voffset;
+#endif
+}
+
+template <int V>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(V >= 0 && V <= 63, "vmcnt is 6 bits");
+    // gfx9 s_waitcnt: vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] | vmcnt[5:4] << 14
+    __builtin_amdgcn_s_waitcnt((V & 15) | (7 << 4) | (15 << 8) | ((V >> 4) << 14));
+}
+__device__ __forceinline__ void wait_lgkmcnt0() { __builtin_amdgcn_s_waitcnt((15) | (7 << 4) | (0 << 8) | (3 << 14)); }
+
+template <int FMT, int ST>
+__device__ __forceinline__ void dma_issue(const uint8_t* __restrict__ W, int64_t row_bytes, int64_t row_begin,
+                                          int64_t row_end, int ntiles, int t, const int (&off)[StreamShape<FMT, ST>::kLoads],
+                                          uint8_t* lbuf) {
+    constexpr int L = StreamShape<FMT, ST>::kLoads;
+    const bool live = t < ntiles;
+    const int64_t r0 = row_begin + (int64_t)(live ? t : 0) * ST;
+    const int64_t rows_here = row_end - r0 < ST ? row_end - r0 : ST;
+    const int num = live ? (int)(rows_here * row_bytes) : 0;
+    const __amdgpu_buffer_rsrc_t rsrc =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(W + r0 * row_bytes), (short)0, num, kBufferRsrcWord3);
+#pragma unroll
+    for (int k = 0; k < L; ++k)
+        load_lds16(rsrc, lbuf + 1024 * k, off[k]);
+}
+
+// Slots of the ring that x[NT][512 of the slice] occupies at the start.
+template <int FMT, int ST, int NT>
+constexpr int dma_x_slots() { return (NT * kSlice * 4 + StreamShape<FMT, ST>::kBufBytes - 1) / StreamShape<FMT, ST>::kBufBytes; }
+
+// XSEP: x gets a region of its own after the rings ([waves][NT][2 KB]), so all D
+// tiles are issued at once; otherwise x borrows the last ring slots and the
+// tiles for them are issued after x is read.
+template <int FMT, int NT, int ST, int D, bool XSEP, class Out>
+__device__ __forceinline__ void dma_rows(const uint8_t* __restrict__ W, int64_t row_bytes, int cols, int nsl,
+                                         const float* __restrict__ x, const int64_t (&xoff)[NT], int64_t row_begin,
+                                         int64_t row_end, Out out) {
+    using F = Fmt<FMT>;
+    using S = StreamShape<FMT, ST>;
+    constexpr int TP = pad_pow2(NT);
+    constexpr int RB = ST / 2;
+    constexpr int N = RB * TP;
+    constexpr int L = S::kLoads;
+    constexpr int X = XSEP ? 0 : dma_x_slots<FMT, ST, NT>();
+    static_assert(N <= 32, "tile rows * tokens too large");
+    static_assert(X < D, "x must leave at least one slot for the first tile");
+    static_assert((D - 1) * L <= 63, "vmcnt holds at most 63 outstanding loads");
+    extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: keeps descriptors and M0 scalar
+    const int nw = blockDim.x >> 6;
+    const int g = lane >> 5;
+    const int li = lane & 31;
+    const int s = wave % nsl;
+    const int rg = wave / nsl;
+    const int RG = nw / nsl;
+    const int k0 = s * kSlice;
+    const int ntiles = (int)((row_end - row_begin + ST - 1) / ST);
+    uint8_t* ring = smem + wave * D * S::kBufBytes;
+    uint8_t* xl = XSEP ? smem + nw * D * S::kBufBytes + wave * NT * 2048 : ring + (D - X) * S::kBufBytes;
+    float* part = reinterpret_cast<float*>(smem + nw * (D * S::kBufBytes + (XSEP ? NT * 2048 : 0)));  // [tiles][nsl][2][N]
+
+    const int64_t rest = row_bytes - (int64_t)s * S::kChunks * 16;
+    const int cs = rest / 16 < S::kChunks ? (int)(rest / 16) : S::kChunks;
+    int off[L];
+#pragma unroll
+    for (int k = 0; k < L; ++k) {
+        const int j = 64 * k + lane;
+        const int r = j / S::kChunks, c = j % S::kChunks;
+        off[k] = (r < ST && c < cs) ? (int)(r * row_bytes) + s * S::kChunks * 16 + 16 * c : kNoLoad;
+    }
+    const bool lane_ok = F::lane_valid(li, k0, cols);
+    const bool upper_ok = lane_ok && F::upper_valid(li, k0, cols);
+    bool writer;
+    const int my_idx = butterfly_index<N>(li, writer);
+
+    // x of the slice, token n at xl + 2048 n (k past cols reads as zero), then the
+    // first D - X tiles
+#pragma unroll
+    for (int n = 0; n < NT; ++n) {
+        const __amdgpu_buffer_rsrc_t xr_rsrc =
+            __builtin_amdgcn_make_buffer_rsrc((void*)(x + xoff[n] + k0), (short)0, (cols - k0) * 4, kBufferRsrcWord3);
+        load_lds16(xr_rsrc, xl + 2048 * n, 16 * lane);
+        load_lds16(xr_rsrc, xl + 2048 * n + 1024, 16 * lane + 1024);
+    }
+#pragma unroll
+    for (int i = 0; i < D - X; ++i)
+        dma_issue<FMT, ST>(W, row_bytes, row_begin, row_end, ntiles, rg + i * RG, off, ring + i * S::kBufBytes);
+    // x and tile 0 have landed once at most (D - X - 1) * L newer loads remain
+    wait_vmcnt<(D - X - 1) * L>();
+    float xr[NT][kWeightsPerLane];
+    {
+        const int b0 = F::kbase(li, 0), b1 = F::kbase(li, 1);
+#pragma unroll
+        for (int n = 0; n < NT; ++n) {
+            const float4* p0 = reinterpret_cast<const float4*>(xl + 2048 * n + 4 * b0);
+            const float4* p1 = reinterpret_cast<const float4*>(xl + 2048 * n + 4 * b1);
+            const float4 a = p0[0], b = p0[1], c = p1[0], d = p1[1];
+            xr[n][0] = a.x; xr[n][1] = a.y; xr[n][2] = a.z; xr[n][3] = a.w;
+            xr[n][4] = b.x; xr[n][5] = b.y; xr[n][6] = b.z; xr[n][7] = b.w;
+            xr[n][8] = c.x; xr[n][9] = c.y; xr[n][10] = c.z; xr[n][11] = c.w;
+            xr[n][12] = d.x; xr[n][13] = d.y; xr[n][14] = d.z; xr[n][15] = d.w;
+        }
+    }
+    if constexpr (X > 0) {
+        wait_lgkmcnt0();  // x is in registers: its slots take tiles D - X .. D - 1
+#pragma unroll
+        for (int i = D - X; i < D; ++i)
+            dma_issue<FMT, ST>(W, row_bytes, row_begin, row_end, ntiles, rg + i * RG, off, ring + i * S::kBufBytes);
+    }
+
+    // this wave's tiles: rg, rg + RG, ...
+    const int mine = ntiles > rg ? (ntiles - rg + RG - 1) / RG : 0;
+    for (int i = 0; i < mine; ++i) {
+        uint8_t* buf = ring + (i % D) * S::kBufBytes;
+        wait_vmcnt<(D - 1) * L>();
+        tile_compute<FMT, NT, ST>(buf, part, xr, li, g, s, nsl, rg + i * RG, lane_ok, upper_ok, my_idx, writer);
+        wait_lgkmcnt0();
+        dma_issue<FMT, ST>(W, row_bytes, row_begin, row_end, ntiles, rg + (i + D) * RG, off, buf);
+    }
+    wait_vmcnt<0>();
+    __syncthreads();
+    // every output of the workgroup: sum the slices' partials in slice order
+    const int nrows = (int)(row_end - row_begin);
+    for (int o = tid; o < nrows * NT; o += blockDim.x) {
+        const int rr = o / NT, t = o % NT;
+        const int tl = rr / ST, rin = rr % ST;
+        const int gg = rin & 1, i = rin >> 1;
+        const float* base = part + ((size_t)tl * nsl * 2 + gg) * N + i * TP + t;
+        float sum = base[0];
+        for (int w = 1; w < nsl; ++w) sum = sum + base[(size_t)w * 2 * N];
+        out(t, row_begin + rr, sum);
+    }
+}
+
 // ------------------------------------------------------ matrix-core variant
 // The same streamed tiles (16 rows), contracted on the matrix cores with
 // v_mfma_f32_16x16x32_bf16: D[16 x 16] = A[16 x 32] . B[32 x 16] per block.
@@ -695,12 +867,37 @@ __device__ __forceinline__ uint32_t x_piece(float x, int p) {
     return (uint32_t)__builtin_bit_cast(uint16_t, v);
 }
 
+// Loads of one 16-row Q8_0 tile (as stream_issue).  The per-lane byte offsets are
+// recomputed at every issue from an opaque copy of the lane id, so they hold no
+// registers across the loop (the A fragments need them).  j / 34 is exact as
+// (j * 1928) >> 16 for every chunk index j < 578.
+__device__ __forceinline__ void mfma_issue(const uint8_t* __restrict__ W, int row_bytes, int64_t row_begin,
+                                           int64_t row_end, int ntiles, int t, int lane, int cs, int sbase,
+                                           V4 (&R)[StreamShape<QG_FMT_Q8_0, 16>::kLoads]) {
+    constexpr int L = StreamShape<QG_FMT_Q8_0, 16>::kLoads;
+    static_assert(64 * L <= 578, "chunk index past the exact range of the division");
+    int l = lane;
+    asm volatile("" : "+v"(l));
+    const bool live = t < ntiles;
+    const int64_t r0 = row_begin + (int64_t)(live ? t : 0) * 16;
+    const int64_t rows_here = row_end - r0 < 16 ? row_end - r0 : 16;
+    const int num = live ? (int)(rows_here * row_bytes) : 0;
+    const __amdgpu_buffer_rsrc_t rsrc =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(W + r0 * row_bytes), (short)0, num, kBufferRsrcWord3);
+#pragma unroll
+    for (int k = 0; k < L; ++k) {
+        const int j = 64 * k + l;
+        const int r = (j * 1928) >> 16, c = j - 34 * r;
+        const int o = (r < 16 && c < cs) ? r * row_bytes + sbase + 16 * c : kNoLoad;
+        R[k] = __builtin_amdgcn_raw_buffer_load_b128(rsrc, o, 0, 0);
+    }
+}
+
 // One 16-row tile of one k slice: registers -> LDS, the next-but-one tile into R,
 // then one MFMA per block; the three pieces of each token are added at the end.
 template <int NT>
-__device__ __forceinline__ void mfma_tile_q8(const uint8_t* __restrict__ W, int64_t row_bytes, int64_t row_begin,
-                                             int64_t row_end, int ntiles, int t, int ahead,
-                                             const int (&off)[StreamShape<QG_FMT_Q8_0, 16>::kLoads],
+__device__ __forceinline__ void mfma_tile_q8(const uint8_t* __restrict__ W, int row_bytes, int64_t row_begin,
+                                             int64_t row_end, int ntiles, int t, int ahead, int cs, int sbase,
                                              V4 (&R)[StreamShape<QG_FMT_Q8_0, 16>::kLoads], uint8_t* buf, float* part,
                                              const V4 (&afrag)[16], int lane, int n, int g, int s, int nsl, int nblk) {
     using S = StreamShape<QG_FMT_Q8_0, 16>;
@@ -708,7 +905,7 @@ __device__ __forceinline__ void mfma_tile_q8(const uint8_t* __restrict__ W, int6
     constexpr int TP = pad_pow2(NT);
 #pragma unroll
     for (int k = 0; k < L; ++k) *reinterpret_cast<V4*>(buf + (64 * k + lane) * 16) = R[k];
-    stream_issue<QG_FMT_Q8_0, 16>(W, row_bytes, row_begin, row_end, ntiles, t + ahead, off, R);
+    mfma_issue(W, row_bytes, row_begin, row_end, ntiles, t + ahead, lane, cs, sbase, R);
     const uint8_t* rowp = buf + n * (S::kChunks * 16);
     F4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
     // Blocks past a short last slice read stale (finite) codes against zero A
@@ -767,13 +964,8 @@ __device__ __forceinline__ void mfma_rows_q8(const uint8_t* __restrict__ W, int6
     const int64_t rest = row_bytes - (int64_t)s * S::kChunks * 16;
     const int cs = rest / 16 < S::kChunks ? (int)(rest / 16) : S::kChunks;
     const int nblk = (int)(rest / 34) < 16 ? (int)(rest / 34) : 16;  // blocks of this slice
-    int off[L];
-#pragma unroll
-    for (int k = 0; k < L; ++k) {
-        const int j = 64 * k + lane;
-        const int r = j / S::kChunks, c = j % S::kChunks;
-        off[k] = (r < ST && c < cs) ? (int)(r * row_bytes) + s * S::kChunks * 16 + 16 * c : kNoLoad;
-    }
+    const int sbase = s * S::kChunks * 16;
+    const int rbytes = (int)row_bytes;  // 16 rows of a tile fit in int32 (checked on the host)
 
     // A fragments of the slice's 16 blocks (x is small and shared: its loads hit in L2)
     const int am = lane & 15, ap = am >> 2, at = am & 3;
@@ -795,13 +987,16 @@ __device__ __forceinline__ void mfma_rows_q8(const uint8_t* __restrict__ W, int6
         if (b == 7) __builtin_amdgcn_sched_barrier(0);  // two rounds of x loads: bounds live registers
     }
 
-    // one tile in flight per wave (the A fragments hold the registers a second
-    // would need; a CU's waves together still keep enough bytes in flight)
-    V4 ra[L];
-    stream_issue<FMT, ST>(W, row_bytes, row_begin, row_end, ntiles, rg, off, ra);
-    for (int t = rg; t < ntiles; t += RG)
-        mfma_tile_q8<NT>(W, row_bytes, row_begin, row_end, ntiles, t, RG, off, ra, buf, part, afrag, lane, n, g, s, nsl,
-                         nblk);
+    // two tiles in flight per wave, as in the VALU kernel
+    V4 ra[L], rb[L];
+    mfma_issue(W, rbytes, row_begin, row_end, ntiles, rg, lane, cs, sbase, ra);
+    mfma_issue(W, rbytes, row_begin, row_end, ntiles, rg + RG, lane, cs, sbase, rb);
+    for (int t = rg; t < ntiles; t += 2 * RG) {
+        mfma_tile_q8<NT>(W, rbytes, row_begin, row_end, ntiles, t, 2 * RG, cs, sbase, ra, buf, part, afrag, lane, n, g,
+                         s, nsl, nblk);
+        mfma_tile_q8<NT>(W, rbytes, row_begin, row_end, ntiles, t + RG, 2 * RG, cs, sbase, rb, buf, part, afrag, lane,
+                         n, g, s, nsl, nblk);
+    }
     __syncthreads();
     const int nrows = (int)(row_end - row_begin);
     for (int o = tid; o < nrows * NT; o += blockDim.x) {
@@ -838,6 +1033,19 @@ __global__ void __launch_bounds__(64 * kMaxWaves) qgemv_stream_kernel(DenseArgs 
     float* __restrict__ y = a.y;
     const int64_t rows = a.rows;
     stream_rows<FMT, T, ST>(a.W, a.row_bytes, a.cols, a.nslices, a.x, xoff, row_begin, row_end,
+                            [=](int t, int64_t row, float v) { y[t * rows + row] = v; });
+}
+
+template <int FMT, int T, int ST, int D, bool XSEP>
+__global__ void __launch_bounds__(64 * kMaxWaves) qgemv_dma_kernel(DenseArgs a) {
+    const int64_t row_begin = (int64_t)blockIdx.x * a.rows_per_wg;
+    const int64_t row_end = row_begin + a.rows_per_wg < a.rows ? row_begin + a.rows_per_wg : a.rows;
+    int64_t xoff[T];
+#pragma unroll
+    for (int t = 0; t < T; ++t) xoff[t] = (int64_t)t * a.cols;
+    float* __restrict__ y = a.y;
+    const int64_t rows = a.rows;
+    dma_rows<FMT, T, ST, D, XSEP>(a.W, a.row_bytes, a.cols, a.nslices, a.x, xoff, row_begin, row_end,
                             [=](int t, int64_t row, float v) { y[t * rows + row] = v; });
 }
 
@@ -985,6 +1193,35 @@ DenseFn stream_for(int T, int rb) {
     }
 }
 
+// LDS-DMA streamed kernels: 8-row tiles, ring depths 2, 3, 4, 6
+template <int FMT, int T, int D>
+DenseFn dma_depth(bool xsep) {
+    if (xsep) return qgemv_dma_kernel<FMT, T, 8, D, true>;
+    if constexpr (dma_x_slots<FMT, 8, T>() < D) return qgemv_dma_kernel<FMT, T, 8, D, false>;
+    return nullptr;
+}
+
+template <int FMT, int T>
+DenseFn dma_entry(int depth, bool xsep) {
+    switch (depth) {
+    case 2: return dma_depth<FMT, T, 2>(xsep);
+    case 3: return dma_depth<FMT, T, 3>(xsep);
+    case 4: return dma_depth<FMT, T, 4>(xsep);
+    case 6: return dma_depth<FMT, T, 6>(xsep);
+    default: return nullptr;
+    }
+}
+
+template <int FMT>
+DenseFn dma_for(int T, int depth, bool xsep) {
+    switch (T) {
+    case 1: return dma_entry<FMT, 1>(depth, xsep);
+    case 2: return dma_entry<FMT, 2>(depth, xsep);
+    case 3: return dma_entry<FMT, 3>(depth, xsep);
+    default: return dma_entry<FMT, 4>(depth, xsep);
+    }
+}
+
 template <int FMT>
 DenseFn mfma_for(int T) {
     if constexpr (FMT == QG_FMT_Q8_0) {
@@ -1033,6 +1270,19 @@ int launch_stream(int fmt, int T, const Tile& tile, const DenseArgs& a, void* st
     const int64_t nwg = (a.rows + tile.rows_per_wg - 1) / tile.rows_per_wg;
     hipLaunchKernelGGL(fn, dim3((unsigned)nwg), dim3(64 * tile.waves_per_wg),
                        stream_lds_bytes(fmt, tile, T, a.nslices), (hipStream_t)stream, a);
+    return (int)hipGetLastError();
+}
+
+int launch_dma(int fmt, int T, const Tile& tile, const DenseArgs& a, void* stream) {
+    const bool xsep = tile.kind == 3;
+    DenseFn fn = tile.rows_per_batch != 4 ? nullptr
+               : fmt == QG_FMT_Q8_0 ? dma_for<QG_FMT_Q8_0>(T, tile.depth, xsep)
+               : fmt == QG_FMT_Q4_0 ? dma_for<QG_FMT_Q4_0>(T, tile.depth, xsep)
+                                    : dma_for<QG_FMT_BF16>(T, tile.depth, xsep);
+    if (!fn) return (int)hipErrorInvalidValue;
+    const int64_t nwg = (a.rows + tile.rows_per_wg - 1) / tile.rows_per_wg;
+    hipLaunchKernelGGL(fn, dim3((unsigned)nwg), dim3(64 * tile.waves_per_wg), dma_lds_bytes(fmt, tile, T, a.nslices),
+                       (hipStream_t)stream, a);
     return (int)hipGetLastError();
 }
 

@@ -106,5 +106,5 @@ def unpack_q4_0(packed: np.ndarray, rows: int, cols: int):
 def query_tile(fmt, rows: int, cols: int, T: int) -> dict:
     st, t = _lib.qg_query_tile(_fmt(fmt), rows, cols, T)
     _lib.check(st, "qg_query_tile")
-    keys = ("lanes_per_row", "rows_per_batch", "waves_per_wg", "k_slice", "rows_per_wg", "mfma", "kind")
+    keys = ("lanes_per_row", "rows_per_batch", "waves_per_wg", "k_slice", "rows_per_wg", "mfma", "kind", "depth")
     return dict(zip(keys, t))

@@ -48,9 +48,11 @@
  * format (fmt = q8_0 | q4_0 | bf16): rb rows per lane group per batch or tile
  * (1, 2, 4, 8 or 16), nw waves per workgroup (1..12), rw rows per workgroup (a
  * multiple of 2*rb), k the kernel kind: d (each lane loads its own bytes), s
- * (rows streamed through LDS; needs rows of a multiple of 16 bytes) or m (as s,
- * contracted on the matrix cores; Q8_0 with rb 8 only).  A malformed or
- * out-of-set value makes every call of that format return QG_EINVAL.
+ * (rows streamed through LDS via registers; needs rows of a multiple of 16
+ * bytes), l<D> (streamed by direct-to-LDS loads, D = 2, 3, 4 or 6 tiles in
+ * flight per wave; rb 4) or m (as s, contracted on the matrix cores; Q8_0 with
+ * rb 8 only).  A malformed or out-of-set value makes every call of that format
+ * return QG_EINVAL.
  */
 #ifndef QGEMV_H
 #define QGEMV_H
@@ -73,7 +75,7 @@ typedef enum {
 typedef enum { QG_FMT_Q8_0 = 0, QG_FMT_Q4_0 = 1, QG_FMT_BF16 = 2 } qg_format;
 
 #define QG_MAX_T 4
-#define QG_TILE_FIELDS 7 /* lanes_per_row, rows_per_batch, waves_per_wg, k_slice, rows_per_wg, mfma, kind */
+#define QG_TILE_FIELDS 8 /* lanes_per_row, rows_per_batch, waves_per_wg, k_slice, rows_per_wg, mfma, kind, depth */
 
 /* Q8_0 weights: cols % 32 == 0; W holds rows * cols/32 * 34 bytes. */
 int qgemv_q8_0(int64_t rows, int64_t cols, int T, const void* W, const float* x, float* y, void* stream);
@@ -111,8 +113,10 @@ int qg_pack_q4_0(int64_t rows, int64_t cols, const uint16_t* d_bits, const uint8
 int qg_unpack_q4_0(int64_t rows, int64_t cols, const void* in, uint16_t* d_bits, uint8_t* codes);
 
 /* The tile a call with these arguments would use (after QGEMV_TILE):
- * out_tile = {lanes_per_row, rows_per_batch, waves_per_wg, k_slice, rows_per_wg, mfma, kind}
- * (kind 0: direct loads, 1: streamed through LDS; mfma 1: matrix-core contraction). */
+ * out_tile = {lanes_per_row, rows_per_batch, waves_per_wg, k_slice, rows_per_wg, mfma, kind, depth}
+ * (kind 0: direct loads, 1: streamed through LDS via registers, 2: streamed by
+ * direct-to-LDS loads with `depth` tiles in flight per wave; mfma 1: matrix-core
+ * contraction). */
 int qg_query_tile(int fmt, int64_t rows, int64_t cols, int T, int out_tile[QG_TILE_FIELDS]);
 
 /* Static description of a status code (never NULL). */

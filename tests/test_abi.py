@@ -161,8 +161,17 @@ def test_tile_query_and_override(lib, monkeypatch):
     assert (t["rows_per_batch"], t["waves_per_wg"], t["rows_per_wg"]) == (2, 5, 8)
     q4 = ops.query_tile("q4_0", 10240, 2560, 4)  # other formats keep their default
     assert (q4["rows_per_batch"], q4["rows_per_wg"]) != (2, 8)
-    # malformed, outside the set, or not compiled (16 rows x 4 tokens; pipelined RB=8 at T=4)
-    for bad in ("q8_0:3,5,8", "q8_0:2,13,8", "q8_0:2,5,6", "q9:2,5,8", "q8_0:2,5", "q8_0:16,5,32", "q8_0:8,5,32"):
+    # LDS-DMA kind: depth after 'l'
+    monkeypatch.setenv("QGEMV_TILE", "q8_0:4,5,48,l6")
+    t = ops.query_tile("q8_0", 10240, 2560, 4)
+    assert (t["kind"], t["depth"], t["rows_per_wg"]) == (2, 6, 48)
+    monkeypatch.setenv("QGEMV_TILE", "q8_0:4,5,48,l2")  # T=1: x takes one slot of two
+    assert ops.query_tile("q8_0", 10240, 2560, 1)["depth"] == 2
+    # malformed, outside the set, or not compiled (16 rows x 4 tokens; pipelined RB=8 at T=4;
+    # DMA depth 5; DMA depth 2 at T=4, where x takes two slots; DMA with rb 2; a DMA ring
+    # past the LDS)
+    for bad in ("q8_0:3,5,8", "q8_0:2,13,8", "q8_0:2,5,6", "q9:2,5,8", "q8_0:2,5", "q8_0:16,5,32", "q8_0:8,5,32",
+                "q8_0:4,5,48,l5", "q8_0:4,5,48,l2", "q8_0:2,5,48,l4", "q8_0:4,10,48,l6", "q8_0:4,5,48,l", "q8_0:4,5,48,l6x"):
         monkeypatch.setenv("QGEMV_TILE", bad)
         st, _ = _lib.qg_query_tile(0, 10240, 2560, 4)
         assert st == _lib.QG_EINVAL, bad

@@ -209,7 +209,7 @@ def test_direct_and_streamed_kernels_agree_bitwise(torch, monkeypatch, name):
         xd = dev(torch, c["x"][:T])
         outs = {}
         for tile in (f"{fmt}:2,{nw},4,d", f"{fmt}:4,{nw},8,d", f"{fmt}:4,{nw},16,s", f"{fmt}:4,{nw},40,s",
-                     f"{fmt}:8,{nw},32,s"):
+                     f"{fmt}:8,{nw},32,s", f"{fmt}:4,{nw},32,l4"):
             monkeypatch.setenv("QGEMV_TILE", tile)
             st, t = _lib.qg_query_tile(c["fmt"], c["rows"], c["cols"], T)
             if st != 0:
@@ -221,6 +221,36 @@ def test_direct_and_streamed_kernels_agree_bitwise(torch, monkeypatch, name):
             assert np.array_equal(y, ref), (name, T, tile)
         assert any(t.endswith(",d") for t in outs)
         assert any(t.endswith(",s") for t in outs) or (fmt == "bf16" and T >= 3)  # no streamed bf16 at T>=3
+
+
+@pytest.mark.parametrize("name", ["c1_q8_0_2560x2560", "c2a_q8_0_10240x2560", "c2b_q8_0_2560x6144",
+                                  "c3_q4_0_8192x2560", "c3_bf16_8192x2560"])
+def test_dma_ring_depths_agree_bitwise(torch, monkeypatch, name):
+    """The LDS-DMA kind at every compiled ring depth and several row tilings
+    (partial rings, more tiles than slots, a ragged last tile) gives the bits of
+    the register-streamed and direct kinds."""
+    c = I.dense_case(name)
+    fmt = NAMES[c["fmt"]]
+    Wd = dev(torch, c["W"])
+    nw = -(-c["cols"] // 512)
+    for T in (1, 2, 3, 4):
+        xd = dev(torch, c["x"][:T])
+        monkeypatch.setenv("QGEMV_TILE", f"{fmt}:2,{nw},4,d")
+        ref = ops.gemv(fmt, Wd, xd, c["rows"]).cpu().numpy()
+        ran = 0
+        for d in (2, 3, 4, 6):
+            for rw, k in ((8, "l"), (40, "l"), (48, "L"), (120, "l"), (16, "L"), (120, "L")):
+                tile = f"{fmt}:4,{nw},{rw},{k}{d}"
+                monkeypatch.setenv("QGEMV_TILE", tile)
+                st, _t = _lib.qg_query_tile(c["fmt"], c["rows"], c["cols"], T)
+                if st != 0:
+                    continue  # x does not leave a slot, or the ring does not fit the LDS
+                say(f"[dma] {name} T={T} tile={tile}")
+                y = ops.gemv(fmt, Wd, xd, c["rows"]).cpu().numpy()
+                assert np.array_equal(y, ref), (name, T, tile)
+                ran += 1
+        # 12 slices: a ring of 3 slots per wave, which x needs at T >= 3, passes the LDS
+        assert ran >= 3 or (name == "c2b_q8_0_2560x6144" and T >= 3), (name, T, ran)
 
 
 def test_tile_override_other_k_split(torch, orc, monkeypatch):
