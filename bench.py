@@ -146,6 +146,74 @@ def summarize_pmc(fetch_dir, write_dir, nbytes):
         print(f"| {k} | {fetch[k]:.1f} | {write.get(k, 0.0):.1f} | {rb:.0f} | {rb + wb:.0f} | {(rb + wb) / nbytes:.3f} |")
 
 
+def time_entry(torch, stream, launch, calls):
+    """µs per call of ``launch(i)`` over ``calls`` back-to-back calls (after 20 warm-up calls)."""
+    for i in range(20):
+        launch(i)
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s.record(stream)
+    for i in range(calls):
+        launch(i)
+    e.record(stream)
+    torch.cuda.synchronize()
+    return s.elapsed_time(e) * 1e3 / calls
+
+
+def other_workloads(torch, stream):
+    """The other shapes the pages time, T = 1..4, for the record (not part of
+    ``value``).  Timing does not depend on the weight values, so each ring copy is
+    random bytes drawn on the device; every call streams from HBM (ring >= 1 GiB)."""
+    out = {}
+    sp = stream.cuda_stream
+    for name in ("c1_q8_0_2560x2560", "c2b_q8_0_2560x6144", "c3_q4_0_8192x2560", "c3_bf16_8192x2560",
+                 "c4_q8_0_248320x5120"):
+        fmt, rows, cols, _ = I.CONFIGS[name]
+        nb = _lib.qg_packed_bytes(fmt, rows, cols)
+        ring = [torch.randint(0, 256, (nb,), dtype=torch.uint8, device="cuda")
+                for _ in range(max(1, -(-RING_BYTES // nb)))]
+        x = torch.randn(4, cols, device="cuda")
+        y = torch.empty(4, rows, device="cuda")
+        entry = {0: _lib.qgemv_q8_0, 1: _lib.qgemv_q4_0, 2: _lib.qgemv_bf16}[fmt]
+        calls = max(50, min(2000, int(4e9 / nb)))
+        res = {}
+        for T in (1, 2, 3, 4):
+            def launch(i, T=T):
+                st = entry(rows, cols, T, ring[i % len(ring)].data_ptr(), x.data_ptr(), y.data_ptr(), sp)
+                if st:
+                    _lib.check(st, name)
+            us = time_entry(torch, stream, launch, calls)
+            res[str(T)] = dict(us_per_call=round(us, 3), gbs=round(nb / us / 1e3, 1),
+                               pct_peak=round(100 * nb / us / 1e3 / HBM_PEAK_GBS, 1),
+                               tile=ops.query_tile(I.FMT_NAMES[fmt], rows, cols, T))
+        out[name] = dict(weight_bytes_per_call=nb, calls=calls, ring_copies=len(ring), per_T=res)
+        del ring
+    # grouped experts: 256 Q4_0 experts of 512 x 2560; each token picks 10 distinct
+    # experts, none shared; bytes per call = the distinct experts' bytes
+    g = I.GROUPED["c5_q4_0_experts"]
+    E, rows, cols, topk = g["n_experts"], g["rows"], g["cols"], g["topk"]
+    table = _lib.qg_packed_bytes(g["fmt"], E * rows, cols)
+    ring = [torch.randint(0, 256, (table,), dtype=torch.uint8, device="cuda")
+            for _ in range(max(1, -(-RING_BYTES // table)))]
+    ids_all = torch.from_numpy(I.expert_ids(I.rng_for(0), E, 4, topk)).cuda()
+    x = torch.randn(4, cols, device="cuda")
+    y = torch.empty(4, topk, rows, device="cuda")
+    res = {}
+    for T in (1, 2, 3, 4):
+        ids = ids_all[:T].contiguous()
+        nb = T * topk * table // E  # distinct experts read
+        def launch(i, T=T, ids=ids):
+            st = _lib.qgemv_grouped_experts(g["fmt"], E, rows, cols, T, topk, ids.data_ptr(),
+                                            ring[i % len(ring)].data_ptr(), x.data_ptr(), y.data_ptr(), sp)
+            if st:
+                _lib.check(st, "grouped")
+        us = time_entry(torch, stream, launch, 1000)
+        res[str(T)] = dict(us_per_call=round(us, 3), bytes_read=nb, gbs=round(nb / us / 1e3, 1),
+                           pct_peak=round(100 * nb / us / 1e3 / HBM_PEAK_GBS, 1))
+    out["c5_q4_0_experts"] = dict(table_bytes=table, ring_copies=len(ring), topk=topk, per_T=res)
+    del ring
+    return out
+
+
 def cpu_baseline(case, budget_s: float):
     """The oracle, untuned, on the host cores: whole steps (T = 1..4) of the same
     workload repeated until about ``budget_s`` seconds have passed."""
@@ -172,7 +240,7 @@ def main():
     ap.add_argument("--steps", type=int, default=2000)
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="oracle time budget; 0 skips the CPU leg")
-    ap.add_argument("--no-extra", action="store_true", help="skip the 2560x6144 detail timing")
+    ap.add_argument("--no-extra", action="store_true", help="skip the timings of the other workloads")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="N",
                     help="after the timed region, run N plain copies of the weight size (PMC calibration)")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
@@ -241,23 +309,7 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
-    detail = {}
-    if not args.no_extra:
-        c2 = I.dense_case(ALSO)
-        r2 = ring_of(torch, c2["W"])
-        x2 = torch.from_numpy(c2["x"]).cuda()
-        y2 = torch.empty((4, c2["rows"]), dtype=torch.float32, device="cuda")
-        nb2 = _lib.qg_packed_bytes(c2["fmt"], c2["rows"], c2["cols"])
-        d2 = {}
-        for T in Ts:
-            time_calls(torch, c2["fmt"], r2, x2[:T], c2["rows"], T, 50, stream, y2)
-            s, e = time_calls(torch, c2["fmt"], r2, x2[:T], c2["rows"], T, 1000, stream, y2)
-            torch.cuda.synchronize()
-            us = s.elapsed_time(e)
-            d2[str(T)] = dict(us_per_call=round(us, 3), gbs=round(nb2 / us / 1e3, 1),
-                              pct_peak=round(100 * nb2 / us / 1e3 / HBM_PEAK_GBS, 1))
-        detail[ALSO] = d2
-        del r2
+    detail = {} if args.no_extra else other_workloads(torch, stream)
 
     cpu = cpu_baseline(case, args.cpu_seconds) if args.cpu_seconds > 0 else None
 

@@ -55,14 +55,14 @@ bool parse_tile_spec(const std::string& spec, Tile* t, std::string* why) {
     int rb = 0, nw = 0, rw = 0, depth = 0;
     char kind = 0, tail = 0;
     int got = sscanf(spec.c_str(), "%d,%d,%d,%c%c", &rb, &nw, &rw, &kind, &tail);
-    if (got == 5 && (kind == 'l' || kind == 'L')) {  // l<depth> or L<depth>
+    if (got == 5 && (kind == 'l' || kind == 'L' || kind == 'u')) {  // l<depth>, L<depth>, u<depth>
         char tail2 = 0;
-        const char* f = kind == 'l' ? "%d,%d,%d,l%d%c" : "%d,%d,%d,L%d%c";
+        const char* f = kind == 'l' ? "%d,%d,%d,l%d%c" : kind == 'L' ? "%d,%d,%d,L%d%c" : "%d,%d,%d,u%d%c";
         got = sscanf(spec.c_str(), f, &rb, &nw, &rw, &depth, &tail2) == 4 ? 4 : -1;
     }
-    const bool dma = kind == 'l' || kind == 'L';
+    const bool dma = kind == 'l' || kind == 'L' || kind == 'u';
     if (!(got == 3 || (got == 4 && (kind == 'd' || kind == 's' || kind == 'm' || (dma && depth > 0))))) {
-        *why = "tile '" + spec + "' is not rb,nw,rw[,d|s|m|l<depth>|L<depth>]";
+        *why = "tile '" + spec + "' is not rb,nw,rw[,d|s|m|l<depth>|L<depth>|u<depth>]";
         return false;
     }
     if (!valid_rb(rb) || nw < 1 || nw > kMaxWaves || rw < 2 * rb || rw % (2 * rb) || rw > (1 << 20)) {
@@ -72,7 +72,7 @@ bool parse_tile_spec(const std::string& spec, Tile* t, std::string* why) {
     t->rows_per_batch = rb;
     t->waves_per_wg = nw;
     t->rows_per_wg = rw;
-    t->kind = got == 4 ? (kind == 'd' ? 0 : kind == 'l' ? 2 : kind == 'L' ? 3 : 1) : -1;  // -1: choose later
+    t->kind = got == 4 ? (kind == 'd' ? 0 : kind == 'l' ? 2 : kind == 'L' ? 3 : kind == 'u' ? 4 : 1) : -1;  // -1: later
     t->mfma = got == 4 && kind == 'm';
     t->depth = got == 4 && dma ? depth : 0;
     return true;
@@ -95,7 +95,9 @@ const TuneEntry kTuned[] = {
     {QG_FMT_Q8_0, 2560, 6144, 0, "4,12,16,s"},     // register-streamed beats DMA at 12 slices
     {QG_FMT_Q8_0, 248320, 5120, 1, "4,10,64,l2"},  // LM head, one token
     {QG_FMT_Q4_0, 8192, 2560, 1, "4,5,8,d"},       // direct: 6.5 vs 7.8 µs
-    {QG_FMT_Q4_0, 8192, 2560, 4, "4,10,32,s"},     // two row groups per slice: 9.8 vs 11.3 µs
+    {QG_FMT_Q4_0, 8192, 2560, 2, "4,10,32,s"},     // two row groups per slice: 8.0 vs 9.3 µs
+    {QG_FMT_Q4_0, 8192, 2560, 3, "4,10,32,s"},     //   9.0 vs 10.6 µs
+    {QG_FMT_Q4_0, 8192, 2560, 4, "4,10,32,s"},     //   9.8 vs 11.3 µs
 };
 
 Tile default_tile(int fmt, int64_t rows, int64_t cols, int T) {
@@ -204,6 +206,17 @@ int pick_tile(int fmt, int64_t rows, int64_t cols, int T, Tile* t) {
     if (t->kind < 0)  // override without a kind: streamed when the shape and tile allow it
         t->kind = stream_shape && stream_supported(fmt, T, t->rows_per_batch) &&
                   stream_lds_bytes(fmt, *t, T, (int)nslices) <= kMaxLds;
+    if (t->kind == 4) {
+        if (row_bytes(fmt, cols) % 16 != 0)
+            return fail(QG_EINVAL, "streamed tile needs rows of a multiple of 16 bytes");
+        if (!units_supported(t->rows_per_batch, t->depth))
+            return fail(QG_EINVAL, "unit-balanced tile rb=%d depth=%d is not compiled (rb 4; depth 2..4)",
+                        t->rows_per_batch, t->depth);
+        if (units_lds_bytes(fmt, *t, T, cols) > kMaxLds)
+            return fail(QG_EINVAL, "tile needs %zu B of LDS (x, rows_per_wg %d or depth %d too large)",
+                        units_lds_bytes(fmt, *t, T, cols), t->rows_per_wg, t->depth);
+        return QG_OK;
+    }
     if (t->kind == 2 || t->kind == 3) {
         if (!stream_shape)
             return fail(QG_EINVAL, "streamed tile needs rows of a multiple of 16 bytes and waves_per_wg a multiple of "
@@ -278,7 +291,8 @@ int run_dense(int fmt, int64_t rows, int64_t cols, int T, const void* W, const f
     a.nslices = (int)((cols + kSlice - 1) / kSlice);
     a.rows_per_wg = tile.rows_per_wg;
     if ((rows + tile.rows_per_wg - 1) / tile.rows_per_wg > 0x7FFFFFFF) return fail(QG_EUNSUPPORTED, "grid too large");
-    int err = tile.kind >= 2   ? launch_dma(fmt, T, tile, a, stream)
+    int err = tile.kind == 4   ? launch_units(fmt, T, tile, a, stream)
+              : tile.kind >= 2 ? launch_dma(fmt, T, tile, a, stream)
               : tile.kind == 1 ? launch_stream(fmt, T, tile, a, stream)
                                : launch_dense(fmt, T, tile, a, stream);
     if (err) return fail(QG_EHIP, "kernel launch failed: %s", hip_error_name(err));
@@ -321,11 +335,33 @@ int qgemv_grouped_experts(int fmt, int64_t n_experts, int64_t rows, int64_t cols
         return fail(QG_EINVAL, "y overlaps W, x or ids");
     Tile tile;
     if ((st = pick_tile(fmt, rows, cols, QG_MAX_T, &tile))) return st;  // one kernel for 1..4 tokens per expert
-    if (tile.kind != 0) {  // the grouped kernel runs the direct path: one wave per slice
+    const int64_t nsl = (cols + kSlice - 1) / kSlice;
+    std::string why;
+    Tile probe = tile;
+    const bool overridden = tile_override(fmt, &probe, &why) == 1;
+    if (!overridden && row_bytes(fmt, cols) % 16 == 0 && nsl <= kMaxWaves) {
+        // LDS-DMA streamed, x staged apart (any number of tokens per expert fits
+        // one ring of two slots).  Rows per workgroup: the workgroups of all
+        // slots (at most T * topk distinct experts) fit in about one round of
+        // two workgroups per CU.
+        tile.kind = 3;
+        tile.depth = 2;
+        tile.mfma = 0;
+        tile.rows_per_batch = 4;
+        tile.waves_per_wg = (int)nsl;
+        int64_t rw = ((int64_t)T * topk * rows / 480 + 7) / 8 * 8;
+        tile.rows_per_wg = (int)(rw < 16 ? 16 : rw > 256 ? 256 : rw);
+        if (dma_lds_bytes(fmt, tile, T, (int)nsl) > kMaxLds) tile.kind = 1;  // fall back below
+    }
+    if (tile.kind == 2 || tile.kind == 3) {  // any DMA tile runs the grouped DMA kernel, x staged apart
+        tile.kind = 3;
+        if (tile.depth != 3) tile.depth = 2;
+        if (tile.waves_per_wg % nsl != 0 || dma_lds_bytes(fmt, tile, T, (int)nsl) > kMaxLds) tile.kind = 1;
+    }
+    if (tile.kind != 0 && tile.kind != 3) {  // the grouped kernel runs the direct path: one wave per slice
         tile.kind = 0;
         tile.depth = 0;
         tile.mfma = 0;
-        const int64_t nsl = (cols + kSlice - 1) / kSlice;
         if (tile.waves_per_wg > nsl) tile.waves_per_wg = (int)nsl;
         tile.rows_per_wg = 2 * tile.rows_per_batch;
         if (!tile_supported(fmt, QG_MAX_T, tile.rows_per_batch, one_shot(tile, (int)((cols + kSlice - 1) / kSlice))))

@@ -19,8 +19,9 @@ struct Tile {
     int mfma;            // 1: streamed tiles contracted on the matrix cores (kind 1 only)
     int kind;            // 0: direct (lanes load their own bytes); 1: streamed through LDS via
                          // registers; 2: streamed by LDS-DMA loads into a ring of `depth` buffers,
-                         // x staged in the ring's last slots; 3: as 2, x staged in its own region
-    int depth;           // kinds 2, 3: tiles in flight per wave (2, 3, 4 or 6); 0 otherwise
+                         // x staged in the ring's last slots; 3: as 2, x staged in its own region;
+                         // 4: unit-balanced LDS-DMA (waves take equal shares of (slice, tile) units)
+    int depth;           // kinds 2, 3: tiles in flight per wave (2, 3, 4 or 6); kind 4: 2..4; 0 otherwise
 };
 
 constexpr int kLanesPerRow = 32;
@@ -88,6 +89,17 @@ inline size_t dma_lds_bytes(int fmt, const Tile& t, int T, int nslices) {
            ntiles * nslices * 2 * t.rows_per_batch * pad_tokens(T) * 4;
 }
 
+// Unit-balanced DMA kernel: x[T][cols] staged whole, then per-wave rings of
+// `depth` 8-row tile slots, then partial sums.  Any number of waves.
+inline bool units_supported(int rb, int depth) { return rb == 4 && depth >= 2 && depth <= 4; }
+inline size_t units_lds_bytes(int fmt, const Tile& t, int T, int64_t cols) {
+    const size_t nslices = (size_t)((cols + kSlice - 1) / kSlice);
+    const size_t ntiles = (size_t)(t.rows_per_wg + 2 * t.rows_per_batch - 1) / (2 * t.rows_per_batch);
+    return ((size_t)T * cols * 4 + 1023) / 1024 * 1024 +
+           (size_t)t.waves_per_wg * t.depth * stream_buf_bytes(fmt, t.rows_per_batch) +
+           ntiles * nslices * 2 * t.rows_per_batch * pad_tokens(T) * 4;
+}
+
 // Matrix-core streamed kernel: 16-row tiles (rb 8), Q8_0, any T.
 inline bool mfma_supported(int fmt, int rb) { return fmt == QG_FMT_Q8_0 && rb == 8; }
 
@@ -132,6 +144,7 @@ struct GroupedArgs {
 int launch_dense(int fmt, int T, const Tile& tile, const DenseArgs& a, void* stream);
 int launch_stream(int fmt, int T, const Tile& tile, const DenseArgs& a, void* stream);
 int launch_dma(int fmt, int T, const Tile& tile, const DenseArgs& a, void* stream);
+int launch_units(int fmt, int T, const Tile& tile, const DenseArgs& a, void* stream);
 int launch_grouped(int fmt, const Tile& tile, const GroupedArgs& a, void* stream);
 const char* hip_error_name(int err);
 

@@ -722,10 +722,46 @@ constexpr int dma_x_slots() { return (NT * kSlice * 4 + StreamShape<FMT, ST>::kB
 // XSEP: x gets a region of its own after the rings ([waves][NT][2 KB]), so all D
 // tiles are issued at once; otherwise x borrows the last ring slots and the
 // tiles for them are issued after x is read.
-template <int FMT, int NT, int ST, int D, bool XSEP, class Out>
+// Per-lane byte offsets of a wave's loads within a tile of its slice s.
+template <int FMT, int ST>
+__device__ __forceinline__ void tile_offsets(int64_t row_bytes, int s, int lane, int (&off)[StreamShape<FMT, ST>::kLoads]) {
+    using S = StreamShape<FMT, ST>;
+    const int64_t rest = row_bytes - (int64_t)s * S::kChunks * 16;
+    const int cs = rest / 16 < S::kChunks ? (int)(rest / 16) : S::kChunks;
+#pragma unroll
+    for (int k = 0; k < S::kLoads; ++k) {
+        const int j = 64 * k + lane;
+        const int r = j / S::kChunks, c = j % S::kChunks;
+        off[k] = (r < ST && c < cs) ? (int)(r * row_bytes) + s * S::kChunks * 16 + 16 * c : kNoLoad;
+    }
+}
+
+// The first D tiles of the wave's ring, issued before x is known (dma_rows with
+// PRE then skips them): lets a caller start the weight stream while it still
+// works out which activations apply.
+template <int FMT, int ST, int D>
+__device__ __forceinline__ void dma_prefetch(const uint8_t* __restrict__ W, int64_t row_bytes, int nsl, int64_t row_begin,
+                                             int64_t row_end) {
+    using S = StreamShape<FMT, ST>;
+    extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int nw = blockDim.x >> 6;
+    const int s = wave % nsl, rg = wave / nsl, RG = nw / nsl;
+    const int ntiles = (int)((row_end - row_begin + ST - 1) / ST);
+    int off[S::kLoads];
+    tile_offsets<FMT, ST>(row_bytes, s, lane, off);
+#pragma unroll
+    for (int i = 0; i < D; ++i)
+        dma_issue<FMT, ST>(W, row_bytes, row_begin, row_end, ntiles, rg + i * RG, off,
+                           smem + (wave * D + i) * S::kBufBytes);
+}
+
+template <int FMT, int NT, int ST, int D, bool XSEP, class Out, bool PRE = false>
 __device__ __forceinline__ void dma_rows(const uint8_t* __restrict__ W, int64_t row_bytes, int cols, int nsl,
                                          const float* __restrict__ x, const int64_t (&xoff)[NT], int64_t row_begin,
                                          int64_t row_end, Out out) {
+    static_assert(!PRE || XSEP, "prefetched tiles need x staged apart");
     using F = Fmt<FMT>;
     using S = StreamShape<FMT, ST>;
     constexpr int TP = pad_pow2(NT);
@@ -753,22 +789,15 @@ __device__ __forceinline__ void dma_rows(const uint8_t* __restrict__ W, int64_t 
     uint8_t* xl = XSEP ? smem + nw * D * S::kBufBytes + wave * NT * 2048 : ring + (D - X) * S::kBufBytes;
     float* part = reinterpret_cast<float*>(smem + nw * (D * S::kBufBytes + (XSEP ? NT * 2048 : 0)));  // [tiles][nsl][2][N]
 
-    const int64_t rest = row_bytes - (int64_t)s * S::kChunks * 16;
-    const int cs = rest / 16 < S::kChunks ? (int)(rest / 16) : S::kChunks;
     int off[L];
-#pragma unroll
-    for (int k = 0; k < L; ++k) {
-        const int j = 64 * k + lane;
-        const int r = j / S::kChunks, c = j % S::kChunks;
-        off[k] = (r < ST && c < cs) ? (int)(r * row_bytes) + s * S::kChunks * 16 + 16 * c : kNoLoad;
-    }
+    tile_offsets<FMT, ST>(row_bytes, s, lane, off);
     const bool lane_ok = F::lane_valid(li, k0, cols);
     const bool upper_ok = lane_ok && F::upper_valid(li, k0, cols);
     bool writer;
     const int my_idx = butterfly_index<N>(li, writer);
 
     // x of the slice, token n at xl + 2048 n (k past cols reads as zero), then the
-    // first D - X tiles
+    // first D - X tiles (with PRE the D tiles are already on their way, older than x)
 #pragma unroll
     for (int n = 0; n < NT; ++n) {
         const __amdgpu_buffer_rsrc_t xr_rsrc =
@@ -776,11 +805,15 @@ __device__ __forceinline__ void dma_rows(const uint8_t* __restrict__ W, int64_t 
         load_lds16(xr_rsrc, xl + 2048 * n, 16 * lane);
         load_lds16(xr_rsrc, xl + 2048 * n + 1024, 16 * lane + 1024);
     }
+    if constexpr (PRE) {
+        wait_vmcnt<0>();  // x is the newest load
+    } else {
 #pragma unroll
-    for (int i = 0; i < D - X; ++i)
-        dma_issue<FMT, ST>(W, row_bytes, row_begin, row_end, ntiles, rg + i * RG, off, ring + i * S::kBufBytes);
-    // x and tile 0 have landed once at most (D - X - 1) * L newer loads remain
-    wait_vmcnt<(D - X - 1) * L>();
+        for (int i = 0; i < D - X; ++i)
+            dma_issue<FMT, ST>(W, row_bytes, row_begin, row_end, ntiles, rg + i * RG, off, ring + i * S::kBufBytes);
+        // x and tile 0 have landed once at most (D - X - 1) * L newer loads remain
+        wait_vmcnt<(D - X - 1) * L>();
+    }
     float xr[NT][kWeightsPerLane];
     {
         const int b0 = F::kbase(li, 0), b1 = F::kbase(li, 1);
@@ -814,6 +847,132 @@ __device__ __forceinline__ void dma_rows(const uint8_t* __restrict__ W, int64_t 
     wait_vmcnt<0>();
     __syncthreads();
     // every output of the workgroup: sum the slices' partials in slice order
+    const int nrows = (int)(row_end - row_begin);
+    for (int o = tid; o < nrows * NT; o += blockDim.x) {
+        const int rr = o / NT, t = o % NT;
+        const int tl = rr / ST, rin = rr % ST;
+        const int gg = rin & 1, i = rin >> 1;
+        const float* base = part + ((size_t)tl * nsl * 2 + gg) * N + i * TP + t;
+        float sum = base[0];
+        for (int w = 1; w < nsl; ++w) sum = sum + base[(size_t)w * 2 * N];
+        out(t, row_begin + rr, sum);
+    }
+}
+
+// ------------------------------------------------- unit-balanced DMA variant
+// Work units are (k slice, 8-row tile) pairs of the workgroup's rows, in
+// slice-major order; wave w of NW takes the contiguous range
+// [w U / NW, (w + 1) U / NW) of the U units, so every wave (and every SIMD) gets
+// the same work to within one unit whatever the number of slices.  The whole of
+// x[T][cols] is staged in LDS once per workgroup (each wave loads a share, then
+// one barrier); a wave reloads its x registers from LDS when its slice changes.
+// Units stream through a ring of D LDS slots with the waits of dma_rows.  Each
+// unit's arithmetic and the final slice-order sum are those of the other
+// kinds, so the results are bit for bit the same.
+template <int FMT, int NT, int D, class Out>
+__device__ __forceinline__ void unit_rows(const uint8_t* __restrict__ W, int64_t row_bytes, int cols, int nsl,
+                                          const float* __restrict__ x, int64_t row_begin, int64_t row_end, Out out) {
+    using F = Fmt<FMT>;
+    constexpr int ST = 8;
+    using S = StreamShape<FMT, ST>;
+    constexpr int TP = pad_pow2(NT);
+    constexpr int RB = ST / 2;
+    constexpr int N = RB * TP;
+    constexpr int L = S::kLoads;
+    static_assert(D * L <= 63, "vmcnt holds at most 63 outstanding loads");
+    extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int nw = blockDim.x >> 6;
+    const int g = lane >> 5;
+    const int li = lane & 31;
+    const int ntiles = (int)((row_end - row_begin + ST - 1) / ST);
+    const int xbytes = NT * cols * 4;
+    uint8_t* xl = smem;                                                     // x[NT][cols]
+    uint8_t* ring = smem + ((xbytes + 1023) & ~1023) + wave * D * S::kBufBytes;
+    float* part = reinterpret_cast<float*>(smem + ((xbytes + 1023) & ~1023) + nw * D * S::kBufBytes);  // [tiles][nsl][2][N]
+
+    // this wave's units
+    const int U = nsl * ntiles;
+    const int u0 = (int)((int64_t)wave * U / nw), u1 = (int)((int64_t)(wave + 1) * U / nw);
+
+    // per-lane chunk geometry of one tile (row r, chunk c) for each load; the
+    // slice only shifts the offset and bounds the chunks
+    int rc_off[L], rc_c[L];
+#pragma unroll
+    for (int k = 0; k < L; ++k) {
+        const int j = 64 * k + lane;
+        const int r = j / S::kChunks, c = j % S::kChunks;
+        rc_off[k] = r < ST ? (int)(r * row_bytes) + 16 * c : -1;
+        rc_c[k] = c;
+    }
+    auto issue = [&](int u, uint8_t* lbuf) __attribute__((always_inline)) {
+        const bool live = u < u1;
+        const int su = live ? u / ntiles : 0, tu = live ? u % ntiles : ntiles;
+        int off[L];
+        const int64_t rest = row_bytes - (int64_t)su * S::kChunks * 16;
+        const int cs = rest / 16 < S::kChunks ? (int)(rest / 16) : S::kChunks;
+#pragma unroll
+        for (int k = 0; k < L; ++k)
+            off[k] = (rc_off[k] >= 0 && rc_c[k] < cs) ? rc_off[k] + su * S::kChunks * 16 : kNoLoad;
+        dma_issue<FMT, ST>(W, row_bytes, row_begin, row_end, ntiles, tu, off, lbuf);
+    };
+
+    // x: 1 KB pieces of the flattened x[NT][cols], shared out round-robin
+    {
+        const __amdgpu_buffer_rsrc_t xr_rsrc = __builtin_amdgcn_make_buffer_rsrc((void*)x, (short)0, xbytes, kBufferRsrcWord3);
+        const int npieces = (xbytes + 1023) / 1024;
+        for (int j = wave; j < npieces; j += nw) load_lds16(xr_rsrc, xl + 1024 * j, 1024 * j + 16 * lane);
+    }
+#pragma unroll
+    for (int i = 0; i < D; ++i) issue(u0 + i, ring + i * S::kBufBytes);
+    wait_vmcnt<D * L>();  // this wave's share of x has landed ...
+    // ... and every other wave's.  A bare s_barrier: __syncthreads() would also
+    // wait for the tiles in flight.  The empty asm keeps the compiler from moving
+    // LDS accesses across it.
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+
+    float xr[NT][kWeightsPerLane];
+    int cur = -1;
+    bool lane_ok = false, upper_ok = false;
+    bool writer;
+    const int my_idx = butterfly_index<N>(li, writer);
+    for (int u = u0; u < u1; ++u) {
+        const int i = u - u0;
+        const int su = u / ntiles, tu = u % ntiles;
+        if (su != cur) {  // uniform
+            cur = su;
+            const int k0 = su * kSlice;
+            lane_ok = F::lane_valid(li, k0, cols);
+            upper_ok = lane_ok && F::upper_valid(li, k0, cols);
+            // x of the slice (a lane past cols reads its token's first values; its
+            // products are discarded)
+            const int b0 = lane_ok ? k0 + F::kbase(li, 0) : 0;
+            const int b1 = lane_ok ? k0 + F::kbase(li, 1) : 0;
+            const int b1c = b1 + 8 <= cols ? b1 : b0;
+#pragma unroll
+            for (int n = 0; n < NT; ++n) {
+                const float4* p0 = reinterpret_cast<const float4*>(xl + 4 * (n * cols + b0));
+                const float4* p1 = reinterpret_cast<const float4*>(xl + 4 * (n * cols + b1c));
+                const float4 a = p0[0], b = p0[1], c = p1[0], d = p1[1];
+                xr[n][0] = a.x; xr[n][1] = a.y; xr[n][2] = a.z; xr[n][3] = a.w;
+                xr[n][4] = b.x; xr[n][5] = b.y; xr[n][6] = b.z; xr[n][7] = b.w;
+                xr[n][8] = c.x; xr[n][9] = c.y; xr[n][10] = c.z; xr[n][11] = c.w;
+                xr[n][12] = d.x; xr[n][13] = d.y; xr[n][14] = d.z; xr[n][15] = d.w;
+            }
+        }
+        uint8_t* buf = ring + (i % D) * S::kBufBytes;
+        wait_vmcnt<(D - 1) * L>();
+        tile_compute<FMT, NT, ST>(buf, part, xr, li, g, su, nsl, tu, lane_ok, upper_ok, my_idx, writer);
+        wait_lgkmcnt0();
+        issue(u + D, buf);
+    }
+    wait_vmcnt<0>();
+    __syncthreads();
     const int nrows = (int)(row_end - row_begin);
     for (int o = tid; o < nrows * NT; o += blockDim.x) {
         const int rr = o / NT, t = o % NT;
@@ -1049,6 +1208,16 @@ __global__ void __launch_bounds__(64 * kMaxWaves) qgemv_dma_kernel(DenseArgs a) 
                             [=](int t, int64_t row, float v) { y[t * rows + row] = v; });
 }
 
+template <int FMT, int T, int D>
+__global__ void __launch_bounds__(64 * kMaxWaves) qgemv_units_kernel(DenseArgs a) {
+    const int64_t row_begin = (int64_t)blockIdx.x * a.rows_per_wg;
+    const int64_t row_end = row_begin + a.rows_per_wg < a.rows ? row_begin + a.rows_per_wg : a.rows;
+    float* __restrict__ y = a.y;
+    const int64_t rows = a.rows;
+    unit_rows<FMT, T, D>(a.W, a.row_bytes, a.cols, a.nslices, a.x, row_begin, row_end,
+                         [=](int t, int64_t row, float v) { y[t * rows + row] = v; });
+}
+
 template <int T>
 __global__ void __launch_bounds__(64 * kMaxWaves) qgemv_mfma_q8_kernel(DenseArgs a) {
     const int64_t row_begin = (int64_t)blockIdx.x * a.rows_per_wg;
@@ -1095,31 +1264,105 @@ __device__ __forceinline__ void grouped_run(const GroupedArgs& a, int e, uint32_
                            });
 }
 
-template <int FMT, int RB, bool ONE_SHOT>
-__global__ void __launch_bounds__(64 * kMaxWaves) qgemv_grouped_kernel(GroupedArgs a) {
+// The slot / row range of a grouped workgroup and the expert it serves.  Returns
+// false when the workgroup has nothing to do: its id is out of range (its
+// output rows are then filled with NaN) or an earlier slot names the same
+// expert (that slot's workgroup computes it for every token).
+__device__ __forceinline__ bool grouped_slot(const GroupedArgs& a, int& e, int64_t& row_begin, int64_t& row_end) {
     const int slot = blockIdx.x / a.tiles_per_expert;
     const int tile = blockIdx.x % a.tiles_per_expert;
-    const int64_t row_begin = (int64_t)tile * a.rows_per_wg;
-    const int64_t row_end = row_begin + a.rows_per_wg < a.rows ? row_begin + a.rows_per_wg : a.rows;
-    const int e = a.ids[slot];
+    row_begin = (int64_t)tile * a.rows_per_wg;
+    row_end = row_begin + a.rows_per_wg < a.rows ? row_begin + a.rows_per_wg : a.rows;
+    e = a.ids[slot];
     if (e < 0 || e >= a.n_experts) {  // precondition violated: make it visible
         float* yrow = a.y + (int64_t)slot * a.rows;
         for (int64_t r = row_begin + threadIdx.x; r < row_end; r += blockDim.x) yrow[r] = __builtin_nanf("");
-        return;
+        return false;
     }
-    for (int i = 0; i < slot; ++i)
-        if (a.ids[i] == e) return;  // an earlier slot's workgroup handles e
-    uint32_t tokmask = 0;  // bit t: token t chose e
-    for (int t = 0; t < a.T; ++t) {
-        bool uses = false;
-        for (int j = 0; j < a.topk; ++j) uses |= (a.ids[t * a.topk + j] == e);
-        if (uses) tokmask |= 1u << t;
+    return true;
+}
+
+// One pass over ids, 64 at a time in parallel lanes: does an earlier slot name e
+// (false: that slot's workgroup serves it), and which tokens chose e.
+__device__ __forceinline__ bool grouped_tokens(const GroupedArgs& a, int e, uint32_t& tokmask) {
+    const int slot = blockIdx.x / a.tiles_per_expert;
+    const int n = a.T * a.topk;
+    const int lane = threadIdx.x & 63;
+    bool earlier = false;
+    tokmask = 0;  // bit t: token t chose e
+    for (int c = 0; c < n; c += 64) {
+        const int i = c + lane;
+        const bool m = i < n && a.ids[i] == e;
+        earlier |= __ballot(m && i < slot) != 0;
+        for (int t = 0; t < a.T; ++t)
+            if (__ballot(m && i / a.topk == t) != 0) tokmask |= 1u << t;
     }
+    return !earlier;
+}
+
+__device__ __forceinline__ bool grouped_prologue(const GroupedArgs& a, int& e, uint32_t& tokmask, int64_t& row_begin,
+                                                 int64_t& row_end) {
+    return grouped_slot(a, e, row_begin, row_end) && grouped_tokens(a, e, tokmask);
+}
+
+template <int FMT, int RB, bool ONE_SHOT>
+__global__ void __launch_bounds__(64 * kMaxWaves) qgemv_grouped_kernel(GroupedArgs a) {
+    int e;
+    uint32_t tokmask;
+    int64_t row_begin, row_end;
+    if (!grouped_prologue(a, e, tokmask, row_begin, row_end)) return;
     switch (__builtin_popcount(tokmask)) {
     case 1: grouped_run<FMT, 1, RB, ONE_SHOT>(a, e, tokmask, row_begin, row_end); break;
     case 2: grouped_run<FMT, 2, RB, ONE_SHOT>(a, e, tokmask, row_begin, row_end); break;
     case 3: grouped_run<FMT, 3, RB, ONE_SHOT>(a, e, tokmask, row_begin, row_end); break;
     default: grouped_run<FMT, 4, RB, ONE_SHOT>(a, e, tokmask, row_begin, row_end); break;
+    }
+}
+
+// Grouped experts on the LDS-DMA streamed path (x staged apart, so any number of
+// tokens per expert fits the same ring).
+template <int FMT, int NE, int D>
+__device__ __forceinline__ void grouped_dma_run(const GroupedArgs& a, int e, uint32_t tokmask, int64_t row_begin,
+                                                int64_t row_end) {
+    const uint32_t tokmask0 = tokmask;
+    int64_t xoff[NE];
+#pragma unroll
+    for (int n = 0; n < NE; ++n) {
+        xoff[n] = (int64_t)__builtin_ctz(tokmask) * a.cols;
+        tokmask &= tokmask - 1;
+    }
+    const int32_t* __restrict__ ids = a.ids;
+    float* __restrict__ y = a.y;
+    const int topk = a.topk;
+    const int64_t rows = a.rows;
+    auto out = [=](int n, int64_t row, float v) {
+                                      uint32_t m = tokmask0;  // token of output n: the n-th set bit
+                                      for (int i = 0; i < n; ++i) m &= m - 1;
+                                      const int t = __builtin_ctz(m);
+                                      for (int j = 0; j < topk; ++j)
+                                          if (ids[t * topk + j] == e) y[((int64_t)t * topk + j) * rows + row] = v;
+                                  };
+    dma_rows<FMT, NE, 8, D, true, decltype(out), true>(a.W + (int64_t)e * a.expert_bytes, a.row_bytes, a.cols,
+                                                      a.nslices, a.x, xoff, row_begin, row_end, out);
+}
+
+template <int FMT, int D>
+__global__ void __launch_bounds__(64 * kMaxWaves) qgemv_grouped_dma_kernel(GroupedArgs a) {
+    int e;
+    uint32_t tokmask;
+    int64_t row_begin, row_end;
+    if (!grouped_slot(a, e, row_begin, row_end)) return;
+    // the expert's weights start streaming while the ids are scanned
+    dma_prefetch<FMT, 8, D>(a.W + (int64_t)e * a.expert_bytes, a.row_bytes, a.nslices, row_begin, row_end);
+    if (!grouped_tokens(a, e, tokmask)) {
+        wait_vmcnt<0>();  // an earlier slot serves e: drain the prefetch before leaving
+        return;
+    }
+    switch (__builtin_popcount(tokmask)) {
+    case 1: grouped_dma_run<FMT, 1, D>(a, e, tokmask, row_begin, row_end); break;
+    case 2: grouped_dma_run<FMT, 2, D>(a, e, tokmask, row_begin, row_end); break;
+    case 3: grouped_dma_run<FMT, 3, D>(a, e, tokmask, row_begin, row_end); break;
+    default: grouped_dma_run<FMT, 4, D>(a, e, tokmask, row_begin, row_end); break;
     }
 }
 
@@ -1222,6 +1465,26 @@ DenseFn dma_for(int T, int depth, bool xsep) {
     }
 }
 
+template <int FMT, int T>
+DenseFn units_entry(int depth) {
+    switch (depth) {
+    case 2: return qgemv_units_kernel<FMT, T, 2>;
+    case 3: return qgemv_units_kernel<FMT, T, 3>;
+    case 4: return qgemv_units_kernel<FMT, T, 4>;
+    default: return nullptr;
+    }
+}
+
+template <int FMT>
+DenseFn units_for(int T, int depth) {
+    switch (T) {
+    case 1: return units_entry<FMT, 1>(depth);
+    case 2: return units_entry<FMT, 2>(depth);
+    case 3: return units_entry<FMT, 3>(depth);
+    default: return units_entry<FMT, 4>(depth);
+    }
+}
+
 template <int FMT>
 DenseFn mfma_for(int T) {
     if constexpr (FMT == QG_FMT_Q8_0) {
@@ -1286,7 +1549,35 @@ int launch_dma(int fmt, int T, const Tile& tile, const DenseArgs& a, void* strea
     return (int)hipGetLastError();
 }
 
+int launch_units(int fmt, int T, const Tile& tile, const DenseArgs& a, void* stream) {
+    DenseFn fn = tile.rows_per_batch != 4 ? nullptr
+               : fmt == QG_FMT_Q8_0 ? units_for<QG_FMT_Q8_0>(T, tile.depth)
+               : fmt == QG_FMT_Q4_0 ? units_for<QG_FMT_Q4_0>(T, tile.depth)
+                                    : units_for<QG_FMT_BF16>(T, tile.depth);
+    if (!fn) return (int)hipErrorInvalidValue;
+    const int64_t nwg = (a.rows + tile.rows_per_wg - 1) / tile.rows_per_wg;
+    hipLaunchKernelGGL(fn, dim3((unsigned)nwg), dim3(64 * tile.waves_per_wg), units_lds_bytes(fmt, tile, T, a.cols),
+                       (hipStream_t)stream, a);
+    return (int)hipGetLastError();
+}
+
 int launch_grouped(int fmt, const Tile& tile, const GroupedArgs& a, void* stream) {
+    if (tile.kind == 3) {
+        GroupedFn fn = nullptr;
+        if (tile.rows_per_batch == 4 && tile.depth == 2)
+            fn = fmt == QG_FMT_Q8_0 ? qgemv_grouped_dma_kernel<QG_FMT_Q8_0, 2>
+               : fmt == QG_FMT_Q4_0 ? qgemv_grouped_dma_kernel<QG_FMT_Q4_0, 2>
+                                    : qgemv_grouped_dma_kernel<QG_FMT_BF16, 2>;
+        if (tile.rows_per_batch == 4 && tile.depth == 3)
+            fn = fmt == QG_FMT_Q8_0 ? qgemv_grouped_dma_kernel<QG_FMT_Q8_0, 3>
+               : fmt == QG_FMT_Q4_0 ? qgemv_grouped_dma_kernel<QG_FMT_Q4_0, 3>
+                                    : qgemv_grouped_dma_kernel<QG_FMT_BF16, 3>;
+        if (!fn) return (int)hipErrorInvalidValue;
+        const int64_t nwg = (int64_t)a.T * a.topk * a.tiles_per_expert;
+        hipLaunchKernelGGL(fn, dim3((unsigned)nwg), dim3(64 * tile.waves_per_wg), dma_lds_bytes(fmt, tile, a.T, a.nslices),
+                           (hipStream_t)stream, a);
+        return (int)hipGetLastError();
+    }
     const int rbi = rb_index(tile.rows_per_batch);
     GroupedFn fn;
     if (one_shot(tile, a.nslices))

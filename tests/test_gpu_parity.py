@@ -249,6 +249,17 @@ def test_dma_ring_depths_agree_bitwise(torch, monkeypatch, name):
                 y = ops.gemv(fmt, Wd, xd, c["rows"]).cpu().numpy()
                 assert np.array_equal(y, ref), (name, T, tile)
                 ran += 1
+        for d in (2, 3, 4):  # unit-balanced kind: any number of waves
+            for nwu, rw in ((4, 40), (8, 16), (3, 120), (4, 8)):
+                tile = f"{fmt}:4,{nwu},{rw},u{d}"
+                monkeypatch.setenv("QGEMV_TILE", tile)
+                st, _t = _lib.qg_query_tile(c["fmt"], c["rows"], c["cols"], T)
+                if st != 0:
+                    continue  # x and the rings do not fit the LDS
+                say(f"[units] {name} T={T} tile={tile}")
+                y = ops.gemv(fmt, Wd, xd, c["rows"]).cpu().numpy()
+                assert np.array_equal(y, ref), (name, T, tile)
+                ran += 1
         # 12 slices: a ring of 3 slots per wave, which x needs at T >= 3, passes the LDS
         assert ran >= 3 or (name == "c2b_q8_0_2560x6144" and T >= 3), (name, T, ran)
 
@@ -352,20 +363,27 @@ def test_grouped_config(torch, orc):
 
 
 @pytest.mark.parametrize("fmt", [Q4, Q8, BF])
-def test_grouped_sharing(torch, orc, fmt):
-    rng = np.random.default_rng(10 + fmt)
-    n_experts, rows, cols = 12, 200, 1024
-    W = I.weights(rng, fmt, n_experts * rows, cols)
-    x = I.activations(rng, cols)
+def test_grouped_sharing(torch, orc, monkeypatch, fmt):
+    """Shared and duplicated experts on the default (LDS-DMA) path, on the direct
+    path (tile override), and at a width whose rows are not 16-byte aligned."""
     cases = [
         np.array([[3, 5], [3, 7], [3, 5], [3, 9]], np.int32),   # expert 3 shared by 4 tokens, 5 by 2
         np.array([[1, 1, 2], [2, 2, 1], [0, 11, 2], [11, 0, 4]], np.int32),  # duplicates inside a token
         np.array([[7, 8, 9, 10]], np.int32),                    # T = 1
         np.array([[4, 6], [6, 4], [4, 6]], np.int32),           # T = 3, ne = 3
     ]
-    for ids in cases:
-        T = ids.shape[0]
-        grouped_check(torch, orc, fmt, n_experts, rows, cols, ids, W, x[:T], "sharing")
+    n_experts, rows = 12, 200
+    for cols, tile in ((1024, None), (1024, f"{NAMES[fmt]}:4,2,8,d"), (1056 if fmt != BF else 1048, None)):
+        if tile:
+            monkeypatch.setenv("QGEMV_TILE", tile)
+        else:
+            monkeypatch.delenv("QGEMV_TILE", raising=False)
+        rng = np.random.default_rng(10 + fmt + cols)
+        W = I.weights(rng, fmt, n_experts * rows, cols)
+        x = I.activations(rng, cols)
+        for ids in cases:
+            T = ids.shape[0]
+            grouped_check(torch, orc, fmt, n_experts, rows, cols, ids, W, x[:T], f"sharing cols={cols} tile={tile}")
 
 
 def test_grouped_bad_id_gives_nan_rows(torch, orc):
