@@ -61,8 +61,8 @@ bool parse_tile_spec(const std::string& spec, Tile* t, std::string* why) {
         got = sscanf(spec.c_str(), f, &rb, &nw, &rw, &depth, &tail2) == 4 ? 4 : -1;
     }
     const bool dma = kind == 'l' || kind == 'L' || kind == 'u';
-    if (!(got == 3 || (got == 4 && (kind == 'd' || kind == 's' || kind == 'm' || (dma && depth > 0))))) {
-        *why = "tile '" + spec + "' is not rb,nw,rw[,d|s|m|l<depth>|L<depth>|u<depth>]";
+    if (!(got == 3 || (got == 4 && (kind == 'd' || kind == 's' || kind == 'm' || kind == 'p' || (dma && depth > 0))))) {
+        *why = "tile '" + spec + "' is not rb,nw,rw[,d|s|m|p|l<depth>|L<depth>|u<depth>]";
         return false;
     }
     if (!valid_rb(rb) || nw < 1 || nw > kMaxWaves || rw < 2 * rb || rw % (2 * rb) || rw > (1 << 20)) {
@@ -73,7 +73,7 @@ bool parse_tile_spec(const std::string& spec, Tile* t, std::string* why) {
     t->waves_per_wg = nw;
     t->rows_per_wg = rw;
     t->kind = got == 4 ? (kind == 'd' ? 0 : kind == 'l' ? 2 : kind == 'L' ? 3 : kind == 'u' ? 4 : 1) : -1;  // -1: later
-    t->mfma = got == 4 && kind == 'm';
+    t->mfma = got == 4 && kind == 'm' ? 1 : got == 4 && kind == 'p' ? 2 : 0;
     t->depth = got == 4 && dma ? depth : 0;
     return true;
 }
@@ -93,7 +93,10 @@ struct TuneEntry {
 // ring depth) where the rule's pick loses by more than a few percent.
 const TuneEntry kTuned[] = {
     {QG_FMT_Q8_0, 2560, 6144, 0, "4,12,16,s"},     // register-streamed beats DMA at 12 slices
-    {QG_FMT_Q8_0, 248320, 5120, 1, "4,10,64,l2"},  // LM head, one token
+    // LM head: the persistent matrix-core kernel at every T (one kind for all T
+    // keeps a token's bits independent of T): 252 / 258 / 270 / 280 µs; the VALU
+    // kernels give 230 / 247 / 285 / 311
+    {QG_FMT_Q8_0, 248320, 5120, 0, "8,10,64,p"},
     {QG_FMT_Q4_0, 8192, 2560, 1, "4,5,8,d"},       // direct: 6.5 vs 7.8 µs
     {QG_FMT_Q4_0, 8192, 2560, 2, "4,10,32,s"},     // two row groups per slice: 8.0 vs 9.3 µs
     {QG_FMT_Q4_0, 8192, 2560, 3, "4,10,32,s"},     //   9.0 vs 10.6 µs
@@ -238,6 +241,17 @@ int pick_tile(int fmt, int64_t rows, int64_t cols, int T, Tile* t) {
         if (t->mfma ? !mfma_supported(fmt, t->rows_per_batch) : !stream_supported(fmt, T, t->rows_per_batch))
             return fail(QG_EINVAL, "streamed%s rows_per_batch %d is not compiled for this format and T=%d",
                         t->mfma ? " matrix-core" : "", t->rows_per_batch, T);
+        if (t->mfma == 2) {  // persistent: one wave per slice, rows_per_wg = buffered chunk of 16-row tiles
+            if (t->waves_per_wg != nslices)
+                return fail(QG_EINVAL, "persistent matrix-core tile needs waves_per_wg == the %lld k slices",
+                            (long long)nslices);
+            if (t->rows_per_wg % 16 != 0)
+                return fail(QG_EINVAL, "persistent matrix-core tile needs rows_per_wg a multiple of 16");
+            if (mfma_persist_lds_bytes(*t, T) > kMaxLds)
+                return fail(QG_EINVAL, "tile needs %zu B of LDS (rows_per_wg %d too large)", mfma_persist_lds_bytes(*t, T),
+                            t->rows_per_wg);
+            return QG_OK;
+        }
         if (stream_lds_bytes(fmt, *t, T, (int)nslices) > kMaxLds)
             return fail(QG_EINVAL, "tile needs %zu B of LDS (rows_per_wg %d too large)",
                         stream_lds_bytes(fmt, *t, T, (int)nslices), t->rows_per_wg);

@@ -16,7 +16,7 @@ struct Tile {
     int waves_per_wg;    // NW: waves per workgroup; wave w takes k slices w, w+NW, ...
     int k_slice;         // 512 (fixed by the kernels)
     int rows_per_wg;     // RW: rows per workgroup (multiple of 2*RB)
-    int mfma;            // 1: streamed tiles contracted on the matrix cores (kind 1 only)
+    int mfma;            // 1: streamed tiles contracted on the matrix cores (kind 1 only); 2: its persistent form
     int kind;            // 0: direct (lanes load their own bytes); 1: streamed through LDS via
                          // registers; 2: streamed by LDS-DMA loads into a ring of `depth` buffers,
                          // x staged in the ring's last slots; 3: as 2, x staged in its own region;
@@ -102,6 +102,14 @@ inline size_t units_lds_bytes(int fmt, const Tile& t, int T, int64_t cols) {
 
 // Matrix-core streamed kernel: 16-row tiles (rb 8), Q8_0, any T.
 inline bool mfma_supported(int fmt, int rb) { return fmt == QG_FMT_Q8_0 && rb == 8; }
+// Its persistent form: one workgroup per CU (256 CUs), one wave per k slice;
+// rows_per_wg is the chunk of rows whose partial sums are buffered (two chunks).
+constexpr int kPersistGrid = 256;
+inline size_t mfma_persist_lds_bytes(const Tile& t, int T) {
+    const size_t chunk_tiles = (size_t)t.rows_per_wg / 16;
+    return (size_t)t.waves_per_wg * stream_buf_bytes(QG_FMT_Q8_0, 8) +
+           2 * chunk_tiles * t.waves_per_wg * 16 * pad_tokens(T) * 4 + 16;
+}
 
 inline bool tile_supported(int fmt, int T, int rb, bool oneshot) {
     if (!valid_rb(rb) || rb * pad_tokens(T) > 32) return false;

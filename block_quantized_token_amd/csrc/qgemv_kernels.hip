@@ -165,6 +165,12 @@ __device__ __forceinline__ void permlane16_swap(float& a, float& b) {
     asm volatile("s_nop 1\n\tv_permlane16_swap_b32 %0, %1" : "+v"(a), "+v"(b));
 }
 
+// v_permlane32_swap: a lane of the lower half ends with (its a, the a of lane + 32),
+// a lane of the upper half with (the b of lane - 32, its b).
+__device__ __forceinline__ void permlane32_swap(float& a, float& b) {
+    asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1" : "+v"(a), "+v"(b));
+}
+
 template <int N>
 __device__ __forceinline__ void butterfly32(float (&v)[N], int li) {
     // stage 16: after the swap, a lane of row 0 holds (its a, row 1's a) and a lane
@@ -1016,14 +1022,18 @@ __device__ __forceinline__ V4 codes_to_bf16(uint32_t c0, uint32_t c1) {
     return r;
 }
 
-// piece p of x as bf16 bits: p = 0 -> RNE(x); 1 -> RNE(x - hi); 2 -> the rest
-__device__ __forceinline__ uint32_t x_piece(float x, int p) {
-    const __bf16 hi = (__bf16)x;
-    const float r1 = x - (float)hi;
-    const __bf16 mid = (__bf16)r1;
-    const __bf16 lo = (__bf16)(r1 - (float)mid);
-    const __bf16 v = p == 0 ? hi : p == 1 ? mid : lo;
-    return (uint32_t)__builtin_bit_cast(uint16_t, v);
+// Piece p of x (bf16 bits) in an exact three-way split by truncation:
+// hi = x with its low 16 bits cleared, mid = the same of x - hi, lo = x - hi - mid.
+// x has a 24-bit significand: x - hi is exact and holds at most 16 significant
+// bits, x - hi - mid at most 8, so lo is exactly a bf16 and hi + mid + lo = x.
+// m1 = (p >= 1), m2 = (p >= 2) as 0/1 floats select the piece without branches:
+// fma(-0, t, v) = v and fma(-1, t, v) = v - t, both exact.
+__device__ __forceinline__ uint32_t x_piece(float x, float m1, float m2) {
+    const float t1 = __builtin_bit_cast(float, __builtin_bit_cast(uint32_t, x) & 0xFFFF0000u);
+    const float v1 = __builtin_fmaf(-m1, t1, x);
+    const float t2 = __builtin_bit_cast(float, __builtin_bit_cast(uint32_t, v1) & 0xFFFF0000u);
+    const float v2 = __builtin_fmaf(-m2, t2, v1);
+    return __builtin_bit_cast(uint32_t, v2) >> 16;  // exact: v2's low 16 bits are zero when p == 2
 }
 
 // Loads of one 16-row Q8_0 tile (as stream_issue).  The per-lane byte offsets are
@@ -1052,23 +1062,35 @@ __device__ __forceinline__ void mfma_issue(const uint8_t* __restrict__ W, int ro
     }
 }
 
-// One 16-row tile of one k slice: registers -> LDS, the next-but-one tile into R,
-// then one MFMA per block; the three pieces of each token are added at the end.
+constexpr int kMfmaRowStride = 560;  // 16 rows x 560 B = 8960 B: within the 9 KB per-wave buffer
+static_assert(16 * kMfmaRowStride <= StreamShape<QG_FMT_Q8_0, 16>::kBufBytes, "padded tile exceeds the wave buffer");
+
 template <int NT>
 __device__ __forceinline__ void mfma_tile_q8(const uint8_t* __restrict__ W, int row_bytes, int64_t row_begin,
                                              int64_t row_end, int ntiles, int t, int ahead, int cs, int sbase,
                                              V4 (&R)[StreamShape<QG_FMT_Q8_0, 16>::kLoads], uint8_t* buf, float* part,
-                                             const V4 (&afrag)[16], int lane, int n, int g, int s, int nsl, int nblk) {
+                                             const V4 (&afrag)[16], int lane, int n, int g, int s, int nsl, int nblk,
+                                             int pt) {
     using S = StreamShape<QG_FMT_Q8_0, 16>;
     constexpr int L = S::kLoads;
     constexpr int TP = pad_pow2(NT);
+    // registers -> LDS with each 544-byte row slice at a 560-byte stride: the
+    // 16 rows the B fragments read at once then fall in distinct banks
 #pragma unroll
-    for (int k = 0; k < L; ++k) *reinterpret_cast<V4*>(buf + (64 * k + lane) * 16) = R[k];
+    for (int k = 0; k < L; ++k) {
+        const int j = 64 * k + lane;
+        const int r = (j * 1928) >> 16, c = j - 34 * r;  // j / 34, j % 34 (exact for j < 578)
+        if (r < 16) *reinterpret_cast<V4*>(buf + r * kMfmaRowStride + 16 * c) = R[k];
+    }
     mfma_issue(W, row_bytes, row_begin, row_end, ntiles, t + ahead, lane, cs, sbase, R);
-    const uint8_t* rowp = buf + n * (S::kChunks * 16);
-    F4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+    const uint8_t* rowp = buf + n * kMfmaRowStride;
+    // Four accumulators (block b goes to b % 4) so consecutive blocks' matrix
+    // products and scalings overlap; combined in a fixed order at the end.
     // Blocks past a short last slice read stale (finite) codes against zero A
     // fragments; their scale is forced to 0 so a stale Inf/NaN cannot leak in.
+    F4 acc4[4];
+#pragma unroll
+    for (int a = 0; a < 4; ++a) acc4[a] = F4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
     for (int b = 0; b < 16; ++b) {
         const uint8_t* blk = rowp + 34 * b;
@@ -1080,18 +1102,52 @@ __device__ __forceinline__ void mfma_tile_q8(const uint8_t* __restrict__ W, int 
         const F4 dd = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(BF8, afrag[b]),
                                                                __builtin_bit_cast(BF8, bq), z, 0, 0, 0);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[j] = __builtin_fmaf(d, dd[j], acc[j]);
+        for (int j = 0; j < 4; ++j) acc4[b & 3][j] = __builtin_fmaf(d, dd[j], acc4[b & 3][j]);
     }
-    // pieces of token j sit in lanes n (hi), n + 16 (mid), n + 32 (lo): added in that order
+    F4 acc;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[j] = (acc4[0][j] + acc4[1][j]) + (acc4[2][j] + acc4[3][j]);
+    // pieces of token j sit in lanes n (hi), n + 16 (mid), n + 32 (lo): added in
+    // that order.  permlane16_swap brings lane n + 16's value to lane n (rows 0/1
+    // of the wave trade places), permlane32_swap lane n + 32's (halves trade).
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-        const float mid = __shfl_down(acc[j], 16, 64);
-        const float lo = __shfl_down(acc[j], 32, 64);
+        float mid = acc[j], lo = acc[j], junk16 = acc[j], junk32 = acc[j];
+        permlane16_swap(junk16, mid);
+        permlane32_swap(junk32, lo);
         acc[j] = (acc[j] + mid) + lo;
     }
     if (g == 0) {
 #pragma unroll
-        for (int j = 0; j < NT; ++j) part[(((size_t)t * nsl + s) * 16 + n) * TP + j] = acc[j];
+        for (int j = 0; j < NT; ++j) part[(((size_t)pt * nsl + s) * 16 + n) * TP + j] = acc[j];
+    }
+}
+
+// A fragments of a slice's 16 blocks: lane l holds row m = l % 16 (piece m / 4 of
+// token m % 4; rows 12..15 and tokens >= NT are zero) at k = 8 (l / 16) .. + 7 of
+// each block.  x is small and shared: its loads hit in L2.
+template <int NT>
+__device__ __forceinline__ void mfma_afrag(const float* __restrict__ x, const int64_t (&xoff)[NT], int k0, int cols,
+                                           int lane, int g, V4 (&afrag)[16]) {
+    const int am = lane & 15, ap = am >> 2, at = am & 3;
+    const bool arow = ap < 3 && at < NT;
+    int64_t xo = 0;
+#pragma unroll
+    for (int t = 0; t < NT; ++t) xo = at == t ? xoff[t] : xo;
+    const float m1 = ap >= 1 ? 1.0f : 0.0f, m2 = ap >= 2 ? 1.0f : 0.0f;
+#pragma unroll
+    for (int b = 0; b < 16; ++b) {
+        const int kb = k0 + 32 * b + 8 * g;
+        const bool ok = arow && kb < cols;
+        const float4* px = reinterpret_cast<const float4*>(x + (ok ? xo + kb : 0));
+        const float4 u = px[0], v = px[1];
+        const float xs[8] = {u.x, u.y, u.z, u.w, v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const uint32_t lo16 = x_piece(xs[2 * i], m1, m2), hi16 = x_piece(xs[2 * i + 1], m1, m2);
+            afrag[b][i] = ok ? lo16 | (hi16 << 16) : 0u;
+        }
+        if (b == 7) __builtin_amdgcn_sched_barrier(0);  // two rounds of x loads: bounds live registers
     }
 }
 
@@ -1126,36 +1182,17 @@ __device__ __forceinline__ void mfma_rows_q8(const uint8_t* __restrict__ W, int6
     const int sbase = s * S::kChunks * 16;
     const int rbytes = (int)row_bytes;  // 16 rows of a tile fit in int32 (checked on the host)
 
-    // A fragments of the slice's 16 blocks (x is small and shared: its loads hit in L2)
-    const int am = lane & 15, ap = am >> 2, at = am & 3;
-    const bool arow = ap < 3 && at < NT;
-    int64_t xo = 0;
-#pragma unroll
-    for (int t = 0; t < NT; ++t) xo = at == t ? xoff[t] : xo;
     V4 afrag[16];
-#pragma unroll
-    for (int b = 0; b < 16; ++b) {
-        const int kb = k0 + 32 * b + 8 * g;
-        const bool ok = arow && kb < cols;
-        const float4* px = reinterpret_cast<const float4*>(x + (ok ? xo + kb : 0));
-        const float4 u = px[0], v = px[1];
-        afrag[b][0] = ok ? x_piece(u.x, ap) | (x_piece(u.y, ap) << 16) : 0u;
-        afrag[b][1] = ok ? x_piece(u.z, ap) | (x_piece(u.w, ap) << 16) : 0u;
-        afrag[b][2] = ok ? x_piece(v.x, ap) | (x_piece(v.y, ap) << 16) : 0u;
-        afrag[b][3] = ok ? x_piece(v.z, ap) | (x_piece(v.w, ap) << 16) : 0u;
-        if (b == 7) __builtin_amdgcn_sched_barrier(0);  // two rounds of x loads: bounds live registers
-    }
+    mfma_afrag<NT>(x, xoff, k0, cols, lane, g, afrag);
 
-    // two tiles in flight per wave, as in the VALU kernel
-    V4 ra[L], rb[L];
+    // one tile in flight per wave in registers (the A fragments and the four
+    // accumulators leave no room for a second); a CU's waves together keep
+    // enough bytes in flight
+    V4 ra[L];
     mfma_issue(W, rbytes, row_begin, row_end, ntiles, rg, lane, cs, sbase, ra);
-    mfma_issue(W, rbytes, row_begin, row_end, ntiles, rg + RG, lane, cs, sbase, rb);
-    for (int t = rg; t < ntiles; t += 2 * RG) {
-        mfma_tile_q8<NT>(W, rbytes, row_begin, row_end, ntiles, t, 2 * RG, cs, sbase, ra, buf, part, afrag, lane, n, g,
-                         s, nsl, nblk);
-        mfma_tile_q8<NT>(W, rbytes, row_begin, row_end, ntiles, t + RG, 2 * RG, cs, sbase, rb, buf, part, afrag, lane,
-                         n, g, s, nsl, nblk);
-    }
+    for (int t = rg; t < ntiles; t += RG)
+        mfma_tile_q8<NT>(W, rbytes, row_begin, row_end, ntiles, t, RG, cs, sbase, ra, buf, part, afrag, lane, n, g, s,
+                         nsl, nblk, t);
     __syncthreads();
     const int nrows = (int)(row_end - row_begin);
     for (int o = tid; o < nrows * NT; o += blockDim.x) {
@@ -1166,6 +1203,83 @@ __device__ __forceinline__ void mfma_rows_q8(const uint8_t* __restrict__ W, int6
         for (int w = 1; w < nsl; ++w) sum = sum + base[(size_t)w * 16 * TP];
         out(t, row_begin + rr, sum);
     }
+}
+
+// Persistent form of the matrix-core kernel: one workgroup per CU takes a
+// balanced contiguous range of 16-row tiles, computes its A fragments once, and
+// streams the whole range.  Partial sums go to one of two chunk buffers of C
+// tiles; the last wave to finish a chunk (an LDS arrival counter) sums the
+// slices and writes y while the others go on, so no wave waits at a barrier.
+// A wave may start filling a chunk buffer only after the chunk that last used
+// it has been summed (a generation count per buffer; the wave that sums it is
+// never waiting on anything, so every wait ends).
+template <int NT, class Out>
+__device__ __forceinline__ void mfma_persist_q8(const uint8_t* __restrict__ W, int64_t rows, int64_t row_bytes, int cols,
+                                                int nsl, int C, const float* __restrict__ x, const int64_t (&xoff)[NT],
+                                                Out out) {
+    constexpr int FMT = QG_FMT_Q8_0;
+    constexpr int ST = 16;
+    using S = StreamShape<FMT, ST>;
+    constexpr int L = S::kLoads;
+    constexpr int TP = pad_pow2(NT);
+    extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int nw = blockDim.x >> 6;  // == nsl: one wave per k slice
+    const int n = lane & 15, g = lane >> 4;
+    const int s = wave;
+    const int64_t TT = (rows + ST - 1) / ST;
+    const int64_t t0 = (int64_t)blockIdx.x * TT / gridDim.x, t1 = (int64_t)(blockIdx.x + 1) * TT / gridDim.x;
+    const int64_t row_begin = t0 * ST;
+    const int64_t row_end = t1 * ST < rows ? t1 * ST : rows;
+    const int ntiles = (int)(t1 - t0);
+    uint8_t* buf = smem + wave * S::kBufBytes;
+    float* part = reinterpret_cast<float*>(smem + nw * S::kBufBytes);            // [2][C][nsl][16][TP]
+    int* ctl = reinterpret_cast<int*>(part + (size_t)2 * C * nsl * 16 * TP);     // arrivals[2], generation[2]
+    if (tid < 4) ctl[tid] = 0;
+    __syncthreads();
+
+    const int64_t rest = row_bytes - (int64_t)s * S::kChunks * 16;
+    const int cs = rest / 16 < S::kChunks ? (int)(rest / 16) : S::kChunks;
+    const int nblk = (int)(rest / 34) < 16 ? (int)(rest / 34) : 16;
+    const int sbase = s * S::kChunks * 16;
+    const int rbytes = (int)row_bytes;
+
+    V4 afrag[16];
+    mfma_afrag<NT>(x, xoff, s * kSlice, cols, lane, g, afrag);
+    V4 ra[L];
+    mfma_issue(W, rbytes, row_begin, row_end, ntiles, 0, lane, cs, sbase, ra);
+    for (int c = 0; c * C < ntiles; ++c) {
+        const int pb = c & 1;
+        if (c >= 2) {  // chunk c - 2 (same buffer) must have been summed
+            while (__atomic_load_n(&ctl[2 + pb], __ATOMIC_ACQUIRE) < (c >> 1)) __builtin_amdgcn_s_sleep(1);
+        }
+        const int tend = (c + 1) * C < ntiles ? (c + 1) * C : ntiles;
+        for (int t = c * C; t < tend; ++t)
+            mfma_tile_q8<NT>(W, rbytes, row_begin, row_end, ntiles, t, 1, cs, sbase, ra, buf, part, afrag, lane, n, g,
+                             s, nsl, nblk, pb * C + (t - c * C));
+        int last = 0;
+        if (lane == 0) last = __atomic_fetch_add(&ctl[pb], 1, __ATOMIC_ACQ_REL) == nw - 1;
+        last = __shfl(last, 0, 64);
+        if (last) {  // every wave's partials of chunk c are in: sum the slices in order
+            const int64_t r0 = row_begin + (int64_t)c * C * ST;
+            const int nr = (int)((row_end - r0) < (int64_t)C * ST ? (row_end - r0) : (int64_t)C * ST);
+            for (int o = lane; o < nr * NT; o += 64) {
+                const int rr = o / NT, t = o % NT;
+                const float* base = part + (((size_t)(pb * C + rr / ST) * nsl) * 16 + rr % ST) * TP + t;
+                float sum = base[0];
+                for (int w = 1; w < nsl; ++w) sum = sum + base[(size_t)w * 16 * TP];
+                out(t, r0 + rr, sum);
+            }
+            if (lane == 0) {
+                __atomic_store_n(&ctl[pb], 0, __ATOMIC_RELAXED);
+                __atomic_fetch_add(&ctl[2 + pb], 1, __ATOMIC_RELEASE);
+            }
+        }
+    }
+    wait_vmcnt<0>();  // the last (empty) prefetch returns before the wave ends
 }
 
 // ---------------------------------------------------------------- kernels
@@ -1216,6 +1330,17 @@ __global__ void __launch_bounds__(64 * kMaxWaves) qgemv_units_kernel(DenseArgs a
     const int64_t rows = a.rows;
     unit_rows<FMT, T, D>(a.W, a.row_bytes, a.cols, a.nslices, a.x, row_begin, row_end,
                          [=](int t, int64_t row, float v) { y[t * rows + row] = v; });
+}
+
+template <int T>
+__global__ void __launch_bounds__(64 * kMaxWaves) qgemv_mfma_persist_kernel(DenseArgs a) {
+    int64_t xoff[T];
+#pragma unroll
+    for (int t = 0; t < T; ++t) xoff[t] = (int64_t)t * a.cols;
+    float* __restrict__ y = a.y;
+    const int64_t rows = a.rows;
+    mfma_persist_q8<T>(a.W, a.rows, a.row_bytes, a.cols, a.nslices, a.rows_per_wg / 16, a.x, xoff,
+                       [=](int t, int64_t row, float v) { y[t * rows + row] = v; });
 }
 
 template <int T>
@@ -1520,6 +1645,16 @@ int launch_dense(int fmt, int T, const Tile& tile, const DenseArgs& a, void* str
 
 int launch_stream(int fmt, int T, const Tile& tile, const DenseArgs& a, void* stream) {
     DenseFn fn;
+    if (tile.mfma == 2) {  // persistent: one workgroup per CU (at most one per 16-row tile)
+        if (fmt != QG_FMT_Q8_0 || tile.rows_per_batch != 8 || tile.waves_per_wg != a.nslices) return (int)hipErrorInvalidValue;
+        fn = T == 1 ? qgemv_mfma_persist_kernel<1> : T == 2 ? qgemv_mfma_persist_kernel<2>
+           : T == 3 ? qgemv_mfma_persist_kernel<3> : qgemv_mfma_persist_kernel<4>;
+        const int64_t tiles = (a.rows + 15) / 16;
+        const int64_t nwg = tiles < kPersistGrid ? tiles : kPersistGrid;
+        hipLaunchKernelGGL(fn, dim3((unsigned)nwg), dim3(64 * tile.waves_per_wg), mfma_persist_lds_bytes(tile, T),
+                           (hipStream_t)stream, a);
+        return (int)hipGetLastError();
+    }
     if (tile.mfma)
         fn = tile.rows_per_batch != 8 ? nullptr
            : fmt == QG_FMT_Q8_0 ? mfma_for<QG_FMT_Q8_0>(T)

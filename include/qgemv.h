@@ -50,8 +50,11 @@
  * multiple of 2*rb), k the kernel kind: d (each lane loads its own bytes), s
  * (rows streamed through LDS via registers; needs rows of a multiple of 16
  * bytes), l<D> (streamed by direct-to-LDS loads, D = 2, 3, 4 or 6 tiles in
- * flight per wave; rb 4) or m (as s, contracted on the matrix cores; Q8_0 with
- * rb 8 only).  A malformed or out-of-set value makes every call of that format
+ * flight per wave; rb 4; L<D> the same with x staged apart), u<D> (as l, waves
+ * take equal shares of (slice, tile) units; any nw), m (as s, contracted on the
+ * matrix cores; Q8_0 with rb 8 only) or p (m in persistent form: one workgroup
+ * per CU, nw = the k slices, rw = the chunk of rows whose partial sums are
+ * buffered).  A malformed or out-of-set value makes every call of that format
  * return QG_EINVAL.
  */
 #ifndef QGEMV_H
@@ -114,9 +117,10 @@ int qg_unpack_q4_0(int64_t rows, int64_t cols, const void* in, uint16_t* d_bits,
 
 /* The tile a call with these arguments would use (after QGEMV_TILE):
  * out_tile = {lanes_per_row, rows_per_batch, waves_per_wg, k_slice, rows_per_wg, mfma, kind, depth}
- * (kind 0: direct loads, 1: streamed through LDS via registers, 2: streamed by
- * direct-to-LDS loads with `depth` tiles in flight per wave; mfma 1: matrix-core
- * contraction). */
+ * (kind 0: direct loads, 1: streamed through LDS via registers, 2 / 3: streamed
+ * by direct-to-LDS loads with `depth` tiles in flight per wave (3: x staged
+ * apart), 4: unit-balanced direct-to-LDS; mfma 1: matrix-core contraction,
+ * 2: its persistent form). */
 int qg_query_tile(int fmt, int64_t rows, int64_t cols, int T, int out_tile[QG_TILE_FIELDS]);
 
 /* Static description of a status code (never NULL). */

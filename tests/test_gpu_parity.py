@@ -337,6 +337,36 @@ def test_mfma_x_pieces_full_range(torch, orc, monkeypatch):
     assert_parity(y, ref, bound, "mfma x pieces")
 
 
+def test_mfma_persistent_agrees_bitwise(torch, orc, monkeypatch):
+    """The persistent matrix-core kernel (one workgroup per CU, chunked partial
+    sums summed by the last-arriving wave) gives the bits of the per-workgroup
+    matrix-core kernel, and matches the oracle, on ragged and small shapes."""
+    shapes = [(1, 256), (17, 768), (67, 2560), (300, 1024), (2560, 2560), (10240, 2560), (2560, 6144), (4099, 512)]
+    for rows, cols in shapes:
+        rng = np.random.default_rng(rows + 7 * cols)
+        W = I.weights(rng, Q8, rows, cols)
+        x = I.activations(rng, cols)
+        Wd = dev(torch, W)
+        for chunk in (16, 128):
+            monkeypatch.setenv("QGEMV_TILE", mfma_tile(cols, 32))
+            ref = gpu_gemv(torch, Q8, Wd, x, rows)
+            nsl = -(-cols // 512)
+            monkeypatch.setenv("QGEMV_TILE", f"q8_0:8,{nsl},{chunk},p")
+            say(f"[persist] {rows}x{cols} chunk={chunk}")
+            y = check_dense(torch, orc, Q8, rows, cols, W, x, f"persist {rows}x{cols} chunk={chunk}")
+            assert np.array_equal(y, ref), (rows, cols, chunk)
+
+
+def test_mfma_persistent_lm_head_sampled(torch, orc, monkeypatch):
+    name = "c4_q8_0_248320x5120"
+    c = I.dense_case(name)
+    rows = c["rows"]
+    monkeypatch.setenv("QGEMV_TILE", "q8_0:8,10,128,p")
+    rng = np.random.default_rng(654)
+    sel = np.unique(np.concatenate([rng.choice(rows, 2000, replace=False), [0, 15, 16, rows - 17, rows - 1]]))
+    check_dense(torch, orc, c["fmt"], rows, c["cols"], c["W"], c["x"], f"persist {name}", sel=sel)
+
+
 # ---------------------------------------------------------- grouped experts
 def grouped_check(torch, orc, fmt, n_experts, rows, cols, ids, W, x, what):
     say(f"[{what}] fmt={NAMES[fmt]} experts={n_experts} rows={rows} cols={cols} ids={ids.tolist()}")
