@@ -69,8 +69,12 @@ def kernel_name(tile, T):
     """Device symbol of the kernel a call with ``tile`` launches (Q8_0)."""
     if tile["kind"] in (2, 3):
         return f"qgemv_dma_kernel<0, {T}, {2 * tile['rows_per_batch']}, {tile['depth']}, {str(tile['kind'] == 3).lower()}>"
+    if tile["kind"] == 1 and tile["mfma"] == 2:
+        return f"qgemv_mfma_persist_kernel<{T}>"
     if tile["kind"] == 1 and tile["mfma"]:
         return f"qgemv_mfma_q8_kernel<{T}>"
+    if tile["kind"] == 4:
+        return f"qgemv_units_kernel<0, {T}, {tile['depth']}>"
     if tile["kind"] == 1:
         return f"qgemv_stream_kernel<0, {T}, {2 * tile['rows_per_batch']}>"
     one_shot = str(tile["rows_per_wg"] == 2 * tile["rows_per_batch"]).lower()
