@@ -189,6 +189,21 @@ def other_workloads(torch, stream):
             res[str(T)] = dict(us_per_call=round(us, 3), gbs=round(nb / us / 1e3, 1),
                                pct_peak=round(100 * nb / us / 1e3 / HBM_PEAK_GBS, 1),
                                tile=ops.query_tile(I.FMT_NAMES[fmt], rows, cols, T))
+        if name == "c4_q8_0_248320x5120":  # the fused LM-head argmax (y never written)
+            idx = torch.empty(4, dtype=torch.int32, device="cuda")
+            val = torch.empty(4, device="cuda")
+            work = torch.empty(4, dtype=torch.int64, device="cuda")
+            am = {}
+            for T in (1, 2, 3, 4):
+                def launch(i, T=T):
+                    st = _lib.qgemv_argmax(fmt, rows, cols, T, ring[i % len(ring)].data_ptr(), x.data_ptr(),
+                                           work.data_ptr(), idx.data_ptr(), val.data_ptr(), sp)
+                    if st:
+                        _lib.check(st, "argmax")
+                us = time_entry(torch, stream, launch, calls)
+                am[str(T)] = dict(us_per_call=round(us, 3), gbs=round(nb / us / 1e3, 1),
+                                  pct_peak=round(100 * nb / us / 1e3 / HBM_PEAK_GBS, 1))
+            out["c4_argmax_fused"] = dict(weight_bytes_per_call=nb, calls=calls, per_T=am)
         out[name] = dict(weight_bytes_per_call=nb, calls=calls, ring_copies=len(ring), per_T=res)
         del ring
     # grouped experts: 256 Q4_0 experts of 512 x 2560; each token picks 10 distinct

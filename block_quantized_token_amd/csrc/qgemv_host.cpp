@@ -313,6 +313,58 @@ int run_dense(int fmt, int64_t rows, int64_t cols, int T, const void* W, const f
     return ok();
 }
 
+int run_argmax(int fmt, int64_t rows, int64_t cols, int T, const void* W, const float* x, void* work, int32_t* idx,
+               float* val, void* stream) {
+    int64_t rbytes = 0;
+    int st = check_common(fmt, rows, cols, T, W, x, val, &rbytes);
+    if (st) return st;
+    if (!work || !idx) return fail(QG_EINVAL, "null pointer (work=%p idx=%p)", work, (void*)idx);
+    if (!aligned(work, 8) || !aligned(idx, 4)) return fail(QG_EALIGN, "work must be 8-byte and idx 4-byte aligned");
+    const size_t wbytes = (size_t)(rbytes * rows), xbytes = (size_t)T * cols * 4;
+    const void* outs[3] = {work, idx, val};
+    const size_t outb[3] = {(size_t)T * 8, (size_t)T * 4, (size_t)T * 4};
+    for (int i = 0; i < 3; ++i) {
+        if (overlap(outs[i], outb[i], W, wbytes) || overlap(outs[i], outb[i], x, xbytes))
+            return fail(QG_EINVAL, "an output overlaps W or x");
+        for (int j = 0; j < i; ++j)
+            if (overlap(outs[i], outb[i], outs[j], outb[j])) return fail(QG_EINVAL, "work, idx and val overlap");
+    }
+    Tile tile;
+    if ((st = pick_tile(fmt, rows, cols, T, &tile))) return st;
+    const int64_t nsl = (cols + kSlice - 1) / kSlice;
+    // The fused argmax runs on the persistent matrix-core, LDS-DMA (depth 2..4),
+    // register-streamed (8-row tiles) and direct (rb 2) kernels, all with the
+    // per-row arithmetic of the dense call; other tiles map onto one of these.
+    const bool persist = tile.kind == 1 && tile.mfma == 2;
+    if ((tile.kind == 2 || tile.kind == 3) && tile.depth > 4) {
+        tile.depth = 4;
+        if (tile.kind == 2 && !dma_supported(fmt, T, 4, 4, false)) tile.kind = 3;
+        if (dma_lds_bytes(fmt, tile, T, (int)nsl) > kMaxLds) tile.kind = 0;
+    }
+    if (tile.kind == 4 || (tile.kind == 1 && tile.mfma == 1)) tile.kind = 0;
+    if (tile.kind == 1 && !persist && (tile.rows_per_batch != 4 || !stream_supported(fmt, T, 4))) tile.kind = 0;
+    if (tile.kind == 0) {  // direct, rb 2, one wave per slice when the slices fit a workgroup
+        tile.mfma = 0;
+        tile.depth = 0;
+        tile.rows_per_batch = 2;
+        tile.waves_per_wg = (int)(nsl < kMaxWaves ? nsl : kMaxWaves);
+        tile.rows_per_wg = one_shot(Tile{32, 2, tile.waves_per_wg, kSlice, 4, 0, 0, 0}, (int)nsl) ? 4 : 16;
+    }
+    DenseArgs a;
+    a.W = (const uint8_t*)W;
+    a.x = x;
+    a.y = nullptr;  // never written
+    a.rows = rows;
+    a.row_bytes = rbytes;
+    a.cols = (int)cols;
+    a.nslices = (int)nsl;
+    a.rows_per_wg = tile.rows_per_wg;
+    if ((rows + tile.rows_per_wg - 1) / tile.rows_per_wg > 0x7FFFFFFF) return fail(QG_EUNSUPPORTED, "grid too large");
+    const int err = launch_argmax(fmt, T, tile, a, work, idx, val, stream);
+    if (err) return fail(QG_EHIP, "kernel launch failed: %s", hip_error_name(err));
+    return ok();
+}
+
 }  // namespace
 }  // namespace qg
 
@@ -330,6 +382,11 @@ int qgemv_q4_0(int64_t rows, int64_t cols, int T, const void* W, const float* x,
 
 int qgemv_bf16(int64_t rows, int64_t cols, int T, const void* W, const float* x, float* y, void* stream) {
     return run_dense(QG_FMT_BF16, rows, cols, T, W, x, y, stream);
+}
+
+int qgemv_argmax(int fmt, int64_t rows, int64_t cols, int T, const void* W, const float* x, void* work, int32_t* idx,
+                 float* val, void* stream) {
+    return run_argmax(fmt, rows, cols, T, W, x, work, idx, val, stream);
 }
 
 int qgemv_grouped_experts(int fmt, int64_t n_experts, int64_t rows, int64_t cols, int T, int topk,

@@ -153,6 +153,9 @@ int launch_dense(int fmt, int T, const Tile& tile, const DenseArgs& a, void* str
 int launch_stream(int fmt, int T, const Tile& tile, const DenseArgs& a, void* stream);
 int launch_dma(int fmt, int T, const Tile& tile, const DenseArgs& a, void* stream);
 int launch_units(int fmt, int T, const Tile& tile, const DenseArgs& a, void* stream);
+// Fused argmax: fills work (uint64[T]), runs the mat-vec, writes idx/val (3 launches).
+int launch_argmax(int fmt, int T, const Tile& tile, const DenseArgs& a, void* work, int32_t* idx, float* val,
+                  void* stream);
 int launch_grouped(int fmt, const Tile& tile, const GroupedArgs& a, void* stream);
 const char* hip_error_name(int err);
 

@@ -30,6 +30,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "qgemv_internal.h"
 
 namespace qg {
@@ -354,7 +356,7 @@ __device__ __forceinline__ void reduce_batch(float (&acc)[RB][pad_pow2(NT)], int
 template <int FMT, int NT, int RB, bool ONE_SHOT, class Out>
 __device__ __forceinline__ void gemv_rows(const uint8_t* __restrict__ W, int64_t row_bytes, int cols, int nslices,
                                           const float* __restrict__ x, const int64_t (&xoff)[NT], int64_t row_begin,
-                                          int64_t row_end, Out out) {
+                                          int64_t row_end, Out&& out) {
     using F = Fmt<FMT>;
     using Raw = typename F::Raw;
     constexpr int TP = pad_pow2(NT);
@@ -600,7 +602,7 @@ __device__ __forceinline__ void stream_tile(const uint8_t* __restrict__ W, int64
 template <int FMT, int NT, int ST, class Out>
 __device__ __forceinline__ void stream_rows(const uint8_t* __restrict__ W, int64_t row_bytes, int cols, int nsl,
                                             const float* __restrict__ x, const int64_t (&xoff)[NT], int64_t row_begin,
-                                            int64_t row_end, Out out) {
+                                            int64_t row_end, Out&& out) {
     using F = Fmt<FMT>;
     using S = StreamShape<FMT, ST>;
     constexpr int TP = pad_pow2(NT);
@@ -766,7 +768,7 @@ __device__ __forceinline__ void dma_prefetch(const uint8_t* __restrict__ W, int6
 template <int FMT, int NT, int ST, int D, bool XSEP, class Out, bool PRE = false>
 __device__ __forceinline__ void dma_rows(const uint8_t* __restrict__ W, int64_t row_bytes, int cols, int nsl,
                                          const float* __restrict__ x, const int64_t (&xoff)[NT], int64_t row_begin,
-                                         int64_t row_end, Out out) {
+                                         int64_t row_end, Out&& out) {
     static_assert(!PRE || XSEP, "prefetched tiles need x staged apart");
     using F = Fmt<FMT>;
     using S = StreamShape<FMT, ST>;
@@ -1216,7 +1218,7 @@ __device__ __forceinline__ void mfma_rows_q8(const uint8_t* __restrict__ W, int6
 template <int NT, class Out>
 __device__ __forceinline__ void mfma_persist_q8(const uint8_t* __restrict__ W, int64_t rows, int64_t row_bytes, int cols,
                                                 int nsl, int C, const float* __restrict__ x, const int64_t (&xoff)[NT],
-                                                Out out) {
+                                                Out&& out) {
     constexpr int FMT = QG_FMT_Q8_0;
     constexpr int ST = 16;
     using S = StreamShape<FMT, ST>;
@@ -1282,6 +1284,64 @@ __device__ __forceinline__ void mfma_persist_q8(const uint8_t* __restrict__ W, i
     wait_vmcnt<0>();  // the last (empty) prefetch returns before the wave ends
 }
 
+// ------------------------------------------------------ fused argmax over rows
+// The LM-head step right after the mat-vec (the drafter's LM head in the mlxcel
+// drafter-cost issue): per token, the row with the largest y and that y, with y
+// never written.  A (value, row) pair is packed into one 64-bit key whose
+// unsigned order is (value, then lower row first): the value's bits mapped to an
+// order-preserving unsigned integer in the high half, 0xFFFFFFFF - row in the
+// low half.  Each thread keeps its best key per token, each wave reduces its
+// lanes' keys, and one 64-bit atomic max per wave and token merges workgroups;
+// max is order-independent, so the result does not depend on scheduling.
+__device__ __forceinline__ uint64_t argmax_key(float v, int64_t row) {
+    const uint32_t u = __builtin_bit_cast(uint32_t, v);
+    const uint32_t ord = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+    return ((uint64_t)ord << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)row);
+}
+
+template <int NT>
+struct ArgmaxOut {
+    uint64_t best[NT];
+    __device__ ArgmaxOut() {
+#pragma unroll
+        for (int t = 0; t < NT; ++t) best[t] = 0;
+    }
+    __device__ void operator()(int t, int64_t row, float v) {
+        const uint64_t k = argmax_key(v, row);
+#pragma unroll
+        for (int j = 0; j < NT; ++j)  // t varies across lanes: no dynamic indexing
+            if (j == t && k > best[j]) best[j] = k;
+    }
+    // wave maximum of each token's key, merged into work[t] by lane 0
+    __device__ void merge(unsigned long long* work) {
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+            uint64_t k = best[t];
+#pragma unroll
+            for (int m = 32; m >= 1; m >>= 1) {
+                const uint32_t lo = __shfl_xor((uint32_t)k, m, 64), hi = __shfl_xor((uint32_t)(k >> 32), m, 64);
+                const uint64_t o = ((uint64_t)hi << 32) | lo;
+                k = o > k ? o : k;
+            }
+            if ((threadIdx.x & 63) == 0 && k != 0) atomicMax(work + t, (unsigned long long)k);
+        }
+    }
+};
+
+__global__ void qgemv_argmax_init_kernel(unsigned long long* work, int T) {
+    if ((int)threadIdx.x < T) work[threadIdx.x] = 0;
+}
+
+__global__ void qgemv_argmax_finish_kernel(const unsigned long long* work, int32_t* idx, float* val, int T) {
+    const int t = threadIdx.x;
+    if (t >= T) return;
+    const uint64_t k = work[t];
+    const uint32_t ord = (uint32_t)(k >> 32);
+    const uint32_t u = (ord & 0x80000000u) ? (ord & 0x7FFFFFFFu) : ~ord;
+    idx[t] = (int32_t)(0xFFFFFFFFu - (uint32_t)k);
+    val[t] = __builtin_bit_cast(float, u);
+}
+
 // ---------------------------------------------------------------- kernels
 template <int FMT, int T, int RB, bool ONE_SHOT>
 __global__ void __launch_bounds__(64 * kMaxWaves) qgemv_dense_kernel(DenseArgs a) {
@@ -1341,6 +1401,52 @@ __global__ void __launch_bounds__(64 * kMaxWaves) qgemv_mfma_persist_kernel(Dens
     const int64_t rows = a.rows;
     mfma_persist_q8<T>(a.W, a.rows, a.row_bytes, a.cols, a.nslices, a.rows_per_wg / 16, a.x, xoff,
                        [=](int t, int64_t row, float v) { y[t * rows + row] = v; });
+}
+
+template <int FMT, int T, int ST, int D, bool XSEP>
+__global__ void __launch_bounds__(64 * kMaxWaves) qgemv_dma_argmax_kernel(DenseArgs a, unsigned long long* work) {
+    const int64_t row_begin = (int64_t)blockIdx.x * a.rows_per_wg;
+    const int64_t row_end = row_begin + a.rows_per_wg < a.rows ? row_begin + a.rows_per_wg : a.rows;
+    int64_t xoff[T];
+#pragma unroll
+    for (int t = 0; t < T; ++t) xoff[t] = (int64_t)t * a.cols;
+    ArgmaxOut<T> best;
+    dma_rows<FMT, T, ST, D, XSEP>(a.W, a.row_bytes, a.cols, a.nslices, a.x, xoff, row_begin, row_end, best);
+    best.merge(work);
+}
+
+template <int T>
+__global__ void __launch_bounds__(64 * kMaxWaves) qgemv_persist_argmax_kernel(DenseArgs a, unsigned long long* work) {
+    int64_t xoff[T];
+#pragma unroll
+    for (int t = 0; t < T; ++t) xoff[t] = (int64_t)t * a.cols;
+    ArgmaxOut<T> best;
+    mfma_persist_q8<T>(a.W, a.rows, a.row_bytes, a.cols, a.nslices, a.rows_per_wg / 16, a.x, xoff, best);
+    best.merge(work);
+}
+
+template <int FMT, int T, bool ONE_SHOT>
+__global__ void __launch_bounds__(64 * kMaxWaves) qgemv_dense_argmax_kernel(DenseArgs a, unsigned long long* work) {
+    const int64_t row_begin = (int64_t)blockIdx.x * a.rows_per_wg;
+    const int64_t row_end = row_begin + a.rows_per_wg < a.rows ? row_begin + a.rows_per_wg : a.rows;
+    int64_t xoff[T];
+#pragma unroll
+    for (int t = 0; t < T; ++t) xoff[t] = (int64_t)t * a.cols;
+    ArgmaxOut<T> best;
+    gemv_rows<FMT, T, 2, ONE_SHOT>(a.W, a.row_bytes, a.cols, a.nslices, a.x, xoff, row_begin, row_end, best);
+    best.merge(work);
+}
+
+template <int FMT, int T>
+__global__ void __launch_bounds__(64 * kMaxWaves) qgemv_stream_argmax_kernel(DenseArgs a, unsigned long long* work) {
+    const int64_t row_begin = (int64_t)blockIdx.x * a.rows_per_wg;
+    const int64_t row_end = row_begin + a.rows_per_wg < a.rows ? row_begin + a.rows_per_wg : a.rows;
+    int64_t xoff[T];
+#pragma unroll
+    for (int t = 0; t < T; ++t) xoff[t] = (int64_t)t * a.cols;
+    ArgmaxOut<T> best;
+    stream_rows<FMT, T, 8>(a.W, a.row_bytes, a.cols, a.nslices, a.x, xoff, row_begin, row_end, best);
+    best.merge(work);
 }
 
 template <int T>
@@ -1467,7 +1573,7 @@ __device__ __forceinline__ void grouped_dma_run(const GroupedArgs& a, int e, uin
                                       for (int j = 0; j < topk; ++j)
                                           if (ids[t * topk + j] == e) y[((int64_t)t * topk + j) * rows + row] = v;
                                   };
-    dma_rows<FMT, NE, 8, D, true, decltype(out), true>(a.W + (int64_t)e * a.expert_bytes, a.row_bytes, a.cols,
+    dma_rows<FMT, NE, 8, D, true, decltype(out)&, true>(a.W + (int64_t)e * a.expert_bytes, a.row_bytes, a.cols,
                                                       a.nslices, a.x, xoff, row_begin, row_end, out);
 }
 
@@ -1693,6 +1799,100 @@ int launch_units(int fmt, int T, const Tile& tile, const DenseArgs& a, void* str
     const int64_t nwg = (a.rows + tile.rows_per_wg - 1) / tile.rows_per_wg;
     hipLaunchKernelGGL(fn, dim3((unsigned)nwg), dim3(64 * tile.waves_per_wg), units_lds_bytes(fmt, tile, T, a.cols),
                        (hipStream_t)stream, a);
+    return (int)hipGetLastError();
+}
+
+using ArgmaxFn = void (*)(DenseArgs, unsigned long long*);
+
+template <int FMT, int T>
+ArgmaxFn argmax_dma_entry(int depth, bool xsep) {
+    auto pick = [&](auto dtag) -> ArgmaxFn {
+        constexpr int D = decltype(dtag)::value;
+        if (xsep) return qgemv_dma_argmax_kernel<FMT, T, 8, D, true>;
+        if constexpr (dma_x_slots<FMT, 8, T>() < D) return qgemv_dma_argmax_kernel<FMT, T, 8, D, false>;
+        return nullptr;
+    };
+    switch (depth) {
+    case 2: return pick(std::integral_constant<int, 2>{});
+    case 3: return pick(std::integral_constant<int, 3>{});
+    case 4: return pick(std::integral_constant<int, 4>{});
+    default: return nullptr;
+    }
+}
+
+template <int FMT>
+ArgmaxFn argmax_dma_for(int T, int depth, bool xsep) {
+    switch (T) {
+    case 1: return argmax_dma_entry<FMT, 1>(depth, xsep);
+    case 2: return argmax_dma_entry<FMT, 2>(depth, xsep);
+    case 3: return argmax_dma_entry<FMT, 3>(depth, xsep);
+    default: return argmax_dma_entry<FMT, 4>(depth, xsep);
+    }
+}
+
+template <int FMT>
+ArgmaxFn argmax_stream_for(int T) {
+    switch (T) {
+    case 1: return qgemv_stream_argmax_kernel<FMT, 1>;
+    case 2: return qgemv_stream_argmax_kernel<FMT, 2>;
+    case 3:
+        if constexpr (FMT != QG_FMT_BF16) return qgemv_stream_argmax_kernel<FMT, 3>;
+        return nullptr;
+    default:
+        if constexpr (FMT != QG_FMT_BF16) return qgemv_stream_argmax_kernel<FMT, 4>;
+        return nullptr;
+    }
+}
+
+template <int FMT>
+ArgmaxFn argmax_dense_for(int T, bool os) {
+    switch (T) {
+    case 1: return os ? qgemv_dense_argmax_kernel<FMT, 1, true> : qgemv_dense_argmax_kernel<FMT, 1, false>;
+    case 2: return os ? qgemv_dense_argmax_kernel<FMT, 2, true> : qgemv_dense_argmax_kernel<FMT, 2, false>;
+    case 3: return os ? qgemv_dense_argmax_kernel<FMT, 3, true> : qgemv_dense_argmax_kernel<FMT, 3, false>;
+    default: return os ? qgemv_dense_argmax_kernel<FMT, 4, true> : qgemv_dense_argmax_kernel<FMT, 4, false>;
+    }
+}
+
+int launch_argmax(int fmt, int T, const Tile& tile, const DenseArgs& a, void* work, int32_t* idx, float* val,
+                  void* stream) {
+    ArgmaxFn fn = nullptr;
+    int64_t nwg = 0;
+    size_t lds = 0;
+    if (tile.kind == 1 && tile.mfma == 2 && fmt == QG_FMT_Q8_0 && tile.rows_per_batch == 8 &&
+        tile.waves_per_wg == a.nslices) {
+        fn = T == 1 ? qgemv_persist_argmax_kernel<1> : T == 2 ? qgemv_persist_argmax_kernel<2>
+           : T == 3 ? qgemv_persist_argmax_kernel<3> : qgemv_persist_argmax_kernel<4>;
+        const int64_t tiles = (a.rows + 15) / 16;
+        nwg = tiles < kPersistGrid ? tiles : kPersistGrid;
+        lds = mfma_persist_lds_bytes(tile, T);
+    } else if ((tile.kind == 2 || tile.kind == 3) && tile.rows_per_batch == 4) {
+        const bool xsep = tile.kind == 3;
+        fn = fmt == QG_FMT_Q8_0 ? argmax_dma_for<QG_FMT_Q8_0>(T, tile.depth, xsep)
+           : fmt == QG_FMT_Q4_0 ? argmax_dma_for<QG_FMT_Q4_0>(T, tile.depth, xsep)
+                                : argmax_dma_for<QG_FMT_BF16>(T, tile.depth, xsep);
+        nwg = (a.rows + tile.rows_per_wg - 1) / tile.rows_per_wg;
+        lds = dma_lds_bytes(fmt, tile, T, a.nslices);
+    } else if (tile.kind == 1 && !tile.mfma && tile.rows_per_batch == 4 && stream_supported(fmt, T, 4)) {
+        fn = fmt == QG_FMT_Q8_0 ? argmax_stream_for<QG_FMT_Q8_0>(T)
+           : fmt == QG_FMT_Q4_0 ? argmax_stream_for<QG_FMT_Q4_0>(T)
+                                : argmax_stream_for<QG_FMT_BF16>(T);
+        nwg = (a.rows + tile.rows_per_wg - 1) / tile.rows_per_wg;
+        lds = stream_lds_bytes(fmt, tile, T, a.nslices);
+    } else if (tile.kind == 0 && tile.rows_per_batch == 2) {
+        const bool os = one_shot(tile, a.nslices);
+        fn = fmt == QG_FMT_Q8_0 ? argmax_dense_for<QG_FMT_Q8_0>(T, os)
+           : fmt == QG_FMT_Q4_0 ? argmax_dense_for<QG_FMT_Q4_0>(T, os)
+                                : argmax_dense_for<QG_FMT_BF16>(T, os);
+        nwg = (a.rows + tile.rows_per_wg - 1) / tile.rows_per_wg;
+        lds = lds_bytes(tile, T);
+    }
+    if (!fn) return (int)hipErrorInvalidValue;
+    unsigned long long* w = (unsigned long long*)work;
+    hipLaunchKernelGGL(qgemv_argmax_init_kernel, dim3(1), dim3(64), 0, (hipStream_t)stream, w, T);
+    hipLaunchKernelGGL(fn, dim3((unsigned)nwg), dim3(64 * tile.waves_per_wg), lds, (hipStream_t)stream, a, w);
+    hipLaunchKernelGGL(qgemv_argmax_finish_kernel, dim3(1), dim3(64), 0, (hipStream_t)stream, (const unsigned long long*)w,
+                       idx, val, T);
     return (int)hipGetLastError();
 }
 

@@ -45,6 +45,30 @@ def gemv(fmt, W, x, rows: int, out=None):
     return out
 
 
+def argmax(fmt, W, x, rows: int, work=None):
+    """(idx int32 [T], val fp32 [T]): per token, the row with the largest W . x[t]
+    (lowest row on ties) and its value, without writing the [T][rows] product."""
+    import torch
+    f = _fmt(fmt)
+    _require_device(W, "W")
+    _require_device(x, "x")
+    if x.dtype != torch.float32 or x.dim() != 2:
+        raise ValueError("x must be fp32 [T][cols]")
+    T, cols = x.shape
+    need = _lib.qg_packed_bytes(f, rows, cols)
+    if need == 0 or W.numel() * W.element_size() < need:
+        raise ValueError(f"W holds {W.numel() * W.element_size()} bytes, the shape needs {need}")
+    if work is None:
+        work = torch.empty(T, dtype=torch.int64, device=x.device)
+    _require_device(work, "work")
+    idx = torch.empty(T, dtype=torch.int32, device=x.device)
+    val = torch.empty(T, dtype=torch.float32, device=x.device)
+    st = _lib.qgemv_argmax(f, rows, cols, T, W.data_ptr(), x.data_ptr(), work.data_ptr(), idx.data_ptr(), val.data_ptr(),
+                           _stream(torch, x.device))
+    _lib.check(st, "qgemv_argmax")
+    return idx, val
+
+
 def grouped_experts(fmt, W, x, ids, n_experts: int, rows: int, out=None):
     """y[T][topk][rows] = W_{ids[t][j]} . x[t]; ids int32 [T][topk] on the device."""
     import torch

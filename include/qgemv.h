@@ -102,6 +102,24 @@ int qgemv_bf16(int64_t rows, int64_t cols, int T, const void* W, const float* x,
 int qgemv_grouped_experts(int fmt, int64_t n_experts, int64_t rows, int64_t cols, int T, int topk,
                           const int32_t* ids, const void* W, const float* x, float* y, void* stream);
 
+/*
+ * Fused mat-vec + argmax over rows, for the LM head that follows the verify
+ * pass (the drafter-cost issue, "perf(speculative): cut the MTP drafter's
+ * per-step cost...", fused LM-head / argmax proposal): for each t < T,
+ *     idx[t] = the row r with the largest y[t][r] = sum_k w[r][k] * x[t][k]
+ *              (ties: the lowest r),   val[t] = that y[t][r].
+ * y is never written.  W, x as for the dense entry points; work (DEVICE, 8-byte
+ * aligned, T uint64 values, contents overwritten), idx (DEVICE int32[T]) and
+ * val (DEVICE float[T]) belong to the caller and must not overlap W, x or one
+ * another.  Each y[t][r] is the same float the dense entry point computes for
+ * these arguments, so idx/val equal the argmax of its output.  Needs rows of a
+ * multiple of 16 bytes (else QG_EUNSUPPORTED).  Three kernel launches on
+ * `stream` (clear work, mat-vec with per-workgroup maxima merged by atomic
+ * max on work, unpack work into idx/val).
+ */
+int qgemv_argmax(int fmt, int64_t rows, int64_t cols, int T, const void* W, const float* x, void* work,
+                 int32_t* idx, float* val, void* stream);
+
 /* ---- host-only helpers (no GPU needed) ---------------------------------- */
 
 /* Packed bytes of a rows x cols matrix of fmt; 0 if the shape is invalid. */

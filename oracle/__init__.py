@@ -122,6 +122,15 @@ class Oracle:
             raise ValueError(f"oracle_gemv rc={rc}")
         return y, b
 
+    def argmax(self, fmt: int, rows: int, cols: int, W, x):
+        """The fused LM-head step written out: per token, the row with the largest
+        y (the lowest such row on ties) and that y, from the fp64 mat-vec above.
+        Returns (idx int64 [T], val fp64 [T], y, bound); y and bound are what the
+        acceptance test needs to tell near-ties apart."""
+        y, bound = self.gemv(fmt, rows, cols, W, x)
+        idx = np.argmax(y, axis=1)  # numpy returns the first (lowest) index of the maximum
+        return idx, y[np.arange(y.shape[0]), idx], y, bound
+
     def grouped(self, fmt: int, n_experts: int, rows: int, cols: int, ids, W, x):
         """Returns (y, bound), each fp64 [T][topk][rows]."""
         W = self._u8(W)

@@ -141,6 +141,27 @@ def test_grouped_argument_errors(lib, args, status):
     assert _lib.qgemv_grouped_experts(*args) == status, _lib.last_error()
 
 
+V0, K0 = 0x50000000, 0x60000000
+
+
+@pytest.mark.parametrize("args, status", [
+    ((0, 64, 256, 1, W0, X0, 0, I0, V0), _lib.QG_EINVAL),          # null work
+    ((0, 64, 256, 1, W0, X0, K0, 0, V0), _lib.QG_EINVAL),          # null idx
+    ((0, 64, 256, 1, W0, X0, K0, I0, 0), _lib.QG_EINVAL),          # null val
+    ((0, 64, 256, 5, W0, X0, K0, I0, V0), _lib.QG_EINVAL),         # T 5
+    ((7, 64, 256, 1, W0, X0, K0, I0, V0), _lib.QG_EINVAL),         # bad fmt
+    ((0, 64, 256, 1, W0, X0, K0 + 4, I0, V0), _lib.QG_EALIGN),     # work not 8-byte aligned
+    ((0, 64, 256, 1, W0, X0, K0, I0 + 2, V0), _lib.QG_EALIGN),     # idx misaligned
+    ((0, 64, 256, 2, W0, X0, K0, I0, I0 + 4), _lib.QG_EINVAL),     # val overlaps idx
+    ((0, 64, 256, 1, W0, X0, W0 + 8, I0, V0), _lib.QG_EINVAL),     # work inside W
+    ((0, 64, 256, 1, W0, X0, K0, X0, V0), _lib.QG_EINVAL),         # idx overlaps x
+])
+def test_argmax_argument_errors(lib, args, status):
+    assert _lib.qgemv_argmax(*args) == status, _lib.last_error()
+    assert _lib.last_error()
+
+
+
 def test_tile_query_and_override(lib, monkeypatch):
     monkeypatch.delenv("QGEMV_TILE", raising=False)
     t = ops.query_tile("q8_0", 10240, 2560, 1)

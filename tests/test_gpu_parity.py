@@ -367,6 +367,76 @@ def test_mfma_persistent_lm_head_sampled(torch, orc, monkeypatch):
     check_dense(torch, orc, c["fmt"], rows, c["cols"], c["W"], c["x"], f"persist {name}", sel=sel)
 
 
+# ------------------------------------------------------------- fused argmax
+def argmax_check(torch, orc, fmt, rows, cols, W, x, what, sel_oracle=True):
+    """Fused argmax against (a) the argmax of the dense call's own output, bit for
+    bit (same per-row arithmetic, lowest row on ties), and (b) the oracle: the
+    chosen row's exact y is within the error bounds of the true maximum."""
+    Wd, xd = dev(torch, W), dev(torch, x)
+    idx, val = ops.argmax(NAMES[fmt], Wd, xd, rows)
+    torch.cuda.synchronize()
+    idx, val = idx.cpu().numpy(), val.cpu().numpy()
+    y = ops.gemv(NAMES[fmt], Wd, xd, rows).cpu().numpy()
+    assert idx.tolist() == np.argmax(y, axis=1).tolist(), what
+    assert np.array_equal(val, y[np.arange(y.shape[0]), idx]), what
+    if sel_oracle:
+        oi, ov, yo, bo = orc.argmax(fmt, rows, cols, W, x)
+        tol = 1e-4 * bo + 1e-6
+        for t in range(x.shape[0]):
+            assert yo[t, idx[t]] >= ov[t] - (tol[t, idx[t]] + tol[t, oi[t]]), (what, t, idx[t], oi[t])
+            assert abs(val[t] - yo[t, idx[t]]) <= tol[t, idx[t]], (what, t)
+    return idx, val
+
+
+@pytest.mark.parametrize("name", ["c1_q8_0_2560x2560", "c2a_q8_0_10240x2560", "c2b_q8_0_2560x6144",
+                                  "c3_q4_0_8192x2560", "c3_bf16_8192x2560"])
+def test_argmax_configs(torch, orc, name):
+    c = I.dense_case(name)
+    for T in (1, 2, 3, 4):
+        say(f"[argmax] {name} T={T}")
+        argmax_check(torch, orc, c["fmt"], c["rows"], c["cols"], c["W"], c["x"][:T], f"{name} T={T}")
+
+
+def test_argmax_lm_head(torch, orc):
+    name = "c4_q8_0_248320x5120"
+    c = I.dense_case(name)
+    for T in (1, 4):
+        say(f"[argmax] {name} T={T}")
+        argmax_check(torch, orc, c["fmt"], c["rows"], c["cols"], c["W"], c["x"][:T], f"{name} T={T}", sel_oracle=T == 4)
+
+
+def test_argmax_ties_negatives_and_kinds(torch, orc, monkeypatch):
+    """Exact ties (duplicated largest rows: the lowest wins), all-negative outputs,
+    ragged row counts, and every kernel kind the fused argmax runs on."""
+    rng = np.random.default_rng(31)
+    for rows, cols in ((1, 256), (67, 512), (1000, 2560), (333, 736)):
+        W = I.weights(rng, Q8, rows, cols)
+        x = I.activations(rng, cols)
+        if rows > 10:  # copy the largest row of token 0 over two later rows and an earlier one
+            y0, _ = orc.gemv(Q8, rows, cols, W, x[:1])
+            best = int(np.argmax(y0[0]))
+            rb = I.packed_row_bytes(Q8, cols)
+            W = W.copy()
+            for r in (rows // 3, rows - 1, 2):
+                W[r * rb:(r + 1) * rb] = W[best * rb:(best + 1) * rb]
+        neg = -np.abs(x)  # a second activation pattern
+        for kind_tile in (None, "q8_0:4,{nsl},40,l3", "q8_0:4,{nsl},48,L2", "q8_0:4,{nsl},16,s", "q8_0:2,{nsl},4,d",
+                          "q8_0:8,{nsl},64,p"):
+            nsl = -(-cols // 512)
+            if kind_tile:
+                monkeypatch.setenv("QGEMV_TILE", kind_tile.format(nsl=nsl))
+            else:
+                monkeypatch.delenv("QGEMV_TILE", raising=False)
+            if kind_tile and cols % 256 and not kind_tile.endswith(",d"):
+                continue  # streamed kinds need 16-byte rows
+            what = f"{rows}x{cols} tile={kind_tile}"
+            say(f"[argmax] {what}")
+            idx, _ = argmax_check(torch, orc, Q8, rows, cols, W, x, what)
+            if rows > 10:
+                assert idx[0] == min(2, best), what
+            argmax_check(torch, orc, Q8, rows, cols, W, neg, what + " neg-x")
+
+
 # ---------------------------------------------------------- grouped experts
 def grouped_check(torch, orc, fmt, n_experts, rows, cols, ids, W, x, what):
     say(f"[{what}] fmt={NAMES[fmt]} experts={n_experts} rows={rows} cols={cols} ids={ids.tolist()}")

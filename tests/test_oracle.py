@@ -256,3 +256,39 @@ def test_pins_catch_planted_mistake(mutant):
         oracle_pkg.build(path, mutant=mutant)
         fails = pin_failures(oracle_pkg.Oracle(path))
     assert fails, f"mutant {mutant} ({MUTANTS[mutant]}) passed every pin"
+
+
+# ---------------------------------------------------------------- argmax
+def test_argmax_ties_take_the_lowest_row(orc):
+    """Rows 3 and 6 are the same largest row; rows 1 and 4 equal but smaller."""
+    rows, cols = 8, 64
+    d = np.full((rows, cols // 32), 0x3C00, dtype=np.uint16)           # scale 1
+    codes = np.zeros((rows, cols), dtype=np.int8)
+    codes[1, :] = 2
+    codes[3, :] = 5
+    codes[4, :] = 2
+    codes[6, :] = 5
+    W = I.pack_q8_0(d, codes)
+    x = np.ones((2, cols), dtype=np.float32)
+    x[1] = -1.0                                                         # token 1: every y <= 0, max is 0
+    idx, val, _, _ = orc.argmax(I.FMT_Q8_0, rows, cols, W, x)
+    assert idx.tolist() == [3, 0] and val.tolist() == [5.0 * cols, 0.0]
+
+
+def test_argmax_all_negative(orc):
+    rows, cols = 5, 32
+    d = np.full((rows, 1), 0x3C00, dtype=np.uint16)
+    codes = np.array([[-9] * 32, [-2] * 32, [-7] * 32, [-2] * 32, [-3] * 32], dtype=np.int8)
+    idx, val, _, _ = orc.argmax(I.FMT_Q8_0, rows, cols, I.pack_q8_0(d, codes), np.ones((1, cols), np.float32))
+    assert idx.tolist() == [1] and val.tolist() == [-64.0]
+
+
+def test_argmax_matches_brute_force(orc):
+    rng = np.random.default_rng(77)
+    rows, cols = 300, 512
+    W = I.weights(rng, I.FMT_Q4_0, rows, cols)
+    x = I.activations(rng, cols)
+    idx, val, _, _ = orc.argmax(I.FMT_Q4_0, rows, cols, W, x)
+    y = x.astype(np.float64) @ numpy_dequant(I.FMT_Q4_0, rows, cols, W).T
+    assert idx.tolist() == np.argmax(y, axis=1).tolist()
+    assert np.allclose(val, y.max(axis=1), rtol=0, atol=1e-9 * np.abs(y).max())
