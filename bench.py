@@ -50,7 +50,7 @@ def ring_of(torch, W: np.ndarray, min_bytes: int = RING_BYTES):
 
 
 def time_calls(torch, fmt, ring, x_dev, rows, T, calls, stream, y_dev):
-    """Back-to-back calls over the ring between two events on ``stream``; returns ms."""
+    """Back-to-back calls over the ring between two events on ``stream``; returns the (start, end) events."""
     entry = {0: _lib.qgemv_q8_0, 1: _lib.qgemv_q4_0, 2: _lib.qgemv_bf16}[fmt]
     cols = x_dev.shape[1]
     xp, yp, sp = x_dev.data_ptr(), y_dev.data_ptr(), stream.cuda_stream
@@ -308,12 +308,28 @@ def main():
     total_ms = sum(ms.values())
     value = args.steps * len(Ts) * nbytes / (total_ms * 1e-3) / 1e9
 
+    # after the timed region: 7 repeats per T (median, min, max of µs per call over
+    # runs of >= 2 ms each) and a cache-warm figure (one buffer, 256 MB MALL-resident)
+    reps = {}
+    n_rep = max(20, int(2e3 / max(1e-3, min(ms.values()) * 1e3 / args.steps)))
+    for T in Ts:
+        vals = []
+        for _ in range(7):
+            s_, e_ = time_calls(torch, fmt, ring, x_dev[:T], rows, T, n_rep, stream, y_dev)
+            torch.cuda.synchronize()
+            vals.append(s_.elapsed_time(e_) * 1e3 / n_rep)
+        s_, e_ = time_calls(torch, fmt, ring[:1], x_dev[:T], rows, T, n_rep, stream, y_dev)
+        torch.cuda.synchronize()
+        vals.sort()
+        reps[T] = dict(median=round(vals[3], 3), min=round(vals[0], 3), max=round(vals[-1], 3),
+                       warm_us=round(s_.elapsed_time(e_) * 1e3 / n_rep, 3), calls=n_rep)
+
     per_T = {}
     for T in Ts:
         us = ms[T] * 1e3 / args.steps
         per_T[str(T)] = dict(us_per_call=round(us, 3), gbs=round(nbytes / us / 1e3, 1),
                              pct_peak=round(100 * nbytes / us / 1e3 / HBM_PEAK_GBS, 1),
-                             tile=ops.query_tile("q8_0", rows, cols, T))
+                             repeats_us=reps[T], tile=ops.query_tile("q8_0", rows, cols, T))
     dom = max(Ts, key=lambda T: ms[T])
     dom_us = ms[dom] * 1e3 / args.steps
     achieved = nbytes / dom_us / 1e3

@@ -17,7 +17,7 @@ QG_MAX_T = 4
 QG_TILE_FIELDS = 8
 
 EXPORTS = (
-    "qgemv_q8_0", "qgemv_q4_0", "qgemv_bf16", "qgemv_grouped_experts", "qgemv_argmax", "qg_packed_bytes",
+    "qgemv_q8_0", "qgemv_q4_0", "qgemv_bf16", "qgemv_grouped_experts", "qgemv_argmax", "qgemv_rows", "qg_packed_bytes",
     "qg_pack_q8_0", "qg_unpack_q8_0", "qg_pack_q4_0", "qg_unpack_q4_0", "qg_query_tile",
     "qg_status_string", "qg_last_error",
 )
@@ -47,6 +47,8 @@ def load() -> ctypes.CDLL:
         f.argtypes = [i64, i64, i32, vp, vp, vp, vp]
     L.qgemv_grouped_experts.restype = i32
     L.qgemv_grouped_experts.argtypes = [i32, i64, i64, i64, i32, i32, vp, vp, vp, vp, vp]
+    L.qgemv_rows.restype = i32
+    L.qgemv_rows.argtypes = [i32, i64, i64, i64, vp, i32, vp, vp, vp, vp]
     L.qgemv_argmax.restype = i32
     L.qgemv_argmax.argtypes = [i32, i64, i64, i32, vp, vp, vp, vp, vp, vp]
     L.qg_packed_bytes.restype = sz
@@ -93,6 +95,10 @@ def qgemv_bf16(rows, cols, T, W, x, y, stream=None) -> int:
 
 def qgemv_grouped_experts(fmt, n_experts, rows, cols, T, topk, ids, W, x, y, stream=None) -> int:
     return load().qgemv_grouped_experts(fmt, n_experts, rows, cols, T, topk, ids, W, x, y, stream)
+
+
+def qgemv_rows(fmt, rows, cols, n_sel, ids, T, W, x, y, stream=None) -> int:
+    return load().qgemv_rows(fmt, rows, cols, n_sel, ids, T, W, x, y, stream)
 
 
 def qgemv_argmax(fmt, rows, cols, T, W, x, work, idx, val, stream=None) -> int:

@@ -365,6 +365,48 @@ int run_argmax(int fmt, int64_t rows, int64_t cols, int T, const void* W, const 
     return ok();
 }
 
+int run_rows(int fmt, int64_t rows, int64_t cols, int64_t n_sel, const int32_t* ids, int T, const void* W,
+             const float* x, float* y, void* stream) {
+    int64_t rbytes = 0;
+    int st = check_common(fmt, rows, cols, T, W, x, y, &rbytes);
+    if (st) return st;
+    if (!ids) return fail(QG_EINVAL, "null ids");
+    if (n_sel < 1 || n_sel > 0x7FFFFFFF) return fail(QG_EINVAL, "n_sel=%lld must be in 1..2^31-1", (long long)n_sel);
+    if (!aligned(ids, 4)) return fail(QG_EALIGN, "ids must be 4-byte aligned");
+    const size_t wbytes = (size_t)(rbytes * rows), xbytes = (size_t)T * cols * 4, ybytes = (size_t)T * n_sel * 4;
+    const int64_t nsl = (cols + kSlice - 1) / kSlice;
+    if (rbytes % 16 != 0 || nsl > kMaxWaves)
+        return fail(QG_EUNSUPPORTED, "row subset needs rows of a multiple of 16 bytes and at most %d k slices", kMaxWaves);
+    if ((int64_t)wbytes >= 0x7FFFFFF0LL)
+        return fail(QG_EUNSUPPORTED, "row subset addresses W with 32-bit offsets: %zu bytes is too many", wbytes);
+    if (overlap(y, ybytes, W, wbytes) || overlap(y, ybytes, x, xbytes) || overlap(y, ybytes, ids, (size_t)n_sel * 4))
+        return fail(QG_EINVAL, "y overlaps W, x or ids");
+    Tile tile{};
+    tile.lanes_per_row = kLanesPerRow;
+    tile.k_slice = kSlice;
+    tile.kind = 2;
+    tile.depth = 2;
+    tile.rows_per_batch = 4;
+    tile.waves_per_wg = (int)nsl;
+    int64_t rw = (n_sel / 256 + 7) / 8 * 8;
+    tile.rows_per_wg = (int)(rw < 16 ? 16 : rw > 64 ? 64 : rw);  // one id per lane: at most 64
+    while (gather_lds_bytes(fmt, tile, T, (int)nsl) > kMaxLds && tile.rows_per_wg > 16) tile.rows_per_wg /= 2;
+    if (gather_lds_bytes(fmt, tile, T, (int)nsl) > kMaxLds)
+        return fail(QG_EUNSUPPORTED, "row subset: the LDS rings do not fit %lld slices of this format", (long long)nsl);
+    DenseArgs a;
+    a.W = (const uint8_t*)W;
+    a.x = x;
+    a.y = y;
+    a.rows = rows;
+    a.row_bytes = rbytes;
+    a.cols = (int)cols;
+    a.nslices = (int)nsl;
+    a.rows_per_wg = tile.rows_per_wg;
+    const int err = launch_gather(fmt, T, tile, a, ids, n_sel, stream);
+    if (err) return fail(QG_EHIP, "kernel launch failed: %s", hip_error_name(err));
+    return ok();
+}
+
 }  // namespace
 }  // namespace qg
 
@@ -382,6 +424,11 @@ int qgemv_q4_0(int64_t rows, int64_t cols, int T, const void* W, const float* x,
 
 int qgemv_bf16(int64_t rows, int64_t cols, int T, const void* W, const float* x, float* y, void* stream) {
     return run_dense(QG_FMT_BF16, rows, cols, T, W, x, y, stream);
+}
+
+int qgemv_rows(int fmt, int64_t rows, int64_t cols, int64_t n_sel, const int32_t* ids, int T, const void* W,
+               const float* x, float* y, void* stream) {
+    return run_rows(fmt, rows, cols, n_sel, ids, T, W, x, y, stream);
 }
 
 int qgemv_argmax(int fmt, int64_t rows, int64_t cols, int T, const void* W, const float* x, void* work, int32_t* idx,

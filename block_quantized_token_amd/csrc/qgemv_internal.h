@@ -89,6 +89,13 @@ inline size_t dma_lds_bytes(int fmt, const Tile& t, int T, int nslices) {
            ntiles * nslices * 2 * t.rows_per_batch * pad_tokens(T) * 4;
 }
 
+// Row-subset kernel: rings of `depth` 8-row slots per wave, then partial sums (x in registers).
+inline size_t gather_lds_bytes(int fmt, const Tile& t, int T, int nslices) {
+    const size_t ntiles = (size_t)(t.rows_per_wg + 2 * t.rows_per_batch - 1) / (2 * t.rows_per_batch);
+    return (size_t)t.waves_per_wg * t.depth * stream_buf_bytes(fmt, t.rows_per_batch) +
+           ntiles * nslices * 2 * t.rows_per_batch * pad_tokens(T) * 4;
+}
+
 // Unit-balanced DMA kernel: x[T][cols] staged whole, then per-wave rings of
 // `depth` 8-row tile slots, then partial sums.  Any number of waves.
 inline bool units_supported(int rb, int depth) { return rb == 4 && depth >= 2 && depth <= 4; }
@@ -157,6 +164,8 @@ int launch_units(int fmt, int T, const Tile& tile, const DenseArgs& a, void* str
 int launch_argmax(int fmt, int T, const Tile& tile, const DenseArgs& a, void* work, int32_t* idx, float* val,
                   void* stream);
 int launch_grouped(int fmt, const Tile& tile, const GroupedArgs& a, void* stream);
+// Row subset: y[t][i] = W[ids[i]] . x[t], i < nsel (kind-3 tile, rb 4, depth 2, rows_per_wg <= 64).
+int launch_gather(int fmt, int T, const Tile& tile, const DenseArgs& a, const int32_t* ids, int64_t nsel, void* stream);
 const char* hip_error_name(int err);
 
 }  // namespace qg

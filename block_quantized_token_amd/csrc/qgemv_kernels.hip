@@ -867,6 +867,97 @@ __device__ __forceinline__ void dma_rows(const uint8_t* __restrict__ W, int64_t 
     }
 }
 
+// ------------------------------------------------------ row-subset (gather)
+// The mat-vec over a list of rows, y[t][i] = W[ids[i]] . x[t] (the draft-vocabulary
+// LM head in the mlxcel drafter-cost issue: the drafter reads only the rows of the
+// tokens it may propose).  As dma_rows (x in registers, loaded with the ids before
+// any load to LDS, so the ring needs no slots for it), but a tile's 8 rows
+// are ids[...] of the workgroup's range: every wave first loads those ids (one
+// per lane, at most 64 per workgroup), and each load lane takes its row's id
+// from the lane that holds it.  The descriptor spans all of W (< 2 GB, so every
+// byte offset fits the 32-bit offset); an id outside [0, rows) loads nothing and
+// its outputs are NaN.
+template <int FMT, int NT, int D, class Out>
+__device__ __forceinline__ void gather_rows(const uint8_t* __restrict__ W, int64_t rows, int64_t row_bytes, int cols,
+                                            int nsl, const int32_t* __restrict__ ids, const float* __restrict__ x,
+                                            int64_t sel_begin, int64_t sel_end, Out&& out) {
+    using F = Fmt<FMT>;
+    constexpr int ST = 8;
+    using S = StreamShape<FMT, ST>;
+    constexpr int TP = pad_pow2(NT);
+    constexpr int RB = ST / 2;
+    constexpr int N = RB * TP;
+    constexpr int L = S::kLoads;
+    static_assert((D - 1) * L <= 63, "vmcnt holds at most 63 outstanding loads");
+    extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int nw = blockDim.x >> 6;
+    const int g = lane >> 5, li = lane & 31;
+    const int s = wave % nsl, rg = wave / nsl, RG = nw / nsl;
+    const int k0 = s * kSlice;
+    const int nsel = (int)(sel_end - sel_begin);  // <= 64
+    const int ntiles = (nsel + ST - 1) / ST;
+    uint8_t* ring = smem + wave * D * S::kBufBytes;
+    float* part = reinterpret_cast<float*>(smem + nw * D * S::kBufBytes);  // [tiles][nsl][2][N]
+
+    // the workgroup's row ids (one per lane) and the slice of x, into registers,
+    // all complete before the first load to LDS
+    const int my_id = lane < nsel ? ids[sel_begin + lane] : -1;
+    const bool my_ok = my_id >= 0 && my_id < rows;
+    const int64_t rest = row_bytes - (int64_t)s * S::kChunks * 16;
+    const int cs = rest / 16 < S::kChunks ? (int)(rest / 16) : S::kChunks;
+    const __amdgpu_buffer_rsrc_t wr =
+        __builtin_amdgcn_make_buffer_rsrc((void*)W, (short)0, (int)(rows * row_bytes), kBufferRsrcWord3);
+    auto issue = [&](int t, uint8_t* lbuf) __attribute__((always_inline)) {
+#pragma unroll
+        for (int k = 0; k < L; ++k) {
+            const int j = 64 * k + lane;
+            const int r = j / S::kChunks, c = j % S::kChunks;
+            const int src = t * ST + r;  // lane holding this row's id
+            const int id = __shfl(my_id, src & 63, 64);
+            const int ok = __shfl((int)my_ok, src & 63, 64);
+            const bool live = t < ntiles && r < ST && src < nsel && c < cs && ok;
+            load_lds16(wr, lbuf + 1024 * k, live ? (int)(id * row_bytes) + s * S::kChunks * 16 + 16 * c : kNoLoad);
+        }
+    };
+
+    const bool lane_ok = F::lane_valid(li, k0, cols);
+    const bool upper_ok = lane_ok && F::upper_valid(li, k0, cols);
+    bool writer;
+    const int my_idx = butterfly_index<N>(li, writer);
+    int64_t xoff[NT];
+#pragma unroll
+    for (int n = 0; n < NT; ++n) xoff[n] = (int64_t)n * cols;
+    float xr[NT][kWeightsPerLane];
+    load_x<FMT, NT>(x, xoff, k0, li, lane_ok, cols, xr);
+    wait_vmcnt<0>();  // ids and x are in registers
+#pragma unroll
+    for (int i = 0; i < D; ++i) issue(rg + i * RG, ring + i * S::kBufBytes);
+    const int mine = ntiles > rg ? (ntiles - rg + RG - 1) / RG : 0;
+    for (int i = 0; i < mine; ++i) {
+        uint8_t* buf = ring + (i % D) * S::kBufBytes;
+        wait_vmcnt<(D - 1) * L>();
+        tile_compute<FMT, NT, ST>(buf, part, xr, li, g, s, nsl, rg + i * RG, lane_ok, upper_ok, my_idx, writer);
+        wait_lgkmcnt0();
+        issue(rg + (i + D) * RG, buf);
+    }
+    wait_vmcnt<0>();
+    __syncthreads();
+    for (int o = tid; o < nsel * NT; o += blockDim.x) {
+        const int rr = o / NT, t = o % NT;
+        const int tl = rr / ST, rin = rr % ST;
+        const int gg = rin & 1, i = rin >> 1;
+        const float* base = part + ((size_t)tl * nsl * 2 + gg) * N + i * TP + t;
+        float sum = base[0];
+        for (int w = 1; w < nsl; ++w) sum = sum + base[(size_t)w * 2 * N];
+        const int id = ids[sel_begin + rr];
+        out(t, sel_begin + rr, id >= 0 && id < rows ? sum : __builtin_nanf(""));
+    }
+}
+
 // ------------------------------------------------- unit-balanced DMA variant
 // Work units are (k slice, 8-row tile) pairs of the workgroup's rows, in
 // slice-major order; wave w of NW takes the contiguous range
@@ -1449,6 +1540,15 @@ __global__ void __launch_bounds__(64 * kMaxWaves) qgemv_stream_argmax_kernel(Den
     best.merge(work);
 }
 
+template <int FMT, int T>
+__global__ void __launch_bounds__(64 * kMaxWaves) qgemv_gather_kernel(DenseArgs a, const int32_t* ids, int64_t nsel) {
+    const int64_t sel_begin = (int64_t)blockIdx.x * a.rows_per_wg;
+    const int64_t sel_end = sel_begin + a.rows_per_wg < nsel ? sel_begin + a.rows_per_wg : nsel;
+    float* __restrict__ y = a.y;
+    gather_rows<FMT, T, 2>(a.W, a.rows, a.row_bytes, a.cols, a.nslices, ids, a.x, sel_begin, sel_end,
+                           [=](int t, int64_t i, float v) { y[t * nsel + i] = v; });
+}
+
 template <int T>
 __global__ void __launch_bounds__(64 * kMaxWaves) qgemv_mfma_q8_kernel(DenseArgs a) {
     const int64_t row_begin = (int64_t)blockIdx.x * a.rows_per_wg;
@@ -1893,6 +1993,27 @@ int launch_argmax(int fmt, int T, const Tile& tile, const DenseArgs& a, void* wo
     hipLaunchKernelGGL(fn, dim3((unsigned)nwg), dim3(64 * tile.waves_per_wg), lds, (hipStream_t)stream, a, w);
     hipLaunchKernelGGL(qgemv_argmax_finish_kernel, dim3(1), dim3(64), 0, (hipStream_t)stream, (const unsigned long long*)w,
                        idx, val, T);
+    return (int)hipGetLastError();
+}
+
+int launch_gather(int fmt, int T, const Tile& tile, const DenseArgs& a, const int32_t* ids, int64_t nsel, void* stream) {
+    using GatherFn = void (*)(DenseArgs, const int32_t*, int64_t);
+    GatherFn fn = nullptr;
+    auto pick = [&](auto ftag) -> GatherFn {
+        constexpr int F = decltype(ftag)::value;
+        switch (T) {
+        case 1: return qgemv_gather_kernel<F, 1>;
+        case 2: return qgemv_gather_kernel<F, 2>;
+        case 3: return qgemv_gather_kernel<F, 3>;
+        default: return qgemv_gather_kernel<F, 4>;
+        }
+    };
+    fn = fmt == QG_FMT_Q8_0 ? pick(std::integral_constant<int, QG_FMT_Q8_0>{})
+       : fmt == QG_FMT_Q4_0 ? pick(std::integral_constant<int, QG_FMT_Q4_0>{})
+                            : pick(std::integral_constant<int, QG_FMT_BF16>{});
+    const int64_t nwg = (nsel + tile.rows_per_wg - 1) / tile.rows_per_wg;
+    hipLaunchKernelGGL(fn, dim3((unsigned)nwg), dim3(64 * tile.waves_per_wg), gather_lds_bytes(fmt, tile, T, a.nslices),
+                       (hipStream_t)stream, a, ids, nsel);
     return (int)hipGetLastError();
 }
 

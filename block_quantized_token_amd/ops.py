@@ -45,6 +45,30 @@ def gemv(fmt, W, x, rows: int, out=None):
     return out
 
 
+def gemv_rows(fmt, W, x, rows: int, ids, out=None):
+    """y[T][len(ids)] = W[ids[i]] . x[t]: the mat-vec over a subset of W's rows
+    (ids int32 on the device; an id outside [0, rows) gives a NaN column)."""
+    import torch
+    f = _fmt(fmt)
+    for t, n in ((W, "W"), (x, "x"), (ids, "ids")):
+        _require_device(t, n)
+    if x.dtype != torch.float32 or x.dim() != 2:
+        raise ValueError("x must be fp32 [T][cols]")
+    if ids.dtype != torch.int32 or ids.dim() != 1:
+        raise ValueError("ids must be int32 [n_sel]")
+    T, cols = x.shape
+    need = _lib.qg_packed_bytes(f, rows, cols)
+    if need == 0 or W.numel() * W.element_size() < need:
+        raise ValueError(f"W holds {W.numel() * W.element_size()} bytes, the shape needs {need}")
+    if out is None:
+        out = torch.empty((T, ids.numel()), dtype=torch.float32, device=x.device)
+    _require_device(out, "out")
+    st = _lib.qgemv_rows(f, rows, cols, ids.numel(), ids.data_ptr(), T, W.data_ptr(), x.data_ptr(), out.data_ptr(),
+                         _stream(torch, x.device))
+    _lib.check(st, "qgemv_rows")
+    return out
+
+
 def argmax(fmt, W, x, rows: int, work=None):
     """(idx int32 [T], val fp32 [T]): per token, the row with the largest W . x[t]
     (lowest row on ties) and its value, without writing the [T][rows] product."""

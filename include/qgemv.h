@@ -120,6 +120,22 @@ int qgemv_grouped_experts(int fmt, int64_t n_experts, int64_t rows, int64_t cols
 int qgemv_argmax(int fmt, int64_t rows, int64_t cols, int T, const void* W, const float* x, void* work,
                  int32_t* idx, float* val, void* stream);
 
+/*
+ * Row subset: the mat-vec over a list of rows, for a draft-vocabulary LM head
+ * that reads only the rows of the tokens the drafter may propose (the drafter-
+ * cost issue, "perf(speculative): cut the MTP drafter's per-step cost...",
+ * draft-vocabulary item):
+ *     y[t][i] = sum_k w[ids[i]][k] * x[t][k]      t < T, i < n_sel
+ * W holds all `rows` rows of fmt (as for the dense entry points); ids is a
+ * DEVICE int32[n_sel] (any order, repeats allowed); y is fp32 [T][n_sel].  An id
+ * outside [0, rows) cannot be reported synchronously: its output column is NaN.
+ * Each y[t][i] equals the dense call's y[t][ids[i]] computed by the VALU
+ * kernels.  Needs rows of a multiple of 16 bytes, cols <= 6144 (BF16: 4608)
+ * and W under 2 GB (else QG_EUNSUPPORTED).
+ */
+int qgemv_rows(int fmt, int64_t rows, int64_t cols, int64_t n_sel, const int32_t* ids, int T, const void* W,
+               const float* x, float* y, void* stream);
+
 /* ---- host-only helpers (no GPU needed) ---------------------------------- */
 
 /* Packed bytes of a rows x cols matrix of fmt; 0 if the shape is invalid. */

@@ -205,3 +205,19 @@ def test_binding_refuses_cpu_tensors(lib):
     x = torch.zeros(1, 32)
     with pytest.raises(ValueError):
         ops.gemv("q8_0", W, x, rows=4)
+
+
+@pytest.mark.parametrize("args, status", [
+    ((0, 64, 256, 8, 0, 1, W0, X0, Y0), _lib.QG_EINVAL),            # null ids
+    ((0, 64, 256, 0, I0, 1, W0, X0, Y0), _lib.QG_EINVAL),           # no rows selected
+    ((0, 64, 256, 8, I0 + 2, 1, W0, X0, Y0), _lib.QG_EALIGN),       # ids misaligned
+    ((0, 64, 256, 8, I0, 1, W0, X0, I0 + 4), _lib.QG_EINVAL),       # y overlaps ids
+    ((0, 64, 256, 8, I0, 5, W0, X0, Y0), _lib.QG_EINVAL),           # T 5
+    ((0, 64, 32, 8, I0, 1, W0, X0, Y0), _lib.QG_EUNSUPPORTED),      # 34-byte rows
+    ((0, 64, 8192, 8, I0, 1, W0, X0, Y0), _lib.QG_EUNSUPPORTED),    # 16 k slices
+    ((0, 1 << 20, 2560, 8, I0, 1, W0, X0, Y0), _lib.QG_EUNSUPPORTED),  # W of 2.85 GB
+    ((2, 64, 5120, 8, I0, 1, W0, X0, Y0), _lib.QG_EUNSUPPORTED),    # BF16 rings of 10 slices
+])
+def test_rows_subset_argument_errors(lib, args, status):
+    assert _lib.qgemv_rows(*args) == status, _lib.last_error()
+    assert _lib.last_error()

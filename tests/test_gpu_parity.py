@@ -437,6 +437,67 @@ def test_argmax_ties_negatives_and_kinds(torch, orc, monkeypatch):
             argmax_check(torch, orc, Q8, rows, cols, W, neg, what + " neg-x")
 
 
+# ------------------------------------------------------------- row subset
+def rows_check(torch, orc, monkeypatch, fmt, rows, cols, W, x, ids, what):
+    """Row subset against the oracle on the selected rows and, bit for bit,
+    against the dense call's own output at those rows (a VALU LDS-DMA tile)."""
+    Wd, xd = dev(torch, W), dev(torch, x)
+    y = ops.gemv_rows(NAMES[fmt], Wd, xd, rows, dev(torch, ids.astype(np.int32))).cpu().numpy()
+    ok = (ids >= 0) & (ids < rows)
+    assert np.isnan(y[:, ~ok]).all(), what
+    if ok.any():
+        ref, bound = orc.gemv(fmt, rows, cols, W, x, sel=ids[ok])
+        assert_parity(y[:, ok], ref, bound, what)
+        nsl = -(-cols // 512)
+        monkeypatch.setenv("QGEMV_TILE", f"{NAMES[fmt]}:4,{nsl},16,L2")
+        if _lib.qg_query_tile(fmt, rows, cols, x.shape[0])[0] != 0:  # its LDS is too large: the direct kind
+            monkeypatch.setenv("QGEMV_TILE", f"{NAMES[fmt]}:4,{nsl},8,d")
+        full = ops.gemv(NAMES[fmt], Wd, xd, rows).cpu().numpy()
+        monkeypatch.delenv("QGEMV_TILE")
+        assert np.array_equal(y[:, ok], full[:, ids[ok]]), what
+
+
+@pytest.mark.parametrize("fmt", [Q8, Q4, BF])
+def test_rows_subset_shapes(torch, orc, monkeypatch, fmt):
+    rng = np.random.default_rng(40 + fmt)
+    for rows, cols in ((100, 256), (333, 2560), (70, 6144 if fmt != BF else 4608)):
+        W = I.weights(rng, fmt, rows, cols)
+        x = I.activations(rng, cols)
+        for n_sel in (1, 7, 65, 130):
+            ids = rng.integers(0, rows, n_sel)          # unsorted, with repeats
+            for T in (1, 4):
+                say(f"[rows] fmt={NAMES[fmt]} {rows}x{cols} n_sel={n_sel} T={T}")
+                rows_check(torch, orc, monkeypatch, fmt, rows, cols, W, x[:T], ids, f"{rows}x{cols} n={n_sel} T={T}")
+
+
+def test_rows_subset_bad_ids(torch, orc, monkeypatch):
+    rng = np.random.default_rng(3)
+    rows, cols = 50, 512
+    W = I.weights(rng, Q8, rows, cols)
+    x = I.activations(rng, cols)
+    ids = np.array([3, -1, 49, 50, 7, 1 << 30, 0], dtype=np.int64)
+    rows_check(torch, orc, monkeypatch, Q8, rows, cols, W, x, ids, "bad ids")
+
+
+def test_rows_subset_draft_vocabulary(torch, orc, monkeypatch):
+    """32,768 of the LM head's 248,320 rows (a draft vocabulary), T = 1..4."""
+    c = I.dense_case("c4_q8_0_248320x5120")
+    rng = np.random.default_rng(8)
+    ids = np.sort(rng.choice(c["rows"], 32768, replace=False))
+    Wd, xd = dev(torch, c["W"]), dev(torch, c["x"])
+    monkeypatch.setenv("QGEMV_TILE", "q8_0:4,10,8,d")  # a VALU tile that fits the LDS at T = 4
+    full = ops.gemv("q8_0", Wd, xd, c["rows"]).cpu().numpy()
+    monkeypatch.delenv("QGEMV_TILE")
+    idd = dev(torch, ids.astype(np.int32))
+    samp = rng.choice(len(ids), 500, replace=False)
+    for T in (1, 2, 3, 4):
+        say(f"[rows] draft vocabulary T={T}")
+        y = ops.gemv_rows("q8_0", Wd, xd[:T].contiguous(), c["rows"], idd).cpu().numpy()
+        assert np.array_equal(y, full[:T, ids]), T
+        ref, bound = orc.gemv(Q8, c["rows"], c["cols"], c["W"], c["x"][:T], sel=ids[samp])
+        assert_parity(y[:, samp], ref, bound, f"draft vocabulary T={T}")
+
+
 # ---------------------------------------------------------- grouped experts
 def grouped_check(torch, orc, fmt, n_experts, rows, cols, ids, W, x, what):
     say(f"[{what}] fmt={NAMES[fmt]} experts={n_experts} rows={rows} cols={cols} ids={ids.tolist()}")
