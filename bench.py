@@ -204,6 +204,24 @@ def other_workloads(torch, stream):
                 am[str(T)] = dict(us_per_call=round(us, 3), gbs=round(nb / us / 1e3, 1),
                                   pct_peak=round(100 * nb / us / 1e3 / HBM_PEAK_GBS, 1))
             out["c4_argmax_fused"] = dict(weight_bytes_per_call=nb, calls=calls, per_T=am)
+            # a draft vocabulary: 32,768 distinct rows of the head, sorted, read through the row subset
+            # (7 disjoint vocabularies in turn, 1.25 GB together, so each call's rows come from HBM)
+            nsel = 32768
+            perm = torch.randperm(rows, device="cuda")
+            idsets = [torch.sort(perm[j * nsel:(j + 1) * nsel].to(torch.int32)).values for j in range(rows // nsel)]
+            ys = torch.empty(4, nsel, device="cuda")
+            sub = nsel * (nb // rows)
+            rs = {}
+            for T in (1, 2, 3, 4):
+                def launch(i, T=T):
+                    st = _lib.qgemv_rows(fmt, rows, cols, nsel, idsets[i % len(idsets)].data_ptr(), T,
+                                         ring[0].data_ptr(), x.data_ptr(), ys.data_ptr(), sp)
+                    if st:
+                        _lib.check(st, "rows")
+                us = time_entry(torch, stream, launch, max(200, calls))
+                rs[str(T)] = dict(us_per_call=round(us, 3), bytes_read=sub, gbs=round(sub / us / 1e3, 1),
+                                  pct_peak=round(100 * sub / us / 1e3 / HBM_PEAK_GBS, 1))
+            out["c4_rows_32768"] = dict(n_sel=nsel, vocabularies=len(idsets), per_T=rs)
         out[name] = dict(weight_bytes_per_call=nb, calls=calls, ring_copies=len(ring), per_T=res)
         del ring
     # grouped experts: 256 Q4_0 experts of 512 x 2560; each token picks 10 distinct
