@@ -19,8 +19,9 @@ QG_TILE_FIELDS = 8
 EXPORTS = (
     "qgemv_q8_0", "qgemv_q4_0", "qgemv_bf16", "qgemv_grouped_experts", "qgemv_argmax", "qgemv_rows", "qg_packed_bytes",
     "qg_pack_q8_0", "qg_unpack_q8_0", "qg_pack_q4_0", "qg_unpack_q4_0", "qg_query_tile",
-    "qg_status_string", "qg_last_error",
+    "qg_status_string", "qg_last_error", "qg_quantize_q8_0", "qg_quantize_q4_0",
 )
+QG_Q4_ABSMAX, QG_Q4_LLOYD = 0, 1
 
 
 class QGError(RuntimeError):
@@ -57,6 +58,10 @@ def load() -> ctypes.CDLL:
         f = getattr(L, name)
         f.restype = i32
         f.argtypes = [i64, i64, vp, vp, vp]
+    L.qg_quantize_q8_0.restype = i32
+    L.qg_quantize_q8_0.argtypes = [i64, i64, vp, vp, vp]
+    L.qg_quantize_q4_0.restype = i32
+    L.qg_quantize_q4_0.argtypes = [i64, i64, i32, vp, vp, vp]
     L.qg_query_tile.restype = i32
     L.qg_query_tile.argtypes = [i32, i64, i64, i32, ctypes.POINTER(ctypes.c_int)]
     L.qg_status_string.restype = ctypes.c_char_p
@@ -123,6 +128,14 @@ def qg_pack_q4_0(rows, cols, d_bits, codes, out) -> int:
 
 def qg_unpack_q4_0(rows, cols, packed, d_bits, codes) -> int:
     return load().qg_unpack_q4_0(rows, cols, packed, d_bits, codes)
+
+
+def qg_quantize_q8_0(rows, cols, src, dst, stream=None) -> int:
+    return load().qg_quantize_q8_0(rows, cols, src, dst, stream)
+
+
+def qg_quantize_q4_0(rows, cols, method, src, dst, stream=None) -> int:
+    return load().qg_quantize_q4_0(rows, cols, method, src, dst, stream)
 
 
 def qg_query_tile(fmt, rows, cols, T):

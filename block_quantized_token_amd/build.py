@@ -30,11 +30,19 @@ def build(verbose: bool = False, extra_hip_flags=()) -> str:
     host_o = os.path.join(BUILD, "qgemv_host.o")
     kern_o = os.path.join(BUILD, "qgemv_kernels.o")
     _run(["g++", *HOST_FLAGS, "-c", os.path.join(CSRC, "qgemv_host.cpp"), "-o", host_o], verbose)
-    _run([os.path.join(ROCM, "bin", "hipcc"), *HIP_FLAGS, *extra_hip_flags, "-c", "-x", "hip",
-          os.path.join(CSRC, "qgemv_kernels.hip"), "-o", kern_o], verbose)
+    quant_o = os.path.join(BUILD, "qquant_kernels.o")
+    hipcc = os.path.join(ROCM, "bin", "hipcc")
+    # the two kernel sources compile side by side (the mat-vec one takes minutes)
+    quant = subprocess.Popen([hipcc, *HIP_FLAGS, *extra_hip_flags, "-c", "-x", "hip",
+                              os.path.join(CSRC, "qquant_kernels.hip"), "-o", quant_o])
+    try:
+        _run([hipcc, *HIP_FLAGS, *extra_hip_flags, "-c", "-x", "hip", os.path.join(CSRC, "qgemv_kernels.hip"),
+              "-o", kern_o], verbose)
+    finally:
+        if quant.wait() != 0:
+            raise subprocess.CalledProcessError(quant.returncode, "hipcc qquant_kernels.hip")
     tmp = LIB + f".tmp{os.getpid()}"
-    _run([os.path.join(ROCM, "bin", "hipcc"), "--offload-arch=gfx950", "-shared", "-fPIC", host_o, kern_o,
-          "-o", tmp], verbose)
+    _run([hipcc, "--offload-arch=gfx950", "-shared", "-fPIC", host_o, kern_o, quant_o, "-o", tmp], verbose)
     os.replace(tmp, LIB)
     return LIB
 

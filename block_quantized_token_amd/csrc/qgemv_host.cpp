@@ -407,6 +407,25 @@ int run_rows(int fmt, int64_t rows, int64_t cols, int64_t n_sel, const int32_t* 
     return ok();
 }
 
+// Quantizers: kind 0 Q8_0, 1 Q4_0 absmax, 2 Q4_0 Lloyd.
+int run_quantize(int kind, int64_t rows, int64_t cols, const float* src, void* dst, void* stream) {
+    const char* name = kind == 0 ? "qg_quantize_q8_0" : "qg_quantize_q4_0";
+    if (!src || !dst) return fail(QG_EINVAL, "%s: null pointer (src=%p dst=%p)", name, (const void*)src, dst);
+    if (rows <= 0 || cols <= 0) return fail(QG_EINVAL, "rows=%lld cols=%lld must be positive", (long long)rows, (long long)cols);
+    if (cols % 32) return fail(QG_EINVAL, "%s needs whole 32-value blocks: cols=%lld", name, (long long)cols);
+    if (cols > kMaxCols || rows >= kMaxRows)
+        return fail(QG_EUNSUPPORTED, "rows=%lld cols=%lld beyond the supported range", (long long)rows, (long long)cols);
+    if (!aligned(src, 16) || !aligned(dst, 16))
+        return fail(QG_EALIGN, "src and dst must be 16-byte aligned (src=%p dst=%p)", (const void*)src, dst);
+    const int64_t nblocks = rows * (cols / 32);
+    if ((nblocks + 255) / 256 > 0x7FFFFFFF) return fail(QG_EUNSUPPORTED, "grid too large");
+    if (overlap(src, (size_t)nblocks * 128, dst, (size_t)nblocks * (kind == 0 ? 34 : 18)))
+        return fail(QG_EINVAL, "dst overlaps src");
+    const int err = launch_quantize(kind, src, (uint8_t*)dst, nblocks, stream);
+    if (err) return fail(QG_EHIP, "kernel launch failed: %s", hip_error_name(err));
+    return ok();
+}
+
 }  // namespace
 }  // namespace qg
 
@@ -504,6 +523,15 @@ int qgemv_grouped_experts(int fmt, int64_t n_experts, int64_t rows, int64_t cols
     int err = launch_grouped(fmt, tile, a, stream);
     if (err) return fail(QG_EHIP, "kernel launch failed: %s", hip_error_name(err));
     return ok();
+}
+
+int qg_quantize_q8_0(int64_t rows, int64_t cols, const float* src, void* dst, void* stream) {
+    return run_quantize(0, rows, cols, src, dst, stream);
+}
+
+int qg_quantize_q4_0(int64_t rows, int64_t cols, int method, const float* src, void* dst, void* stream) {
+    if (method != QG_Q4_ABSMAX && method != QG_Q4_LLOYD) return fail(QG_EINVAL, "unknown Q4_0 method %d", method);
+    return run_quantize(method == QG_Q4_ABSMAX ? 1 : 2, rows, cols, src, dst, stream);
 }
 
 size_t qg_packed_bytes(int fmt, int64_t rows, int64_t cols) {

@@ -166,6 +166,9 @@ int launch_argmax(int fmt, int T, const Tile& tile, const DenseArgs& a, void* wo
 int launch_grouped(int fmt, const Tile& tile, const GroupedArgs& a, void* stream);
 // Row subset: y[t][i] = W[ids[i]] . x[t], i < nsel (kind-3 tile, rb 4, depth 2, rows_per_wg <= 64).
 int launch_gather(int fmt, int T, const Tile& tile, const DenseArgs& a, const int32_t* ids, int64_t nsel, void* stream);
+// Quantizers (qquant_kernels.hip): kind 0 Q8_0, 1 Q4_0 absmax, 2 Q4_0 Lloyd; nblocks
+// blocks of 32 fp32 values in, as many packed blocks out.
+int launch_quantize(int kind, const float* src, uint8_t* dst, int64_t nblocks, void* stream);
 const char* hip_error_name(int err);
 
 }  // namespace qg

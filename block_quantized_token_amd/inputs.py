@@ -85,6 +85,21 @@ def activations(rng: np.random.Generator, cols: int, T: int = MAX_T) -> np.ndarr
     return np.ascontiguousarray(x[:T])
 
 
+def dense_fp32(rng: np.random.Generator, rows: int, cols: int, sigma: float = 0.02) -> np.ndarray:
+    """fp32 [rows][cols] values to quantize: N(0,1) * sigma, as a weight matrix is
+    initialised; one block in 16 has one element 20x larger (an outlier), one in
+    64 is all zero and one in 64 is scaled by 1e-6 (its fp16 scale underflows)."""
+    v = rng.standard_normal((rows, cols)) * sigma
+    blocks = v.reshape(rows * (cols // 32), 32)
+    kind = rng.random(blocks.shape[0])
+    pos = rng.integers(0, 32, blocks.shape[0])
+    out = kind < 1 / 16
+    blocks[out, pos[out]] *= 20
+    blocks[(kind >= 1 / 16) & (kind < 1 / 16 + 1 / 64)] = 0
+    blocks[kind >= 1 - 1 / 64] *= 1e-6
+    return blocks.reshape(rows, cols).astype(np.float32)
+
+
 def expert_ids(rng: np.random.Generator, n_experts: int, T: int, topk: int) -> np.ndarray:
     assert T * topk <= n_experts
     return rng.permutation(n_experts)[: T * topk].astype(np.int32).reshape(T, topk)

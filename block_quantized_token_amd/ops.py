@@ -117,6 +117,35 @@ def grouped_experts(fmt, W, x, ids, n_experts: int, rows: int, out=None):
     return out
 
 
+def quantize(fmt, src, method: str = "absmax", out=None):
+    """Packed Q8_0 / Q4_0 bytes (uint8 device tensor) of fp32 [rows][cols] values
+    on the device; Q4_0 takes method "absmax" or "lloyd"."""
+    import torch
+    f = _fmt(fmt)
+    _require_device(src, "src")
+    if src.dtype != torch.float32 or src.dim() != 2:
+        raise ValueError("src must be fp32 [rows][cols]")
+    rows, cols = src.shape
+    need = _lib.qg_packed_bytes(f, rows, cols)
+    if f not in (_lib.QG_FMT_Q8_0, _lib.QG_FMT_Q4_0) or need == 0:
+        raise ValueError("quantizers exist for q8_0 and q4_0 with cols a multiple of 32")
+    if out is None:
+        out = torch.empty(need, dtype=torch.uint8, device=src.device)
+    _require_device(out, "out")
+    if out.numel() * out.element_size() < need:
+        raise ValueError(f"out holds {out.numel() * out.element_size()} bytes, the shape needs {need}")
+    s = _stream(torch, src.device)
+    if f == _lib.QG_FMT_Q8_0:
+        if method != "absmax":
+            raise ValueError("q8_0 has the absmax quantizer only")
+        st = _lib.qg_quantize_q8_0(rows, cols, src.data_ptr(), out.data_ptr(), s)
+    else:
+        m = {"absmax": _lib.QG_Q4_ABSMAX, "lloyd": _lib.QG_Q4_LLOYD}[method]
+        st = _lib.qg_quantize_q4_0(rows, cols, m, src.data_ptr(), out.data_ptr(), s)
+    _lib.check(st, "qg_quantize")
+    return out
+
+
 def pack_q8_0(d_bits: np.ndarray, codes: np.ndarray) -> np.ndarray:
     rows, cols = codes.shape
     d = np.ascontiguousarray(d_bits, dtype=np.uint16)

@@ -136,6 +136,32 @@ int qgemv_argmax(int fmt, int64_t rows, int64_t cols, int T, const void* W, cons
 int qgemv_rows(int fmt, int64_t rows, int64_t cols, int64_t n_sel, const int32_t* ids, int T, const void* W,
                const float* x, float* y, void* stream);
 
+/*
+ * Quantizers: fp32 values -> packed blocks, on the device, in the layout the
+ * entry points above read.  The pages name the quantizers their weights come
+ * from but not their steps (opus-mtp-turbo: Track 1 report, item 3 "Q4_0 / Q5_0
+ * draft weights": Q4_0 from a "Lloyd" quantizer; "Where the time goes"
+ * (meld-turbo-performance): dense projections re-encoded to Q8_0).  Per block
+ * of 32 values, every decision in fp32:
+ *   Q8_0             d = max|v| / 127, code = round(v * (1/d)), halves away
+ *                    from zero.
+ *   Q4_0 QG_Q4_ABSMAX  d = (the first element of largest magnitude, signed) / -8,
+ *                    code = min(15, trunc(v * (1/d) + 8.5)); that element gets 0.
+ *   Q4_0 QG_Q4_LLOYD   from the absmax codes, alternate the least-squares scale
+ *                    d = sum v*(c-8) / sum (c-8)^2 (index order) and nearest-
+ *                    level codes clamp(floor(v * (1/d) + 8.5), 0, 15) until the
+ *                    codes repeat, at most 8 fits; d is the last fit.
+ * The block stores fp16(d) (nearest, ties to even); a block whose fp16 scale
+ * would be zero is stored as zeros (d = +0, codes 0 / 8).
+ * src: DEVICE fp32 [rows][cols] (cols a multiple of 32); dst: DEVICE, the
+ * qg_packed_bytes(fmt, rows, cols) packed bytes, overwritten.  Both 16-byte
+ * aligned, not overlapping.  Non-finite inputs give unspecified bytes.
+ * Stream-ordered and asynchronous like the mat-vec calls.
+ */
+enum { QG_Q4_ABSMAX = 0, QG_Q4_LLOYD = 1 };
+int qg_quantize_q8_0(int64_t rows, int64_t cols, const float* src, void* dst, void* stream);
+int qg_quantize_q4_0(int64_t rows, int64_t cols, int method, const float* src, void* dst, void* stream);
+
 /* ---- host-only helpers (no GPU needed) ---------------------------------- */
 
 /* Packed bytes of a rows x cols matrix of fmt; 0 if the shape is invalid. */

@@ -60,6 +60,12 @@ class Oracle:
         L.oracle_grouped.restype = i32
         L.oracle_grouped.argtypes = [i32, i64, i64, i64, i32, i32, vp, vp, vp, vp, vp]
         L.oracle_num_threads.restype = i32
+        L.oracle_f32_to_fp16_array.restype = None
+        L.oracle_f32_to_fp16_array.argtypes = [i64, vp, vp]
+        L.oracle_quantize_q8_0.restype = i32
+        L.oracle_quantize_q8_0.argtypes = [i64, i64, vp, vp]
+        L.oracle_quantize_q4_0.restype = i32
+        L.oracle_quantize_q4_0.argtypes = [i64, i64, i32, vp, vp]
         self.L = L
 
     # scalars -----------------------------------------------------------
@@ -130,6 +136,29 @@ class Oracle:
         y, bound = self.gemv(fmt, rows, cols, W, x)
         idx = np.argmax(y, axis=1)  # numpy returns the first (lowest) index of the maximum
         return idx, y[np.arange(y.shape[0]), idx], y, bound
+
+    def to_fp16_bits(self, v) -> np.ndarray:
+        """fp32 values -> binary16 bit patterns (nearest, ties to even)."""
+        v = np.ascontiguousarray(v, dtype=np.float32).reshape(-1)
+        out = np.empty(v.size, dtype=np.uint16)
+        self.L.oracle_f32_to_fp16_array(v.size, v.ctypes.data, out.ctypes.data)
+        return out
+
+    def quantize(self, fmt: int, rows: int, cols: int, src, method: int = 0) -> np.ndarray:
+        """fp32 [rows][cols] -> packed Q8_0 (method 0) or Q4_0 (method 0 absmax, 1 Lloyd) bytes."""
+        src = np.ascontiguousarray(src, dtype=np.float32)
+        assert src.size == rows * cols
+        out = np.empty(self.packed_bytes(fmt, rows, cols), dtype=np.uint8)
+        if fmt == FMT_Q8_0:
+            assert method == 0
+            rc = self.L.oracle_quantize_q8_0(rows, cols, src.ctypes.data, out.ctypes.data)
+        elif fmt == FMT_Q4_0:
+            rc = self.L.oracle_quantize_q4_0(rows, cols, method, src.ctypes.data, out.ctypes.data)
+        else:
+            raise ValueError("quantizers exist for Q8_0 and Q4_0")
+        if rc:
+            raise ValueError(f"oracle_quantize rc={rc}")
+        return out
 
     def grouped(self, fmt: int, n_experts: int, rows: int, cols: int, ids, W, x):
         """Returns (y, bound), each fp64 [T][topk][rows]."""

@@ -28,6 +28,9 @@
  * first, then the codes; Q4_0 byte j holds code j in its low nibble and code
  * j + 16 in its high nibble.
  *
+ * The file ends with the quantizers that make those blocks from fp32 values
+ * (see the comment there for what they compute and why).
+ *
  * Every function returns 0 on success, or a negative number for bad arguments
  * (the oracle raises where the library would return a status code).
  *
@@ -37,6 +40,7 @@
 #include <math.h>
 #include <stddef.h>
 #include <stdint.h>
+#include <string.h>
 
 #ifndef ORACLE_MUTANT
 #define ORACLE_MUTANT 0
@@ -245,6 +249,212 @@ int oracle_grouped(int fmt, int64_t n_experts, int64_t rows, int64_t cols, int T
         int t = (int)(slot / topk);
         const uint8_t* row = W + ((int64_t)ids[slot] * rows + r) * rb;
         dot_row(fmt, row, cols, x + (int64_t)t * cols, &y[q], &bound[q]);
+    }
+    return 0;
+}
+
+/* ------------------------------------------------------------ quantizers */
+/*
+ * The quantizers that produce the packed blocks on the device (opus-mtp-turbo:
+ * Track 1 report, item 3 "Q4_0 / Q5_0 draft weights": Q4_0 draft weights made by
+ * the "Lloyd" quantizer of the hyper-connection loader; "Where the time goes"
+ * (meld-turbo-performance), the re-encoding of dense projections to Q8_0).  The
+ * pages name the quantizers but print no procedure, so these are the plainest
+ * readings: symmetric absmax rounding for Q8_0, the absmax rule that maps the
+ * block's signed extreme to code 0 for Q4_0, and for "Lloyd" alternating
+ * least-squares fits of the scale with nearest-level assignments of the codes,
+ * started from the absmax rule.  Every decision that turns a float into a code
+ * is taken in fp32, one operation at a time in the order written (no fused
+ * multiply-add), because a code is an integer the two sides must agree on.
+ */
+
+/* fp32 -> binary16, round to nearest, ties to even, from the bit definition:
+ * a finite |f| >= 65520 (the midpoint of 65504 and 2^16) overflows to inf;
+ * below 2^-14 the value is an integer multiple of 2^-24 (subnormal, or the
+ * smallest normal when it rounds up to 1024); otherwise 1024..2047 units of
+ * 2^(e-10) for 2^e <= |f| < 2^(e+1).                                        */
+uint16_t oracle_f32_to_fp16(float f)
+{
+    uint32_t u;
+    memcpy(&u, &f, 4);
+    uint16_t sign = (uint16_t)((u >> 16) & 0x8000u);
+    if ((u & 0x7F800000u) == 0x7F800000u) return (u & 0x007FFFFFu) ? (uint16_t)(sign | 0x7E00u) : (uint16_t)(sign | 0x7C00u);
+    double a = fabs((double)f); /* exact */
+    if (a >= 65520.0) return (uint16_t)(sign | 0x7C00u);
+    if (a < ldexp(1.0, -14)) {
+#if ORACLE_MUTANT == 12
+        double n = floor(ldexp(a, 24)); /* truncates instead of rounding */
+#else
+        double n = nearbyint(ldexp(a, 24)); /* default rounding mode: nearest, ties to even */
+#endif
+        return (uint16_t)(sign | (uint16_t)n);
+    }
+    int e2;
+    frexp(a, &e2); /* a = m * 2^e2, 0.5 <= m < 1, so 2^(e2-1) <= a < 2^e2 */
+    int e = e2 - 1;
+#if ORACLE_MUTANT == 12
+    double n = floor(ldexp(a, 10 - e));
+#else
+    double n = nearbyint(ldexp(a, 10 - e)); /* 1024 <= n <= 2048 */
+#endif
+    if (n == 2048.0) {
+        n = 1024.0;
+        e += 1;
+    }
+    if (e + 15 >= 31) return (uint16_t)(sign | 0x7C00u);
+    return (uint16_t)(sign | (uint16_t)((e + 15) << 10) | (uint16_t)(n - 1024.0));
+}
+
+void oracle_f32_to_fp16_array(int64_t n, const float* src, uint16_t* out)
+{
+    for (int64_t i = 0; i < n; ++i) out[i] = oracle_f32_to_fp16(src[i]);
+}
+
+static void put_le16(uint8_t* p, uint16_t v)
+{
+    p[0] = (uint8_t)(v & 0xFF);
+    p[1] = (uint8_t)(v >> 8);
+}
+
+/*
+ * Q8_0: per block of 32, d = max|v| / 127 and code = round(v / d), computed as
+ * v * (1/d) and rounded half away from zero; the block stores fp16(d).  A block
+ * whose d rounds to a zero fp16 (max|v| below about 127 * 2^-25, all-zero blocks
+ * included) decodes to zeros whatever its codes, and is stored with d = +0 and
+ * codes 0.  Inputs must be finite (else -2).  out: rows * cols/32 blocks of 34
+ * bytes.
+ */
+int oracle_quantize_q8_0(int64_t rows, int64_t cols, const float* src, uint8_t* out)
+{
+    if (rows <= 0 || cols <= 0 || cols % 32 || !src || !out) return -1;
+    int64_t nblk = rows * (cols / 32);
+    for (int64_t i = 0; i < nblk * 32; ++i)
+        if (!isfinite(src[i])) return -2;
+#pragma omp parallel for schedule(static)
+    for (int64_t b = 0; b < nblk; ++b) {
+        const float* v = src + b * 32;
+        uint8_t* o = out + b * 34;
+        float amax = 0.0f;
+        for (int j = 0; j < 32; ++j) {
+            float a = fabsf(v[j]);
+            if (a > amax) amax = a;
+        }
+#if ORACLE_MUTANT == 8
+        float d = amax / 128.0f; /* wrong level count */
+#else
+        float d = amax / 127.0f;
+#endif
+        uint16_t dh = oracle_f32_to_fp16(d);
+        float id = 1.0f / d;
+        if ((dh & 0x7FFF) == 0) {
+            dh = 0;
+            id = 0.0f;
+        }
+        put_le16(o, dh);
+        for (int j = 0; j < 32; ++j) {
+            float q = v[j] * id;
+#if ORACLE_MUTANT == 9
+            o[2 + j] = (uint8_t)(int8_t)(int)q; /* truncates */
+#else
+            o[2 + j] = (uint8_t)(int8_t)(int)roundf(q);
+#endif
+        }
+    }
+    return 0;
+}
+
+/* The Q4_0 absmax rule on one block: the element of largest magnitude (the
+ * first one on ties), with its sign, is mapped to code 0, d = that value / -8,
+ * code = min(15, trunc(v * (1/d) + 8.5)).  Returns d.  A block whose d rounds
+ * to a zero fp16 is the zero block: d = +0, codes 8.                        */
+static float q4_absmax(const float* v, int* c)
+{
+    float amax = 0.0f, vmax = 0.0f;
+    for (int j = 0; j < 32; ++j)
+        if (amax < fabsf(v[j])) {
+            amax = fabsf(v[j]);
+            vmax = v[j];
+        }
+#if ORACLE_MUTANT == 10
+    (void)vmax;
+    float d = amax / -8.0f; /* sign of the extreme dropped */
+#else
+    float d = vmax / -8.0f;
+#endif
+    float id = 1.0f / d;
+    if ((oracle_f32_to_fp16(d) & 0x7FFF) == 0) {
+        d = 0.0f;
+        id = 0.0f;
+    }
+    for (int j = 0; j < 32; ++j) {
+        float t = v[j] * id;
+        t = t + 8.5f;
+        int q = (int)t;
+        c[j] = q < 15 ? q : 15;
+    }
+    return d;
+}
+
+/* "Lloyd": fit d to the codes by least squares, d = sum v*q / sum q*q with
+ * q = code - 8 (the sums in index order), re-assign every code to the nearest
+ * level for that d, clamp(floor(v * (1/d) + 8.5), 0, 15), and repeat until the
+ * codes stop changing; at most ORACLE_LLOYD_ROUNDS fits.  The stored scale is
+ * the last fit, so it is the least-squares scale of the stored codes.  The zero
+ * block of the absmax rule (all codes 8) is kept as it is.  (Each term v*q has
+ * the sign of d, and the fit is a weighted mean of v/q, so |d| <= max|v| keeps
+ * the extreme's |q| >= 1: every fitted |d| is at least max|v| / 2048, a normal
+ * fp32 whenever the start is not the zero block.)                           */
+#define ORACLE_LLOYD_ROUNDS 8
+static float q4_lloyd(const float* v, int* c)
+{
+    float d = q4_absmax(v, c);
+#if ORACLE_MUTANT == 11
+    return d; /* no refinement */
+#endif
+    for (int it = 0; it < ORACLE_LLOYD_ROUNDS; ++it) {
+        float s1 = 0.0f;
+        int s2 = 0;
+        for (int j = 0; j < 32; ++j) {
+            int q = c[j] - 8;
+            s1 = s1 + v[j] * (float)q;
+            s2 += q * q;
+        }
+        if (s2 == 0) break;
+        d = s1 / (float)s2;
+        if (it == ORACLE_LLOYD_ROUNDS - 1 || d == 0.0f) break;
+        float id = 1.0f / d;
+        int changed = 0;
+        for (int j = 0; j < 32; ++j) {
+            float t = v[j] * id;
+            t = t + 8.5f;
+            t = floorf(t);
+            int q = t < 0.0f ? 0 : t > 15.0f ? 15 : (int)t;
+            changed |= q != c[j];
+            c[j] = q;
+        }
+        if (!changed) break;
+    }
+    return d;
+}
+
+/*
+ * Q4_0: method 0 the absmax rule, method 1 the Lloyd refinement above.  Byte j
+ * of a block's 16 code bytes holds code j in its low nibble and code j + 16 in
+ * its high nibble.  out: rows * cols/32 blocks of 18 bytes.
+ */
+int oracle_quantize_q4_0(int64_t rows, int64_t cols, int method, const float* src, uint8_t* out)
+{
+    if (rows <= 0 || cols <= 0 || cols % 32 || !src || !out || (method != 0 && method != 1)) return -1;
+    int64_t nblk = rows * (cols / 32);
+    for (int64_t i = 0; i < nblk * 32; ++i)
+        if (!isfinite(src[i])) return -2;
+#pragma omp parallel for schedule(static)
+    for (int64_t b = 0; b < nblk; ++b) {
+        int c[32];
+        float d = method ? q4_lloyd(src + b * 32, c) : q4_absmax(src + b * 32, c);
+        uint8_t* o = out + b * 18;
+        put_le16(o, oracle_f32_to_fp16(d));
+        for (int j = 0; j < 16; ++j) o[2 + j] = (uint8_t)(c[j] | (c[j + 16] << 4));
     }
     return 0;
 }

@@ -47,3 +47,29 @@ def bandwidth_rows():
                 out.append((FMTS[fmt], int(n_in), int(n_out), int(ntok), float(ous), float(ogbs),
                             float(nus), float(ngbs)))
     return out
+
+
+def quant_vectors():
+    return sorted(n for n in os.listdir(GOLDEN) if n.startswith("q") and n.endswith(".txt"))
+
+
+def load_quant(name):
+    """A hand-quantized block: fmt, method (0 absmax, 1 Lloyd), v fp32[32], d bits, codes."""
+    out = {}
+    with open(os.path.join(GOLDEN, name)) as f:
+        for line in f:
+            line = line.split("#", 1)[0].strip()
+            if not line:
+                continue
+            key, *vals = line.split()
+            if key == "fmt":
+                out["fmt"] = FMTS[vals[0]]
+            elif key == "method":
+                out["method"] = {"absmax": 0, "lloyd": 1}[vals[0]]
+            elif key == "v":
+                out["v"] = np.array([float(v) for v in vals], dtype=np.float32)
+            elif key == "d":
+                out["d"] = int(vals[0], 16)
+            elif key == "codes":
+                out["codes"] = np.array([int(v) for v in vals], dtype=np.int64)
+    return out

@@ -221,3 +221,19 @@ def test_binding_refuses_cpu_tensors(lib):
 def test_rows_subset_argument_errors(lib, args, status):
     assert _lib.qgemv_rows(*args) == status, _lib.last_error()
     assert _lib.last_error()
+
+
+@pytest.mark.parametrize("call, status", [
+    (lambda: _lib.qg_quantize_q8_0(4, 64, 0, Y0), _lib.QG_EINVAL),              # null src
+    (lambda: _lib.qg_quantize_q8_0(4, 64, X0, 0), _lib.QG_EINVAL),              # null dst
+    (lambda: _lib.qg_quantize_q8_0(0, 64, X0, Y0), _lib.QG_EINVAL),             # no rows
+    (lambda: _lib.qg_quantize_q8_0(4, 48, X0, Y0), _lib.QG_EINVAL),             # partial block
+    (lambda: _lib.qg_quantize_q8_0(4, 64, X0 + 4, Y0), _lib.QG_EALIGN),         # src misaligned
+    (lambda: _lib.qg_quantize_q4_0(4, 64, 0, X0, Y0 + 2, None), _lib.QG_EALIGN),  # dst misaligned
+    (lambda: _lib.qg_quantize_q4_0(4, 64, 2, X0, Y0, None), _lib.QG_EINVAL),    # unknown method
+    (lambda: _lib.qg_quantize_q4_0(4, 64, 1, X0, X0 + 256, None), _lib.QG_EINVAL),  # dst overlaps src
+    (lambda: _lib.qg_quantize_q8_0(1, 1 << 25, X0, Y0), _lib.QG_EUNSUPPORTED),  # cols beyond range
+])
+def test_quantizer_argument_errors(lib, call, status):
+    assert call() == status, _lib.last_error()
+    assert _lib.last_error()
