@@ -248,6 +248,66 @@ def other_workloads(torch, stream):
                            pct_peak=round(100 * nb / us / 1e3 / HBM_PEAK_GBS, 1))
     out["c5_q4_0_experts"] = dict(table_bytes=table, ring_copies=len(ring), topk=topk, per_T=res)
     del ring
+    # the routed-experts layer: gate+up (one launch, two tables) then down, at the
+    # audit's expert overlap (share 0.65) and with none; bytes = distinct experts'
+    # gate, up and down tables
+    L = I.EXPERT_LAYER
+    E, ff, emb, topk, lf = L["n_experts"], L["n_ff"], L["n_embd"], L["topk"], L["fmt"]
+    tb = _lib.qg_packed_bytes(lf, E * ff, emb)  # one table (gate, up and down are the same size)
+    copies = max(1, -(-RING_BYTES // (3 * tb)))
+    tabs = [[torch.randint(0, 256, (tb,), dtype=torch.uint8, device="cuda") for _ in range(3)] for _ in range(copies)]
+    x = torch.randn(4, emb, device="cuda")
+    h = torch.randn(4, topk, ff, device="cuda")
+    yg = torch.empty(4, topk, ff, device="cuda")
+    yu = torch.empty_like(yg)
+    yd = torch.empty(4, topk, emb, device="cuda")
+    for share in ("0.65", "0"):
+        res = {}
+        for T in (1, 2, 3, 4):
+            unique = I.UNIQUE_AT_SHARE_065[T] if share == "0.65" else topk * T
+            ids = torch.from_numpy(I.expert_ids_shared(I.rng_for(T), E, T, topk, unique)).cuda()
+            def gu(i, T=T, ids=ids):
+                Wg, Wu, _ = tabs[i % copies]
+                st = _lib.qgemv_experts_gate_up(lf, E, ff, emb, T, topk, ids.data_ptr(), Wg.data_ptr(), Wu.data_ptr(),
+                                                x.data_ptr(), yg.data_ptr(), yu.data_ptr(), sp)
+                if st:
+                    _lib.check(st, "gate_up")
+            def dn(i, T=T, ids=ids):
+                st = _lib.qgemv_experts_down(lf, E, emb, ff, T, topk, ids.data_ptr(), tabs[i % copies][2].data_ptr(),
+                                             h.data_ptr(), yd.data_ptr(), sp)
+                if st:
+                    _lib.check(st, "down")
+            def layer(i):
+                gu(i)
+                dn(i)
+            per = tb // E
+            r = {}
+            for label, fn, nbytes in (("gate_up", gu, 2 * unique * per), ("down", dn, unique * per),
+                                      ("layer", layer, 3 * unique * per)):
+                us = time_entry(torch, stream, fn, 1000)
+                r[label] = dict(us_per_call=round(us, 3), bytes_read=nbytes, gbs=round(nbytes / us / 1e3, 1),
+                                pct_peak=round(100 * nbytes / us / 1e3 / HBM_PEAK_GBS, 1))
+            res[str(T)] = dict(distinct_experts=unique, **r)
+        out[f"expert_layer_q4_0_share{share}"] = dict(table_bytes=tb, ring_copies=copies, per_T=res)
+    del tabs
+    # on-device quantizers: fp32 in, packed blocks out; bytes = fp32 read + packed written
+    for label, fmt, method, rows, cols in (("quantize_q8_0_10240x2560", I.FMT_Q8_0, 0, 10240, 2560),
+                                           ("quantize_q4_0_absmax_8192x2560", I.FMT_Q4_0, 0, 8192, 2560),
+                                           ("quantize_q4_0_lloyd_8192x2560", I.FMT_Q4_0, 1, 8192, 2560)):
+        sb = rows * cols * 4
+        nb = _lib.qg_packed_bytes(fmt, rows, cols)
+        srcs = [torch.randn(rows, cols, device="cuda") * 0.02 for _ in range(max(1, -(-RING_BYTES // sb)))]
+        dst = torch.empty(nb, dtype=torch.uint8, device="cuda")
+        def launch(i, fmt=fmt, method=method, rows=rows, cols=cols):
+            a = srcs[i % len(srcs)].data_ptr()
+            st = (_lib.qg_quantize_q8_0(rows, cols, a, dst.data_ptr(), sp) if fmt == I.FMT_Q8_0 else
+                  _lib.qg_quantize_q4_0(rows, cols, method, a, dst.data_ptr(), sp))
+            if st:
+                _lib.check(st, "quantize")
+        us = time_entry(torch, stream, launch, 300)
+        out[label] = dict(bytes_per_call=sb + nb, read=sb, written=nb, ring_copies=len(srcs), us_per_call=round(us, 3),
+                          gbs=round((sb + nb) / us / 1e3, 1), pct_peak=round(100 * (sb + nb) / us / 1e3 / HBM_PEAK_GBS, 1))
+        del srcs
     return out
 
 

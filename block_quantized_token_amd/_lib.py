@@ -19,7 +19,8 @@ QG_TILE_FIELDS = 8
 EXPORTS = (
     "qgemv_q8_0", "qgemv_q4_0", "qgemv_bf16", "qgemv_grouped_experts", "qgemv_argmax", "qgemv_rows", "qg_packed_bytes",
     "qg_pack_q8_0", "qg_unpack_q8_0", "qg_pack_q4_0", "qg_unpack_q4_0", "qg_query_tile",
-    "qg_status_string", "qg_last_error", "qg_quantize_q8_0", "qg_quantize_q4_0",
+    "qg_status_string", "qg_last_error", "qg_quantize_q8_0", "qg_quantize_q4_0", "qgemv_experts_gate_up",
+    "qgemv_experts_down",
 )
 QG_Q4_ABSMAX, QG_Q4_LLOYD = 0, 1
 
@@ -48,6 +49,10 @@ def load() -> ctypes.CDLL:
         f.argtypes = [i64, i64, i32, vp, vp, vp, vp]
     L.qgemv_grouped_experts.restype = i32
     L.qgemv_grouped_experts.argtypes = [i32, i64, i64, i64, i32, i32, vp, vp, vp, vp, vp]
+    L.qgemv_experts_gate_up.restype = i32
+    L.qgemv_experts_gate_up.argtypes = [i32, i64, i64, i64, i32, i32, vp, vp, vp, vp, vp, vp, vp]
+    L.qgemv_experts_down.restype = i32
+    L.qgemv_experts_down.argtypes = [i32, i64, i64, i64, i32, i32, vp, vp, vp, vp, vp]
     L.qgemv_rows.restype = i32
     L.qgemv_rows.argtypes = [i32, i64, i64, i64, vp, i32, vp, vp, vp, vp]
     L.qgemv_argmax.restype = i32
@@ -100,6 +105,14 @@ def qgemv_bf16(rows, cols, T, W, x, y, stream=None) -> int:
 
 def qgemv_grouped_experts(fmt, n_experts, rows, cols, T, topk, ids, W, x, y, stream=None) -> int:
     return load().qgemv_grouped_experts(fmt, n_experts, rows, cols, T, topk, ids, W, x, y, stream)
+
+
+def qgemv_experts_gate_up(fmt, n_experts, rows, cols, T, topk, ids, Wg, Wu, x, yg, yu, stream=None) -> int:
+    return load().qgemv_experts_gate_up(fmt, n_experts, rows, cols, T, topk, ids, Wg, Wu, x, yg, yu, stream)
+
+
+def qgemv_experts_down(fmt, n_experts, rows, cols, T, topk, ids, W, h, y, stream=None) -> int:
+    return load().qgemv_experts_down(fmt, n_experts, rows, cols, T, topk, ids, W, h, y, stream)
 
 
 def qgemv_rows(fmt, rows, cols, n_sel, ids, T, W, x, y, stream=None) -> int:

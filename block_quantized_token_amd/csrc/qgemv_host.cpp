@@ -407,6 +407,92 @@ int run_rows(int fmt, int64_t rows, int64_t cols, int64_t n_sel, const int32_t* 
     return ok();
 }
 
+// Grouped experts: one table (W), or two tables of the same shape in one launch
+// (W2, outputs y2: gate and up); x per token [T][cols] or per slot
+// [T][topk][cols] (per_slot: the down projection).
+int run_grouped(int fmt, int64_t n_experts, int64_t rows, int64_t cols, int T, int topk, const int32_t* ids,
+                const void* W, const void* W2, const float* x, float* y, float* y2, int per_slot, void* stream) {
+    int64_t rbytes = 0;
+    int st = check_common(fmt, rows, cols, T, W, x, y, &rbytes);
+    if (st) return st;
+    const int parts = W2 ? 2 : 1;
+    if (W2 && (!aligned(W2, 16) || !aligned(y2, 4))) return fail(QG_EALIGN, "Wu must be 16-byte and yu 4-byte aligned");
+    if (!ids) return fail(QG_EINVAL, "null ids");
+    if (n_experts < 1 || n_experts > 0x7FFFFFFF) return fail(QG_EINVAL, "n_experts=%lld must be in 1..2^31-1", (long long)n_experts);
+    if (topk < 1 || topk > 4096) return fail(QG_EINVAL, "topk=%d must be in 1..4096", topk);
+    if (!aligned(ids, 4)) return fail(QG_EALIGN, "ids must be 4-byte aligned");
+    const int64_t ebytes = rbytes * rows;
+    if (ebytes > INT64_MAX / n_experts) return fail(QG_EUNSUPPORTED, "expert table too large");
+    const size_t ybytes = (size_t)T * topk * rows * 4, wbytes = (size_t)(ebytes * n_experts);
+    const size_t xbytes = (size_t)T * (per_slot ? topk : 1) * cols * 4;
+    float* outs[2] = {y, y2};
+    for (int p = 0; p < parts; ++p)
+        if (overlap(outs[p], ybytes, W, wbytes) || overlap(outs[p], ybytes, x, xbytes) ||
+            overlap(outs[p], ybytes, ids, (size_t)T * topk * 4) || (W2 && overlap(outs[p], ybytes, W2, wbytes)))
+            return fail(QG_EINVAL, "an output overlaps W, x or ids");
+    if (parts == 2 && overlap(y, ybytes, y2, ybytes)) return fail(QG_EINVAL, "yg and yu overlap");
+    Tile tile;
+    if ((st = pick_tile(fmt, rows, cols, QG_MAX_T, &tile))) return st;  // one kernel for 1..4 tokens per expert
+    const int64_t nsl = (cols + kSlice - 1) / kSlice;
+    std::string why;
+    Tile probe = tile;
+    const bool overridden = tile_override(fmt, &probe, &why) == 1;
+    if (!overridden && row_bytes(fmt, cols) % 16 == 0 && nsl <= kMaxWaves) {
+        // LDS-DMA streamed, x staged apart (any number of tokens per expert fits
+        // one ring of two slots).  Rows per workgroup: the workgroups of all
+        // slots (at most T * topk distinct experts) fit in about one round of
+        // two workgroups per CU.
+        tile.kind = 3;
+        tile.depth = 2;
+        tile.mfma = 0;
+        tile.rows_per_batch = 4;
+        // fewer than 4 k slices (the down projection's short rows): row groups of
+        // waves share the workgroup's rows, 4 waves or more in all
+        const int64_t rg = nsl >= 4 ? 1 : (4 + nsl - 1) / nsl;
+        tile.waves_per_wg = (int)(nsl * rg);
+        int64_t rw = ((int64_t)T * topk * parts * rows / 480 + 7) / 8 * 8;
+        tile.rows_per_wg = (int)(rw < 16 * rg ? 16 * rg : rw > 256 ? 256 : rw);
+        if (dma_lds_bytes(fmt, tile, T, (int)nsl) > kMaxLds) tile.kind = 1;  // fall back below
+    }
+    if (tile.kind == 2 || tile.kind == 3) {  // any DMA tile runs the grouped DMA kernel, x staged apart
+        tile.kind = 3;
+        if (tile.depth != 3) tile.depth = 2;
+        if (tile.waves_per_wg % nsl != 0 || dma_lds_bytes(fmt, tile, T, (int)nsl) > kMaxLds) tile.kind = 1;
+    }
+    if (tile.kind != 0 && tile.kind != 3) {  // the grouped kernel runs the direct path: one wave per slice
+        tile.kind = 0;
+        tile.depth = 0;
+        tile.mfma = 0;
+        if (tile.waves_per_wg > nsl) tile.waves_per_wg = (int)nsl;
+        tile.rows_per_wg = 2 * tile.rows_per_batch;
+        if (!tile_supported(fmt, QG_MAX_T, tile.rows_per_batch, one_shot(tile, (int)((cols + kSlice - 1) / kSlice))))
+            tile.rows_per_batch = 2, tile.rows_per_wg = 4;
+    }
+    GroupedArgs a;
+    a.W = (const uint8_t*)W;
+    a.x = x;
+    a.y = y;
+    a.ids = ids;
+    a.rows = rows;
+    a.row_bytes = rbytes;
+    a.expert_bytes = ebytes;
+    a.n_experts = (int)n_experts;
+    a.cols = (int)cols;
+    a.nslices = (int)((cols + kSlice - 1) / kSlice);
+    a.rows_per_wg = tile.rows_per_wg;
+    a.tiles_per_expert = (int)((rows + tile.rows_per_wg - 1) / tile.rows_per_wg);
+    a.T = T;
+    a.topk = topk;
+    a.W2 = (const uint8_t*)W2;
+    a.y2 = y2;
+    a.parts = parts;
+    a.per_slot_x = per_slot;
+    if ((int64_t)T * topk * a.tiles_per_expert * parts > 0x7FFFFFFF) return fail(QG_EUNSUPPORTED, "grid too large");
+    int err = launch_grouped(fmt, tile, a, stream);
+    if (err) return fail(QG_EHIP, "kernel launch failed: %s", hip_error_name(err));
+    return ok();
+}
+
 // Quantizers: kind 0 Q8_0, 1 Q4_0 absmax, 2 Q4_0 Lloyd.
 int run_quantize(int kind, int64_t rows, int64_t cols, const float* src, void* dst, void* stream) {
     const char* name = kind == 0 ? "qg_quantize_q8_0" : "qg_quantize_q4_0";
@@ -457,72 +543,18 @@ int qgemv_argmax(int fmt, int64_t rows, int64_t cols, int T, const void* W, cons
 
 int qgemv_grouped_experts(int fmt, int64_t n_experts, int64_t rows, int64_t cols, int T, int topk,
                           const int32_t* ids, const void* W, const float* x, float* y, void* stream) {
-    int64_t rbytes = 0;
-    int st = check_common(fmt, rows, cols, T, W, x, y, &rbytes);
-    if (st) return st;
-    if (!ids) return fail(QG_EINVAL, "null ids");
-    if (n_experts < 1 || n_experts > 0x7FFFFFFF) return fail(QG_EINVAL, "n_experts=%lld must be in 1..2^31-1", (long long)n_experts);
-    if (topk < 1 || topk > 4096) return fail(QG_EINVAL, "topk=%d must be in 1..4096", topk);
-    if (!aligned(ids, 4)) return fail(QG_EALIGN, "ids must be 4-byte aligned");
-    const int64_t ebytes = rbytes * rows;
-    if (ebytes > INT64_MAX / n_experts) return fail(QG_EUNSUPPORTED, "expert table too large");
-    const size_t ybytes = (size_t)T * topk * rows * 4;
-    if (overlap(y, ybytes, W, (size_t)(ebytes * n_experts)) || overlap(y, ybytes, x, (size_t)T * cols * 4) ||
-        overlap(y, ybytes, ids, (size_t)T * topk * 4))
-        return fail(QG_EINVAL, "y overlaps W, x or ids");
-    Tile tile;
-    if ((st = pick_tile(fmt, rows, cols, QG_MAX_T, &tile))) return st;  // one kernel for 1..4 tokens per expert
-    const int64_t nsl = (cols + kSlice - 1) / kSlice;
-    std::string why;
-    Tile probe = tile;
-    const bool overridden = tile_override(fmt, &probe, &why) == 1;
-    if (!overridden && row_bytes(fmt, cols) % 16 == 0 && nsl <= kMaxWaves) {
-        // LDS-DMA streamed, x staged apart (any number of tokens per expert fits
-        // one ring of two slots).  Rows per workgroup: the workgroups of all
-        // slots (at most T * topk distinct experts) fit in about one round of
-        // two workgroups per CU.
-        tile.kind = 3;
-        tile.depth = 2;
-        tile.mfma = 0;
-        tile.rows_per_batch = 4;
-        tile.waves_per_wg = (int)nsl;
-        int64_t rw = ((int64_t)T * topk * rows / 480 + 7) / 8 * 8;
-        tile.rows_per_wg = (int)(rw < 16 ? 16 : rw > 256 ? 256 : rw);
-        if (dma_lds_bytes(fmt, tile, T, (int)nsl) > kMaxLds) tile.kind = 1;  // fall back below
-    }
-    if (tile.kind == 2 || tile.kind == 3) {  // any DMA tile runs the grouped DMA kernel, x staged apart
-        tile.kind = 3;
-        if (tile.depth != 3) tile.depth = 2;
-        if (tile.waves_per_wg % nsl != 0 || dma_lds_bytes(fmt, tile, T, (int)nsl) > kMaxLds) tile.kind = 1;
-    }
-    if (tile.kind != 0 && tile.kind != 3) {  // the grouped kernel runs the direct path: one wave per slice
-        tile.kind = 0;
-        tile.depth = 0;
-        tile.mfma = 0;
-        if (tile.waves_per_wg > nsl) tile.waves_per_wg = (int)nsl;
-        tile.rows_per_wg = 2 * tile.rows_per_batch;
-        if (!tile_supported(fmt, QG_MAX_T, tile.rows_per_batch, one_shot(tile, (int)((cols + kSlice - 1) / kSlice))))
-            tile.rows_per_batch = 2, tile.rows_per_wg = 4;
-    }
-    GroupedArgs a;
-    a.W = (const uint8_t*)W;
-    a.x = x;
-    a.y = y;
-    a.ids = ids;
-    a.rows = rows;
-    a.row_bytes = rbytes;
-    a.expert_bytes = ebytes;
-    a.n_experts = (int)n_experts;
-    a.cols = (int)cols;
-    a.nslices = (int)((cols + kSlice - 1) / kSlice);
-    a.rows_per_wg = tile.rows_per_wg;
-    a.tiles_per_expert = (int)((rows + tile.rows_per_wg - 1) / tile.rows_per_wg);
-    a.T = T;
-    a.topk = topk;
-    if ((int64_t)T * topk * a.tiles_per_expert > 0x7FFFFFFF) return fail(QG_EUNSUPPORTED, "grid too large");
-    int err = launch_grouped(fmt, tile, a, stream);
-    if (err) return fail(QG_EHIP, "kernel launch failed: %s", hip_error_name(err));
-    return ok();
+    return run_grouped(fmt, n_experts, rows, cols, T, topk, ids, W, nullptr, x, y, nullptr, 0, stream);
+}
+
+int qgemv_experts_gate_up(int fmt, int64_t n_experts, int64_t rows, int64_t cols, int T, int topk, const int32_t* ids,
+                          const void* Wg, const void* Wu, const float* x, float* yg, float* yu, void* stream) {
+    if (!Wu || !yu) return fail(QG_EINVAL, "null pointer (Wu=%p yu=%p)", Wu, (void*)yu);
+    return run_grouped(fmt, n_experts, rows, cols, T, topk, ids, Wg, Wu, x, yg, yu, 0, stream);
+}
+
+int qgemv_experts_down(int fmt, int64_t n_experts, int64_t rows, int64_t cols, int T, int topk, const int32_t* ids,
+                       const void* W, const float* h, float* y, void* stream) {
+    return run_grouped(fmt, n_experts, rows, cols, T, topk, ids, W, nullptr, h, y, nullptr, 1, stream);
 }
 
 int qg_quantize_q8_0(int64_t rows, int64_t cols, const float* src, void* dst, void* stream) {

@@ -153,6 +153,10 @@ struct GroupedArgs {
     int tiles_per_expert;
     int T;
     int topk;
+    const uint8_t* W2;  // parts == 2: the second table (up, beside gate in W), same shape
+    float* y2;          // parts == 2: its outputs, [T][topk][rows]
+    int parts;          // 1, or 2 (W and W2 in one launch)
+    int per_slot_x;     // 0: x is [T][cols], one row per token; 1: [T][topk][cols], one per slot
 };
 
 // Launchers (qgemv_kernels.hip).  Return a hipError_t value as int.

@@ -1562,139 +1562,208 @@ __global__ void __launch_bounds__(64 * kMaxWaves) qgemv_mfma_q8_kernel(DenseArgs
                     [=](int t, int64_t row, float v) { y[t * rows + row] = v; });
 }
 
-// Grouped experts: workgroup (slot, tile) with slot = (t, j).  The workgroup of
-// the first slot that names expert e streams e's rows once for every token that
-// chose e (the M5 audit's expert grouping, section 1 item 2, done here inside
-// each workgroup from the tiny ids array instead of a separate plan pass);
-// workgroups of later slots with the same e exit at once.
-template <int FMT, int NE, int RB, bool ONE_SHOT>
-__device__ __forceinline__ void grouped_run(const GroupedArgs& a, int e, uint32_t tokmask, int64_t row_begin, int64_t row_end) {
-    const uint32_t tokmask0 = tokmask;
-    int tk[NE];  // the NE tokens that chose e, ascending
-#pragma unroll
-    for (int n = 0; n < NE; ++n) {
-        tk[n] = __builtin_ctz(tokmask);
-        tokmask &= tokmask - 1;
-    }
-    int64_t xoff[NE];
-#pragma unroll
-    for (int n = 0; n < NE; ++n) xoff[n] = (int64_t)tk[n] * a.cols;
-    const int32_t* __restrict__ ids = a.ids;
-    float* __restrict__ y = a.y;
-    const int topk = a.topk;
-    const int64_t rows = a.rows;
-    gemv_rows<FMT, NE, RB, ONE_SHOT>(a.W + (int64_t)e * a.expert_bytes, a.row_bytes, a.cols, a.nslices, a.x, xoff, row_begin,
-                           row_end, [=](int n, int64_t row, float v) {
-                               // token of output n: the n-th set bit of tokmask (n varies
-                               // across lanes, so no array indexing here)
-                               uint32_t m = tokmask0;
-                               for (int i = 0; i < n; ++i) m &= m - 1;
-                               const int t = __builtin_ctz(m);
-                               for (int j = 0; j < topk; ++j)
-                                   if (ids[t * topk + j] == e) y[((int64_t)t * topk + j) * rows + row] = v;
-                           });
+// Grouped experts: workgroup (slot, part, tile) with slot = (t, j).  Each
+// expert's rows are streamed once for every token that chose it (the M5
+// audit's expert grouping, section 1 item 2, done here inside each workgroup
+// from the tiny ids array instead of a separate plan pass): the n workgroups
+// whose slots name expert e split each tile of e's rows n ways, and each
+// computes its share for all of e's tokens, so sharing costs no parallelism.
+// Two parts: the gate and up tables of one expert in one launch (part 1 reads
+// W2, writes y2).  Per-slot inputs (the down projection, whose input differs
+// for every (token, expert) pair): the slots naming e form groups of up to T,
+// each with its own x row, and the members of a group split its rows.
+
+// The outputs a serving workgroup computes: ne activation vectors (tokens, or
+// slots with per-slot inputs) and where each result goes.
+struct GroupTargets {
+    uint32_t tokmask;  // per-token inputs: bit t set = token t chose e
+    uint64_t slots;    // per-slot inputs: up to 4 slot indices, 16 bits each
+    int ne;
+    int rank, nwork;   // this workgroup's share of the rows: rank of nwork
+};
+
+// The share `rank` of `nwork` of a row range, in whole 8-row tiles (possibly empty).
+__device__ __forceinline__ void share_rows(const GroupTargets& g, int64_t& row_begin, int64_t& row_end) {
+    const int64_t nt = (row_end - row_begin + 7) / 8;
+    const int64_t t0 = nt * g.rank / g.nwork, t1 = nt * (g.rank + 1) / g.nwork;
+    const int64_t e = row_begin + 8 * t1;
+    row_begin += 8 * t0;
+    if (e < row_end) row_end = e;
 }
 
-// The slot / row range of a grouped workgroup and the expert it serves.  Returns
-// false when the workgroup has nothing to do: its id is out of range (its
-// output rows are then filled with NaN) or an earlier slot names the same
-// expert (that slot's workgroup computes it for every token).
-__device__ __forceinline__ bool grouped_slot(const GroupedArgs& a, int& e, int64_t& row_begin, int64_t& row_end) {
-    const int slot = blockIdx.x / a.tiles_per_expert;
-    const int tile = blockIdx.x % a.tiles_per_expert;
+template <int NE>
+__device__ __forceinline__ void group_offsets(const GroupedArgs& a, const GroupTargets& g, int64_t (&xoff)[NE]) {
+    uint32_t m = g.tokmask;
+#pragma unroll
+    for (int n = 0; n < NE; ++n) {
+        if (a.per_slot_x) {
+            xoff[n] = (int64_t)((g.slots >> (16 * n)) & 0xFFFF) * a.cols;
+        } else {
+            xoff[n] = (int64_t)__builtin_ctz(m) * a.cols;
+            m &= m - 1;
+        }
+    }
+}
+
+// Output n of a tile row: per-slot, its slot's row; per-token, every slot of the
+// n-th token that names e (n varies across lanes, so no array indexing here).
+__device__ __forceinline__ void group_store(const GroupedArgs& a, float* __restrict__ y, int e, const GroupTargets& g,
+                                            int n, int64_t row, float v) {
+    if (a.per_slot_x) {
+        const int slot = (int)((g.slots >> (16 * n)) & 0xFFFF);
+        y[(int64_t)slot * a.rows + row] = v;
+        return;
+    }
+    uint32_t m = g.tokmask;
+    for (int i = 0; i < n; ++i) m &= m - 1;
+    const int t = __builtin_ctz(m);
+    for (int j = 0; j < a.topk; ++j)
+        if (a.ids[t * a.topk + j] == e) y[((int64_t)t * a.topk + j) * a.rows + row] = v;
+}
+
+template <int FMT, int NE, int RB, bool ONE_SHOT>
+__device__ __forceinline__ void grouped_run(const GroupedArgs& a, const uint8_t* W, float* y, int e, const GroupTargets& g,
+                                            int64_t row_begin, int64_t row_end) {
+    int64_t xoff[NE];
+    group_offsets<NE>(a, g, xoff);
+    gemv_rows<FMT, NE, RB, ONE_SHOT>(W + (int64_t)e * a.expert_bytes, a.row_bytes, a.cols, a.nslices, a.x, xoff, row_begin,
+                                     row_end, [=](int n, int64_t row, float v) { group_store(a, y, e, g, n, row, v); });
+}
+
+// The slot, part and row range of a grouped workgroup and the expert it serves.
+// Returns false when its id is out of range: its output rows are then NaN.
+__device__ __forceinline__ bool grouped_slot(const GroupedArgs& a, int& e, const uint8_t*& W, float*& y,
+                                             int64_t& row_begin, int64_t& row_end) {
+    const int per_slot = a.tiles_per_expert * a.parts;
+    const int slot = blockIdx.x / per_slot;
+    int tile = blockIdx.x % per_slot;
+    const int part = tile >= a.tiles_per_expert;
+    tile -= part * a.tiles_per_expert;
+    W = part ? a.W2 : a.W;
+    y = part ? a.y2 : a.y;
     row_begin = (int64_t)tile * a.rows_per_wg;
     row_end = row_begin + a.rows_per_wg < a.rows ? row_begin + a.rows_per_wg : a.rows;
     e = a.ids[slot];
     if (e < 0 || e >= a.n_experts) {  // precondition violated: make it visible
-        float* yrow = a.y + (int64_t)slot * a.rows;
+        float* yrow = y + (int64_t)slot * a.rows;
         for (int64_t r = row_begin + threadIdx.x; r < row_end; r += blockDim.x) yrow[r] = __builtin_nanf("");
         return false;
     }
     return true;
 }
 
-// One pass over ids, 64 at a time in parallel lanes: does an earlier slot name e
-// (false: that slot's workgroup serves it), and which tokens chose e.
-__device__ __forceinline__ bool grouped_tokens(const GroupedArgs& a, int e, uint32_t& tokmask) {
-    const int slot = blockIdx.x / a.tiles_per_expert;
+// Bits of a 64-slot chunk starting at c that lie below `slot`.
+__device__ __forceinline__ uint64_t below(int slot, int c) {
+    return slot - c >= 64 ? ~0ull : slot - c <= 0 ? 0ull : (1ull << (slot - c)) - 1;
+}
+
+// Passes over ids, 64 at a time in parallel lanes: whom this workgroup computes
+// for and its share of the rows.  Per-token inputs: every token that chose e;
+// the workers are the slots naming e.  Per-slot inputs: the slots naming e in
+// rank order form groups of T (one group when every token names an expert at
+// most once); the workers are the group's slots.
+__device__ __forceinline__ void grouped_targets(const GroupedArgs& a, int e, GroupTargets& g) {
+    const int slot = blockIdx.x / (a.tiles_per_expert * a.parts);
     const int n = a.T * a.topk;
     const int lane = threadIdx.x & 63;
-    bool earlier = false;
-    tokmask = 0;  // bit t: token t chose e
+    g.tokmask = 0;
+    g.slots = 0;
+    g.ne = 0;
+    int before = 0, total = 0;
     for (int c = 0; c < n; c += 64) {
         const int i = c + lane;
         const bool m = i < n && a.ids[i] == e;
-        earlier |= __ballot(m && i < slot) != 0;
-        for (int t = 0; t < a.T; ++t)
-            if (__ballot(m && i / a.topk == t) != 0) tokmask |= 1u << t;
+        const uint64_t b = __ballot(m);  // uniform
+        before += __builtin_popcountll(b & below(slot, c));
+        total += __builtin_popcountll(b);
+        if (!a.per_slot_x)
+            for (int t = 0; t < a.T; ++t)
+                if (__ballot(m && i / a.topk == t) != 0) g.tokmask |= 1u << t;
     }
-    return !earlier;
-}
-
-__device__ __forceinline__ bool grouped_prologue(const GroupedArgs& a, int& e, uint32_t& tokmask, int64_t& row_begin,
-                                                 int64_t& row_end) {
-    return grouped_slot(a, e, row_begin, row_end) && grouped_tokens(a, e, tokmask);
+    if (!a.per_slot_x) {
+        g.ne = __builtin_popcount(g.tokmask);
+        g.rank = before;
+        g.nwork = total;
+        return;
+    }
+    const int G = a.T;  // inputs per group: at most T, what the workgroup's LDS is sized for
+    const int g0 = before / G * G;
+    g.rank = before - g0;
+    g.nwork = total - g0 < G ? total - g0 : G;
+    int rank = 0;  // rank of the first slot of the chunk among e's slots
+    for (int c = 0; c < n && g.ne < g.nwork; c += 64) {
+        const int i = c + lane;
+        uint64_t b = __ballot(i < n && a.ids[i] == e);
+        for (; b && g.ne < g.nwork; b &= b - 1, ++rank)
+            if (rank >= g0) {
+                g.slots |= (uint64_t)(c + __builtin_ctzll(b)) << (16 * g.ne);
+                ++g.ne;
+            }
+    }
 }
 
 template <int FMT, int RB, bool ONE_SHOT>
 __global__ void __launch_bounds__(64 * kMaxWaves) qgemv_grouped_kernel(GroupedArgs a) {
     int e;
-    uint32_t tokmask;
+    const uint8_t* W;
+    float* y;
     int64_t row_begin, row_end;
-    if (!grouped_prologue(a, e, tokmask, row_begin, row_end)) return;
-    switch (__builtin_popcount(tokmask)) {
-    case 1: grouped_run<FMT, 1, RB, ONE_SHOT>(a, e, tokmask, row_begin, row_end); break;
-    case 2: grouped_run<FMT, 2, RB, ONE_SHOT>(a, e, tokmask, row_begin, row_end); break;
-    case 3: grouped_run<FMT, 3, RB, ONE_SHOT>(a, e, tokmask, row_begin, row_end); break;
-    default: grouped_run<FMT, 4, RB, ONE_SHOT>(a, e, tokmask, row_begin, row_end); break;
+    GroupTargets g;
+    if (!grouped_slot(a, e, W, y, row_begin, row_end)) return;
+    grouped_targets(a, e, g);
+    share_rows(g, row_begin, row_end);
+    if (row_begin >= row_end) return;
+    switch (g.ne) {
+    case 1: grouped_run<FMT, 1, RB, ONE_SHOT>(a, W, y, e, g, row_begin, row_end); break;
+    case 2: grouped_run<FMT, 2, RB, ONE_SHOT>(a, W, y, e, g, row_begin, row_end); break;
+    case 3: grouped_run<FMT, 3, RB, ONE_SHOT>(a, W, y, e, g, row_begin, row_end); break;
+    default: grouped_run<FMT, 4, RB, ONE_SHOT>(a, W, y, e, g, row_begin, row_end); break;
     }
 }
 
 // Grouped experts on the LDS-DMA streamed path (x staged apart, so any number of
-// tokens per expert fits the same ring).
-template <int FMT, int NE, int D>
-__device__ __forceinline__ void grouped_dma_run(const GroupedArgs& a, int e, uint32_t tokmask, int64_t row_begin,
-                                                int64_t row_end) {
-    const uint32_t tokmask0 = tokmask;
+// inputs per expert fits the same ring).
+template <int FMT, int NE, int D, bool PRE>
+__device__ __forceinline__ void grouped_dma_run(const GroupedArgs& a, const uint8_t* W, float* y, int e,
+                                                const GroupTargets& g, int64_t row_begin, int64_t row_end) {
     int64_t xoff[NE];
-#pragma unroll
-    for (int n = 0; n < NE; ++n) {
-        xoff[n] = (int64_t)__builtin_ctz(tokmask) * a.cols;
-        tokmask &= tokmask - 1;
+    group_offsets<NE>(a, g, xoff);
+    auto out = [=](int n, int64_t row, float v) { group_store(a, y, e, g, n, row, v); };
+    dma_rows<FMT, NE, 8, D, true, decltype(out)&, PRE>(W + (int64_t)e * a.expert_bytes, a.row_bytes, a.cols, a.nslices,
+                                                     a.x, xoff, row_begin, row_end, out);
+}
+
+template <int FMT, int D, bool PRE>
+__device__ __forceinline__ void grouped_dma_switch(const GroupedArgs& a, const uint8_t* W, float* y, int e,
+                                                   const GroupTargets& g, int64_t row_begin, int64_t row_end) {
+    switch (g.ne) {
+    case 1: grouped_dma_run<FMT, 1, D, PRE>(a, W, y, e, g, row_begin, row_end); break;
+    case 2: grouped_dma_run<FMT, 2, D, PRE>(a, W, y, e, g, row_begin, row_end); break;
+    case 3: grouped_dma_run<FMT, 3, D, PRE>(a, W, y, e, g, row_begin, row_end); break;
+    default: grouped_dma_run<FMT, 4, D, PRE>(a, W, y, e, g, row_begin, row_end); break;
     }
-    const int32_t* __restrict__ ids = a.ids;
-    float* __restrict__ y = a.y;
-    const int topk = a.topk;
-    const int64_t rows = a.rows;
-    auto out = [=](int n, int64_t row, float v) {
-                                      uint32_t m = tokmask0;  // token of output n: the n-th set bit
-                                      for (int i = 0; i < n; ++i) m &= m - 1;
-                                      const int t = __builtin_ctz(m);
-                                      for (int j = 0; j < topk; ++j)
-                                          if (ids[t * topk + j] == e) y[((int64_t)t * topk + j) * rows + row] = v;
-                                  };
-    dma_rows<FMT, NE, 8, D, true, decltype(out)&, true>(a.W + (int64_t)e * a.expert_bytes, a.row_bytes, a.cols,
-                                                      a.nslices, a.x, xoff, row_begin, row_end, out);
 }
 
 template <int FMT, int D>
 __global__ void __launch_bounds__(64 * kMaxWaves) qgemv_grouped_dma_kernel(GroupedArgs a) {
     int e;
-    uint32_t tokmask;
+    const uint8_t* W;
+    float* y;
     int64_t row_begin, row_end;
-    if (!grouped_slot(a, e, row_begin, row_end)) return;
-    // the expert's weights start streaming while the ids are scanned
-    dma_prefetch<FMT, 8, D>(a.W + (int64_t)e * a.expert_bytes, a.row_bytes, a.nslices, row_begin, row_end);
-    if (!grouped_tokens(a, e, tokmask)) {
-        wait_vmcnt<0>();  // an earlier slot serves e: drain the prefetch before leaving
+    if (!grouped_slot(a, e, W, y, row_begin, row_end)) return;
+    // the first tiles of the range start streaming while the ids are scanned;
+    // they are this workgroup's own when its share starts the range
+    dma_prefetch<FMT, 8, D>(W + (int64_t)e * a.expert_bytes, a.row_bytes, a.nslices, row_begin, row_end);
+    GroupTargets g;
+    grouped_targets(a, e, g);
+    const int64_t first = row_begin;
+    share_rows(g, row_begin, row_end);
+    if (row_begin < row_end && row_begin == first) {
+        grouped_dma_switch<FMT, D, true>(a, W, y, e, g, row_begin, row_end);
         return;
     }
-    switch (__builtin_popcount(tokmask)) {
-    case 1: grouped_dma_run<FMT, 1, D>(a, e, tokmask, row_begin, row_end); break;
-    case 2: grouped_dma_run<FMT, 2, D>(a, e, tokmask, row_begin, row_end); break;
-    case 3: grouped_dma_run<FMT, 3, D>(a, e, tokmask, row_begin, row_end); break;
-    default: grouped_dma_run<FMT, 4, D>(a, e, tokmask, row_begin, row_end); break;
-    }
+    wait_vmcnt<0>();  // the prefetch is not this share's: drain it
+    if (row_begin < row_end) grouped_dma_switch<FMT, D, false>(a, W, y, e, g, row_begin, row_end);
 }
 
 // --------------------------------------------------------------- dispatch
@@ -2029,7 +2098,7 @@ int launch_grouped(int fmt, const Tile& tile, const GroupedArgs& a, void* stream
                : fmt == QG_FMT_Q4_0 ? qgemv_grouped_dma_kernel<QG_FMT_Q4_0, 3>
                                     : qgemv_grouped_dma_kernel<QG_FMT_BF16, 3>;
         if (!fn) return (int)hipErrorInvalidValue;
-        const int64_t nwg = (int64_t)a.T * a.topk * a.tiles_per_expert;
+        const int64_t nwg = (int64_t)a.T * a.topk * a.tiles_per_expert * a.parts;
         hipLaunchKernelGGL(fn, dim3((unsigned)nwg), dim3(64 * tile.waves_per_wg), dma_lds_bytes(fmt, tile, a.T, a.nslices),
                            (hipStream_t)stream, a);
         return (int)hipGetLastError();
@@ -2045,7 +2114,7 @@ int launch_grouped(int fmt, const Tile& tile, const GroupedArgs& a, void* stream
            : fmt == QG_FMT_Q4_0 ? grouped_for<QG_FMT_Q4_0, false>(rbi)
                                 : grouped_for<QG_FMT_BF16, false>(rbi);
     if (!fn) return (int)hipErrorInvalidValue;
-    const int64_t nwg = (int64_t)a.T * a.topk * a.tiles_per_expert;
+    const int64_t nwg = (int64_t)a.T * a.topk * a.tiles_per_expert * a.parts;
     hipLaunchKernelGGL(fn, dim3((unsigned)nwg), dim3(64 * tile.waves_per_wg), lds_bytes(tile, a.T), (hipStream_t)stream,
                        a);
     return (int)hipGetLastError();

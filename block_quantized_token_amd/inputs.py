@@ -105,6 +105,38 @@ def expert_ids(rng: np.random.Generator, n_experts: int, T: int, topk: int) -> n
     return rng.permutation(n_experts)[: T * topk].astype(np.int32).reshape(T, topk)
 
 
+# Distinct experts over the T tokens of a verify pass at the M5 audit's expert
+# overlap (share 0.65: 18.1 distinct at T = 3 and 21.3 at T = 4 in its section
+# 2.2; T = 2 taken as 10 + 0.35 * 10, rounded); share 0 is T * topk.
+UNIQUE_AT_SHARE_065 = {1: 10, 2: 14, 3: 18, 4: 21}
+
+
+def expert_ids_shared(rng: np.random.Generator, n_experts: int, T: int, topk: int, unique: int) -> np.ndarray:
+    """[T][topk] ids naming exactly ``unique`` distinct experts, each token's topk
+    distinct.  Token 0 takes topk new experts; the other new experts are dealt to
+    tokens 1..T-1 in turn; each token fills its other slots with experts that
+    earlier tokens use, drawn at random; each row is shuffled."""
+    assert topk <= unique <= min(T * topk, n_experts) and (T > 1 or unique == topk)
+    pool = rng.permutation(n_experts)[:unique]
+    ids = np.empty((T, topk), dtype=np.int32)
+    ids[0] = pool[:topk]
+    new = pool[topk:]
+    share = [0] * T
+    for i in range(len(new)):
+        share[1 + i % (T - 1)] += 1
+    assert max(share) <= topk
+    used, k = list(pool[:topk]), 0
+    for t in range(1, T):
+        mine = list(new[k:k + share[t]])
+        k += share[t]
+        pick = list(rng.choice(np.array(used), topk - len(mine), replace=False))
+        row = np.array(mine + pick, dtype=np.int32)
+        rng.shuffle(row)
+        ids[t] = row
+        used += mine
+    return ids
+
+
 # ------------------------------------------------------------- byte layout
 def pack_q8_0(d: np.ndarray, codes: np.ndarray) -> np.ndarray:
     rows, nb = d.shape
@@ -176,6 +208,10 @@ CONFIGS = {
     "c4_q8_0_248320x5120": (FMT_Q8_0, 248320, 5120, (1, 2, 3, 4)),
 }
 GROUPED = {"c5_q4_0_experts": dict(fmt=FMT_Q4_0, n_experts=256, rows=512, cols=2560, T=4, topk=10)}
+# The routed-experts layer around it: gate and up of [512][2560] each, down of
+# [2560][512], 256 experts, Q4_0 (the C5 expert shape, the down projection its
+# transpose).
+EXPERT_LAYER = dict(fmt=FMT_Q4_0, n_experts=256, n_ff=512, n_embd=2560, topk=10)
 
 
 def dense_case(name: str, seed: int = 0):
@@ -198,3 +234,18 @@ def grouped_case(name: str = "c5_q4_0_experts", seed: int = 0):
     x = activations(rng, g["cols"], g["T"])
     ids = expert_ids(rng, g["n_experts"], g["T"], g["topk"])
     return dict(g, W=W, x=x, ids=ids)
+
+
+def expert_layer_case(T: int, unique: int, seed: int = 0):
+    """Gate, up and down tables, x [T][n_embd], per-slot inputs h [T][topk][n_ff]
+    and ids with ``unique`` distinct experts, for the routed-experts layer."""
+    g = EXPERT_LAYER
+    rng = rng_for(seed)
+    E, ff, emb = g["n_experts"], g["n_ff"], g["n_embd"]
+    Wg = weights(rng, g["fmt"], E * ff, emb)
+    Wu = weights(rng, g["fmt"], E * ff, emb)
+    Wd = weights(rng, g["fmt"], E * emb, ff)
+    x = activations(rng, emb, T)
+    h = rng.standard_normal((T, g["topk"], ff)).astype(np.float32)
+    ids = expert_ids_shared(rng, E, T, g["topk"], unique)
+    return dict(g, T=T, Wg=Wg, Wu=Wu, Wd=Wd, x=x, h=h, ids=ids)

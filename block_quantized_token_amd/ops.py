@@ -146,6 +146,53 @@ def quantize(fmt, src, method: str = "absmax", out=None):
     return out
 
 
+def _experts_checks(torch, f, tables, ids, n_experts, rows, cols):
+    if ids.dtype != torch.int32 or ids.dim() != 2:
+        raise ValueError("ids must be int32 [T][topk]")
+    need = _lib.qg_packed_bytes(f, rows * n_experts, cols)
+    for W in tables:
+        _require_device(W, "W")
+        if need == 0 or W.numel() * W.element_size() < need:
+            raise ValueError(f"a table holds {W.numel() * W.element_size()} bytes, the experts need {need}")
+
+
+def experts_gate_up(fmt, Wg, Wu, x, ids, n_experts: int, rows: int):
+    """(yg, yu), each [T][topk][rows]: the gate and up projections of the experts
+    each token picked (ids int32 [T][topk]), both tables streamed by one launch."""
+    import torch
+    f = _fmt(fmt)
+    _require_device(x, "x")
+    _require_device(ids, "ids")
+    T, cols = x.shape
+    _experts_checks(torch, f, (Wg, Wu), ids, n_experts, rows, cols)
+    if ids.shape[0] != T:
+        raise ValueError("ids and x disagree on T")
+    topk = ids.shape[1]
+    yg = torch.empty((T, topk, rows), dtype=torch.float32, device=x.device)
+    yu = torch.empty_like(yg)
+    st = _lib.qgemv_experts_gate_up(f, n_experts, rows, cols, T, topk, ids.data_ptr(), Wg.data_ptr(), Wu.data_ptr(),
+                                    x.data_ptr(), yg.data_ptr(), yu.data_ptr(), _stream(torch, x.device))
+    _lib.check(st, "qgemv_experts_gate_up")
+    return yg, yu
+
+
+def experts_down(fmt, W, h, ids, n_experts: int, rows: int):
+    """y[T][topk][rows] = W_{ids[t][j]} . h[t][j] for the per-pair inputs h [T][topk][cols]."""
+    import torch
+    f = _fmt(fmt)
+    _require_device(h, "h")
+    _require_device(ids, "ids")
+    if h.dtype != torch.float32 or h.dim() != 3 or tuple(h.shape[:2]) != tuple(ids.shape):
+        raise ValueError("h must be fp32 [T][topk][cols] matching ids")
+    T, topk, cols = h.shape
+    _experts_checks(torch, f, (W,), ids, n_experts, rows, cols)
+    y = torch.empty((T, topk, rows), dtype=torch.float32, device=h.device)
+    st = _lib.qgemv_experts_down(f, n_experts, rows, cols, T, topk, ids.data_ptr(), W.data_ptr(), h.data_ptr(),
+                                 y.data_ptr(), _stream(torch, h.device))
+    _lib.check(st, "qgemv_experts_down")
+    return y
+
+
 def pack_q8_0(d_bits: np.ndarray, codes: np.ndarray) -> np.ndarray:
     rows, cols = codes.shape
     d = np.ascontiguousarray(d_bits, dtype=np.uint16)

@@ -103,6 +103,28 @@ int qgemv_grouped_experts(int fmt, int64_t n_experts, int64_t rows, int64_t cols
                           const int32_t* ids, const void* W, const float* x, float* y, void* stream);
 
 /*
+ * The expert projections of a routed-experts layer (M5 audit, section 1 item
+ * 2 and the section 2.2 table: the gate/up projection and the down projection
+ * of the experts the tokens picked, with tokens grouped by expert so that an
+ * expert picked by several tokens is read once -- 65% overlap between the
+ * tokens' expert sets in the audit's verify setting):
+ *   gate/up  yg[t][j][r] = sum_k Wg_{ids[t][j]}[r][k] * x[t][k]
+ *            yu[t][j][r] = sum_k Wu_{ids[t][j]}[r][k] * x[t][k]
+ *            Wg and Wu are two tables like W above (rows = the experts' hidden
+ *            width, cols = the model width), both streamed by one launch.
+ *   down     y[t][j][r] = sum_k Wd_{ids[t][j]}[r][k] * h[t][j][k]
+ *            h is a DEVICE fp32 [T][topk][cols]: one input per (token, expert)
+ *            pair; the pairs naming one expert share one pass over its rows.
+ * No activation is applied between them (the pages do not give it; the
+ * caller computes h from yg and yu).  Conventions and errors as
+ * qgemv_grouped_experts; every output must not overlap any input.
+ */
+int qgemv_experts_gate_up(int fmt, int64_t n_experts, int64_t rows, int64_t cols, int T, int topk, const int32_t* ids,
+                          const void* Wg, const void* Wu, const float* x, float* yg, float* yu, void* stream);
+int qgemv_experts_down(int fmt, int64_t n_experts, int64_t rows, int64_t cols, int T, int topk, const int32_t* ids,
+                       const void* W, const float* h, float* y, void* stream);
+
+/*
  * Fused mat-vec + argmax over rows, for the LM head that follows the verify
  * pass (the drafter-cost issue, "perf(speculative): cut the MTP drafter's
  * per-step cost...", fused LM-head / argmax proposal): for each t < T,

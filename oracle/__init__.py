@@ -60,6 +60,8 @@ class Oracle:
         L.oracle_grouped.restype = i32
         L.oracle_grouped.argtypes = [i32, i64, i64, i64, i32, i32, vp, vp, vp, vp, vp]
         L.oracle_num_threads.restype = i32
+        L.oracle_grouped_per_slot.restype = i32
+        L.oracle_grouped_per_slot.argtypes = [i32, i64, i64, i64, i32, i32, vp, vp, vp, vp, vp]
         L.oracle_f32_to_fp16_array.restype = None
         L.oracle_f32_to_fp16_array.argtypes = [i64, vp, vp]
         L.oracle_quantize_q8_0.restype = i32
@@ -136,6 +138,28 @@ class Oracle:
         y, bound = self.gemv(fmt, rows, cols, W, x)
         idx = np.argmax(y, axis=1)  # numpy returns the first (lowest) index of the maximum
         return idx, y[np.arange(y.shape[0]), idx], y, bound
+
+    def gate_up(self, fmt: int, n_experts: int, rows: int, cols: int, ids, Wg, Wu, x):
+        """The gate and up projections of the routed experts: the grouped product of
+        each table with the tokens' x.  Returns ((yg, bound_g), (yu, bound_u))."""
+        return self.grouped(fmt, n_experts, rows, cols, ids, Wg, x), self.grouped(fmt, n_experts, rows, cols, ids, Wu, x)
+
+    def down(self, fmt: int, n_experts: int, rows: int, cols: int, ids, W, h):
+        """y[t][j] = W_{ids[t][j]} . h[t][j] for per-slot inputs h [T][topk][cols].
+        Returns (y, bound), each fp64 [T][topk][rows]."""
+        W = self._u8(W)
+        ids = np.ascontiguousarray(ids, dtype=np.int32)
+        h = np.ascontiguousarray(h, dtype=np.float32)
+        T, topk = ids.shape
+        assert h.shape == (T, topk, cols)
+        assert W.size >= self.packed_bytes(fmt, n_experts * rows, cols)
+        y = np.empty((T, topk, rows), dtype=np.float64)
+        b = np.empty((T, topk, rows), dtype=np.float64)
+        rc = self.L.oracle_grouped_per_slot(fmt, n_experts, rows, cols, T, topk, ids.ctypes.data, W.ctypes.data,
+                                            h.ctypes.data, y.ctypes.data, b.ctypes.data)
+        if rc:
+            raise ValueError(f"oracle_grouped_per_slot rc={rc}")
+        return y, b
 
     def to_fp16_bits(self, v) -> np.ndarray:
         """fp32 values -> binary16 bit patterns (nearest, ties to even)."""

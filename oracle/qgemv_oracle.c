@@ -253,6 +253,34 @@ int oracle_grouped(int fmt, int64_t n_experts, int64_t rows, int64_t cols, int T
     return 0;
 }
 
+/*
+ * The down projection of the routed experts: y[t][j][r] = W_{ids[t][j]}[r] . h[t][j],
+ * one input row h[t][j] (cols values) per slot, written out slot by slot (M5
+ * multi-token audit, section 1 item 2: the down projection applied to each
+ * (token, expert) pair).  An id outside [0, n_experts) is an error (-2).
+ */
+int oracle_grouped_per_slot(int fmt, int64_t n_experts, int64_t rows, int64_t cols, int T, int topk,
+                            const int32_t* ids, const uint8_t* W, const float* h, double* y, double* bound)
+{
+    int64_t rb = oracle_row_bytes(fmt, cols);
+    if (rb < 0 || n_experts < 1 || rows <= 0 || T < 1 || topk < 1 || !ids || !W || !h || !y || !bound)
+        return -1;
+    for (int i = 0; i < T * topk; ++i)
+        if (ids[i] < 0 || ids[i] >= n_experts) return -2;
+    int64_t nslot = (int64_t)T * topk;
+#pragma omp parallel for schedule(static)
+    for (int64_t q = 0; q < nslot * rows; ++q) {
+        int64_t slot = q / rows, r = q % rows;
+        const uint8_t* row = W + ((int64_t)ids[slot] * rows + r) * rb;
+#if ORACLE_MUTANT == 13
+        dot_row(fmt, row, cols, h + (slot / topk) * cols, &y[q], &bound[q]); /* input of the token's first slot */
+#else
+        dot_row(fmt, row, cols, h + slot * cols, &y[q], &bound[q]);
+#endif
+    }
+    return 0;
+}
+
 /* ------------------------------------------------------------ quantizers */
 /*
  * The quantizers that produce the packed blocks on the device (opus-mtp-turbo:

@@ -237,3 +237,19 @@ def test_rows_subset_argument_errors(lib, args, status):
 def test_quantizer_argument_errors(lib, call, status):
     assert call() == status, _lib.last_error()
     assert _lib.last_error()
+
+
+@pytest.mark.parametrize("call, status", [
+    (lambda: _lib.qgemv_experts_gate_up(0, 8, 64, 256, 1, 2, I0, W0, 0, X0, Y0, Y0 + 4096), _lib.QG_EINVAL),  # null Wu
+    (lambda: _lib.qgemv_experts_gate_up(0, 8, 64, 256, 1, 2, I0, W0, W0, X0, Y0, 0), _lib.QG_EINVAL),         # null yu
+    (lambda: _lib.qgemv_experts_gate_up(0, 8, 64, 256, 1, 2, I0, W0, W0 + 8, X0, Y0, Y0 + 4096),
+     _lib.QG_EALIGN),                                                                                          # Wu misaligned
+    (lambda: _lib.qgemv_experts_gate_up(0, 8, 64, 256, 1, 2, I0, W0, W0, X0, Y0, Y0 + 4), _lib.QG_EINVAL),     # yg, yu overlap
+    (lambda: _lib.qgemv_experts_gate_up(0, 8, 64, 256, 1, 2, I0, W0, 0x50000000, X0, Y0, 0x50000000),
+     _lib.QG_EINVAL),                                                                                          # yu overlaps Wu
+    (lambda: _lib.qgemv_experts_down(0, 8, 64, 256, 2, 2, I0, W0, X0, X0 + 2048), _lib.QG_EINVAL),           # y overlaps h
+    (lambda: _lib.qgemv_experts_down(0, 8, 64, 256, 5, 2, I0, W0, X0, Y0), _lib.QG_EINVAL),                   # T 5
+])
+def test_expert_projection_argument_errors(lib, call, status):
+    assert call() == status, _lib.last_error()
+    assert _lib.last_error()

@@ -116,6 +116,25 @@ def pin_failures(o):
             ry, rb = numpy_gemv(fmt, rows, cols, W, x)
             if not (np.all(np.abs(y - ry) <= 1e-12 * rb + 1e-300) and np.allclose(b, rb, rtol=1e-12, atol=0)):
                 fails.append(f"brute force fmt={fmt} {rows}x{cols}")
+    # down projection (per-slot inputs): with every input of token t equal to x[t]
+    # it is the grouped product; each slot is the brute force of its expert's rows
+    E, rows, cols = 6, 40, 96
+    rng = np.random.default_rng(21)
+    W = I.weights(rng, Q8, E * rows, cols)
+    ids = np.array([[1, 4, 1], [5, 0, 2]], dtype=np.int32)  # an expert twice in one token too
+    x = I.activations(rng, cols, 2)
+    yd, _ = o.down(Q8, E, rows, cols, ids, W, np.repeat(x[:, None, :], 3, axis=1))
+    if not np.array_equal(yd, o.grouped(Q8, E, rows, cols, ids, W, x)[0]):
+        fails.append("down with per-token inputs != grouped")
+    h = rng.standard_normal((2, 3, cols)).astype(np.float32)
+    yd, _ = o.down(Q8, E, rows, cols, ids, W, h)
+    erb = rows * I.packed_row_bytes(Q8, cols)
+    for t in range(2):
+        for j in range(3):
+            e = int(ids[t, j])
+            ry, rb = numpy_gemv(Q8, rows, cols, W[e * erb:(e + 1) * erb], h[t, j][None])
+            if not np.all(np.abs(yd[t, j] - ry[0]) <= 1e-12 * rb[0] + 1e-300):
+                fails.append(f"down slot ({t},{j}) != brute force")
     # dyadic: every partial sum exact, so equality with the brute force is exact
     for fmt in (Q8, Q4):
         rows, cols = 33, 640
@@ -246,6 +265,7 @@ MUTANTS = {
     5: "token index reversed",
     6: "fp16 subnormal scales flushed to zero",
     7: "fp16 / bf16 read big-endian",
+    13: "down projection reads the token's first input for every slot",
 }
 
 
