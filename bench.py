@@ -151,16 +151,20 @@ def summarize_pmc(fetch_dir, write_dir, nbytes):
 
 
 def time_entry(torch, stream, launch, calls):
-    """µs per call of ``launch(i)`` over ``calls`` back-to-back calls (after 20 warm-up calls)."""
+    """µs per call of ``launch(i)``: the median of 3 runs of ``calls`` back-to-back
+    calls each (after 20 warm-up calls)."""
     for i in range(20):
         launch(i)
-    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    s.record(stream)
-    for i in range(calls):
-        launch(i)
-    e.record(stream)
-    torch.cuda.synchronize()
-    return s.elapsed_time(e) * 1e3 / calls
+    runs = []
+    for _ in range(3):
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s.record(stream)
+        for i in range(calls):
+            launch(i)
+        e.record(stream)
+        torch.cuda.synchronize()
+        runs.append(s.elapsed_time(e) * 1e3 / calls)
+    return sorted(runs)[1]
 
 
 def other_workloads(torch, stream):

@@ -93,10 +93,15 @@ struct TuneEntry {
 // ring depth) where the rule's pick loses by more than a few percent.
 const TuneEntry kTuned[] = {
     {QG_FMT_Q8_0, 2560, 6144, 0, "4,12,16,s"},     // register-streamed beats DMA at 12 slices
-    // LM head: the persistent matrix-core kernel at every T (one kind for all T
-    // keeps a token's bits independent of T): 252 / 258 / 270 / 280 µs; the VALU
-    // kernels give 230 / 247 / 285 / 311
-    {QG_FMT_Q8_0, 248320, 5120, 0, "8,10,64,p"},
+    // LM head: the LDS-DMA VALU kernel at T <= 2 (231 / 247 µs against 252 / 258
+    // for the matrix cores), the persistent matrix-core kernel at T >= 3 (270 / 278
+    // µs against 285 / 311).  A token's bits agree across T = 1, 2 and across
+    // T = 3, 4, not between the two pairs; a caller who needs one kind for all T
+    // pins it with QGEMV_TILE.
+    {QG_FMT_Q8_0, 248320, 5120, 1, "4,10,64,l2"},
+    {QG_FMT_Q8_0, 248320, 5120, 2, "4,10,256,l2"},
+    {QG_FMT_Q8_0, 248320, 5120, 3, "8,10,64,p"},
+    {QG_FMT_Q8_0, 248320, 5120, 4, "8,10,64,p"},
     {QG_FMT_Q4_0, 8192, 2560, 1, "4,5,8,d"},       // direct: 6.5 vs 7.8 µs
     {QG_FMT_Q4_0, 8192, 2560, 2, "4,10,32,s"},     // two row groups per slice: 8.0 vs 9.3 µs
     {QG_FMT_Q4_0, 8192, 2560, 3, "4,10,32,s"},     //   9.0 vs 10.6 µs

@@ -1403,18 +1403,40 @@ struct ArgmaxOut {
         for (int j = 0; j < NT; ++j)  // t varies across lanes: no dynamic indexing
             if (j == t && k > best[j]) best[j] = k;
     }
-    // wave maximum of each token's key, merged into work[t] by lane 0
+    // The workgroup's maximum of each token's key merged into work[t] by one
+    // atomic per token: wave maxima by butterfly, then across waves through the
+    // LDS.  Every thread of the workgroup calls it after its last use of the LDS
+    // (which needs 8 * NT bytes per wave).  One atomic per workgroup instead of
+    // one per wave: these 64-bit atomics are resolved past the XCDs' L2s, one
+    // address at a time, and thousands of them per call cost tens of µs.
     __device__ void merge(unsigned long long* work) {
+        extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+        unsigned long long* keys = reinterpret_cast<unsigned long long*>(smem);
+        uint64_t k[NT];
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
-            uint64_t k = best[t];
+            k[t] = best[t];
 #pragma unroll
             for (int m = 32; m >= 1; m >>= 1) {
-                const uint32_t lo = __shfl_xor((uint32_t)k, m, 64), hi = __shfl_xor((uint32_t)(k >> 32), m, 64);
+                const uint32_t lo = __shfl_xor((uint32_t)k[t], m, 64), hi = __shfl_xor((uint32_t)(k[t] >> 32), m, 64);
                 const uint64_t o = ((uint64_t)hi << 32) | lo;
-                k = o > k ? o : k;
+                k[t] = o > k[t] ? o : k[t];
             }
-            if ((threadIdx.x & 63) == 0 && k != 0) atomicMax(work + t, (unsigned long long)k);
+        }
+        const int wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
+        __syncthreads();  // every wave is done with the LDS
+        if ((threadIdx.x & 63) == 0) {
+#pragma unroll
+            for (int t = 0; t < NT; ++t) keys[wave * NT + t] = k[t];
+        }
+        __syncthreads();
+        if ((int)threadIdx.x < NT) {
+            unsigned long long m = 0;
+            for (int w = 0; w < nw; ++w) {
+                const unsigned long long o = keys[w * NT + threadIdx.x];
+                m = o > m ? o : m;
+            }
+            if (m != 0) atomicMax(work + threadIdx.x, m);
         }
     }
 };
@@ -2057,6 +2079,8 @@ int launch_argmax(int fmt, int T, const Tile& tile, const DenseArgs& a, void* wo
         lds = lds_bytes(tile, T);
     }
     if (!fn) return (int)hipErrorInvalidValue;
+    const size_t keys = (size_t)tile.waves_per_wg * T * 8;  // the workgroup merge's wave maxima
+    if (lds < keys) lds = keys;
     unsigned long long* w = (unsigned long long*)work;
     hipLaunchKernelGGL(qgemv_argmax_init_kernel, dim3(1), dim3(64), 0, (hipStream_t)stream, w, T);
     hipLaunchKernelGGL(fn, dim3((unsigned)nwg), dim3(64 * tile.waves_per_wg), lds, (hipStream_t)stream, a, w);

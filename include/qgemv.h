@@ -36,11 +36,14 @@
  *     value: QG_OK, or a qg_status; qg_last_error() then holds a message.
  *   - Thread-safe: the only shared state is an immutable tile table and a
  *     thread-local error string.
- *   - Each token's outputs are computed in the same order whatever T is, so
- *     y[t] at T tokens equals y[t] at T' tokens bit for bit (the pages note
+ *   - A kernel computes each token's outputs in the same order whatever T is,
+ *     so y[t] at T tokens equals y[t] at T' tokens bit for bit (the pages note
  *     that each token's sum should not depend on the token count: opus-mtp-
- *     turbo report, finding 3) -- as long as QGEMV_TILE does not change the
- *     k split (waves per workgroup) between the calls.
+ *     turbo report, finding 3) when both calls run the same kind of kernel
+ *     with the same k split.  The default tiles keep one kind for all T except
+ *     on the 248,320 x 5,120 Q8_0 LM head, where the vector-ALU kernel is the
+ *     faster at T <= 2 and the matrix cores at T >= 3 (bits agree within each
+ *     pair); QGEMV_TILE pins one kind for every T.
  *   - Accuracy: |y - exact| <= 1e-4 * sum_k |w_k * x_k| + 1e-6 per output
  *     (fp32 accumulation of exactly decoded weights).
  *
