@@ -15,6 +15,8 @@ HIP_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-ffp-contract=off", "-Wall",
     # packed fp32 instructions are kept out of every code object
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # leading scalar kernel arguments arrive in SGPRs at wave launch
+    "-mllvm", "-amdgpu-kernarg-preload-count=16",
 ]
 HOST_FLAGS = ["-O2", "-std=c++17", "-fPIC", "-ffp-contract=off", "-Wall", "-Wextra", "-Werror"]
 

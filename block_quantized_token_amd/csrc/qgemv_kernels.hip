@@ -356,7 +356,7 @@ __device__ __forceinline__ void reduce_batch(float (&acc)[RB][pad_pow2(NT)], int
 template <int FMT, int NT, int RB, bool ONE_SHOT, class Out>
 __device__ __forceinline__ void gemv_rows(const uint8_t* __restrict__ W, int64_t row_bytes, int cols, int nslices,
                                           const float* __restrict__ x, const int64_t (&xoff)[NT], int64_t row_begin,
-                                          int64_t row_end, Out&& out) {
+                                          int64_t row_end, int nw, Out&& out) {
     using F = Fmt<FMT>;
     using Raw = typename F::Raw;
     constexpr int TP = pad_pow2(NT);
@@ -367,7 +367,7 @@ __device__ __forceinline__ void gemv_rows(const uint8_t* __restrict__ W, int64_t
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: keeps buffer descriptors scalar
-    const int nw = blockDim.x >> 6;
+    // nw: waves per workgroup, an argument
     const int g = lane >> 5;   // which of the two rows of a step
     const int li = lane & 31;  // lane within the row
     const int nbatch = (int)((row_end - row_begin + 2 * RB - 1) / (2 * RB));
@@ -602,7 +602,7 @@ __device__ __forceinline__ void stream_tile(const uint8_t* __restrict__ W, int64
 template <int FMT, int NT, int ST, class Out>
 __device__ __forceinline__ void stream_rows(const uint8_t* __restrict__ W, int64_t row_bytes, int cols, int nsl,
                                             const float* __restrict__ x, const int64_t (&xoff)[NT], int64_t row_begin,
-                                            int64_t row_end, Out&& out) {
+                                            int64_t row_end, int nw, Out&& out) {
     using F = Fmt<FMT>;
     using S = StreamShape<FMT, ST>;
     constexpr int TP = pad_pow2(NT);
@@ -615,7 +615,7 @@ __device__ __forceinline__ void stream_rows(const uint8_t* __restrict__ W, int64
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: keeps buffer descriptors scalar
-    const int nw = blockDim.x >> 6;
+    // nw: waves per workgroup, an argument
     const int g = lane >> 5;
     const int li = lane & 31;
     // waves = slices x row groups: wave (s, rg) takes k slice s of tiles rg, rg + RG, ...
@@ -768,7 +768,7 @@ __device__ __forceinline__ void dma_prefetch(const uint8_t* __restrict__ W, int6
 template <int FMT, int NT, int ST, int D, bool XSEP, class Out, bool PRE = false>
 __device__ __forceinline__ void dma_rows(const uint8_t* __restrict__ W, int64_t row_bytes, int cols, int nsl,
                                          const float* __restrict__ x, const int64_t (&xoff)[NT], int64_t row_begin,
-                                         int64_t row_end, Out&& out) {
+                                         int64_t row_end, int nw, Out&& out) {
     static_assert(!PRE || XSEP, "prefetched tiles need x staged apart");
     using F = Fmt<FMT>;
     using S = StreamShape<FMT, ST>;
@@ -785,7 +785,7 @@ __device__ __forceinline__ void dma_rows(const uint8_t* __restrict__ W, int64_t 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: keeps descriptors and M0 scalar
-    const int nw = blockDim.x >> 6;
+    // nw: waves per workgroup (an argument, so no load of the dispatch's sizes)
     const int g = lane >> 5;
     const int li = lane & 31;
     const int s = wave % nsl;
@@ -1456,43 +1456,46 @@ __global__ void qgemv_argmax_finish_kernel(const unsigned long long* work, int32
 }
 
 // ---------------------------------------------------------------- kernels
+// The dense-path kernels take scalar arguments (not a struct): they can be
+// preloaded into SGPRs at wave launch, so a wave issues its first loads without
+// waiting on a kernel-argument load (nw: waves per workgroup, for the same reason).
 template <int FMT, int T, int RB, bool ONE_SHOT>
-__global__ void __launch_bounds__(64 * kMaxWaves) qgemv_dense_kernel(DenseArgs a) {
-    const int64_t row_begin = (int64_t)blockIdx.x * a.rows_per_wg;
-    const int64_t row_end = row_begin + a.rows_per_wg < a.rows ? row_begin + a.rows_per_wg : a.rows;
+__global__ void __launch_bounds__(64 * kMaxWaves)
+qgemv_dense_kernel(const uint8_t* __restrict__ W, const float* __restrict__ x, float* __restrict__ y, int64_t rows,
+                   int64_t row_bytes, int cols, int nslices, int rows_per_wg, int nw) {
+    const int64_t row_begin = (int64_t)blockIdx.x * rows_per_wg;
+    const int64_t row_end = row_begin + rows_per_wg < rows ? row_begin + rows_per_wg : rows;
     int64_t xoff[T];
 #pragma unroll
-    for (int t = 0; t < T; ++t) xoff[t] = (int64_t)t * a.cols;
-    float* __restrict__ y = a.y;
-    const int64_t rows = a.rows;
-    gemv_rows<FMT, T, RB, ONE_SHOT>(a.W, a.row_bytes, a.cols, a.nslices, a.x, xoff, row_begin, row_end,
-                          [=](int t, int64_t row, float v) { y[t * rows + row] = v; });
+    for (int t = 0; t < T; ++t) xoff[t] = (int64_t)t * cols;
+    gemv_rows<FMT, T, RB, ONE_SHOT>(W, row_bytes, cols, nslices, x, xoff, row_begin, row_end, nw,
+                                    [=](int t, int64_t row, float v) { y[t * rows + row] = v; });
 }
 
 template <int FMT, int T, int ST>
-__global__ void __launch_bounds__(64 * kMaxWaves) qgemv_stream_kernel(DenseArgs a) {
-    const int64_t row_begin = (int64_t)blockIdx.x * a.rows_per_wg;
-    const int64_t row_end = row_begin + a.rows_per_wg < a.rows ? row_begin + a.rows_per_wg : a.rows;
+__global__ void __launch_bounds__(64 * kMaxWaves)
+qgemv_stream_kernel(const uint8_t* __restrict__ W, const float* __restrict__ x, float* __restrict__ y, int64_t rows,
+                    int64_t row_bytes, int cols, int nslices, int rows_per_wg, int nw) {
+    const int64_t row_begin = (int64_t)blockIdx.x * rows_per_wg;
+    const int64_t row_end = row_begin + rows_per_wg < rows ? row_begin + rows_per_wg : rows;
     int64_t xoff[T];
 #pragma unroll
-    for (int t = 0; t < T; ++t) xoff[t] = (int64_t)t * a.cols;
-    float* __restrict__ y = a.y;
-    const int64_t rows = a.rows;
-    stream_rows<FMT, T, ST>(a.W, a.row_bytes, a.cols, a.nslices, a.x, xoff, row_begin, row_end,
+    for (int t = 0; t < T; ++t) xoff[t] = (int64_t)t * cols;
+    stream_rows<FMT, T, ST>(W, row_bytes, cols, nslices, x, xoff, row_begin, row_end, nw,
                             [=](int t, int64_t row, float v) { y[t * rows + row] = v; });
 }
 
 template <int FMT, int T, int ST, int D, bool XSEP>
-__global__ void __launch_bounds__(64 * kMaxWaves) qgemv_dma_kernel(DenseArgs a) {
-    const int64_t row_begin = (int64_t)blockIdx.x * a.rows_per_wg;
-    const int64_t row_end = row_begin + a.rows_per_wg < a.rows ? row_begin + a.rows_per_wg : a.rows;
+__global__ void __launch_bounds__(64 * kMaxWaves)
+qgemv_dma_kernel(const uint8_t* __restrict__ W, const float* __restrict__ x, float* __restrict__ y, int64_t rows,
+                 int64_t row_bytes, int cols, int nslices, int rows_per_wg, int nw) {
+    const int64_t row_begin = (int64_t)blockIdx.x * rows_per_wg;
+    const int64_t row_end = row_begin + rows_per_wg < rows ? row_begin + rows_per_wg : rows;
     int64_t xoff[T];
 #pragma unroll
-    for (int t = 0; t < T; ++t) xoff[t] = (int64_t)t * a.cols;
-    float* __restrict__ y = a.y;
-    const int64_t rows = a.rows;
-    dma_rows<FMT, T, ST, D, XSEP>(a.W, a.row_bytes, a.cols, a.nslices, a.x, xoff, row_begin, row_end,
-                            [=](int t, int64_t row, float v) { y[t * rows + row] = v; });
+    for (int t = 0; t < T; ++t) xoff[t] = (int64_t)t * cols;
+    dma_rows<FMT, T, ST, D, XSEP>(W, row_bytes, cols, nslices, x, xoff, row_begin, row_end, nw,
+                                  [=](int t, int64_t row, float v) { y[t * rows + row] = v; });
 }
 
 template <int FMT, int T, int D>
@@ -1524,7 +1527,8 @@ __global__ void __launch_bounds__(64 * kMaxWaves) qgemv_dma_argmax_kernel(DenseA
 #pragma unroll
     for (int t = 0; t < T; ++t) xoff[t] = (int64_t)t * a.cols;
     ArgmaxOut<T> best;
-    dma_rows<FMT, T, ST, D, XSEP>(a.W, a.row_bytes, a.cols, a.nslices, a.x, xoff, row_begin, row_end, best);
+    dma_rows<FMT, T, ST, D, XSEP>(a.W, a.row_bytes, a.cols, a.nslices, a.x, xoff, row_begin, row_end,
+                                  (int)(blockDim.x >> 6), best);
     best.merge(work);
 }
 
@@ -1546,7 +1550,8 @@ __global__ void __launch_bounds__(64 * kMaxWaves) qgemv_dense_argmax_kernel(Dens
 #pragma unroll
     for (int t = 0; t < T; ++t) xoff[t] = (int64_t)t * a.cols;
     ArgmaxOut<T> best;
-    gemv_rows<FMT, T, 2, ONE_SHOT>(a.W, a.row_bytes, a.cols, a.nslices, a.x, xoff, row_begin, row_end, best);
+    gemv_rows<FMT, T, 2, ONE_SHOT>(a.W, a.row_bytes, a.cols, a.nslices, a.x, xoff, row_begin, row_end,
+                                   (int)(blockDim.x >> 6), best);
     best.merge(work);
 }
 
@@ -1558,7 +1563,8 @@ __global__ void __launch_bounds__(64 * kMaxWaves) qgemv_stream_argmax_kernel(Den
 #pragma unroll
     for (int t = 0; t < T; ++t) xoff[t] = (int64_t)t * a.cols;
     ArgmaxOut<T> best;
-    stream_rows<FMT, T, 8>(a.W, a.row_bytes, a.cols, a.nslices, a.x, xoff, row_begin, row_end, best);
+    stream_rows<FMT, T, 8>(a.W, a.row_bytes, a.cols, a.nslices, a.x, xoff, row_begin, row_end, (int)(blockDim.x >> 6),
+                           best);
     best.merge(work);
 }
 
@@ -1649,7 +1655,7 @@ __device__ __forceinline__ void grouped_run(const GroupedArgs& a, const uint8_t*
     int64_t xoff[NE];
     group_offsets<NE>(a, g, xoff);
     gemv_rows<FMT, NE, RB, ONE_SHOT>(W + (int64_t)e * a.expert_bytes, a.row_bytes, a.cols, a.nslices, a.x, xoff, row_begin,
-                                     row_end, [=](int n, int64_t row, float v) { group_store(a, y, e, g, n, row, v); });
+                                     row_end, (int)(blockDim.x >> 6), [=](int n, int64_t row, float v) { group_store(a, y, e, g, n, row, v); });
 }
 
 // The slot, part and row range of a grouped workgroup and the expert it serves.
@@ -1752,7 +1758,7 @@ __device__ __forceinline__ void grouped_dma_run(const GroupedArgs& a, const uint
     group_offsets<NE>(a, g, xoff);
     auto out = [=](int n, int64_t row, float v) { group_store(a, y, e, g, n, row, v); };
     dma_rows<FMT, NE, 8, D, true, decltype(out)&, PRE>(W + (int64_t)e * a.expert_bytes, a.row_bytes, a.cols, a.nslices,
-                                                     a.x, xoff, row_begin, row_end, out);
+                                                     a.x, xoff, row_begin, row_end, (int)(blockDim.x >> 6), out);
 }
 
 template <int FMT, int D, bool PRE>
@@ -1790,6 +1796,8 @@ __global__ void __launch_bounds__(64 * kMaxWaves) qgemv_grouped_dma_kernel(Group
 
 // --------------------------------------------------------------- dispatch
 using DenseFn = void (*)(DenseArgs);
+// the dense-path kernels with scalar arguments (W, x, y, rows, row_bytes, cols, nslices, rows_per_wg, nw)
+using DmaFn = void (*)(const uint8_t*, const float*, float*, int64_t, int64_t, int, int, int, int);
 using GroupedFn = void (*)(GroupedArgs);
 
 int rb_index(int rb) { return rb == 1 ? 0 : rb == 2 ? 1 : rb == 4 ? 2 : rb == 8 ? 3 : 4; }
@@ -1797,7 +1805,7 @@ int rb_index(int rb) { return rb == 1 ? 0 : rb == 2 ? 1 : rb == 4 ? 2 : rb == 8 
 // Only the (format, T, RB, mode) combinations of the compiled set (tile_supported)
 // are instantiated.
 template <int FMT, int T, bool OS>
-DenseFn dense_entry(int rbi) {
+DmaFn dense_entry(int rbi) {
     constexpr int TP = pad_pow2(T);
     if (rbi == 0) return qgemv_dense_kernel<FMT, T, 1, OS>;
     if (rbi == 1) return qgemv_dense_kernel<FMT, T, 2, OS>;
@@ -1814,7 +1822,7 @@ DenseFn dense_entry(int rbi) {
 }
 
 template <int FMT, bool OS>
-DenseFn dense_for(int T, int rbi) {
+DmaFn dense_for(int T, int rbi) {
     switch (T) {
     case 1: return dense_entry<FMT, 1, OS>(rbi);
     case 2: return dense_entry<FMT, 2, OS>(rbi);
@@ -1838,7 +1846,7 @@ GroupedFn grouped_for(int rbi) {
 // the (format, T, tile) combinations of stream_supported: the ones that fit the
 // register budget without spilling
 template <int FMT, int T>
-DenseFn stream_entry(int rb) {
+DmaFn stream_entry(int rb) {
     if constexpr (FMT != QG_FMT_BF16 || T <= 2) {
         if (rb == 4) return qgemv_stream_kernel<FMT, T, 8>;
     }
@@ -1849,7 +1857,7 @@ DenseFn stream_entry(int rb) {
 }
 
 template <int FMT>
-DenseFn stream_for(int T, int rb) {
+DmaFn stream_for(int T, int rb) {
     switch (T) {
     case 1: return stream_entry<FMT, 1>(rb);
     case 2: return stream_entry<FMT, 2>(rb);
@@ -1859,15 +1867,16 @@ DenseFn stream_for(int T, int rb) {
 }
 
 // LDS-DMA streamed kernels: 8-row tiles, ring depths 2, 3, 4, 6
+
 template <int FMT, int T, int D>
-DenseFn dma_depth(bool xsep) {
+DmaFn dma_depth(bool xsep) {
     if (xsep) return qgemv_dma_kernel<FMT, T, 8, D, true>;
     if constexpr (dma_x_slots<FMT, 8, T>() < D) return qgemv_dma_kernel<FMT, T, 8, D, false>;
     return nullptr;
 }
 
 template <int FMT, int T>
-DenseFn dma_entry(int depth, bool xsep) {
+DmaFn dma_entry(int depth, bool xsep) {
     switch (depth) {
     case 2: return dma_depth<FMT, T, 2>(xsep);
     case 3: return dma_depth<FMT, T, 3>(xsep);
@@ -1878,7 +1887,7 @@ DenseFn dma_entry(int depth, bool xsep) {
 }
 
 template <int FMT>
-DenseFn dma_for(int T, int depth, bool xsep) {
+DmaFn dma_for(int T, int depth, bool xsep) {
     switch (T) {
     case 1: return dma_entry<FMT, 1>(depth, xsep);
     case 2: return dma_entry<FMT, 2>(depth, xsep);
@@ -1924,7 +1933,7 @@ DenseFn mfma_for(int T) {
 
 int launch_dense(int fmt, int T, const Tile& tile, const DenseArgs& a, void* stream) {
     const int rbi = rb_index(tile.rows_per_batch);
-    DenseFn fn;
+    DmaFn fn;
     if (one_shot(tile, a.nslices))
         fn = fmt == QG_FMT_Q8_0 ? dense_for<QG_FMT_Q8_0, true>(T, rbi)
            : fmt == QG_FMT_Q4_0 ? dense_for<QG_FMT_Q4_0, true>(T, rbi)
@@ -1936,7 +1945,7 @@ int launch_dense(int fmt, int T, const Tile& tile, const DenseArgs& a, void* str
     if (!fn) return (int)hipErrorInvalidValue;
     const int64_t nwg = (a.rows + tile.rows_per_wg - 1) / tile.rows_per_wg;
     hipLaunchKernelGGL(fn, dim3((unsigned)nwg), dim3(64 * tile.waves_per_wg), lds_bytes(tile, T), (hipStream_t)stream,
-                       a);
+                       a.W, a.x, a.y, a.rows, a.row_bytes, a.cols, a.nslices, a.rows_per_wg, tile.waves_per_wg);
     return (int)hipGetLastError();
 }
 
@@ -1952,32 +1961,38 @@ int launch_stream(int fmt, int T, const Tile& tile, const DenseArgs& a, void* st
                            (hipStream_t)stream, a);
         return (int)hipGetLastError();
     }
-    if (tile.mfma)
+    const int64_t nwg = (a.rows + tile.rows_per_wg - 1) / tile.rows_per_wg;
+    if (tile.mfma) {
         fn = tile.rows_per_batch != 8 ? nullptr
            : fmt == QG_FMT_Q8_0 ? mfma_for<QG_FMT_Q8_0>(T)
            : fmt == QG_FMT_Q4_0 ? mfma_for<QG_FMT_Q4_0>(T)
                                 : mfma_for<QG_FMT_BF16>(T);
-    else
-        fn = fmt == QG_FMT_Q8_0 ? stream_for<QG_FMT_Q8_0>(T, tile.rows_per_batch)
-           : fmt == QG_FMT_Q4_0 ? stream_for<QG_FMT_Q4_0>(T, tile.rows_per_batch)
-                                : stream_for<QG_FMT_BF16>(T, tile.rows_per_batch);
-    if (!fn) return (int)hipErrorInvalidValue;
-    const int64_t nwg = (a.rows + tile.rows_per_wg - 1) / tile.rows_per_wg;
-    hipLaunchKernelGGL(fn, dim3((unsigned)nwg), dim3(64 * tile.waves_per_wg),
-                       stream_lds_bytes(fmt, tile, T, a.nslices), (hipStream_t)stream, a);
+        if (!fn) return (int)hipErrorInvalidValue;
+        hipLaunchKernelGGL(fn, dim3((unsigned)nwg), dim3(64 * tile.waves_per_wg),
+                           stream_lds_bytes(fmt, tile, T, a.nslices), (hipStream_t)stream, a);
+        return (int)hipGetLastError();
+    }
+    const DmaFn sfn = fmt == QG_FMT_Q8_0 ? stream_for<QG_FMT_Q8_0>(T, tile.rows_per_batch)
+                    : fmt == QG_FMT_Q4_0 ? stream_for<QG_FMT_Q4_0>(T, tile.rows_per_batch)
+                                         : stream_for<QG_FMT_BF16>(T, tile.rows_per_batch);
+    if (!sfn) return (int)hipErrorInvalidValue;
+    hipLaunchKernelGGL(sfn, dim3((unsigned)nwg), dim3(64 * tile.waves_per_wg), stream_lds_bytes(fmt, tile, T, a.nslices),
+                       (hipStream_t)stream, a.W, a.x, a.y, a.rows, a.row_bytes, a.cols, a.nslices, a.rows_per_wg,
+                       tile.waves_per_wg);
     return (int)hipGetLastError();
 }
 
 int launch_dma(int fmt, int T, const Tile& tile, const DenseArgs& a, void* stream) {
     const bool xsep = tile.kind == 3;
-    DenseFn fn = tile.rows_per_batch != 4 ? nullptr
-               : fmt == QG_FMT_Q8_0 ? dma_for<QG_FMT_Q8_0>(T, tile.depth, xsep)
-               : fmt == QG_FMT_Q4_0 ? dma_for<QG_FMT_Q4_0>(T, tile.depth, xsep)
-                                    : dma_for<QG_FMT_BF16>(T, tile.depth, xsep);
+    DmaFn fn = tile.rows_per_batch != 4 ? nullptr
+             : fmt == QG_FMT_Q8_0 ? dma_for<QG_FMT_Q8_0>(T, tile.depth, xsep)
+             : fmt == QG_FMT_Q4_0 ? dma_for<QG_FMT_Q4_0>(T, tile.depth, xsep)
+                                  : dma_for<QG_FMT_BF16>(T, tile.depth, xsep);
     if (!fn) return (int)hipErrorInvalidValue;
     const int64_t nwg = (a.rows + tile.rows_per_wg - 1) / tile.rows_per_wg;
     hipLaunchKernelGGL(fn, dim3((unsigned)nwg), dim3(64 * tile.waves_per_wg), dma_lds_bytes(fmt, tile, T, a.nslices),
-                       (hipStream_t)stream, a);
+                       (hipStream_t)stream, a.W, a.x, a.y, a.rows, a.row_bytes, a.cols, a.nslices, a.rows_per_wg,
+                       tile.waves_per_wg);
     return (int)hipGetLastError();
 }
 
