@@ -54,18 +54,28 @@ __global__ void __launch_bounds__(kQThreads) quantize_kernel(const float* __rest
     const int64_t b0 = (int64_t)blockIdx.x * kQThreads;
     const int nb = nblocks - b0 < kQThreads ? (int)(nblocks - b0) : kQThreads;
 
-    // 32 KB of input: 8 float4 per block, consecutive lanes on consecutive 16 B
+    // 32 KB of input: 8 float4 per block, consecutive lanes on consecutive 16 B.
+    // A full workgroup issues all 8 loads before it stores any (a bounds check
+    // per load would make each one wait for the previous); the last, partial
+    // workgroup checks each.
     const f32x4* s4 = reinterpret_cast<const f32x4*>(src + b0 * 32);
+    auto put = [&](int idx, const f32x4& v) {
+        float* p = xs + (idx >> 3) * kQStride + (idx & 7) * 4;
+        p[0] = v.x;
+        p[1] = v.y;
+        p[2] = v.z;
+        p[3] = v.w;
+    };
+    if (nb == kQThreads) {
+        f32x4 v[8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        const int idx = t + kQThreads * i;
-        if (idx < nb * 8) {
-            const f32x4 v = __builtin_nontemporal_load(s4 + idx);
-            float* p = xs + (idx >> 3) * kQStride + (idx & 7) * 4;
-            p[0] = v.x;
-            p[1] = v.y;
-            p[2] = v.z;
-            p[3] = v.w;
+        for (int i = 0; i < 8; ++i) v[i] = __builtin_nontemporal_load(s4 + t + kQThreads * i);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) put(t + kQThreads * i, v[i]);
+    } else {
+        for (int i = 0; i < 8; ++i) {
+            const int idx = t + kQThreads * i;
+            if (idx < nb * 8) put(idx, __builtin_nontemporal_load(s4 + idx));
         }
     }
     __syncthreads();
