@@ -395,6 +395,11 @@ __device__ __forceinline__ void gemv_rows(const uint8_t* __restrict__ W, int64_t
         Raw ra[RB];
         issue_batch(c, row_begin, F::slice_offset(s), lane_ok ? li : 0, upper_ok, ra);
         load_x<FMT, NT>(x, xoff, k0, li, lane_ok, cols, xr);
+        // every load is issued before the first use of any: otherwise the
+        // scheduler may pull an early decode up to just after its load and
+        // make the wave wait for it before issuing the rest (not for the
+        // widest batches, whose registers would then spill)
+        if constexpr (sizeof(Raw) * RB <= 256) __builtin_amdgcn_sched_barrier(0);
         accumulate_batch<FMT, NT, RB>(ra, xr, lane_ok, upper_ok, acc);
         float v[N];
 #pragma unroll
