@@ -335,6 +335,54 @@ def cpu_baseline(case, budget_s: float):
                 us_per_call=round(el / (steps * 4) * 1e6, 1))
 
 
+def _kernel_short(name):
+    return name.replace("void ", "").replace("qg::(anonymous namespace)::", "").split("(")[0]
+
+
+def summarize_trace(trace_dir):
+    """Per-kernel call count and duration from a rocprofv3 --kernel-trace --stats run."""
+    import csv
+    import glob
+    files = glob.glob(os.path.join(trace_dir, "**", "*kernel_stats.csv"), recursive=True)
+    if not files:
+        sys.exit(f"no kernel_stats.csv under {trace_dir}")
+    print(f"kernel_source_sha256: {source_digest()}")
+    print()
+    print("| kernel | calls | average us | min us | max us | share of kernel time |")
+    print("|---|---|---|---|---|---|")
+    for r in csv.DictReader(open(files[0])):
+        name = _kernel_short(r["Name"])
+        if not name.startswith(("qgemv", "quantize")):
+            continue
+        print(f"| {name} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.3f} | {int(r['MinNs']) / 1e3:.3f} | "
+              f"{int(r['MaxNs']) / 1e3:.3f} | {float(r['Percentage']):.2f}% |")
+
+
+def summarize_counters(counter_dir):
+    """Per-kernel medians over dispatches of every counter of a rocprofv3 --pmc run."""
+    import csv
+    import glob
+    files = glob.glob(os.path.join(counter_dir, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        sys.exit(f"no counter_collection.csv under {counter_dir}")
+    acc = {}
+    for f in files:
+        for r in csv.DictReader(open(f)):
+            name = _kernel_short(r["Kernel_Name"])
+            if not name.startswith("qgemv"):
+                continue
+            d = acc.setdefault(name, {}).setdefault(r["Counter_Name"], {})
+            d[r["Dispatch_Id"]] = d.get(r["Dispatch_Id"], 0.0) + float(r["Counter_Value"])
+    print(f"kernel_source_sha256: {source_digest()}")
+    counters = sorted({c for v in acc.values() for c in v})
+    print()
+    print("| kernel | " + " | ".join(counters) + " |")
+    print("|---" * (len(counters) + 1) + "|")
+    for k in sorted(acc):
+        med = [sorted(acc[k][c].values())[len(acc[k][c]) // 2] if c in acc[k] else float("nan") for c in counters]
+        print(f"| {k} | " + " | ".join(f"{m:.4g}" for m in med) + " |")
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -346,8 +394,18 @@ def main():
                     help="after the timed region, run N plain copies of the weight size (PMC calibration)")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="print the HBM traffic table from two rocprofv3 --pmc runs of this script and exit")
+    ap.add_argument("--summarize-trace", metavar="TRACE_DIR",
+                    help="print the per-kernel table of a rocprofv3 --kernel-trace --stats run and exit")
+    ap.add_argument("--summarize-counters", metavar="PMC_DIR",
+                    help="print per-kernel medians of every counter of a rocprofv3 --pmc run and exit")
     args = ap.parse_args()
 
+    if args.summarize_trace:
+        summarize_trace(args.summarize_trace)
+        return
+    if args.summarize_counters:
+        summarize_counters(args.summarize_counters)
+        return
     if args.summarize_pmc:
         fmt, rows, cols, _ = I.CONFIGS[WORKLOAD]
         summarize_pmc(*args.summarize_pmc, _lib.qg_packed_bytes(fmt, rows, cols))

@@ -68,3 +68,23 @@ def test_stored_traffic_needs_the_same_kernel_source(tmp_path, monkeypatch):
     assert bench.measured_traffic("qgemv_y<1>") is None
     f.write_text(f.read_text().replace(bench.source_digest(), "0" * 16))
     assert bench.measured_traffic("qgemv_x<1>") is None
+
+
+def test_trace_and_counter_summaries(tmp_path, capsys):
+    d = tmp_path / "t"
+    d.mkdir()
+    (d / "run_kernel_stats.csv").write_text(
+        "Name,Calls,TotalDurationNs,AverageNs,Percentage,MinNs,MaxNs,StdDev\n"
+        '"void qg::(anonymous namespace)::qgemv_dma_kernel<0, 1, 8, 2, false>(unsigned char const*)",10,80000,8000.0,'
+        "60.0,7000,9000,10\n"
+        '"at::native::elementwise_kernel",5,100,20.0,1.0,10,30,1\n')
+    bench.summarize_trace(str(d))
+    out = capsys.readouterr().out
+    assert "| qgemv_dma_kernel<0, 1, 8, 2, false> | 10 | 8.000 | 7.000 | 9.000 | 60.00% |" in out
+    assert "elementwise" not in out
+    _write_pmc(tmp_path / "c", "SQ_WAVES", [(1, "void qg::(anonymous namespace)::qgemv_x<1>(a)", 5.0),
+                                            (1, "void qg::(anonymous namespace)::qgemv_x<1>(a)", 7.0),
+                                            (2, "void qg::(anonymous namespace)::qgemv_x<1>(a)", 100.0)])
+    bench.summarize_counters(str(tmp_path / "c"))
+    out = capsys.readouterr().out
+    assert "| qgemv_x<1> | 100 |" in out  # per-dispatch sums (12, 100): the median of two is the upper
