@@ -335,6 +335,41 @@ def cpu_baseline(case, budget_s: float):
                 us_per_call=round(el / (steps * 4) * 1e6, 1))
 
 
+def cpu_baseline_per_workload(sample_rows: int = 2048):
+    """The oracle on every other workload, at T = 1..4: a sample of rows (all of them
+    when fewer; x and the expert table as in the workload), timed once per T and
+    scaled to the workload's rows.  Seeded inputs of each workload's shape."""
+    import oracle
+    o = oracle.get()
+    out = {}
+    for name in ("c1_q8_0_2560x2560", "c2b_q8_0_2560x6144", "c3_q4_0_8192x2560", "c3_bf16_8192x2560",
+                 "c4_q8_0_248320x5120"):
+        fmt, rows, cols, _ = I.CONFIGS[name]
+        n = min(rows, sample_rows)
+        rng = I.rng_for(0)
+        W = I.weights(rng, fmt, n, cols)
+        x = I.activations(rng, cols)
+        nb = o.packed_bytes(fmt, rows, cols)
+        res = {}
+        for T in (1, 2, 3, 4):
+            t0 = time.perf_counter()
+            o.gemv(fmt, n, cols, W, x[:T])
+            us = (time.perf_counter() - t0) * 1e6 * rows / n
+            res[str(T)] = dict(us_per_call=round(us, 1), gbs=round(nb / us / 1e3, 3))
+        out[name] = dict(sample=f"{n} of {rows} rows, scaled", per_T=res)
+    g = I.grouped_case()
+    res = {}
+    for T in (1, 2, 3, 4):
+        ids = g["ids"][:T]
+        t0 = time.perf_counter()
+        o.grouped(g["fmt"], g["n_experts"], g["rows"], g["cols"], ids, g["W"], g["x"][:T])
+        us = (time.perf_counter() - t0) * 1e6
+        nb = T * g["topk"] * o.packed_bytes(g["fmt"], g["rows"], g["cols"])
+        res[str(T)] = dict(us_per_call=round(us, 1), gbs=round(nb / us / 1e3, 3))
+    out["c5_q4_0_experts"] = dict(sample="every slot", per_T=res)
+    return out
+
+
 def _kernel_short(name):
     return name.replace("void ", "").replace("qg::(anonymous namespace)::", "").split("(")[0]
 
@@ -487,6 +522,8 @@ def main():
     detail = {} if args.no_extra else other_workloads(torch, stream)
 
     cpu = cpu_baseline(case, args.cpu_seconds) if args.cpu_seconds > 0 else None
+    if cpu is not None and not args.no_extra:
+        cpu["per_workload"] = cpu_baseline_per_workload()
 
     out = {
         "metric": METRIC,
