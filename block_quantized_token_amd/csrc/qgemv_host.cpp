@@ -92,6 +92,17 @@ struct TuneEntry {
 // MI355X, µs per call at T = 1..4 from sweeps over (kind, rows per workgroup,
 // ring depth) where the rule's pick loses by more than a few percent.
 const TuneEntry kTuned[] = {
+    // 2560 x 2560: the direct one-shot kernel (4 rows per workgroup, 640 workgroups)
+    // at T <= 3 (4.7 / 5.3 / 6.2 µs against 5.5 / 5.9 / 6.5 for the rule's LDS-DMA
+    // tile), register-streamed at T = 4 (6.6 against 7.1)
+    {QG_FMT_Q8_0, 2560, 2560, 1, "2,5,4,d"},
+    {QG_FMT_Q8_0, 2560, 2560, 2, "2,5,4,d"},
+    {QG_FMT_Q8_0, 2560, 2560, 3, "2,5,4,d"},
+    {QG_FMT_Q8_0, 2560, 2560, 4, "4,5,16,s"},
+    // 10240 x 2560: the rule's LDS-DMA ring at T <= 2; at T >= 3, x staged apart
+    // and a ring of two (10.5 / 11.7 µs against 10.9 / 11.9 with x in the ring)
+    {QG_FMT_Q8_0, 10240, 2560, 3, "4,5,40,L2"},
+    {QG_FMT_Q8_0, 10240, 2560, 4, "4,5,40,L2"},
     {QG_FMT_Q8_0, 2560, 6144, 0, "4,12,16,s"},     // register-streamed beats DMA at 12 slices
     // LM head: the LDS-DMA VALU kernel at T <= 2 (231 / 247 µs against 252 / 258
     // for the matrix cores), the persistent matrix-core kernel at T >= 3 (270 / 278
@@ -102,10 +113,13 @@ const TuneEntry kTuned[] = {
     {QG_FMT_Q8_0, 248320, 5120, 2, "4,10,256,l2"},
     {QG_FMT_Q8_0, 248320, 5120, 3, "8,10,64,p"},
     {QG_FMT_Q8_0, 248320, 5120, 4, "8,10,64,p"},
-    {QG_FMT_Q4_0, 8192, 2560, 1, "4,5,8,d"},       // direct: 6.5 vs 7.8 µs
-    {QG_FMT_Q4_0, 8192, 2560, 2, "4,10,32,s"},     // two row groups per slice: 8.0 vs 9.3 µs
-    {QG_FMT_Q4_0, 8192, 2560, 3, "4,10,32,s"},     //   9.0 vs 10.6 µs
-    {QG_FMT_Q4_0, 8192, 2560, 4, "4,10,32,s"},     //   9.8 vs 11.3 µs
+    {QG_FMT_Q4_0, 8192, 2560, 1, "4,5,8,d"},       // direct: 6.0 vs 7.7 µs for the LDS-DMA ring
+    {QG_FMT_Q4_0, 8192, 2560, 2, "4,5,8,d"},       //   7.2 vs 7.8 µs for two row groups per slice
+    {QG_FMT_Q4_0, 8192, 2560, 3, "4,5,8,d"},       //   8.5 vs 8.7 µs
+    {QG_FMT_Q4_0, 8192, 2560, 4, "4,10,32,s"},     // two row groups per slice: 9.5 vs 10.1 µs direct
+    // BF16 8192 x 2560: direct at T <= 2 (8.5 / 9.4 µs against 9.6 / 10.0 for the rule's tile)
+    {QG_FMT_BF16, 8192, 2560, 1, "4,5,8,d"},
+    {QG_FMT_BF16, 8192, 2560, 2, "4,5,8,d"},
 };
 
 Tile default_tile(int fmt, int64_t rows, int64_t cols, int T) {
