@@ -315,6 +315,32 @@ def other_workloads(torch, stream):
     return out
 
 
+def read_probe(torch, stream, nbytes):
+    """Context for the roofline: the library's plain read kernel (qg_read_probe:
+    coalesced 16-byte loads, nothing else) over ``nbytes`` streamed from HBM (a
+    ring of >= 1 GiB, as the mat-vec's weights) and over one 1 GiB buffer; the
+    fastest of a few workgroup limits for each."""
+    sp = stream.cuda_stream
+    out = torch.zeros(1, dtype=torch.int32, device="cuda")
+    ring = [torch.full((nbytes // 4,), 1, dtype=torch.int32, device="cuda") for _ in range(max(1, -(-RING_BYTES // nbytes)))]
+    big = torch.full((RING_BYTES // 4,), 1, dtype=torch.int32, device="cuda")
+    res = {"kernel": "read_probe_kernel (qg_read_probe)"}
+    for label, bufs, size, calls in (("bench_size", ring, nbytes, 400), ("1gib", [big], RING_BYTES, 20)):
+        best = None
+        for groups in (512, 1024, 2048, 4096, 8192):
+            def launch(i, bufs=bufs, size=size, groups=groups):
+                st = _lib.qg_read_probe(bufs[i % len(bufs)].data_ptr(), size, groups, 0xFFFFFFFF, out.data_ptr(), sp)
+                if st:
+                    _lib.check(st, "read probe")
+            us = time_entry(torch, stream, launch, calls)
+            if best is None or us < best[0]:
+                best = (us, groups)
+        res[label] = dict(bytes=size, us_per_call=round(best[0], 3), gbs=round(size / best[0] / 1e3, 1),
+                          pct_peak=round(100 * size / best[0] / 1e3 / HBM_PEAK_GBS, 1), max_groups=best[1])
+    del ring, big
+    return res
+
+
 def cpu_baseline(case, budget_s: float):
     """The oracle, untuned, on the host cores: whole steps (T = 1..4) of the same
     workload repeated until about ``budget_s`` seconds have passed."""
@@ -520,6 +546,8 @@ def main():
         del src, dst
 
     detail = {} if args.no_extra else other_workloads(torch, stream)
+    if not args.no_extra:
+        detail["hbm_read_probe"] = read_probe(torch, stream, nbytes)
 
     cpu = cpu_baseline(case, args.cpu_seconds) if args.cpu_seconds > 0 else None
     if cpu is not None and not args.no_extra:

@@ -20,7 +20,7 @@ EXPORTS = (
     "qgemv_q8_0", "qgemv_q4_0", "qgemv_bf16", "qgemv_grouped_experts", "qgemv_argmax", "qgemv_rows", "qg_packed_bytes",
     "qg_pack_q8_0", "qg_unpack_q8_0", "qg_pack_q4_0", "qg_unpack_q4_0", "qg_query_tile",
     "qg_status_string", "qg_last_error", "qg_quantize_q8_0", "qg_quantize_q4_0", "qgemv_experts_gate_up",
-    "qgemv_experts_down",
+    "qgemv_experts_down", "qg_read_probe",
 )
 QG_Q4_ABSMAX, QG_Q4_LLOYD = 0, 1
 
@@ -67,6 +67,8 @@ def load() -> ctypes.CDLL:
     L.qg_quantize_q8_0.argtypes = [i64, i64, vp, vp, vp]
     L.qg_quantize_q4_0.restype = i32
     L.qg_quantize_q4_0.argtypes = [i64, i64, i32, vp, vp, vp]
+    L.qg_read_probe.restype = i32
+    L.qg_read_probe.argtypes = [vp, i64, i64, ctypes.c_uint32, vp, vp]
     L.qg_query_tile.restype = i32
     L.qg_query_tile.argtypes = [i32, i64, i64, i32, ctypes.POINTER(ctypes.c_int)]
     L.qg_status_string.restype = ctypes.c_char_p
@@ -149,6 +151,10 @@ def qg_quantize_q8_0(rows, cols, src, dst, stream=None) -> int:
 
 def qg_quantize_q4_0(rows, cols, method, src, dst, stream=None) -> int:
     return load().qg_quantize_q4_0(rows, cols, method, src, dst, stream)
+
+
+def qg_read_probe(src, nbytes, max_groups, magic, out, stream=None) -> int:
+    return load().qg_read_probe(src, nbytes, max_groups, magic, out, stream)
 
 
 def qg_query_tile(fmt, rows, cols, T):

@@ -33,18 +33,20 @@ def build(verbose: bool = False, extra_hip_flags=()) -> str:
     kern_o = os.path.join(BUILD, "qgemv_kernels.o")
     _run(["g++", *HOST_FLAGS, "-c", os.path.join(CSRC, "qgemv_host.cpp"), "-o", host_o], verbose)
     quant_o = os.path.join(BUILD, "qquant_kernels.o")
+    probe_o = os.path.join(BUILD, "qprobe_kernels.o")
     hipcc = os.path.join(ROCM, "bin", "hipcc")
-    # the two kernel sources compile side by side (the mat-vec one takes minutes)
-    quant = subprocess.Popen([hipcc, *HIP_FLAGS, *extra_hip_flags, "-c", "-x", "hip",
-                              os.path.join(CSRC, "qquant_kernels.hip"), "-o", quant_o])
+    # the small kernel sources compile beside the mat-vec one (which takes minutes)
+    side = [subprocess.Popen([hipcc, *HIP_FLAGS, *extra_hip_flags, "-c", "-x", "hip", os.path.join(CSRC, src), "-o", obj])
+            for src, obj in (("qquant_kernels.hip", quant_o), ("qprobe_kernels.hip", probe_o))]
     try:
         _run([hipcc, *HIP_FLAGS, *extra_hip_flags, "-c", "-x", "hip", os.path.join(CSRC, "qgemv_kernels.hip"),
               "-o", kern_o], verbose)
     finally:
-        if quant.wait() != 0:
-            raise subprocess.CalledProcessError(quant.returncode, "hipcc qquant_kernels.hip")
+        for proc in side:
+            if proc.wait() != 0:
+                raise subprocess.CalledProcessError(proc.returncode, " ".join(proc.args))
     tmp = LIB + f".tmp{os.getpid()}"
-    _run([hipcc, "--offload-arch=gfx950", "-shared", "-fPIC", host_o, kern_o, quant_o, "-o", tmp], verbose)
+    _run([hipcc, "--offload-arch=gfx950", "-shared", "-fPIC", host_o, kern_o, quant_o, probe_o, "-o", tmp], verbose)
     os.replace(tmp, LIB)
     return LIB
 

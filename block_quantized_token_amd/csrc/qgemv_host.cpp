@@ -531,6 +531,18 @@ int run_quantize(int kind, int64_t rows, int64_t cols, const float* src, void* d
     return ok();
 }
 
+int run_read_probe(const void* src, int64_t bytes, int64_t max_groups, uint32_t magic, uint32_t* out, void* stream) {
+    if (!src || !out) return fail(QG_EINVAL, "qg_read_probe: null pointer (src=%p out=%p)", src, (void*)out);
+    if (bytes <= 0 || bytes % 16) return fail(QG_EINVAL, "qg_read_probe: bytes=%lld must be a positive multiple of 16", (long long)bytes);
+    if (max_groups < 1 || max_groups > 0x7FFFFFFF)
+        return fail(QG_EINVAL, "qg_read_probe: max_groups=%lld outside 1..2^31-1", (long long)max_groups);
+    if (!aligned(src, 16) || !aligned(out, 4)) return fail(QG_EALIGN, "qg_read_probe: src must be 16-byte, out 4-byte aligned");
+    if (overlap(out, 4, src, (size_t)bytes)) return fail(QG_EINVAL, "qg_read_probe: out overlaps src");
+    const int err = launch_read_probe(src, bytes, max_groups, magic, out, stream);
+    if (err) return fail(QG_EHIP, "kernel launch failed: %s", hip_error_name(err));
+    return ok();
+}
+
 }  // namespace
 }  // namespace qg
 
@@ -574,6 +586,10 @@ int qgemv_experts_gate_up(int fmt, int64_t n_experts, int64_t rows, int64_t cols
 int qgemv_experts_down(int fmt, int64_t n_experts, int64_t rows, int64_t cols, int T, int topk, const int32_t* ids,
                        const void* W, const float* h, float* y, void* stream) {
     return run_grouped(fmt, n_experts, rows, cols, T, topk, ids, W, nullptr, h, y, nullptr, 1, stream);
+}
+
+int qg_read_probe(const void* src, int64_t bytes, int64_t max_groups, uint32_t magic, uint32_t* out, void* stream) {
+    return run_read_probe(src, bytes, max_groups, magic, out, stream);
 }
 
 int qg_quantize_q8_0(int64_t rows, int64_t cols, const float* src, void* dst, void* stream) {

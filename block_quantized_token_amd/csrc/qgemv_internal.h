@@ -173,6 +173,10 @@ int launch_gather(int fmt, int T, const Tile& tile, const DenseArgs& a, const in
 // Quantizers (qquant_kernels.hip): kind 0 Q8_0, 1 Q4_0 absmax, 2 Q4_0 Lloyd; nblocks
 // blocks of 32 fp32 values in, as many packed blocks out.
 int launch_quantize(int kind, const float* src, uint8_t* dst, int64_t nblocks, void* stream);
+// HBM read probe (qprobe_kernels.hip): reads `bytes` (a multiple of 16) once, with
+// at most max_groups workgroups of 256 lanes; stores to *out only in practice never.
+int launch_read_probe(const void* src, int64_t bytes, int64_t max_groups, uint32_t magic, uint32_t* out,
+                      void* stream);
 const char* hip_error_name(int err);
 
 }  // namespace qg

@@ -187,6 +187,18 @@ enum { QG_Q4_ABSMAX = 0, QG_Q4_LLOYD = 1 };
 int qg_quantize_q8_0(int64_t rows, int64_t cols, const float* src, void* dst, void* stream);
 int qg_quantize_q4_0(int64_t rows, int64_t cols, int method, const float* src, void* dst, void* stream);
 
+/* HBM read probe, for measurement only: reads `bytes` of src (DEVICE, 16-byte
+ * aligned, bytes a positive multiple of 16) once, with coalesced 16-byte loads
+ * and nothing else, using at most max_groups workgroups of 256 lanes.  It gives
+ * the plain streaming-read time of a buffer, the reference the pages set their
+ * mat-vec bandwidth against ("Where the time goes on an M2 Max", its bandwidth
+ * table and the peak it quotes).  out: DEVICE, 4-byte aligned, not inside src;
+ * written only when a wave's XOR of the words it read equals `magic` (so the
+ * loads cannot be dropped), its contents otherwise unchanged.  QG_EINVAL on null
+ * pointers, bad sizes or overlap; QG_EALIGN on misalignment.  Stream-ordered and
+ * asynchronous. */
+int qg_read_probe(const void* src, int64_t bytes, int64_t max_groups, uint32_t magic, uint32_t* out, void* stream);
+
 /* ---- host-only helpers (no GPU needed) ---------------------------------- */
 
 /* Packed bytes of a rows x cols matrix of fmt; 0 if the shape is invalid. */

@@ -256,3 +256,24 @@ def test_quantizer_argument_errors(lib, call, status):
 def test_expert_projection_argument_errors(lib, call, status):
     assert call() == status, _lib.last_error()
     assert _lib.last_error()
+
+
+def test_read_probe_rejects_bad_arguments(lib):
+    """The probe's argument checks run before any HIP call (no GPU needed)."""
+    buf = ctypes.create_string_buffer(64 + 16)
+    src = (ctypes.addressof(buf) + 15) & ~15
+    out = src + 48  # inside src when bytes >= 52
+    cases = [
+        ((None, 32, 1, 0, src + 32), _lib.QG_EINVAL),
+        ((src, 32, 1, 0, None), _lib.QG_EINVAL),
+        ((src, 0, 1, 0, src + 32), _lib.QG_EINVAL),
+        ((src, 24, 1, 0, src + 32), _lib.QG_EINVAL),
+        ((src, 32, 0, 0, src + 32), _lib.QG_EINVAL),
+        ((src + 4, 32, 1, 0, src + 48), _lib.QG_EALIGN),
+        ((src, 32, 1, 0, src + 34), _lib.QG_EALIGN),
+        ((src, 64, 1, 0, out), _lib.QG_EINVAL),
+    ]
+    for args, status in cases:
+        assert _lib.qg_read_probe(*args) == status, (args, _lib.last_error())
+        assert _lib.last_error()
+
