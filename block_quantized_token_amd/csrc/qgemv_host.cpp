@@ -104,13 +104,15 @@ const TuneEntry kTuned[] = {
     {QG_FMT_Q8_0, 10240, 2560, 3, "4,5,40,L2"},
     {QG_FMT_Q8_0, 10240, 2560, 4, "4,5,40,L2"},
     {QG_FMT_Q8_0, 2560, 6144, 0, "4,12,16,s"},     // register-streamed beats DMA at 12 slices
-    // LM head: the LDS-DMA VALU kernel at T <= 2 (231 / 247 µs against 252 / 258
-    // for the matrix cores), the persistent matrix-core kernel at T >= 3 (270 / 278
+    // LM head: the LDS-DMA VALU kernel at T <= 2 (233 / 241 µs against 249 / 256
+    // for the matrix cores), the persistent matrix-core kernel at T >= 3 (267 / 275
     // µs against 285 / 311).  A token's bits agree across T = 1, 2 and across
     // T = 3, 4, not between the two pairs; a caller who needs one kind for all T
-    // pins it with QGEMV_TILE.
-    {QG_FMT_Q8_0, 248320, 5120, 1, "4,10,64,l2"},
-    {QG_FMT_Q8_0, 248320, 5120, 2, "4,10,256,l2"},
+    // pins it with QGEMV_TILE.  512 rows per workgroup (485 workgroups): the same
+    // time as 64 at T = 1 and 3 µs less at T = 2, and an eighth of the fused
+    // argmax's per-workgroup merges (239 / 247 µs against 250 / 253).
+    {QG_FMT_Q8_0, 248320, 5120, 1, "4,10,512,l2"},
+    {QG_FMT_Q8_0, 248320, 5120, 2, "4,10,512,l2"},
     {QG_FMT_Q8_0, 248320, 5120, 3, "8,10,64,p"},
     {QG_FMT_Q8_0, 248320, 5120, 4, "8,10,64,p"},
     {QG_FMT_Q4_0, 8192, 2560, 1, "4,5,8,d"},       // direct: 6.0 vs 7.7 µs for the LDS-DMA ring
