@@ -55,14 +55,15 @@ bool parse_tile_spec(const std::string& spec, Tile* t, std::string* why) {
     int rb = 0, nw = 0, rw = 0, depth = 0;
     char kind = 0, tail = 0;
     int got = sscanf(spec.c_str(), "%d,%d,%d,%c%c", &rb, &nw, &rw, &kind, &tail);
-    if (got == 5 && (kind == 'l' || kind == 'L' || kind == 'u')) {  // l<depth>, L<depth>, u<depth>
+    if (got == 5 && (kind == 'l' || kind == 'L' || kind == 'u' || kind == 'h')) {  // l|L|u|h<depth>
         char tail2 = 0;
-        const char* f = kind == 'l' ? "%d,%d,%d,l%d%c" : kind == 'L' ? "%d,%d,%d,L%d%c" : "%d,%d,%d,u%d%c";
+        const char* f = kind == 'l' ? "%d,%d,%d,l%d%c" : kind == 'L' ? "%d,%d,%d,L%d%c"
+                      : kind == 'u' ? "%d,%d,%d,u%d%c" : "%d,%d,%d,h%d%c";
         got = sscanf(spec.c_str(), f, &rb, &nw, &rw, &depth, &tail2) == 4 ? 4 : -1;
     }
-    const bool dma = kind == 'l' || kind == 'L' || kind == 'u';
+    const bool dma = kind == 'l' || kind == 'L' || kind == 'u' || kind == 'h';
     if (!(got == 3 || (got == 4 && (kind == 'd' || kind == 's' || kind == 'm' || kind == 'p' || (dma && depth > 0))))) {
-        *why = "tile '" + spec + "' is not rb,nw,rw[,d|s|m|p|l<depth>|L<depth>|u<depth>]";
+        *why = "tile '" + spec + "' is not rb,nw,rw[,d|s|m|p|l<depth>|L<depth>|u<depth>|h<depth>]";
         return false;
     }
     if (!valid_rb(rb) || nw < 1 || nw > kMaxWaves || rw < 2 * rb || rw % (2 * rb) || rw > (1 << 20)) {
@@ -72,7 +73,8 @@ bool parse_tile_spec(const std::string& spec, Tile* t, std::string* why) {
     t->rows_per_batch = rb;
     t->waves_per_wg = nw;
     t->rows_per_wg = rw;
-    t->kind = got == 4 ? (kind == 'd' ? 0 : kind == 'l' ? 2 : kind == 'L' ? 3 : kind == 'u' ? 4 : 1) : -1;  // -1: later
+    t->kind = got == 4 ? (kind == 'd' ? 0 : kind == 'l' ? 2 : kind == 'L' ? 3 : kind == 'u' ? 4 : kind == 'h' ? 7 : 1)
+                       : -1;  // -1: later
     t->mfma = got == 4 && kind == 'm' ? 1 : got == 4 && kind == 'p' ? 2 : 0;
     t->depth = got == 4 && dma ? depth : 0;
     return true;
@@ -99,10 +101,10 @@ const TuneEntry kTuned[] = {
     {QG_FMT_Q8_0, 2560, 2560, 2, "2,5,4,d"},
     {QG_FMT_Q8_0, 2560, 2560, 3, "2,5,4,d"},
     {QG_FMT_Q8_0, 2560, 2560, 4, "4,5,16,s"},
-    // 10240 x 2560: the rule's LDS-DMA ring at T <= 2; at T >= 3, x staged apart
-    // and a ring of two (10.5 / 11.7 µs against 10.9 / 11.9 with x in the ring)
-    {QG_FMT_Q8_0, 10240, 2560, 3, "4,5,40,L2"},
-    {QG_FMT_Q8_0, 10240, 2560, 4, "4,5,40,L2"},
+    // 10240 x 2560: 256-wide k slices, ten waves of half a slice's work (three or
+    // two per SIMD instead of five full waves, two of them on one SIMD): 7.7 / 8.3 /
+    // 9.1 / 9.9 µs against 8.0 / 9.1 / 10.5 / 11.7 for the 512-wide LDS-DMA ring
+    {QG_FMT_Q8_0, 10240, 2560, 0, "4,10,40,h2"},
     {QG_FMT_Q8_0, 2560, 6144, 0, "4,12,16,s"},     // register-streamed beats DMA at 12 slices
     // LM head: the LDS-DMA VALU kernel at T <= 2 (233 / 241 µs against 249 / 256
     // for the matrix cores), the persistent matrix-core kernel at T >= 3 (267 / 275
@@ -241,6 +243,18 @@ int pick_tile(int fmt, int64_t rows, int64_t cols, int T, Tile* t) {
                         units_lds_bytes(fmt, *t, T, cols), t->rows_per_wg, t->depth);
         return QG_OK;
     }
+    if (t->kind == 7) {
+        const int64_t nsl256 = cols / 256;
+        if (cols % 256 || t->waves_per_wg % nsl256 != 0)
+            return fail(QG_EINVAL, "half-slice tile needs cols a multiple of 256 and waves_per_wg a multiple of the "
+                                   "%lld 256-wide slices", (long long)nsl256);
+        if (!half_supported(fmt, t->rows_per_batch, t->depth))
+            return fail(QG_EINVAL, "half-slice tile is compiled for q8_0 with rb 4 and depth 2 or 3");
+        if (half_lds_bytes(*t, T, (int)nsl256) > kMaxLds)
+            return fail(QG_EINVAL, "tile needs %zu B of LDS (rows_per_wg %d or depth %d too large)",
+                        half_lds_bytes(*t, T, (int)nsl256), t->rows_per_wg, t->depth);
+        return QG_OK;
+    }
     if (t->kind == 2 || t->kind == 3) {
         if (!stream_shape)
             return fail(QG_EINVAL, "streamed tile needs rows of a multiple of 16 bytes and waves_per_wg a multiple of "
@@ -326,7 +340,8 @@ int run_dense(int fmt, int64_t rows, int64_t cols, int T, const void* W, const f
     a.nslices = (int)((cols + kSlice - 1) / kSlice);
     a.rows_per_wg = tile.rows_per_wg;
     if ((rows + tile.rows_per_wg - 1) / tile.rows_per_wg > 0x7FFFFFFF) return fail(QG_EUNSUPPORTED, "grid too large");
-    int err = tile.kind == 4   ? launch_units(fmt, T, tile, a, stream)
+    int err = tile.kind == 7   ? launch_half(fmt, T, tile, a, stream)
+              : tile.kind == 4 ? launch_units(fmt, T, tile, a, stream)
               : tile.kind >= 2 ? launch_dma(fmt, T, tile, a, stream)
               : tile.kind == 1 ? launch_stream(fmt, T, tile, a, stream)
                                : launch_dense(fmt, T, tile, a, stream);
@@ -362,6 +377,7 @@ int run_argmax(int fmt, int64_t rows, int64_t cols, int T, const void* W, const 
         if (tile.kind == 2 && !dma_supported(fmt, T, 4, 4, false)) tile.kind = 3;
         if (dma_lds_bytes(fmt, tile, T, (int)nsl) > kMaxLds) tile.kind = 0;
     }
+    if (tile.kind == 7 && (fmt != QG_FMT_Q8_0 || half_lds_bytes(tile, T, (int)(cols / 256)) > kMaxLds)) tile.kind = 0;
     if (tile.kind == 4 || (tile.kind == 1 && tile.mfma == 1)) tile.kind = 0;
     if (tile.kind == 1 && !persist && (tile.rows_per_batch != 4 || !stream_supported(fmt, T, 4))) tile.kind = 0;
     if (tile.kind == 0) {  // direct, rb 2, one wave per slice when the slices fit a workgroup

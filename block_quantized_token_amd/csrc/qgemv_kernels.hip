@@ -872,6 +872,182 @@ __device__ __forceinline__ void dma_rows(const uint8_t* __restrict__ W, int64_t 
     }
 }
 
+// --------------------------------------- half slices: 16 lanes per row (Q8_0)
+// The LDS-DMA kernel with k cut into 256-wide slices (8 blocks, 272 bytes of a
+// row) and one wave per slice: a 32-column-block matrix of 10240 x 2560 runs ten
+// waves per workgroup, three or two per SIMD with half a slice's work each,
+// instead of five waves that put two full shares on one SIMD.  A row's 16 lanes
+// own 16 weights each (the lane layout of the 512-wide kernels, blocks 0..7);
+// the four 16-lane groups of a wave take rows g and g + 4 of an 8-row tile, and
+// reduce over their 16 lanes with the four DPP stages of the halving butterfly.
+// Slices are summed in order at the end, so a token's bits do not depend on T.
+constexpr int kHalfSlice = 256;
+struct HalfShape {                 // Q8_0, 8-row tiles
+    static constexpr int kChunks = 17;                   // 8 blocks x 34 B per row slice
+    static constexpr int kLoads = (8 * kChunks + 63) / 64;  // 3
+    static constexpr int kBufBytes = kLoads * 1024;      // per ring slot
+};
+
+template <int N>
+__device__ __forceinline__ void butterfly16(float (&v)[N], int li) {
+    constexpr int ctrls[4] = {0x140, 0x141, 0x4E, 0xB1};
+#pragma unroll
+    for (int st = 0; st < 4; ++st) {
+        const int m = 8 >> st;
+        const int cnt = N >> st;
+        if (cnt >= 2) {
+            const bool up = (li & m) != 0;
+#pragma unroll
+            for (int i = 0; i < cnt / 2; ++i) {
+                const float lo = v[i] + dpp_f(v[i], ctrls[st]);
+                const float hi = v[i + cnt / 2] + dpp_f(v[i + cnt / 2], ctrls[st]);
+                v[i] = up ? hi : lo;
+            }
+        } else {
+            v[0] = v[0] + dpp_f(v[0], ctrls[st]);
+        }
+    }
+}
+
+template <int N>
+__device__ __forceinline__ int butterfly16_index(int li, bool& writer) {
+    int idx = 0;
+    writer = true;
+#pragma unroll
+    for (int st = 0; st < 4; ++st) {
+        const int m = 8 >> st;
+        const int cnt = N >> st;
+        if (cnt >= 2) {
+            if (li & m) idx += cnt / 2;
+        } else if (li & m) {
+            writer = false;
+        }
+    }
+    return idx;
+}
+
+// Lane l of load k fetches chunk j = 64 k + l of the tile's slice: row j / 17,
+// chunk j % 17 (past the tile's 8 rows or the slice's chunks: nothing, zeros).
+__device__ __forceinline__ void half_offsets(int64_t row_bytes, int s, int lane, int (&off)[HalfShape::kLoads]) {
+    const int64_t rest = row_bytes - (int64_t)s * HalfShape::kChunks * 16;
+    const int cs = rest / 16 < HalfShape::kChunks ? (int)(rest / 16) : HalfShape::kChunks;
+#pragma unroll
+    for (int k = 0; k < HalfShape::kLoads; ++k) {
+        const int j = 64 * k + lane;
+        const int r = j / HalfShape::kChunks, c = j % HalfShape::kChunks;
+        off[k] = (r < 8 && c < cs) ? (int)(r * row_bytes) + s * HalfShape::kChunks * 16 + 16 * c : kNoLoad;
+    }
+}
+
+__device__ __forceinline__ void half_issue(const uint8_t* __restrict__ W, int64_t row_bytes, int64_t row_begin,
+                                           int64_t row_end, int ntiles, int t, const int (&off)[HalfShape::kLoads],
+                                           uint8_t* lbuf) {
+    const bool live = t < ntiles;
+    const int64_t r0 = row_begin + (int64_t)(live ? t : 0) * 8;
+    const int64_t rows_here = row_end - r0 < 8 ? row_end - r0 : 8;
+    const int num = live ? (int)(rows_here * row_bytes) : 0;
+    const __amdgpu_buffer_rsrc_t rsrc =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(W + r0 * row_bytes), (short)0, num, kBufferRsrcWord3);
+#pragma unroll
+    for (int k = 0; k < HalfShape::kLoads; ++k) load_lds16(rsrc, lbuf + 1024 * k, off[k]);
+}
+
+template <int NT, int D, class Out>
+__device__ __forceinline__ void half_rows(const uint8_t* __restrict__ W, int64_t row_bytes, int cols, int nsl,
+                                          const float* __restrict__ x, int64_t row_begin, int64_t row_end, int nw,
+                                          Out&& out) {
+    using F = Fmt<QG_FMT_Q8_0>;
+    constexpr int TP = pad_pow2(NT);
+    constexpr int RB = 2;  // rows per 16-lane group per tile
+    constexpr int N = RB * TP;
+    constexpr int L = HalfShape::kLoads;
+    static_assert(D * L <= 63, "vmcnt holds at most 63 outstanding loads");
+    extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: keeps descriptors and M0 scalar
+    const int g = lane >> 4;   // 16-lane group: rows g and g + 4 of a tile
+    const int li = lane & 15;
+    const int s = wave % nsl, rg = wave / nsl, RG = nw / nsl;
+    const int k0 = s * kHalfSlice;
+    const int ntiles = (int)((row_end - row_begin + 7) / 8);
+    uint8_t* ring = smem + wave * D * HalfShape::kBufBytes;
+    uint8_t* xl = smem + nw * D * HalfShape::kBufBytes + wave * NT * 1024;          // x[NT][256] of the slice
+    float* part = reinterpret_cast<float*>(smem + nw * (D * HalfShape::kBufBytes + NT * 1024));  // [tiles][nsl][4][N]
+
+    int off[L];
+    half_offsets(row_bytes, s, lane, off);
+    const bool lane_ok = F::lane_valid(li, k0, cols);
+    bool writer;
+    const int my_idx = butterfly16_index<N>(li, writer);
+
+    // x of the slice (k past cols reads as zero), then the first D tiles
+#pragma unroll
+    for (int n = 0; n < NT; ++n) {
+        const __amdgpu_buffer_rsrc_t xr_rsrc =
+            __builtin_amdgcn_make_buffer_rsrc((void*)(x + (int64_t)n * cols + k0), (short)0, (cols - k0) * 4,
+                                              kBufferRsrcWord3);
+        load_lds16(xr_rsrc, xl + 1024 * n, 16 * lane);
+    }
+#pragma unroll
+    for (int i = 0; i < D; ++i)
+        half_issue(W, row_bytes, row_begin, row_end, ntiles, rg + i * RG, off, ring + i * HalfShape::kBufBytes);
+    wait_vmcnt<D * L>();  // x is older than every tile
+    float xr[NT][kWeightsPerLane];
+    {
+        const int b0 = F::kbase(li, 0), b1 = F::kbase(li, 1);
+#pragma unroll
+        for (int n = 0; n < NT; ++n) {
+            const float4* p0 = reinterpret_cast<const float4*>(xl + 1024 * n + 4 * b0);
+            const float4* p1 = reinterpret_cast<const float4*>(xl + 1024 * n + 4 * b1);
+            const float4 a = p0[0], b = p0[1], c = p1[0], d = p1[1];
+            xr[n][0] = a.x; xr[n][1] = a.y; xr[n][2] = a.z; xr[n][3] = a.w;
+            xr[n][4] = b.x; xr[n][5] = b.y; xr[n][6] = b.z; xr[n][7] = b.w;
+            xr[n][8] = c.x; xr[n][9] = c.y; xr[n][10] = c.z; xr[n][11] = c.w;
+            xr[n][12] = d.x; xr[n][13] = d.y; xr[n][14] = d.z; xr[n][15] = d.w;
+        }
+    }
+
+    const int mine = ntiles > rg ? (ntiles - rg + RG - 1) / RG : 0;
+    for (int i = 0; i < mine; ++i) {
+        uint8_t* buf = ring + (i % D) * HalfShape::kBufBytes;
+        const int t = rg + i * RG;
+        wait_vmcnt<(D - 1) * L>();
+        typename F::Raw raw[RB];
+#pragma unroll
+        for (int r = 0; r < RB; ++r) raw[r] = lds_lane<QG_FMT_Q8_0>(buf + (4 * r + g) * (HalfShape::kChunks * 16), li);
+        float acc[RB][TP];
+#pragma unroll
+        for (int r = 0; r < RB; ++r)
+#pragma unroll
+            for (int n = 0; n < TP; ++n) acc[r][n] = 0.0f;
+        accumulate_batch<QG_FMT_Q8_0, NT, RB>(raw, xr, lane_ok, true, acc);
+        float v[N];
+#pragma unroll
+        for (int r = 0; r < RB; ++r)
+#pragma unroll
+            for (int n = 0; n < TP; ++n) v[r * TP + n] = acc[r][n];
+        butterfly16<N>(v, li);
+        if (writer) part[(((size_t)t * nsl + s) * 4 + g) * N + my_idx] = v[0];
+        wait_lgkmcnt0();
+        half_issue(W, row_bytes, row_begin, row_end, ntiles, rg + (i + D) * RG, off, buf);
+    }
+    wait_vmcnt<0>();
+    __syncthreads();
+    // every output of the workgroup: sum the slices' partials in slice order
+    const int nrows = (int)(row_end - row_begin);
+    for (int o = tid; o < nrows * NT; o += blockDim.x) {
+        const int rr = o / NT, tk = o % NT;
+        const int tl = rr / 8, rin = rr % 8;
+        const int gg = rin & 3, r = rin >> 2;
+        const float* base = part + ((size_t)tl * nsl * 4 + gg) * N + r * TP + tk;
+        float sum = base[0];
+        for (int w = 1; w < nsl; ++w) sum = sum + base[(size_t)w * 4 * N];
+        out(tk, row_begin + rr, sum);
+    }
+}
+
 // ------------------------------------------------------ row-subset (gather)
 // The mat-vec over a list of rows, y[t][i] = W[ids[i]] . x[t] (the draft-vocabulary
 // LM head in the mlxcel drafter-cost issue: the drafter reads only the rows of the
@@ -1503,6 +1679,16 @@ qgemv_dma_kernel(const uint8_t* __restrict__ W, const float* __restrict__ x, flo
                                   [=](int t, int64_t row, float v) { y[t * rows + row] = v; });
 }
 
+template <int T, int D>
+__global__ void __launch_bounds__(64 * kMaxWaves)
+qgemv_half_kernel(const uint8_t* __restrict__ W, const float* __restrict__ x, float* __restrict__ y, int64_t rows,
+                  int64_t row_bytes, int cols, int nslices, int rows_per_wg, int nw) {
+    const int64_t row_begin = (int64_t)blockIdx.x * rows_per_wg;
+    const int64_t row_end = row_begin + rows_per_wg < rows ? row_begin + rows_per_wg : rows;
+    half_rows<T, D>(W, row_bytes, cols, nslices, x, row_begin, row_end, nw,
+                    [=](int t, int64_t row, float v) { y[t * rows + row] = v; });
+}
+
 template <int FMT, int T, int D>
 __global__ void __launch_bounds__(64 * kMaxWaves) qgemv_units_kernel(DenseArgs a) {
     const int64_t row_begin = (int64_t)blockIdx.x * a.rows_per_wg;
@@ -1534,6 +1720,15 @@ __global__ void __launch_bounds__(64 * kMaxWaves) qgemv_dma_argmax_kernel(DenseA
     ArgmaxOut<T> best;
     dma_rows<FMT, T, ST, D, XSEP>(a.W, a.row_bytes, a.cols, a.nslices, a.x, xoff, row_begin, row_end,
                                   (int)(blockDim.x >> 6), best);
+    best.merge(work);
+}
+
+template <int T, int D>
+__global__ void __launch_bounds__(64 * kMaxWaves) qgemv_half_argmax_kernel(DenseArgs a, unsigned long long* work) {
+    const int64_t row_begin = (int64_t)blockIdx.x * a.rows_per_wg;
+    const int64_t row_end = row_begin + a.rows_per_wg < a.rows ? row_begin + a.rows_per_wg : a.rows;
+    ArgmaxOut<T> best;
+    half_rows<T, D>(a.W, a.row_bytes, a.cols, a.nslices, a.x, row_begin, row_end, (int)(blockDim.x >> 6), best);
     best.merge(work);
 }
 
@@ -2013,6 +2208,29 @@ int launch_units(int fmt, int T, const Tile& tile, const DenseArgs& a, void* str
     return (int)hipGetLastError();
 }
 
+template <int T>
+DmaFn half_entry(int depth) {
+    switch (depth) {
+    case 2: return qgemv_half_kernel<T, 2>;
+    case 3: return qgemv_half_kernel<T, 3>;
+    default: return nullptr;
+    }
+}
+
+int launch_half(int fmt, int T, const Tile& tile, const DenseArgs& a, void* stream) {
+    const int nsl = (int)(a.cols / kHalfSlice);
+    if (fmt != QG_FMT_Q8_0 || tile.rows_per_batch != 4 || a.cols % kHalfSlice || tile.waves_per_wg % nsl)
+        return (int)hipErrorInvalidValue;
+    const DmaFn fn = T == 1 ? half_entry<1>(tile.depth) : T == 2 ? half_entry<2>(tile.depth)
+                   : T == 3 ? half_entry<3>(tile.depth) : half_entry<4>(tile.depth);
+    if (!fn) return (int)hipErrorInvalidValue;
+    const int64_t nwg = (a.rows + tile.rows_per_wg - 1) / tile.rows_per_wg;
+    hipLaunchKernelGGL(fn, dim3((unsigned)nwg), dim3(64 * tile.waves_per_wg), half_lds_bytes(tile, T, nsl),
+                       (hipStream_t)stream, a.W, a.x, a.y, a.rows, a.row_bytes, a.cols, nsl, a.rows_per_wg,
+                       tile.waves_per_wg);
+    return (int)hipGetLastError();
+}
+
 using ArgmaxFn = void (*)(DenseArgs, unsigned long long*);
 
 template <int FMT, int T>
@@ -2065,12 +2283,23 @@ ArgmaxFn argmax_dense_for(int T, bool os) {
     }
 }
 
-int launch_argmax(int fmt, int T, const Tile& tile, const DenseArgs& a, void* work, int32_t* idx, float* val,
+int launch_argmax(int fmt, int T, const Tile& tile, const DenseArgs& a_in, void* work, int32_t* idx, float* val,
                   void* stream) {
     ArgmaxFn fn = nullptr;
     int64_t nwg = 0;
     size_t lds = 0;
-    if (tile.kind == 1 && tile.mfma == 2 && fmt == QG_FMT_Q8_0 && tile.rows_per_batch == 8 &&
+    DenseArgs a = a_in;
+    if (tile.kind == 7 && fmt == QG_FMT_Q8_0 && tile.rows_per_batch == 4 && a.cols % kHalfSlice == 0 &&
+        tile.waves_per_wg % (a.cols / kHalfSlice) == 0) {
+        a.nslices = a.cols / kHalfSlice;  // 256-wide slices
+        const int d = tile.depth;
+        fn = T == 1 ? (d == 2 ? qgemv_half_argmax_kernel<1, 2> : d == 3 ? qgemv_half_argmax_kernel<1, 3> : nullptr)
+           : T == 2 ? (d == 2 ? qgemv_half_argmax_kernel<2, 2> : d == 3 ? qgemv_half_argmax_kernel<2, 3> : nullptr)
+           : T == 3 ? (d == 2 ? qgemv_half_argmax_kernel<3, 2> : d == 3 ? qgemv_half_argmax_kernel<3, 3> : nullptr)
+                    : (d == 2 ? qgemv_half_argmax_kernel<4, 2> : d == 3 ? qgemv_half_argmax_kernel<4, 3> : nullptr);
+        nwg = (a.rows + tile.rows_per_wg - 1) / tile.rows_per_wg;
+        lds = half_lds_bytes(tile, T, a.nslices);
+    } else if (tile.kind == 1 && tile.mfma == 2 && fmt == QG_FMT_Q8_0 && tile.rows_per_batch == 8 &&
         tile.waves_per_wg == a.nslices) {
         fn = T == 1 ? qgemv_persist_argmax_kernel<1> : T == 2 ? qgemv_persist_argmax_kernel<2>
            : T == 3 ? qgemv_persist_argmax_kernel<3> : qgemv_persist_argmax_kernel<4>;

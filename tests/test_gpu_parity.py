@@ -190,10 +190,10 @@ def test_repeat_calls_bitwise(torch):
 
 
 def test_tile_override_keeps_bits(torch, monkeypatch):
-    """Different row tilings with the same k split give identical bits."""
+    """Different row tilings with the same k split (512-wide slices) give identical bits."""
     c = I.dense_case("c2a_q8_0_10240x2560")
     Wd, xd = dev(torch, c["W"]), dev(torch, c["x"])
-    monkeypatch.delenv("QGEMV_TILE", raising=False)
+    monkeypatch.setenv("QGEMV_TILE", "q8_0:4,5,40,L2")
     base = ops.gemv("q8_0", Wd, xd, c["rows"]).cpu().numpy()
     for tile in ("q8_0:1,5,2", "q8_0:2,5,8", "q8_0:1,5,64", "q8_0:2,5,100"):
         monkeypatch.setenv("QGEMV_TILE", tile)
@@ -266,6 +266,45 @@ def test_dma_ring_depths_agree_bitwise(torch, monkeypatch, name):
                 ran += 1
         # 12 slices: a ring of 3 slots per wave, which x needs at T >= 3, passes the LDS
         assert ran >= 3 or (name == "c2b_q8_0_2560x6144" and T >= 3), (name, T, ran)
+
+
+# ------------------------------------- 256-wide k slices, 16 lanes per row (h<depth>)
+def half_tile(cols, rw=40, depth=2, rg=1):
+    return f"q8_0:4,{(cols // 256) * rg},{rw},h{depth}"
+
+
+@pytest.mark.parametrize("name,rw,depth", [("c2a_q8_0_10240x2560", 40, 2), ("c2a_q8_0_10240x2560", 40, 3),
+                                           ("c1_q8_0_2560x2560", 16, 2)])
+def test_half_slice_config_full(torch, orc, monkeypatch, name, rw, depth):
+    """The half-slice kernel on the workloads: parity at every T, a token's bits equal across T."""
+    c = I.dense_case(name)
+    monkeypatch.setenv("QGEMV_TILE", half_tile(c["cols"], rw, depth))
+    st, t = _lib.qg_query_tile(c["fmt"], c["rows"], c["cols"], 4)
+    assert st == 0 and t[6] == 7 and t[7] == depth, (st, t)
+    check_dense(torch, orc, c["fmt"], c["rows"], c["cols"], c["W"], c["x"], f"half {name} rw={rw} d={depth}")
+
+
+def test_half_slice_tiny_and_dyadic(torch, orc, monkeypatch):
+    """Ragged rows (partial tiles, fewer tiles than the ring), one to twelve slices,
+    two row groups; dyadic inputs bitwise."""
+    for rows in TINY_ROWS:
+        for cols in (256, 512, 768, 1280, 2304, 3072):
+            for rw, depth, rg in ((8, 2, 1), (24, 3, 1), (16, 2, 2)):
+                monkeypatch.setenv("QGEMV_TILE", half_tile(cols, rw, depth, rg))
+                if _lib.qg_query_tile(Q8, rows, cols, 4)[0]:
+                    continue  # more than twelve waves
+                rng = np.random.default_rng(rows * 1000 + cols + rw)
+                W = I.weights(rng, Q8, rows, cols)
+                x = I.activations(rng, cols)
+                check_dense(torch, orc, Q8, rows, cols, W, x, f"half tiny rw={rw} d={depth} rg={rg}")
+    rng = np.random.default_rng(97)
+    rows, cols = 1000, 2816
+    W = dyadic_weights(rng, Q8, rows, cols)
+    x = (rng.integers(-4, 5, (4, cols)) / 4.0).astype(np.float32)
+    monkeypatch.setenv("QGEMV_TILE", half_tile(cols, 40, 2))
+    y = gpu_gemv(torch, Q8, dev(torch, W), x, rows)
+    ref, _ = orc.gemv(Q8, rows, cols, W, x)
+    assert np.array_equal(y.astype(np.float64), ref)
 
 
 def test_tile_override_other_k_split(torch, orc, monkeypatch):
