@@ -216,8 +216,9 @@ int qg_unpack_q4_0(int64_t rows, int64_t cols, const void* in, uint16_t* d_bits,
  * out_tile = {lanes_per_row, rows_per_batch, waves_per_wg, k_slice, rows_per_wg, mfma, kind, depth}
  * (kind 0: direct loads, 1: streamed through LDS via registers, 2 / 3: streamed
  * by direct-to-LDS loads with `depth` tiles in flight per wave (3: x staged
- * apart), 4: unit-balanced direct-to-LDS; mfma 1: matrix-core contraction,
- * 2: its persistent form). */
+ * apart), 4: unit-balanced direct-to-LDS, 7: direct-to-LDS on 256-wide k slices
+ * with 16 lanes per row (Q8_0); mfma 1: matrix-core contraction, 2: its
+ * persistent form). */
 int qg_query_tile(int fmt, int64_t rows, int64_t cols, int T, int out_tile[QG_TILE_FIELDS]);
 
 /* Static description of a status code (never NULL). */
