@@ -248,11 +248,11 @@ int pick_tile(int fmt, int64_t rows, int64_t cols, int T, Tile* t) {
         if (cols % 256 || t->waves_per_wg % nsl256 != 0)
             return fail(QG_EINVAL, "half-slice tile needs cols a multiple of 256 and waves_per_wg a multiple of the "
                                    "%lld 256-wide slices", (long long)nsl256);
-        if (!half_supported(fmt, t->rows_per_batch, t->depth))
-            return fail(QG_EINVAL, "half-slice tile is compiled for q8_0 with rb 4 and depth 2 or 3");
-        if (half_lds_bytes(*t, T, (int)nsl256) > kMaxLds)
+        if (!half_supported(t->rows_per_batch, t->depth))
+            return fail(QG_EINVAL, "half-slice tile is compiled with rb 4 and depth 2 or 3");
+        if (half_lds_bytes(fmt, *t, T, (int)nsl256) > kMaxLds)
             return fail(QG_EINVAL, "tile needs %zu B of LDS (rows_per_wg %d or depth %d too large)",
-                        half_lds_bytes(*t, T, (int)nsl256), t->rows_per_wg, t->depth);
+                        half_lds_bytes(fmt, *t, T, (int)nsl256), t->rows_per_wg, t->depth);
         return QG_OK;
     }
     if (t->kind == 2 || t->kind == 3) {
@@ -377,7 +377,7 @@ int run_argmax(int fmt, int64_t rows, int64_t cols, int T, const void* W, const 
         if (tile.kind == 2 && !dma_supported(fmt, T, 4, 4, false)) tile.kind = 3;
         if (dma_lds_bytes(fmt, tile, T, (int)nsl) > kMaxLds) tile.kind = 0;
     }
-    if (tile.kind == 7 && (fmt != QG_FMT_Q8_0 || half_lds_bytes(tile, T, (int)(cols / 256)) > kMaxLds)) tile.kind = 0;
+    if (tile.kind == 7 && half_lds_bytes(fmt, tile, T, (int)(cols / 256)) > kMaxLds) tile.kind = 0;
     if (tile.kind == 4 || (tile.kind == 1 && tile.mfma == 1)) tile.kind = 0;
     if (tile.kind == 1 && !persist && (tile.rows_per_batch != 4 || !stream_supported(fmt, T, 4))) tile.kind = 0;
     if (tile.kind == 0) {  // direct, rb 2, one wave per slice when the slices fit a workgroup

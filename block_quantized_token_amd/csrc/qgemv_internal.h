@@ -21,7 +21,7 @@ struct Tile {
                          // registers; 2: streamed by LDS-DMA loads into a ring of `depth` buffers,
                          // x staged in the ring's last slots; 3: as 2, x staged in its own region;
                          // 4: unit-balanced LDS-DMA (waves take equal shares of (slice, tile) units);
-                         // 7: LDS-DMA on 256-wide k slices, 16 lanes per row (Q8_0)
+                         // 7: LDS-DMA on 256-wide k slices, 16 lanes per row
     int depth;           // kinds 2, 3: tiles in flight per wave (2, 3, 4 or 6); kind 4: 2..4; kind 7: 2, 3; 0 otherwise
 };
 
@@ -90,14 +90,16 @@ inline size_t dma_lds_bytes(int fmt, const Tile& t, int T, int nslices) {
            ntiles * nslices * 2 * t.rows_per_batch * pad_tokens(T) * 4;
 }
 
-// Half-slice LDS-DMA kernel (kind 7): Q8_0, 256-wide k slices (cols a multiple of
-// 256), one wave per slice (times row groups), 8-row tiles (rb 4) in rings of
-// `depth` (2 or 3) 3 KB slots, x of the slice staged apart ([waves][T][1 KB]),
-// then partial sums [tiles][slices][4 groups][2 rows * pad(T)].
-inline bool half_supported(int fmt, int rb, int depth) { return fmt == QG_FMT_Q8_0 && rb == 4 && (depth == 2 || depth == 3); }
-inline size_t half_lds_bytes(const Tile& t, int T, int nslices256) {
+// Half-slice LDS-DMA kernel (kind 7): 256-wide k slices (cols a multiple of 256),
+// one wave per slice (times row groups), 8-row tiles (rb 4) in rings of `depth`
+// (2 or 3) slots of 3 / 2 / 4 KB (Q8_0 / Q4_0 / BF16), x of the slice staged apart
+// ([waves][T][1 KB]), then partial sums [tiles][slices][4 groups][2 rows * pad(T)].
+inline bool half_supported(int rb, int depth) { return rb == 4 && (depth == 2 || depth == 3); }
+inline size_t half_slot_bytes(int fmt) { return (size_t)((8 * (stream_chunks(fmt) / 2) + 63) / 64) * 1024; }
+inline size_t half_lds_bytes(int fmt, const Tile& t, int T, int nslices256) {
     const size_t ntiles = (size_t)(t.rows_per_wg + 7) / 8;
-    return (size_t)t.waves_per_wg * (t.depth * 3072 + (size_t)T * 1024) + ntiles * nslices256 * 4 * 2 * pad_tokens(T) * 4;
+    return (size_t)t.waves_per_wg * (t.depth * half_slot_bytes(fmt) + (size_t)T * 1024) +
+           ntiles * nslices256 * 4 * 2 * pad_tokens(T) * 4;
 }
 
 // Row-subset kernel: rings of `depth` 8-row slots per wave, then partial sums (x in registers).

@@ -872,9 +872,9 @@ __device__ __forceinline__ void dma_rows(const uint8_t* __restrict__ W, int64_t 
     }
 }
 
-// --------------------------------------- half slices: 16 lanes per row (Q8_0)
-// The LDS-DMA kernel with k cut into 256-wide slices (8 blocks, 272 bytes of a
-// row) and one wave per slice: a 32-column-block matrix of 10240 x 2560 runs ten
+// ------------------------------------------------ half slices: 16 lanes per row
+// The LDS-DMA kernel with k cut into 256-wide slices (8 blocks: 272 / 144 bytes
+// of a Q8_0 / Q4_0 row, 512 of a BF16 row) and one wave per slice: a 32-column-block matrix of 10240 x 2560 runs ten
 // waves per workgroup, three or two per SIMD with half a slice's work each,
 // instead of five waves that put two full shares on one SIMD.  A row's 16 lanes
 // own 16 weights each (the lane layout of the 512-wide kernels, blocks 0..7);
@@ -882,10 +882,11 @@ __device__ __forceinline__ void dma_rows(const uint8_t* __restrict__ W, int64_t 
 // reduce over their 16 lanes with the four DPP stages of the halving butterfly.
 // Slices are summed in order at the end, so a token's bits do not depend on T.
 constexpr int kHalfSlice = 256;
-struct HalfShape {                 // Q8_0, 8-row tiles
-    static constexpr int kChunks = 17;                   // 8 blocks x 34 B per row slice
-    static constexpr int kLoads = (8 * kChunks + 63) / 64;  // 3
-    static constexpr int kBufBytes = kLoads * 1024;      // per ring slot
+template <int FMT>
+struct HalfShape {  // 8-row tiles
+    static constexpr int kChunks = StreamFmt<FMT>::kChunks / 2;  // 16-byte chunks per row slice: 17, 9, 32
+    static constexpr int kLoads = (8 * kChunks + 63) / 64;       // 3, 2, 4
+    static constexpr int kBufBytes = kLoads * 1024;              // per ring slot
 };
 
 template <int N>
@@ -926,21 +927,24 @@ __device__ __forceinline__ int butterfly16_index(int li, bool& writer) {
     return idx;
 }
 
-// Lane l of load k fetches chunk j = 64 k + l of the tile's slice: row j / 17,
-// chunk j % 17 (past the tile's 8 rows or the slice's chunks: nothing, zeros).
-__device__ __forceinline__ void half_offsets(int64_t row_bytes, int s, int lane, int (&off)[HalfShape::kLoads]) {
-    const int64_t rest = row_bytes - (int64_t)s * HalfShape::kChunks * 16;
-    const int cs = rest / 16 < HalfShape::kChunks ? (int)(rest / 16) : HalfShape::kChunks;
+// Lane l of load k fetches chunk j = 64 k + l of the tile's slice: row j / C,
+// chunk j % C (past the tile's 8 rows or the slice's chunks: nothing, zeros).
+template <int FMT>
+__device__ __forceinline__ void half_offsets(int64_t row_bytes, int s, int lane, int (&off)[HalfShape<FMT>::kLoads]) {
+    using H = HalfShape<FMT>;
+    const int64_t rest = row_bytes - (int64_t)s * H::kChunks * 16;
+    const int cs = rest / 16 < H::kChunks ? (int)(rest / 16) : H::kChunks;
 #pragma unroll
-    for (int k = 0; k < HalfShape::kLoads; ++k) {
+    for (int k = 0; k < H::kLoads; ++k) {
         const int j = 64 * k + lane;
-        const int r = j / HalfShape::kChunks, c = j % HalfShape::kChunks;
-        off[k] = (r < 8 && c < cs) ? (int)(r * row_bytes) + s * HalfShape::kChunks * 16 + 16 * c : kNoLoad;
+        const int r = j / H::kChunks, c = j % H::kChunks;
+        off[k] = (r < 8 && c < cs) ? (int)(r * row_bytes) + s * H::kChunks * 16 + 16 * c : kNoLoad;
     }
 }
 
+template <int FMT>
 __device__ __forceinline__ void half_issue(const uint8_t* __restrict__ W, int64_t row_bytes, int64_t row_begin,
-                                           int64_t row_end, int ntiles, int t, const int (&off)[HalfShape::kLoads],
+                                           int64_t row_end, int ntiles, int t, const int (&off)[HalfShape<FMT>::kLoads],
                                            uint8_t* lbuf) {
     const bool live = t < ntiles;
     const int64_t r0 = row_begin + (int64_t)(live ? t : 0) * 8;
@@ -949,18 +953,19 @@ __device__ __forceinline__ void half_issue(const uint8_t* __restrict__ W, int64_
     const __amdgpu_buffer_rsrc_t rsrc =
         __builtin_amdgcn_make_buffer_rsrc((void*)(W + r0 * row_bytes), (short)0, num, kBufferRsrcWord3);
 #pragma unroll
-    for (int k = 0; k < HalfShape::kLoads; ++k) load_lds16(rsrc, lbuf + 1024 * k, off[k]);
+    for (int k = 0; k < HalfShape<FMT>::kLoads; ++k) load_lds16(rsrc, lbuf + 1024 * k, off[k]);
 }
 
-template <int NT, int D, class Out>
+template <int FMT, int NT, int D, class Out>
 __device__ __forceinline__ void half_rows(const uint8_t* __restrict__ W, int64_t row_bytes, int cols, int nsl,
                                           const float* __restrict__ x, int64_t row_begin, int64_t row_end, int nw,
                                           Out&& out) {
-    using F = Fmt<QG_FMT_Q8_0>;
+    using F = Fmt<FMT>;
+    using H = HalfShape<FMT>;
     constexpr int TP = pad_pow2(NT);
     constexpr int RB = 2;  // rows per 16-lane group per tile
     constexpr int N = RB * TP;
-    constexpr int L = HalfShape::kLoads;
+    constexpr int L = H::kLoads;
     static_assert(D * L <= 63, "vmcnt holds at most 63 outstanding loads");
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
 
@@ -972,13 +977,14 @@ __device__ __forceinline__ void half_rows(const uint8_t* __restrict__ W, int64_t
     const int s = wave % nsl, rg = wave / nsl, RG = nw / nsl;
     const int k0 = s * kHalfSlice;
     const int ntiles = (int)((row_end - row_begin + 7) / 8);
-    uint8_t* ring = smem + wave * D * HalfShape::kBufBytes;
-    uint8_t* xl = smem + nw * D * HalfShape::kBufBytes + wave * NT * 1024;          // x[NT][256] of the slice
-    float* part = reinterpret_cast<float*>(smem + nw * (D * HalfShape::kBufBytes + NT * 1024));  // [tiles][nsl][4][N]
+    uint8_t* ring = smem + wave * D * H::kBufBytes;
+    uint8_t* xl = smem + nw * D * H::kBufBytes + wave * NT * 1024;          // x[NT][256] of the slice
+    float* part = reinterpret_cast<float*>(smem + nw * (D * H::kBufBytes + NT * 1024));  // [tiles][nsl][4][N]
 
     int off[L];
-    half_offsets(row_bytes, s, lane, off);
+    half_offsets<FMT>(row_bytes, s, lane, off);
     const bool lane_ok = F::lane_valid(li, k0, cols);
+    const bool upper_ok = lane_ok && F::upper_valid(li, k0, cols);
     bool writer;
     const int my_idx = butterfly16_index<N>(li, writer);
 
@@ -992,7 +998,7 @@ __device__ __forceinline__ void half_rows(const uint8_t* __restrict__ W, int64_t
     }
 #pragma unroll
     for (int i = 0; i < D; ++i)
-        half_issue(W, row_bytes, row_begin, row_end, ntiles, rg + i * RG, off, ring + i * HalfShape::kBufBytes);
+        half_issue<FMT>(W, row_bytes, row_begin, row_end, ntiles, rg + i * RG, off, ring + i * H::kBufBytes);
     wait_vmcnt<D * L>();  // x is older than every tile
     float xr[NT][kWeightsPerLane];
     {
@@ -1011,18 +1017,18 @@ __device__ __forceinline__ void half_rows(const uint8_t* __restrict__ W, int64_t
 
     const int mine = ntiles > rg ? (ntiles - rg + RG - 1) / RG : 0;
     for (int i = 0; i < mine; ++i) {
-        uint8_t* buf = ring + (i % D) * HalfShape::kBufBytes;
+        uint8_t* buf = ring + (i % D) * H::kBufBytes;
         const int t = rg + i * RG;
         wait_vmcnt<(D - 1) * L>();
         typename F::Raw raw[RB];
 #pragma unroll
-        for (int r = 0; r < RB; ++r) raw[r] = lds_lane<QG_FMT_Q8_0>(buf + (4 * r + g) * (HalfShape::kChunks * 16), li);
+        for (int r = 0; r < RB; ++r) raw[r] = lds_lane<FMT>(buf + (4 * r + g) * (H::kChunks * 16), li);
         float acc[RB][TP];
 #pragma unroll
         for (int r = 0; r < RB; ++r)
 #pragma unroll
             for (int n = 0; n < TP; ++n) acc[r][n] = 0.0f;
-        accumulate_batch<QG_FMT_Q8_0, NT, RB>(raw, xr, lane_ok, true, acc);
+        accumulate_batch<FMT, NT, RB>(raw, xr, lane_ok, upper_ok, acc);
         float v[N];
 #pragma unroll
         for (int r = 0; r < RB; ++r)
@@ -1031,7 +1037,7 @@ __device__ __forceinline__ void half_rows(const uint8_t* __restrict__ W, int64_t
         butterfly16<N>(v, li);
         if (writer) part[(((size_t)t * nsl + s) * 4 + g) * N + my_idx] = v[0];
         wait_lgkmcnt0();
-        half_issue(W, row_bytes, row_begin, row_end, ntiles, rg + (i + D) * RG, off, buf);
+        half_issue<FMT>(W, row_bytes, row_begin, row_end, ntiles, rg + (i + D) * RG, off, buf);
     }
     wait_vmcnt<0>();
     __syncthreads();
@@ -1679,14 +1685,14 @@ qgemv_dma_kernel(const uint8_t* __restrict__ W, const float* __restrict__ x, flo
                                   [=](int t, int64_t row, float v) { y[t * rows + row] = v; });
 }
 
-template <int T, int D>
+template <int FMT, int T, int D>
 __global__ void __launch_bounds__(64 * kMaxWaves)
 qgemv_half_kernel(const uint8_t* __restrict__ W, const float* __restrict__ x, float* __restrict__ y, int64_t rows,
                   int64_t row_bytes, int cols, int nslices, int rows_per_wg, int nw) {
     const int64_t row_begin = (int64_t)blockIdx.x * rows_per_wg;
     const int64_t row_end = row_begin + rows_per_wg < rows ? row_begin + rows_per_wg : rows;
-    half_rows<T, D>(W, row_bytes, cols, nslices, x, row_begin, row_end, nw,
-                    [=](int t, int64_t row, float v) { y[t * rows + row] = v; });
+    half_rows<FMT, T, D>(W, row_bytes, cols, nslices, x, row_begin, row_end, nw,
+                         [=](int t, int64_t row, float v) { y[t * rows + row] = v; });
 }
 
 template <int FMT, int T, int D>
@@ -1723,12 +1729,12 @@ __global__ void __launch_bounds__(64 * kMaxWaves) qgemv_dma_argmax_kernel(DenseA
     best.merge(work);
 }
 
-template <int T, int D>
+template <int FMT, int T, int D>
 __global__ void __launch_bounds__(64 * kMaxWaves) qgemv_half_argmax_kernel(DenseArgs a, unsigned long long* work) {
     const int64_t row_begin = (int64_t)blockIdx.x * a.rows_per_wg;
     const int64_t row_end = row_begin + a.rows_per_wg < a.rows ? row_begin + a.rows_per_wg : a.rows;
     ArgmaxOut<T> best;
-    half_rows<T, D>(a.W, a.row_bytes, a.cols, a.nslices, a.x, row_begin, row_end, (int)(blockDim.x >> 6), best);
+    half_rows<FMT, T, D>(a.W, a.row_bytes, a.cols, a.nslices, a.x, row_begin, row_end, (int)(blockDim.x >> 6), best);
     best.merge(work);
 }
 
@@ -2208,30 +2214,60 @@ int launch_units(int fmt, int T, const Tile& tile, const DenseArgs& a, void* str
     return (int)hipGetLastError();
 }
 
-template <int T>
+using ArgmaxFn = void (*)(DenseArgs, unsigned long long*);
+
+template <int FMT, int T>
 DmaFn half_entry(int depth) {
     switch (depth) {
-    case 2: return qgemv_half_kernel<T, 2>;
-    case 3: return qgemv_half_kernel<T, 3>;
+    case 2: return qgemv_half_kernel<FMT, T, 2>;
+    case 3: return qgemv_half_kernel<FMT, T, 3>;
     default: return nullptr;
+    }
+}
+
+template <int FMT>
+DmaFn half_for(int T, int depth) {
+    switch (T) {
+    case 1: return half_entry<FMT, 1>(depth);
+    case 2: return half_entry<FMT, 2>(depth);
+    case 3: return half_entry<FMT, 3>(depth);
+    default: return half_entry<FMT, 4>(depth);
+    }
+}
+
+template <int FMT, int T>
+ArgmaxFn half_argmax_entry(int depth) {
+    switch (depth) {
+    case 2: return qgemv_half_argmax_kernel<FMT, T, 2>;
+    case 3: return qgemv_half_argmax_kernel<FMT, T, 3>;
+    default: return nullptr;
+    }
+}
+
+template <int FMT>
+ArgmaxFn half_argmax_for(int T, int depth) {
+    switch (T) {
+    case 1: return half_argmax_entry<FMT, 1>(depth);
+    case 2: return half_argmax_entry<FMT, 2>(depth);
+    case 3: return half_argmax_entry<FMT, 3>(depth);
+    default: return half_argmax_entry<FMT, 4>(depth);
     }
 }
 
 int launch_half(int fmt, int T, const Tile& tile, const DenseArgs& a, void* stream) {
     const int nsl = (int)(a.cols / kHalfSlice);
-    if (fmt != QG_FMT_Q8_0 || tile.rows_per_batch != 4 || a.cols % kHalfSlice || tile.waves_per_wg % nsl)
-        return (int)hipErrorInvalidValue;
-    const DmaFn fn = T == 1 ? half_entry<1>(tile.depth) : T == 2 ? half_entry<2>(tile.depth)
-                   : T == 3 ? half_entry<3>(tile.depth) : half_entry<4>(tile.depth);
+    if (tile.rows_per_batch != 4 || a.cols % kHalfSlice || tile.waves_per_wg % nsl) return (int)hipErrorInvalidValue;
+    const DmaFn fn = fmt == QG_FMT_Q8_0 ? half_for<QG_FMT_Q8_0>(T, tile.depth)
+                   : fmt == QG_FMT_Q4_0 ? half_for<QG_FMT_Q4_0>(T, tile.depth)
+                                        : half_for<QG_FMT_BF16>(T, tile.depth);
     if (!fn) return (int)hipErrorInvalidValue;
     const int64_t nwg = (a.rows + tile.rows_per_wg - 1) / tile.rows_per_wg;
-    hipLaunchKernelGGL(fn, dim3((unsigned)nwg), dim3(64 * tile.waves_per_wg), half_lds_bytes(tile, T, nsl),
+    hipLaunchKernelGGL(fn, dim3((unsigned)nwg), dim3(64 * tile.waves_per_wg), half_lds_bytes(fmt, tile, T, nsl),
                        (hipStream_t)stream, a.W, a.x, a.y, a.rows, a.row_bytes, a.cols, nsl, a.rows_per_wg,
                        tile.waves_per_wg);
     return (int)hipGetLastError();
 }
 
-using ArgmaxFn = void (*)(DenseArgs, unsigned long long*);
 
 template <int FMT, int T>
 ArgmaxFn argmax_dma_entry(int depth, bool xsep) {
@@ -2289,16 +2325,14 @@ int launch_argmax(int fmt, int T, const Tile& tile, const DenseArgs& a_in, void*
     int64_t nwg = 0;
     size_t lds = 0;
     DenseArgs a = a_in;
-    if (tile.kind == 7 && fmt == QG_FMT_Q8_0 && tile.rows_per_batch == 4 && a.cols % kHalfSlice == 0 &&
+    if (tile.kind == 7 && tile.rows_per_batch == 4 && a.cols % kHalfSlice == 0 &&
         tile.waves_per_wg % (a.cols / kHalfSlice) == 0) {
         a.nslices = a.cols / kHalfSlice;  // 256-wide slices
-        const int d = tile.depth;
-        fn = T == 1 ? (d == 2 ? qgemv_half_argmax_kernel<1, 2> : d == 3 ? qgemv_half_argmax_kernel<1, 3> : nullptr)
-           : T == 2 ? (d == 2 ? qgemv_half_argmax_kernel<2, 2> : d == 3 ? qgemv_half_argmax_kernel<2, 3> : nullptr)
-           : T == 3 ? (d == 2 ? qgemv_half_argmax_kernel<3, 2> : d == 3 ? qgemv_half_argmax_kernel<3, 3> : nullptr)
-                    : (d == 2 ? qgemv_half_argmax_kernel<4, 2> : d == 3 ? qgemv_half_argmax_kernel<4, 3> : nullptr);
+        fn = fmt == QG_FMT_Q8_0 ? half_argmax_for<QG_FMT_Q8_0>(T, tile.depth)
+           : fmt == QG_FMT_Q4_0 ? half_argmax_for<QG_FMT_Q4_0>(T, tile.depth)
+                                : half_argmax_for<QG_FMT_BF16>(T, tile.depth);
         nwg = (a.rows + tile.rows_per_wg - 1) / tile.rows_per_wg;
-        lds = half_lds_bytes(tile, T, a.nslices);
+        lds = half_lds_bytes(fmt, tile, T, a.nslices);
     } else if (tile.kind == 1 && tile.mfma == 2 && fmt == QG_FMT_Q8_0 && tile.rows_per_batch == 8 &&
         tile.waves_per_wg == a.nslices) {
         fn = T == 1 ? qgemv_persist_argmax_kernel<1> : T == 2 ? qgemv_persist_argmax_kernel<2>

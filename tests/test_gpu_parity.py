@@ -269,16 +269,17 @@ def test_dma_ring_depths_agree_bitwise(torch, monkeypatch, name):
 
 
 # ------------------------------------- 256-wide k slices, 16 lanes per row (h<depth>)
-def half_tile(cols, rw=40, depth=2, rg=1):
-    return f"q8_0:4,{(cols // 256) * rg},{rw},h{depth}"
+def half_tile(cols, rw=40, depth=2, rg=1, fmt="q8_0"):
+    return f"{fmt}:4,{(cols // 256) * rg},{rw},h{depth}"
 
 
 @pytest.mark.parametrize("name,rw,depth", [("c2a_q8_0_10240x2560", 40, 2), ("c2a_q8_0_10240x2560", 40, 3),
-                                           ("c1_q8_0_2560x2560", 16, 2)])
+                                           ("c1_q8_0_2560x2560", 16, 2), ("c3_q4_0_8192x2560", 32, 2),
+                                           ("c3_bf16_8192x2560", 32, 2), ("c3_q4_0_8192x2560", 40, 3)])
 def test_half_slice_config_full(torch, orc, monkeypatch, name, rw, depth):
     """The half-slice kernel on the workloads: parity at every T, a token's bits equal across T."""
     c = I.dense_case(name)
-    monkeypatch.setenv("QGEMV_TILE", half_tile(c["cols"], rw, depth))
+    monkeypatch.setenv("QGEMV_TILE", half_tile(c["cols"], rw, depth, fmt=NAMES[c["fmt"]]))
     st, t = _lib.qg_query_tile(c["fmt"], c["rows"], c["cols"], 4)
     assert st == 0 and t[6] == 7 and t[7] == depth, (st, t)
     check_dense(torch, orc, c["fmt"], c["rows"], c["cols"], c["W"], c["x"], f"half {name} rw={rw} d={depth}")
@@ -287,16 +288,17 @@ def test_half_slice_config_full(torch, orc, monkeypatch, name, rw, depth):
 def test_half_slice_tiny_and_dyadic(torch, orc, monkeypatch):
     """Ragged rows (partial tiles, fewer tiles than the ring), one to twelve slices,
     two row groups; dyadic inputs bitwise."""
-    for rows in TINY_ROWS:
-        for cols in (256, 512, 768, 1280, 2304, 3072):
-            for rw, depth, rg in ((8, 2, 1), (24, 3, 1), (16, 2, 2)):
-                monkeypatch.setenv("QGEMV_TILE", half_tile(cols, rw, depth, rg))
-                if _lib.qg_query_tile(Q8, rows, cols, 4)[0]:
-                    continue  # more than twelve waves
-                rng = np.random.default_rng(rows * 1000 + cols + rw)
-                W = I.weights(rng, Q8, rows, cols)
-                x = I.activations(rng, cols)
-                check_dense(torch, orc, Q8, rows, cols, W, x, f"half tiny rw={rw} d={depth} rg={rg}")
+    for fmt in (Q8, Q4, BF):
+        for rows in TINY_ROWS:
+            for cols in (256, 512, 768, 1280, 2304, 3072):
+                for rw, depth, rg in ((8, 2, 1), (24, 3, 1), (16, 2, 2)):
+                    monkeypatch.setenv("QGEMV_TILE", half_tile(cols, rw, depth, rg, NAMES[fmt]))
+                    if _lib.qg_query_tile(fmt, rows, cols, 4)[0]:
+                        continue  # more than twelve waves, or past the LDS
+                    rng = np.random.default_rng(rows * 1000 + cols + rw + fmt)
+                    W = I.weights(rng, fmt, rows, cols)
+                    x = I.activations(rng, cols)
+                    check_dense(torch, orc, fmt, rows, cols, W, x, f"half tiny rw={rw} d={depth} rg={rg}")
     rng = np.random.default_rng(97)
     rows, cols = 1000, 2816
     W = dyadic_weights(rng, Q8, rows, cols)
