@@ -68,7 +68,7 @@ def time_calls(torch, fmt, ring, x_dev, rows, T, calls, stream, y_dev):
 def kernel_name(tile, T):
     """Device symbol of the kernel a call with ``tile`` launches (Q8_0)."""
     if tile["kind"] == 7:
-        return f"qgemv_half_kernel<{T}, {tile['depth']}>"
+        return f"qgemv_half_kernel<0, {T}, {tile['depth']}>"
     if tile["kind"] in (2, 3):
         return f"qgemv_dma_kernel<0, {T}, {2 * tile['rows_per_batch']}, {tile['depth']}, {str(tile['kind'] == 3).lower()}>"
     if tile["kind"] == 1 and tile["mfma"] == 2:

@@ -30,7 +30,7 @@ def test_kernel_names_follow_the_tile():
     assert bench.kernel_name(dict(base, kind=1, depth=0, rows_per_batch=8, mfma=2), 4) == "qgemv_mfma_persist_kernel<4>"
     assert bench.kernel_name(dict(base, kind=4, depth=3), 2) == "qgemv_units_kernel<0, 2, 3>"
     assert bench.kernel_name(dict(base, kind=0, depth=0, rows_per_wg=8), 1) == "qgemv_dense_kernel<0, 1, 4, true>"
-    assert bench.kernel_name(dict(base, kind=7, waves_per_wg=10, depth=2), 4) == "qgemv_half_kernel<4, 2>"
+    assert bench.kernel_name(dict(base, kind=7, waves_per_wg=10, depth=2), 4) == "qgemv_half_kernel<0, 4, 2>"
 
 
 def _write_pmc(dirpath, counter, rows):
