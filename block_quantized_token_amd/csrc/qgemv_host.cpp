@@ -426,7 +426,7 @@ int run_rows(int fmt, int64_t rows, int64_t cols, int64_t n_sel, const int32_t* 
     tile.rows_per_batch = 4;
     tile.waves_per_wg = (int)nsl;
     int64_t rw = (n_sel / 256 + 7) / 8 * 8;
-    tile.rows_per_wg = (int)(rw < 16 ? 16 : rw > 64 ? 64 : rw);  // one id per lane: at most 64
+    tile.rows_per_wg = (int)(rw < 16 ? 16 : rw > 128 ? 128 : rw);  // two ids per lane: at most 128
     while (gather_lds_bytes(fmt, tile, T, (int)nsl) > kMaxLds && tile.rows_per_wg > 16) tile.rows_per_wg /= 2;
     if (gather_lds_bytes(fmt, tile, T, (int)nsl) > kMaxLds)
         return fail(QG_EUNSUPPORTED, "row subset: the LDS rings do not fit %lld slices of this format", (long long)nsl);

@@ -1059,9 +1059,9 @@ __device__ __forceinline__ void half_rows(const uint8_t* __restrict__ W, int64_t
 // LM head in the mlxcel drafter-cost issue: the drafter reads only the rows of the
 // tokens it may propose).  As dma_rows (x in registers, loaded with the ids before
 // any load to LDS, so the ring needs no slots for it), but a tile's 8 rows
-// are ids[...] of the workgroup's range: every wave first loads those ids (one
-// per lane, at most 64 per workgroup), and each load lane takes its row's id
-// from the lane that holds it.  The descriptor spans all of W (< 2 GB, so every
+// are ids[...] of the workgroup's range: every wave first loads those ids (two
+// per lane, at most 128 per workgroup: id j sits in lane j % 64 of register
+// j / 64), and each load lane takes its row's id from the lane that holds it.  The descriptor spans all of W (< 2 GB, so every
 // byte offset fits the 32-bit offset); an id outside [0, rows) loads nothing and
 // its outputs are NaN.
 template <int FMT, int NT, int D, class Out>
@@ -1085,15 +1085,15 @@ __device__ __forceinline__ void gather_rows(const uint8_t* __restrict__ W, int64
     const int g = lane >> 5, li = lane & 31;
     const int s = wave % nsl, rg = wave / nsl, RG = nw / nsl;
     const int k0 = s * kSlice;
-    const int nsel = (int)(sel_end - sel_begin);  // <= 64
+    const int nsel = (int)(sel_end - sel_begin);  // <= 128
     const int ntiles = (nsel + ST - 1) / ST;
     uint8_t* ring = smem + wave * D * S::kBufBytes;
     float* part = reinterpret_cast<float*>(smem + nw * D * S::kBufBytes);  // [tiles][nsl][2][N]
 
-    // the workgroup's row ids (one per lane) and the slice of x, into registers,
+    // the workgroup's row ids (two per lane) and the slice of x, into registers,
     // all complete before the first load to LDS
-    const int my_id = lane < nsel ? ids[sel_begin + lane] : -1;
-    const bool my_ok = my_id >= 0 && my_id < rows;
+    const int my_id0 = lane < nsel ? ids[sel_begin + lane] : -1;
+    const int my_id1 = 64 + lane < nsel ? ids[sel_begin + 64 + lane] : -1;
     const int64_t rest = row_bytes - (int64_t)s * S::kChunks * 16;
     const int cs = rest / 16 < S::kChunks ? (int)(rest / 16) : S::kChunks;
     const __amdgpu_buffer_rsrc_t wr =
@@ -1103,10 +1103,9 @@ __device__ __forceinline__ void gather_rows(const uint8_t* __restrict__ W, int64
         for (int k = 0; k < L; ++k) {
             const int j = 64 * k + lane;
             const int r = j / S::kChunks, c = j % S::kChunks;
-            const int src = t * ST + r;  // lane holding this row's id
-            const int id = __shfl(my_id, src & 63, 64);
-            const int ok = __shfl((int)my_ok, src & 63, 64);
-            const bool live = t < ntiles && r < ST && src < nsel && c < cs && ok;
+            const int src = t * ST + r;  // the row's place in the range; tile t < 8 reads ids 0..63
+            const int id = __shfl(t < 64 / ST ? my_id0 : my_id1, src & 63, 64);
+            const bool live = t < ntiles && r < ST && src < nsel && c < cs && id >= 0 && id < rows;
             load_lds16(wr, lbuf + 1024 * k, live ? (int)(id * row_bytes) + s * S::kChunks * 16 + 16 * c : kNoLoad);
         }
     };

@@ -515,6 +515,22 @@ def test_rows_subset_shapes(torch, orc, monkeypatch, fmt):
                 rows_check(torch, orc, monkeypatch, fmt, rows, cols, W, x[:T], ids, f"{rows}x{cols} n={n_sel} T={T}")
 
 
+@pytest.mark.parametrize("fmt", [Q8, Q4, BF])
+def test_rows_subset_wide_workgroups(torch, orc, monkeypatch, fmt):
+    """Subsets long enough for 80 and 128 ids per workgroup (ids 64.. held in a
+    second register), each with a short last workgroup."""
+    rng = np.random.default_rng(50 + fmt)
+    rows, cols = 333, 2560
+    W = I.weights(rng, fmt, rows, cols)
+    x = I.activations(rng, cols)
+    for n_sel in (20001, 32768 + 77):
+        ids = rng.integers(0, rows, n_sel)
+        ids[rng.choice(n_sel, 9, replace=False)] = -5  # a few bad ids spread over the range
+        for T in (1, 4):
+            say(f"[rows] fmt={NAMES[fmt]} {rows}x{cols} n_sel={n_sel} T={T}")
+            rows_check(torch, orc, monkeypatch, fmt, rows, cols, W, x[:T], ids, f"{rows}x{cols} n={n_sel} T={T}")
+
+
 def test_rows_subset_bad_ids(torch, orc, monkeypatch):
     rng = np.random.default_rng(3)
     rows, cols = 50, 512
