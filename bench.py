@@ -12,7 +12,7 @@ bytes / time per call, 1 GB = 1e9 B, weight bytes counted once per call
 whatever T is.  ``value`` = all weight bytes of the K timed steps / their wall
 time on the launch stream (hipEvents), with every input already in HBM.
 
-Prints ONE JSON line (rank 0).  ``--gpus`` above 1 is refused: this build runs
+Prints ONE JSON line (rank 0).  ``--gpus`` above 1 is refused: the benchmark runs
 on one GPU.
 """
 from __future__ import annotations
@@ -475,8 +475,8 @@ def main():
         return
 
     if args.gpus != 1:
-        print(f"bench.py: --gpus {args.gpus} refused: this build measures one GPU only "
-              "(the mat-vec shards by rows; see DESIGN.md)", file=sys.stderr)
+        print(f"bench.py: --gpus {args.gpus} refused: only one GPU is measured "
+              "(the mat-vec would shard by rows, one slab of W per GPU, with no collective)", file=sys.stderr)
         sys.exit(2)
 
     import torch

@@ -6,7 +6,7 @@
 // Track 1 report, item 3 "Q4_0 / Q5_0 draft weights"), and dense projections
 // are re-encoded to Q8_0 ("Where the time goes", meld-turbo-performance).
 // Computed here, per block of 32 values, with every decision in fp32 one
-// operation at a time (the build has no FMA contraction):
+// operation at a time (compiled with FMA contraction off):
 //   Q8_0         d = max|v| / 127; code = round(v * (1/d)), halves away from 0.
 //   Q4_0 absmax  the first element of largest magnitude, with its sign, is
 //                mapped to code 0: d = that value / -8;
