@@ -698,10 +698,11 @@ int qg_query_tile(int fmt, int64_t rows, int64_t cols, int T, int out_tile[QG_TI
     Tile t;
     int st = pick_tile(fmt, rows, cols, T, &t);
     if (st) return st;
-    out_tile[0] = t.lanes_per_row;
+    const bool half = t.kind == 7;  // 256-wide k slices, 16 lanes per row
+    out_tile[0] = half ? 16 : t.lanes_per_row;
     out_tile[1] = t.rows_per_batch;
     out_tile[2] = t.waves_per_wg;
-    out_tile[3] = t.k_slice;
+    out_tile[3] = half ? 256 : t.k_slice;
     out_tile[4] = t.rows_per_wg;
     out_tile[5] = t.mfma;
     out_tile[6] = t.kind;

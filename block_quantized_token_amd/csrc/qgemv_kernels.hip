@@ -1036,6 +1036,8 @@ __device__ __forceinline__ void half_rows(const uint8_t* __restrict__ W, int64_t
             for (int n = 0; n < TP; ++n) v[r * TP + n] = acc[r][n];
         butterfly16<N>(v, li);
         if (writer) part[(((size_t)t * nsl + s) * 4 + g) * N + my_idx] = v[0];
+        // the slot is refilled once its reads have returned; refilling it before the
+        // math (as soon as the bytes are in registers) measured slower at T >= 2
         wait_lgkmcnt0();
         half_issue<FMT>(W, row_bytes, row_begin, row_end, ntiles, rg + (i + D) * RG, off, buf);
     }

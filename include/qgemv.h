@@ -50,15 +50,21 @@
  * Environment: QGEMV_TILE="fmt:rb,nw,rw[,k][;fmt:...]" overrides the tile for a
  * format (fmt = q8_0 | q4_0 | bf16): rb rows per lane group per batch or tile
  * (1, 2, 4, 8 or 16), nw waves per workgroup (1..12), rw rows per workgroup (a
- * multiple of 2*rb), k the kernel kind: d (each lane loads its own bytes), s
- * (rows streamed through LDS via registers; needs rows of a multiple of 16
- * bytes), l<D> (streamed by direct-to-LDS loads, D = 2, 3, 4 or 6 tiles in
- * flight per wave; rb 4; L<D> the same with x staged apart), u<D> (as l, waves
- * take equal shares of (slice, tile) units; any nw), m (as s, contracted on the
- * matrix cores; Q8_0 with rb 8 only) or p (m in persistent form: one workgroup
- * per CU, nw = the k slices, rw = the chunk of rows whose partial sums are
- * buffered).  A malformed or out-of-set value makes every call of that format
- * return QG_EINVAL.
+ * multiple of 2*rb), k the kernel kind:
+ *   d     each lane loads its own bytes;
+ *   s     rows streamed through LDS via registers (rows of a multiple of 16 bytes);
+ *   l<D>  streamed by direct-to-LDS loads, D = 2, 3, 4 or 6 tiles in flight per
+ *         wave; rb 4;
+ *   L<D>  as l<D>, with x staged apart;
+ *   u<D>  as l<D>, waves take equal shares of (slice, tile) units; any nw;
+ *   h<D>  direct-to-LDS loads on 256-wide k slices with 16 lanes per row, D = 2
+ *         or 3 tiles in flight per wave; rb 4, cols a multiple of 256, nw a
+ *         multiple of cols/256 (at most 12 slices); all three formats;
+ *   m     as s, contracted on the matrix cores; Q8_0 with rb 8 only;
+ *   p     m in persistent form: one workgroup per CU, nw = the k slices, rw =
+ *         the chunk of rows whose partial sums are buffered.
+ * A malformed or out-of-set value makes every call of that format return
+ * QG_EINVAL.
  */
 #ifndef QGEMV_H
 #define QGEMV_H
@@ -217,8 +223,8 @@ int qg_unpack_q4_0(int64_t rows, int64_t cols, const void* in, uint16_t* d_bits,
  * (kind 0: direct loads, 1: streamed through LDS via registers, 2 / 3: streamed
  * by direct-to-LDS loads with `depth` tiles in flight per wave (3: x staged
  * apart), 4: unit-balanced direct-to-LDS, 7: direct-to-LDS on 256-wide k slices
- * with 16 lanes per row (Q8_0); mfma 1: matrix-core contraction, 2: its
- * persistent form). */
+ * with 16 lanes per row (any format; k_slice 256, lanes_per_row 16); mfma 1:
+ * matrix-core contraction, 2: its persistent form). */
 int qg_query_tile(int fmt, int64_t rows, int64_t cols, int T, int out_tile[QG_TILE_FIELDS]);
 
 /* Static description of a status code (never NULL). */

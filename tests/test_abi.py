@@ -165,13 +165,14 @@ def test_argmax_argument_errors(lib, args, status):
 def test_tile_query_and_override(lib, monkeypatch):
     monkeypatch.delenv("QGEMV_TILE", raising=False)
     t = ops.query_tile("q8_0", 10240, 2560, 1)
-    assert t["lanes_per_row"] == 32 and t["k_slice"] == 512 and t["waves_per_wg"] % 5 == 0  # 5 k slices
+    # the 256-wide k slices of the half-slice kind: 16 lanes per row, one wave per slice
+    assert (t["kind"], t["lanes_per_row"], t["k_slice"], t["waves_per_wg"]) == (7, 16, 256, 10)
     # the k split must not depend on T (bit-identical tokens across T): waves
     # that each reduce one slice (streamed kinds; direct with waves >= slices)
     # or the same number of slice-looping waves
     def k_split(t, cols):
-        nsl = -(-cols // 512)
-        return nsl if t["kind"] == 1 else min(t["waves_per_wg"], nsl)
+        nsl = -(-cols // t["k_slice"])
+        return (t["k_slice"], nsl if t["kind"] in (1, 7) else min(t["waves_per_wg"], nsl))
     for fmt in ("q8_0", "q4_0", "bf16"):
         for rows, cols in ((10240, 2560), (2560, 6144), (248320, 5120), (8192, 2560), (7, 65536)):
             # the Q8_0 LM head runs the VALU kernel at T <= 2 and the matrix cores at T >= 3
@@ -202,12 +203,84 @@ def test_tile_query_and_override(lib, monkeypatch):
         assert _lib.qgemv_q8_0(10240, 2560, 4, W0, X0, Y0) == _lib.QG_EINVAL
 
 
+def test_header_names_every_tile_kind(lib, monkeypatch):
+    """Every kind letter QGEMV_TILE accepts is documented in the header, and every
+    documented letter is accepted for some tile."""
+    text = open(HEADER).read()
+    para = text[text.index("QGEMV_TILE="):text.index("QG_EINVAL.\n */")]
+    documented = set(re.findall(r"^ \*   ([a-zA-Z])(?:<D>)?\s", para, flags=re.M))
+    # (kind, spec suffix, shape) that the compiled set accepts
+    probes = {"d": ("d", 10240, 2560, "2,5,8"), "s": ("s", 10240, 2560, "4,5,16"),
+              "l": ("l2", 10240, 2560, "4,5,40"), "L": ("L2", 10240, 2560, "4,5,40"),
+              "u": ("u2", 10240, 2560, "4,4,40"), "h": ("h2", 10240, 2560, "4,10,40"),
+              "m": ("m", 10240, 2560, "8,5,32"), "p": ("p", 248320, 5120, "8,10,64")}
+    accepted = set()
+    for letter in "abcdefghijklmnopqrstuvwxyzABCDEFGHIJKLMNOPQRSTUVWXYZ":
+        suffix, rows, cols, head = probes.get(letter, (letter, 10240, 2560, "4,10,40"))
+        for spec in (f"{head},{suffix}", f"{head},{letter}2", f"{head},{letter}"):
+            monkeypatch.setenv("QGEMV_TILE", "q8_0:" + spec)
+            st, _ = _lib.qg_query_tile(0, rows, cols, 1)
+            if st == _lib.QG_OK:
+                accepted.add(letter)
+                break
+    monkeypatch.delenv("QGEMV_TILE")
+    assert accepted == documented == set(probes), (accepted, documented)
+
+
 def test_binding_refuses_cpu_tensors(lib):
     torch = pytest.importorskip("torch")
     W = torch.zeros(34 * 4, dtype=torch.uint8)
     x = torch.zeros(1, 32)
-    with pytest.raises(ValueError):
+    with pytest.raises(ValueError, match="GPU tensor"):
         ops.gemv("q8_0", W, x, rows=4)
+
+
+def _binding_cases(torch):
+    """(call, message) pairs: each call passes one buffer of the wrong dtype, rank or
+    size, which the binding must refuse before any kernel could run past its end."""
+    f32, i32, i64 = torch.float32, torch.int32, torch.int64
+    rows, cols, E = 8, 256, 4
+    W = torch.zeros(rows * cols // 32 * 34, dtype=torch.uint8)
+    WE = torch.zeros(E * rows * cols // 32 * 18, dtype=torch.uint8)
+    x = torch.zeros(2, cols)
+    ids1 = torch.zeros(5, dtype=i32)
+    ids2 = torch.zeros(2, 3, dtype=i32)
+    h = torch.zeros(2, 3, cols)
+    return [
+        (lambda: ops.gemv("q8_0", W, x.half(), rows), "x must be fp32"),
+        (lambda: ops.gemv("q8_0", W, x[0], rows), "x must be fp32"),
+        (lambda: ops.gemv("q8_0", W[:-1], x, rows), "W holds"),
+        (lambda: ops.gemv("q8_0", W, x, rows, out=torch.zeros(2, rows, dtype=torch.float16)), "out must be"),
+        (lambda: ops.gemv("q8_0", W, x, rows, out=torch.zeros(2 * rows - 1)), "out holds"),
+        (lambda: ops.gemv_rows("q8_0", W, x.bfloat16(), rows, ids1), "x must be fp32"),
+        (lambda: ops.gemv_rows("q8_0", W, x, rows, ids1.long()), "ids must be int32"),
+        (lambda: ops.gemv_rows("q8_0", W, x, rows, ids1, out=torch.zeros(2 * 5 - 1)), "out holds"),
+        (lambda: ops.gemv_rows("q8_0", W, x, rows, ids1, out=torch.zeros(2, 5, dtype=i32)), "out must be"),
+        (lambda: ops.argmax("q8_0", W, x.double(), rows), "x must be fp32"),
+        (lambda: ops.argmax("q8_0", W, x, rows, work=torch.zeros(2, dtype=i32)), "work must be"),
+        (lambda: ops.argmax("q8_0", W, x, rows, work=torch.zeros(1, dtype=i64)), "work holds"),
+        (lambda: ops.grouped_experts("q4_0", WE, x.half(), ids2, E, rows), "x must be fp32"),
+        (lambda: ops.grouped_experts("q4_0", WE, x.reshape(2, 1, cols), ids2, E, rows), "x must be fp32"),
+        (lambda: ops.grouped_experts("q4_0", WE[:-1], x, ids2, E, rows), "W holds"),
+        (lambda: ops.grouped_experts("q4_0", WE, x, ids2, E, rows, out=torch.zeros(2 * 3 * rows - 1)), "out holds"),
+        (lambda: ops.grouped_experts("q4_0", WE, x, ids2, E, rows, out=torch.zeros(2, 3, rows, dtype=f32).half()),
+         "out must be"),
+        (lambda: ops.grouped_experts("q4_0", WE, x, ids2[:1], E, rows), "disagree on T"),
+        (lambda: ops.experts_gate_up("q4_0", WE, WE, x.half(), ids2, E, rows), "x must be fp32"),
+        (lambda: ops.experts_gate_up("q4_0", WE, WE[:-1], x, ids2, E, rows), "W holds"),
+        (lambda: ops.experts_gate_up("q4_0", WE, WE, x, ids2.long(), E, rows), "ids must be int32"),
+        (lambda: ops.experts_down("q4_0", WE, h.half(), ids2, E, rows), "h must be fp32"),
+        (lambda: ops.experts_down("q4_0", WE[:-1], h, ids2, E, rows), "W holds"),
+        (lambda: ops.quantize("q8_0", x.half()), "src must be fp32"),
+        (lambda: ops.quantize("q8_0", x, out=torch.zeros(10, dtype=torch.uint8)), "out holds"),
+    ]
+
+
+def test_binding_refuses_wrong_dtypes_ranks_and_sizes(lib):
+    torch = pytest.importorskip("torch")
+    for call, msg in _binding_cases(torch):
+        with pytest.raises(ValueError, match=msg):
+            call()
 
 
 @pytest.mark.parametrize("args, status", [
