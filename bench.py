@@ -343,58 +343,173 @@ def read_probe(torch, stream, nbytes):
     return res
 
 
+def host_info(torch):
+    """What the numbers were measured on: host CPU, ROCm, torch and the GPU."""
+    info = {"cpu_model": None, "logical_cpus": os.cpu_count()}
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                info["cpu_model"] = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    try:
+        info["rocm_version"] = open(os.path.join(os.environ.get("ROCM_PATH", "/opt/rocm"), ".info", "version")).read().strip()
+    except OSError:
+        info["rocm_version"] = None
+    info["torch"] = torch.__version__
+    info["hip_runtime"] = getattr(torch.version, "hip", None)
+    props = torch.cuda.get_device_properties(0)
+    info["gpu"] = props.name
+    info["gpu_arch"] = getattr(props, "gcnArchName", None)
+    info["compute_units"] = props.multi_processor_count
+    return info
+
+
+def _numeric_leaves(obj, path=""):
+    if isinstance(obj, dict):
+        for k, v in obj.items():
+            yield from _numeric_leaves(v, f"{path}.{k}" if path else str(k))
+    elif isinstance(obj, list):
+        for i, v in enumerate(obj):
+            yield from _numeric_leaves(v, f"{path}[{i}]")
+    elif isinstance(obj, (int, float)) and not isinstance(obj, bool):
+        yield path, obj
+
+
+CLOCK_CMD = ["amd-smi", "metric", "-g", "0", "--clock", "--power", "--json"]
+
+
+def gpu_clocks():
+    """One amd-smi sample of GPU 0's clocks and power (a child process; the values
+    are what the tool reports, MHz and W), or the reason there is none."""
+    import subprocess
+    try:
+        r = subprocess.run(CLOCK_CMD, capture_output=True, text=True, timeout=20)
+    except (OSError, subprocess.SubprocessError) as e:
+        return {"error": f"amd-smi: {type(e).__name__}: {str(e)[:200]}"}
+    return _parse_clocks(r.stdout)
+
+
+def _parse_clocks(text):
+    try:
+        keep = clock_fields(json.loads(text))
+    except ValueError as e:
+        return {"error": f"amd-smi output: {str(e)[:200]}"}
+    return keep if keep else {"raw": text[:400]}
+
+
+def clocks_under_load(torch, batch, min_s):
+    """Run ``batch()`` (a few calls of the workload) back to back for at least
+    ``min_s`` seconds while one amd-smi sample is taken, so the sample shows the
+    clocks the calls run at (an idle GPU drops to its idle clock within a fraction
+    of a second); returns the sample."""
+    import subprocess
+    try:
+        p = subprocess.Popen(CLOCK_CMD, stdout=subprocess.PIPE, stderr=subprocess.DEVNULL, text=True)
+    except OSError as e:
+        p, res = None, {"error": f"amd-smi: {type(e).__name__}: {str(e)[:200]}"}
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < min_s or (p is not None and p.poll() is None):
+        batch()
+        torch.cuda.synchronize()
+        if p is not None and time.perf_counter() - t0 > 30:
+            p.kill()
+    if p is not None:
+        out, _ = p.communicate()
+        res = _parse_clocks(out)
+    return res
+
+
+def clock_fields(data):
+    """The gfx / memory clock and power values of an amd-smi metric JSON document."""
+    keep = {}
+    for path, v in _numeric_leaves(data):
+        p = path.lower()
+        if ("gfx" in p or "mem" in p or "power" in p) and (".clk." in p or "power" in p) and "value" in p:
+            keep[path] = v
+    return dict(list(keep.items())[:24])
+
+
+def _median_call(fn, repeats):
+    runs = []
+    for _ in range(repeats):
+        t0 = time.perf_counter()
+        fn()
+        runs.append(time.perf_counter() - t0)
+    runs.sort()
+    return runs[len(runs) // 2]
+
+
 def cpu_baseline(case, budget_s: float):
     """The oracle, untuned, on the host cores: whole steps (T = 1..4) of the same
-    workload repeated until about ``budget_s`` seconds have passed."""
+    workload repeated until about ``budget_s`` seconds have passed; the value is
+    their total rate, with the median of the step times beside it."""
     import oracle
     o = oracle.get()
     fmt, rows, cols, W, x = case["fmt"], case["rows"], case["cols"], case["W"], case["x"]
     nbytes = o.packed_bytes(fmt, rows, cols)
-    steps, t0 = 0, time.perf_counter()
+    steps, t0, step_s = 0, time.perf_counter(), []
     while True:
+        ts = time.perf_counter()
         for T in (1, 2, 3, 4):
             o.gemv(fmt, rows, cols, W, x[:T])
+        step_s.append(time.perf_counter() - ts)
         steps += 1
         el = time.perf_counter() - t0
-        if el >= budget_s:
+        if el >= budget_s and steps >= 3:
             break
+    step_s.sort()
+    med = step_s[len(step_s) // 2]
     return dict(value=round(steps * 4 * nbytes / el / 1e9, 3), unit="GB/s", cores=o.num_threads(), kind="oracle",
                 sample=f"{steps} full steps (T=1,2,3,4) of Q8_0 10240x2560 in {el:.1f} s",
-                us_per_call=round(el / (steps * 4) * 1e6, 1))
+                us_per_call=round(el / (steps * 4) * 1e6, 1),
+                median_step_gbs=round(4 * nbytes / med / 1e9, 3), median_step_s=round(med, 4))
 
 
-def cpu_baseline_per_workload(sample_rows: int = 2048):
-    """The oracle on every other workload, at T = 1..4: a sample of rows (all of them
-    when fewer; x and the expert table as in the workload), timed once per T and
-    scaled to the workload's rows.  Seeded inputs of each workload's shape."""
+def cpu_baseline_per_workload():
+    """The oracle on every other workload at full size, at T = 1..4: the median of 3
+    runs (one for the 1.35 GB LM head) on all host threads; and on one thread for
+    the dense configs C1-C3 at T = 1 and 4 (median of 3).  Seeded inputs of each
+    workload's shape."""
     import oracle
     o = oracle.get()
+    threads = o.num_threads()
     out = {}
-    for name in ("c1_q8_0_2560x2560", "c2b_q8_0_2560x6144", "c3_q4_0_8192x2560", "c3_bf16_8192x2560",
-                 "c4_q8_0_248320x5120"):
-        fmt, rows, cols, _ = I.CONFIGS[name]
-        n = min(rows, sample_rows)
-        rng = I.rng_for(0)
-        W = I.weights(rng, fmt, n, cols)
-        x = I.activations(rng, cols)
+    single = {}
+    for name in ("c1_q8_0_2560x2560", "c2a_q8_0_10240x2560", "c2b_q8_0_2560x6144", "c3_q4_0_8192x2560",
+                 "c3_bf16_8192x2560", "c4_q8_0_248320x5120"):
+        c = I.dense_case(name)
+        fmt, rows, cols, W, x = c["fmt"], c["rows"], c["cols"], c["W"], c["x"]
         nb = o.packed_bytes(fmt, rows, cols)
+        reps = 1 if rows * cols > (1 << 28) else 3
         res = {}
         for T in (1, 2, 3, 4):
-            t0 = time.perf_counter()
-            o.gemv(fmt, n, cols, W, x[:T])
-            us = (time.perf_counter() - t0) * 1e6 * rows / n
-            res[str(T)] = dict(us_per_call=round(us, 1), gbs=round(nb / us / 1e3, 3))
-        out[name] = dict(sample=f"{n} of {rows} rows, scaled", per_T=res)
+            s_ = _median_call(lambda T=T: o.gemv(fmt, rows, cols, W, x[:T]), reps)
+            res[str(T)] = dict(us_per_call=round(s_ * 1e6, 1), gbs=round(nb / s_ / 1e9, 3))
+        if name != "c2a_q8_0_10240x2560":
+            out[name] = dict(sample=f"all {rows} rows, median of {reps}", threads=threads, per_T=res)
+        if name != "c4_q8_0_248320x5120":
+            o.set_num_threads(1)
+            try:
+                r1 = {}
+                for T in (1, 4):
+                    s_ = _median_call(lambda T=T: o.gemv(fmt, rows, cols, W, x[:T]), 3)
+                    r1[str(T)] = dict(us_per_call=round(s_ * 1e6, 1), gbs=round(nb / s_ / 1e9, 4))
+            finally:
+                o.set_num_threads(threads)
+            single[name] = r1
+        del c, W
     g = I.grouped_case()
     res = {}
     for T in (1, 2, 3, 4):
         ids = g["ids"][:T]
-        t0 = time.perf_counter()
-        o.grouped(g["fmt"], g["n_experts"], g["rows"], g["cols"], ids, g["W"], g["x"][:T])
-        us = (time.perf_counter() - t0) * 1e6
+        s_ = _median_call(lambda T=T, ids=ids: o.grouped(g["fmt"], g["n_experts"], g["rows"], g["cols"], ids, g["W"],
+                                                          g["x"][:T]), 3)
         nb = T * g["topk"] * o.packed_bytes(g["fmt"], g["rows"], g["cols"])
-        res[str(T)] = dict(us_per_call=round(us, 1), gbs=round(nb / us / 1e3, 3))
-    out["c5_q4_0_experts"] = dict(sample="every slot", per_T=res)
+        res[str(T)] = dict(us_per_call=round(s_ * 1e6, 1), gbs=round(nb / s_ / 1e9, 3))
+    out["c5_q4_0_experts"] = dict(sample="every slot, median of 3", threads=threads, per_T=res)
+    out["single_thread"] = dict(sample="all rows, T = 1 and 4, median of 3, one host thread", per_workload=single)
     return out
 
 
@@ -496,7 +611,14 @@ def main():
     Ts = (1, 2, 3, 4)
     log(f"bench: {WORKLOAD} {nbytes} B/call, ring {len(ring)} copies, steps {args.steps}, warmup {args.warmup}")
 
-    # warmup: every T, walking the ring
+    # settle: the same calls back to back for at least 0.2 s (and while one clock
+    # sample is taken), so the timed region starts at the clocks sustained load
+    # runs at (a fresh or idle GPU ramps its clocks up over the first
+    # milliseconds); then the W warmup steps, then the timed steps
+    def batch():
+        for T in Ts:
+            time_calls(torch, fmt, ring, x_dev[:T], rows, T, 25, stream, y_dev)
+    clocks_before = clocks_under_load(torch, batch, 0.2)
     for T in Ts:
         time_calls(torch, fmt, ring, x_dev[:T], rows, T, args.warmup, stream, y_dev)
     torch.cuda.synchronize()
@@ -507,6 +629,7 @@ def main():
     evs = {T: time_calls(torch, fmt, ring, x_dev[:T], rows, T, args.steps, stream, y_dev) for T in Ts}
     torch.cuda.synchronize()
     wall_s = time.perf_counter() - t_wall
+    clocks_after = clocks_under_load(torch, batch, 0.05)  # the same calls keep the GPU busy while sampled
     ms = {T: evs[T][0].elapsed_time(evs[T][1]) for T in Ts}
     total_ms = sum(ms.values())
     value = args.steps * len(Ts) * nbytes / (total_ms * 1e-3) / 1e9
@@ -578,6 +701,8 @@ def main():
                      "kernel": dom_kernel, "T": dom, "us_per_launch": round(dom_us, 3),
                      "bytes_per_launch": nbytes},
         "cpu_baseline": cpu,
+        "host": host_info(torch),
+        "gpu_clocks": {"before_timed_region": clocks_before, "after_timed_region": clocks_after},
         "detail": detail,
         "wall_s_timed_region": round(wall_s, 3),
     }

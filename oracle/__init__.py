@@ -60,6 +60,8 @@ class Oracle:
         L.oracle_grouped.restype = i32
         L.oracle_grouped.argtypes = [i32, i64, i64, i64, i32, i32, vp, vp, vp, vp, vp]
         L.oracle_num_threads.restype = i32
+        L.oracle_set_num_threads.restype = None
+        L.oracle_set_num_threads.argtypes = [i32]
         L.oracle_grouped_per_slot.restype = i32
         L.oracle_grouped_per_slot.argtypes = [i32, i64, i64, i64, i32, i32, vp, vp, vp, vp, vp]
         L.oracle_f32_to_fp16_array.restype = None
@@ -85,6 +87,10 @@ class Oracle:
 
     def num_threads(self) -> int:
         return self.L.oracle_num_threads()
+
+    def set_num_threads(self, n: int) -> None:
+        """Threads of the following calls (timing only; results do not depend on it)."""
+        self.L.oracle_set_num_threads(int(n))
 
     # arrays ------------------------------------------------------------
     @staticmethod

@@ -496,3 +496,15 @@ int oracle_num_threads(void)
     return 1;
 #endif
 }
+
+/* Threads the next calls use (the host's logical cores by default); timing only,
+ * the results do not depend on it. */
+void oracle_set_num_threads(int n)
+{
+#ifdef _OPENMP
+    extern void omp_set_num_threads(int);
+    omp_set_num_threads(n > 0 ? n : 1);
+#else
+    (void)n;
+#endif
+}

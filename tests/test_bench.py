@@ -89,3 +89,16 @@ def test_trace_and_counter_summaries(tmp_path, capsys):
     bench.summarize_counters(str(tmp_path / "c"))
     out = capsys.readouterr().out
     assert "| qgemv_x<1> | 100 |" in out  # per-dispatch sums (12, 100): the median of two is the upper
+
+
+def test_clock_fields_keep_clocks_and_power():
+    doc = [{"gpu": 0, "power": {"socket_power": {"value": 512, "unit": "W"}},
+            "clock": {"gfx_0": {"clk": {"value": 2100, "unit": "MHz"}, "min_clk": {"value": 500}},
+                      "mem_0": {"clk": {"value": 1900, "unit": "MHz"}}, "vclk_0": {"clk": {"value": 29}}}}]
+    got = bench.clock_fields(doc)
+    assert got == {"[0].power.socket_power.value": 512, "[0].clock.gfx_0.clk.value": 2100,
+                   "[0].clock.mem_0.clk.value": 1900}
+
+
+def test_clock_sample_never_raises():
+    assert isinstance(bench.gpu_clocks(), dict)  # without a GPU: the reason, not an exception

@@ -169,19 +169,6 @@ def test_config_full(torch, orc, name):
     check_dense(torch, orc, c["fmt"], c["rows"], c["cols"], c["W"], c["x"], name)
 
 
-def test_lm_head_sampled(torch, orc):
-    """248,320 x 5,120 Q8_0 at full size; the oracle checks a sample of rows, every
-    output is finite, and a token's rows agree bit for bit across T = 1, 2 and across T = 3, 4."""
-    name = "c4_q8_0_248320x5120"
-    say(f"[{name}] generating 1.35 GB of packed weights")
-    c = I.dense_case(name)
-    rows = c["rows"]
-    rng = np.random.default_rng(123)
-    sel = np.unique(np.concatenate([rng.choice(rows, 3000, replace=False), [0, 1, rows // 2, rows - 2, rows - 1]]))
-    # VALU kernels at T <= 2, matrix cores at T >= 3 (the fastest for each)
-    check_dense(torch, orc, c["fmt"], rows, c["cols"], c["W"], c["x"], name, sel=sel, same_bits=((1, 2), (3, 4)))
-
-
 def test_repeat_calls_bitwise(torch):
     c = I.dense_case("c2a_q8_0_10240x2560")
     Wd, xd = dev(torch, c["W"]), dev(torch, c["x"])
@@ -358,16 +345,6 @@ def test_mfma_dyadic_bitwise(torch, orc, monkeypatch):
     assert np.array_equal(y.astype(np.float64), ref)
 
 
-def test_mfma_lm_head_sampled(torch, orc, monkeypatch):
-    name = "c4_q8_0_248320x5120"
-    c = I.dense_case(name)
-    rows = c["rows"]
-    monkeypatch.setenv("QGEMV_TILE", mfma_tile(c["cols"], 192))
-    rng = np.random.default_rng(321)
-    sel = np.unique(np.concatenate([rng.choice(rows, 2000, replace=False), [0, 15, 16, rows - 17, rows - 1]]))
-    check_dense(torch, orc, c["fmt"], rows, c["cols"], c["W"], c["x"], f"mfma {name}", sel=sel)
-
-
 def test_mfma_x_pieces_full_range(torch, orc, monkeypatch):
     """x with full 24-bit significands over a wide exponent range (the kernel
     splits each x into three bf16 pieces)."""
@@ -402,16 +379,6 @@ def test_mfma_persistent_agrees_bitwise(torch, orc, monkeypatch):
             assert np.array_equal(y, ref), (rows, cols, chunk)
 
 
-def test_mfma_persistent_lm_head_sampled(torch, orc, monkeypatch):
-    name = "c4_q8_0_248320x5120"
-    c = I.dense_case(name)
-    rows = c["rows"]
-    monkeypatch.setenv("QGEMV_TILE", "q8_0:8,10,128,p")
-    rng = np.random.default_rng(654)
-    sel = np.unique(np.concatenate([rng.choice(rows, 2000, replace=False), [0, 15, 16, rows - 17, rows - 1]]))
-    check_dense(torch, orc, c["fmt"], rows, c["cols"], c["W"], c["x"], f"persist {name}", sel=sel)
-
-
 # ------------------------------------------------------------- fused argmax
 def argmax_check(torch, orc, fmt, rows, cols, W, x, what, sel_oracle=True):
     """Fused argmax against (a) the argmax of the dense call's own output, bit for
@@ -440,14 +407,6 @@ def test_argmax_configs(torch, orc, name):
     for T in (1, 2, 3, 4):
         say(f"[argmax] {name} T={T}")
         argmax_check(torch, orc, c["fmt"], c["rows"], c["cols"], c["W"], c["x"][:T], f"{name} T={T}")
-
-
-def test_argmax_lm_head(torch, orc):
-    name = "c4_q8_0_248320x5120"
-    c = I.dense_case(name)
-    for T in (1, 4):
-        say(f"[argmax] {name} T={T}")
-        argmax_check(torch, orc, c["fmt"], c["rows"], c["cols"], c["W"], c["x"][:T], f"{name} T={T}", sel_oracle=T == 4)
 
 
 def test_argmax_ties_negatives_and_kinds(torch, orc, monkeypatch):
@@ -538,25 +497,6 @@ def test_rows_subset_bad_ids(torch, orc, monkeypatch):
     x = I.activations(rng, cols)
     ids = np.array([3, -1, 49, 50, 7, 1 << 30, 0], dtype=np.int64)
     rows_check(torch, orc, monkeypatch, Q8, rows, cols, W, x, ids, "bad ids")
-
-
-def test_rows_subset_draft_vocabulary(torch, orc, monkeypatch):
-    """32,768 of the LM head's 248,320 rows (a draft vocabulary), T = 1..4."""
-    c = I.dense_case("c4_q8_0_248320x5120")
-    rng = np.random.default_rng(8)
-    ids = np.sort(rng.choice(c["rows"], 32768, replace=False))
-    Wd, xd = dev(torch, c["W"]), dev(torch, c["x"])
-    monkeypatch.setenv("QGEMV_TILE", "q8_0:4,10,8,d")  # a VALU tile that fits the LDS at T = 4
-    full = ops.gemv("q8_0", Wd, xd, c["rows"]).cpu().numpy()
-    monkeypatch.delenv("QGEMV_TILE")
-    idd = dev(torch, ids.astype(np.int32))
-    samp = rng.choice(len(ids), 500, replace=False)
-    for T in (1, 2, 3, 4):
-        say(f"[rows] draft vocabulary T={T}")
-        y = ops.gemv_rows("q8_0", Wd, xd[:T].contiguous(), c["rows"], idd).cpu().numpy()
-        assert np.array_equal(y, full[:T, ids]), T
-        ref, bound = orc.gemv(Q8, c["rows"], c["cols"], c["W"], c["x"][:T], sel=ids[samp])
-        assert_parity(y[:, samp], ref, bound, f"draft vocabulary T={T}")
 
 
 # ---------------------------------------------------------- grouped experts
