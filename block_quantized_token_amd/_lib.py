@@ -20,7 +20,7 @@ EXPORTS = (
     "qgemv_q8_0", "qgemv_q4_0", "qgemv_bf16", "qgemv_grouped_experts", "qgemv_argmax", "qgemv_rows", "qg_packed_bytes",
     "qg_pack_q8_0", "qg_unpack_q8_0", "qg_pack_q4_0", "qg_unpack_q4_0", "qg_query_tile",
     "qg_status_string", "qg_last_error", "qg_quantize_q8_0", "qg_quantize_q4_0", "qgemv_experts_gate_up",
-    "qgemv_experts_down", "qg_read_probe",
+    "qgemv_experts_down", "qg_read_probe", "qgemv_argmax_noalloc",
 )
 QG_Q4_ABSMAX, QG_Q4_LLOYD = 0, 1
 
@@ -57,6 +57,8 @@ def load() -> ctypes.CDLL:
     L.qgemv_rows.argtypes = [i32, i64, i64, i64, vp, i32, vp, vp, vp, vp]
     L.qgemv_argmax.restype = i32
     L.qgemv_argmax.argtypes = [i32, i64, i64, i32, vp, vp, vp, vp, vp, vp]
+    L.qgemv_argmax_noalloc.restype = i32
+    L.qgemv_argmax_noalloc.argtypes = [i32, i64, i64, i32, vp, vp, vp, vp, vp]
     L.qg_packed_bytes.restype = sz
     L.qg_packed_bytes.argtypes = [i32, i64, i64]
     for name in ("qg_pack_q8_0", "qg_unpack_q8_0", "qg_pack_q4_0", "qg_unpack_q4_0"):
@@ -123,6 +125,10 @@ def qgemv_rows(fmt, rows, cols, n_sel, ids, T, W, x, y, stream=None) -> int:
 
 def qgemv_argmax(fmt, rows, cols, T, W, x, work, idx, val, stream=None) -> int:
     return load().qgemv_argmax(fmt, rows, cols, T, W, x, work, idx, val, stream)
+
+
+def qgemv_argmax_noalloc(fmt, rows, cols, T, W, x, idx, val, stream=None) -> int:
+    return load().qgemv_argmax_noalloc(fmt, rows, cols, T, W, x, idx, val, stream)
 
 
 def qg_packed_bytes(fmt, rows, cols) -> int:

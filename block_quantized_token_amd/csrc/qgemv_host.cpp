@@ -593,6 +593,20 @@ int qgemv_argmax(int fmt, int64_t rows, int64_t cols, int T, const void* W, cons
     return run_argmax(fmt, rows, cols, T, W, x, work, idx, val, stream);
 }
 
+int qgemv_argmax_noalloc(int fmt, int64_t rows, int64_t cols, int T, const void* W, const float* x, int32_t* idx,
+                         float* val, void* stream) {
+    // every argument is checked before the first HIP call (the scratch lookup)
+    int64_t rbytes = 0;
+    int st = check_common(fmt, rows, cols, T, W, x, val, &rbytes);
+    if (st) return st;
+    if (!idx) return fail(QG_EINVAL, "null idx");
+    if (!aligned(idx, 4)) return fail(QG_EALIGN, "idx must be 4-byte aligned");
+    void* keys = nullptr;
+    const int err = argmax_scratch(&keys);
+    if (err) return fail(QG_EHIP, "device scratch of the argmax keys not addressable: %s", hip_error_name(err));
+    return run_argmax(fmt, rows, cols, T, W, x, keys, idx, val, stream);
+}
+
 int qgemv_grouped_experts(int fmt, int64_t n_experts, int64_t rows, int64_t cols, int T, int topk,
                           const int32_t* ids, const void* W, const float* x, float* y, void* stream) {
     return run_grouped(fmt, n_experts, rows, cols, T, topk, ids, W, nullptr, x, y, nullptr, 0, stream);

@@ -193,4 +193,12 @@ int launch_read_probe(const void* src, int64_t bytes, int64_t max_groups, uint32
                       void* stream);
 const char* hip_error_name(int err);
 
+// Keys of the allocation-free fused argmax (one per token) and the devices whose
+// copy of them the library can address.
+constexpr int kArgmaxScratchKeys = QG_MAX_T;
+constexpr int kMaxDevices = 64;
+// The current device's copy of the allocation-free argmax's keys (device memory of
+// kArgmaxScratchKeys uint64 values, looked up once per device); 0 or a hipError_t.
+int argmax_scratch(void** out);
+
 }  // namespace qg

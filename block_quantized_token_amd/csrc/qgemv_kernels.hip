@@ -30,9 +30,17 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <mutex>
 #include <type_traits>
 
 #include "qgemv_internal.h"
+
+// The allocation-free fused argmax keeps its per-token 64-bit keys here instead of
+// in a caller-owned workspace: QG_MAX_T of them (32 bytes), one copy per GPU the
+// library runs on, held until the process ends.  Host code never uses this name as
+// an address (on the host it is only a stand-in for the device symbol): it passes
+// the address hipGetSymbolAddress returns for the current device.
+static __device__ __align__(256) unsigned long long scratch[qg::kArgmaxScratchKeys];
 
 namespace qg {
 namespace {
@@ -2429,5 +2437,27 @@ int launch_grouped(int fmt, const Tile& tile, const GroupedArgs& a, void* stream
 }
 
 const char* hip_error_name(int err) { return hipGetErrorString((hipError_t)err); }
+
+namespace {
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+}  // namespace
+
+int argmax_scratch(void** out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return (int)e;
+    if (dev < 0 || dev >= kMaxDevices) return (int)hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {  // once per device, with that device current
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return (int)e;
+        if (!p) return (int)hipErrorInvalidSymbol;
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return 0;
+}
 
 }  // namespace qg

@@ -152,6 +152,22 @@ int qgemv_argmax(int fmt, int64_t rows, int64_t cols, int T, const void* W, cons
                  int32_t* idx, float* val, void* stream);
 
 /*
+ * qgemv_argmax without the work argument, for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc): the per-token keys live in a library-owned device array of
+ * QG_MAX_T uint64 values, one copy per GPU, set up at the first call on that GPU
+ * (with it current) and held until the process ends.  The call allocates
+ * nothing and calls no allocating routine.  Every call on one GPU uses that
+ * GPU's array (each call clears the keys it uses first): calls that can overlap
+ * in time on one GPU -- different streams, or threads without ordering -- race
+ * and must not be issued.  Arguments, results, ordering and errors otherwise as
+ * qgemv_argmax (T above QG_MAX_T is QG_EINVAL; QG_EHIP if the array cannot be
+ * addressed on the current device).
+ */
+int qgemv_argmax_noalloc(int fmt, int64_t rows, int64_t cols, int T, const void* W, const float* x, int32_t* idx,
+                         float* val, void* stream);
+
+/*
  * Row subset: the mat-vec over a list of rows, for a draft-vocabulary LM head
  * that reads only the rows of the tokens the drafter may propose (the drafter-
  * cost issue, "perf(speculative): cut the MTP drafter's per-step cost...",
