@@ -67,6 +67,8 @@ def time_calls(torch, fmt, ring, x_dev, rows, T, calls, stream, y_dev):
 
 def kernel_name(tile, T):
     """Device symbol of the kernel a call with ``tile`` launches (Q8_0)."""
+    if tile["kind"] == 8:
+        return f"qgemv_mx_kernel<0, {T}>"
     if tile["kind"] == 7:
         return f"qgemv_half_kernel<0, {T}, {tile['depth']}>"
     if tile["kind"] in (2, 3):
@@ -108,10 +110,12 @@ def measured_traffic(kernel):
     return int(float(rows[kernel][4]))
 
 
-def summarize_pmc(fetch_dir, write_dir, nbytes):
+def summarize_pmc(fetch_dir, write_dir, nbytes, alg_bytes=None):
     """Per-kernel HBM traffic from two rocprofv3 --pmc runs of this script
     (FETCH_SIZE, then WRITE_SIZE; KiB per dispatch), each scaled by what the same
-    counter reads for the calibration copy (nbytes read, nbytes written)."""
+    counter reads for the calibration copy (nbytes read, nbytes written), set
+    beside ``alg_bytes`` algorithmic bytes per launch (default nbytes)."""
+    alg_bytes = alg_bytes or nbytes
     import csv
     import glob
 
@@ -140,7 +144,7 @@ def summarize_pmc(fetch_dir, write_dir, nbytes):
     print(f"kernel_source_sha256: {source_digest()}")
     print(f"calibration: {cal} moves {nbytes} B each way; FETCH_SIZE reads {fetch[cal]:.1f} KiB "
           f"(scale {f_scale:.4f}), WRITE_SIZE reads {write[cal]:.1f} KiB (scale {w_scale:.4f})")
-    print(f"algorithmic bytes per launch: {nbytes} weight bytes (+ x and y, under 0.3%)")
+    print(f"algorithmic bytes per launch: {alg_bytes} weight bytes (+ x and y)")
     print()
     print("| kernel | FETCH_SIZE KiB | WRITE_SIZE KiB | scaled read B | scaled read + write B | vs algorithmic |")
     print("|---|---|---|---|---|---|")
@@ -149,7 +153,7 @@ def summarize_pmc(fetch_dir, write_dir, nbytes):
             continue
         rb = fetch[k] * 1024.0 * f_scale
         wb = write.get(k, 0.0) * 1024.0 * w_scale
-        print(f"| {k} | {fetch[k]:.1f} | {write.get(k, 0.0):.1f} | {rb:.0f} | {rb + wb:.0f} | {(rb + wb) / nbytes:.3f} |")
+        print(f"| {k} | {fetch[k]:.1f} | {write.get(k, 0.0):.1f} | {rb:.0f} | {rb + wb:.0f} | {(rb + wb) / alg_bytes:.3f} |")
 
 
 def time_entry(torch, stream, launch, calls):
@@ -561,6 +565,73 @@ def summarize_counters(counter_dir):
         print(f"| {k} | " + " | ".join(f"{m:.4g}" for m in med) + " |")
 
 
+PROFILE_WORKLOADS = ("c1_q8_0_2560x2560", "c2a_q8_0_10240x2560", "c2b_q8_0_2560x6144", "c3_q4_0_8192x2560",
+                     "c3_bf16_8192x2560", "c4_q8_0_248320x5120", "c4_argmax", "c5_q4_0_experts")
+
+
+def profile_workload(torch, stream, name, calls, tiles):
+    """Untimed calls for rocprofv3 to trace or count: ``calls`` calls at each T = 1..4
+    of one workload for each tile spec in ``tiles`` ("default" = the library's own
+    tile; a spec outside what the library runs at some T is skipped there), walking a
+    ring of device-random weights of >= 1 GiB so every call streams from HBM."""
+    import os as _os
+    sp = stream.cuda_stream
+    if name == "c5_q4_0_experts":
+        g = I.GROUPED[name]
+        E, rows, cols, topk = g["n_experts"], g["rows"], g["cols"], g["topk"]
+        nb = _lib.qg_packed_bytes(g["fmt"], E * rows, cols)
+        ring = [torch.randint(0, 256, (nb,), dtype=torch.uint8, device="cuda") for _ in range(max(1, -(-RING_BYTES // nb)))]
+        ids_all = torch.from_numpy(I.expert_ids(I.rng_for(0), E, 4, topk)).cuda()
+        x = torch.randn(4, cols, device="cuda")
+        y = torch.empty(4, topk, rows, device="cuda")
+        fmt_name = I.FMT_NAMES[g["fmt"]]
+
+        def call(T, i):
+            ids = ids_all[:T].contiguous()
+            return _lib.qgemv_grouped_experts(g["fmt"], E, rows, cols, T, topk, ids.data_ptr(), ring[i % len(ring)].data_ptr(),
+                                              x.data_ptr(), y.data_ptr(), sp)
+    else:
+        base = "c4_q8_0_248320x5120" if name == "c4_argmax" else name
+        fmt, rows, cols, _ = I.CONFIGS[base]
+        fmt_name = I.FMT_NAMES[fmt]
+        nb = _lib.qg_packed_bytes(fmt, rows, cols)
+        ring = [torch.randint(0, 256, (nb,), dtype=torch.uint8, device="cuda") for _ in range(max(1, -(-RING_BYTES // nb)))]
+        x = torch.randn(4, cols, device="cuda")
+        y = torch.empty(4, rows, device="cuda")
+        entry = {0: _lib.qgemv_q8_0, 1: _lib.qgemv_q4_0, 2: _lib.qgemv_bf16}[fmt]
+        work = torch.empty(4, dtype=torch.int64, device="cuda")
+        idx = torch.empty(4, dtype=torch.int32, device="cuda")
+        val = torch.empty(4, device="cuda")
+
+        def call(T, i):
+            W = ring[i % len(ring)].data_ptr()
+            if name == "c4_argmax":
+                return _lib.qgemv_argmax(fmt, rows, cols, T, W, x.data_ptr(), work.data_ptr(), idx.data_ptr(),
+                                         val.data_ptr(), sp)
+            return entry(rows, cols, T, W, x.data_ptr(), y.data_ptr(), sp)
+    saved = _os.environ.get("QGEMV_TILE")
+    try:
+        for spec in tiles:
+            if spec == "default":
+                _os.environ.pop("QGEMV_TILE", None)
+            else:
+                _os.environ["QGEMV_TILE"] = f"{fmt_name}:{spec}"
+            for T in (1, 2, 3, 4):
+                if call(T, 0) != _lib.QG_OK:
+                    log(f"profile: {name} tile {spec} T={T} not run: {_lib.last_error()}")
+                    continue
+                for i in range(1, calls):
+                    _lib.check(call(T, i), name)
+                torch.cuda.synchronize()
+                log(f"profile: {name} tile {spec} T={T}: {calls} calls")
+    finally:
+        if saved is None:
+            _os.environ.pop("QGEMV_TILE", None)
+        else:
+            _os.environ["QGEMV_TILE"] = saved
+    del ring
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -570,6 +641,11 @@ def main():
     ap.add_argument("--no-extra", action="store_true", help="skip the timings of the other workloads")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="N",
                     help="after the timed region, run N plain copies of the weight size (PMC calibration)")
+    ap.add_argument("--profile", choices=PROFILE_WORKLOADS, metavar="WORKLOAD",
+                    help="untimed calls of one workload for rocprofv3 (see --calls, --tiles); no JSON line")
+    ap.add_argument("--calls", type=int, default=20, help="calls per T and tile with --profile")
+    ap.add_argument("--tiles", default="default", help="space-separated QGEMV_TILE specs for --profile")
+    ap.add_argument("--bytes", type=int, default=0, help="algorithmic bytes per launch for --summarize-pmc")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="print the HBM traffic table from two rocprofv3 --pmc runs of this script and exit")
     ap.add_argument("--summarize-trace", metavar="TRACE_DIR",
@@ -586,7 +662,7 @@ def main():
         return
     if args.summarize_pmc:
         fmt, rows, cols, _ = I.CONFIGS[WORKLOAD]
-        summarize_pmc(*args.summarize_pmc, _lib.qg_packed_bytes(fmt, rows, cols))
+        summarize_pmc(*args.summarize_pmc, _lib.qg_packed_bytes(fmt, rows, cols), args.bytes or None)
         return
 
     if args.gpus != 1:
@@ -601,6 +677,16 @@ def main():
     _lib.load()
     torch.cuda.set_device(0)
     stream = torch.cuda.current_stream()
+    if args.profile:
+        profile_workload(torch, stream, args.profile, args.calls, args.tiles.split())
+        if args.copy_calibration:
+            nb = _lib.qg_packed_bytes(I.FMT_Q8_0, 10240, 2560)
+            src = torch.empty(nb // 4, dtype=torch.float32, device="cuda").fill_(1.0)
+            dst = torch.empty_like(src)
+            for _ in range(args.copy_calibration):
+                torch.mul(src, 1.0, out=dst)
+            torch.cuda.synchronize()
+        return
 
     case = I.dense_case(WORKLOAD)
     fmt, rows, cols = case["fmt"], case["rows"], case["cols"]

@@ -62,8 +62,9 @@ bool parse_tile_spec(const std::string& spec, Tile* t, std::string* why) {
         got = sscanf(spec.c_str(), f, &rb, &nw, &rw, &depth, &tail2) == 4 ? 4 : -1;
     }
     const bool dma = kind == 'l' || kind == 'L' || kind == 'u' || kind == 'h';
-    if (!(got == 3 || (got == 4 && (kind == 'd' || kind == 's' || kind == 'm' || kind == 'p' || (dma && depth > 0))))) {
-        *why = "tile '" + spec + "' is not rb,nw,rw[,d|s|m|p|l<depth>|L<depth>|u<depth>|h<depth>]";
+    if (!(got == 3 ||
+          (got == 4 && (kind == 'd' || kind == 's' || kind == 'm' || kind == 'p' || kind == 'x' || (dma && depth > 0))))) {
+        *why = "tile '" + spec + "' is not rb,nw,rw[,d|s|m|p|x|l<depth>|L<depth>|u<depth>|h<depth>]";
         return false;
     }
     if (!valid_rb(rb) || nw < 1 || nw > kMaxWaves || rw < 2 * rb || rw % (2 * rb) || rw > (1 << 20)) {
@@ -73,10 +74,11 @@ bool parse_tile_spec(const std::string& spec, Tile* t, std::string* why) {
     t->rows_per_batch = rb;
     t->waves_per_wg = nw;
     t->rows_per_wg = rw;
-    t->kind = got == 4 ? (kind == 'd' ? 0 : kind == 'l' ? 2 : kind == 'L' ? 3 : kind == 'u' ? 4 : kind == 'h' ? 7 : 1)
+    t->kind = got == 4 ? (kind == 'd' ? 0 : kind == 'l' ? 2 : kind == 'L' ? 3 : kind == 'u' ? 4 : kind == 'h' ? 7
+                          : kind == 'x' ? 8 : 1)
                        : -1;  // -1: later
     t->mfma = got == 4 && kind == 'm' ? 1 : got == 4 && kind == 'p' ? 2 : 0;
-    t->depth = got == 4 && dma ? depth : 0;
+    t->depth = got == 4 && dma ? depth : got == 4 && kind == 'x' ? 1 : 0;
     return true;
 }
 
@@ -94,17 +96,20 @@ struct TuneEntry {
 // MI355X, µs per call at T = 1..4 from sweeps over (kind, rows per workgroup,
 // ring depth) where the rule's pick loses by more than a few percent.
 const TuneEntry kTuned[] = {
-    // 2560 x 2560: the direct one-shot kernel (4 rows per workgroup, 640 workgroups)
-    // at T <= 3 (4.7 / 5.3 / 6.2 µs against 5.5 / 5.9 / 6.5 for the rule's LDS-DMA
-    // tile), register-streamed at T = 4 (6.6 against 7.1)
-    {QG_FMT_Q8_0, 2560, 2560, 1, "2,5,4,d"},
-    {QG_FMT_Q8_0, 2560, 2560, 2, "2,5,4,d"},
-    {QG_FMT_Q8_0, 2560, 2560, 3, "2,5,4,d"},
-    {QG_FMT_Q8_0, 2560, 2560, 4, "4,5,16,s"},
-    // 10240 x 2560: 256-wide k slices, ten waves of half a slice's work (three or
-    // two per SIMD instead of five full waves, two of them on one SIMD): 7.7 / 8.3 /
-    // 9.1 / 9.9 µs against 8.0 / 9.1 / 10.5 / 11.7 for the 512-wide LDS-DMA ring
-    {QG_FMT_Q8_0, 10240, 2560, 0, "4,10,40,h2"},
+    // 256-wide k slices on the matrix cores (one 16-row tile in flight per wave),
+    // the same kind at every T; µs per call at T = 1..4 against the best earlier
+    // kinds (vector-ALU, themselves one kind per shape):
+    //   10240 x 2560 Q8_0: 7.6 / 7.8 / 8.0 / 8.1 (48 rows per workgroup: three
+    //     full tiles per wave; 40 rows, 256 workgroups: 8.0 / 8.1 / 8.3 / 8.4)
+    //     against 7.9 / 8.3 / 9.1 / 9.8 for the half-slice vector-ALU ring;
+    //   2560 x 2560 Q8_0: 4.5-4.9 / 4.7-5.0 / 4.9-5.1 / 5.1-5.3 against 4.6 / 5.3 /
+    //     6.2 / 6.5 (direct at T <= 3, register-streamed at T = 4);
+    //   8192 x 2560 Q4_0: 6.3 / 6.5 / 6.6 / 6.9 against 6.1 / 7.2 / 8.5 / 9.5;
+    //   8192 x 2560 BF16: 9.4 / 9.5 / 9.6 / 9.5 against 8.5 / 9.4 / 10.4 / 10.9.
+    {QG_FMT_Q8_0, 10240, 2560, 0, "4,10,48,x"},
+    {QG_FMT_Q8_0, 2560, 2560, 0, "4,10,16,x"},
+    {QG_FMT_Q4_0, 8192, 2560, 0, "4,10,32,x"},
+    {QG_FMT_BF16, 8192, 2560, 0, "4,10,32,x"},
     {QG_FMT_Q8_0, 2560, 6144, 0, "4,12,16,s"},     // register-streamed beats DMA at 12 slices
     // LM head: the LDS-DMA VALU kernel at T <= 2 (233 / 241 µs against 249 / 256
     // for the matrix cores), the persistent matrix-core kernel at T >= 3 (267 / 275
@@ -117,13 +122,6 @@ const TuneEntry kTuned[] = {
     {QG_FMT_Q8_0, 248320, 5120, 2, "4,10,512,l2"},
     {QG_FMT_Q8_0, 248320, 5120, 3, "8,10,64,p"},
     {QG_FMT_Q8_0, 248320, 5120, 4, "8,10,64,p"},
-    {QG_FMT_Q4_0, 8192, 2560, 1, "4,5,8,d"},       // direct: 6.0 vs 7.7 µs for the LDS-DMA ring
-    {QG_FMT_Q4_0, 8192, 2560, 2, "4,5,8,d"},       //   7.2 vs 7.8 µs for two row groups per slice
-    {QG_FMT_Q4_0, 8192, 2560, 3, "4,5,8,d"},       //   8.5 vs 8.7 µs
-    {QG_FMT_Q4_0, 8192, 2560, 4, "4,10,32,s"},     // two row groups per slice: 9.5 vs 10.1 µs direct
-    // BF16 8192 x 2560: direct at T <= 2 (8.5 / 9.4 µs against 9.6 / 10.0 for the rule's tile)
-    {QG_FMT_BF16, 8192, 2560, 1, "4,5,8,d"},
-    {QG_FMT_BF16, 8192, 2560, 2, "4,5,8,d"},
 };
 
 Tile default_tile(int fmt, int64_t rows, int64_t cols, int T) {
@@ -137,6 +135,20 @@ Tile default_tile(int fmt, int64_t rows, int64_t cols, int T) {
         std::string why;
         if (e.fmt == fmt && e.rows == rows && e.cols == cols && (e.T == 0 || e.T == T) && parse_tile_spec(e.tile, &t, &why))
             return t;
+    }
+    // up to 12 256-wide slices: the matrix cores, one wave per slice, about one
+    // workgroup per CU in whole 16-row tiles (the tuned shapes above follow this)
+    if (cols % 256 == 0 && cols / 256 <= kMaxWaves && row_bytes(fmt, cols) * 16 < 0x7FFFFFFF) {
+        t.kind = 8;
+        t.depth = 1;
+        t.rows_per_batch = 4;
+        t.waves_per_wg = (int)(cols / 256);
+        int64_t rw = ((rows + 255) / 256 + 15) / 16 * 16;
+        t.rows_per_wg = (int)(rw > 1024 ? 1024 : rw);
+        while (t.rows_per_wg > 16 && mx_lds_bytes(fmt, t, T, t.waves_per_wg) > kMaxLds) t.rows_per_wg -= 16;
+        if (mx_lds_bytes(fmt, t, T, t.waves_per_wg) <= kMaxLds) return t;
+        t.kind = 0;
+        t.depth = 0;
     }
     // fewest waves that cover the slices in equal rounds
     const int64_t rounds = (nslices + kMaxWaves - 1) / kMaxWaves;
@@ -243,6 +255,18 @@ int pick_tile(int fmt, int64_t rows, int64_t cols, int T, Tile* t) {
                         units_lds_bytes(fmt, *t, T, cols), t->rows_per_wg, t->depth);
         return QG_OK;
     }
+    if (t->kind == 8) {
+        const int64_t nsl256 = cols / 256;
+        if (cols % 256 || t->waves_per_wg % nsl256 != 0)
+            return fail(QG_EINVAL, "matrix-core half-slice tile needs cols a multiple of 256 and waves_per_wg a "
+                                   "multiple of the %lld 256-wide slices", (long long)nsl256);
+        if (row_bytes(fmt, cols) * 16 > 0x7FFFFFFF)
+            return fail(QG_EINVAL, "matrix-core half-slice tile needs 16 rows within a 2 GB descriptor");
+        if (mx_lds_bytes(fmt, *t, T, (int)nsl256) > kMaxLds)
+            return fail(QG_EINVAL, "tile needs %zu B of LDS (rows_per_wg %d too large)",
+                        mx_lds_bytes(fmt, *t, T, (int)nsl256), t->rows_per_wg);
+        return QG_OK;
+    }
     if (t->kind == 7) {
         const int64_t nsl256 = cols / 256;
         if (cols % 256 || t->waves_per_wg % nsl256 != 0)
@@ -340,7 +364,8 @@ int run_dense(int fmt, int64_t rows, int64_t cols, int T, const void* W, const f
     a.nslices = (int)((cols + kSlice - 1) / kSlice);
     a.rows_per_wg = tile.rows_per_wg;
     if ((rows + tile.rows_per_wg - 1) / tile.rows_per_wg > 0x7FFFFFFF) return fail(QG_EUNSUPPORTED, "grid too large");
-    int err = tile.kind == 7   ? launch_half(fmt, T, tile, a, stream)
+    int err = tile.kind == 8   ? launch_mx(fmt, T, tile, a, stream)
+              : tile.kind == 7 ? launch_half(fmt, T, tile, a, stream)
               : tile.kind == 4 ? launch_units(fmt, T, tile, a, stream)
               : tile.kind >= 2 ? launch_dma(fmt, T, tile, a, stream)
               : tile.kind == 1 ? launch_stream(fmt, T, tile, a, stream)
@@ -378,6 +403,7 @@ int run_argmax(int fmt, int64_t rows, int64_t cols, int T, const void* W, const 
         if (dma_lds_bytes(fmt, tile, T, (int)nsl) > kMaxLds) tile.kind = 0;
     }
     if (tile.kind == 7 && half_lds_bytes(fmt, tile, T, (int)(cols / 256)) > kMaxLds) tile.kind = 0;
+    if (tile.kind == 8 && mx_lds_bytes(fmt, tile, T, (int)(cols / 256)) > kMaxLds) tile.kind = 0;
     if (tile.kind == 4 || (tile.kind == 1 && tile.mfma == 1)) tile.kind = 0;
     if (tile.kind == 1 && !persist && (tile.rows_per_batch != 4 || !stream_supported(fmt, T, 4))) tile.kind = 0;
     if (tile.kind == 0) {  // direct, rb 2, one wave per slice when the slices fit a workgroup
@@ -712,8 +738,8 @@ int qg_query_tile(int fmt, int64_t rows, int64_t cols, int T, int out_tile[QG_TI
     Tile t;
     int st = pick_tile(fmt, rows, cols, T, &t);
     if (st) return st;
-    const bool half = t.kind == 7;  // 256-wide k slices, 16 lanes per row
-    out_tile[0] = half ? 16 : t.lanes_per_row;
+    const bool half = t.kind == 7 || t.kind == 8;  // 256-wide k slices
+    out_tile[0] = t.kind == 8 ? 4 : half ? 16 : t.lanes_per_row;  // kind 8: a row's block sits in 4 lanes
     out_tile[1] = t.rows_per_batch;
     out_tile[2] = t.waves_per_wg;
     out_tile[3] = half ? 256 : t.k_slice;

@@ -21,7 +21,8 @@ struct Tile {
                          // registers; 2: streamed by LDS-DMA loads into a ring of `depth` buffers,
                          // x staged in the ring's last slots; 3: as 2, x staged in its own region;
                          // 4: unit-balanced LDS-DMA (waves take equal shares of (slice, tile) units);
-                         // 7: LDS-DMA on 256-wide k slices, 16 lanes per row
+                         // 7: LDS-DMA on 256-wide k slices, 16 lanes per row; 8: matrix cores on
+                         // 256-wide k slices fed by LDS-DMA loads of 16-row tiles
     int depth;           // kinds 2, 3: tiles in flight per wave (2, 3, 4 or 6); kind 4: 2..4; kind 7: 2, 3; 0 otherwise
 };
 
@@ -102,6 +103,16 @@ inline size_t half_lds_bytes(int fmt, const Tile& t, int T, int nslices256) {
            ntiles * nslices256 * 4 * 2 * pad_tokens(T) * 4;
 }
 
+// Kind 8 (matrix cores on 256-wide slices): one 16-row tile slot per wave (exactly the
+// tile's bytes), a region per wave for x and then its bf16 pieces (1536 * T bytes),
+// then partial sums [16-row tiles][slices][16][pad(T)].
+inline size_t mx_slot_bytes(int fmt) { return (size_t)16 * (stream_chunks(fmt) / 2) * 16; }
+inline size_t mx_lds_bytes(int fmt, const Tile& t, int T, int nslices256) {
+    const size_t ntiles = (size_t)(t.rows_per_wg + 15) / 16;
+    return (size_t)t.waves_per_wg * (mx_slot_bytes(fmt) + 1536 * (size_t)T) +
+           ntiles * nslices256 * 16 * pad_tokens(T) * 4;
+}
+
 // Row-subset kernel: rings of `depth` 8-row slots per wave, then partial sums (x in registers).
 inline size_t gather_lds_bytes(int fmt, const Tile& t, int T, int nslices) {
     const size_t ntiles = (size_t)(t.rows_per_wg + 2 * t.rows_per_batch - 1) / (2 * t.rows_per_batch);
@@ -178,6 +189,7 @@ int launch_stream(int fmt, int T, const Tile& tile, const DenseArgs& a, void* st
 int launch_dma(int fmt, int T, const Tile& tile, const DenseArgs& a, void* stream);
 int launch_units(int fmt, int T, const Tile& tile, const DenseArgs& a, void* stream);
 int launch_half(int fmt, int T, const Tile& tile, const DenseArgs& a, void* stream);
+int launch_mx(int fmt, int T, const Tile& tile, const DenseArgs& a, void* stream);
 // Fused argmax: fills work (uint64[T]), runs the mat-vec, writes idx/val (3 launches).
 int launch_argmax(int fmt, int T, const Tile& tile, const DenseArgs& a, void* work, int32_t* idx, float* val,
                   void* stream);

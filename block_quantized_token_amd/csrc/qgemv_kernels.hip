@@ -1571,6 +1571,230 @@ __device__ __forceinline__ void mfma_persist_q8(const uint8_t* __restrict__ W, i
     wait_vmcnt<0>();  // the last (empty) prefetch returns before the wave ends
 }
 
+// ------------------------- matrix cores on the LDS-DMA ring, 256-wide slices (kind 8)
+// The half-slice kernel's work split (one wave per 256-wide k slice, every
+// wave walks the workgroup's rows) with 16-row tiles contracted on the matrix
+// cores: per 32-weight block of a tile, one v_mfma_f32_16x16x32_bf16 with
+//   A = the slice's x split exactly into three bf16 pieces (row m = 4p + t holds
+//       piece p of token t; rows with t >= T and rows 12..15 are zero), and
+//   B = the block's codes of the 16 rows as bf16 (exact; Q4_0 as 16 (c - 8)),
+// so every product is exact; lane l gets the block's sums for row l % 16, which
+// it scales by that row's d and accumulates in fp32 (BF16: the matrix core
+// accumulates straight into the running sum).  At the end of a tile the three
+// pieces of each token are added in a fixed order.  A token's rows of A never
+// touch another token's, so its bits do not depend on T; the work per tile does
+// not depend on T either.
+// The split is done once per wave and cooperatively: each lane splits four x
+// values of every token and the pieces reach the fragment layout through LDS.
+// Each wave keeps one tile in flight, refilled as soon as the tile's bytes are
+// in registers; measured on 10240 x 2560, a second tile in flight or a refill
+// after the math is slower (the vector-ALU kernels behave alike).
+template <int FMT>
+struct MxShape {
+    static constexpr int kChunks = StreamFmt<FMT>::kChunks / 2;          // 16-byte chunks of a 256-wide row slice
+    static constexpr int kSlot = 16 * kChunks * 16;                       // a 16-row tile: 4352, 2304, 8192 B
+    static constexpr int kLoads = (16 * kChunks + 63) / 64;               // 5, 3, 8
+    static constexpr int kLastLanes = 16 * kChunks - 64 * (kLoads - 1);   // lanes of the last load: 16, 16, 64
+    static constexpr int kBlockBytes = FMT == QG_FMT_Q8_0 ? 34 : FMT == QG_FMT_Q4_0 ? 18 : 64;
+};
+
+// One 16-row tile of the wave's slice into its slot: lane l of load k fetches
+// chunk 64 k + l (row / chunk of the slice); lanes past the tile's last chunk do
+// not load, so the slot is exactly the tile's bytes; rows past the range are
+// outside the descriptor and read as zeros.
+template <int FMT>
+__device__ __forceinline__ void mx_issue(const uint8_t* __restrict__ W, int64_t row_bytes, int64_t row_begin,
+                                         int64_t row_end, int ntiles, int t, const int (&off)[MxShape<FMT>::kLoads],
+                                         uint8_t* slot, int lane) {
+    using M = MxShape<FMT>;
+    const bool live = t < ntiles;
+    const int64_t r0 = row_begin + (int64_t)(live ? t : 0) * 16;
+    const int64_t rows_here = row_end - r0 < 16 ? row_end - r0 : 16;
+    const int num = live ? (int)(rows_here * row_bytes) : 0;
+    const __amdgpu_buffer_rsrc_t rsrc =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(W + r0 * row_bytes), (short)0, num, kBufferRsrcWord3);
+#pragma unroll
+    for (int k = 0; k < M::kLoads - 1; ++k) load_lds16(rsrc, slot + 1024 * k, off[k]);
+    if (M::kLastLanes == 64 || lane < M::kLastLanes) load_lds16(rsrc, slot + 1024 * (M::kLoads - 1), off[M::kLoads - 1]);
+}
+
+// Byte q of the 12-byte window w[3] as an fp32 (signed).
+__device__ __forceinline__ uint32_t mx_byte_f32(const uint32_t (&w)[3], int q) {
+    return __builtin_bit_cast(uint32_t, (float)(int32_t)(int8_t)(w[q >> 2] >> (8 * (q & 3))));
+}
+
+// The B fragment of block b for lane (row n, k group g): 8 codes as bf16 pairs,
+// and the block's scale of that row (Q4_0: d / 16).  Q8_0 / Q4_0 blocks of an
+// even index start 2 bytes past a dword, so their codes are read as an aligned
+// 12-byte window whose bytes 2..9 are taken (the byte positions are constants
+// after unrolling).
+template <int FMT>
+__device__ __forceinline__ V4 mx_bfrag(const uint8_t* rowp, int b, int g, float& d) {
+    using M = MxShape<FMT>;
+    V4 r;
+    if constexpr (FMT == QG_FMT_BF16) {
+        const U4a q = *reinterpret_cast<const U4a*>(rowp + M::kBlockBytes * b + 16 * g);
+        r[0] = q.v[0]; r[1] = q.v[1]; r[2] = q.v[2]; r[3] = q.v[3];
+        d = 1.0f;
+    } else {
+        const uint8_t* blk = rowp + M::kBlockBytes * b;
+        // Q8_0: the lane's codes are bytes 8g..8g+7 of the block's 32; Q4_0: the low
+        // (g < 2) or high (g >= 2) nibbles of code bytes 8(g & 1)..+7, i.e. codes 8g..8g+7
+        const int cb = FMT == QG_FMT_Q8_0 ? 8 * g : 8 * (g & 1);
+        const int sh = (b & 1) ? 0 : 2;  // where the codes start in the window
+        const uint32_t* p = reinterpret_cast<const uint32_t*>(blk + 2 + cb - sh);
+        uint32_t w[3] = {p[0], p[1], sh ? p[2] : 0u};
+        if constexpr (FMT == QG_FMT_Q4_0) {
+            // nibble c -> the signed byte 16 (c - 8): flip bit 3, move the nibble to the top
+            const int ns = g >= 2 ? 0 : 4;
+#pragma unroll
+            for (int i = 0; i < 3; ++i) w[i] = ((w[i] << ns) & 0xF0F0F0F0u) ^ 0x80808080u;
+        }
+        uint32_t f[8];
+#pragma unroll
+        for (int q = 0; q < 8; ++q) f[q] = mx_byte_f32(w, q + sh);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) r[q] = __builtin_amdgcn_perm(f[2 * q + 1], f[2 * q], 0x07060302u);
+        const float dv = half_bits_to_float(*reinterpret_cast<const uint16_t*>(blk));
+        d = FMT == QG_FMT_Q4_0 ? dv * 0.0625f : dv;
+    }
+    return r;
+}
+
+template <int FMT, int NT, class Out>
+__device__ __forceinline__ void mx_rows(const uint8_t* __restrict__ W, int64_t row_bytes, int cols, int nsl,
+                                        const float* __restrict__ x, int64_t row_begin, int64_t row_end, int nw,
+                                        Out&& out) {
+    using M = MxShape<FMT>;
+    constexpr int TP = pad_pow2(NT);
+    constexpr int L = M::kLoads;
+    constexpr int REG = 1536 * NT;  // per wave: x [NT][256] fp32, then the A pieces [8][4][3][NT] x 16 B
+    extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: keeps descriptors and M0 scalar
+    const int n = lane & 15, g = lane >> 4;
+    const int s = wave % nsl, rg = wave / nsl, RG = nw / nsl;
+    const int k0 = s * kHalfSlice;
+    const int ntiles = (int)((row_end - row_begin + 15) / 16);
+    uint8_t* slot = smem + wave * M::kSlot;
+    uint8_t* reg = smem + nw * M::kSlot + wave * REG;
+    float* part = reinterpret_cast<float*>(smem + nw * (M::kSlot + REG));  // [tiles][nsl][16 rows][TP]
+
+    int off[L];
+#pragma unroll
+    for (int k = 0; k < L; ++k) {
+        const int j = 64 * k + lane;
+        const int r = j / M::kChunks, c = j % M::kChunks;
+        off[k] = r < 16 ? (int)(r * row_bytes) + s * M::kChunks * 16 + 16 * c : kNoLoad;
+    }
+    // x of the slice, then the wave's first tile (x is older: waited for first)
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+        const __amdgpu_buffer_rsrc_t xr =
+            __builtin_amdgcn_make_buffer_rsrc((void*)(x + (int64_t)t * cols + k0), (short)0, 1024, kBufferRsrcWord3);
+        load_lds16(xr, reg + 1024 * t, 16 * lane);
+    }
+    mx_issue<FMT>(W, row_bytes, row_begin, row_end, ntiles, rg, off, slot, lane);
+    wait_vmcnt<L>();
+
+    // split: lane l takes k = 4 l .. 4 l + 3 of every token; piece p of x[t][k] goes
+    // to the 16-byte fragment (block k / 32, group (k % 32) / 8, row 4p + t)
+    V4 afrag[8];
+    {
+        float4 xv[NT];
+#pragma unroll
+        for (int t = 0; t < NT; ++t) xv[t] = *reinterpret_cast<const float4*>(reg + 1024 * t + 16 * lane);
+        wait_lgkmcnt0();  // every lane's x is read before the pieces overwrite it
+        const int b = lane >> 3, gg = (lane & 7) >> 1, half = (lane & 1) * 8;
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+            const float vv[4] = {xv[t].x, xv[t].y, xv[t].z, xv[t].w};
+            uint32_t pc[3][4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                // hi = x with its low 16 bits cleared, mid = the same of x - hi, lo = x - hi - mid:
+                // exact (x has 24 significant bits), and each piece is exactly a bf16
+                const uint32_t v = __builtin_bit_cast(uint32_t, vv[q]);
+                const float r1 = vv[q] - __builtin_bit_cast(float, v & 0xFFFF0000u);
+                const uint32_t u1 = __builtin_bit_cast(uint32_t, r1);
+                const float r2 = r1 - __builtin_bit_cast(float, u1 & 0xFFFF0000u);
+                pc[0][q] = v;
+                pc[1][q] = u1;
+                pc[2][q] = __builtin_bit_cast(uint32_t, r2);
+            }
+#pragma unroll
+            for (int p = 0; p < 3; ++p) {
+                uint2 w2;
+                w2.x = __builtin_amdgcn_perm(pc[p][1], pc[p][0], 0x07060302u);
+                w2.y = __builtin_amdgcn_perm(pc[p][3], pc[p][2], 0x07060302u);
+                *reinterpret_cast<uint2*>(reg + b * (192 * NT) + (gg * 3 * NT + p * NT + t) * 16 + half) = w2;
+            }
+        }
+        wait_lgkmcnt0();
+        const int am = lane & 15, ap = am >> 2, at = am & 3;
+        const bool arow = ap < 3 && at < NT;
+        const int idx = arow ? (g * 3 * NT + ap * NT + at) * 16 : 0;
+#pragma unroll
+        for (int bb = 0; bb < 8; ++bb) {
+            const V4 v = *reinterpret_cast<const V4*>(reg + bb * (192 * NT) + idx);
+            afrag[bb] = arow ? v : V4{0u, 0u, 0u, 0u};
+        }
+    }
+
+    const int mine = ntiles > rg ? (ntiles - rg + RG - 1) / RG : 0;
+    const uint8_t* rowp = slot + n * (M::kChunks * 16);
+    for (int i = 0; i < mine; ++i) {
+        const int t = rg + i * RG;
+        wait_vmcnt<0>();  // the slot holds tile t
+        V4 bq[8];
+        float dq[8];
+#pragma unroll
+        for (int b = 0; b < 8; ++b) bq[b] = mx_bfrag<FMT>(rowp, b, g, dq[b]);
+        wait_lgkmcnt0();  // the tile is in registers: the slot takes the next one
+        if (i + 1 < mine) mx_issue<FMT>(W, row_bytes, row_begin, row_end, ntiles, t + RG, off, slot, lane);
+        F4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int b = 0; b < 8; ++b) {
+            if constexpr (FMT == QG_FMT_BF16) {
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(BF8, afrag[b]),
+                                                              __builtin_bit_cast(BF8, bq[b]), acc, 0, 0, 0);
+            } else {
+                const F4 z = {0.0f, 0.0f, 0.0f, 0.0f};
+                const F4 dd = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(BF8, afrag[b]),
+                                                                      __builtin_bit_cast(BF8, bq[b]), z, 0, 0, 0);
+#pragma unroll
+                for (int j = 0; j < 4; ++j) acc[j] = __builtin_fmaf(dq[b], dd[j], acc[j]);
+            }
+        }
+        // token j's pieces sit in lanes n (hi), n + 16 (mid), n + 32 (lo): (hi + mid) + lo
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            float mid = acc[j], lo = acc[j], junk16 = acc[j], junk32 = acc[j];
+            permlane16_swap(junk16, mid);
+            permlane32_swap(junk32, lo);
+            acc[j] = (acc[j] + mid) + lo;
+        }
+        if (lane < 16) {
+            float* pp = part + (((size_t)t * nsl + s) * 16 + n) * TP;
+#pragma unroll
+            for (int j = 0; j < TP; ++j) pp[j] = acc[j];
+        }
+    }
+    wait_vmcnt<0>();  // a wave with no tile still drains its empty load
+    __syncthreads();
+    // every output of the workgroup: sum the slices' partials in slice order
+    const int nrows = (int)(row_end - row_begin);
+    for (int o = tid; o < nrows * NT; o += blockDim.x) {
+        const int rr = o / NT, tk = o % NT;
+        const float* base = part + ((size_t)(rr >> 4) * nsl * 16 + (rr & 15)) * TP + tk;
+        float sum = base[0];
+        for (int w = 1; w < nsl; ++w) sum = sum + base[(size_t)w * 16 * TP];
+        out(tk, row_begin + rr, sum);
+    }
+}
+
 // ------------------------------------------------------ fused argmax over rows
 // The LM-head step right after the mat-vec (the drafter's LM head in the mlxcel
 // drafter-cost issue): per token, the row with the largest y and that y, with y
@@ -1704,6 +1928,16 @@ qgemv_half_kernel(const uint8_t* __restrict__ W, const float* __restrict__ x, fl
                          [=](int t, int64_t row, float v) { y[t * rows + row] = v; });
 }
 
+template <int FMT, int T>
+__global__ void __launch_bounds__(64 * kMaxWaves)
+qgemv_mx_kernel(const uint8_t* __restrict__ W, const float* __restrict__ x, float* __restrict__ y, int64_t rows,
+                int64_t row_bytes, int cols, int nslices, int rows_per_wg, int nw) {
+    const int64_t row_begin = (int64_t)blockIdx.x * rows_per_wg;
+    const int64_t row_end = row_begin + rows_per_wg < rows ? row_begin + rows_per_wg : rows;
+    mx_rows<FMT, T>(W, row_bytes, cols, nslices, x, row_begin, row_end, nw,
+                    [=](int t, int64_t row, float v) { y[t * rows + row] = v; });
+}
+
 template <int FMT, int T, int D>
 __global__ void __launch_bounds__(64 * kMaxWaves) qgemv_units_kernel(DenseArgs a) {
     const int64_t row_begin = (int64_t)blockIdx.x * a.rows_per_wg;
@@ -1744,6 +1978,15 @@ __global__ void __launch_bounds__(64 * kMaxWaves) qgemv_half_argmax_kernel(Dense
     const int64_t row_end = row_begin + a.rows_per_wg < a.rows ? row_begin + a.rows_per_wg : a.rows;
     ArgmaxOut<T> best;
     half_rows<FMT, T, D>(a.W, a.row_bytes, a.cols, a.nslices, a.x, row_begin, row_end, (int)(blockDim.x >> 6), best);
+    best.merge(work);
+}
+
+template <int FMT, int T>
+__global__ void __launch_bounds__(64 * kMaxWaves) qgemv_mx_argmax_kernel(DenseArgs a, unsigned long long* work) {
+    const int64_t row_begin = (int64_t)blockIdx.x * a.rows_per_wg;
+    const int64_t row_end = row_begin + a.rows_per_wg < a.rows ? row_begin + a.rows_per_wg : a.rows;
+    ArgmaxOut<T> best;
+    mx_rows<FMT, T>(a.W, a.row_bytes, a.cols, a.nslices, a.x, row_begin, row_end, (int)(blockDim.x >> 6), best);
     best.merge(work);
 }
 
@@ -2263,6 +2506,38 @@ ArgmaxFn half_argmax_for(int T, int depth) {
     }
 }
 
+template <int FMT>
+DmaFn mx_for(int T) {
+    switch (T) {
+    case 1: return qgemv_mx_kernel<FMT, 1>;
+    case 2: return qgemv_mx_kernel<FMT, 2>;
+    case 3: return qgemv_mx_kernel<FMT, 3>;
+    default: return qgemv_mx_kernel<FMT, 4>;
+    }
+}
+
+template <int FMT>
+ArgmaxFn mx_argmax_for(int T) {
+    switch (T) {
+    case 1: return qgemv_mx_argmax_kernel<FMT, 1>;
+    case 2: return qgemv_mx_argmax_kernel<FMT, 2>;
+    case 3: return qgemv_mx_argmax_kernel<FMT, 3>;
+    default: return qgemv_mx_argmax_kernel<FMT, 4>;
+    }
+}
+
+int launch_mx(int fmt, int T, const Tile& tile, const DenseArgs& a, void* stream) {
+    const int nsl = (int)(a.cols / kHalfSlice);
+    if (a.cols % kHalfSlice || tile.waves_per_wg % nsl) return (int)hipErrorInvalidValue;
+    const DmaFn fn = fmt == QG_FMT_Q8_0 ? mx_for<QG_FMT_Q8_0>(T) : fmt == QG_FMT_Q4_0 ? mx_for<QG_FMT_Q4_0>(T)
+                                                                                    : mx_for<QG_FMT_BF16>(T);
+    const int64_t nwg = (a.rows + tile.rows_per_wg - 1) / tile.rows_per_wg;
+    hipLaunchKernelGGL(fn, dim3((unsigned)nwg), dim3(64 * tile.waves_per_wg), mx_lds_bytes(fmt, tile, T, nsl),
+                       (hipStream_t)stream, a.W, a.x, a.y, a.rows, a.row_bytes, a.cols, nsl, a.rows_per_wg,
+                       tile.waves_per_wg);
+    return (int)hipGetLastError();
+}
+
 int launch_half(int fmt, int T, const Tile& tile, const DenseArgs& a, void* stream) {
     const int nsl = (int)(a.cols / kHalfSlice);
     if (tile.rows_per_batch != 4 || a.cols % kHalfSlice || tile.waves_per_wg % nsl) return (int)hipErrorInvalidValue;
@@ -2334,7 +2609,14 @@ int launch_argmax(int fmt, int T, const Tile& tile, const DenseArgs& a_in, void*
     int64_t nwg = 0;
     size_t lds = 0;
     DenseArgs a = a_in;
-    if (tile.kind == 7 && tile.rows_per_batch == 4 && a.cols % kHalfSlice == 0 &&
+    if (tile.kind == 8 && a.cols % kHalfSlice == 0 && tile.waves_per_wg % (a.cols / kHalfSlice) == 0) {
+        a.nslices = a.cols / kHalfSlice;  // 256-wide slices
+        fn = fmt == QG_FMT_Q8_0 ? mx_argmax_for<QG_FMT_Q8_0>(T)
+           : fmt == QG_FMT_Q4_0 ? mx_argmax_for<QG_FMT_Q4_0>(T)
+                                : mx_argmax_for<QG_FMT_BF16>(T);
+        nwg = (a.rows + tile.rows_per_wg - 1) / tile.rows_per_wg;
+        lds = mx_lds_bytes(fmt, tile, T, a.nslices);
+    } else if (tile.kind == 7 && tile.rows_per_batch == 4 && a.cols % kHalfSlice == 0 &&
         tile.waves_per_wg % (a.cols / kHalfSlice) == 0) {
         a.nslices = a.cols / kHalfSlice;  // 256-wide slices
         fn = fmt == QG_FMT_Q8_0 ? half_argmax_for<QG_FMT_Q8_0>(T, tile.depth)

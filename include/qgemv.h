@@ -60,6 +60,11 @@
  *   h<D>  direct-to-LDS loads on 256-wide k slices with 16 lanes per row, D = 2
  *         or 3 tiles in flight per wave; rb 4, cols a multiple of 256, nw a
  *         multiple of cols/256 (at most 12 slices); all three formats;
+ *   x     matrix cores on 256-wide k slices: 16-row tiles streamed by direct-to-LDS
+ *         loads, one in flight per wave, each block contracted as one bf16 matrix
+ *         product against an exact three-piece split of x; rb only sets which
+ *         rw are valid, cols a multiple of 256, nw a multiple of cols/256; all
+ *         three formats;
  *   m     as s, contracted on the matrix cores; Q8_0 with rb 8 only;
  *   p     m in persistent form: one workgroup per CU, nw = the k slices, rw =
  *         the chunk of rows whose partial sums are buffered.
@@ -239,8 +244,10 @@ int qg_unpack_q4_0(int64_t rows, int64_t cols, const void* in, uint16_t* d_bits,
  * (kind 0: direct loads, 1: streamed through LDS via registers, 2 / 3: streamed
  * by direct-to-LDS loads with `depth` tiles in flight per wave (3: x staged
  * apart), 4: unit-balanced direct-to-LDS, 7: direct-to-LDS on 256-wide k slices
- * with 16 lanes per row (any format; k_slice 256, lanes_per_row 16); mfma 1:
- * matrix-core contraction, 2: its persistent form). */
+ * with 16 lanes per row (any format; k_slice 256, lanes_per_row 16), 8: matrix
+ * cores on 256-wide k slices fed by direct-to-LDS loads (any format; k_slice 256,
+ * lanes_per_row 4: a row's 32-weight block is spread over 4 lanes); mfma 1:
+ * matrix-core contraction of kind 1, 2: its persistent form). */
 int qg_query_tile(int fmt, int64_t rows, int64_t cols, int T, int out_tile[QG_TILE_FIELDS]);
 
 /* Static description of a status code (never NULL). */

@@ -165,14 +165,14 @@ def test_argmax_argument_errors(lib, args, status):
 def test_tile_query_and_override(lib, monkeypatch):
     monkeypatch.delenv("QGEMV_TILE", raising=False)
     t = ops.query_tile("q8_0", 10240, 2560, 1)
-    # the 256-wide k slices of the half-slice kind: 16 lanes per row, one wave per slice
-    assert (t["kind"], t["lanes_per_row"], t["k_slice"], t["waves_per_wg"]) == (7, 16, 256, 10)
+    # matrix cores on 256-wide k slices, one wave per slice (a row's block spread over 4 lanes)
+    assert (t["kind"], t["lanes_per_row"], t["k_slice"], t["waves_per_wg"]) == (8, 4, 256, 10)
     # the k split must not depend on T (bit-identical tokens across T): waves
     # that each reduce one slice (streamed kinds; direct with waves >= slices)
     # or the same number of slice-looping waves
     def k_split(t, cols):
         nsl = -(-cols // t["k_slice"])
-        return (t["k_slice"], nsl if t["kind"] in (1, 7) else min(t["waves_per_wg"], nsl))
+        return (t["k_slice"], nsl if t["kind"] in (1, 7, 8) else min(t["waves_per_wg"], nsl))
     for fmt in ("q8_0", "q4_0", "bf16"):
         for rows, cols in ((10240, 2560), (2560, 6144), (248320, 5120), (8192, 2560), (7, 65536)):
             # the Q8_0 LM head runs the VALU kernel at T <= 2 and the matrix cores at T >= 3
@@ -213,7 +213,8 @@ def test_header_names_every_tile_kind(lib, monkeypatch):
     probes = {"d": ("d", 10240, 2560, "2,5,8"), "s": ("s", 10240, 2560, "4,5,16"),
               "l": ("l2", 10240, 2560, "4,5,40"), "L": ("L2", 10240, 2560, "4,5,40"),
               "u": ("u2", 10240, 2560, "4,4,40"), "h": ("h2", 10240, 2560, "4,10,40"),
-              "m": ("m", 10240, 2560, "8,5,32"), "p": ("p", 248320, 5120, "8,10,64")}
+              "m": ("m", 10240, 2560, "8,5,32"), "p": ("p", 248320, 5120, "8,10,64"),
+              "x": ("x", 10240, 2560, "4,10,40")}
     accepted = set()
     for letter in "abcdefghijklmnopqrstuvwxyzABCDEFGHIJKLMNOPQRSTUVWXYZ":
         suffix, rows, cols, head = probes.get(letter, (letter, 10240, 2560, "4,10,40"))

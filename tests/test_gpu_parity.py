@@ -296,6 +296,91 @@ def test_half_slice_tiny_and_dyadic(torch, orc, monkeypatch):
     assert np.array_equal(y.astype(np.float64), ref)
 
 
+# ------------------------------------ matrix cores on 256-wide slices (kind x)
+def mx_tile(cols, rw=40, rg=1, fmt="q8_0"):
+    return f"{fmt}:4,{(cols // 256) * rg},{rw},x"
+
+
+@pytest.mark.parametrize("name,rw", [("c2a_q8_0_10240x2560", 40), ("c2a_q8_0_10240x2560", 32),
+                                     ("c1_q8_0_2560x2560", 16), ("c3_q4_0_8192x2560", 32),
+                                     ("c3_bf16_8192x2560", 32), ("c3_bf16_8192x2560", 40)])
+def test_mx_config_full(torch, orc, monkeypatch, name, rw):
+    """Matrix cores on 256-wide slices on the workloads: parity at every T, a token's bits equal across T."""
+    c = I.dense_case(name)
+    monkeypatch.setenv("QGEMV_TILE", mx_tile(c["cols"], rw, fmt=NAMES[c["fmt"]]))
+    st, t = _lib.qg_query_tile(c["fmt"], c["rows"], c["cols"], 4)
+    assert st == 0 and t[6] == 8 and t[3] == 256, (st, t)
+    check_dense(torch, orc, c["fmt"], c["rows"], c["cols"], c["W"], c["x"], f"mx {name} rw={rw}")
+
+
+def test_mx_row_tilings_keep_bits(torch, monkeypatch):
+    """The same 256-wide k split at any rows per workgroup and row groups: identical bits."""
+    c = I.dense_case("c2a_q8_0_10240x2560")
+    Wd, xd = dev(torch, c["W"]), dev(torch, c["x"])
+    monkeypatch.setenv("QGEMV_TILE", mx_tile(c["cols"], 48))
+    base = ops.gemv("q8_0", Wd, xd, c["rows"]).cpu().numpy()
+    for rw in (16, 24, 40, 64, 200):
+        monkeypatch.setenv("QGEMV_TILE", mx_tile(c["cols"], rw))
+        say(f"[mx tiling] rw={rw}")
+        assert np.array_equal(ops.gemv("q8_0", Wd, xd, c["rows"]).cpu().numpy(), base), rw
+
+
+def test_mx_tiny_ragged_and_row_groups(torch, orc, monkeypatch):
+    """Ragged rows (a partial last 16-row tile, waves with no tile), one to twelve
+    slices, two and three row groups, every format."""
+    for fmt in (Q8, Q4, BF):
+        for rows in TINY_ROWS + (40, 100):
+            for cols in (256, 512, 768, 1280, 2304, 3072):
+                for rw, rg in ((16, 1), (40, 1), (24, 2), (48, 3)):
+                    monkeypatch.setenv("QGEMV_TILE", mx_tile(cols, rw, rg, NAMES[fmt]))
+                    if _lib.qg_query_tile(fmt, rows, cols, 4)[0]:
+                        continue  # more than twelve waves, or past the LDS
+                    rng = np.random.default_rng(rows * 1000 + cols + rw + fmt)
+                    W = I.weights(rng, fmt, rows, cols)
+                    x = I.activations(rng, cols)
+                    check_dense(torch, orc, fmt, rows, cols, W, x, f"mx tiny rw={rw} rg={rg}")
+
+
+def test_mx_exact_inputs_bitwise(torch, orc, monkeypatch):
+    """Inputs whose exact result is representable: dyadic weights and x (every partial
+    sum a multiple of 2^-6 below 2^20), and identity-like matrices (y = a permutation
+    of x, whose 24-bit significands the three bf16 pieces carry exactly)."""
+    rng = np.random.default_rng(97)
+    for fmt, rows, cols in ((Q8, 1000, 2816), (Q4, 777, 2560), (Q8, 10240, 2560)):
+        W = dyadic_weights(rng, fmt, rows, cols)
+        x = (rng.integers(-4, 5, (4, cols)) / 4.0).astype(np.float32)
+        monkeypatch.setenv("QGEMV_TILE", mx_tile(cols, 40, fmt=NAMES[fmt]))
+        y = gpu_gemv(torch, fmt, dev(torch, W), x, rows)
+        ref, _ = orc.gemv(fmt, rows, cols, W, x)
+        assert np.array_equal(y.astype(np.float64), ref), (fmt, rows, cols)
+    for fmt, n in ((Q8, 256), (Q8, 1024), (Q4, 1024)):
+        perm = rng.permutation(n)
+        d = np.full((n, n // 32), 0x3C00, dtype=np.uint16)
+        if fmt == Q8:
+            codes = np.zeros((n, n), dtype=np.int8)
+            codes[np.arange(n), perm] = 1
+            W = I.pack_q8_0(d, codes)
+        else:
+            codes = np.full((n, n), 8, dtype=np.uint8)
+            codes[np.arange(n), perm] = 9
+            W = I.pack_q4_0(d, codes)
+        mant = rng.integers(1 << 23, 1 << 24, (4, n)).astype(np.float64)
+        x = (mant * 2.0 ** rng.integers(-60, 20, (4, n)) * rng.choice([-1, 1], (4, n))).astype(np.float32)
+        monkeypatch.setenv("QGEMV_TILE", mx_tile(n, 16, fmt=NAMES[fmt]))
+        y = gpu_gemv(torch, fmt, dev(torch, W), x, n)
+        assert np.array_equal(y, x[:, perm]), (fmt, n)
+    n = 512  # BF16 identity
+    perm = rng.permutation(n)
+    dense = np.zeros((n, n), dtype=np.float32)
+    dense[np.arange(n), perm] = 1.0
+    W = (dense.view(np.uint32) >> 16).astype(np.uint16).view(np.uint8).reshape(-1)
+    mant = rng.integers(1 << 23, 1 << 24, (4, n)).astype(np.float64)
+    x = (mant * 2.0 ** rng.integers(-60, 20, (4, n)) * rng.choice([-1, 1], (4, n))).astype(np.float32)
+    monkeypatch.setenv("QGEMV_TILE", mx_tile(n, 16, fmt="bf16"))
+    y = gpu_gemv(torch, BF, dev(torch, W), x, n)
+    assert np.array_equal(y, x[:, perm])
+
+
 def test_tile_override_other_k_split(torch, orc, monkeypatch):
     c = I.dense_case("c2b_q8_0_2560x6144")
     monkeypatch.setenv("QGEMV_TILE", "q8_0:2,4,16")  # 12 slices over 4 waves
@@ -425,10 +510,14 @@ def test_argmax_ties_negatives_and_kinds(torch, orc, monkeypatch):
                 W[r * rb:(r + 1) * rb] = W[best * rb:(best + 1) * rb]
         neg = -np.abs(x)  # a second activation pattern
         for kind_tile in (None, "q8_0:4,{nsl},40,l3", "q8_0:4,{nsl},48,L2", "q8_0:4,{nsl},16,s", "q8_0:2,{nsl},4,d",
-                          "q8_0:8,{nsl},64,p"):
-            nsl = -(-cols // 512)
+                          "q8_0:8,{nsl},64,p", "q8_0:4,{nsl256},40,x", "q8_0:4,{nsl256},24,h2"):
+            nsl, nsl256 = -(-cols // 512), cols // 256
+            if "{nsl256}" in (kind_tile or "") and cols % 256:
+                continue  # 256-wide slices
             if kind_tile:
-                monkeypatch.setenv("QGEMV_TILE", kind_tile.format(nsl=nsl))
+                kind_tile = kind_tile.format(nsl=nsl, nsl256=nsl256)
+            if kind_tile:
+                monkeypatch.setenv("QGEMV_TILE", kind_tile)
             else:
                 monkeypatch.delenv("QGEMV_TILE", raising=False)
             if kind_tile and cols % 256 and not kind_tile.endswith(",d"):
@@ -510,12 +599,14 @@ def grouped_check(torch, orc, fmt, n_experts, rows, cols, ids, W, x, what):
     return y
 
 
-def test_grouped_config(torch, orc):
+def test_grouped_config(torch, orc, monkeypatch):
     g = I.grouped_case()
     y = grouped_check(torch, orc, g["fmt"], g["n_experts"], g["rows"], g["cols"], g["ids"], g["W"], g["x"], "c5")
-    # equals the plain kernel on each selected expert, bit for bit
+    # equals the plain call on each selected expert bit for bit, run on the vector-ALU
+    # LDS-DMA kind the grouped kernel shares its arithmetic with (512-wide k slices)
     rb = I.packed_row_bytes(g["fmt"], g["cols"])
     Wd = dev(torch, g["W"])
+    monkeypatch.setenv("QGEMV_TILE", f"{NAMES[g['fmt']]}:4,{g['cols'] // 512},24,L2")
     for t in range(g["T"]):
         for j in (0, g["topk"] - 1):
             e = int(g["ids"][t, j])
