@@ -62,9 +62,9 @@ bool parse_tile_spec(const std::string& spec, Tile* t, std::string* why) {
         got = sscanf(spec.c_str(), f, &rb, &nw, &rw, &depth, &tail2) == 4 ? 4 : -1;
     }
     const bool dma = kind == 'l' || kind == 'L' || kind == 'u' || kind == 'h';
-    if (!(got == 3 ||
-          (got == 4 && (kind == 'd' || kind == 's' || kind == 'm' || kind == 'p' || kind == 'x' || (dma && depth > 0))))) {
-        *why = "tile '" + spec + "' is not rb,nw,rw[,d|s|m|p|x|l<depth>|L<depth>|u<depth>|h<depth>]";
+    if (!(got == 3 || (got == 4 && (kind == 'd' || kind == 's' || kind == 'm' || kind == 'p' || kind == 'x' ||
+                                     kind == 'P' || (dma && depth > 0))))) {
+        *why = "tile '" + spec + "' is not rb,nw,rw[,d|s|m|p|x|P|l<depth>|L<depth>|u<depth>|h<depth>]";
         return false;
     }
     if (!valid_rb(rb) || nw < 1 || nw > kMaxWaves || rw < 2 * rb || rw % (2 * rb) || rw > (1 << 20)) {
@@ -75,10 +75,10 @@ bool parse_tile_spec(const std::string& spec, Tile* t, std::string* why) {
     t->waves_per_wg = nw;
     t->rows_per_wg = rw;
     t->kind = got == 4 ? (kind == 'd' ? 0 : kind == 'l' ? 2 : kind == 'L' ? 3 : kind == 'u' ? 4 : kind == 'h' ? 7
-                          : kind == 'x' ? 8 : 1)
+                          : kind == 'x' ? 8 : kind == 'P' ? 9 : 1)
                        : -1;  // -1: later
     t->mfma = got == 4 && kind == 'm' ? 1 : got == 4 && kind == 'p' ? 2 : 0;
-    t->depth = got == 4 && dma ? depth : got == 4 && kind == 'x' ? 1 : 0;
+    t->depth = got == 4 && dma ? depth : got == 4 && (kind == 'x' || kind == 'P') ? 1 : 0;
     return true;
 }
 
@@ -111,17 +111,13 @@ const TuneEntry kTuned[] = {
     {QG_FMT_Q4_0, 8192, 2560, 0, "4,10,32,x"},
     {QG_FMT_BF16, 8192, 2560, 0, "4,10,32,x"},
     {QG_FMT_Q8_0, 2560, 6144, 0, "4,12,16,s"},     // register-streamed beats DMA at 12 slices
-    // LM head: the LDS-DMA VALU kernel at T <= 2 (233 / 241 µs against 249 / 256
-    // for the matrix cores), the persistent matrix-core kernel at T >= 3 (267 / 275
-    // µs against 285 / 311).  A token's bits agree across T = 1, 2 and across
-    // T = 3, 4, not between the two pairs; a caller who needs one kind for all T
-    // pins it with QGEMV_TILE.  512 rows per workgroup (485 workgroups): the same
-    // time as 64 at T = 1 and 3 µs less at T = 2, and an eighth of the fused
-    // argmax's per-workgroup merges (239 / 247 µs against 250 / 253).
-    {QG_FMT_Q8_0, 248320, 5120, 1, "4,10,512,l2"},
-    {QG_FMT_Q8_0, 248320, 5120, 2, "4,10,512,l2"},
-    {QG_FMT_Q8_0, 248320, 5120, 3, "8,10,64,p"},
-    {QG_FMT_Q8_0, 248320, 5120, 4, "8,10,64,p"},
+    // LM head, 248,320 x 5,120 Q8_0: the persistent matrix-core kernel on the
+    // LDS-DMA ring, one kind at every T, so a token's bits do not depend on T:
+    // 234 / 237 / 241 / 245 µs at T = 1..4 against 234 / 243 / 269 / 279 for the
+    // best earlier kinds (the LDS-DMA vector-ALU ring at T <= 2, the persistent
+    // matrix cores with x in registers at T >= 3).  Chunks of 3 or 4 tiles time
+    // alike; 2 tiles cost 1-4 µs.
+    {QG_FMT_Q8_0, 248320, 5120, 0, "4,10,48,P"},
 };
 
 Tile default_tile(int fmt, int64_t rows, int64_t cols, int T) {
@@ -135,6 +131,21 @@ Tile default_tile(int fmt, int64_t rows, int64_t cols, int T) {
         std::string why;
         if (e.fmt == fmt && e.rows == rows && e.cols == cols && (e.T == 0 || e.T == T) && parse_tile_spec(e.tile, &t, &why))
             return t;
+    }
+    // Q8_0 matrices far beyond the 256 MB last-level cache, up to 12 512-wide
+    // slices: the persistent matrix cores on the LDS-DMA ring, chunks of 3 tiles
+    // (151,936 x 3,584: 105 / 108 / 110 / 112 µs at T = 1..4 against 116 / 126 /
+    // 144 / 162; at 65,536 x 5,120, 357 MB, it still loses at T <= 2)
+    if (fmt == QG_FMT_Q8_0 && rows * row_bytes(fmt, cols) >= (int64_t)512 << 20 && cols % kSlice == 0 &&
+        nslices <= kMaxWaves) {
+        t.kind = 9;
+        t.depth = 1;
+        t.rows_per_batch = 4;
+        t.waves_per_wg = (int)nslices;
+        t.rows_per_wg = 48;
+        if (mxp_lds_bytes(fmt, t, T) <= kMaxLds) return t;
+        t.kind = 0;
+        t.depth = 0;
     }
     // up to 12 256-wide slices: the matrix cores, one wave per slice, about one
     // workgroup per CU in whole 16-row tiles (the tuned shapes above follow this)
@@ -255,6 +266,19 @@ int pick_tile(int fmt, int64_t rows, int64_t cols, int T, Tile* t) {
                         units_lds_bytes(fmt, *t, T, cols), t->rows_per_wg, t->depth);
         return QG_OK;
     }
+    if (t->kind == 9) {
+        if (cols % kSlice || t->waves_per_wg != nslices)
+            return fail(QG_EINVAL, "persistent matrix-core ring tile needs cols a multiple of 512 and waves_per_wg == "
+                                   "the %lld 512-wide slices", (long long)nslices);
+        if (t->rows_per_wg % 16)
+            return fail(QG_EINVAL, "persistent matrix-core ring tile needs rows_per_wg (the chunk) a multiple of 16");
+        if (row_bytes(fmt, cols) * 16 > 0x7FFFFFFF)
+            return fail(QG_EINVAL, "persistent matrix-core ring tile needs 16 rows within a 2 GB descriptor");
+        if (mxp_lds_bytes(fmt, *t, T) > kMaxLds)
+            return fail(QG_EINVAL, "tile needs %zu B of LDS (rows_per_wg %d too large)", mxp_lds_bytes(fmt, *t, T),
+                        t->rows_per_wg);
+        return QG_OK;
+    }
     if (t->kind == 8) {
         const int64_t nsl256 = cols / 256;
         if (cols % 256 || t->waves_per_wg % nsl256 != 0)
@@ -364,7 +388,8 @@ int run_dense(int fmt, int64_t rows, int64_t cols, int T, const void* W, const f
     a.nslices = (int)((cols + kSlice - 1) / kSlice);
     a.rows_per_wg = tile.rows_per_wg;
     if ((rows + tile.rows_per_wg - 1) / tile.rows_per_wg > 0x7FFFFFFF) return fail(QG_EUNSUPPORTED, "grid too large");
-    int err = tile.kind == 8   ? launch_mx(fmt, T, tile, a, stream)
+    int err = tile.kind == 9   ? launch_mxp(fmt, T, tile, a, stream)
+              : tile.kind == 8 ? launch_mx(fmt, T, tile, a, stream)
               : tile.kind == 7 ? launch_half(fmt, T, tile, a, stream)
               : tile.kind == 4 ? launch_units(fmt, T, tile, a, stream)
               : tile.kind >= 2 ? launch_dma(fmt, T, tile, a, stream)
@@ -404,6 +429,7 @@ int run_argmax(int fmt, int64_t rows, int64_t cols, int T, const void* W, const 
     }
     if (tile.kind == 7 && half_lds_bytes(fmt, tile, T, (int)(cols / 256)) > kMaxLds) tile.kind = 0;
     if (tile.kind == 8 && mx_lds_bytes(fmt, tile, T, (int)(cols / 256)) > kMaxLds) tile.kind = 0;
+    if (tile.kind == 9 && mxp_lds_bytes(fmt, tile, T) > kMaxLds) tile.kind = 0;
     if (tile.kind == 4 || (tile.kind == 1 && tile.mfma == 1)) tile.kind = 0;
     if (tile.kind == 1 && !persist && (tile.rows_per_batch != 4 || !stream_supported(fmt, T, 4))) tile.kind = 0;
     if (tile.kind == 0) {  // direct, rb 2, one wave per slice when the slices fit a workgroup
@@ -739,7 +765,7 @@ int qg_query_tile(int fmt, int64_t rows, int64_t cols, int T, int out_tile[QG_TI
     int st = pick_tile(fmt, rows, cols, T, &t);
     if (st) return st;
     const bool half = t.kind == 7 || t.kind == 8;  // 256-wide k slices
-    out_tile[0] = t.kind == 8 ? 4 : half ? 16 : t.lanes_per_row;  // kind 8: a row's block sits in 4 lanes
+    out_tile[0] = t.kind >= 8 ? 4 : half ? 16 : t.lanes_per_row;  // kinds 8, 9: a row's block sits in 4 lanes
     out_tile[1] = t.rows_per_batch;
     out_tile[2] = t.waves_per_wg;
     out_tile[3] = half ? 256 : t.k_slice;

@@ -22,7 +22,8 @@ struct Tile {
                          // x staged in the ring's last slots; 3: as 2, x staged in its own region;
                          // 4: unit-balanced LDS-DMA (waves take equal shares of (slice, tile) units);
                          // 7: LDS-DMA on 256-wide k slices, 16 lanes per row; 8: matrix cores on
-                         // 256-wide k slices fed by LDS-DMA loads of 16-row tiles
+                         // 256-wide k slices fed by LDS-DMA loads of 16-row tiles; 9: persistent
+                         // matrix cores on 512-wide slices fed by LDS-DMA loads
     int depth;           // kinds 2, 3: tiles in flight per wave (2, 3, 4 or 6); kind 4: 2..4; kind 7: 2, 3; 0 otherwise
 };
 
@@ -113,6 +114,19 @@ inline size_t mx_lds_bytes(int fmt, const Tile& t, int T, int nslices256) {
            ntiles * nslices256 * 16 * pad_tokens(T) * 4;
 }
 
+// Kind 9 (persistent matrix cores on 512-wide slices): one 16-row tile slot per wave
+// (the tile's bytes, at least 8 KB: x and its pieces are staged in it first), two chunk
+// buffers of rows_per_wg / 16 tiles of partial sums [2][C][slices][16][pad(T)],
+// four control words.
+inline size_t mxp_slot_bytes(int fmt) {
+    const size_t tile = (size_t)16 * stream_chunks(fmt) * 16;
+    return tile > 8192 ? tile : 8192;
+}
+inline size_t mxp_lds_bytes(int fmt, const Tile& t, int T) {
+    return (size_t)t.waves_per_wg * mxp_slot_bytes(fmt) +
+           (size_t)2 * (t.rows_per_wg / 16) * t.waves_per_wg * 16 * pad_tokens(T) * 4 + 16;
+}
+
 // Row-subset kernel: rings of `depth` 8-row slots per wave, then partial sums (x in registers).
 inline size_t gather_lds_bytes(int fmt, const Tile& t, int T, int nslices) {
     const size_t ntiles = (size_t)(t.rows_per_wg + 2 * t.rows_per_batch - 1) / (2 * t.rows_per_batch);
@@ -190,6 +204,7 @@ int launch_dma(int fmt, int T, const Tile& tile, const DenseArgs& a, void* strea
 int launch_units(int fmt, int T, const Tile& tile, const DenseArgs& a, void* stream);
 int launch_half(int fmt, int T, const Tile& tile, const DenseArgs& a, void* stream);
 int launch_mx(int fmt, int T, const Tile& tile, const DenseArgs& a, void* stream);
+int launch_mxp(int fmt, int T, const Tile& tile, const DenseArgs& a, void* stream);
 // Fused argmax: fills work (uint64[T]), runs the mat-vec, writes idx/val (3 launches).
 int launch_argmax(int fmt, int T, const Tile& tile, const DenseArgs& a, void* work, int32_t* idx, float* val,
                   void* stream);

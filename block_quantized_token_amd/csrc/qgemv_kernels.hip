@@ -1623,19 +1623,24 @@ __device__ __forceinline__ uint32_t mx_byte_f32(const uint32_t (&w)[3], int q) {
     return __builtin_bit_cast(uint32_t, (float)(int32_t)(int8_t)(w[q >> 2] >> (8 * (q & 3))));
 }
 
-// The B fragment of block b for lane (row n, k group g): 8 codes as bf16 pairs,
-// and the block's scale of that row (Q4_0: d / 16).  Q8_0 / Q4_0 blocks of an
-// even index start 2 bytes past a dword, so their codes are read as an aligned
-// 12-byte window whose bytes 2..9 are taken (the byte positions are constants
-// after unrolling).
+// The bytes of block b that lane (row n, k group g) needs, as read from the
+// LDS: Q8_0 / Q4_0 blocks of an even index start 2 bytes past a dword, so their
+// codes are read as an aligned 12-byte window whose bytes 2..9 are taken (odd
+// blocks: an 8-byte window); BF16: the 16 bytes of the lane's 8 codes.  `d`
+// holds the block's fp16 scale bits.
+struct MxRaw {
+    uint32_t w[4];
+    uint32_t d;
+};
+
 template <int FMT>
-__device__ __forceinline__ V4 mx_bfrag(const uint8_t* rowp, int b, int g, float& d) {
+__device__ __forceinline__ MxRaw mx_braw(const uint8_t* rowp, int b, int g) {
     using M = MxShape<FMT>;
-    V4 r;
+    MxRaw r;
     if constexpr (FMT == QG_FMT_BF16) {
         const U4a q = *reinterpret_cast<const U4a*>(rowp + M::kBlockBytes * b + 16 * g);
-        r[0] = q.v[0]; r[1] = q.v[1]; r[2] = q.v[2]; r[3] = q.v[3];
-        d = 1.0f;
+        r.w[0] = q.v[0]; r.w[1] = q.v[1]; r.w[2] = q.v[2]; r.w[3] = q.v[3];
+        r.d = 0;
     } else {
         const uint8_t* blk = rowp + M::kBlockBytes * b;
         // Q8_0: the lane's codes are bytes 8g..8g+7 of the block's 32; Q4_0: the low
@@ -1643,7 +1648,23 @@ __device__ __forceinline__ V4 mx_bfrag(const uint8_t* rowp, int b, int g, float&
         const int cb = FMT == QG_FMT_Q8_0 ? 8 * g : 8 * (g & 1);
         const int sh = (b & 1) ? 0 : 2;  // where the codes start in the window
         const uint32_t* p = reinterpret_cast<const uint32_t*>(blk + 2 + cb - sh);
-        uint32_t w[3] = {p[0], p[1], sh ? p[2] : 0u};
+        r.w[0] = p[0]; r.w[1] = p[1]; r.w[2] = sh ? p[2] : 0u; r.w[3] = 0u;
+        r.d = *reinterpret_cast<const uint16_t*>(blk);
+    }
+    return r;
+}
+
+// The B fragment of block b from its bytes: 8 codes as bf16 pairs, and the
+// block's scale (Q4_0: d / 16; BF16: 1).
+template <int FMT>
+__device__ __forceinline__ V4 mx_bconv(const MxRaw& raw, int b, int g, float& d) {
+    V4 r;
+    if constexpr (FMT == QG_FMT_BF16) {
+        r[0] = raw.w[0]; r[1] = raw.w[1]; r[2] = raw.w[2]; r[3] = raw.w[3];
+        d = 1.0f;
+    } else {
+        const int sh = (b & 1) ? 0 : 2;
+        uint32_t w[3] = {raw.w[0], raw.w[1], raw.w[2]};
         if constexpr (FMT == QG_FMT_Q4_0) {
             // nibble c -> the signed byte 16 (c - 8): flip bit 3, move the nibble to the top
             const int ns = g >= 2 ? 0 : 4;
@@ -1655,10 +1676,16 @@ __device__ __forceinline__ V4 mx_bfrag(const uint8_t* rowp, int b, int g, float&
         for (int q = 0; q < 8; ++q) f[q] = mx_byte_f32(w, q + sh);
 #pragma unroll
         for (int q = 0; q < 4; ++q) r[q] = __builtin_amdgcn_perm(f[2 * q + 1], f[2 * q], 0x07060302u);
-        const float dv = half_bits_to_float(*reinterpret_cast<const uint16_t*>(blk));
+        const float dv = half_bits_to_float((uint16_t)raw.d);
         d = FMT == QG_FMT_Q4_0 ? dv * 0.0625f : dv;
     }
     return r;
+}
+
+// The B fragment of block b for lane (row n, k group g) and the block's scale.
+template <int FMT>
+__device__ __forceinline__ V4 mx_bfrag(const uint8_t* rowp, int b, int g, float& d) {
+    return mx_bconv<FMT>(mx_braw<FMT>(rowp, b, g), b, g, d);
 }
 
 template <int FMT, int NT, class Out>
@@ -1793,6 +1820,222 @@ __device__ __forceinline__ void mx_rows(const uint8_t* __restrict__ W, int64_t r
         for (int w = 1; w < nsl; ++w) sum = sum + base[(size_t)w * 16 * TP];
         out(tk, row_begin + rr, sum);
     }
+}
+
+// ----------------- persistent matrix cores on the LDS-DMA ring, 512-wide slices (kind 9)
+// For long matrices (the LM head): one workgroup per CU walks a contiguous range
+// of 16-row tiles, one wave per 512-wide k slice (16 blocks), with the
+// arithmetic of kind 8 per block.  A wave's slot holds one 16-row tile of its
+// slice; its bytes are read raw into registers (the conversion to bf16 waits
+// for the MFMAs, which keeps the registers within three waves per SIMD) and the
+// slot is refilled at once.  Before the first tile the slot stages x and its
+// bf16 pieces (two rounds of eight blocks), so the A fragments cost one pass
+// per wave and no LDS of their own.  Partial sums go to two chunk buffers of C
+// tiles; the wave that completes a chunk (an LDS arrival counter) adds its
+// slices in slice order and stores the outputs; a wave reuses a chunk buffer
+// only once its previous chunk has been summed (a generation count), and the
+// wave that sums never waits, so every wait ends.
+template <int FMT>
+struct MxpShape {
+    static constexpr int kChunks = StreamFmt<FMT>::kChunks;              // 16-byte chunks of a row slice: 34, 18, 64
+    static constexpr int kRow = 16 * kChunks;                             // 544, 288, 1024 B
+    static constexpr int kTile = 16 * kRow;                               // 8704, 4608, 16384 B
+    static constexpr int kSlot = kTile > 8192 ? kTile : 8192;             // x of four tokens fits too
+    static constexpr int kLoads = (16 * kChunks + 63) / 64;               // 9, 5, 16
+    static constexpr int kLastLanes = 16 * kChunks - 64 * (kLoads - 1);   // 32, 32, 64
+};
+
+// 16-row tile t of the wave's slice into its slot: lane l of load k fetches
+// chunk 64 k + l (row / chunk of the row slice); rows past the range are
+// outside the descriptor and read as zeros.
+template <int FMT>
+__device__ __forceinline__ void mxp_issue(const uint8_t* __restrict__ W, int64_t row_bytes, int64_t row_begin,
+                                          int64_t row_end, int t, const int (&off)[MxpShape<FMT>::kLoads],
+                                          uint8_t* slot, int lane) {
+    using M = MxpShape<FMT>;
+    const int64_t r0 = row_begin + (int64_t)t * 16;
+    const int64_t rows_here = row_end - r0 < 16 ? row_end - r0 : 16;
+    const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(W + r0 * row_bytes), (short)0, (int)(rows_here * row_bytes), kBufferRsrcWord3);
+#pragma unroll
+    for (int k = 0; k < M::kLoads - 1; ++k) load_lds16(rsrc, slot + 1024 * k, off[k]);
+    if (M::kLastLanes == 64 || lane < M::kLastLanes) load_lds16(rsrc, slot + 1024 * (M::kLoads - 1), off[M::kLoads - 1]);
+}
+
+// The MFMAs of the 16 blocks of one tile, from their bytes: acc += scale *
+// (pieces x codes) per block, in block order.
+template <int FMT>
+__device__ __forceinline__ void mxp_math(const V4 (&afrag)[16], const MxRaw (&raw)[16], int g, F4& acc) {
+#pragma unroll
+    for (int b = 0; b < 16; ++b) {
+        float dq;
+        const V4 bq = mx_bconv<FMT>(raw[b], b, g, dq);
+        if constexpr (FMT == QG_FMT_BF16) {
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(BF8, afrag[b]),
+                                                          __builtin_bit_cast(BF8, bq), acc, 0, 0, 0);
+        } else {
+            const F4 z = {0.0f, 0.0f, 0.0f, 0.0f};
+            const F4 dd = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(BF8, afrag[b]),
+                                                                  __builtin_bit_cast(BF8, bq), z, 0, 0, 0);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) acc[j] = __builtin_fmaf(dq, dd[j], acc[j]);
+        }
+    }
+}
+
+// The partial sums of one row for every token, read or written at once.
+template <int N>
+struct alignas(4 * N) Vec {
+    float v[N];
+};
+
+template <int FMT, int NT, class Out>
+__device__ __forceinline__ void mxp_rows(const uint8_t* __restrict__ W, int64_t rows, int64_t row_bytes, int cols,
+                                         int nsl, int C, const float* __restrict__ x, Out&& out) {
+    using M = MxpShape<FMT>;
+    constexpr int TP = pad_pow2(NT);
+    constexpr int L = M::kLoads;
+    static_assert(NT * 2048 <= M::kSlot && 1536 * NT <= M::kSlot, "x and its pieces are staged in the slot");
+    extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int nw = blockDim.x >> 6;  // == nsl: one wave per k slice
+    const int n = lane & 15, g = lane >> 4;
+    const int s = wave;
+    const int k0 = s * kSlice;
+    const int64_t TT = (rows + 15) / 16;
+    const int64_t t0 = (int64_t)blockIdx.x * TT / gridDim.x, t1 = (int64_t)(blockIdx.x + 1) * TT / gridDim.x;
+    const int64_t row_begin = t0 * 16;
+    const int64_t row_end = t1 * 16 < rows ? t1 * 16 : rows;
+    const int ntiles = (int)(t1 - t0);
+    uint8_t* slot = smem + wave * M::kSlot;
+    float* part = reinterpret_cast<float*>(smem + nw * M::kSlot);              // [2][C][nsl][16][TP]
+    int* ctl = reinterpret_cast<int*>(part + (size_t)2 * C * nsl * 16 * TP);   // arrivals[2], generation[2]
+    if (tid < 4) ctl[tid] = 0;
+
+    int off[L];
+#pragma unroll
+    for (int k = 0; k < L; ++k) {
+        const int j = 64 * k + lane;
+        const int r = j / M::kChunks, c = j % M::kChunks;
+        off[k] = r < 16 ? (int)(r * row_bytes) + s * M::kRow + 16 * c : kNoLoad;
+    }
+    // x of the slice into the slot (token t at 2048 t), then into registers: lane
+    // l takes k = 4 l .. 4 l + 3 of each 256-wide half
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+        const __amdgpu_buffer_rsrc_t xr =
+            __builtin_amdgcn_make_buffer_rsrc((void*)(x + (int64_t)t * cols + k0), (short)0, 2048, kBufferRsrcWord3);
+        load_lds16(xr, slot + 2048 * t, 16 * lane);
+        load_lds16(xr, slot + 2048 * t + 1024, 16 * lane + 1024);
+    }
+    wait_vmcnt<0>();
+    float4 xv[2][NT];
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int t = 0; t < NT; ++t) xv[h][t] = *reinterpret_cast<const float4*>(slot + 2048 * t + 1024 * h + 16 * lane);
+    V4 afrag[16];
+    {
+        const int b = lane >> 3, gg = (lane & 7) >> 1, half = (lane & 1) * 8;
+        const int am = lane & 15, ap = am >> 2, at = am & 3;
+        const bool arow = ap < 3 && at < NT;
+        const int idx = arow ? (g * 3 * NT + ap * NT + at) * 16 : 0;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            wait_lgkmcnt0();  // the slot's previous contents are read by every lane
+#pragma unroll
+            for (int t = 0; t < NT; ++t) {
+                const float vv[4] = {xv[h][t].x, xv[h][t].y, xv[h][t].z, xv[h][t].w};
+                uint32_t pc[3][4];
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const uint32_t v = __builtin_bit_cast(uint32_t, vv[q]);
+                    const float r1 = vv[q] - __builtin_bit_cast(float, v & 0xFFFF0000u);
+                    const uint32_t u1 = __builtin_bit_cast(uint32_t, r1);
+                    const float r2 = r1 - __builtin_bit_cast(float, u1 & 0xFFFF0000u);
+                    pc[0][q] = v;
+                    pc[1][q] = u1;
+                    pc[2][q] = __builtin_bit_cast(uint32_t, r2);
+                }
+#pragma unroll
+                for (int p = 0; p < 3; ++p) {
+                    uint2 w2;
+                    w2.x = __builtin_amdgcn_perm(pc[p][1], pc[p][0], 0x07060302u);
+                    w2.y = __builtin_amdgcn_perm(pc[p][3], pc[p][2], 0x07060302u);
+                    *reinterpret_cast<uint2*>(slot + b * (192 * NT) + (gg * 3 * NT + p * NT + t) * 16 + half) = w2;
+                }
+            }
+            wait_lgkmcnt0();
+#pragma unroll
+            for (int bb = 0; bb < 8; ++bb) {
+                const V4 v = *reinterpret_cast<const V4*>(slot + bb * (192 * NT) + idx);
+                afrag[8 * h + bb] = arow ? v : V4{0u, 0u, 0u, 0u};
+            }
+        }
+    }
+    wait_lgkmcnt0();  // the pieces are in registers: the slot takes the first tile
+    __syncthreads();  // (also publishes the cleared control words)
+    if (ntiles > 0) mxp_issue<FMT>(W, row_bytes, row_begin, row_end, 0, off, slot, lane);
+
+    const uint8_t* rowp = slot + n * M::kRow;
+    for (int c = 0; c * C < ntiles; ++c) {
+        const int pb = c & 1;
+        if (c >= 2) {  // chunk c - 2 (same buffer) must have been summed
+            while (__atomic_load_n(&ctl[2 + pb], __ATOMIC_ACQUIRE) < (c >> 1)) __builtin_amdgcn_s_sleep(1);
+        }
+        const int tend = (c + 1) * C < ntiles ? (c + 1) * C : ntiles;
+        for (int t = c * C; t < tend; ++t) {
+            wait_vmcnt<0>();  // the slot holds tile t
+            MxRaw raw[16];
+#pragma unroll
+            for (int b = 0; b < 16; ++b) raw[b] = mx_braw<FMT>(rowp, b, g);
+            wait_lgkmcnt0();  // the tile is in registers: the slot takes the next one
+            if (t + 1 < ntiles) mxp_issue<FMT>(W, row_bytes, row_begin, row_end, t + 1, off, slot, lane);
+            F4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+            mxp_math<FMT>(afrag, raw, g, acc);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                float mid = acc[j], lo = acc[j], junk16 = acc[j], junk32 = acc[j];
+                permlane16_swap(junk16, mid);
+                permlane32_swap(junk32, lo);
+                acc[j] = (acc[j] + mid) + lo;
+            }
+            if (lane < 16) {
+                float* pp = part + (((size_t)(pb * C + t - c * C) * nsl + s) * 16 + n) * TP;
+#pragma unroll
+                for (int j = 0; j < TP; ++j) pp[j] = acc[j];
+            }
+        }
+        // publish this wave's partials of chunk c, then count the arrival
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+        int last = 0;
+        if (lane == 0) last = __atomic_fetch_add(&ctl[pb], 1, __ATOMIC_ACQ_REL) == nw - 1;
+        last = __shfl(last, 0, 64);
+        if (last) {  // every wave's partials of chunk c are in: sum the slices in order
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+            const int64_t r0 = row_begin + (int64_t)c * C * 16;
+            const int nr = (int)((row_end - r0) < (int64_t)C * 16 ? (row_end - r0) : (int64_t)C * 16);
+            for (int rr = lane; rr < nr; rr += 64) {  // a lane per row, all tokens at once
+                const float* base = part + (((size_t)(pb * C + rr / 16) * nsl) * 16 + rr % 16) * TP;
+                Vec<TP> sum = *reinterpret_cast<const Vec<TP>*>(base);
+                for (int w = 1; w < nsl; ++w) {
+                    const Vec<TP> v = *reinterpret_cast<const Vec<TP>*>(base + (size_t)w * 16 * TP);
+#pragma unroll
+                    for (int tk = 0; tk < NT; ++tk) sum.v[tk] = sum.v[tk] + v.v[tk];
+                }
+#pragma unroll
+                for (int tk = 0; tk < NT; ++tk) out(tk, r0 + rr, sum.v[tk]);
+            }
+            if (lane == 0) {
+                __atomic_store_n(&ctl[pb], 0, __ATOMIC_RELAXED);
+                __atomic_fetch_add(&ctl[2 + pb], 1, __ATOMIC_RELEASE);
+            }
+        }
+    }
+    wait_vmcnt<0>();
 }
 
 // ------------------------------------------------------ fused argmax over rows
@@ -1978,6 +2221,21 @@ __global__ void __launch_bounds__(64 * kMaxWaves) qgemv_half_argmax_kernel(Dense
     const int64_t row_end = row_begin + a.rows_per_wg < a.rows ? row_begin + a.rows_per_wg : a.rows;
     ArgmaxOut<T> best;
     half_rows<FMT, T, D>(a.W, a.row_bytes, a.cols, a.nslices, a.x, row_begin, row_end, (int)(blockDim.x >> 6), best);
+    best.merge(work);
+}
+
+template <int FMT, int T>
+__global__ void __launch_bounds__(64 * kMaxWaves) qgemv_mxp_kernel(DenseArgs a) {
+    float* __restrict__ y = a.y;
+    const int64_t rows = a.rows;
+    mxp_rows<FMT, T>(a.W, a.rows, a.row_bytes, a.cols, a.nslices, a.rows_per_wg / 16, a.x,
+                     [=](int t, int64_t row, float v) { y[t * rows + row] = v; });
+}
+
+template <int FMT, int T>
+__global__ void __launch_bounds__(64 * kMaxWaves) qgemv_mxp_argmax_kernel(DenseArgs a, unsigned long long* work) {
+    ArgmaxOut<T> best;
+    mxp_rows<FMT, T>(a.W, a.rows, a.row_bytes, a.cols, a.nslices, a.rows_per_wg / 16, a.x, best);
     best.merge(work);
 }
 
@@ -2526,6 +2784,39 @@ ArgmaxFn mx_argmax_for(int T) {
     }
 }
 
+template <int FMT>
+DenseFn mxp_for(int T) {
+    switch (T) {
+    case 1: return qgemv_mxp_kernel<FMT, 1>;
+    case 2: return qgemv_mxp_kernel<FMT, 2>;
+    case 3: return qgemv_mxp_kernel<FMT, 3>;
+    default: return qgemv_mxp_kernel<FMT, 4>;
+    }
+}
+
+template <int FMT>
+ArgmaxFn mxp_argmax_for(int T) {
+    switch (T) {
+    case 1: return qgemv_mxp_argmax_kernel<FMT, 1>;
+    case 2: return qgemv_mxp_argmax_kernel<FMT, 2>;
+    case 3: return qgemv_mxp_argmax_kernel<FMT, 3>;
+    default: return qgemv_mxp_argmax_kernel<FMT, 4>;
+    }
+}
+
+int launch_mxp(int fmt, int T, const Tile& tile, const DenseArgs& a_in, void* stream) {
+    DenseArgs a = a_in;
+    a.nslices = (int)(a.cols / kSlice);
+    if (a.cols % kSlice || tile.waves_per_wg != a.nslices || tile.rows_per_wg % 16) return (int)hipErrorInvalidValue;
+    const DenseFn fn = fmt == QG_FMT_Q8_0 ? mxp_for<QG_FMT_Q8_0>(T) : fmt == QG_FMT_Q4_0 ? mxp_for<QG_FMT_Q4_0>(T)
+                                                                                      : mxp_for<QG_FMT_BF16>(T);
+    const int64_t tiles = (a.rows + 15) / 16;
+    const int64_t nwg = tiles < kPersistGrid ? tiles : kPersistGrid;
+    hipLaunchKernelGGL(fn, dim3((unsigned)nwg), dim3(64 * tile.waves_per_wg), mxp_lds_bytes(fmt, tile, T),
+                       (hipStream_t)stream, a);
+    return (int)hipGetLastError();
+}
+
 int launch_mx(int fmt, int T, const Tile& tile, const DenseArgs& a, void* stream) {
     const int nsl = (int)(a.cols / kHalfSlice);
     if (a.cols % kHalfSlice || tile.waves_per_wg % nsl) return (int)hipErrorInvalidValue;
@@ -2609,7 +2900,15 @@ int launch_argmax(int fmt, int T, const Tile& tile, const DenseArgs& a_in, void*
     int64_t nwg = 0;
     size_t lds = 0;
     DenseArgs a = a_in;
-    if (tile.kind == 8 && a.cols % kHalfSlice == 0 && tile.waves_per_wg % (a.cols / kHalfSlice) == 0) {
+    if (tile.kind == 9 && a.cols % kSlice == 0 && tile.waves_per_wg == a.cols / kSlice && tile.rows_per_wg % 16 == 0) {
+        a.nslices = a.cols / kSlice;
+        fn = fmt == QG_FMT_Q8_0 ? mxp_argmax_for<QG_FMT_Q8_0>(T)
+           : fmt == QG_FMT_Q4_0 ? mxp_argmax_for<QG_FMT_Q4_0>(T)
+                                : mxp_argmax_for<QG_FMT_BF16>(T);
+        const int64_t tiles = (a.rows + 15) / 16;
+        nwg = tiles < kPersistGrid ? tiles : kPersistGrid;
+        lds = mxp_lds_bytes(fmt, tile, T);
+    } else if (tile.kind == 8 && a.cols % kHalfSlice == 0 && tile.waves_per_wg % (a.cols / kHalfSlice) == 0) {
         a.nslices = a.cols / kHalfSlice;  // 256-wide slices
         fn = fmt == QG_FMT_Q8_0 ? mx_argmax_for<QG_FMT_Q8_0>(T)
            : fmt == QG_FMT_Q4_0 ? mx_argmax_for<QG_FMT_Q4_0>(T)

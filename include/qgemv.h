@@ -40,10 +40,9 @@
  *     so y[t] at T tokens equals y[t] at T' tokens bit for bit (the pages note
  *     that each token's sum should not depend on the token count: opus-mtp-
  *     turbo report, finding 3) when both calls run the same kind of kernel
- *     with the same k split.  The default tiles keep one kind for all T except
- *     on the 248,320 x 5,120 Q8_0 LM head, where the vector-ALU kernel is the
- *     faster at T <= 2 and the matrix cores at T >= 3 (bits agree within each
- *     pair); QGEMV_TILE pins one kind for every T.
+ *     with the same k split.  The default tiles keep one kind and one k split
+ *     for all T on every shape (the 248,320 x 5,120 Q8_0 LM head included);
+ *     QGEMV_TILE pins a kind for every T.
  *   - Accuracy: |y - exact| <= 1e-4 * sum_k |w_k * x_k| + 1e-6 per output
  *     (fp32 accumulation of exactly decoded weights).
  *
@@ -67,7 +66,12 @@
  *         three formats;
  *   m     as s, contracted on the matrix cores; Q8_0 with rb 8 only;
  *   p     m in persistent form: one workgroup per CU, nw = the k slices, rw =
- *         the chunk of rows whose partial sums are buffered.
+ *         the chunk of rows whose partial sums are buffered;
+ *   P     x in persistent form on 512-wide k slices: one workgroup per CU, one
+ *         16-row tile in flight per wave, nw = cols/512 (cols a multiple of
+ *         512, at most 12 slices), rw = the chunk of rows (a multiple of 16)
+ *         whose partial sums are buffered; rb only sets which rw are valid;
+ *         all three formats.
  * A malformed or out-of-set value makes every call of that format return
  * QG_EINVAL.
  */
@@ -246,7 +250,8 @@ int qg_unpack_q4_0(int64_t rows, int64_t cols, const void* in, uint16_t* d_bits,
  * apart), 4: unit-balanced direct-to-LDS, 7: direct-to-LDS on 256-wide k slices
  * with 16 lanes per row (any format; k_slice 256, lanes_per_row 16), 8: matrix
  * cores on 256-wide k slices fed by direct-to-LDS loads (any format; k_slice 256,
- * lanes_per_row 4: a row's 32-weight block is spread over 4 lanes); mfma 1:
+ * lanes_per_row 4: a row's 32-weight block is spread over 4 lanes), 9: kind 8 in
+ * persistent form on 512-wide k slices (k_slice 512, lanes_per_row 4); mfma 1:
  * matrix-core contraction of kind 1, 2: its persistent form). */
 int qg_query_tile(int fmt, int64_t rows, int64_t cols, int T, int out_tile[QG_TILE_FIELDS]);
 

@@ -6,7 +6,8 @@ The oracle runs once, at T = 4, over all rows: a token's oracle result does not
 depend on T (pinned on the CPU by test_oracle's T-prefix check), so y[:T] of that
 one run is the reference for every T.  Each kernel kind that can serve the head
 (the default tiles, the LDS-DMA vector-ALU ring, the register-streamed kernel, the
-per-workgroup and persistent matrix-core kernels) is compared output by output at
+per-workgroup and persistent matrix-core kernels, the persistent matrix-core
+kernel fed by the LDS-DMA ring) is compared output by output at
 T = 1..4, and the fused argmax against the tolerance-aware oracle rule at T = 1..4.
 """
 import sys
@@ -93,6 +94,7 @@ def test_default_tiles_every_output(torch, head, monkeypatch):
     ("4,10,32,s", "register-streamed"),
     ("8,10,192,m", "matrix cores per workgroup"),
     ("8,10,64,p", "persistent matrix cores"),
+    ("4,10,64,P", "persistent matrix cores on the LDS-DMA ring"),
 ])
 def test_kind_every_output_and_t_invariant(torch, head, monkeypatch, tile, what):
     ys = check_kind(torch, head, monkeypatch, tile, what)

@@ -381,6 +381,85 @@ def test_mx_exact_inputs_bitwise(torch, orc, monkeypatch):
     assert np.array_equal(y, x[:, perm])
 
 
+# ----------------- persistent matrix cores on 512-wide slices fed by the ring (kind P)
+def mxp_tile(cols, chunk=4, fmt="q8_0"):
+    return f"{fmt}:4,{cols // 512},{16 * chunk},P"
+
+
+@pytest.mark.parametrize("name,chunk", [("c2a_q8_0_10240x2560", 4), ("c1_q8_0_2560x2560", 2),
+                                        ("c2b_q8_0_2560x6144", 4), ("c3_q4_0_8192x2560", 4),
+                                        ("c3_bf16_8192x2560", 2)])
+def test_mxp_config_full(torch, orc, monkeypatch, name, chunk):
+    """The persistent ring kind on the workloads: parity at every T, a token's bits equal across T."""
+    c = I.dense_case(name)
+    monkeypatch.setenv("QGEMV_TILE", mxp_tile(c["cols"], chunk, NAMES[c["fmt"]]))
+    st, t = _lib.qg_query_tile(c["fmt"], c["rows"], c["cols"], 4)
+    assert st == 0 and t[6] == 9 and t[3] == 512, (st, t)
+    check_dense(torch, orc, c["fmt"], c["rows"], c["cols"], c["W"], c["x"], f"mxp {name} chunk={chunk}")
+
+
+def test_mxp_ragged_chunks_and_formats(torch, orc, monkeypatch):
+    """Ragged rows (a partial last tile; fewer tiles than workgroups; several tiles
+    and chunks per workgroup, so both chunk buffers are reused), one to twelve
+    slices, chunks of one to eight tiles, every format."""
+    for fmt in (Q8, Q4, BF):
+        for rows, cols in ((1, 512), (3, 1024), (17, 512), (67, 2560), (1000, 1536), (4096 + 37, 512),
+                           (20480 + 9, 1024), (777, 6144)):
+            for chunk in (1, 2, 8):
+                monkeypatch.setenv("QGEMV_TILE", mxp_tile(cols, chunk, NAMES[fmt]))
+                nw = cols // 512  # slots of max(tile, 8 KB), chunk buffers of 16 rows x pad(4) fp32 per slice
+                lds = nw * {Q8: 8704, Q4: 8192, BF: 16384}[fmt] + 2 * chunk * nw * 16 * 4 * 4 + 16
+                st = _lib.qg_query_tile(fmt, rows, cols, 4)[0]
+                assert (st == 0) == (lds <= 160 * 1024), (fmt, rows, cols, chunk, st)
+                if st:
+                    continue
+                rng = np.random.default_rng(rows * 1000 + cols + chunk + fmt)
+                W = I.weights(rng, fmt, rows, cols)
+                x = I.activations(rng, cols)
+                check_dense(torch, orc, fmt, rows, cols, W, x, f"mxp {rows}x{cols} chunk={chunk}")
+
+
+def test_mxp_chunks_keep_bits(torch, monkeypatch):
+    """The same 512-wide k split at any chunk size: identical bits."""
+    c = I.dense_case("c2a_q8_0_10240x2560")
+    Wd, xd = dev(torch, c["W"]), dev(torch, c["x"])
+    monkeypatch.setenv("QGEMV_TILE", mxp_tile(c["cols"], 4))
+    base = ops.gemv("q8_0", Wd, xd, c["rows"]).cpu().numpy()
+    for chunk in (1, 2, 3, 8):
+        monkeypatch.setenv("QGEMV_TILE", mxp_tile(c["cols"], chunk))
+        say(f"[mxp chunk] {chunk}")
+        assert np.array_equal(ops.gemv("q8_0", Wd, xd, c["rows"]).cpu().numpy(), base), chunk
+
+
+def test_mxp_exact_inputs_bitwise(torch, orc, monkeypatch):
+    """Dyadic inputs (exact result representable) and identity-like matrices (y = a
+    permutation of x, carried exactly by the three bf16 pieces)."""
+    rng = np.random.default_rng(98)
+    for fmt, rows, cols in ((Q8, 1000, 3072), (Q4, 777, 2560), (Q8, 10240, 2560)):
+        W = dyadic_weights(rng, fmt, rows, cols)
+        x = (rng.integers(-4, 5, (4, cols)) / 4.0).astype(np.float32)
+        monkeypatch.setenv("QGEMV_TILE", mxp_tile(cols, 2, NAMES[fmt]))
+        y = gpu_gemv(torch, fmt, dev(torch, W), x, rows)
+        ref, _ = orc.gemv(fmt, rows, cols, W, x)
+        assert np.array_equal(y.astype(np.float64), ref), (fmt, rows, cols)
+    for fmt, n in ((Q8, 512), (Q8, 1024), (Q4, 1024)):
+        perm = rng.permutation(n)
+        d = np.full((n, n // 32), 0x3C00, dtype=np.uint16)
+        if fmt == Q8:
+            codes = np.zeros((n, n), dtype=np.int8)
+            codes[np.arange(n), perm] = 1
+            W = I.pack_q8_0(d, codes)
+        else:
+            codes = np.full((n, n), 8, dtype=np.uint8)
+            codes[np.arange(n), perm] = 9
+            W = I.pack_q4_0(d, codes)
+        mant = rng.integers(1 << 23, 1 << 24, (4, n)).astype(np.float64)
+        x = (mant * 2.0 ** rng.integers(-60, 20, (4, n)) * rng.choice([-1, 1], (4, n))).astype(np.float32)
+        monkeypatch.setenv("QGEMV_TILE", mxp_tile(n, 1, NAMES[fmt]))
+        y = gpu_gemv(torch, fmt, dev(torch, W), x, n)
+        assert np.array_equal(y, x[:, perm]), (fmt, n)
+
+
 def test_tile_override_other_k_split(torch, orc, monkeypatch):
     c = I.dense_case("c2b_q8_0_2560x6144")
     monkeypatch.setenv("QGEMV_TILE", "q8_0:2,4,16")  # 12 slices over 4 waves
@@ -510,10 +589,13 @@ def test_argmax_ties_negatives_and_kinds(torch, orc, monkeypatch):
                 W[r * rb:(r + 1) * rb] = W[best * rb:(best + 1) * rb]
         neg = -np.abs(x)  # a second activation pattern
         for kind_tile in (None, "q8_0:4,{nsl},40,l3", "q8_0:4,{nsl},48,L2", "q8_0:4,{nsl},16,s", "q8_0:2,{nsl},4,d",
-                          "q8_0:8,{nsl},64,p", "q8_0:4,{nsl256},40,x", "q8_0:4,{nsl256},24,h2"):
+                          "q8_0:8,{nsl},64,p", "q8_0:4,{nsl256},40,x", "q8_0:4,{nsl256},24,h2",
+                          "q8_0:4,{nsl},32,P"):
             nsl, nsl256 = -(-cols // 512), cols // 256
             if "{nsl256}" in (kind_tile or "") and cols % 256:
                 continue  # 256-wide slices
+            if (kind_tile or "").endswith(",P") and cols % 512:
+                continue  # 512-wide slices
             if kind_tile:
                 kind_tile = kind_tile.format(nsl=nsl, nsl256=nsl256)
             if kind_tile:
