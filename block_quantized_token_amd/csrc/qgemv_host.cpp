@@ -526,7 +526,33 @@ int run_grouped(int fmt, int64_t n_experts, int64_t rows, int64_t cols, int T, i
     std::string why;
     Tile probe = tile;
     const bool overridden = tile_override(fmt, &probe, &why) == 1;
-    if (!overridden && row_bytes(fmt, cols) % 16 == 0 && nsl <= kMaxWaves) {
+    const int64_t nsl256 = cols / 256;
+    const bool mx_ok = cols % 256 == 0 && nsl256 <= kMaxWaves && rbytes * 16 < 0x7FFFFFFF;
+    if (!overridden && mx_ok) {
+        // the matrix cores on 256-wide slices (kind 8's tiles); fewer than 4 slices
+        // (the down projection's short rows): row groups of waves, 4 waves or more.
+        // Rows per workgroup: the fewest that keep all slots' workgroups within
+        // one per CU (256 experts of 512 x 2560 Q4_0, 10 slots a token, µs at
+        // T = 1..4: 32 rows 7.7 / 12.9 / 13.3 / 21.2, 48 rows 9.0 / 9.2 / 15.9 / 17.4,
+        // 64 rows 10.3 / 10.4 / 10.6 / 19.9, 96 rows 13.0 / 13.1 / 13.2 / 13.4: a
+        // second round of workgroups costs more than longer ones).
+        tile.kind = 8;
+        tile.depth = 1;
+        tile.mfma = 0;
+        tile.rows_per_batch = 4;
+        const int64_t rg = nsl256 >= 4 ? 1 : (4 + nsl256 - 1) / nsl256;
+        tile.waves_per_wg = (int)(nsl256 * rg);
+        const int64_t slots = (int64_t)T * topk * parts;
+        int64_t rw = 16 * rg;
+        while (rw < 512 && rw < rows && slots * ((rows + rw - 1) / rw) > kPersistGrid) rw += 16;
+        tile.rows_per_wg = (int)rw;
+        while (tile.rows_per_wg > 16 && mx_lds_bytes(fmt, tile, T, (int)nsl256) > kMaxLds) tile.rows_per_wg -= 16;
+    }
+    if (tile.kind == 8) {  // default or pinned: checked as the launch needs it, else the paths below
+        if (!mx_ok || tile.waves_per_wg % nsl256 || tile.rows_per_wg % 16 ||
+            mx_lds_bytes(fmt, tile, T, (int)nsl256) > kMaxLds)
+            tile.kind = 1;
+    } else if (!overridden && row_bytes(fmt, cols) % 16 == 0 && nsl <= kMaxWaves) {
         // LDS-DMA streamed, x staged apart (any number of tokens per expert fits
         // one ring of two slots).  Rows per workgroup: the workgroups of all
         // slots (at most T * topk distinct experts) fit in about one round of
@@ -551,7 +577,7 @@ int run_grouped(int fmt, int64_t n_experts, int64_t rows, int64_t cols, int T, i
         if (tile.depth != 3) tile.depth = 2;
         if (tile.waves_per_wg % nsl != 0 || dma_lds_bytes(fmt, tile, T, (int)nsl) > kMaxLds) tile.kind = 1;
     }
-    if (tile.kind != 0 && tile.kind != 3) {  // the grouped kernel runs the direct path: one wave per slice
+    if (tile.kind != 0 && tile.kind != 3 && tile.kind != 8) {  // the grouped kernel runs the direct path: one wave per slice
         tile.kind = 0;
         tile.depth = 0;
         tile.mfma = 0;

@@ -1585,7 +1585,9 @@ __device__ __forceinline__ void mfma_persist_q8(const uint8_t* __restrict__ W, i
 // touch another token's, so its bits do not depend on T; the work per tile does
 // not depend on T either.
 // The split is done once per wave and cooperatively: each lane splits four x
-// values of every token and the pieces reach the fragment layout through LDS.
+// values of every token and the pieces reach the fragment layout through LDS
+// (each lane loading the 64 values its fragments hold straight from memory
+// instead multiplies x's cache traffic by 16 and measured 20-50 % slower).
 // Each wave keeps one tile in flight, refilled as soon as the tile's bytes are
 // in registers; measured on 10240 x 2560, a second tile in flight or a refill
 // after the math is slower (the vector-ALU kernels behave alike).
@@ -1688,10 +1690,11 @@ __device__ __forceinline__ V4 mx_bfrag(const uint8_t* rowp, int b, int g, float&
     return mx_bconv<FMT>(mx_braw<FMT>(rowp, b, g), b, g, d);
 }
 
+// Token t's x is the row at x + xoff[t] (the dense path: t * cols).
 template <int FMT, int NT, class Out>
-__device__ __forceinline__ void mx_rows(const uint8_t* __restrict__ W, int64_t row_bytes, int cols, int nsl,
-                                        const float* __restrict__ x, int64_t row_begin, int64_t row_end, int nw,
-                                        Out&& out) {
+__device__ __forceinline__ void mx_rows(const uint8_t* __restrict__ W, int64_t row_bytes, int nsl,
+                                        const float* __restrict__ x, const int64_t (&xoff)[NT], int64_t row_begin,
+                                        int64_t row_end, int nw, Out&& out) {
     using M = MxShape<FMT>;
     constexpr int TP = pad_pow2(NT);
     constexpr int L = M::kLoads;
@@ -1720,7 +1723,7 @@ __device__ __forceinline__ void mx_rows(const uint8_t* __restrict__ W, int64_t r
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
         const __amdgpu_buffer_rsrc_t xr =
-            __builtin_amdgcn_make_buffer_rsrc((void*)(x + (int64_t)t * cols + k0), (short)0, 1024, kBufferRsrcWord3);
+            __builtin_amdgcn_make_buffer_rsrc((void*)(x + xoff[t] + k0), (short)0, 1024, kBufferRsrcWord3);
         load_lds16(xr, reg + 1024 * t, 16 * lane);
     }
     mx_issue<FMT>(W, row_bytes, row_begin, row_end, ntiles, rg, off, slot, lane);
@@ -2177,7 +2180,10 @@ qgemv_mx_kernel(const uint8_t* __restrict__ W, const float* __restrict__ x, floa
                 int64_t row_bytes, int cols, int nslices, int rows_per_wg, int nw) {
     const int64_t row_begin = (int64_t)blockIdx.x * rows_per_wg;
     const int64_t row_end = row_begin + rows_per_wg < rows ? row_begin + rows_per_wg : rows;
-    mx_rows<FMT, T>(W, row_bytes, cols, nslices, x, row_begin, row_end, nw,
+    int64_t xoff[T];
+#pragma unroll
+    for (int t = 0; t < T; ++t) xoff[t] = (int64_t)t * cols;
+    mx_rows<FMT, T>(W, row_bytes, nslices, x, xoff, row_begin, row_end, nw,
                     [=](int t, int64_t row, float v) { y[t * rows + row] = v; });
 }
 
@@ -2244,7 +2250,10 @@ __global__ void __launch_bounds__(64 * kMaxWaves) qgemv_mx_argmax_kernel(DenseAr
     const int64_t row_begin = (int64_t)blockIdx.x * a.rows_per_wg;
     const int64_t row_end = row_begin + a.rows_per_wg < a.rows ? row_begin + a.rows_per_wg : a.rows;
     ArgmaxOut<T> best;
-    mx_rows<FMT, T>(a.W, a.row_bytes, a.cols, a.nslices, a.x, row_begin, row_end, (int)(blockDim.x >> 6), best);
+    int64_t xoff[T];
+#pragma unroll
+    for (int t = 0; t < T; ++t) xoff[t] = (int64_t)t * a.cols;
+    mx_rows<FMT, T>(a.W, a.row_bytes, a.nslices, a.x, xoff, row_begin, row_end, (int)(blockDim.x >> 6), best);
     best.merge(work);
 }
 
@@ -2326,12 +2335,13 @@ struct GroupTargets {
     int rank, nwork;   // this workgroup's share of the rows: rank of nwork
 };
 
-// The share `rank` of `nwork` of a row range, in whole 8-row tiles (possibly empty).
+// The share `rank` of `nwork` of a row range, in whole R-row tiles (possibly empty).
+template <int R = 8>
 __device__ __forceinline__ void share_rows(const GroupTargets& g, int64_t& row_begin, int64_t& row_end) {
-    const int64_t nt = (row_end - row_begin + 7) / 8;
+    const int64_t nt = (row_end - row_begin + R - 1) / R;
     const int64_t t0 = nt * g.rank / g.nwork, t1 = nt * (g.rank + 1) / g.nwork;
-    const int64_t e = row_begin + 8 * t1;
-    row_begin += 8 * t0;
+    const int64_t e = row_begin + R * t1;
+    row_begin += R * t0;
     if (e < row_end) row_end = e;
 }
 
@@ -2508,6 +2518,37 @@ __global__ void __launch_bounds__(64 * kMaxWaves) qgemv_grouped_dma_kernel(Group
     }
     wait_vmcnt<0>();  // the prefetch is not this share's: drain it
     if (row_begin < row_end) grouped_dma_switch<FMT, D, false>(a, W, y, e, g, row_begin, row_end);
+}
+
+// Grouped experts on the matrix cores (kind 8's tiles): the same slots, sharing
+// and outputs, the workgroup's rows shared in 16-row tiles; x of each input is
+// split into its bf16 pieces per wave as on the dense path.
+template <int FMT, int NE>
+__device__ __forceinline__ void grouped_mx_run(const GroupedArgs& a, const uint8_t* W, float* y, int e,
+                                               const GroupTargets& g, int64_t row_begin, int64_t row_end) {
+    int64_t xoff[NE];
+    group_offsets<NE>(a, g, xoff);
+    mx_rows<FMT, NE>(W + (int64_t)e * a.expert_bytes, a.row_bytes, a.cols / kHalfSlice, a.x, xoff, row_begin, row_end,
+                     (int)(blockDim.x >> 6), [=](int n, int64_t row, float v) { group_store(a, y, e, g, n, row, v); });
+}
+
+template <int FMT>
+__global__ void __launch_bounds__(64 * kMaxWaves) qgemv_grouped_mx_kernel(GroupedArgs a) {
+    int e;
+    const uint8_t* W;
+    float* y;
+    int64_t row_begin, row_end;
+    if (!grouped_slot(a, e, W, y, row_begin, row_end)) return;
+    GroupTargets g;
+    grouped_targets(a, e, g);
+    share_rows<16>(g, row_begin, row_end);
+    if (row_begin >= row_end) return;
+    switch (g.ne) {
+    case 1: grouped_mx_run<FMT, 1>(a, W, y, e, g, row_begin, row_end); break;
+    case 2: grouped_mx_run<FMT, 2>(a, W, y, e, g, row_begin, row_end); break;
+    case 3: grouped_mx_run<FMT, 3>(a, W, y, e, g, row_begin, row_end); break;
+    default: grouped_mx_run<FMT, 4>(a, W, y, e, g, row_begin, row_end); break;
+    }
 }
 
 // --------------------------------------------------------------- dispatch
@@ -2984,6 +3025,17 @@ int launch_gather(int fmt, int T, const Tile& tile, const DenseArgs& a, const in
 }
 
 int launch_grouped(int fmt, const Tile& tile, const GroupedArgs& a, void* stream) {
+    if (tile.kind == 8) {
+        const int nsl = a.cols / kHalfSlice;
+        if (a.cols % kHalfSlice || tile.waves_per_wg % nsl || tile.rows_per_wg % 16) return (int)hipErrorInvalidValue;
+        const GroupedFn fn = fmt == QG_FMT_Q8_0 ? qgemv_grouped_mx_kernel<QG_FMT_Q8_0>
+                           : fmt == QG_FMT_Q4_0 ? qgemv_grouped_mx_kernel<QG_FMT_Q4_0>
+                                                : qgemv_grouped_mx_kernel<QG_FMT_BF16>;
+        const int64_t nwg = (int64_t)a.T * a.topk * a.tiles_per_expert * a.parts;
+        hipLaunchKernelGGL(fn, dim3((unsigned)nwg), dim3(64 * tile.waves_per_wg), mx_lds_bytes(fmt, tile, a.T, nsl),
+                           (hipStream_t)stream, a);
+        return (int)hipGetLastError();
+    }
     if (tile.kind == 3) {
         GroupedFn fn = nullptr;
         if (tile.rows_per_batch == 4 && tile.depth == 2)

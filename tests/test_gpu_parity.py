@@ -684,11 +684,13 @@ def grouped_check(torch, orc, fmt, n_experts, rows, cols, ids, W, x, what):
 def test_grouped_config(torch, orc, monkeypatch):
     g = I.grouped_case()
     y = grouped_check(torch, orc, g["fmt"], g["n_experts"], g["rows"], g["cols"], g["ids"], g["W"], g["x"], "c5")
-    # equals the plain call on each selected expert bit for bit, run on the vector-ALU
-    # LDS-DMA kind the grouped kernel shares its arithmetic with (512-wide k slices)
+    # equals the plain call on each selected expert bit for bit, run on the kind the
+    # grouped kernel shares its arithmetic with (matrix cores on 256-wide k slices)
+    st, t = _lib.qg_query_tile(g["fmt"], g["rows"], g["cols"], g["T"])
+    assert st == 0 and t[6] == 8, t
     rb = I.packed_row_bytes(g["fmt"], g["cols"])
     Wd = dev(torch, g["W"])
-    monkeypatch.setenv("QGEMV_TILE", f"{NAMES[g['fmt']]}:4,{g['cols'] // 512},24,L2")
+    monkeypatch.setenv("QGEMV_TILE", f"{NAMES[g['fmt']]}:4,{g['cols'] // 256},32,x")
     for t in range(g["T"]):
         for j in (0, g["topk"] - 1):
             e = int(g["ids"][t, j])
@@ -699,8 +701,9 @@ def test_grouped_config(torch, orc, monkeypatch):
 
 @pytest.mark.parametrize("fmt", [Q4, Q8, BF])
 def test_grouped_sharing(torch, orc, monkeypatch, fmt):
-    """Shared and duplicated experts on the default (LDS-DMA) path, on the direct
-    path (tile override), and at a width whose rows are not 16-byte aligned."""
+    """Shared and duplicated experts on the default (matrix-core) path, on the
+    LDS-DMA vector-ALU and direct paths (tile overrides), pinned matrix-core tiles
+    with row groups, and at a width whose rows are not 16-byte aligned."""
     cases = [
         np.array([[3, 5], [3, 7], [3, 5], [3, 9]], np.int32),   # expert 3 shared by 4 tokens, 5 by 2
         np.array([[1, 1, 2], [2, 2, 1], [0, 11, 2], [11, 0, 4]], np.int32),  # duplicates inside a token
@@ -708,7 +711,9 @@ def test_grouped_sharing(torch, orc, monkeypatch, fmt):
         np.array([[4, 6], [6, 4], [4, 6]], np.int32),           # T = 3, ne = 3
     ]
     n_experts, rows = 12, 200
-    for cols, tile in ((1024, None), (1024, f"{NAMES[fmt]}:4,2,8,d"), (1056 if fmt != BF else 1048, None)):
+    for cols, tile in ((1024, None), (1024, f"{NAMES[fmt]}:4,2,8,d"), (1024, f"{NAMES[fmt]}:4,2,24,L2"),
+                       (1024, f"{NAMES[fmt]}:4,8,64,x"), (768, f"{NAMES[fmt]}:4,3,16,x"),
+                       (1056 if fmt != BF else 1048, None)):
         if tile:
             monkeypatch.setenv("QGEMV_TILE", tile)
         else:
