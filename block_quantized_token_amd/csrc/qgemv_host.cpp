@@ -55,16 +55,16 @@ bool parse_tile_spec(const std::string& spec, Tile* t, std::string* why) {
     int rb = 0, nw = 0, rw = 0, depth = 0;
     char kind = 0, tail = 0;
     int got = sscanf(spec.c_str(), "%d,%d,%d,%c%c", &rb, &nw, &rw, &kind, &tail);
-    if (got == 5 && (kind == 'l' || kind == 'L' || kind == 'u' || kind == 'h')) {  // l|L|u|h<depth>
+    if (got == 5 && (kind == 'l' || kind == 'L' || kind == 'u' || kind == 'h' || kind == 'x')) {  // l|L|u|h|x<depth>
         char tail2 = 0;
         const char* f = kind == 'l' ? "%d,%d,%d,l%d%c" : kind == 'L' ? "%d,%d,%d,L%d%c"
-                      : kind == 'u' ? "%d,%d,%d,u%d%c" : "%d,%d,%d,h%d%c";
+                      : kind == 'u' ? "%d,%d,%d,u%d%c" : kind == 'h' ? "%d,%d,%d,h%d%c" : "%d,%d,%d,x%d%c";
         got = sscanf(spec.c_str(), f, &rb, &nw, &rw, &depth, &tail2) == 4 ? 4 : -1;
     }
     const bool dma = kind == 'l' || kind == 'L' || kind == 'u' || kind == 'h';
-    if (!(got == 3 || (got == 4 && (kind == 'd' || kind == 's' || kind == 'm' || kind == 'p' || kind == 'x' ||
-                                     kind == 'P' || (dma && depth > 0))))) {
-        *why = "tile '" + spec + "' is not rb,nw,rw[,d|s|m|p|x|P|l<depth>|L<depth>|u<depth>|h<depth>]";
+    if (!(got == 3 || (got == 4 && (kind == 'd' || kind == 's' || kind == 'm' || kind == 'p' || kind == 'P' ||
+                                     (kind == 'x' && depth >= 0 && depth <= 2) || (dma && depth > 0))))) {
+        *why = "tile '" + spec + "' is not rb,nw,rw[,d|s|m|p|x|x2|P|l<depth>|L<depth>|u<depth>|h<depth>]";
         return false;
     }
     if (!valid_rb(rb) || nw < 1 || nw > kMaxWaves || rw < 2 * rb || rw % (2 * rb) || rw > (1 << 20)) {
@@ -78,7 +78,7 @@ bool parse_tile_spec(const std::string& spec, Tile* t, std::string* why) {
                           : kind == 'x' ? 8 : kind == 'P' ? 9 : 1)
                        : -1;  // -1: later
     t->mfma = got == 4 && kind == 'm' ? 1 : got == 4 && kind == 'p' ? 2 : 0;
-    t->depth = got == 4 && dma ? depth : got == 4 && (kind == 'x' || kind == 'P') ? 1 : 0;
+    t->depth = got == 4 && dma ? depth : got == 4 && kind == 'x' ? (depth ? depth : 1) : got == 4 && kind == 'P' ? 1 : 0;
     return true;
 }
 
@@ -284,8 +284,8 @@ int pick_tile(int fmt, int64_t rows, int64_t cols, int T, Tile* t) {
         if (cols % 256 || t->waves_per_wg % nsl256 != 0)
             return fail(QG_EINVAL, "matrix-core half-slice tile needs cols a multiple of 256 and waves_per_wg a "
                                    "multiple of the %lld 256-wide slices", (long long)nsl256);
-        if (row_bytes(fmt, cols) * 16 > 0x7FFFFFFF)
-            return fail(QG_EINVAL, "matrix-core half-slice tile needs 16 rows within a 2 GB descriptor");
+        if (row_bytes(fmt, cols) * 16 * t->depth > 0x7FFFFFFF)
+            return fail(QG_EINVAL, "matrix-core half-slice tile needs %d rows within a 2 GB descriptor", 16 * t->depth);
         if (mx_lds_bytes(fmt, *t, T, (int)nsl256) > kMaxLds)
             return fail(QG_EINVAL, "tile needs %zu B of LDS (rows_per_wg %d too large)",
                         mx_lds_bytes(fmt, *t, T, (int)nsl256), t->rows_per_wg);
@@ -533,9 +533,10 @@ int run_grouped(int fmt, int64_t n_experts, int64_t rows, int64_t cols, int T, i
         // (the down projection's short rows): row groups of waves, 4 waves or more.
         // Rows per workgroup: the fewest that keep all slots' workgroups within
         // one per CU (256 experts of 512 x 2560 Q4_0, 10 slots a token, µs at
-        // T = 1..4: 32 rows 7.7 / 12.9 / 13.3 / 21.2, 48 rows 9.0 / 9.2 / 15.9 / 17.4,
-        // 64 rows 10.3 / 10.4 / 10.6 / 19.9, 96 rows 13.0 / 13.1 / 13.2 / 13.4: a
-        // second round of workgroups costs more than longer ones).
+        // T = 1..4: 32 rows 7.4 / 12.9 / 13.2 / 18.8, 48 rows 8.6 / 8.8 / 15.7 / 15.9,
+        // 64 rows 10.0 / 10.1 / 10.3 / 18.4, 96 rows 12.6 / 12.7 / 12.8 / 13.0: more
+        // workgroups than CUs cost more than longer ones, even where two fit a CU;
+        // 32-row tiles, x2, are no faster).
         tile.kind = 8;
         tile.depth = 1;
         tile.mfma = 0;
@@ -549,7 +550,7 @@ int run_grouped(int fmt, int64_t n_experts, int64_t rows, int64_t cols, int T, i
         while (tile.rows_per_wg > 16 && mx_lds_bytes(fmt, tile, T, (int)nsl256) > kMaxLds) tile.rows_per_wg -= 16;
     }
     if (tile.kind == 8) {  // default or pinned: checked as the launch needs it, else the paths below
-        if (!mx_ok || tile.waves_per_wg % nsl256 || tile.rows_per_wg % 16 ||
+        if (!mx_ok || tile.waves_per_wg % nsl256 || tile.rows_per_wg % 16 || rbytes * 32 * tile.depth >= 0x7FFFFFFF ||
             mx_lds_bytes(fmt, tile, T, (int)nsl256) > kMaxLds)
             tile.kind = 1;
     } else if (!overridden && row_bytes(fmt, cols) % 16 == 0 && nsl <= kMaxWaves) {

@@ -104,14 +104,15 @@ inline size_t half_lds_bytes(int fmt, const Tile& t, int T, int nslices256) {
            ntiles * nslices256 * 4 * 2 * pad_tokens(T) * 4;
 }
 
-// Kind 8 (matrix cores on 256-wide slices): one 16-row tile slot per wave (exactly the
-// tile's bytes), a region per wave for x and then its bf16 pieces (1536 * T bytes),
-// then partial sums [16-row tiles][slices][16][pad(T)].
-inline size_t mx_slot_bytes(int fmt) { return (size_t)16 * (stream_chunks(fmt) / 2) * 16; }
+// Kind 8 (matrix cores on 256-wide slices): one tile slot per wave (exactly the tile's
+// bytes), a region per wave for one token's bf16 pieces (1536 bytes), then partial
+// sums [tiles][slices][tile rows][pad(T)].
+// `depth` is the tile's groups of 16 rows (1 or 2).
+inline size_t mx_slot_bytes(int fmt, int R = 1) { return (size_t)16 * R * (stream_chunks(fmt) / 2) * 16; }
 inline size_t mx_lds_bytes(int fmt, const Tile& t, int T, int nslices256) {
-    const size_t ntiles = (size_t)(t.rows_per_wg + 15) / 16;
-    return (size_t)t.waves_per_wg * (mx_slot_bytes(fmt) + 1536 * (size_t)T) +
-           ntiles * nslices256 * 16 * pad_tokens(T) * 4;
+    const int R = t.depth == 2 ? 2 : 1;
+    const size_t ntiles = (size_t)(t.rows_per_wg + 16 * R - 1) / (16 * R);
+    return (size_t)t.waves_per_wg * (mx_slot_bytes(fmt, R) + 1536) + ntiles * nslices256 * 16 * R * pad_tokens(T) * 4;
 }
 
 // Kind 9 (persistent matrix cores on 512-wide slices): one 16-row tile slot per wave

@@ -1591,27 +1591,30 @@ __device__ __forceinline__ void mfma_persist_q8(const uint8_t* __restrict__ W, i
 // Each wave keeps one tile in flight, refilled as soon as the tile's bytes are
 // in registers; measured on 10240 x 2560, a second tile in flight or a refill
 // after the math is slower (the vector-ALU kernels behave alike).
-template <int FMT>
+// A tile is R groups of 16 rows (R = 2: twice the bytes in flight per wave, for
+// the formats with short rows).
+template <int FMT, int R = 1>
 struct MxShape {
     static constexpr int kChunks = StreamFmt<FMT>::kChunks / 2;          // 16-byte chunks of a 256-wide row slice
-    static constexpr int kSlot = 16 * kChunks * 16;                       // a 16-row tile: 4352, 2304, 8192 B
-    static constexpr int kLoads = (16 * kChunks + 63) / 64;               // 5, 3, 8
-    static constexpr int kLastLanes = 16 * kChunks - 64 * (kLoads - 1);   // lanes of the last load: 16, 16, 64
+    static constexpr int kRows = 16 * R;                                  // rows of a tile
+    static constexpr int kSlot = kRows * kChunks * 16;                    // 16 rows: 4352, 2304, 8192 B
+    static constexpr int kLoads = (kRows * kChunks + 63) / 64;            // 16 rows: 5, 3, 8
+    static constexpr int kLastLanes = kRows * kChunks - 64 * (kLoads - 1);  // lanes of the last load (16 rows: 16, 16, 64)
     static constexpr int kBlockBytes = FMT == QG_FMT_Q8_0 ? 34 : FMT == QG_FMT_Q4_0 ? 18 : 64;
 };
 
-// One 16-row tile of the wave's slice into its slot: lane l of load k fetches
-// chunk 64 k + l (row / chunk of the slice); lanes past the tile's last chunk do
-// not load, so the slot is exactly the tile's bytes; rows past the range are
+// One tile of the wave's slice into its slot: lane l of load k fetches chunk
+// 64 k + l (row / chunk of the slice); lanes past the tile's last chunk do not
+// load, so the slot is exactly the tile's bytes; rows past the range are
 // outside the descriptor and read as zeros.
-template <int FMT>
+template <int FMT, int R = 1>
 __device__ __forceinline__ void mx_issue(const uint8_t* __restrict__ W, int64_t row_bytes, int64_t row_begin,
-                                         int64_t row_end, int ntiles, int t, const int (&off)[MxShape<FMT>::kLoads],
+                                         int64_t row_end, int ntiles, int t, const int (&off)[MxShape<FMT, R>::kLoads],
                                          uint8_t* slot, int lane) {
-    using M = MxShape<FMT>;
+    using M = MxShape<FMT, R>;
     const bool live = t < ntiles;
-    const int64_t r0 = row_begin + (int64_t)(live ? t : 0) * 16;
-    const int64_t rows_here = row_end - r0 < 16 ? row_end - r0 : 16;
+    const int64_t r0 = row_begin + (int64_t)(live ? t : 0) * M::kRows;
+    const int64_t rows_here = row_end - r0 < M::kRows ? row_end - r0 : M::kRows;
     const int num = live ? (int)(rows_here * row_bytes) : 0;
     const __amdgpu_buffer_rsrc_t rsrc =
         __builtin_amdgcn_make_buffer_rsrc((void*)(W + r0 * row_bytes), (short)0, num, kBufferRsrcWord3);
@@ -1690,15 +1693,47 @@ __device__ __forceinline__ V4 mx_bfrag(const uint8_t* rowp, int b, int g, float&
     return mx_bconv<FMT>(mx_braw<FMT>(rowp, b, g), b, g, d);
 }
 
-// Token t's x is the row at x + xoff[t] (the dense path: t * cols).
-template <int FMT, int NT, class Out>
+// The wave's first tile of a row range, issued ahead of the rest of the
+// prologue (the grouped kernel's scan of the ids); mx_rows<..., PRE = true> then
+// does not issue it again.
+template <int FMT, int R>
+__device__ __forceinline__ void mx_prefetch(const uint8_t* __restrict__ W, int64_t row_bytes, int nsl, int64_t row_begin,
+                                            int64_t row_end) {
+    using M = MxShape<FMT, R>;
+    extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int s = wave % nsl, rg = wave / nsl;
+    const int ntiles = (int)((row_end - row_begin + M::kRows - 1) / M::kRows);
+    int off[M::kLoads];
+#pragma unroll
+    for (int k = 0; k < M::kLoads; ++k) {
+        const int j = 64 * k + lane;
+        const int r = j / M::kChunks, c = j % M::kChunks;
+        off[k] = r < M::kRows ? (int)(r * row_bytes) + s * M::kChunks * 16 + 16 * c : kNoLoad;
+    }
+    mx_issue<FMT, R>(W, row_bytes, row_begin, row_end, ntiles, rg, off, smem + wave * M::kSlot, lane);
+}
+
+// x of token t of the wave's slice: lane l holds k = 4 l .. 4 l + 3 of the
+// slice's 256 in xv[t] (one coalesced 1 KB row per token, loaded by the caller).
+template <int FMT, int NT>
+__device__ __forceinline__ void mx_load_x(const float* __restrict__ x, const int64_t (&xoff)[NT], int nsl,
+                                          float4 (&xv)[NT]) {
+    const int k0 = ((int)__builtin_amdgcn_readfirstlane(threadIdx.x >> 6) % nsl) * kHalfSlice;
+#pragma unroll
+    for (int t = 0; t < NT; ++t) xv[t] = *reinterpret_cast<const float4*>(x + xoff[t] + k0 + 4 * (threadIdx.x & 63));
+}
+
+template <int FMT, int NT, int R, bool PRE = false, class Out>
 __device__ __forceinline__ void mx_rows(const uint8_t* __restrict__ W, int64_t row_bytes, int nsl,
-                                        const float* __restrict__ x, const int64_t (&xoff)[NT], int64_t row_begin,
-                                        int64_t row_end, int nw, Out&& out) {
-    using M = MxShape<FMT>;
+                                        const float4 (&xv)[NT], int64_t row_begin, int64_t row_end, int nw,
+                                        Out&& out) {
+    using M = MxShape<FMT, R>;
+    constexpr int RT = M::kRows;
     constexpr int TP = pad_pow2(NT);
     constexpr int L = M::kLoads;
-    constexpr int REG = 1536 * NT;  // per wave: x [NT][256] fp32, then the A pieces [8][4][3][NT] x 16 B
+    constexpr int REG = 1536;  // per wave: one token's bf16 pieces [8 blocks][4 groups][3 pieces] x 16 B
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
 
     const int tid = threadIdx.x;
@@ -1706,38 +1741,32 @@ __device__ __forceinline__ void mx_rows(const uint8_t* __restrict__ W, int64_t r
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: keeps descriptors and M0 scalar
     const int n = lane & 15, g = lane >> 4;
     const int s = wave % nsl, rg = wave / nsl, RG = nw / nsl;
-    const int k0 = s * kHalfSlice;
-    const int ntiles = (int)((row_end - row_begin + 15) / 16);
+    const int ntiles = (int)((row_end - row_begin + RT - 1) / RT);
     uint8_t* slot = smem + wave * M::kSlot;
     uint8_t* reg = smem + nw * M::kSlot + wave * REG;
-    float* part = reinterpret_cast<float*>(smem + nw * (M::kSlot + REG));  // [tiles][nsl][16 rows][TP]
+    float* part = reinterpret_cast<float*>(smem + nw * (M::kSlot + REG));  // [tiles][nsl][RT rows][TP]
 
     int off[L];
 #pragma unroll
     for (int k = 0; k < L; ++k) {
         const int j = 64 * k + lane;
         const int r = j / M::kChunks, c = j % M::kChunks;
-        off[k] = r < 16 ? (int)(r * row_bytes) + s * M::kChunks * 16 + 16 * c : kNoLoad;
+        off[k] = r < RT ? (int)(r * row_bytes) + s * M::kChunks * 16 + 16 * c : kNoLoad;
     }
-    // x of the slice, then the wave's first tile (x is older: waited for first)
-#pragma unroll
-    for (int t = 0; t < NT; ++t) {
-        const __amdgpu_buffer_rsrc_t xr =
-            __builtin_amdgcn_make_buffer_rsrc((void*)(x + xoff[t] + k0), (short)0, 1024, kBufferRsrcWord3);
-        load_lds16(xr, reg + 1024 * t, 16 * lane);
-    }
-    mx_issue<FMT>(W, row_bytes, row_begin, row_end, ntiles, rg, off, slot, lane);
-    wait_vmcnt<L>();
+    // the wave's first tile, unless PRE has it on its way already (x is older)
+    if constexpr (!PRE) mx_issue<FMT, R>(W, row_bytes, row_begin, row_end, ntiles, rg, off, slot, lane);
 
-    // split: lane l takes k = 4 l .. 4 l + 3 of every token; piece p of x[t][k] goes
-    // to the 16-byte fragment (block k / 32, group (k % 32) / 8, row 4p + t)
+    // split, one token at a time through the wave's region: piece p of x[t][k] goes
+    // to the 16-byte fragment (block k / 32, group (k % 32) / 8, piece p), which the
+    // lane of A's row 4p + t and group (k % 32) / 8 then reads.  A wave's LDS
+    // operations take effect in program order, so the next token's writes land
+    // after this token's reads.
     V4 afrag[8];
     {
-        float4 xv[NT];
-#pragma unroll
-        for (int t = 0; t < NT; ++t) xv[t] = *reinterpret_cast<const float4*>(reg + 1024 * t + 16 * lane);
-        wait_lgkmcnt0();  // every lane's x is read before the pieces overwrite it
         const int b = lane >> 3, gg = (lane & 7) >> 1, half = (lane & 1) * 8;
+        const int am = lane & 15, ap = am >> 2, at = am & 3;
+#pragma unroll
+        for (int bb = 0; bb < 8; ++bb) afrag[bb] = V4{0u, 0u, 0u, 0u};
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
             const float vv[4] = {xv[t].x, xv[t].y, xv[t].z, xv[t].w};
@@ -1759,17 +1788,12 @@ __device__ __forceinline__ void mx_rows(const uint8_t* __restrict__ W, int64_t r
                 uint2 w2;
                 w2.x = __builtin_amdgcn_perm(pc[p][1], pc[p][0], 0x07060302u);
                 w2.y = __builtin_amdgcn_perm(pc[p][3], pc[p][2], 0x07060302u);
-                *reinterpret_cast<uint2*>(reg + b * (192 * NT) + (gg * 3 * NT + p * NT + t) * 16 + half) = w2;
+                *reinterpret_cast<uint2*>(reg + b * 192 + (gg * 3 + p) * 16 + half) = w2;
             }
-        }
-        wait_lgkmcnt0();
-        const int am = lane & 15, ap = am >> 2, at = am & 3;
-        const bool arow = ap < 3 && at < NT;
-        const int idx = arow ? (g * 3 * NT + ap * NT + at) * 16 : 0;
+            if (ap < 3 && at == t) {
 #pragma unroll
-        for (int bb = 0; bb < 8; ++bb) {
-            const V4 v = *reinterpret_cast<const V4*>(reg + bb * (192 * NT) + idx);
-            afrag[bb] = arow ? v : V4{0u, 0u, 0u, 0u};
+                for (int bb = 0; bb < 8; ++bb) afrag[bb] = *reinterpret_cast<const V4*>(reg + bb * 192 + (g * 3 + ap) * 16);
+            }
         }
     }
 
@@ -1778,38 +1802,44 @@ __device__ __forceinline__ void mx_rows(const uint8_t* __restrict__ W, int64_t r
     for (int i = 0; i < mine; ++i) {
         const int t = rg + i * RG;
         wait_vmcnt<0>();  // the slot holds tile t
-        V4 bq[8];
-        float dq[8];
+        MxRaw raw[R][8];
 #pragma unroll
-        for (int b = 0; b < 8; ++b) bq[b] = mx_bfrag<FMT>(rowp, b, g, dq[b]);
+        for (int h = 0; h < R; ++h)
+#pragma unroll
+            for (int b = 0; b < 8; ++b) raw[h][b] = mx_braw<FMT>(rowp + 16 * h * (M::kChunks * 16), b, g);
         wait_lgkmcnt0();  // the tile is in registers: the slot takes the next one
-        if (i + 1 < mine) mx_issue<FMT>(W, row_bytes, row_begin, row_end, ntiles, t + RG, off, slot, lane);
-        F4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+        if (i + 1 < mine) mx_issue<FMT, R>(W, row_bytes, row_begin, row_end, ntiles, t + RG, off, slot, lane);
 #pragma unroll
-        for (int b = 0; b < 8; ++b) {
-            if constexpr (FMT == QG_FMT_BF16) {
-                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(BF8, afrag[b]),
-                                                              __builtin_bit_cast(BF8, bq[b]), acc, 0, 0, 0);
-            } else {
-                const F4 z = {0.0f, 0.0f, 0.0f, 0.0f};
-                const F4 dd = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(BF8, afrag[b]),
-                                                                      __builtin_bit_cast(BF8, bq[b]), z, 0, 0, 0);
+        for (int h = 0; h < R; ++h) {
+            F4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-                for (int j = 0; j < 4; ++j) acc[j] = __builtin_fmaf(dq[b], dd[j], acc[j]);
+            for (int b = 0; b < 8; ++b) {
+                float dq;
+                const V4 bq = mx_bconv<FMT>(raw[h][b], b, g, dq);
+                if constexpr (FMT == QG_FMT_BF16) {
+                    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(BF8, afrag[b]),
+                                                                  __builtin_bit_cast(BF8, bq), acc, 0, 0, 0);
+                } else {
+                    const F4 z = {0.0f, 0.0f, 0.0f, 0.0f};
+                    const F4 dd = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(BF8, afrag[b]),
+                                                                          __builtin_bit_cast(BF8, bq), z, 0, 0, 0);
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) acc[j] = __builtin_fmaf(dq, dd[j], acc[j]);
+                }
             }
-        }
-        // token j's pieces sit in lanes n (hi), n + 16 (mid), n + 32 (lo): (hi + mid) + lo
+            // token j's pieces sit in lanes n (hi), n + 16 (mid), n + 32 (lo): (hi + mid) + lo
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            float mid = acc[j], lo = acc[j], junk16 = acc[j], junk32 = acc[j];
-            permlane16_swap(junk16, mid);
-            permlane32_swap(junk32, lo);
-            acc[j] = (acc[j] + mid) + lo;
-        }
-        if (lane < 16) {
-            float* pp = part + (((size_t)t * nsl + s) * 16 + n) * TP;
+            for (int j = 0; j < 4; ++j) {
+                float mid = acc[j], lo = acc[j], junk16 = acc[j], junk32 = acc[j];
+                permlane16_swap(junk16, mid);
+                permlane32_swap(junk32, lo);
+                acc[j] = (acc[j] + mid) + lo;
+            }
+            if (lane < 16) {
+                float* pp = part + (((size_t)t * nsl + s) * RT + 16 * h + n) * TP;
 #pragma unroll
-            for (int j = 0; j < TP; ++j) pp[j] = acc[j];
+                for (int j = 0; j < TP; ++j) pp[j] = acc[j];
+            }
         }
     }
     wait_vmcnt<0>();  // a wave with no tile still drains its empty load
@@ -1818,9 +1848,9 @@ __device__ __forceinline__ void mx_rows(const uint8_t* __restrict__ W, int64_t r
     const int nrows = (int)(row_end - row_begin);
     for (int o = tid; o < nrows * NT; o += blockDim.x) {
         const int rr = o / NT, tk = o % NT;
-        const float* base = part + ((size_t)(rr >> 4) * nsl * 16 + (rr & 15)) * TP + tk;
+        const float* base = part + ((size_t)(rr / RT) * nsl * RT + rr % RT) * TP + tk;
         float sum = base[0];
-        for (int w = 1; w < nsl; ++w) sum = sum + base[(size_t)w * 16 * TP];
+        for (int w = 1; w < nsl; ++w) sum = sum + base[(size_t)w * RT * TP];
         out(tk, row_begin + rr, sum);
     }
 }
@@ -2174,7 +2204,7 @@ qgemv_half_kernel(const uint8_t* __restrict__ W, const float* __restrict__ x, fl
                          [=](int t, int64_t row, float v) { y[t * rows + row] = v; });
 }
 
-template <int FMT, int T>
+template <int FMT, int T, int R>
 __global__ void __launch_bounds__(64 * kMaxWaves)
 qgemv_mx_kernel(const uint8_t* __restrict__ W, const float* __restrict__ x, float* __restrict__ y, int64_t rows,
                 int64_t row_bytes, int cols, int nslices, int rows_per_wg, int nw) {
@@ -2183,7 +2213,9 @@ qgemv_mx_kernel(const uint8_t* __restrict__ W, const float* __restrict__ x, floa
     int64_t xoff[T];
 #pragma unroll
     for (int t = 0; t < T; ++t) xoff[t] = (int64_t)t * cols;
-    mx_rows<FMT, T>(W, row_bytes, nslices, x, xoff, row_begin, row_end, nw,
+    float4 xv[T];
+    mx_load_x<FMT, T>(x, xoff, nslices, xv);
+    mx_rows<FMT, T, R>(W, row_bytes, nslices, xv, row_begin, row_end, nw,
                     [=](int t, int64_t row, float v) { y[t * rows + row] = v; });
 }
 
@@ -2245,7 +2277,7 @@ __global__ void __launch_bounds__(64 * kMaxWaves) qgemv_mxp_argmax_kernel(DenseA
     best.merge(work);
 }
 
-template <int FMT, int T>
+template <int FMT, int T, int R>
 __global__ void __launch_bounds__(64 * kMaxWaves) qgemv_mx_argmax_kernel(DenseArgs a, unsigned long long* work) {
     const int64_t row_begin = (int64_t)blockIdx.x * a.rows_per_wg;
     const int64_t row_end = row_begin + a.rows_per_wg < a.rows ? row_begin + a.rows_per_wg : a.rows;
@@ -2253,7 +2285,9 @@ __global__ void __launch_bounds__(64 * kMaxWaves) qgemv_mx_argmax_kernel(DenseAr
     int64_t xoff[T];
 #pragma unroll
     for (int t = 0; t < T; ++t) xoff[t] = (int64_t)t * a.cols;
-    mx_rows<FMT, T>(a.W, a.row_bytes, a.nslices, a.x, xoff, row_begin, row_end, (int)(blockDim.x >> 6), best);
+    float4 xv[T];
+    mx_load_x<FMT, T>(a.x, xoff, a.nslices, xv);
+    mx_rows<FMT, T, R>(a.W, a.row_bytes, a.nslices, xv, row_begin, row_end, (int)(blockDim.x >> 6), best);
     best.merge(work);
 }
 
@@ -2330,7 +2364,9 @@ __global__ void __launch_bounds__(64 * kMaxWaves) qgemv_mfma_q8_kernel(DenseArgs
 // slots with per-slot inputs) and where each result goes.
 struct GroupTargets {
     uint32_t tokmask;  // per-token inputs: bit t set = token t chose e
-    uint64_t slots;    // per-slot inputs: up to 4 slot indices, 16 bits each
+    uint64_t slots;    // up to 4 slot indices, 16 bits each: per-slot inputs, the group's slots;
+                       // per-token inputs, the slot of each token (in token order) that names e
+    int dup;           // per-token inputs: some token names e in more than one slot
     int ne;
     int rank, nwork;   // this workgroup's share of the rows: rank of nwork
 };
@@ -2363,7 +2399,7 @@ __device__ __forceinline__ void group_offsets(const GroupedArgs& a, const GroupT
 // n-th token that names e (n varies across lanes, so no array indexing here).
 __device__ __forceinline__ void group_store(const GroupedArgs& a, float* __restrict__ y, int e, const GroupTargets& g,
                                             int n, int64_t row, float v) {
-    if (a.per_slot_x) {
+    if (a.per_slot_x || !g.dup) {
         const int slot = (int)((g.slots >> (16 * n)) & 0xFFFF);
         y[(int64_t)slot * a.rows + row] = v;
         return;
@@ -2416,23 +2452,35 @@ __device__ __forceinline__ uint64_t below(int slot, int c) {
 // the workers are the slots naming e.  Per-slot inputs: the slots naming e in
 // rank order form groups of T (one group when every token names an expert at
 // most once); the workers are the group's slots.
-__device__ __forceinline__ void grouped_targets(const GroupedArgs& a, int e, GroupTargets& g) {
+// id0: the lane's id of the first 64 (-1 past the end), when loaded ahead.
+__device__ __forceinline__ void grouped_targets(const GroupedArgs& a, int e, GroupTargets& g, int id0 = -2) {
     const int slot = blockIdx.x / (a.tiles_per_expert * a.parts);
     const int n = a.T * a.topk;
     const int lane = threadIdx.x & 63;
     g.tokmask = 0;
     g.slots = 0;
+    g.dup = 0;
     g.ne = 0;
     int before = 0, total = 0;
     for (int c = 0; c < n; c += 64) {
         const int i = c + lane;
-        const bool m = i < n && a.ids[i] == e;
+        const bool m = i < n && (c == 0 && id0 != -2 ? id0 : a.ids[i]) == e;
         const uint64_t b = __ballot(m);  // uniform
         before += __builtin_popcountll(b & below(slot, c));
         total += __builtin_popcountll(b);
-        if (!a.per_slot_x)
-            for (int t = 0; t < a.T; ++t)
-                if (__ballot(m && i / a.topk == t) != 0) g.tokmask |= 1u << t;
+        if (!a.per_slot_x) {
+            // the slots naming e in ascending order: tokens come in ascending order,
+            // so the k-th new token is the k-th of tokmask
+            for (uint64_t bb = b; bb; bb &= bb - 1) {
+                const int si = c + __builtin_ctzll(bb), t = si / a.topk;
+                if (g.tokmask >> t & 1) {
+                    g.dup = 1;
+                } else {
+                    g.slots |= (uint64_t)si << (16 * __builtin_popcount(g.tokmask));
+                    g.tokmask |= 1u << t;
+                }
+            }
+        }
     }
     if (!a.per_slot_x) {
         g.ne = __builtin_popcount(g.tokmask);
@@ -2523,32 +2571,78 @@ __global__ void __launch_bounds__(64 * kMaxWaves) qgemv_grouped_dma_kernel(Group
 // Grouped experts on the matrix cores (kind 8's tiles): the same slots, sharing
 // and outputs, the workgroup's rows shared in 16-row tiles; x of each input is
 // split into its bf16 pieces per wave as on the dense path.
-template <int FMT, int NE>
+// Per-token inputs: every token's x of the wave's slice is loaded ahead (xall),
+// and the group's NE inputs are picked from it; per-slot inputs are loaded here.
+template <int FMT, int NE, int R, bool PRE>
 __device__ __forceinline__ void grouped_mx_run(const GroupedArgs& a, const uint8_t* W, float* y, int e,
-                                               const GroupTargets& g, int64_t row_begin, int64_t row_end) {
-    int64_t xoff[NE];
-    group_offsets<NE>(a, g, xoff);
-    mx_rows<FMT, NE>(W + (int64_t)e * a.expert_bytes, a.row_bytes, a.cols / kHalfSlice, a.x, xoff, row_begin, row_end,
-                     (int)(blockDim.x >> 6), [=](int n, int64_t row, float v) { group_store(a, y, e, g, n, row, v); });
+                                               const GroupTargets& g, const float4 (&xall)[QG_MAX_T],
+                                               int64_t row_begin, int64_t row_end) {
+    const int nsl = a.cols / kHalfSlice;
+    float4 xv[NE];
+    if (a.per_slot_x) {
+        int64_t xoff[NE];
+        group_offsets<NE>(a, g, xoff);
+        mx_load_x<FMT, NE>(a.x, xoff, nsl, xv);
+    } else {
+        uint32_t m = g.tokmask;
+#pragma unroll
+        for (int i = 0; i < NE; ++i) {
+            const int t = __builtin_ctz(m);  // uniform
+            m &= m - 1;
+#pragma unroll
+            for (int u = 0; u < QG_MAX_T; ++u)
+                if (u == t) xv[i] = xall[u];
+        }
+    }
+    mx_rows<FMT, NE, R, PRE>(W + (int64_t)e * a.expert_bytes, a.row_bytes, nsl, xv, row_begin, row_end,
+                             (int)(blockDim.x >> 6),
+                             [=](int n, int64_t row, float v) { group_store(a, y, e, g, n, row, v); });
 }
 
-template <int FMT>
+template <int FMT, int R, bool PRE>
+__device__ __forceinline__ void grouped_mx_switch(const GroupedArgs& a, const uint8_t* W, float* y, int e,
+                                                  const GroupTargets& g, const float4 (&xall)[QG_MAX_T],
+                                                  int64_t row_begin, int64_t row_end) {
+    switch (g.ne) {
+    case 1: grouped_mx_run<FMT, 1, R, PRE>(a, W, y, e, g, xall, row_begin, row_end); break;
+    case 2: grouped_mx_run<FMT, 2, R, PRE>(a, W, y, e, g, xall, row_begin, row_end); break;
+    case 3: grouped_mx_run<FMT, 3, R, PRE>(a, W, y, e, g, xall, row_begin, row_end); break;
+    default: grouped_mx_run<FMT, 4, R, PRE>(a, W, y, e, g, xall, row_begin, row_end); break;
+    }
+}
+
+template <int FMT, int R>
 __global__ void __launch_bounds__(64 * kMaxWaves) qgemv_grouped_mx_kernel(GroupedArgs a) {
+    // loads that do not depend on the expert go first: the first 64 ids of the
+    // scan and (per-token inputs) every token's x; then the expert's first tile
+    // starts streaming while the ids are scanned; it is this workgroup's own
+    // when its share starts the range
+    const int lane = threadIdx.x & 63;
+    const int nid = a.T * a.topk;
+    const int id0 = lane < nid ? a.ids[lane] : -1;
+    float4 xall[QG_MAX_T];
+    if (!a.per_slot_x) {
+        const int k0 = ((int)__builtin_amdgcn_readfirstlane(threadIdx.x >> 6) % (a.cols / kHalfSlice)) * kHalfSlice;
+#pragma unroll
+        for (int t = 0; t < QG_MAX_T; ++t)
+            if (t < a.T) xall[t] = *reinterpret_cast<const float4*>(a.x + (int64_t)t * a.cols + k0 + 4 * lane);
+    }
     int e;
     const uint8_t* W;
     float* y;
     int64_t row_begin, row_end;
     if (!grouped_slot(a, e, W, y, row_begin, row_end)) return;
+    mx_prefetch<FMT, R>(W + (int64_t)e * a.expert_bytes, a.row_bytes, a.cols / kHalfSlice, row_begin, row_end);
     GroupTargets g;
-    grouped_targets(a, e, g);
-    share_rows<16>(g, row_begin, row_end);
-    if (row_begin >= row_end) return;
-    switch (g.ne) {
-    case 1: grouped_mx_run<FMT, 1>(a, W, y, e, g, row_begin, row_end); break;
-    case 2: grouped_mx_run<FMT, 2>(a, W, y, e, g, row_begin, row_end); break;
-    case 3: grouped_mx_run<FMT, 3>(a, W, y, e, g, row_begin, row_end); break;
-    default: grouped_mx_run<FMT, 4>(a, W, y, e, g, row_begin, row_end); break;
+    grouped_targets(a, e, g, id0);
+    const int64_t first = row_begin;
+    share_rows<16 * R>(g, row_begin, row_end);
+    if (row_begin < row_end && row_begin == first) {
+        grouped_mx_switch<FMT, R, true>(a, W, y, e, g, xall, row_begin, row_end);
+        return;
     }
+    wait_vmcnt<0>();  // the prefetch is not this share's: drain it
+    if (row_begin < row_end) grouped_mx_switch<FMT, R, false>(a, W, y, e, g, xall, row_begin, row_end);
 }
 
 // --------------------------------------------------------------- dispatch
@@ -2806,22 +2900,38 @@ ArgmaxFn half_argmax_for(int T, int depth) {
 }
 
 template <int FMT>
-DmaFn mx_for(int T) {
+DmaFn mx_for(int T, int R) {
+    if (R == 2) {
+        switch (T) {
+        case 1: return qgemv_mx_kernel<FMT, 1, 2>;
+        case 2: return qgemv_mx_kernel<FMT, 2, 2>;
+        case 3: return qgemv_mx_kernel<FMT, 3, 2>;
+        default: return qgemv_mx_kernel<FMT, 4, 2>;
+        }
+    }
     switch (T) {
-    case 1: return qgemv_mx_kernel<FMT, 1>;
-    case 2: return qgemv_mx_kernel<FMT, 2>;
-    case 3: return qgemv_mx_kernel<FMT, 3>;
-    default: return qgemv_mx_kernel<FMT, 4>;
+    case 1: return qgemv_mx_kernel<FMT, 1, 1>;
+    case 2: return qgemv_mx_kernel<FMT, 2, 1>;
+    case 3: return qgemv_mx_kernel<FMT, 3, 1>;
+    default: return qgemv_mx_kernel<FMT, 4, 1>;
     }
 }
 
 template <int FMT>
-ArgmaxFn mx_argmax_for(int T) {
+ArgmaxFn mx_argmax_for(int T, int R) {
+    if (R == 2) {
+        switch (T) {
+        case 1: return qgemv_mx_argmax_kernel<FMT, 1, 2>;
+        case 2: return qgemv_mx_argmax_kernel<FMT, 2, 2>;
+        case 3: return qgemv_mx_argmax_kernel<FMT, 3, 2>;
+        default: return qgemv_mx_argmax_kernel<FMT, 4, 2>;
+        }
+    }
     switch (T) {
-    case 1: return qgemv_mx_argmax_kernel<FMT, 1>;
-    case 2: return qgemv_mx_argmax_kernel<FMT, 2>;
-    case 3: return qgemv_mx_argmax_kernel<FMT, 3>;
-    default: return qgemv_mx_argmax_kernel<FMT, 4>;
+    case 1: return qgemv_mx_argmax_kernel<FMT, 1, 1>;
+    case 2: return qgemv_mx_argmax_kernel<FMT, 2, 1>;
+    case 3: return qgemv_mx_argmax_kernel<FMT, 3, 1>;
+    default: return qgemv_mx_argmax_kernel<FMT, 4, 1>;
     }
 }
 
@@ -2861,8 +2971,9 @@ int launch_mxp(int fmt, int T, const Tile& tile, const DenseArgs& a_in, void* st
 int launch_mx(int fmt, int T, const Tile& tile, const DenseArgs& a, void* stream) {
     const int nsl = (int)(a.cols / kHalfSlice);
     if (a.cols % kHalfSlice || tile.waves_per_wg % nsl) return (int)hipErrorInvalidValue;
-    const DmaFn fn = fmt == QG_FMT_Q8_0 ? mx_for<QG_FMT_Q8_0>(T) : fmt == QG_FMT_Q4_0 ? mx_for<QG_FMT_Q4_0>(T)
-                                                                                    : mx_for<QG_FMT_BF16>(T);
+    const int R = tile.depth == 2 ? 2 : 1;
+    const DmaFn fn = fmt == QG_FMT_Q8_0 ? mx_for<QG_FMT_Q8_0>(T, R) : fmt == QG_FMT_Q4_0 ? mx_for<QG_FMT_Q4_0>(T, R)
+                                                                                        : mx_for<QG_FMT_BF16>(T, R);
     const int64_t nwg = (a.rows + tile.rows_per_wg - 1) / tile.rows_per_wg;
     hipLaunchKernelGGL(fn, dim3((unsigned)nwg), dim3(64 * tile.waves_per_wg), mx_lds_bytes(fmt, tile, T, nsl),
                        (hipStream_t)stream, a.W, a.x, a.y, a.rows, a.row_bytes, a.cols, nsl, a.rows_per_wg,
@@ -2951,9 +3062,10 @@ int launch_argmax(int fmt, int T, const Tile& tile, const DenseArgs& a_in, void*
         lds = mxp_lds_bytes(fmt, tile, T);
     } else if (tile.kind == 8 && a.cols % kHalfSlice == 0 && tile.waves_per_wg % (a.cols / kHalfSlice) == 0) {
         a.nslices = a.cols / kHalfSlice;  // 256-wide slices
-        fn = fmt == QG_FMT_Q8_0 ? mx_argmax_for<QG_FMT_Q8_0>(T)
-           : fmt == QG_FMT_Q4_0 ? mx_argmax_for<QG_FMT_Q4_0>(T)
-                                : mx_argmax_for<QG_FMT_BF16>(T);
+        const int R = tile.depth == 2 ? 2 : 1;
+        fn = fmt == QG_FMT_Q8_0 ? mx_argmax_for<QG_FMT_Q8_0>(T, R)
+           : fmt == QG_FMT_Q4_0 ? mx_argmax_for<QG_FMT_Q4_0>(T, R)
+                                : mx_argmax_for<QG_FMT_BF16>(T, R);
         nwg = (a.rows + tile.rows_per_wg - 1) / tile.rows_per_wg;
         lds = mx_lds_bytes(fmt, tile, T, a.nslices);
     } else if (tile.kind == 7 && tile.rows_per_batch == 4 && a.cols % kHalfSlice == 0 &&
@@ -3028,9 +3140,10 @@ int launch_grouped(int fmt, const Tile& tile, const GroupedArgs& a, void* stream
     if (tile.kind == 8) {
         const int nsl = a.cols / kHalfSlice;
         if (a.cols % kHalfSlice || tile.waves_per_wg % nsl || tile.rows_per_wg % 16) return (int)hipErrorInvalidValue;
-        const GroupedFn fn = fmt == QG_FMT_Q8_0 ? qgemv_grouped_mx_kernel<QG_FMT_Q8_0>
-                           : fmt == QG_FMT_Q4_0 ? qgemv_grouped_mx_kernel<QG_FMT_Q4_0>
-                                                : qgemv_grouped_mx_kernel<QG_FMT_BF16>;
+        const bool r2 = tile.depth == 2;
+        const GroupedFn fn = fmt == QG_FMT_Q8_0 ? (r2 ? qgemv_grouped_mx_kernel<QG_FMT_Q8_0, 2> : qgemv_grouped_mx_kernel<QG_FMT_Q8_0, 1>)
+                           : fmt == QG_FMT_Q4_0 ? (r2 ? qgemv_grouped_mx_kernel<QG_FMT_Q4_0, 2> : qgemv_grouped_mx_kernel<QG_FMT_Q4_0, 1>)
+                                                : (r2 ? qgemv_grouped_mx_kernel<QG_FMT_BF16, 2> : qgemv_grouped_mx_kernel<QG_FMT_BF16, 1>);
         const int64_t nwg = (int64_t)a.T * a.topk * a.tiles_per_expert * a.parts;
         hipLaunchKernelGGL(fn, dim3((unsigned)nwg), dim3(64 * tile.waves_per_wg), mx_lds_bytes(fmt, tile, a.T, nsl),
                            (hipStream_t)stream, a);

@@ -63,7 +63,7 @@
  *         loads, one in flight per wave, each block contracted as one bf16 matrix
  *         product against an exact three-piece split of x; rb only sets which
  *         rw are valid, cols a multiple of 256, nw a multiple of cols/256; all
- *         three formats;
+ *         three formats; x2: the same with 32-row tiles (the same bits);
  *   m     as s, contracted on the matrix cores; Q8_0 with rb 8 only;
  *   p     m in persistent form: one workgroup per CU, nw = the k slices, rw =
  *         the chunk of rows whose partial sums are buffered;

@@ -203,7 +203,8 @@ def test_tile_query_and_override(lib, monkeypatch):
     # past the LDS)
     for bad in ("q8_0:3,5,8", "q8_0:2,13,8", "q8_0:2,5,6", "q9:2,5,8", "q8_0:2,5", "q8_0:16,5,32", "q8_0:8,5,32",
                 "q8_0:4,5,48,l5", "q8_0:4,5,48,l2", "q8_0:2,5,48,l4", "q8_0:4,10,48,l6", "q8_0:4,5,48,l", "q8_0:4,5,48,l6x",
-                "q8_0:4,10,48,P", "q8_0:4,5,40,P", "q8_0:4,5,1024,P"):  # P: nw != slices, rw % 16, LDS
+                "q8_0:4,10,48,P", "q8_0:4,5,40,P", "q8_0:4,5,1024,P",  # P: nw != slices, rw % 16, LDS
+                "q8_0:4,10,48,x3", "q8_0:4,10,48,x0x"):
         monkeypatch.setenv("QGEMV_TILE", bad)
         st, _ = _lib.qg_query_tile(0, 10240, 2560, 4)
         assert st == _lib.QG_EINVAL, bad

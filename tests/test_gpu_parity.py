@@ -297,48 +297,52 @@ def test_half_slice_tiny_and_dyadic(torch, orc, monkeypatch):
 
 
 # ------------------------------------ matrix cores on 256-wide slices (kind x)
-def mx_tile(cols, rw=40, rg=1, fmt="q8_0"):
-    return f"{fmt}:4,{(cols // 256) * rg},{rw},x"
+def mx_tile(cols, rw=40, rg=1, fmt="q8_0", r=1):
+    return f"{fmt}:4,{(cols // 256) * rg},{rw},x" + ("2" if r == 2 else "")
 
 
-@pytest.mark.parametrize("name,rw", [("c2a_q8_0_10240x2560", 40), ("c2a_q8_0_10240x2560", 32),
-                                     ("c1_q8_0_2560x2560", 16), ("c3_q4_0_8192x2560", 32),
-                                     ("c3_bf16_8192x2560", 32), ("c3_bf16_8192x2560", 40)])
-def test_mx_config_full(torch, orc, monkeypatch, name, rw):
-    """Matrix cores on 256-wide slices on the workloads: parity at every T, a token's bits equal across T."""
+@pytest.mark.parametrize("name,rw,r", [("c2a_q8_0_10240x2560", 40, 1), ("c2a_q8_0_10240x2560", 32, 1),
+                                       ("c1_q8_0_2560x2560", 16, 1), ("c3_q4_0_8192x2560", 32, 1),
+                                       ("c3_bf16_8192x2560", 32, 1), ("c3_bf16_8192x2560", 40, 1),
+                                       ("c2a_q8_0_10240x2560", 64, 2), ("c3_q4_0_8192x2560", 32, 2),
+                                       ("c3_q4_0_8192x2560", 48, 2), ("c1_q8_0_2560x2560", 32, 2)])
+def test_mx_config_full(torch, orc, monkeypatch, name, rw, r):
+    """Matrix cores on 256-wide slices on the workloads, tiles of 16 or 32 rows:
+    parity at every T, a token's bits equal across T."""
     c = I.dense_case(name)
-    monkeypatch.setenv("QGEMV_TILE", mx_tile(c["cols"], rw, fmt=NAMES[c["fmt"]]))
+    monkeypatch.setenv("QGEMV_TILE", mx_tile(c["cols"], rw, fmt=NAMES[c["fmt"]], r=r))
     st, t = _lib.qg_query_tile(c["fmt"], c["rows"], c["cols"], 4)
-    assert st == 0 and t[6] == 8 and t[3] == 256, (st, t)
-    check_dense(torch, orc, c["fmt"], c["rows"], c["cols"], c["W"], c["x"], f"mx {name} rw={rw}")
+    assert st == 0 and t[6] == 8 and t[3] == 256 and t[7] == r, (st, t)
+    check_dense(torch, orc, c["fmt"], c["rows"], c["cols"], c["W"], c["x"], f"mx {name} rw={rw} r={r}")
 
 
 def test_mx_row_tilings_keep_bits(torch, monkeypatch):
-    """The same 256-wide k split at any rows per workgroup and row groups: identical bits."""
+    """The same 256-wide k split at any rows per workgroup, row groups and tile
+    height (16 or 32 rows): identical bits."""
     c = I.dense_case("c2a_q8_0_10240x2560")
     Wd, xd = dev(torch, c["W"]), dev(torch, c["x"])
     monkeypatch.setenv("QGEMV_TILE", mx_tile(c["cols"], 48))
     base = ops.gemv("q8_0", Wd, xd, c["rows"]).cpu().numpy()
-    for rw in (16, 24, 40, 64, 200):
-        monkeypatch.setenv("QGEMV_TILE", mx_tile(c["cols"], rw))
-        say(f"[mx tiling] rw={rw}")
-        assert np.array_equal(ops.gemv("q8_0", Wd, xd, c["rows"]).cpu().numpy(), base), rw
+    for rw, r in ((16, 1), (24, 1), (40, 1), (64, 1), (200, 1), (32, 2), (48, 2), (64, 2), (96, 2)):
+        monkeypatch.setenv("QGEMV_TILE", mx_tile(c["cols"], rw, r=r))
+        say(f"[mx tiling] rw={rw} r={r}")
+        assert np.array_equal(ops.gemv("q8_0", Wd, xd, c["rows"]).cpu().numpy(), base), (rw, r)
 
 
 def test_mx_tiny_ragged_and_row_groups(torch, orc, monkeypatch):
-    """Ragged rows (a partial last 16-row tile, waves with no tile), one to twelve
-    slices, two and three row groups, every format."""
+    """Ragged rows (a partial last tile, waves with no tile), one to twelve
+    slices, two and three row groups, tiles of 16 and 32 rows, every format."""
     for fmt in (Q8, Q4, BF):
         for rows in TINY_ROWS + (40, 100):
             for cols in (256, 512, 768, 1280, 2304, 3072):
-                for rw, rg in ((16, 1), (40, 1), (24, 2), (48, 3)):
-                    monkeypatch.setenv("QGEMV_TILE", mx_tile(cols, rw, rg, NAMES[fmt]))
+                for rw, rg, r in ((16, 1, 1), (40, 1, 1), (24, 2, 1), (48, 3, 1), (32, 1, 2), (40, 2, 2)):
+                    monkeypatch.setenv("QGEMV_TILE", mx_tile(cols, rw, rg, NAMES[fmt], r))
                     if _lib.qg_query_tile(fmt, rows, cols, 4)[0]:
                         continue  # more than twelve waves, or past the LDS
                     rng = np.random.default_rng(rows * 1000 + cols + rw + fmt)
                     W = I.weights(rng, fmt, rows, cols)
                     x = I.activations(rng, cols)
-                    check_dense(torch, orc, fmt, rows, cols, W, x, f"mx tiny rw={rw} rg={rg}")
+                    check_dense(torch, orc, fmt, rows, cols, W, x, f"mx tiny rw={rw} rg={rg} r={r}")
 
 
 def test_mx_exact_inputs_bitwise(torch, orc, monkeypatch):
@@ -589,8 +593,8 @@ def test_argmax_ties_negatives_and_kinds(torch, orc, monkeypatch):
                 W[r * rb:(r + 1) * rb] = W[best * rb:(best + 1) * rb]
         neg = -np.abs(x)  # a second activation pattern
         for kind_tile in (None, "q8_0:4,{nsl},40,l3", "q8_0:4,{nsl},48,L2", "q8_0:4,{nsl},16,s", "q8_0:2,{nsl},4,d",
-                          "q8_0:8,{nsl},64,p", "q8_0:4,{nsl256},40,x", "q8_0:4,{nsl256},24,h2",
-                          "q8_0:4,{nsl},32,P"):
+                          "q8_0:8,{nsl},64,p", "q8_0:4,{nsl256},40,x", "q8_0:4,{nsl256},64,x2",
+                          "q8_0:4,{nsl256},24,h2", "q8_0:4,{nsl},32,P"):
             nsl, nsl256 = -(-cols // 512), cols // 256
             if "{nsl256}" in (kind_tile or "") and cols % 256:
                 continue  # 256-wide slices
@@ -713,6 +717,7 @@ def test_grouped_sharing(torch, orc, monkeypatch, fmt):
     n_experts, rows = 12, 200
     for cols, tile in ((1024, None), (1024, f"{NAMES[fmt]}:4,2,8,d"), (1024, f"{NAMES[fmt]}:4,2,24,L2"),
                        (1024, f"{NAMES[fmt]}:4,8,64,x"), (768, f"{NAMES[fmt]}:4,3,16,x"),
+                       (1024, f"{NAMES[fmt]}:4,4,64,x2"), (768, f"{NAMES[fmt]}:4,6,32,x2"),
                        (1056 if fmt != BF else 1048, None)):
         if tile:
             monkeypatch.setenv("QGEMV_TILE", tile)
