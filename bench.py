@@ -67,8 +67,10 @@ def time_calls(torch, fmt, ring, x_dev, rows, T, calls, stream, y_dev):
 
 def kernel_name(tile, T):
     """Device symbol of the kernel a call with ``tile`` launches (Q8_0)."""
+    if tile["kind"] == 9:
+        return f"qgemv_mxp_kernel<0, {T}>"
     if tile["kind"] == 8:
-        return f"qgemv_mx_kernel<0, {T}>"
+        return f"qgemv_mx_kernel<0, {T}, {2 if tile['depth'] == 2 else 1}>"
     if tile["kind"] == 7:
         return f"qgemv_half_kernel<0, {T}, {tile['depth']}>"
     if tile["kind"] in (2, 3):
@@ -384,10 +386,18 @@ def _numeric_leaves(obj, path=""):
 CLOCK_CMD = ["amd-smi", "metric", "-g", "0", "--clock", "--power", "--json"]
 
 
+def under_profiler():
+    """True when a rocprofv3 tool library is preloaded: its children (amd-smi is a
+    Python script started through env) would inherit it, so no clock is sampled."""
+    return "rocprof" in os.environ.get("LD_PRELOAD", "")
+
+
 def gpu_clocks():
     """One amd-smi sample of GPU 0's clocks and power (a child process; the values
     are what the tool reports, MHz and W), or the reason there is none."""
     import subprocess
+    if under_profiler():
+        return {"skipped": "under rocprofv3"}
     try:
         r = subprocess.run(CLOCK_CMD, capture_output=True, text=True, timeout=20)
     except (OSError, subprocess.SubprocessError) as e:
@@ -409,10 +419,14 @@ def clocks_under_load(torch, batch, min_s):
     clocks the calls run at (an idle GPU drops to its idle clock within a fraction
     of a second); returns the sample."""
     import subprocess
-    try:
-        p = subprocess.Popen(CLOCK_CMD, stdout=subprocess.PIPE, stderr=subprocess.DEVNULL, text=True)
-    except OSError as e:
-        p, res = None, {"error": f"amd-smi: {type(e).__name__}: {str(e)[:200]}"}
+    p = None
+    if under_profiler():
+        res = {"skipped": "under rocprofv3"}
+    else:
+        try:
+            p = subprocess.Popen(CLOCK_CMD, stdout=subprocess.PIPE, stderr=subprocess.DEVNULL, text=True)
+        except OSError as e:
+            res = {"error": f"amd-smi: {type(e).__name__}: {str(e)[:200]}"}
     t0 = time.perf_counter()
     while time.perf_counter() - t0 < min_s or (p is not None and p.poll() is None):
         batch()
@@ -569,8 +583,8 @@ PROFILE_WORKLOADS = ("c1_q8_0_2560x2560", "c2a_q8_0_10240x2560", "c2b_q8_0_2560x
                      "c3_bf16_8192x2560", "c4_q8_0_248320x5120", "c4_argmax", "c5_q4_0_experts")
 
 
-def profile_workload(torch, stream, name, calls, tiles):
-    """Untimed calls for rocprofv3 to trace or count: ``calls`` calls at each T = 1..4
+def profile_workload(torch, stream, name, calls, tiles, Ts=(1, 2, 3, 4)):
+    """Untimed calls for rocprofv3 to trace or count: ``calls`` calls at each T in ``Ts``
     of one workload for each tile spec in ``tiles`` ("default" = the library's own
     tile; a spec outside what the library runs at some T is skipped there), walking a
     ring of device-random weights of >= 1 GiB so every call streams from HBM."""
@@ -616,7 +630,7 @@ def profile_workload(torch, stream, name, calls, tiles):
                 _os.environ.pop("QGEMV_TILE", None)
             else:
                 _os.environ["QGEMV_TILE"] = f"{fmt_name}:{spec}"
-            for T in (1, 2, 3, 4):
+            for T in Ts:
                 if call(T, 0) != _lib.QG_OK:
                     log(f"profile: {name} tile {spec} T={T} not run: {_lib.last_error()}")
                     continue
@@ -645,6 +659,7 @@ def main():
                     help="untimed calls of one workload for rocprofv3 (see --calls, --tiles); no JSON line")
     ap.add_argument("--calls", type=int, default=20, help="calls per T and tile with --profile")
     ap.add_argument("--tiles", default="default", help="space-separated QGEMV_TILE specs for --profile")
+    ap.add_argument("--profile-t", default="1,2,3,4", help="comma-separated token counts for --profile")
     ap.add_argument("--bytes", type=int, default=0, help="algorithmic bytes per launch for --summarize-pmc")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="print the HBM traffic table from two rocprofv3 --pmc runs of this script and exit")
@@ -678,7 +693,10 @@ def main():
     torch.cuda.set_device(0)
     stream = torch.cuda.current_stream()
     if args.profile:
-        profile_workload(torch, stream, args.profile, args.calls, args.tiles.split())
+        Ts = tuple(int(t) for t in args.profile_t.split(","))
+        if any(t < 1 or t > 4 for t in Ts):
+            sys.exit("--profile-t: token counts are 1..4")
+        profile_workload(torch, stream, args.profile, args.calls, args.tiles.split(), Ts)
         if args.copy_calibration:
             nb = _lib.qg_packed_bytes(I.FMT_Q8_0, 10240, 2560)
             src = torch.empty(nb // 4, dtype=torch.float32, device="cuda").fill_(1.0)

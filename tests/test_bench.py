@@ -31,6 +31,9 @@ def test_kernel_names_follow_the_tile():
     assert bench.kernel_name(dict(base, kind=4, depth=3), 2) == "qgemv_units_kernel<0, 2, 3>"
     assert bench.kernel_name(dict(base, kind=0, depth=0, rows_per_wg=8), 1) == "qgemv_dense_kernel<0, 1, 4, true>"
     assert bench.kernel_name(dict(base, kind=7, waves_per_wg=10, depth=2), 4) == "qgemv_half_kernel<0, 4, 2>"
+    assert bench.kernel_name(dict(base, kind=8, waves_per_wg=10, depth=1), 3) == "qgemv_mx_kernel<0, 3, 1>"
+    assert bench.kernel_name(dict(base, kind=8, waves_per_wg=10, depth=2), 1) == "qgemv_mx_kernel<0, 1, 2>"
+    assert bench.kernel_name(dict(base, kind=9, waves_per_wg=10, depth=1), 4) == "qgemv_mxp_kernel<0, 4>"
 
 
 def _write_pmc(dirpath, counter, rows):
@@ -102,3 +105,11 @@ def test_clock_fields_keep_clocks_and_power():
 
 def test_clock_sample_never_raises():
     assert isinstance(bench.gpu_clocks(), dict)  # without a GPU: the reason, not an exception
+
+
+def test_no_clock_sampling_under_the_profiler(monkeypatch):
+    """amd-smi is a script started through env: under rocprofv3 its process would
+    inherit the tool library, so the bench takes no sample there."""
+    monkeypatch.setenv("LD_PRELOAD", "/opt/rocm/lib/rocprofiler-sdk/librocprofiler-sdk-tool.so")
+    assert bench.gpu_clocks() == {"skipped": "under rocprofv3"}
+    assert bench.clocks_under_load(None, lambda: None, 0.0) == {"skipped": "under rocprofv3"}
