@@ -529,9 +529,8 @@ int run_grouped(int fmt, int64_t n_experts, int64_t rows, int64_t cols, int T, i
     const int64_t nsl256 = cols / 256;
     const bool mx_ok = cols % 256 == 0 && nsl256 <= kMaxWaves && rbytes * 16 < 0x7FFFFFFF;
     if (!overridden && mx_ok) {
-        // the matrix cores on 256-wide slices (kind 8's tiles); fewer than 4 slices
-        // (the down projection's short rows): row groups of waves, 4 waves or more.
-        // Rows per workgroup: the fewest that keep all slots' workgroups within
+        // the matrix cores on 256-wide slices (kind 8's tiles), one wave per slice.
+        // Rows per workgroup for 4 slices or more: the fewest that keep all slots' workgroups within
         // one per CU (256 experts of 512 x 2560 Q4_0, 10 slots a token, µs at
         // T = 1..4: 32 rows 7.4 / 12.9 / 13.2 / 18.8, 48 rows 8.6 / 8.8 / 15.7 / 15.9,
         // 64 rows 10.0 / 10.1 / 10.3 / 18.4, 96 rows 12.6 / 12.7 / 12.8 / 13.0: more
@@ -541,11 +540,19 @@ int run_grouped(int fmt, int64_t n_experts, int64_t rows, int64_t cols, int T, i
         tile.depth = 1;
         tile.mfma = 0;
         tile.rows_per_batch = 4;
-        const int64_t rg = nsl256 >= 4 ? 1 : (4 + nsl256 - 1) / nsl256;
-        tile.waves_per_wg = (int)(nsl256 * rg);
+        tile.waves_per_wg = (int)nsl256;
         const int64_t slots = (int64_t)T * topk * parts;
-        int64_t rw = 16 * rg;
-        while (rw < 512 && rw < rows && slots * ((rows + rw - 1) / rw) > kPersistGrid) rw += 16;
+        int64_t rw = 16;
+        if (nsl256 >= 4) {
+            while (rw < 512 && rw < rows && slots * ((rows + rw - 1) / rw) > kPersistGrid) rw += 16;
+        } else {
+            // short rows (the down projection, 2560 x 512 Q4_0): small workgroups of one
+            // wave per slice, many of them per CU; 32 rows at T = 1, 64 from T = 2 (10 slots
+            // a token at share 0.65, µs at T = 1..4: 6.4 / 8.2 / 9.4 / 11.2, against 6.9 /
+            // 9.2 / 11.5 / 14.5 for the rule above with two row groups of waves)
+            rw = (slots * rows / 800 + 15) / 16 * 16;
+            rw = rw < 16 ? 16 : rw > 64 ? 64 : rw;
+        }
         tile.rows_per_wg = (int)rw;
         while (tile.rows_per_wg > 16 && mx_lds_bytes(fmt, tile, T, (int)nsl256) > kMaxLds) tile.rows_per_wg -= 16;
     }
