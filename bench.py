@@ -69,8 +69,10 @@ def kernel_name(tile, T):
     """Device symbol of the kernel a call with ``tile`` launches (Q8_0)."""
     if tile["kind"] == 9:
         return f"qgemv_mxp_kernel<0, {T}>"
+    if tile["kind"] == 11:
+        return f"qgemv_mx_kernel<0, {T}, 1, 2>"
     if tile["kind"] == 8:
-        return f"qgemv_mx_kernel<0, {T}, {2 if tile['depth'] == 2 else 1}>"
+        return f"qgemv_mx_kernel<0, {T}, {2 if tile['depth'] == 2 else 1}, 1>"
     if tile["kind"] == 7:
         return f"qgemv_half_kernel<0, {T}, {tile['depth']}>"
     if tile["kind"] in (2, 3):

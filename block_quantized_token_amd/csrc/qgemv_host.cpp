@@ -63,8 +63,8 @@ bool parse_tile_spec(const std::string& spec, Tile* t, std::string* why) {
     }
     const bool dma = kind == 'l' || kind == 'L' || kind == 'u' || kind == 'h';
     if (!(got == 3 || (got == 4 && (kind == 'd' || kind == 's' || kind == 'm' || kind == 'p' || kind == 'P' ||
-                                     (kind == 'x' && depth >= 0 && depth <= 2) || (dma && depth > 0))))) {
-        *why = "tile '" + spec + "' is not rb,nw,rw[,d|s|m|p|x|x2|P|l<depth>|L<depth>|u<depth>|h<depth>]";
+                                     kind == 'X' || (kind == 'x' && depth >= 0 && depth <= 2) || (dma && depth > 0))))) {
+        *why = "tile '" + spec + "' is not rb,nw,rw[,d|s|m|p|x|x2|X|P|l<depth>|L<depth>|u<depth>|h<depth>]";
         return false;
     }
     if (!valid_rb(rb) || nw < 1 || nw > kMaxWaves || rw < 2 * rb || rw % (2 * rb) || rw > (1 << 20)) {
@@ -75,10 +75,11 @@ bool parse_tile_spec(const std::string& spec, Tile* t, std::string* why) {
     t->waves_per_wg = nw;
     t->rows_per_wg = rw;
     t->kind = got == 4 ? (kind == 'd' ? 0 : kind == 'l' ? 2 : kind == 'L' ? 3 : kind == 'u' ? 4 : kind == 'h' ? 7
-                          : kind == 'x' ? 8 : kind == 'P' ? 9 : 1)
+                          : kind == 'x' ? 8 : kind == 'P' ? 9 : kind == 'X' ? 11 : 1)
                        : -1;  // -1: later
     t->mfma = got == 4 && kind == 'm' ? 1 : got == 4 && kind == 'p' ? 2 : 0;
-    t->depth = got == 4 && dma ? depth : got == 4 && kind == 'x' ? (depth ? depth : 1) : got == 4 && kind == 'P' ? 1 : 0;
+    t->depth = got == 4 && dma ? depth : got == 4 && kind == 'x' ? (depth ? depth : 1)
+             : got == 4 && (kind == 'P' || kind == 'X') ? 1 : 0;
     return true;
 }
 
@@ -110,7 +111,10 @@ const TuneEntry kTuned[] = {
     {QG_FMT_Q8_0, 2560, 2560, 0, "4,10,16,x"},
     {QG_FMT_Q4_0, 8192, 2560, 0, "4,10,32,x"},
     {QG_FMT_BF16, 8192, 2560, 0, "4,10,32,x"},
-    {QG_FMT_Q8_0, 2560, 6144, 0, "4,12,16,s"},     // register-streamed beats DMA at 12 slices
+    // 2560 x 6144 Q8_0 (24 256-wide slices, more than twelve waves): the matrix cores
+    // on 512-wide slices, 7.2 / 7.7 / 8.1 / 8.7 µs against 7.3 / 7.8 / 8.7 / 9.4 for the
+    // register-streamed vector-ALU kernel
+    {QG_FMT_Q8_0, 2560, 6144, 0, "4,12,16,X"},
     // LM head, 248,320 x 5,120 Q8_0: the persistent matrix-core kernel on the
     // LDS-DMA ring, one kind at every T, so a token's bits do not depend on T:
     // 234 / 237 / 241 / 245 µs at T = 1..4 against 234 / 243 / 269 / 279 for the
@@ -158,6 +162,19 @@ Tile default_tile(int fmt, int64_t rows, int64_t cols, int T) {
         t.rows_per_wg = (int)(rw > 1024 ? 1024 : rw);
         while (t.rows_per_wg > 16 && mx_lds_bytes(fmt, t, T, t.waves_per_wg) > kMaxLds) t.rows_per_wg -= 16;
         if (mx_lds_bytes(fmt, t, T, t.waves_per_wg) <= kMaxLds) return t;
+        t.kind = 0;
+        t.depth = 0;
+    }
+    // more than 12 256-wide slices, up to 12 512-wide ones: the same on 512-wide slices
+    if (cols % kSlice == 0 && nslices <= kMaxWaves && row_bytes(fmt, cols) * 16 < 0x7FFFFFFF) {
+        t.kind = 11;
+        t.depth = 1;
+        t.rows_per_batch = 4;
+        t.waves_per_wg = (int)nslices;
+        int64_t rw = ((rows + 255) / 256 + 15) / 16 * 16;
+        t.rows_per_wg = (int)(rw > 1024 ? 1024 : rw);
+        while (t.rows_per_wg > 16 && mx_lds_bytes(fmt, t, T, (int)nslices) > kMaxLds) t.rows_per_wg -= 16;
+        if (mx_lds_bytes(fmt, t, T, (int)nslices) <= kMaxLds) return t;
         t.kind = 0;
         t.depth = 0;
     }
@@ -279,6 +296,17 @@ int pick_tile(int fmt, int64_t rows, int64_t cols, int T, Tile* t) {
                         t->rows_per_wg);
         return QG_OK;
     }
+    if (t->kind == 11) {
+        if (cols % kSlice || t->waves_per_wg % nslices != 0)
+            return fail(QG_EINVAL, "matrix-core 512-wide-slice tile needs cols a multiple of 512 and waves_per_wg a "
+                                   "multiple of the %lld 512-wide slices", (long long)nslices);
+        if (row_bytes(fmt, cols) * 16 > 0x7FFFFFFF)
+            return fail(QG_EINVAL, "matrix-core 512-wide-slice tile needs 16 rows within a 2 GB descriptor");
+        if (mx_lds_bytes(fmt, *t, T, (int)nslices) > kMaxLds)
+            return fail(QG_EINVAL, "tile needs %zu B of LDS (rows_per_wg %d too large)",
+                        mx_lds_bytes(fmt, *t, T, (int)nslices), t->rows_per_wg);
+        return QG_OK;
+    }
     if (t->kind == 8) {
         const int64_t nsl256 = cols / 256;
         if (cols % 256 || t->waves_per_wg % nsl256 != 0)
@@ -389,7 +417,7 @@ int run_dense(int fmt, int64_t rows, int64_t cols, int T, const void* W, const f
     a.rows_per_wg = tile.rows_per_wg;
     if ((rows + tile.rows_per_wg - 1) / tile.rows_per_wg > 0x7FFFFFFF) return fail(QG_EUNSUPPORTED, "grid too large");
     int err = tile.kind == 9   ? launch_mxp(fmt, T, tile, a, stream)
-              : tile.kind == 8 ? launch_mx(fmt, T, tile, a, stream)
+              : tile.kind == 8 || tile.kind == 11 ? launch_mx(fmt, T, tile, a, stream)
               : tile.kind == 7 ? launch_half(fmt, T, tile, a, stream)
               : tile.kind == 4 ? launch_units(fmt, T, tile, a, stream)
               : tile.kind >= 2 ? launch_dma(fmt, T, tile, a, stream)
@@ -430,6 +458,7 @@ int run_argmax(int fmt, int64_t rows, int64_t cols, int T, const void* W, const 
     if (tile.kind == 7 && half_lds_bytes(fmt, tile, T, (int)(cols / 256)) > kMaxLds) tile.kind = 0;
     if (tile.kind == 8 && mx_lds_bytes(fmt, tile, T, (int)(cols / 256)) > kMaxLds) tile.kind = 0;
     if (tile.kind == 9 && mxp_lds_bytes(fmt, tile, T) > kMaxLds) tile.kind = 0;
+    if (tile.kind == 11 && mx_lds_bytes(fmt, tile, T, (int)(cols / 512)) > kMaxLds) tile.kind = 0;
     if (tile.kind == 4 || (tile.kind == 1 && tile.mfma == 1)) tile.kind = 0;
     if (tile.kind == 1 && !persist && (tile.rows_per_batch != 4 || !stream_supported(fmt, T, 4))) tile.kind = 0;
     if (tile.kind == 0) {  // direct, rb 2, one wave per slice when the slices fit a workgroup
@@ -799,7 +828,7 @@ int qg_query_tile(int fmt, int64_t rows, int64_t cols, int T, int out_tile[QG_TI
     int st = pick_tile(fmt, rows, cols, T, &t);
     if (st) return st;
     const bool half = t.kind == 7 || t.kind == 8;  // 256-wide k slices
-    out_tile[0] = t.kind >= 8 ? 4 : half ? 16 : t.lanes_per_row;  // kinds 8, 9: a row's block sits in 4 lanes
+    out_tile[0] = t.kind >= 8 ? 4 : half ? 16 : t.lanes_per_row;  // kinds 8, 9, 11: a row's block sits in 4 lanes
     out_tile[1] = t.rows_per_batch;
     out_tile[2] = t.waves_per_wg;
     out_tile[3] = half ? 256 : t.k_slice;

@@ -23,7 +23,8 @@ struct Tile {
                          // 4: unit-balanced LDS-DMA (waves take equal shares of (slice, tile) units);
                          // 7: LDS-DMA on 256-wide k slices, 16 lanes per row; 8: matrix cores on
                          // 256-wide k slices fed by LDS-DMA loads of 16-row tiles; 9: persistent
-                         // matrix cores on 512-wide slices fed by LDS-DMA loads
+                         // matrix cores on 512-wide slices fed by LDS-DMA loads; 11: kind 8 on
+                         // 512-wide slices
     int depth;           // kinds 2, 3: tiles in flight per wave (2, 3, 4 or 6); kind 4: 2..4; kind 7: 2, 3; 0 otherwise
 };
 
@@ -107,12 +108,16 @@ inline size_t half_lds_bytes(int fmt, const Tile& t, int T, int nslices256) {
 // Kind 8 (matrix cores on 256-wide slices): one tile slot per wave (exactly the tile's
 // bytes), a region per wave for one token's bf16 pieces (1536 bytes), then partial
 // sums [tiles][slices][tile rows][pad(T)].
-// `depth` is the tile's groups of 16 rows (1 or 2).
-inline size_t mx_slot_bytes(int fmt, int R = 1) { return (size_t)16 * R * (stream_chunks(fmt) / 2) * 16; }
-inline size_t mx_lds_bytes(int fmt, const Tile& t, int T, int nslices256) {
-    const int R = t.depth == 2 ? 2 : 1;
+// `depth` is the tile's groups of 16 rows (1 or 2); kind 11 is kind 8 on 512-wide
+// slices (two 256-wide halves, 16-row tiles), `nslices` the slices of its width.
+inline size_t mx_slot_bytes(int fmt, int R = 1, int H = 1) {
+    return (size_t)16 * R * (stream_chunks(fmt) / 2) * H * 16;
+}
+inline size_t mx_lds_bytes(int fmt, const Tile& t, int T, int nslices) {
+    const int H = t.kind == 11 ? 2 : 1;
+    const int R = t.depth == 2 && H == 1 ? 2 : 1;
     const size_t ntiles = (size_t)(t.rows_per_wg + 16 * R - 1) / (16 * R);
-    return (size_t)t.waves_per_wg * (mx_slot_bytes(fmt, R) + 1536) + ntiles * nslices256 * 16 * R * pad_tokens(T) * 4;
+    return (size_t)t.waves_per_wg * (mx_slot_bytes(fmt, R, H) + 1536) + ntiles * nslices * 16 * R * pad_tokens(T) * 4;
 }
 
 // Kind 9 (persistent matrix cores on 512-wide slices): one 16-row tile slot per wave

@@ -1592,10 +1592,11 @@ __device__ __forceinline__ void mfma_persist_q8(const uint8_t* __restrict__ W, i
 // in registers; measured on 10240 x 2560, a second tile in flight or a refill
 // after the math is slower (the vector-ALU kernels behave alike).
 // A tile is R groups of 16 rows (R = 2: twice the bytes in flight per wave, for
-// the formats with short rows).
-template <int FMT, int R = 1>
+// the formats with short rows) of a slice of H 256-wide halves (H = 2: 512-wide
+// slices, 16 blocks a wave, for rows of more than twelve 256-wide slices).
+template <int FMT, int R = 1, int H = 1>
 struct MxShape {
-    static constexpr int kChunks = StreamFmt<FMT>::kChunks / 2;          // 16-byte chunks of a 256-wide row slice
+    static constexpr int kChunks = StreamFmt<FMT>::kChunks / 2 * H;      // 16-byte chunks of a row slice
     static constexpr int kRows = 16 * R;                                  // rows of a tile
     static constexpr int kSlot = kRows * kChunks * 16;                    // 16 rows: 4352, 2304, 8192 B
     static constexpr int kLoads = (kRows * kChunks + 63) / 64;            // 16 rows: 5, 3, 8
@@ -1607,11 +1608,11 @@ struct MxShape {
 // 64 k + l (row / chunk of the slice); lanes past the tile's last chunk do not
 // load, so the slot is exactly the tile's bytes; rows past the range are
 // outside the descriptor and read as zeros.
-template <int FMT, int R = 1>
+template <int FMT, int R = 1, int H = 1>
 __device__ __forceinline__ void mx_issue(const uint8_t* __restrict__ W, int64_t row_bytes, int64_t row_begin,
-                                         int64_t row_end, int ntiles, int t, const int (&off)[MxShape<FMT, R>::kLoads],
+                                         int64_t row_end, int ntiles, int t, const int (&off)[MxShape<FMT, R, H>::kLoads],
                                          uint8_t* slot, int lane) {
-    using M = MxShape<FMT, R>;
+    using M = MxShape<FMT, R, H>;
     const bool live = t < ntiles;
     const int64_t r0 = row_begin + (int64_t)(live ? t : 0) * M::kRows;
     const int64_t rows_here = row_end - r0 < M::kRows ? row_end - r0 : M::kRows;
@@ -1716,20 +1717,25 @@ __device__ __forceinline__ void mx_prefetch(const uint8_t* __restrict__ W, int64
 }
 
 // x of token t of the wave's slice: lane l holds k = 4 l .. 4 l + 3 of the
-// slice's 256 in xv[t] (one coalesced 1 KB row per token, loaded by the caller).
-template <int FMT, int NT>
+// slice's 256-wide half h in xv[t][h] (one coalesced 1 KB row per token and
+// half, loaded by the caller).
+template <int FMT, int NT, int H = 1>
 __device__ __forceinline__ void mx_load_x(const float* __restrict__ x, const int64_t (&xoff)[NT], int nsl,
-                                          float4 (&xv)[NT]) {
-    const int k0 = ((int)__builtin_amdgcn_readfirstlane(threadIdx.x >> 6) % nsl) * kHalfSlice;
+                                          float4 (&xv)[NT][H]) {
+    const int k0 = ((int)__builtin_amdgcn_readfirstlane(threadIdx.x >> 6) % nsl) * (kHalfSlice * H);
 #pragma unroll
-    for (int t = 0; t < NT; ++t) xv[t] = *reinterpret_cast<const float4*>(x + xoff[t] + k0 + 4 * (threadIdx.x & 63));
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+        for (int h = 0; h < H; ++h)
+            xv[t][h] = *reinterpret_cast<const float4*>(x + xoff[t] + k0 + kHalfSlice * h + 4 * (threadIdx.x & 63));
 }
 
-template <int FMT, int NT, int R, bool PRE = false, class Out>
+template <int FMT, int NT, int R, bool PRE = false, int H = 1, class Out>
 __device__ __forceinline__ void mx_rows(const uint8_t* __restrict__ W, int64_t row_bytes, int nsl,
-                                        const float4 (&xv)[NT], int64_t row_begin, int64_t row_end, int nw,
+                                        const float4 (&xv)[NT][H], int64_t row_begin, int64_t row_end, int nw,
                                         Out&& out) {
-    using M = MxShape<FMT, R>;
+    using M = MxShape<FMT, R, H>;
+    constexpr int NB = 8 * H;  // blocks of a wave's slice
     constexpr int RT = M::kRows;
     constexpr int TP = pad_pow2(NT);
     constexpr int L = M::kLoads;
@@ -1754,22 +1760,24 @@ __device__ __forceinline__ void mx_rows(const uint8_t* __restrict__ W, int64_t r
         off[k] = r < RT ? (int)(r * row_bytes) + s * M::kChunks * 16 + 16 * c : kNoLoad;
     }
     // the wave's first tile, unless PRE has it on its way already (x is older)
-    if constexpr (!PRE) mx_issue<FMT, R>(W, row_bytes, row_begin, row_end, ntiles, rg, off, slot, lane);
+    if constexpr (!PRE) mx_issue<FMT, R, H>(W, row_bytes, row_begin, row_end, ntiles, rg, off, slot, lane);
 
-    // split, one token at a time through the wave's region: piece p of x[t][k] goes
-    // to the 16-byte fragment (block k / 32, group (k % 32) / 8, piece p), which the
-    // lane of A's row 4p + t and group (k % 32) / 8 then reads.  A wave's LDS
-    // operations take effect in program order, so the next token's writes land
-    // after this token's reads.
-    V4 afrag[8];
+    // split, one token and 256-wide half at a time through the wave's region: piece
+    // p of x[t][k] goes to the 16-byte fragment (block k / 32, group (k % 32) / 8,
+    // piece p), which the lane of A's row 4p + t and group (k % 32) / 8 then reads.
+    // A wave's LDS operations take effect in program order, so the next round's
+    // writes land after this round's reads.
+    V4 afrag[NB];
     {
         const int b = lane >> 3, gg = (lane & 7) >> 1, half = (lane & 1) * 8;
         const int am = lane & 15, ap = am >> 2, at = am & 3;
 #pragma unroll
-        for (int bb = 0; bb < 8; ++bb) afrag[bb] = V4{0u, 0u, 0u, 0u};
+        for (int bb = 0; bb < NB; ++bb) afrag[bb] = V4{0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int hx = 0; hx < H; ++hx)
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
-            const float vv[4] = {xv[t].x, xv[t].y, xv[t].z, xv[t].w};
+            const float vv[4] = {xv[t][hx].x, xv[t][hx].y, xv[t][hx].z, xv[t][hx].w};
             uint32_t pc[3][4];
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
@@ -1792,7 +1800,8 @@ __device__ __forceinline__ void mx_rows(const uint8_t* __restrict__ W, int64_t r
             }
             if (ap < 3 && at == t) {
 #pragma unroll
-                for (int bb = 0; bb < 8; ++bb) afrag[bb] = *reinterpret_cast<const V4*>(reg + bb * 192 + (g * 3 + ap) * 16);
+                for (int bb = 0; bb < 8; ++bb)
+                    afrag[8 * hx + bb] = *reinterpret_cast<const V4*>(reg + bb * 192 + (g * 3 + ap) * 16);
             }
         }
     }
@@ -1802,18 +1811,18 @@ __device__ __forceinline__ void mx_rows(const uint8_t* __restrict__ W, int64_t r
     for (int i = 0; i < mine; ++i) {
         const int t = rg + i * RG;
         wait_vmcnt<0>();  // the slot holds tile t
-        MxRaw raw[R][8];
+        MxRaw raw[R][NB];
 #pragma unroll
         for (int h = 0; h < R; ++h)
 #pragma unroll
-            for (int b = 0; b < 8; ++b) raw[h][b] = mx_braw<FMT>(rowp + 16 * h * (M::kChunks * 16), b, g);
+            for (int b = 0; b < NB; ++b) raw[h][b] = mx_braw<FMT>(rowp + 16 * h * (M::kChunks * 16), b, g);
         wait_lgkmcnt0();  // the tile is in registers: the slot takes the next one
-        if (i + 1 < mine) mx_issue<FMT, R>(W, row_bytes, row_begin, row_end, ntiles, t + RG, off, slot, lane);
+        if (i + 1 < mine) mx_issue<FMT, R, H>(W, row_bytes, row_begin, row_end, ntiles, t + RG, off, slot, lane);
 #pragma unroll
         for (int h = 0; h < R; ++h) {
             F4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-            for (int b = 0; b < 8; ++b) {
+            for (int b = 0; b < NB; ++b) {
                 float dq;
                 const V4 bq = mx_bconv<FMT>(raw[h][b], b, g, dq);
                 if constexpr (FMT == QG_FMT_BF16) {
@@ -2204,7 +2213,7 @@ qgemv_half_kernel(const uint8_t* __restrict__ W, const float* __restrict__ x, fl
                          [=](int t, int64_t row, float v) { y[t * rows + row] = v; });
 }
 
-template <int FMT, int T, int R>
+template <int FMT, int T, int R, int H>
 __global__ void __launch_bounds__(64 * kMaxWaves)
 qgemv_mx_kernel(const uint8_t* __restrict__ W, const float* __restrict__ x, float* __restrict__ y, int64_t rows,
                 int64_t row_bytes, int cols, int nslices, int rows_per_wg, int nw) {
@@ -2213,9 +2222,9 @@ qgemv_mx_kernel(const uint8_t* __restrict__ W, const float* __restrict__ x, floa
     int64_t xoff[T];
 #pragma unroll
     for (int t = 0; t < T; ++t) xoff[t] = (int64_t)t * cols;
-    float4 xv[T];
-    mx_load_x<FMT, T>(x, xoff, nslices, xv);
-    mx_rows<FMT, T, R>(W, row_bytes, nslices, xv, row_begin, row_end, nw,
+    float4 xv[T][H];
+    mx_load_x<FMT, T, H>(x, xoff, nslices, xv);
+    mx_rows<FMT, T, R, false, H>(W, row_bytes, nslices, xv, row_begin, row_end, nw,
                     [=](int t, int64_t row, float v) { y[t * rows + row] = v; });
 }
 
@@ -2277,7 +2286,7 @@ __global__ void __launch_bounds__(64 * kMaxWaves) qgemv_mxp_argmax_kernel(DenseA
     best.merge(work);
 }
 
-template <int FMT, int T, int R>
+template <int FMT, int T, int R, int H>
 __global__ void __launch_bounds__(64 * kMaxWaves) qgemv_mx_argmax_kernel(DenseArgs a, unsigned long long* work) {
     const int64_t row_begin = (int64_t)blockIdx.x * a.rows_per_wg;
     const int64_t row_end = row_begin + a.rows_per_wg < a.rows ? row_begin + a.rows_per_wg : a.rows;
@@ -2285,9 +2294,9 @@ __global__ void __launch_bounds__(64 * kMaxWaves) qgemv_mx_argmax_kernel(DenseAr
     int64_t xoff[T];
 #pragma unroll
     for (int t = 0; t < T; ++t) xoff[t] = (int64_t)t * a.cols;
-    float4 xv[T];
-    mx_load_x<FMT, T>(a.x, xoff, a.nslices, xv);
-    mx_rows<FMT, T, R>(a.W, a.row_bytes, a.nslices, xv, row_begin, row_end, (int)(blockDim.x >> 6), best);
+    float4 xv[T][H];
+    mx_load_x<FMT, T, H>(a.x, xoff, a.nslices, xv);
+    mx_rows<FMT, T, R, false, H>(a.W, a.row_bytes, a.nslices, xv, row_begin, row_end, (int)(blockDim.x >> 6), best);
     best.merge(work);
 }
 
@@ -2578,7 +2587,7 @@ __device__ __forceinline__ void grouped_mx_run(const GroupedArgs& a, const uint8
                                                const GroupTargets& g, const float4 (&xall)[QG_MAX_T],
                                                int64_t row_begin, int64_t row_end) {
     const int nsl = a.cols / kHalfSlice;
-    float4 xv[NE];
+    float4 xv[NE][1];
     if (a.per_slot_x) {
         int64_t xoff[NE];
         group_offsets<NE>(a, g, xoff);
@@ -2591,7 +2600,7 @@ __device__ __forceinline__ void grouped_mx_run(const GroupedArgs& a, const uint8
             m &= m - 1;
 #pragma unroll
             for (int u = 0; u < QG_MAX_T; ++u)
-                if (u == t) xv[i] = xall[u];
+                if (u == t) xv[i][0] = xall[u];
         }
     }
     mx_rows<FMT, NE, R, PRE>(W + (int64_t)e * a.expert_bytes, a.row_bytes, nsl, xv, row_begin, row_end,
@@ -2899,40 +2908,35 @@ ArgmaxFn half_argmax_for(int T, int depth) {
     }
 }
 
-template <int FMT>
-DmaFn mx_for(int T, int R) {
-    if (R == 2) {
-        switch (T) {
-        case 1: return qgemv_mx_kernel<FMT, 1, 2>;
-        case 2: return qgemv_mx_kernel<FMT, 2, 2>;
-        case 3: return qgemv_mx_kernel<FMT, 3, 2>;
-        default: return qgemv_mx_kernel<FMT, 4, 2>;
-        }
-    }
+template <int FMT, int R, int H>
+DmaFn mx_entry(int T) {
     switch (T) {
-    case 1: return qgemv_mx_kernel<FMT, 1, 1>;
-    case 2: return qgemv_mx_kernel<FMT, 2, 1>;
-    case 3: return qgemv_mx_kernel<FMT, 3, 1>;
-    default: return qgemv_mx_kernel<FMT, 4, 1>;
+    case 1: return qgemv_mx_kernel<FMT, 1, R, H>;
+    case 2: return qgemv_mx_kernel<FMT, 2, R, H>;
+    case 3: return qgemv_mx_kernel<FMT, 3, R, H>;
+    default: return qgemv_mx_kernel<FMT, 4, R, H>;
+    }
+}
+
+// R: 16-row groups per tile (1, 2); H: 256-wide halves per slice (1, 2; H = 2 with R = 1)
+template <int FMT>
+DmaFn mx_for(int T, int R, int H) {
+    return H == 2 ? mx_entry<FMT, 1, 2>(T) : R == 2 ? mx_entry<FMT, 2, 1>(T) : mx_entry<FMT, 1, 1>(T);
+}
+
+template <int FMT, int R, int H>
+ArgmaxFn mx_argmax_entry(int T) {
+    switch (T) {
+    case 1: return qgemv_mx_argmax_kernel<FMT, 1, R, H>;
+    case 2: return qgemv_mx_argmax_kernel<FMT, 2, R, H>;
+    case 3: return qgemv_mx_argmax_kernel<FMT, 3, R, H>;
+    default: return qgemv_mx_argmax_kernel<FMT, 4, R, H>;
     }
 }
 
 template <int FMT>
-ArgmaxFn mx_argmax_for(int T, int R) {
-    if (R == 2) {
-        switch (T) {
-        case 1: return qgemv_mx_argmax_kernel<FMT, 1, 2>;
-        case 2: return qgemv_mx_argmax_kernel<FMT, 2, 2>;
-        case 3: return qgemv_mx_argmax_kernel<FMT, 3, 2>;
-        default: return qgemv_mx_argmax_kernel<FMT, 4, 2>;
-        }
-    }
-    switch (T) {
-    case 1: return qgemv_mx_argmax_kernel<FMT, 1, 1>;
-    case 2: return qgemv_mx_argmax_kernel<FMT, 2, 1>;
-    case 3: return qgemv_mx_argmax_kernel<FMT, 3, 1>;
-    default: return qgemv_mx_argmax_kernel<FMT, 4, 1>;
-    }
+ArgmaxFn mx_argmax_for(int T, int R, int H) {
+    return H == 2 ? mx_argmax_entry<FMT, 1, 2>(T) : R == 2 ? mx_argmax_entry<FMT, 2, 1>(T) : mx_argmax_entry<FMT, 1, 1>(T);
 }
 
 template <int FMT>
@@ -2969,11 +2973,12 @@ int launch_mxp(int fmt, int T, const Tile& tile, const DenseArgs& a_in, void* st
 }
 
 int launch_mx(int fmt, int T, const Tile& tile, const DenseArgs& a, void* stream) {
-    const int nsl = (int)(a.cols / kHalfSlice);
-    if (a.cols % kHalfSlice || tile.waves_per_wg % nsl) return (int)hipErrorInvalidValue;
-    const int R = tile.depth == 2 ? 2 : 1;
-    const DmaFn fn = fmt == QG_FMT_Q8_0 ? mx_for<QG_FMT_Q8_0>(T, R) : fmt == QG_FMT_Q4_0 ? mx_for<QG_FMT_Q4_0>(T, R)
-                                                                                        : mx_for<QG_FMT_BF16>(T, R);
+    const int H = tile.kind == 11 ? 2 : 1;
+    const int nsl = (int)(a.cols / (kHalfSlice * H));
+    if (a.cols % (kHalfSlice * H) || tile.waves_per_wg % nsl) return (int)hipErrorInvalidValue;
+    const int R = tile.depth == 2 && H == 1 ? 2 : 1;
+    const DmaFn fn = fmt == QG_FMT_Q8_0 ? mx_for<QG_FMT_Q8_0>(T, R, H) : fmt == QG_FMT_Q4_0 ? mx_for<QG_FMT_Q4_0>(T, R, H)
+                                                                                           : mx_for<QG_FMT_BF16>(T, R, H);
     const int64_t nwg = (a.rows + tile.rows_per_wg - 1) / tile.rows_per_wg;
     hipLaunchKernelGGL(fn, dim3((unsigned)nwg), dim3(64 * tile.waves_per_wg), mx_lds_bytes(fmt, tile, T, nsl),
                        (hipStream_t)stream, a.W, a.x, a.y, a.rows, a.row_bytes, a.cols, nsl, a.rows_per_wg,
@@ -3060,12 +3065,14 @@ int launch_argmax(int fmt, int T, const Tile& tile, const DenseArgs& a_in, void*
         const int64_t tiles = (a.rows + 15) / 16;
         nwg = tiles < kPersistGrid ? tiles : kPersistGrid;
         lds = mxp_lds_bytes(fmt, tile, T);
-    } else if (tile.kind == 8 && a.cols % kHalfSlice == 0 && tile.waves_per_wg % (a.cols / kHalfSlice) == 0) {
-        a.nslices = a.cols / kHalfSlice;  // 256-wide slices
-        const int R = tile.depth == 2 ? 2 : 1;
-        fn = fmt == QG_FMT_Q8_0 ? mx_argmax_for<QG_FMT_Q8_0>(T, R)
-           : fmt == QG_FMT_Q4_0 ? mx_argmax_for<QG_FMT_Q4_0>(T, R)
-                                : mx_argmax_for<QG_FMT_BF16>(T, R);
+    } else if ((tile.kind == 8 || tile.kind == 11) && a.cols % (kHalfSlice * (tile.kind == 11 ? 2 : 1)) == 0 &&
+               tile.waves_per_wg % (a.cols / (kHalfSlice * (tile.kind == 11 ? 2 : 1))) == 0) {
+        const int H = tile.kind == 11 ? 2 : 1;
+        a.nslices = a.cols / (kHalfSlice * H);  // 256- or 512-wide slices
+        const int R = tile.depth == 2 && H == 1 ? 2 : 1;
+        fn = fmt == QG_FMT_Q8_0 ? mx_argmax_for<QG_FMT_Q8_0>(T, R, H)
+           : fmt == QG_FMT_Q4_0 ? mx_argmax_for<QG_FMT_Q4_0>(T, R, H)
+                                : mx_argmax_for<QG_FMT_BF16>(T, R, H);
         nwg = (a.rows + tile.rows_per_wg - 1) / tile.rows_per_wg;
         lds = mx_lds_bytes(fmt, tile, T, a.nslices);
     } else if (tile.kind == 7 && tile.rows_per_batch == 4 && a.cols % kHalfSlice == 0 &&

@@ -64,6 +64,8 @@
  *         product against an exact three-piece split of x; rb only sets which
  *         rw are valid, cols a multiple of 256, nw a multiple of cols/256; all
  *         three formats; x2: the same with 32-row tiles (the same bits);
+ *   X     x on 512-wide k slices (16 blocks a wave): cols a multiple of 512,
+ *         nw a multiple of cols/512; the arithmetic of P, so the same bits as P;
  *   m     as s, contracted on the matrix cores; Q8_0 with rb 8 only;
  *   p     m in persistent form: one workgroup per CU, nw = the k slices, rw =
  *         the chunk of rows whose partial sums are buffered;
@@ -251,7 +253,8 @@ int qg_unpack_q4_0(int64_t rows, int64_t cols, const void* in, uint16_t* d_bits,
  * with 16 lanes per row (any format; k_slice 256, lanes_per_row 16), 8: matrix
  * cores on 256-wide k slices fed by direct-to-LDS loads (any format; k_slice 256,
  * lanes_per_row 4: a row's 32-weight block is spread over 4 lanes), 9: kind 8 in
- * persistent form on 512-wide k slices (k_slice 512, lanes_per_row 4); mfma 1:
+ * persistent form on 512-wide k slices (k_slice 512, lanes_per_row 4), 11: kind 8
+ * on 512-wide k slices (k_slice 512, lanes_per_row 4); mfma 1:
  * matrix-core contraction of kind 1, 2: its persistent form). */
 int qg_query_tile(int fmt, int64_t rows, int64_t cols, int T, int out_tile[QG_TILE_FIELDS]);
 

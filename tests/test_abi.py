@@ -172,20 +172,23 @@ def test_tile_query_and_override(lib, monkeypatch):
     # or the same number of slice-looping waves
     def k_split(t, cols):
         nsl = -(-cols // t["k_slice"])
-        return (t["k_slice"], nsl if t["kind"] in (1, 7, 8, 9) else min(t["waves_per_wg"], nsl))
+        return (t["k_slice"], nsl if t["kind"] in (1, 7, 8, 9, 11) else min(t["waves_per_wg"], nsl))
     for fmt in ("q8_0", "q4_0", "bf16"):
         for rows, cols in ((10240, 2560), (2560, 6144), (248320, 5120), (8192, 2560), (7, 65536),
                            (151936, 3584), (65536, 5120)):
             tiles = [ops.query_tile(fmt, rows, cols, T) for T in (1, 2, 3, 4)]
             assert len({k_split(t, cols) for t in tiles}) == 1, (fmt, rows, cols, tiles)
             # the vector-ALU kinds share their arithmetic per k slice; the matrix-core kinds do not
-            arith = {(t["mfma"], t["kind"] if t["kind"] in (8, 9) else -1) for t in tiles}
+            arith = {(t["mfma"], t["kind"] if t["kind"] in (8, 9, 11) else -1) for t in tiles}
             assert len(arith) == 1, (fmt, rows, cols, tiles)
     # the LM head and other Q8_0 matrices past 512 MiB: the persistent matrix cores on 512-wide slices
     for rows, cols in ((248320, 5120), (151936, 3584)):
         t = ops.query_tile("q8_0", rows, cols, 4)
         assert (t["kind"], t["k_slice"], t["waves_per_wg"], t["lanes_per_row"]) == (9, 512, cols // 512, 4), t
     assert ops.query_tile("q8_0", 65536, 5120, 4)["kind"] != 9  # 357 MB: below the threshold
+    # more than twelve 256-wide slices: the matrix cores on 512-wide slices
+    t = ops.query_tile("q8_0", 2560, 6144, 1)
+    assert (t["kind"], t["k_slice"], t["waves_per_wg"], t["lanes_per_row"]) == (11, 512, 12, 4), t
     assert ops.query_tile("q4_0", 248320, 5120, 4)["kind"] != 9
     monkeypatch.setenv("QGEMV_TILE", "q8_0:2,5,8")
     t = ops.query_tile("q8_0", 10240, 2560, 4)
@@ -204,7 +207,7 @@ def test_tile_query_and_override(lib, monkeypatch):
     for bad in ("q8_0:3,5,8", "q8_0:2,13,8", "q8_0:2,5,6", "q9:2,5,8", "q8_0:2,5", "q8_0:16,5,32", "q8_0:8,5,32",
                 "q8_0:4,5,48,l5", "q8_0:4,5,48,l2", "q8_0:2,5,48,l4", "q8_0:4,10,48,l6", "q8_0:4,5,48,l", "q8_0:4,5,48,l6x",
                 "q8_0:4,10,48,P", "q8_0:4,5,40,P", "q8_0:4,5,1024,P",  # P: nw != slices, rw % 16, LDS
-                "q8_0:4,10,48,x3", "q8_0:4,10,48,x0x"):
+                "q8_0:4,10,48,x3", "q8_0:4,10,48,x0x", "q8_0:4,4,48,X", "q8_0:4,5,2048,X"):
         monkeypatch.setenv("QGEMV_TILE", bad)
         st, _ = _lib.qg_query_tile(0, 10240, 2560, 4)
         assert st == _lib.QG_EINVAL, bad
@@ -222,7 +225,8 @@ def test_header_names_every_tile_kind(lib, monkeypatch):
               "l": ("l2", 10240, 2560, "4,5,40"), "L": ("L2", 10240, 2560, "4,5,40"),
               "u": ("u2", 10240, 2560, "4,4,40"), "h": ("h2", 10240, 2560, "4,10,40"),
               "m": ("m", 10240, 2560, "8,5,32"), "p": ("p", 248320, 5120, "8,10,64"),
-              "x": ("x", 10240, 2560, "4,10,40"), "P": ("P", 10240, 2560, "4,5,48")}
+              "x": ("x", 10240, 2560, "4,10,40"), "P": ("P", 10240, 2560, "4,5,48"),
+              "X": ("X", 10240, 2560, "4,5,48")}
     accepted = set()
     for letter in "abcdefghijklmnopqrstuvwxyzABCDEFGHIJKLMNOPQRSTUVWXYZ":
         suffix, rows, cols, head = probes.get(letter, (letter, 10240, 2560, "4,10,40"))

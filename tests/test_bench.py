@@ -31,8 +31,9 @@ def test_kernel_names_follow_the_tile():
     assert bench.kernel_name(dict(base, kind=4, depth=3), 2) == "qgemv_units_kernel<0, 2, 3>"
     assert bench.kernel_name(dict(base, kind=0, depth=0, rows_per_wg=8), 1) == "qgemv_dense_kernel<0, 1, 4, true>"
     assert bench.kernel_name(dict(base, kind=7, waves_per_wg=10, depth=2), 4) == "qgemv_half_kernel<0, 4, 2>"
-    assert bench.kernel_name(dict(base, kind=8, waves_per_wg=10, depth=1), 3) == "qgemv_mx_kernel<0, 3, 1>"
-    assert bench.kernel_name(dict(base, kind=8, waves_per_wg=10, depth=2), 1) == "qgemv_mx_kernel<0, 1, 2>"
+    assert bench.kernel_name(dict(base, kind=8, waves_per_wg=10, depth=1), 3) == "qgemv_mx_kernel<0, 3, 1, 1>"
+    assert bench.kernel_name(dict(base, kind=8, waves_per_wg=10, depth=2), 1) == "qgemv_mx_kernel<0, 1, 2, 1>"
+    assert bench.kernel_name(dict(base, kind=11, waves_per_wg=12, depth=1), 2) == "qgemv_mx_kernel<0, 2, 1, 2>"
     assert bench.kernel_name(dict(base, kind=9, waves_per_wg=10, depth=1), 4) == "qgemv_mxp_kernel<0, 4>"
 
 

@@ -316,6 +316,25 @@ def test_mx_config_full(torch, orc, monkeypatch, name, rw, r):
     check_dense(torch, orc, c["fmt"], c["rows"], c["cols"], c["W"], c["x"], f"mx {name} rw={rw} r={r}")
 
 
+@pytest.mark.parametrize("name,rw", [("c2b_q8_0_2560x6144", 16), ("c2b_q8_0_2560x6144", 48),
+                                     ("c2a_q8_0_10240x2560", 48), ("c3_q4_0_8192x2560", 32),
+                                     ("c3_bf16_8192x2560", 16)])
+def test_mx512_config_full(torch, orc, monkeypatch, name, rw):
+    """Matrix cores on 512-wide slices (kind X) on the workloads: parity at every T,
+    a token's bits equal across T, and the persistent kind's bits (the same arithmetic)."""
+    c = I.dense_case(name)
+    fmt = NAMES[c["fmt"]]
+    nsl = c["cols"] // 512
+    monkeypatch.setenv("QGEMV_TILE", f"{fmt}:4,{nsl},{rw},X")
+    st, t = _lib.qg_query_tile(c["fmt"], c["rows"], c["cols"], 4)
+    assert st == 0 and t[6] == 11 and t[3] == 512, (st, t)
+    y = check_dense(torch, orc, c["fmt"], c["rows"], c["cols"], c["W"], c["x"], f"mx512 {name} rw={rw}")
+    monkeypatch.setenv("QGEMV_TILE", f"{fmt}:4,{nsl},32,P")
+    if _lib.qg_query_tile(c["fmt"], c["rows"], c["cols"], 4)[0] == 0:
+        yp = gpu_gemv(torch, c["fmt"], dev(torch, c["W"]), c["x"], c["rows"])
+        assert np.array_equal(yp, y), name
+
+
 def test_mx_row_tilings_keep_bits(torch, monkeypatch):
     """The same 256-wide k split at any rows per workgroup, row groups and tile
     height (16 or 32 rows): identical bits."""
@@ -335,8 +354,14 @@ def test_mx_tiny_ragged_and_row_groups(torch, orc, monkeypatch):
     for fmt in (Q8, Q4, BF):
         for rows in TINY_ROWS + (40, 100):
             for cols in (256, 512, 768, 1280, 2304, 3072):
-                for rw, rg, r in ((16, 1, 1), (40, 1, 1), (24, 2, 1), (48, 3, 1), (32, 1, 2), (40, 2, 2)):
-                    monkeypatch.setenv("QGEMV_TILE", mx_tile(cols, rw, rg, NAMES[fmt], r))
+                for rw, rg, r in ((16, 1, 1), (40, 1, 1), (24, 2, 1), (48, 3, 1), (32, 1, 2), (40, 2, 2),
+                                  (16, 1, "X"), (48, 2, "X")):
+                    if r == "X":
+                        if cols % 512:
+                            continue
+                        monkeypatch.setenv("QGEMV_TILE", f"{NAMES[fmt]}:4,{cols // 512 * rg},{rw},X")
+                    else:
+                        monkeypatch.setenv("QGEMV_TILE", mx_tile(cols, rw, rg, NAMES[fmt], r))
                     if _lib.qg_query_tile(fmt, rows, cols, 4)[0]:
                         continue  # more than twelve waves, or past the LDS
                     rng = np.random.default_rng(rows * 1000 + cols + rw + fmt)
@@ -594,11 +619,11 @@ def test_argmax_ties_negatives_and_kinds(torch, orc, monkeypatch):
         neg = -np.abs(x)  # a second activation pattern
         for kind_tile in (None, "q8_0:4,{nsl},40,l3", "q8_0:4,{nsl},48,L2", "q8_0:4,{nsl},16,s", "q8_0:2,{nsl},4,d",
                           "q8_0:8,{nsl},64,p", "q8_0:4,{nsl256},40,x", "q8_0:4,{nsl256},64,x2",
-                          "q8_0:4,{nsl256},24,h2", "q8_0:4,{nsl},32,P"):
+                          "q8_0:4,{nsl256},24,h2", "q8_0:4,{nsl},32,P", "q8_0:4,{nsl},48,X"):
             nsl, nsl256 = -(-cols // 512), cols // 256
             if "{nsl256}" in (kind_tile or "") and cols % 256:
                 continue  # 256-wide slices
-            if (kind_tile or "").endswith(",P") and cols % 512:
+            if (kind_tile or "").endswith((",P", ",X")) and cols % 512:
                 continue  # 512-wide slices
             if kind_tile:
                 kind_tile = kind_tile.format(nsl=nsl, nsl256=nsl256)
