@@ -106,11 +106,12 @@ const TuneEntry kTuned[] = {
     //   2560 x 2560 Q8_0: 4.5-4.9 / 4.7-5.0 / 4.9-5.1 / 5.1-5.3 against 4.6 / 5.3 /
     //     6.2 / 6.5 (direct at T <= 3, register-streamed at T = 4);
     //   8192 x 2560 Q4_0: 6.3 / 6.5 / 6.6 / 6.9 against 6.1 / 7.2 / 8.5 / 9.5;
-    //   8192 x 2560 BF16: 9.4 / 9.5 / 9.6 / 9.5 against 8.5 / 9.4 / 10.4 / 10.9.
+    //   8192 x 2560 BF16: 9.4 / 9.5 / 9.6 / 9.5 against 8.5 / 9.4 / 10.4 / 10.9 (on
+    //     512-wide slices, below, 0.3 µs less again).
     {QG_FMT_Q8_0, 10240, 2560, 0, "4,10,48,x"},
     {QG_FMT_Q8_0, 2560, 2560, 0, "4,10,16,x"},
     {QG_FMT_Q4_0, 8192, 2560, 0, "4,10,32,x"},
-    {QG_FMT_BF16, 8192, 2560, 0, "4,10,32,x"},
+    {QG_FMT_BF16, 8192, 2560, 0, "4,5,32,X"},  // 512-wide slices: 9.1 / 9.1 / 9.3 / 9.4 against 9.4 / 9.5 / 9.6 / 9.7
     // 2560 x 6144 Q8_0 (24 256-wide slices, more than twelve waves): the matrix cores
     // on 512-wide slices, 7.2 / 7.7 / 8.1 / 8.7 µs against 7.3 / 7.8 / 8.7 / 9.4 for the
     // register-streamed vector-ALU kernel
@@ -499,18 +500,48 @@ int run_rows(int fmt, int64_t rows, int64_t cols, int64_t n_sel, const int32_t* 
         return fail(QG_EUNSUPPORTED, "row subset addresses W with 32-bit offsets: %zu bytes is too many", wbytes);
     if (overlap(y, ybytes, W, wbytes) || overlap(y, ybytes, x, xbytes) || overlap(y, ybytes, ids, (size_t)n_sel * 4))
         return fail(QG_EINVAL, "y overlaps W, x or ids");
+    // the matrix cores on 256- or 512-wide slices, as the dense call's default kinds
+    // (a tile kind x or X pinned with QGEMV_TILE is taken; its rows per workgroup are
+    // ids per workgroup), else the vector-ALU LDS-DMA kernel on 512-wide slices
     Tile tile{};
     tile.lanes_per_row = kLanesPerRow;
     tile.k_slice = kSlice;
-    tile.kind = 2;
-    tile.depth = 2;
     tile.rows_per_batch = 4;
-    tile.waves_per_wg = (int)nsl;
-    int64_t rw = (n_sel / 256 + 7) / 8 * 8;
-    tile.rows_per_wg = (int)(rw < 16 ? 16 : rw > 128 ? 128 : rw);  // two ids per lane: at most 128
-    while (gather_lds_bytes(fmt, tile, T, (int)nsl) > kMaxLds && tile.rows_per_wg > 16) tile.rows_per_wg /= 2;
-    if (gather_lds_bytes(fmt, tile, T, (int)nsl) > kMaxLds)
-        return fail(QG_EUNSUPPORTED, "row subset: the LDS rings do not fit %lld slices of this format", (long long)nsl);
+    Tile pinned{};
+    std::string why;
+    const int ov = tile_override(fmt, &pinned, &why);
+    if (ov < 0) return fail(QG_EINVAL, "%s", why.c_str());
+    const int64_t nsl256 = cols / 256, nsl512 = cols / 512;
+    if (ov == 1 && (pinned.kind == 8 || pinned.kind == 11)) {
+        tile = pinned;
+        const int64_t n = tile.kind == 11 ? nsl512 : nsl256;
+        if (cols % (tile.kind == 11 ? 512 : 256) || n < 1 || tile.waves_per_wg % n || tile.depth != 1 ||
+            tile.rows_per_wg % 16 || tile.rows_per_wg > 128 || mx_lds_bytes(fmt, tile, T, (int)n) > kMaxLds)
+            return fail(QG_EINVAL, "row subset: pinned matrix-core tile needs 16-row tiles, at most 128 ids per "
+                                   "workgroup and waves a multiple of the slices");
+    } else if (ov != 1 && ((cols % 256 == 0 && nsl256 <= kMaxWaves) || (cols % 512 == 0 && nsl512 <= kMaxWaves))) {
+        const bool narrow = cols % 256 == 0 && nsl256 <= kMaxWaves;
+        tile.kind = narrow ? 8 : 11;
+        tile.depth = 1;
+        tile.waves_per_wg = (int)(narrow ? nsl256 : nsl512);
+        int64_t rw = (n_sel / 256 + 15) / 16 * 16;
+        tile.rows_per_wg = (int)(rw < 16 ? 16 : rw > 128 ? 128 : rw);
+        while (tile.rows_per_wg > 16 && mx_lds_bytes(fmt, tile, T, tile.waves_per_wg) > kMaxLds) tile.rows_per_wg -= 16;
+        if (mx_lds_bytes(fmt, tile, T, tile.waves_per_wg) > kMaxLds) tile.kind = 2;
+    } else {
+        tile.kind = 2;
+    }
+    if (tile.kind == 2) {
+        tile.k_slice = kSlice;
+        tile.depth = 2;
+        tile.rows_per_batch = 4;
+        tile.waves_per_wg = (int)nsl;
+        int64_t rw = (n_sel / 256 + 7) / 8 * 8;
+        tile.rows_per_wg = (int)(rw < 16 ? 16 : rw > 128 ? 128 : rw);  // two ids per lane: at most 128
+        while (gather_lds_bytes(fmt, tile, T, (int)nsl) > kMaxLds && tile.rows_per_wg > 16) tile.rows_per_wg /= 2;
+        if (gather_lds_bytes(fmt, tile, T, (int)nsl) > kMaxLds)
+            return fail(QG_EUNSUPPORTED, "row subset: the LDS rings do not fit %lld slices of this format", (long long)nsl);
+    }
     DenseArgs a;
     a.W = (const uint8_t*)W;
     a.x = x;

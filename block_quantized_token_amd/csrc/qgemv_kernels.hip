@@ -1730,12 +1730,17 @@ __device__ __forceinline__ void mx_load_x(const float* __restrict__ x, const int
             xv[t][h] = *reinterpret_cast<const float4*>(x + xoff[t] + k0 + kHalfSlice * h + 4 * (threadIdx.x & 63));
 }
 
-template <int FMT, int NT, int R, bool PRE = false, int H = 1, class Out>
+// GATHER: the rows are ids[row_begin .. row_end) of W's `wrows` rows (at most 128 a
+// workgroup, W under 2 GB): every wave holds the workgroup's ids in registers (id j
+// in lane j % 64 of register j / 64) and each load lane takes its row's id from the
+// lane that holds it; an id outside [0, wrows) loads nothing (the caller writes NaN).
+template <int FMT, int NT, int R, bool PRE = false, int H = 1, bool GATHER = false, class Out>
 __device__ __forceinline__ void mx_rows(const uint8_t* __restrict__ W, int64_t row_bytes, int nsl,
                                         const float4 (&xv)[NT][H], int64_t row_begin, int64_t row_end, int nw,
-                                        Out&& out) {
+                                        Out&& out, const int32_t* __restrict__ ids = nullptr, int64_t wrows = 0) {
     using M = MxShape<FMT, R, H>;
     constexpr int NB = 8 * H;  // blocks of a wave's slice
+    static_assert(!GATHER || (R == 1 && !PRE), "a gathered tile is 16 rows, issued here");
     constexpr int RT = M::kRows;
     constexpr int TP = pad_pow2(NT);
     constexpr int L = M::kLoads;
@@ -1757,10 +1762,41 @@ __device__ __forceinline__ void mx_rows(const uint8_t* __restrict__ W, int64_t r
     for (int k = 0; k < L; ++k) {
         const int j = 64 * k + lane;
         const int r = j / M::kChunks, c = j % M::kChunks;
-        off[k] = r < RT ? (int)(r * row_bytes) + s * M::kChunks * 16 + 16 * c : kNoLoad;
+        off[k] = r < RT ? (GATHER ? 0 : (int)(r * row_bytes)) + s * M::kChunks * 16 + 16 * c : kNoLoad;
     }
+    int my_id0 = -1, my_id1 = -1;
+    const __amdgpu_buffer_rsrc_t wr =
+        __builtin_amdgcn_make_buffer_rsrc((void*)W, (short)0, GATHER ? (int)(wrows * row_bytes) : 0, kBufferRsrcWord3);
+    if constexpr (GATHER) {
+        const int nsel = (int)(row_end - row_begin);
+        my_id0 = lane < nsel ? ids[row_begin + lane] : -1;
+        my_id1 = 64 + lane < nsel ? ids[row_begin + 64 + lane] : -1;
+    }
+    auto issue = [&](int t) __attribute__((always_inline)) {
+        if constexpr (GATHER) {
+            // every lane takes part in the exchanges (a lane outside a load's exec
+            // would hand its neighbours nothing), then the loads
+            int idk[L];
+#pragma unroll
+            for (int k = 0; k < L; ++k) {
+                const int src = t * 16 + (64 * k + lane) / M::kChunks;  // tiles 0..3 read ids 0..63
+                idk[k] = __shfl(t < 4 ? my_id0 : my_id1, src & 63, 64);
+            }
+#pragma unroll
+            for (int k = 0; k < L; ++k) {
+                if (k == L - 1 && M::kLastLanes < 64 && lane >= M::kLastLanes) break;
+                const int r = (64 * k + lane) / M::kChunks;
+                const int src = t * 16 + r;
+                const int id = idk[k];
+                const bool live = t < ntiles && r < 16 && src < (int)(row_end - row_begin) && id >= 0 && id < wrows;
+                load_lds16(wr, slot + 1024 * k, live ? (int)(id * row_bytes) + off[k] : kNoLoad);
+            }
+        } else {
+            mx_issue<FMT, R, H>(W, row_bytes, row_begin, row_end, ntiles, t, off, slot, lane);
+        }
+    };
     // the wave's first tile, unless PRE has it on its way already (x is older)
-    if constexpr (!PRE) mx_issue<FMT, R, H>(W, row_bytes, row_begin, row_end, ntiles, rg, off, slot, lane);
+    if constexpr (!PRE) issue(rg);
 
     // split, one token and 256-wide half at a time through the wave's region: piece
     // p of x[t][k] goes to the 16-byte fragment (block k / 32, group (k % 32) / 8,
@@ -1817,7 +1853,7 @@ __device__ __forceinline__ void mx_rows(const uint8_t* __restrict__ W, int64_t r
 #pragma unroll
             for (int b = 0; b < NB; ++b) raw[h][b] = mx_braw<FMT>(rowp + 16 * h * (M::kChunks * 16), b, g);
         wait_lgkmcnt0();  // the tile is in registers: the slot takes the next one
-        if (i + 1 < mine) mx_issue<FMT, R, H>(W, row_bytes, row_begin, row_end, ntiles, t + RG, off, slot, lane);
+        if (i + 1 < mine) issue(t + RG);
 #pragma unroll
         for (int h = 0; h < R; ++h) {
             F4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
@@ -2343,6 +2379,28 @@ __global__ void __launch_bounds__(64 * kMaxWaves) qgemv_gather_kernel(DenseArgs 
     float* __restrict__ y = a.y;
     gather_rows<FMT, T, 2>(a.W, a.rows, a.row_bytes, a.cols, a.nslices, ids, a.x, sel_begin, sel_end,
                            [=](int t, int64_t i, float v) { y[t * nsel + i] = v; });
+}
+
+// The row subset on the matrix cores: kind 8 (H = 1) or kind 11 (H = 2) over the ids
+// of the workgroup's range, so y[t][i] is the dense call's y[t][ids[i]] of that kind.
+template <int FMT, int T, int H>
+__global__ void __launch_bounds__(64 * kMaxWaves) qgemv_mx_gather_kernel(DenseArgs a, const int32_t* ids, int64_t nsel) {
+    const int64_t sel_begin = (int64_t)blockIdx.x * a.rows_per_wg;
+    const int64_t sel_end = sel_begin + a.rows_per_wg < nsel ? sel_begin + a.rows_per_wg : nsel;
+    int64_t xoff[T];
+#pragma unroll
+    for (int t = 0; t < T; ++t) xoff[t] = (int64_t)t * a.cols;
+    float4 xv[T][H];
+    mx_load_x<FMT, T, H>(a.x, xoff, a.nslices, xv);
+    float* __restrict__ y = a.y;
+    const int64_t rows = a.rows;
+    mx_rows<FMT, T, 1, false, H, true>(
+        a.W, a.row_bytes, a.nslices, xv, sel_begin, sel_end, (int)(blockDim.x >> 6),
+        [=](int t, int64_t i, float v) {
+            const int id = ids[i];
+            y[t * nsel + i] = id >= 0 && id < rows ? v : __builtin_nanf("");
+        },
+        ids, rows);
 }
 
 template <int T>
@@ -3122,9 +3180,42 @@ int launch_argmax(int fmt, int T, const Tile& tile, const DenseArgs& a_in, void*
     return (int)hipGetLastError();
 }
 
-int launch_gather(int fmt, int T, const Tile& tile, const DenseArgs& a, const int32_t* ids, int64_t nsel, void* stream) {
+int launch_gather(int fmt, int T, const Tile& tile, const DenseArgs& a_in, const int32_t* ids, int64_t nsel, void* stream) {
     using GatherFn = void (*)(DenseArgs, const int32_t*, int64_t);
     GatherFn fn = nullptr;
+    if (tile.kind == 8 || tile.kind == 11) {  // matrix cores on 256- or 512-wide slices
+        DenseArgs a = a_in;
+        const int H = tile.kind == 11 ? 2 : 1;
+        a.nslices = (int)(a.cols / (kHalfSlice * H));
+        if (a.cols % (kHalfSlice * H) || tile.waves_per_wg % a.nslices || tile.rows_per_wg > 128 ||
+            tile.rows_per_wg % 16)
+            return (int)hipErrorInvalidValue;
+        auto pick = [&](auto ftag) -> GatherFn {
+            constexpr int F = decltype(ftag)::value;
+            if (H == 2) {
+                switch (T) {
+                case 1: return qgemv_mx_gather_kernel<F, 1, 2>;
+                case 2: return qgemv_mx_gather_kernel<F, 2, 2>;
+                case 3: return qgemv_mx_gather_kernel<F, 3, 2>;
+                default: return qgemv_mx_gather_kernel<F, 4, 2>;
+                }
+            }
+            switch (T) {
+            case 1: return qgemv_mx_gather_kernel<F, 1, 1>;
+            case 2: return qgemv_mx_gather_kernel<F, 2, 1>;
+            case 3: return qgemv_mx_gather_kernel<F, 3, 1>;
+            default: return qgemv_mx_gather_kernel<F, 4, 1>;
+            }
+        };
+        fn = fmt == QG_FMT_Q8_0 ? pick(std::integral_constant<int, QG_FMT_Q8_0>{})
+           : fmt == QG_FMT_Q4_0 ? pick(std::integral_constant<int, QG_FMT_Q4_0>{})
+                                : pick(std::integral_constant<int, QG_FMT_BF16>{});
+        const int64_t nwg = (nsel + tile.rows_per_wg - 1) / tile.rows_per_wg;
+        hipLaunchKernelGGL(fn, dim3((unsigned)nwg), dim3(64 * tile.waves_per_wg), mx_lds_bytes(fmt, tile, T, a.nslices),
+                           (hipStream_t)stream, a, ids, nsel);
+        return (int)hipGetLastError();
+    }
+    const DenseArgs& a = a_in;
     auto pick = [&](auto ftag) -> GatherFn {
         constexpr int F = decltype(ftag)::value;
         switch (T) {

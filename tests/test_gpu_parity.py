@@ -5,6 +5,7 @@ Dyadic and identity inputs, whose exact result is representable, must match
 bit for bit; so must repeated calls, a token's outputs at different T, and the
 grouped kernel against the plain one.
 """
+import os
 import sys
 
 import numpy as np
@@ -642,20 +643,45 @@ def test_argmax_ties_negatives_and_kinds(torch, orc, monkeypatch):
 
 
 # ------------------------------------------------------------- row subset
-def rows_check(torch, orc, monkeypatch, fmt, rows, cols, W, x, ids, what):
-    """Row subset against the oracle on the selected rows and, bit for bit,
-    against the dense call's own output at those rows (a VALU LDS-DMA tile)."""
+def rows_tile(fmt, rows, cols, T):
+    """The dense tile with the row subset's default arithmetic: the matrix cores on
+    256-wide slices up to 12 of them, else on 512-wide slices up to 12, where the LDS
+    fits; else the vector-ALU kinds on 512-wide slices."""
+    for n, kind in ((cols // 256, "x"), (cols // 512, "X")):
+        width = 256 if kind == "x" else 512
+        if cols % width == 0 and 1 <= n <= 12:
+            spec = f"{NAMES[fmt]}:4,{n},16,{kind}"
+            os.environ["QGEMV_TILE"] = spec
+            ok = _lib.qg_query_tile(fmt, rows, cols, T)[0] == 0
+            del os.environ["QGEMV_TILE"]
+            if ok:
+                return spec
+            break
+    nsl = -(-cols // 512)
+    for spec in (f"{NAMES[fmt]}:4,{nsl},16,L2", f"{NAMES[fmt]}:4,{nsl},8,d"):
+        os.environ["QGEMV_TILE"] = spec
+        ok = _lib.qg_query_tile(fmt, rows, cols, T)[0] == 0
+        del os.environ["QGEMV_TILE"]
+        if ok:
+            return spec
+    raise AssertionError("no tile")
+
+
+def rows_check(torch, orc, monkeypatch, fmt, rows, cols, W, x, ids, what, pin=None):
+    """Row subset against the oracle on the selected rows and, bit for bit, against
+    the dense call's own output at those rows with the same arithmetic (the same
+    matrix-core kind, or a vector-ALU kind on 512-wide slices)."""
     Wd, xd = dev(torch, W), dev(torch, x)
+    if pin:
+        monkeypatch.setenv("QGEMV_TILE", pin)
     y = ops.gemv_rows(NAMES[fmt], Wd, xd, rows, dev(torch, ids.astype(np.int32))).cpu().numpy()
+    monkeypatch.delenv("QGEMV_TILE", raising=False)
     ok = (ids >= 0) & (ids < rows)
     assert np.isnan(y[:, ~ok]).all(), what
     if ok.any():
         ref, bound = orc.gemv(fmt, rows, cols, W, x, sel=ids[ok])
         assert_parity(y[:, ok], ref, bound, what)
-        nsl = -(-cols // 512)
-        monkeypatch.setenv("QGEMV_TILE", f"{NAMES[fmt]}:4,{nsl},16,L2")
-        if _lib.qg_query_tile(fmt, rows, cols, x.shape[0])[0] != 0:  # its LDS is too large: the direct kind
-            monkeypatch.setenv("QGEMV_TILE", f"{NAMES[fmt]}:4,{nsl},8,d")
+        monkeypatch.setenv("QGEMV_TILE", rows_tile(fmt, rows, cols, x.shape[0]))
         full = ops.gemv(NAMES[fmt], Wd, xd, rows).cpu().numpy()
         monkeypatch.delenv("QGEMV_TILE")
         assert np.array_equal(y[:, ok], full[:, ids[ok]]), what
@@ -672,6 +698,14 @@ def test_rows_subset_shapes(torch, orc, monkeypatch, fmt):
             for T in (1, 4):
                 say(f"[rows] fmt={NAMES[fmt]} {rows}x{cols} n_sel={n_sel} T={T}")
                 rows_check(torch, orc, monkeypatch, fmt, rows, cols, W, x[:T], ids, f"{rows}x{cols} n={n_sel} T={T}")
+                spec = rows_tile(fmt, rows, cols, T)
+                pin = spec.replace(",16,", ",32,")
+                monkeypatch.setenv("QGEMV_TILE", pin)
+                fits = _lib.qg_query_tile(fmt, rows, cols, T)[0] == 0
+                monkeypatch.delenv("QGEMV_TILE")
+                if spec.endswith(("x", "X")) and fits:  # the same kind pinned, 32 ids per workgroup
+                    rows_check(torch, orc, monkeypatch, fmt, rows, cols, W, x[:T], ids,
+                               f"{rows}x{cols} n={n_sel} T={T} pin={pin}", pin=pin)
 
 
 @pytest.mark.parametrize("fmt", [Q8, Q4, BF])
