@@ -537,17 +537,35 @@ def _kernel_short(name):
     return name.replace("void ", "").replace("qg::(anonymous namespace)::", "").split("(")[0]
 
 
-def summarize_trace(trace_dir):
-    """Per-kernel call count and duration from a rocprofv3 --kernel-trace --stats run."""
+def summarize_trace(trace_dir, skip_first=0):
+    """Per-kernel call count and duration from a rocprofv3 --kernel-trace --stats run;
+    with ``skip_first`` the run's first that many dispatches of this library's kernels
+    (by start time) are left out, so a pass that only brings the clocks up is not counted."""
     import csv
     import glob
+    print(f"kernel_source_sha256: {source_digest()}")
+    print()
+    share = "share of this library's kernel time" if skip_first else "share of kernel time"
+    print(f"| kernel | calls | average us | min us | max us | {share} |")
+    print("|---|---|---|---|---|---|")
+    if skip_first:
+        files = glob.glob(os.path.join(trace_dir, "**", "*kernel_trace.csv"), recursive=True)
+        if not files:
+            sys.exit(f"no kernel_trace.csv under {trace_dir}")
+        recs = sorted(csv.DictReader(open(files[0])), key=lambda r: int(r["Start_Timestamp"]))
+        recs = [r for r in recs if _kernel_short(r["Kernel_Name"]).startswith(("qgemv", "quantize"))][skip_first:]
+        acc = {}
+        for r in recs:
+            acc.setdefault(_kernel_short(r["Kernel_Name"]), []).append(
+                (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+        total = sum(sum(v) for v in acc.values())
+        for name, v in sorted(acc.items(), key=lambda kv: -sum(kv[1])):
+            print(f"| {name} | {len(v)} | {sum(v) / len(v):.3f} | {min(v):.3f} | {max(v):.3f} | "
+                  f"{100 * sum(v) / total:.2f}% |")
+        return
     files = glob.glob(os.path.join(trace_dir, "**", "*kernel_stats.csv"), recursive=True)
     if not files:
         sys.exit(f"no kernel_stats.csv under {trace_dir}")
-    print(f"kernel_source_sha256: {source_digest()}")
-    print()
-    print("| kernel | calls | average us | min us | max us | share of kernel time |")
-    print("|---|---|---|---|---|---|")
     for r in csv.DictReader(open(files[0])):
         name = _kernel_short(r["Name"])
         if not name.startswith(("qgemv", "quantize")):
@@ -625,6 +643,9 @@ def profile_workload(torch, stream, name, calls, tiles, Ts=(1, 2, 3, 4)):
                 return _lib.qgemv_argmax(fmt, rows, cols, T, W, x.data_ptr(), work.data_ptr(), idx.data_ptr(),
                                          val.data_ptr(), sp)
             return entry(rows, cols, T, W, x.data_ptr(), y.data_ptr(), sp)
+    for w in ring:  # first touch of fresh memory outside the traced calls
+        torch.count_nonzero(w)
+    torch.cuda.synchronize()
     saved = _os.environ.get("QGEMV_TILE")
     try:
         for spec in tiles:
@@ -667,12 +688,14 @@ def main():
                     help="print the HBM traffic table from two rocprofv3 --pmc runs of this script and exit")
     ap.add_argument("--summarize-trace", metavar="TRACE_DIR",
                     help="print the per-kernel table of a rocprofv3 --kernel-trace --stats run and exit")
+    ap.add_argument("--skip-first", type=int, default=0,
+                    help="with --summarize-trace: leave out the run's first N dispatches of this library")
     ap.add_argument("--summarize-counters", metavar="PMC_DIR",
                     help="print per-kernel medians of every counter of a rocprofv3 --pmc run and exit")
     args = ap.parse_args()
 
     if args.summarize_trace:
-        summarize_trace(args.summarize_trace)
+        summarize_trace(args.summarize_trace, args.skip_first)
         return
     if args.summarize_counters:
         summarize_counters(args.summarize_counters)
