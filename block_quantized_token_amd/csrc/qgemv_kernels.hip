@@ -1377,6 +1377,9 @@ __device__ __forceinline__ void mfma_tile_q8(const uint8_t* __restrict__ W, int 
     // products and scalings overlap; combined in a fixed order at the end.
     // Blocks past a short last slice read stale (finite) codes against zero A
     // fragments; their scale is forced to 0 so a stale Inf/NaN cannot leak in.
+    // Only the first NJ of a lane's four rows of D carry tokens (A's rows of tokens
+    // >= NT are zero): the scalings and the piece sums skip the rest.
+    constexpr int NJ = NT < 4 ? NT : 4;
     F4 acc4[4];
 #pragma unroll
     for (int a = 0; a < 4; ++a) acc4[a] = F4{0.0f, 0.0f, 0.0f, 0.0f};
@@ -1391,16 +1394,16 @@ __device__ __forceinline__ void mfma_tile_q8(const uint8_t* __restrict__ W, int 
         const F4 dd = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(BF8, afrag[b]),
                                                                __builtin_bit_cast(BF8, bq), z, 0, 0, 0);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc4[b & 3][j] = __builtin_fmaf(d, dd[j], acc4[b & 3][j]);
+        for (int j = 0; j < NJ; ++j) acc4[b & 3][j] = __builtin_fmaf(d, dd[j], acc4[b & 3][j]);
     }
     F4 acc;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[j] = (acc4[0][j] + acc4[1][j]) + (acc4[2][j] + acc4[3][j]);
+    for (int j = 0; j < NJ; ++j) acc[j] = (acc4[0][j] + acc4[1][j]) + (acc4[2][j] + acc4[3][j]);
     // pieces of token j sit in lanes n (hi), n + 16 (mid), n + 32 (lo): added in
     // that order.  permlane16_swap brings lane n + 16's value to lane n (rows 0/1
     // of the wave trade places), permlane32_swap lane n + 32's (halves trade).
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int j = 0; j < NJ; ++j) {
         float mid = acc[j], lo = acc[j], junk16 = acc[j], junk32 = acc[j];
         permlane16_swap(junk16, mid);
         permlane32_swap(junk32, lo);
@@ -1745,6 +1748,9 @@ __device__ __forceinline__ void mx_rows(const uint8_t* __restrict__ W, int64_t r
     constexpr int TP = pad_pow2(NT);
     constexpr int L = M::kLoads;
     constexpr int REG = 1536;  // per wave: one token's bf16 pieces [8 blocks][4 groups][3 pieces] x 16 B
+    // a lane's rows of D past the first NJ belong to no token (A's rows of tokens >=
+    // NT are zero): their scalings and piece sums are skipped and they stay 0
+    constexpr int NJ = NT < 4 ? NT : 4;
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
 
     const int tid = threadIdx.x;
@@ -1869,12 +1875,12 @@ __device__ __forceinline__ void mx_rows(const uint8_t* __restrict__ W, int64_t r
                     const F4 dd = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(BF8, afrag[b]),
                                                                           __builtin_bit_cast(BF8, bq), z, 0, 0, 0);
 #pragma unroll
-                    for (int j = 0; j < 4; ++j) acc[j] = __builtin_fmaf(dq, dd[j], acc[j]);
+                    for (int j = 0; j < NJ; ++j) acc[j] = __builtin_fmaf(dq, dd[j], acc[j]);
                 }
             }
             // token j's pieces sit in lanes n (hi), n + 16 (mid), n + 32 (lo): (hi + mid) + lo
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
+            for (int j = 0; j < NJ; ++j) {
                 float mid = acc[j], lo = acc[j], junk16 = acc[j], junk32 = acc[j];
                 permlane16_swap(junk16, mid);
                 permlane32_swap(junk32, lo);
@@ -1942,8 +1948,9 @@ __device__ __forceinline__ void mxp_issue(const uint8_t* __restrict__ W, int64_t
 
 // The MFMAs of the 16 blocks of one tile, from their bytes: acc += scale *
 // (pieces x codes) per block, in block order.
-template <int FMT>
+template <int FMT, int NT>
 __device__ __forceinline__ void mxp_math(const V4 (&afrag)[16], const MxRaw (&raw)[16], int g, F4& acc) {
+    constexpr int NJ = NT < 4 ? NT : 4;  // rows of D that carry a token (the rest stay 0)
 #pragma unroll
     for (int b = 0; b < 16; ++b) {
         float dq;
@@ -1956,7 +1963,7 @@ __device__ __forceinline__ void mxp_math(const V4 (&afrag)[16], const MxRaw (&ra
             const F4 dd = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(BF8, afrag[b]),
                                                                   __builtin_bit_cast(BF8, bq), z, 0, 0, 0);
 #pragma unroll
-            for (int j = 0; j < 4; ++j) acc[j] = __builtin_fmaf(dq, dd[j], acc[j]);
+            for (int j = 0; j < NJ; ++j) acc[j] = __builtin_fmaf(dq, dd[j], acc[j]);
         }
     }
 }
@@ -2073,9 +2080,9 @@ __device__ __forceinline__ void mxp_rows(const uint8_t* __restrict__ W, int64_t 
             wait_lgkmcnt0();  // the tile is in registers: the slot takes the next one
             if (t + 1 < ntiles) mxp_issue<FMT>(W, row_bytes, row_begin, row_end, t + 1, off, slot, lane);
             F4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
-            mxp_math<FMT>(afrag, raw, g, acc);
+            mxp_math<FMT, NT>(afrag, raw, g, acc);
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
+            for (int j = 0; j < (NT < 4 ? NT : 4); ++j) {
                 float mid = acc[j], lo = acc[j], junk16 = acc[j], junk32 = acc[j];
                 permlane16_swap(junk16, mid);
                 permlane32_swap(junk32, lo);
