@@ -114,3 +114,24 @@ def test_no_clock_sampling_under_the_profiler(monkeypatch):
     monkeypatch.setenv("LD_PRELOAD", "/opt/rocm/lib/rocprofiler-sdk/librocprofiler-sdk-tool.so")
     assert bench.gpu_clocks() == {"skipped": "under rocprofv3"}
     assert bench.clocks_under_load(None, lambda: None, 0.0) == {"skipped": "under rocprofv3"}
+
+
+def test_trace_summary_leaves_out_the_first_dispatches(tmp_path, capsys):
+    # dispatches listed out of order: the summary sorts them by start time, drops the
+    # first N of this library's kernels (other kernels neither count nor show) and
+    # aggregates the rest per kernel
+    d = tmp_path / "t"
+    d.mkdir()
+    name_a = '"void qg::(anonymous namespace)::qgemv_mxp_kernel<0, 1>(qg::DenseArgs)"'
+    name_b = '"void qg::(anonymous namespace)::qgemv_mxp_kernel<0, 2>(qg::DenseArgs)"'
+    rows = [(name_a, 3000, 3004), (name_a, 1000, 1009), ('"at::native::copy_kernel"', 500, 900),
+            (name_a, 2000, 2005), (name_b, 4000, 4006), (name_b, 5000, 5008)]
+    (d / "run_kernel_trace.csv").write_text(
+        "Kernel_Name,Start_Timestamp,End_Timestamp\n" + "".join(f"{n},{s},{e}\n" for n, s, e in rows))
+    bench.summarize_trace(str(d), skip_first=1)
+    out = capsys.readouterr().out
+    # qgemv_mxp_kernel<0, 1> keeps the dispatches at 2000 (5 ns) and 3000 (4 ns)
+    assert "| qgemv_mxp_kernel<0, 1> | 2 | 0.005 | 0.004 | 0.005 | 39.13% |" in out
+    assert "| qgemv_mxp_kernel<0, 2> | 2 | 0.007 | 0.006 | 0.008 | 60.87% |" in out
+    assert "copy_kernel" not in out
+    assert "share of this library's kernel time" in out
