@@ -137,12 +137,12 @@ Tile default_tile(int fmt, int64_t rows, int64_t cols, int T) {
         if (e.fmt == fmt && e.rows == rows && e.cols == cols && (e.T == 0 || e.T == T) && parse_tile_spec(e.tile, &t, &why))
             return t;
     }
-    // Q8_0 matrices far beyond the 256 MB last-level cache, up to 12 512-wide
-    // slices: the persistent matrix cores on the LDS-DMA ring, chunks of 3 tiles
+    // Q8_0 matrices far beyond the 256 MB last-level cache, up to 11 512-wide
+    // slices (and a wave that sums): the persistent matrix cores on the LDS-DMA ring, chunks of 3 tiles
     // (151,936 x 3,584: 105 / 108 / 110 / 112 µs at T = 1..4 against 116 / 126 /
     // 144 / 162; at 65,536 x 5,120, 357 MB, it still loses at T <= 2)
     if (fmt == QG_FMT_Q8_0 && rows * row_bytes(fmt, cols) >= (int64_t)512 << 20 && cols % kSlice == 0 &&
-        nslices <= kMaxWaves) {
+        nslices + 1 <= kMaxWaves) {
         t.kind = 9;
         t.depth = 1;
         t.rows_per_batch = 4;
@@ -288,6 +288,9 @@ int pick_tile(int fmt, int64_t rows, int64_t cols, int T, Tile* t) {
         if (cols % kSlice || t->waves_per_wg != nslices)
             return fail(QG_EINVAL, "persistent matrix-core ring tile needs cols a multiple of 512 and waves_per_wg == "
                                    "the %lld 512-wide slices", (long long)nslices);
+        if (t->waves_per_wg + 1 > kMaxWaves)  // one more wave sums the chunks
+            return fail(QG_EINVAL, "persistent matrix-core ring tile runs at most %d 512-wide slices (cols <= %d)",
+                        kMaxWaves - 1, (kMaxWaves - 1) * (int)kSlice);
         if (t->rows_per_wg % 16)
             return fail(QG_EINVAL, "persistent matrix-core ring tile needs rows_per_wg (the chunk) a multiple of 16");
         if (row_bytes(fmt, cols) * 16 > 0x7FFFFFFF)

@@ -326,6 +326,19 @@ __device__ __forceinline__ void load_x(const float* __restrict__ x, const int64_
     }
 }
 
+
+// Ordering for the arrival protocols, whose partial sums and counters live in LDS
+// and move only through ds_ instructions.  A wave's LDS operations execute in order
+// and the LDS atomics are serialized, so a release needs this wave's LDS accesses
+// complete (lgkmcnt 0) and an acquire needs none; the asm barriers keep the
+// compiler from moving LDS accesses across.  Unlike a fence, neither waits for the
+// wave's loads into LDS in flight (the next tile), which the protocols never read.
+__device__ __forceinline__ void lds_release() {
+    __builtin_amdgcn_s_waitcnt((15) | (7 << 4) | (0 << 8) | (3 << 14));  // lgkmcnt(0)
+    asm volatile("" ::: "memory");
+}
+__device__ __forceinline__ void lds_acquire() { asm volatile("" ::: "memory"); }
+
 template <int FMT, int NT, int RB, class Out>
 __device__ __forceinline__ void reduce_batch(float (&acc)[RB][pad_pow2(NT)], int b, int64_t rb0, float* part,
                                              int* arrivals, int nw, int wave, int lane, int li, int g, int my_idx,
@@ -340,13 +353,15 @@ __device__ __forceinline__ void reduce_batch(float (&acc)[RB][pad_pow2(NT)], int
     butterfly32<N>(v, li);
     float* mine = part + (((size_t)b * nw + wave) * 2 + g) * N;
     if (writer) mine[my_idx] = v[0];
-    // publish this wave's slots, then count the arrival (one atomic per wave)
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+    // publish this wave's slots, then count the arrival (one atomic per wave); the
+    // slots and the counter are in LDS: the wave does not wait here for its loads in
+    // flight
+    lds_release();
     int prev = 0;
-    if (lane == 0) prev = __hip_atomic_fetch_add(&arrivals[b], 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_WORKGROUP);
+    if (lane == 0) prev = __hip_atomic_fetch_add(&arrivals[b], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
     prev = __shfl(prev, 0, 64);
     if (prev == nw - 1) {  // last arrival: all nw partial sets of batch b are in LDS
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+        lds_acquire();
         if (lane < 2 * N) {
             const int gg = lane / N, idx = lane % N;
             const int t = idx % TP, r = idx / TP;
@@ -719,6 +734,7 @@ __device__ __forceinline__ void wait_vmcnt() {
     __builtin_amdgcn_s_waitcnt((V & 15) | (7 << 4) | (15 << 8) | ((V >> 4) << 14));
 }
 __device__ __forceinline__ void wait_lgkmcnt0() { __builtin_amdgcn_s_waitcnt((15) | (7 << 4) | (0 << 8) | (3 << 14)); }
+
 
 template <int FMT, int ST>
 __device__ __forceinline__ void dma_issue(const uint8_t* __restrict__ W, int64_t row_bytes, int64_t row_begin,
@@ -1546,16 +1562,19 @@ __device__ __forceinline__ void mfma_persist_q8(const uint8_t* __restrict__ W, i
     for (int c = 0; c * C < ntiles; ++c) {
         const int pb = c & 1;
         if (c >= 2) {  // chunk c - 2 (same buffer) must have been summed
-            while (__atomic_load_n(&ctl[2 + pb], __ATOMIC_ACQUIRE) < (c >> 1)) __builtin_amdgcn_s_sleep(1);
+            while (__atomic_load_n(&ctl[2 + pb], __ATOMIC_RELAXED) < (c >> 1)) __builtin_amdgcn_s_sleep(1);
+            lds_acquire();
         }
         const int tend = (c + 1) * C < ntiles ? (c + 1) * C : ntiles;
         for (int t = c * C; t < tend; ++t)
             mfma_tile_q8<NT>(W, rbytes, row_begin, row_end, ntiles, t, 1, cs, sbase, ra, buf, part, afrag, lane, n, g,
                              s, nsl, nblk, pb * C + (t - c * C));
+        lds_release();  // the partials, then the arrival
         int last = 0;
-        if (lane == 0) last = __atomic_fetch_add(&ctl[pb], 1, __ATOMIC_ACQ_REL) == nw - 1;
+        if (lane == 0) last = __atomic_fetch_add(&ctl[pb], 1, __ATOMIC_RELAXED) == nw - 1;
         last = __shfl(last, 0, 64);
         if (last) {  // every wave's partials of chunk c are in: sum the slices in order
+            lds_acquire();
             const int64_t r0 = row_begin + (int64_t)c * C * ST;
             const int nr = (int)((row_end - r0) < (int64_t)C * ST ? (row_end - r0) : (int64_t)C * ST);
             for (int o = lane; o < nr * NT; o += 64) {
@@ -1565,9 +1584,10 @@ __device__ __forceinline__ void mfma_persist_q8(const uint8_t* __restrict__ W, i
                 for (int w = 1; w < nsl; ++w) sum = sum + base[(size_t)w * 16 * TP];
                 out(t, r0 + rr, sum);
             }
+            lds_release();  // the partials are read
             if (lane == 0) {
                 __atomic_store_n(&ctl[pb], 0, __ATOMIC_RELAXED);
-                __atomic_fetch_add(&ctl[2 + pb], 1, __ATOMIC_RELEASE);
+                __atomic_fetch_add(&ctl[2 + pb], 1, __ATOMIC_RELAXED);
             }
         }
     }
@@ -1915,10 +1935,13 @@ __device__ __forceinline__ void mx_rows(const uint8_t* __restrict__ W, int64_t r
 // slot is refilled at once.  Before the first tile the slot stages x and its
 // bf16 pieces (two rounds of eight blocks), so the A fragments cost one pass
 // per wave and no LDS of their own.  Partial sums go to two chunk buffers of C
-// tiles; the wave that completes a chunk (an LDS arrival counter) adds its
-// slices in slice order and stores the outputs; a wave reuses a chunk buffer
-// only once its previous chunk has been summed (a generation count), and the
-// wave that sums never waits, so every wait ends.
+// tiles; one more wave, which streams nothing, waits for each chunk's arrivals
+// (an LDS counter), adds the slices in slice order and stores the outputs, so no
+// streaming wave ever stops its stream to sum (a summing wave that also streams
+// cannot overlap the sums with its tile in flight: the compiler waits for the
+// load into LDS before the protocol's LDS reads).  A wave reuses a chunk buffer
+// only once its previous chunk has been summed (a generation count); the summing
+// wave waits only for arrivals that every streaming wave makes, so every wait ends.
 template <int FMT>
 struct MxpShape {
     static constexpr int kChunks = StreamFmt<FMT>::kChunks;              // 16-byte chunks of a row slice: 34, 18, 64
@@ -1986,7 +2009,8 @@ __device__ __forceinline__ void mxp_rows(const uint8_t* __restrict__ W, int64_t 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int nw = blockDim.x >> 6;  // == nsl: one wave per k slice
+    const int nw = nsl;                // streaming waves: one per k slice
+    const bool summer = wave == nsl;   // the workgroup's last wave sums the chunks
     const int n = lane & 15, g = lane >> 4;
     const int s = wave;
     const int k0 = s * kSlice;
@@ -1995,9 +2019,11 @@ __device__ __forceinline__ void mxp_rows(const uint8_t* __restrict__ W, int64_t 
     const int64_t row_begin = t0 * 16;
     const int64_t row_end = t1 * 16 < rows ? t1 * 16 : rows;
     const int ntiles = (int)(t1 - t0);
-    uint8_t* slot = smem + wave * M::kSlot;
+    uint8_t* slot = smem + (summer ? 0 : wave) * M::kSlot;
     float* part = reinterpret_cast<float*>(smem + nw * M::kSlot);              // [2][C][nsl][16][TP]
-    int* ctl = reinterpret_cast<int*>(part + (size_t)2 * C * nsl * 16 * TP);   // arrivals[2], generation[2]
+    // arrivals[2], generation[2]: an LDS object of their own, so the compiler can see that
+    // reading them never depends on the tile loads into the dynamic LDS in flight
+    __shared__ int ctl[4];
     if (tid < 4) ctl[tid] = 0;
 
     int off[L];
@@ -2008,68 +2034,100 @@ __device__ __forceinline__ void mxp_rows(const uint8_t* __restrict__ W, int64_t 
         off[k] = r < 16 ? (int)(r * row_bytes) + s * M::kRow + 16 * c : kNoLoad;
     }
     // x of the slice into the slot (token t at 2048 t), then into registers: lane
-    // l takes k = 4 l .. 4 l + 3 of each 256-wide half
-#pragma unroll
-    for (int t = 0; t < NT; ++t) {
-        const __amdgpu_buffer_rsrc_t xr =
-            __builtin_amdgcn_make_buffer_rsrc((void*)(x + (int64_t)t * cols + k0), (short)0, 2048, kBufferRsrcWord3);
-        load_lds16(xr, slot + 2048 * t, 16 * lane);
-        load_lds16(xr, slot + 2048 * t + 1024, 16 * lane + 1024);
-    }
-    wait_vmcnt<0>();
-    float4 xv[2][NT];
-#pragma unroll
-    for (int h = 0; h < 2; ++h)
-#pragma unroll
-        for (int t = 0; t < NT; ++t) xv[h][t] = *reinterpret_cast<const float4*>(slot + 2048 * t + 1024 * h + 16 * lane);
+    // l takes k = 4 l .. 4 l + 3 of each 256-wide half (the summing wave has no
+    // slice: it skips the staging and keeps zero fragments)
     V4 afrag[16];
-    {
-        const int b = lane >> 3, gg = (lane & 7) >> 1, half = (lane & 1) * 8;
-        const int am = lane & 15, ap = am >> 2, at = am & 3;
-        const bool arow = ap < 3 && at < NT;
-        const int idx = arow ? (g * 3 * NT + ap * NT + at) * 16 : 0;
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            wait_lgkmcnt0();  // the slot's previous contents are read by every lane
+    for (int b = 0; b < 16; ++b) afrag[b] = V4{0u, 0u, 0u, 0u};
+    if (!summer) {
 #pragma unroll
-            for (int t = 0; t < NT; ++t) {
-                const float vv[4] = {xv[h][t].x, xv[h][t].y, xv[h][t].z, xv[h][t].w};
-                uint32_t pc[3][4];
+        for (int t = 0; t < NT; ++t) {
+            const __amdgpu_buffer_rsrc_t xr =
+                __builtin_amdgcn_make_buffer_rsrc((void*)(x + (int64_t)t * cols + k0), (short)0, 2048, kBufferRsrcWord3);
+            load_lds16(xr, slot + 2048 * t, 16 * lane);
+            load_lds16(xr, slot + 2048 * t + 1024, 16 * lane + 1024);
+        }
+        wait_vmcnt<0>();
+        float4 xv[2][NT];
 #pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const uint32_t v = __builtin_bit_cast(uint32_t, vv[q]);
-                    const float r1 = vv[q] - __builtin_bit_cast(float, v & 0xFFFF0000u);
-                    const uint32_t u1 = __builtin_bit_cast(uint32_t, r1);
-                    const float r2 = r1 - __builtin_bit_cast(float, u1 & 0xFFFF0000u);
-                    pc[0][q] = v;
-                    pc[1][q] = u1;
-                    pc[2][q] = __builtin_bit_cast(uint32_t, r2);
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+            for (int t = 0; t < NT; ++t) xv[h][t] = *reinterpret_cast<const float4*>(slot + 2048 * t + 1024 * h + 16 * lane);
+        {
+            const int b = lane >> 3, gg = (lane & 7) >> 1, half = (lane & 1) * 8;
+            const int am = lane & 15, ap = am >> 2, at = am & 3;
+            const bool arow = ap < 3 && at < NT;
+            const int idx = arow ? (g * 3 * NT + ap * NT + at) * 16 : 0;
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                wait_lgkmcnt0();  // the slot's previous contents are read by every lane
+#pragma unroll
+                for (int t = 0; t < NT; ++t) {
+                    const float vv[4] = {xv[h][t].x, xv[h][t].y, xv[h][t].z, xv[h][t].w};
+                    uint32_t pc[3][4];
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        const uint32_t v = __builtin_bit_cast(uint32_t, vv[q]);
+                        const float r1 = vv[q] - __builtin_bit_cast(float, v & 0xFFFF0000u);
+                        const uint32_t u1 = __builtin_bit_cast(uint32_t, r1);
+                        const float r2 = r1 - __builtin_bit_cast(float, u1 & 0xFFFF0000u);
+                        pc[0][q] = v;
+                        pc[1][q] = u1;
+                        pc[2][q] = __builtin_bit_cast(uint32_t, r2);
+                    }
+#pragma unroll
+                    for (int p = 0; p < 3; ++p) {
+                        uint2 w2;
+                        w2.x = __builtin_amdgcn_perm(pc[p][1], pc[p][0], 0x07060302u);
+                        w2.y = __builtin_amdgcn_perm(pc[p][3], pc[p][2], 0x07060302u);
+                        *reinterpret_cast<uint2*>(slot + b * (192 * NT) + (gg * 3 * NT + p * NT + t) * 16 + half) = w2;
+                    }
                 }
+                wait_lgkmcnt0();
 #pragma unroll
-                for (int p = 0; p < 3; ++p) {
-                    uint2 w2;
-                    w2.x = __builtin_amdgcn_perm(pc[p][1], pc[p][0], 0x07060302u);
-                    w2.y = __builtin_amdgcn_perm(pc[p][3], pc[p][2], 0x07060302u);
-                    *reinterpret_cast<uint2*>(slot + b * (192 * NT) + (gg * 3 * NT + p * NT + t) * 16 + half) = w2;
+                for (int bb = 0; bb < 8; ++bb) {
+                    const V4 v = *reinterpret_cast<const V4*>(slot + bb * (192 * NT) + idx);
+                    afrag[8 * h + bb] = arow ? v : V4{0u, 0u, 0u, 0u};
                 }
-            }
-            wait_lgkmcnt0();
-#pragma unroll
-            for (int bb = 0; bb < 8; ++bb) {
-                const V4 v = *reinterpret_cast<const V4*>(slot + bb * (192 * NT) + idx);
-                afrag[8 * h + bb] = arow ? v : V4{0u, 0u, 0u, 0u};
             }
         }
     }
     wait_lgkmcnt0();  // the pieces are in registers: the slot takes the first tile
     __syncthreads();  // (also publishes the cleared control words)
+    if (summer) {  // every chunk: wait for all slices' partials, sum them in slice order, store
+        for (int c = 0; c * C < ntiles; ++c) {
+            const int pb = c & 1;
+            while (__atomic_load_n(&ctl[pb], __ATOMIC_RELAXED) < nw) __builtin_amdgcn_s_sleep(1);
+            lds_acquire();
+            const int64_t r0 = row_begin + (int64_t)c * C * 16;
+            const int nr = (int)((row_end - r0) < (int64_t)C * 16 ? (row_end - r0) : (int64_t)C * 16);
+            for (int rr = lane; rr < nr; rr += 64) {  // a lane per row, all tokens at once
+                const float* base = part + (((size_t)(pb * C + rr / 16) * nsl) * 16 + rr % 16) * TP;
+                Vec<TP> sum = *reinterpret_cast<const Vec<TP>*>(base);
+                for (int w = 1; w < nsl; ++w) {
+                    const Vec<TP> v = *reinterpret_cast<const Vec<TP>*>(base + (size_t)w * 16 * TP);
+#pragma unroll
+                    for (int tk = 0; tk < NT; ++tk) sum.v[tk] = sum.v[tk] + v.v[tk];
+                }
+#pragma unroll
+                for (int tk = 0; tk < NT; ++tk) out(tk, r0 + rr, sum.v[tk]);
+            }
+            lds_release();  // the partials are read
+            if (lane == 0) {
+                __atomic_store_n(&ctl[pb], 0, __ATOMIC_RELAXED);
+                __atomic_fetch_add(&ctl[2 + pb], 1, __ATOMIC_RELAXED);
+            }
+        }
+        return;
+    }
     if (ntiles > 0) mxp_issue<FMT>(W, row_bytes, row_begin, row_end, 0, off, slot, lane);
 
     const uint8_t* rowp = slot + n * M::kRow;
     for (int c = 0; c * C < ntiles; ++c) {
         const int pb = c & 1;
         if (c >= 2) {  // chunk c - 2 (same buffer) must have been summed
-            while (__atomic_load_n(&ctl[2 + pb], __ATOMIC_ACQUIRE) < (c >> 1)) __builtin_amdgcn_s_sleep(1);
+            while (__atomic_load_n(&ctl[2 + pb], __ATOMIC_RELAXED) < (c >> 1)) __builtin_amdgcn_s_sleep(1);
+            lds_acquire();
         }
         const int tend = (c + 1) * C < ntiles ? (c + 1) * C : ntiles;
         for (int t = c * C; t < tend; ++t) {
@@ -2095,30 +2153,8 @@ __device__ __forceinline__ void mxp_rows(const uint8_t* __restrict__ W, int64_t 
             }
         }
         // publish this wave's partials of chunk c, then count the arrival
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-        int last = 0;
-        if (lane == 0) last = __atomic_fetch_add(&ctl[pb], 1, __ATOMIC_ACQ_REL) == nw - 1;
-        last = __shfl(last, 0, 64);
-        if (last) {  // every wave's partials of chunk c are in: sum the slices in order
-            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
-            const int64_t r0 = row_begin + (int64_t)c * C * 16;
-            const int nr = (int)((row_end - r0) < (int64_t)C * 16 ? (row_end - r0) : (int64_t)C * 16);
-            for (int rr = lane; rr < nr; rr += 64) {  // a lane per row, all tokens at once
-                const float* base = part + (((size_t)(pb * C + rr / 16) * nsl) * 16 + rr % 16) * TP;
-                Vec<TP> sum = *reinterpret_cast<const Vec<TP>*>(base);
-                for (int w = 1; w < nsl; ++w) {
-                    const Vec<TP> v = *reinterpret_cast<const Vec<TP>*>(base + (size_t)w * 16 * TP);
-#pragma unroll
-                    for (int tk = 0; tk < NT; ++tk) sum.v[tk] = sum.v[tk] + v.v[tk];
-                }
-#pragma unroll
-                for (int tk = 0; tk < NT; ++tk) out(tk, r0 + rr, sum.v[tk]);
-            }
-            if (lane == 0) {
-                __atomic_store_n(&ctl[pb], 0, __ATOMIC_RELAXED);
-                __atomic_fetch_add(&ctl[2 + pb], 1, __ATOMIC_RELEASE);
-            }
-        }
+        lds_release();
+        if (lane == 0) __atomic_fetch_add(&ctl[pb], 1, __ATOMIC_RELAXED);
     }
     wait_vmcnt<0>();
 }
@@ -3032,7 +3068,8 @@ int launch_mxp(int fmt, int T, const Tile& tile, const DenseArgs& a_in, void* st
                                                                                       : mxp_for<QG_FMT_BF16>(T);
     const int64_t tiles = (a.rows + 15) / 16;
     const int64_t nwg = tiles < kPersistGrid ? tiles : kPersistGrid;
-    hipLaunchKernelGGL(fn, dim3((unsigned)nwg), dim3(64 * tile.waves_per_wg), mxp_lds_bytes(fmt, tile, T),
+    // one wave per 512-wide slice and one that sums the chunks
+    hipLaunchKernelGGL(fn, dim3((unsigned)nwg), dim3(64 * (tile.waves_per_wg + 1)), mxp_lds_bytes(fmt, tile, T),
                        (hipStream_t)stream, a);
     return (int)hipGetLastError();
 }
@@ -3121,6 +3158,7 @@ int launch_argmax(int fmt, int T, const Tile& tile, const DenseArgs& a_in, void*
     ArgmaxFn fn = nullptr;
     int64_t nwg = 0;
     size_t lds = 0;
+    int waves = tile.waves_per_wg;
     DenseArgs a = a_in;
     if (tile.kind == 9 && a.cols % kSlice == 0 && tile.waves_per_wg == a.cols / kSlice && tile.rows_per_wg % 16 == 0) {
         a.nslices = a.cols / kSlice;
@@ -3130,6 +3168,7 @@ int launch_argmax(int fmt, int T, const Tile& tile, const DenseArgs& a_in, void*
         const int64_t tiles = (a.rows + 15) / 16;
         nwg = tiles < kPersistGrid ? tiles : kPersistGrid;
         lds = mxp_lds_bytes(fmt, tile, T);
+        waves = tile.waves_per_wg + 1;  // and the wave that sums the chunks
     } else if ((tile.kind == 8 || tile.kind == 11) && a.cols % (kHalfSlice * (tile.kind == 11 ? 2 : 1)) == 0 &&
                tile.waves_per_wg % (a.cols / (kHalfSlice * (tile.kind == 11 ? 2 : 1))) == 0) {
         const int H = tile.kind == 11 ? 2 : 1;
@@ -3177,11 +3216,11 @@ int launch_argmax(int fmt, int T, const Tile& tile, const DenseArgs& a_in, void*
         lds = lds_bytes(tile, T);
     }
     if (!fn) return (int)hipErrorInvalidValue;
-    const size_t keys = (size_t)tile.waves_per_wg * T * 8;  // the workgroup merge's wave maxima
+    const size_t keys = (size_t)waves * T * 8;  // the workgroup merge's wave maxima
     if (lds < keys) lds = keys;
     unsigned long long* w = (unsigned long long*)work;
     hipLaunchKernelGGL(qgemv_argmax_init_kernel, dim3(1), dim3(64), 0, (hipStream_t)stream, w, T);
-    hipLaunchKernelGGL(fn, dim3((unsigned)nwg), dim3(64 * tile.waves_per_wg), lds, (hipStream_t)stream, a, w);
+    hipLaunchKernelGGL(fn, dim3((unsigned)nwg), dim3(64 * waves), lds, (hipStream_t)stream, a, w);
     hipLaunchKernelGGL(qgemv_argmax_finish_kernel, dim3(1), dim3(64), 0, (hipStream_t)stream, (const unsigned long long*)w,
                        idx, val, T);
     return (int)hipGetLastError();

@@ -71,9 +71,9 @@
  *         the chunk of rows whose partial sums are buffered;
  *   P     x in persistent form on 512-wide k slices: one workgroup per CU, one
  *         16-row tile in flight per wave, nw = cols/512 (cols a multiple of
- *         512, at most 12 slices), rw = the chunk of rows (a multiple of 16)
- *         whose partial sums are buffered; rb only sets which rw are valid;
- *         all three formats.
+ *         512, at most 11 slices: the workgroup runs one more wave, which sums
+ *         the chunks), rw = the chunk of rows (a multiple of 16) whose partial
+ *         sums are buffered; rb only sets which rw are valid; all three formats.
  * A malformed or out-of-set value makes every call of that format return
  * QG_EINVAL.
  */

@@ -212,6 +212,13 @@ def test_tile_query_and_override(lib, monkeypatch):
         st, _ = _lib.qg_query_tile(0, 10240, 2560, 4)
         assert st == _lib.QG_EINVAL, bad
         assert _lib.qgemv_q8_0(10240, 2560, 4, W0, X0, Y0) == _lib.QG_EINVAL
+    # P runs one more wave than it has slices, which sums the chunks: twelve 512-wide
+    # slices (6144 columns) leave no room for it and are refused; eleven are accepted
+    monkeypatch.setenv("QGEMV_TILE", "q8_0:4,12,48,P")
+    assert _lib.qg_query_tile(0, 2560, 6144, 4)[0] == _lib.QG_EINVAL
+    assert "at most 11" in _lib.last_error()
+    monkeypatch.setenv("QGEMV_TILE", "q8_0:4,11,48,P")
+    assert _lib.qg_query_tile(0, 2560, 5632, 4)[0] == 0
 
 
 def test_header_names_every_tile_kind(lib, monkeypatch):
