@@ -132,6 +132,8 @@ inline size_t mxp_lds_bytes(int fmt, const Tile& t, int T) {
     return (size_t)t.waves_per_wg * mxp_slot_bytes(fmt) +
            (size_t)2 * (t.rows_per_wg / 16) * t.waves_per_wg * 16 * pad_tokens(T) * 4 + 16;
 }
+// ... and, when it fits, the workgroup's outputs [T][ybuf_rows] after them
+inline size_t mxp_ybuf_bytes(int64_t ybuf_rows, int T) { return (size_t)ybuf_rows * T * 4; }
 
 // Row-subset kernel: rings of `depth` 8-row slots per wave, then partial sums (x in registers).
 inline size_t gather_lds_bytes(int fmt, const Tile& t, int T, int nslices) {
@@ -180,6 +182,7 @@ struct DenseArgs {
     int cols;
     int nslices;
     int rows_per_wg;
+    int ybuf_rows = 0;  // kind 9: rows of y a workgroup holds in LDS until its end (0: stores as it goes)
 };
 
 struct GroupedArgs {
