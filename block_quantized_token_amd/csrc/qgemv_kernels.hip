@@ -28,6 +28,7 @@
 // never on T, so a token's result is the same bit for bit at any T (the pages
 // remark on that property: opus-mtp-turbo report, finding 3).
 #include <hip/hip_runtime.h>
+#include <cstdlib>
 #include <stdint.h>
 
 #include <mutex>
@@ -3094,7 +3095,8 @@ int launch_mxp(int fmt, int T, const Tile& tile, const DenseArgs& a_in, void* st
     size_t lds = mxp_lds_bytes(fmt, tile, T);
     const int64_t ycap = (tiles + nwg - 1) / nwg * 16;
     a.ybuf_rows = 0;
-    if (lds + mxp_ybuf_bytes(ycap, T) <= kMaxLds) {
+    const char* direct = getenv("QGEMV_P_DIRECT_STORES");
+    if (!(direct && direct[0] == '1') && lds + mxp_ybuf_bytes(ycap, T) <= kMaxLds) {
         a.ybuf_rows = (int)ycap;
         lds += mxp_ybuf_bytes(ycap, T);
     }

@@ -76,6 +76,9 @@
  *         sums are buffered; rb only sets which rw are valid; all three formats.
  * A malformed or out-of-set value makes every call of that format return
  * QG_EINVAL.
+ * QGEMV_P_DIRECT_STORES=1 makes kind P store each chunk's outputs as it sums them
+ * instead of holding a workgroup's outputs in LDS until its end (what it does by
+ * itself when they do not fit there); the bits are the same either way.
  */
 #ifndef QGEMV_H
 #define QGEMV_H

@@ -225,7 +225,8 @@ def test_header_names_every_tile_kind(lib, monkeypatch):
     """Every kind letter QGEMV_TILE accepts is documented in the header, and every
     documented letter is accepted for some tile."""
     text = open(HEADER).read()
-    para = text[text.index("QGEMV_TILE="):text.index("QG_EINVAL.\n */")]
+    start = text.index("QGEMV_TILE=")
+    para = text[start:text.index("QG_EINVAL.\n", start)]
     documented = set(re.findall(r"^ \*   ([a-zA-Z])(?:<D>)?\s", para, flags=re.M))
     # (kind, spec suffix, shape) that the compiled set accepts
     probes = {"d": ("d", 10240, 2560, "2,5,8"), "s": ("s", 10240, 2560, "4,5,16"),

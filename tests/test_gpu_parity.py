@@ -461,6 +461,22 @@ def test_mxp_chunks_keep_bits(torch, monkeypatch):
         assert np.array_equal(ops.gemv("q8_0", Wd, xd, c["rows"]).cpu().numpy(), base), chunk
 
 
+def test_mxp_direct_stores_keep_bits(torch, orc, monkeypatch):
+    """Kind P holds a workgroup's outputs in LDS and writes them at its end when they fit
+    (every shape here); the direct stores it falls back to on taller matrices, forced by
+    QGEMV_P_DIRECT_STORES, give the same bits and pass the oracle too."""
+    for fmt, rows, cols, chunk in ((Q8, 10240, 2560, 3), (Q4, 4096 + 37, 1024, 1), (BF, 333, 1536, 2)):
+        rng = np.random.default_rng(rows + cols + fmt)
+        W = I.weights(rng, fmt, rows, cols)
+        x = I.activations(rng, cols)
+        monkeypatch.setenv("QGEMV_TILE", mxp_tile(cols, chunk, NAMES[fmt]))
+        monkeypatch.delenv("QGEMV_P_DIRECT_STORES", raising=False)
+        held = check_dense(torch, orc, fmt, rows, cols, W, x, f"mxp held {rows}x{cols}")
+        monkeypatch.setenv("QGEMV_P_DIRECT_STORES", "1")
+        direct = check_dense(torch, orc, fmt, rows, cols, W, x, f"mxp direct {rows}x{cols}")
+        assert np.array_equal(held, direct), (fmt, rows, cols)
+
+
 def test_mxp_exact_inputs_bitwise(torch, orc, monkeypatch):
     """Dyadic inputs (exact result representable) and identity-like matrices (y = a
     permutation of x, carried exactly by the three bf16 pieces)."""
