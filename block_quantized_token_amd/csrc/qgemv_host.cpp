@@ -118,10 +118,10 @@ const TuneEntry kTuned[] = {
     {QG_FMT_Q8_0, 2560, 6144, 0, "4,12,16,X"},
     // LM head, 248,320 x 5,120 Q8_0: the persistent matrix-core kernel on the
     // LDS-DMA ring, one kind at every T, so a token's bits do not depend on T:
-    // 234 / 237 / 241 / 245 µs at T = 1..4 against 234 / 243 / 269 / 279 for the
-    // best earlier kinds (the LDS-DMA vector-ALU ring at T <= 2, the persistent
-    // matrix cores with x in registers at T >= 3).  Chunks of 3 or 4 tiles time
-    // alike; 2 tiles cost 1-4 µs.
+    // 216 / 217 / 219 / 222 µs at T = 1..4 (225 / 227 / 228 / 230 without the
+    // streaming loads) against 234 / 243 / 269 / 279 for the best earlier kinds
+    // (the LDS-DMA vector-ALU ring at T <= 2, the persistent matrix cores with x in
+    // registers at T >= 3).  Chunks of 3 or 4 tiles time alike; 2 tiles cost 1-4 µs.
     {QG_FMT_Q8_0, 248320, 5120, 0, "4,10,48,P"},
 };
 
@@ -137,12 +137,19 @@ Tile default_tile(int fmt, int64_t rows, int64_t cols, int T) {
         if (e.fmt == fmt && e.rows == rows && e.cols == cols && (e.T == 0 || e.T == T) && parse_tile_spec(e.tile, &t, &why))
             return t;
     }
-    // Q8_0 matrices far beyond the 256 MB last-level cache, up to 11 512-wide
-    // slices (and a wave that sums): the persistent matrix cores on the LDS-DMA ring, chunks of 3 tiles
-    // (151,936 x 3,584: 105 / 108 / 110 / 112 µs at T = 1..4 against 116 / 126 /
-    // 144 / 162; at 65,536 x 5,120, 357 MB, it still loses at T <= 2)
-    if (fmt == QG_FMT_Q8_0 && rows * row_bytes(fmt, cols) >= (int64_t)512 << 20 && cols % kSlice == 0 &&
-        nslices + 1 <= kMaxWaves) {
+    // Q8_0 matrices about the size of the 256 MiB last-level cache or larger, up to
+    // 11 512-wide slices (and a wave that sums): the persistent matrix cores on the
+    // LDS-DMA ring, chunks of 3 tiles, with streaming loads.  µs at T = 1..4 against
+    // the rule's next pick: 151,936 x 3,584 (551 MiB) 93.0 / 93.7 / 94.7 / 96.4
+    // against 116 / 126 / 144 / 162 (earlier kinds); 65,536 x 5,120 (340 MiB) 63.3 /
+    // 64.9 / 65.3 / 66.7 against 65.2 / 65.9 / 66.8 / 67.7; 49,152 x 5,120 (255 MiB)
+    // 51.0 / 51.9 / 53.0 / 54.1 against 52.4 / 52.9 / 53.9 / 55.3; at 32,768 x 5,120
+    // (170 MiB) the next pick wins at T >= 2.  With fewer than seven slices a CU
+    // streams too little: 100,000 x 2,560 (259 MiB, five slices) 47.5 / 48.1 / 49.2 /
+    // 51.1 against 46.2 / 46.4 / 47.0 / 47.4, so below 512 MiB those stay on the next pick.
+    const int64_t wbytes = rows * row_bytes(fmt, cols);
+    if (fmt == QG_FMT_Q8_0 && cols % kSlice == 0 && nslices + 1 <= kMaxWaves &&
+        (wbytes >= (int64_t)512 << 20 || (wbytes >= (int64_t)224 << 20 && nslices >= 7))) {
         t.kind = 9;
         t.depth = 1;
         t.rows_per_batch = 4;

@@ -718,11 +718,21 @@ __device__ __forceinline__ void stream_rows(const uint8_t* __restrict__ W, int64
 // ends, since an empty load still writes its zeros.
 typedef __attribute__((address_space(3))) void lds_void_t;
 
+// Cache policy of a load: kStreamPolicy sets the non-temporal bit, so the lines are
+// kept as streaming data that the caches give up first.  Measured per kernel kind
+// (the bits are the same either way): it shortens the LM-head stream by ~10 µs and
+// the Q4_0 and BF16 8192 x 2560 mat-vecs by 0.1-0.5 µs, and lengthens the Q8_0
+// 10240 x 2560 and 2560 x 2560 ones by 0.1-0.4 µs and the grouped experts, whose
+// experts several tokens share, by 0.4-0.6 µs at T >= 2.
+constexpr int kDefaultPolicy = 0;
+constexpr int kStreamPolicy = 2;
+
 // One direct-to-LDS load (16 bytes per lane).  The builtin only exists for the
 // device; the host pass compiles an empty body it never runs.
+template <int POLICY = kDefaultPolicy>
 __device__ __forceinline__ void load_lds16(__amdgpu_buffer_rsrc_t rsrc, uint8_t* lds, int voffset) {
 #if defined(__HIP_DEVICE_COMPILE__)
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void_t*)lds, 16, voffset, 0, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void_t*)lds, 16, voffset, 0, 0, POLICY);
 #else
     (void)rsrc, (void)lds, (void)voffset;
 #endif
@@ -1618,6 +1628,10 @@ __device__ __forceinline__ void mfma_persist_q8(const uint8_t* __restrict__ W, i
 // A tile is R groups of 16 rows (R = 2: twice the bytes in flight per wave, for
 // the formats with short rows) of a slice of H 256-wide halves (H = 2: 512-wide
 // slices, 16 blocks a wave, for rows of more than twelve 256-wide slices).
+// Cache policy of the dense matrix-core kinds' weight loads, by format (measured).
+template <int FMT>
+constexpr int kDensePolicy = FMT == QG_FMT_Q8_0 ? kDefaultPolicy : kStreamPolicy;
+
 template <int FMT, int R = 1, int H = 1>
 struct MxShape {
     static constexpr int kChunks = StreamFmt<FMT>::kChunks / 2 * H;      // 16-byte chunks of a row slice
@@ -1632,7 +1646,7 @@ struct MxShape {
 // 64 k + l (row / chunk of the slice); lanes past the tile's last chunk do not
 // load, so the slot is exactly the tile's bytes; rows past the range are
 // outside the descriptor and read as zeros.
-template <int FMT, int R = 1, int H = 1>
+template <int FMT, int R = 1, int H = 1, int POLICY = kDefaultPolicy>
 __device__ __forceinline__ void mx_issue(const uint8_t* __restrict__ W, int64_t row_bytes, int64_t row_begin,
                                          int64_t row_end, int ntiles, int t, const int (&off)[MxShape<FMT, R, H>::kLoads],
                                          uint8_t* slot, int lane) {
@@ -1644,8 +1658,9 @@ __device__ __forceinline__ void mx_issue(const uint8_t* __restrict__ W, int64_t 
     const __amdgpu_buffer_rsrc_t rsrc =
         __builtin_amdgcn_make_buffer_rsrc((void*)(W + r0 * row_bytes), (short)0, num, kBufferRsrcWord3);
 #pragma unroll
-    for (int k = 0; k < M::kLoads - 1; ++k) load_lds16(rsrc, slot + 1024 * k, off[k]);
-    if (M::kLastLanes == 64 || lane < M::kLastLanes) load_lds16(rsrc, slot + 1024 * (M::kLoads - 1), off[M::kLoads - 1]);
+    for (int k = 0; k < M::kLoads - 1; ++k) load_lds16<POLICY>(rsrc, slot + 1024 * k, off[k]);
+    if (M::kLastLanes == 64 || lane < M::kLastLanes)
+        load_lds16<POLICY>(rsrc, slot + 1024 * (M::kLoads - 1), off[M::kLoads - 1]);
 }
 
 // Byte q of the 12-byte window w[3] as an fp32 (signed).
@@ -1758,7 +1773,8 @@ __device__ __forceinline__ void mx_load_x(const float* __restrict__ x, const int
 // workgroup, W under 2 GB): every wave holds the workgroup's ids in registers (id j
 // in lane j % 64 of register j / 64) and each load lane takes its row's id from the
 // lane that holds it; an id outside [0, wrows) loads nothing (the caller writes NaN).
-template <int FMT, int NT, int R, bool PRE = false, int H = 1, bool GATHER = false, class Out>
+template <int FMT, int NT, int R, bool PRE = false, int H = 1, bool GATHER = false, int POLICY = kDefaultPolicy,
+          class Out>
 __device__ __forceinline__ void mx_rows(const uint8_t* __restrict__ W, int64_t row_bytes, int nsl,
                                         const float4 (&xv)[NT][H], int64_t row_begin, int64_t row_end, int nw,
                                         Out&& out, const int32_t* __restrict__ ids = nullptr, int64_t wrows = 0) {
@@ -1819,7 +1835,7 @@ __device__ __forceinline__ void mx_rows(const uint8_t* __restrict__ W, int64_t r
                 load_lds16(wr, slot + 1024 * k, live ? (int)(id * row_bytes) + off[k] : kNoLoad);
             }
         } else {
-            mx_issue<FMT, R, H>(W, row_bytes, row_begin, row_end, ntiles, t, off, slot, lane);
+            mx_issue<FMT, R, H, POLICY>(W, row_bytes, row_begin, row_end, ntiles, t, off, slot, lane);
         }
     };
     // the wave's first tile, unless PRE has it on its way already (x is older)
@@ -1955,7 +1971,8 @@ struct MxpShape {
 
 // 16-row tile t of the wave's slice into its slot: lane l of load k fetches
 // chunk 64 k + l (row / chunk of the row slice); rows past the range are
-// outside the descriptor and read as zeros.
+// outside the descriptor and read as zeros.  The matrices this kind serves are
+// far beyond the last-level cache: the loads carry the streaming policy.
 template <int FMT>
 __device__ __forceinline__ void mxp_issue(const uint8_t* __restrict__ W, int64_t row_bytes, int64_t row_begin,
                                           int64_t row_end, int t, const int (&off)[MxpShape<FMT>::kLoads],
@@ -1966,8 +1983,9 @@ __device__ __forceinline__ void mxp_issue(const uint8_t* __restrict__ W, int64_t
     const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
         (void*)(W + r0 * row_bytes), (short)0, (int)(rows_here * row_bytes), kBufferRsrcWord3);
 #pragma unroll
-    for (int k = 0; k < M::kLoads - 1; ++k) load_lds16(rsrc, slot + 1024 * k, off[k]);
-    if (M::kLastLanes == 64 || lane < M::kLastLanes) load_lds16(rsrc, slot + 1024 * (M::kLoads - 1), off[M::kLoads - 1]);
+    for (int k = 0; k < M::kLoads - 1; ++k) load_lds16<kStreamPolicy>(rsrc, slot + 1024 * k, off[k]);
+    if (M::kLastLanes == 64 || lane < M::kLastLanes)
+        load_lds16<kStreamPolicy>(rsrc, slot + 1024 * (M::kLoads - 1), off[M::kLoads - 1]);
 }
 
 // The MFMAs of the 16 blocks of one tile, from their bytes: acc += scale *
@@ -2304,7 +2322,7 @@ qgemv_mx_kernel(const uint8_t* __restrict__ W, const float* __restrict__ x, floa
     for (int t = 0; t < T; ++t) xoff[t] = (int64_t)t * cols;
     float4 xv[T][H];
     mx_load_x<FMT, T, H>(x, xoff, nslices, xv);
-    mx_rows<FMT, T, R, false, H>(W, row_bytes, nslices, xv, row_begin, row_end, nw,
+    mx_rows<FMT, T, R, false, H, false, kDensePolicy<FMT>>(W, row_bytes, nslices, xv, row_begin, row_end, nw,
                     [=](int t, int64_t row, float v) { y[t * rows + row] = v; });
 }
 
@@ -2398,7 +2416,8 @@ __global__ void __launch_bounds__(64 * kMaxWaves) qgemv_mx_argmax_kernel(DenseAr
     for (int t = 0; t < T; ++t) xoff[t] = (int64_t)t * a.cols;
     float4 xv[T][H];
     mx_load_x<FMT, T, H>(a.x, xoff, a.nslices, xv);
-    mx_rows<FMT, T, R, false, H>(a.W, a.row_bytes, a.nslices, xv, row_begin, row_end, (int)(blockDim.x >> 6), best);
+    mx_rows<FMT, T, R, false, H, false, kDensePolicy<FMT>>(a.W, a.row_bytes, a.nslices, xv, row_begin, row_end,
+                                                          (int)(blockDim.x >> 6), best);
     best.merge(work);
 }
 

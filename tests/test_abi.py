@@ -181,11 +181,14 @@ def test_tile_query_and_override(lib, monkeypatch):
             # the vector-ALU kinds share their arithmetic per k slice; the matrix-core kinds do not
             arith = {(t["mfma"], t["kind"] if t["kind"] in (8, 9, 11) else -1) for t in tiles}
             assert len(arith) == 1, (fmt, rows, cols, tiles)
-    # the LM head and other Q8_0 matrices past 512 MiB: the persistent matrix cores on 512-wide slices
-    for rows, cols in ((248320, 5120), (151936, 3584)):
+    # the LM head and other Q8_0 matrices of 224 MiB or more with at least seven 512-wide
+    # slices, or of 512 MiB or more: the persistent matrix cores on 512-wide slices
+    for rows, cols in ((248320, 5120), (151936, 3584), (65536, 5120), (49152, 5120)):
         t = ops.query_tile("q8_0", rows, cols, 4)
         assert (t["kind"], t["k_slice"], t["waves_per_wg"], t["lanes_per_row"]) == (9, 512, cols // 512, 4), t
-    assert ops.query_tile("q8_0", 65536, 5120, 4)["kind"] != 9  # 357 MB: below the threshold
+    assert ops.query_tile("q8_0", 32768, 5120, 4)["kind"] != 9  # 170 MiB
+    assert ops.query_tile("q8_0", 100000, 2560, 4)["kind"] != 9  # 259 MiB, five slices
+    assert ops.query_tile("q8_0", 220000, 2560, 4)["kind"] == 9  # 571 MiB
     # more than twelve 256-wide slices: the matrix cores on 512-wide slices
     t = ops.query_tile("q8_0", 2560, 6144, 1)
     assert (t["kind"], t["k_slice"], t["waves_per_wg"], t["lanes_per_row"]) == (11, 512, 12, 4), t
