@@ -118,8 +118,8 @@ const TuneEntry kTuned[] = {
     {QG_FMT_Q8_0, 2560, 6144, 0, "4,12,16,X"},
     // LM head, 248,320 x 5,120 Q8_0: the persistent matrix-core kernel on the
     // LDS-DMA ring, one kind at every T, so a token's bits do not depend on T:
-    // 216 / 217 / 219 / 222 µs at T = 1..4 (225 / 227 / 228 / 230 without the
-    // streaming loads) against 234 / 243 / 269 / 279 for the best earlier kinds
+    // 204 / 203 / 205 / 212 µs at T = 1..4 (225 / 227 / 228 / 230 with every load
+    // under the default cache policy) against 234 / 243 / 269 / 279 for the best earlier kinds
     // (the LDS-DMA vector-ALU ring at T <= 2, the persistent matrix cores with x in
     // registers at T >= 3).  Chunks of 3 or 4 tiles time alike; 2 tiles cost 1-4 µs.
     {QG_FMT_Q8_0, 248320, 5120, 0, "4,10,48,P"},
@@ -139,14 +139,15 @@ Tile default_tile(int fmt, int64_t rows, int64_t cols, int T) {
     }
     // Q8_0 matrices about the size of the 256 MiB last-level cache or larger, up to
     // 11 512-wide slices (and a wave that sums): the persistent matrix cores on the
-    // LDS-DMA ring, chunks of 3 tiles, with streaming loads.  µs at T = 1..4 against
-    // the rule's next pick: 151,936 x 3,584 (551 MiB) 93.0 / 93.7 / 94.7 / 96.4
-    // against 116 / 126 / 144 / 162 (earlier kinds); 65,536 x 5,120 (340 MiB) 63.3 /
-    // 64.9 / 65.3 / 66.7 against 65.2 / 65.9 / 66.8 / 67.7; 49,152 x 5,120 (255 MiB)
-    // 51.0 / 51.9 / 53.0 / 54.1 against 52.4 / 52.9 / 53.9 / 55.3; at 32,768 x 5,120
-    // (170 MiB) the next pick wins at T >= 2.  With fewer than seven slices a CU
-    // streams too little: 100,000 x 2,560 (259 MiB, five slices) 47.5 / 48.1 / 49.2 /
-    // 51.1 against 46.2 / 46.4 / 47.0 / 47.4, so below 512 MiB those stay on the next pick.
+    // LDS-DMA ring, chunks of 3 tiles, with split loads.  µs at T = 1..4 against
+    // the rule's next pick: 151,936 x 3,584 (551 MiB) 87.6 / 87.8 / 90.8 / 93.7
+    // against 116 / 126 / 144 / 162 (earlier kinds); 65,536 x 5,120 (340 MiB) 60.9 /
+    // 61.4 / 62.5 / 64.4 against 65.2 / 65.9 / 66.8 / 67.7; 49,152 x 5,120 (255 MiB)
+    // 48.0 / 48.6 / 49.6 / 51.3 against 52.4 / 52.9 / 53.9 / 55.3; at 32,768 x 5,120
+    // (170 MiB) it loses from T = 2 on (35.6 / 36.3 / 37.5 against 35.5 / 36.1 / 36.6).
+    // With fewer than seven slices a CU streams too little: 100,000 x 2,560
+    // (259 MiB, five slices) 49.0 / 51.2 / 53.3 / 53.6 against 46.6 / 46.9 / 47.5, so
+    // below 512 MiB those stay on the next pick.
     const int64_t wbytes = rows * row_bytes(fmt, cols);
     if (fmt == QG_FMT_Q8_0 && cols % kSlice == 0 && nslices + 1 <= kMaxWaves &&
         (wbytes >= (int64_t)512 << 20 || (wbytes >= (int64_t)224 << 20 && nslices >= 7))) {

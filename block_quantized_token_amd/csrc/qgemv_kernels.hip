@@ -718,14 +718,20 @@ __device__ __forceinline__ void stream_rows(const uint8_t* __restrict__ W, int64
 // ends, since an empty load still writes its zeros.
 typedef __attribute__((address_space(3))) void lds_void_t;
 
-// Cache policy of a load: kStreamPolicy sets the non-temporal bit, so the lines are
-// kept as streaming data that the caches give up first.  Measured per kernel kind
-// (the bits are the same either way): it shortens the LM-head stream by ~10 µs and
-// the Q4_0 and BF16 8192 x 2560 mat-vecs by 0.1-0.5 µs, and lengthens the Q8_0
-// 10240 x 2560 and 2560 x 2560 ones by 0.1-0.4 µs and the grouped experts, whose
-// experts several tokens share, by 0.4-0.6 µs at T >= 2.
+// Cache policy of a load.  kStreamPolicy sets the non-temporal bit, so the caches
+// keep the lines as streaming data that they give up first.  kSplitPolicy is a tag
+// for the weight streams: a wave's row piece rarely starts or ends on a 128-byte
+// line, so the lines at its two ends are shared with the neighbouring pieces, which
+// other waves load; those chunks keep the default policy, so that the line stays
+// for its second reader, and every other chunk streams (the bits are the same
+// under any policy).  Measured per kernel kind: the persistent kind splits (the LM
+// head: 225-230 µs at T = 1..4 with the default policy, 214-220 streaming, 203-210
+// split); the dense matrix-core kinds stream for Q4_0 and BF16 only (kDensePolicy);
+// the grouped experts, whose experts several tokens share, and the gathered row
+// subset keep the default (streaming cost them 0.4-0.6 and 0.3-0.7 µs).
 constexpr int kDefaultPolicy = 0;
 constexpr int kStreamPolicy = 2;
+constexpr int kSplitPolicy = -1;
 
 // One direct-to-LDS load (16 bytes per lane).  The builtin only exists for the
 // device; the host pass compiles an empty body it never runs.
@@ -736,6 +742,43 @@ __device__ __forceinline__ void load_lds16(__amdgpu_buffer_rsrc_t rsrc, uint8_t*
 #else
     (void)rsrc, (void)lds, (void)voffset;
 #endif
+}
+
+// Bit k set: the 16-byte chunk this lane fetches in load k of a tile lies in a
+// 128-byte line that also holds bytes of another row piece.  Lane l of load k
+// fetches chunk 64 k + l of the tile, `chunks` chunks per row piece; the first row
+// piece of the tile starts at byte `first` (an address: the line grid is absolute)
+// and row r's at first + r * row_bytes.  The same for every tile of a range whose
+// tiles lie a multiple of 128 bytes apart.
+template <int LOADS>
+__device__ __forceinline__ uint32_t shared_line_mask(uint64_t first, int64_t row_bytes, int chunks, int rows,
+                                                     int lane) {
+    uint32_t m = 0;
+#pragma unroll
+    for (int k = 0; k < LOADS; ++k) {
+        const int j = 64 * k + lane;
+        const int r = j / chunks, c = j % chunks;
+        const uint64_t ps = first + (uint64_t)r * (uint64_t)row_bytes;  // the piece
+        const uint64_t pe = ps + 16 * (uint64_t)chunks - 1;            // its last byte
+        const uint64_t line = (ps + 16 * (uint64_t)c) >> 7;
+        const bool head = (ps & 127) != 0 && line == (ps >> 7);
+        const bool tail = ((pe + 1) & 127) != 0 && line == (pe >> 7);
+        if (r < rows && (head || tail)) m |= 1u << k;
+    }
+    return m;
+}
+
+// One load of a weight stream under POLICY (kSplitPolicy: the default policy if
+// `shared`, else streaming; the lanes of one load split into two masked loads).
+template <int POLICY>
+__device__ __forceinline__ void load_w16(__amdgpu_buffer_rsrc_t rsrc, uint8_t* lds, int voffset, bool shared) {
+    if constexpr (POLICY == kSplitPolicy) {
+        if (shared) load_lds16<kDefaultPolicy>(rsrc, lds, voffset);
+        else load_lds16<kStreamPolicy>(rsrc, lds, voffset);
+    } else {
+        (void)shared;
+        load_lds16<POLICY>(rsrc, lds, voffset);
+    }
 }
 
 template <int V>
@@ -1628,7 +1671,11 @@ __device__ __forceinline__ void mfma_persist_q8(const uint8_t* __restrict__ W, i
 // A tile is R groups of 16 rows (R = 2: twice the bytes in flight per wave, for
 // the formats with short rows) of a slice of H 256-wide halves (H = 2: 512-wide
 // slices, 16 blocks a wave, for rows of more than twelve 256-wide slices).
-// Cache policy of the dense matrix-core kinds' weight loads, by format (measured).
+// Cache policy of the dense matrix-core kinds' weight loads, by format (measured:
+// streaming takes 0.1-0.5 µs off the Q4_0 and BF16 8192 x 2560 calls and adds
+// 0.1-0.4 µs to the Q8_0 ones; the split the persistent kind uses adds 0.5-1.2 µs
+// to every one of them, whose few tiles per wave leave no room for twice the load
+// instructions).
 template <int FMT>
 constexpr int kDensePolicy = FMT == QG_FMT_Q8_0 ? kDefaultPolicy : kStreamPolicy;
 
@@ -1649,7 +1696,7 @@ struct MxShape {
 template <int FMT, int R = 1, int H = 1, int POLICY = kDefaultPolicy>
 __device__ __forceinline__ void mx_issue(const uint8_t* __restrict__ W, int64_t row_bytes, int64_t row_begin,
                                          int64_t row_end, int ntiles, int t, const int (&off)[MxShape<FMT, R, H>::kLoads],
-                                         uint8_t* slot, int lane) {
+                                         uint8_t* slot, int lane, uint32_t shm = 0) {
     using M = MxShape<FMT, R, H>;
     const bool live = t < ntiles;
     const int64_t r0 = row_begin + (int64_t)(live ? t : 0) * M::kRows;
@@ -1658,9 +1705,9 @@ __device__ __forceinline__ void mx_issue(const uint8_t* __restrict__ W, int64_t 
     const __amdgpu_buffer_rsrc_t rsrc =
         __builtin_amdgcn_make_buffer_rsrc((void*)(W + r0 * row_bytes), (short)0, num, kBufferRsrcWord3);
 #pragma unroll
-    for (int k = 0; k < M::kLoads - 1; ++k) load_lds16<POLICY>(rsrc, slot + 1024 * k, off[k]);
+    for (int k = 0; k < M::kLoads - 1; ++k) load_w16<POLICY>(rsrc, slot + 1024 * k, off[k], (shm >> k) & 1u);
     if (M::kLastLanes == 64 || lane < M::kLastLanes)
-        load_lds16<POLICY>(rsrc, slot + 1024 * (M::kLoads - 1), off[M::kLoads - 1]);
+        load_w16<POLICY>(rsrc, slot + 1024 * (M::kLoads - 1), off[M::kLoads - 1], (shm >> (M::kLoads - 1)) & 1u);
 }
 
 // Byte q of the 12-byte window w[3] as an fp32 (signed).
@@ -1807,6 +1854,12 @@ __device__ __forceinline__ void mx_rows(const uint8_t* __restrict__ W, int64_t r
         const int r = j / M::kChunks, c = j % M::kChunks;
         off[k] = r < RT ? (GATHER ? 0 : (int)(r * row_bytes)) + s * M::kChunks * 16 + 16 * c : kNoLoad;
     }
+    // tiles lie RT rows apart, a multiple of 128 bytes for rows of whole 256-wide slices
+    uint32_t shm = 0;
+    if constexpr (POLICY == kSplitPolicy && !GATHER)
+        shm = shared_line_mask<L>((uint64_t)(uintptr_t)W + (uint64_t)row_begin * (uint64_t)row_bytes +
+                                      (uint64_t)s * M::kChunks * 16,
+                                  row_bytes, M::kChunks, RT, lane);
     int my_id0 = -1, my_id1 = -1;
     const __amdgpu_buffer_rsrc_t wr =
         __builtin_amdgcn_make_buffer_rsrc((void*)W, (short)0, GATHER ? (int)(wrows * row_bytes) : 0, kBufferRsrcWord3);
@@ -1835,7 +1888,7 @@ __device__ __forceinline__ void mx_rows(const uint8_t* __restrict__ W, int64_t r
                 load_lds16(wr, slot + 1024 * k, live ? (int)(id * row_bytes) + off[k] : kNoLoad);
             }
         } else {
-            mx_issue<FMT, R, H, POLICY>(W, row_bytes, row_begin, row_end, ntiles, t, off, slot, lane);
+            mx_issue<FMT, R, H, POLICY>(W, row_bytes, row_begin, row_end, ntiles, t, off, slot, lane, shm);
         }
     };
     // the wave's first tile, unless PRE has it on its way already (x is older)
@@ -1972,20 +2025,21 @@ struct MxpShape {
 // 16-row tile t of the wave's slice into its slot: lane l of load k fetches
 // chunk 64 k + l (row / chunk of the row slice); rows past the range are
 // outside the descriptor and read as zeros.  The matrices this kind serves are
-// far beyond the last-level cache: the loads carry the streaming policy.
+// beyond the last-level cache: the loads stream, but for the chunks in lines
+// shared with a neighbouring piece (`shm`, kSplitPolicy).
 template <int FMT>
 __device__ __forceinline__ void mxp_issue(const uint8_t* __restrict__ W, int64_t row_bytes, int64_t row_begin,
                                           int64_t row_end, int t, const int (&off)[MxpShape<FMT>::kLoads],
-                                          uint8_t* slot, int lane) {
+                                          uint8_t* slot, int lane, uint32_t shm) {
     using M = MxpShape<FMT>;
     const int64_t r0 = row_begin + (int64_t)t * 16;
     const int64_t rows_here = row_end - r0 < 16 ? row_end - r0 : 16;
     const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
         (void*)(W + r0 * row_bytes), (short)0, (int)(rows_here * row_bytes), kBufferRsrcWord3);
 #pragma unroll
-    for (int k = 0; k < M::kLoads - 1; ++k) load_lds16<kStreamPolicy>(rsrc, slot + 1024 * k, off[k]);
+    for (int k = 0; k < M::kLoads - 1; ++k) load_w16<kSplitPolicy>(rsrc, slot + 1024 * k, off[k], (shm >> k) & 1u);
     if (M::kLastLanes == 64 || lane < M::kLastLanes)
-        load_lds16<kStreamPolicy>(rsrc, slot + 1024 * (M::kLoads - 1), off[M::kLoads - 1]);
+        load_w16<kSplitPolicy>(rsrc, slot + 1024 * (M::kLoads - 1), off[M::kLoads - 1], (shm >> (M::kLoads - 1)) & 1u);
 }
 
 // The MFMAs of the 16 blocks of one tile, from their bytes: acc += scale *
@@ -2052,6 +2106,11 @@ __device__ __forceinline__ void mxp_rows(const uint8_t* __restrict__ W, int64_t 
         const int r = j / M::kChunks, c = j % M::kChunks;
         off[k] = r < 16 ? (int)(r * row_bytes) + s * M::kRow + 16 * c : kNoLoad;
     }
+    // tiles lie 16 rows apart: a multiple of 128 bytes for every Q8_0 / Q4_0 / BF16
+    // row of whole 512-wide slices, so one mask serves them all
+    const uint32_t shm = shared_line_mask<L>((uint64_t)(uintptr_t)W + (uint64_t)row_begin * (uint64_t)row_bytes +
+                                                 (uint64_t)s * M::kRow,
+                                             row_bytes, M::kChunks, 16, lane);
     // x of the slice into the slot (token t at 2048 t), then into registers: lane
     // l takes k = 4 l .. 4 l + 3 of each 256-wide half (the summing wave has no
     // slice: it skips the staging and keeps zero fragments)
@@ -2139,7 +2198,7 @@ __device__ __forceinline__ void mxp_rows(const uint8_t* __restrict__ W, int64_t 
         }
         return;
     }
-    if (ntiles > 0) mxp_issue<FMT>(W, row_bytes, row_begin, row_end, 0, off, slot, lane);
+    if (ntiles > 0) mxp_issue<FMT>(W, row_bytes, row_begin, row_end, 0, off, slot, lane, shm);
 
     const uint8_t* rowp = slot + n * M::kRow;
     for (int c = 0; c * C < ntiles; ++c) {
@@ -2155,7 +2214,7 @@ __device__ __forceinline__ void mxp_rows(const uint8_t* __restrict__ W, int64_t 
 #pragma unroll
             for (int b = 0; b < 16; ++b) raw[b] = mx_braw<FMT>(rowp, b, g);
             wait_lgkmcnt0();  // the tile is in registers: the slot takes the next one
-            if (t + 1 < ntiles) mxp_issue<FMT>(W, row_bytes, row_begin, row_end, t + 1, off, slot, lane);
+            if (t + 1 < ntiles) mxp_issue<FMT>(W, row_bytes, row_begin, row_end, t + 1, off, slot, lane, shm);
             F4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
             mxp_math<FMT, NT>(afrag, raw, g, acc);
 #pragma unroll
