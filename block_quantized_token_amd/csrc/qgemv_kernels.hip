@@ -781,6 +781,16 @@ __device__ __forceinline__ void load_w16(__amdgpu_buffer_rsrc_t rsrc, uint8_t* l
     }
 }
 
+// q = a / b, r = a % b for 0 <= a < 16 and b >= 1 (the waves and slices of a
+// workgroup): a short scalar loop in place of a general 32-bit division, which
+// sits in front of a wave's first load (measured 0.03-0.1 µs per call on the
+// 2560-column mat-vecs).
+__device__ __forceinline__ void small_divmod(int a, int b, int& q, int& r) {
+    q = 0;
+    r = a;
+    while (r >= b) { r -= b; ++q; }
+}
+
 template <int V>
 __device__ __forceinline__ void wait_vmcnt() {
     static_assert(V >= 0 && V <= 63, "vmcnt is 6 bits");
@@ -1808,7 +1818,9 @@ __device__ __forceinline__ void mx_prefetch(const uint8_t* __restrict__ W, int64
 template <int FMT, int NT, int H = 1>
 __device__ __forceinline__ void mx_load_x(const float* __restrict__ x, const int64_t (&xoff)[NT], int nsl,
                                           float4 (&xv)[NT][H]) {
-    const int k0 = ((int)__builtin_amdgcn_readfirstlane(threadIdx.x >> 6) % nsl) * (kHalfSlice * H);
+    int rg, s;
+    small_divmod((int)__builtin_amdgcn_readfirstlane(threadIdx.x >> 6), nsl, rg, s);
+    const int k0 = s * (kHalfSlice * H);
 #pragma unroll
     for (int t = 0; t < NT; ++t)
 #pragma unroll
@@ -1841,7 +1853,9 @@ __device__ __forceinline__ void mx_rows(const uint8_t* __restrict__ W, int64_t r
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: keeps descriptors and M0 scalar
     const int n = lane & 15, g = lane >> 4;
-    const int s = wave % nsl, rg = wave / nsl, RG = nw / nsl;
+    int s, rg, RG, rest;
+    small_divmod(wave, nsl, rg, s);
+    small_divmod(nw, nsl, RG, rest);
     const int ntiles = (int)((row_end - row_begin + RT - 1) / RT);
     uint8_t* slot = smem + wave * M::kSlot;
     uint8_t* reg = smem + nw * M::kSlot + wave * REG;
@@ -1938,7 +1952,7 @@ __device__ __forceinline__ void mx_rows(const uint8_t* __restrict__ W, int64_t r
         }
     }
 
-    const int mine = ntiles > rg ? (ntiles - rg + RG - 1) / RG : 0;
+    const int mine = ntiles > rg ? (RG == 1 ? ntiles - rg : (ntiles - rg + RG - 1) / RG) : 0;
     const uint8_t* rowp = slot + n * (M::kChunks * 16);
     for (int i = 0; i < mine; ++i) {
         const int t = rg + i * RG;
