@@ -1847,6 +1847,13 @@ __device__ __forceinline__ void mx_rows(const uint8_t* __restrict__ W, int64_t r
     // a lane's rows of D past the first NJ belong to no token (A's rows of tokens >=
     // NT are zero): their scalings and piece sums are skipped and they stay 0
     constexpr int NJ = NT < 4 ? NT : 4;
+    // three or four tokens: A's row 4t + p holds piece p of token t (token-major), so a
+    // lane holds the three pieces of one token, scales three rows of D per block and
+    // adds its pieces in place; one or two: row 4p + t (piece-major), so a lane scales
+    // only NJ rows and the pieces meet across lanes.  Either way a token's arithmetic
+    // is the same, and so are its bits.
+    constexpr bool TM = NT >= 3;
+    constexpr int NS = TM ? 3 : NJ;  // rows of D a lane scales
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
 
     const int tid = threadIdx.x;
@@ -1910,13 +1917,14 @@ __device__ __forceinline__ void mx_rows(const uint8_t* __restrict__ W, int64_t r
 
     // split, one token and 256-wide half at a time through the wave's region: piece
     // p of x[t][k] goes to the 16-byte fragment (block k / 32, group (k % 32) / 8,
-    // piece p), which the lane of A's row 4p + t and group (k % 32) / 8 then reads.
+    // piece p), which the lane of A's row (4p + t, or 4t + p) and group (k % 32) / 8
+    // then reads.
     // A wave's LDS operations take effect in program order, so the next round's
     // writes land after this round's reads.
     V4 afrag[NB];
     {
         const int b = lane >> 3, gg = (lane & 7) >> 1, half = (lane & 1) * 8;
-        const int am = lane & 15, ap = am >> 2, at = am & 3;
+        const int am = lane & 15, ap = TM ? (am & 3) : (am >> 2), at = TM ? (am >> 2) : (am & 3);
 #pragma unroll
         for (int bb = 0; bb < NB; ++bb) afrag[bb] = V4{0u, 0u, 0u, 0u};
 #pragma unroll
@@ -1979,21 +1987,26 @@ __device__ __forceinline__ void mx_rows(const uint8_t* __restrict__ W, int64_t r
                     const F4 dd = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(BF8, afrag[b]),
                                                                           __builtin_bit_cast(BF8, bq), z, 0, 0, 0);
 #pragma unroll
-                    for (int j = 0; j < NJ; ++j) acc[j] = __builtin_fmaf(dq, dd[j], acc[j]);
+                    for (int j = 0; j < NS; ++j) acc[j] = __builtin_fmaf(dq, dd[j], acc[j]);
                 }
             }
-            // token j's pieces sit in lanes n (hi), n + 16 (mid), n + 32 (lo): (hi + mid) + lo
+            if constexpr (TM) {  // the lane's token g: (hi + mid) + lo
+                const float tok = (acc[0] + acc[1]) + acc[2];
+                if (g < NT) part[(((size_t)t * nsl + s) * RT + 16 * h + n) * TP + g] = tok;
+            } else {
+                // token j's pieces sit in lanes n (hi), n + 16 (mid), n + 32 (lo): (hi + mid) + lo
 #pragma unroll
-            for (int j = 0; j < NJ; ++j) {
-                float mid = acc[j], lo = acc[j], junk16 = acc[j], junk32 = acc[j];
-                permlane16_swap(junk16, mid);
-                permlane32_swap(junk32, lo);
-                acc[j] = (acc[j] + mid) + lo;
-            }
-            if (lane < 16) {
-                float* pp = part + (((size_t)t * nsl + s) * RT + 16 * h + n) * TP;
+                for (int j = 0; j < NJ; ++j) {
+                    float mid = acc[j], lo = acc[j], junk16 = acc[j], junk32 = acc[j];
+                    permlane16_swap(junk16, mid);
+                    permlane32_swap(junk32, lo);
+                    acc[j] = (acc[j] + mid) + lo;
+                }
+                if (lane < 16) {
+                    float* pp = part + (((size_t)t * nsl + s) * RT + 16 * h + n) * TP;
 #pragma unroll
-                for (int j = 0; j < TP; ++j) pp[j] = acc[j];
+                    for (int j = 0; j < TP; ++j) pp[j] = acc[j];
+                }
             }
         }
     }
@@ -2060,7 +2073,9 @@ __device__ __forceinline__ void mxp_issue(const uint8_t* __restrict__ W, int64_t
 // (pieces x codes) per block, in block order.
 template <int FMT, int NT>
 __device__ __forceinline__ void mxp_math(const V4 (&afrag)[16], const MxRaw (&raw)[16], int g, F4& acc) {
-    constexpr int NJ = NT < 4 ? NT : 4;  // rows of D that carry a token (the rest stay 0)
+    // rows of D that carry a token (the rest stay 0); with three or four tokens A is
+    // token-major (row 4t + p) and a lane scales its token's three pieces
+    constexpr int NJ = NT >= 3 ? 3 : NT;
 #pragma unroll
     for (int b = 0; b < 16; ++b) {
         float dq;
@@ -2147,7 +2162,8 @@ __device__ __forceinline__ void mxp_rows(const uint8_t* __restrict__ W, int64_t 
             for (int t = 0; t < NT; ++t) xv[h][t] = *reinterpret_cast<const float4*>(slot + 2048 * t + 1024 * h + 16 * lane);
         {
             const int b = lane >> 3, gg = (lane & 7) >> 1, half = (lane & 1) * 8;
-            const int am = lane & 15, ap = am >> 2, at = am & 3;
+            // A's row 4p + t (piece-major, one or two tokens) or 4t + p (token-major)
+            const int am = lane & 15, ap = NT >= 3 ? (am & 3) : (am >> 2), at = NT >= 3 ? (am >> 2) : (am & 3);
             const bool arow = ap < 3 && at < NT;
             const int idx = arow ? (g * 3 * NT + ap * NT + at) * 16 : 0;
 #pragma unroll
@@ -2231,17 +2247,22 @@ __device__ __forceinline__ void mxp_rows(const uint8_t* __restrict__ W, int64_t 
             if (t + 1 < ntiles) mxp_issue<FMT>(W, row_bytes, row_begin, row_end, t + 1, off, slot, lane, shm);
             F4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
             mxp_math<FMT, NT>(afrag, raw, g, acc);
+            if constexpr (NT >= 3) {  // token-major: the lane's token g, (hi + mid) + lo in place
+                const float tok = (acc[0] + acc[1]) + acc[2];
+                if (g < NT) part[(((size_t)(pb * C + t - c * C) * nsl + s) * 16 + n) * TP + g] = tok;
+            } else {
 #pragma unroll
-            for (int j = 0; j < (NT < 4 ? NT : 4); ++j) {
-                float mid = acc[j], lo = acc[j], junk16 = acc[j], junk32 = acc[j];
-                permlane16_swap(junk16, mid);
-                permlane32_swap(junk32, lo);
-                acc[j] = (acc[j] + mid) + lo;
-            }
-            if (lane < 16) {
-                float* pp = part + (((size_t)(pb * C + t - c * C) * nsl + s) * 16 + n) * TP;
+                for (int j = 0; j < NT; ++j) {
+                    float mid = acc[j], lo = acc[j], junk16 = acc[j], junk32 = acc[j];
+                    permlane16_swap(junk16, mid);
+                    permlane32_swap(junk32, lo);
+                    acc[j] = (acc[j] + mid) + lo;
+                }
+                if (lane < 16) {
+                    float* pp = part + (((size_t)(pb * C + t - c * C) * nsl + s) * 16 + n) * TP;
 #pragma unroll
-                for (int j = 0; j < TP; ++j) pp[j] = acc[j];
+                    for (int j = 0; j < TP; ++j) pp[j] = acc[j];
+                }
             }
         }
         // publish this wave's partials of chunk c, then count the arrival
