@@ -1851,8 +1851,10 @@ __device__ __forceinline__ void mx_rows(const uint8_t* __restrict__ W, int64_t r
     // lane holds the three pieces of one token, scales three rows of D per block and
     // adds its pieces in place; one or two: row 4p + t (piece-major), so a lane scales
     // only NJ rows and the pieces meet across lanes.  Either way a token's arithmetic
-    // is the same, and so are its bits.
-    constexpr bool TM = NT >= 3;
+    // is the same, and so are its bits.  The gathered rows stay piece-major: their
+    // id exchange leaves no registers for the token-major form at three tokens (it
+    // spilled and ran 47 µs against 38 on a 32,768-row subset).
+    constexpr bool TM = NT >= 3 && !GATHER;
     constexpr int NS = TM ? 3 : NJ;  // rows of D a lane scales
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
 
