@@ -788,6 +788,7 @@ __device__ __forceinline__ void load_w16(__amdgpu_buffer_rsrc_t rsrc, uint8_t* l
 __device__ __forceinline__ void small_divmod(int a, int b, int& q, int& r) {
     q = 0;
     r = a;
+    if (b <= 0) return;  // never launched so (the host rejects cols <= 0); no endless loop either way
     while (r >= b) { r -= b; ++q; }
 }
 
