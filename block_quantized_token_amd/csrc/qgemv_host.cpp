@@ -183,7 +183,21 @@ Tile default_tile(int fmt, int64_t rows, int64_t cols, int T) {
         int64_t rw = ((rows + 255) / 256 + 15) / 16 * 16;
         t.rows_per_wg = (int)(rw > 1024 ? 1024 : rw);
         while (t.rows_per_wg > 16 && mx_lds_bytes(fmt, t, T, (int)nslices) > kMaxLds) t.rows_per_wg -= 16;
-        if (mx_lds_bytes(fmt, t, T, (int)nslices) <= kMaxLds) return t;
+        const bool fits = mx_lds_bytes(fmt, t, T, (int)nslices) <= kMaxLds;
+        // when the LDS holds too few rows for one workgroup per CU (long matrices at
+        // T >= 3, whose partial sums take more room), the persistent kind on the same
+        // slices, which has the same arithmetic and so the same bits: Q4_0 248,320 x
+        // 5,120 at T = 3 / 4 ran 204.5 / 206.1 µs in 388 workgroups against 176.8 /
+        // 173.9 persistent (T = 1 / 2: 160.2 / 163.6 in 255 workgroups, persistent 168.2
+        // / 170.5, so those stay).  BF16 (unmeasured there) keeps kind X.
+        if (fits && fmt != QG_FMT_BF16 && (rows + t.rows_per_wg - 1) / t.rows_per_wg > kPersistGrid &&
+            nslices + 1 <= kMaxWaves) {
+            Tile p = t;
+            p.kind = 9;
+            p.rows_per_wg = 48;
+            if (mxp_lds_bytes(fmt, p, T) <= kMaxLds) return p;
+        }
+        if (fits) return t;
         t.kind = 0;
         t.depth = 0;
     }

@@ -2052,11 +2052,19 @@ struct MxpShape {
     static constexpr int kLastLanes = 16 * kChunks - 64 * (kLoads - 1);   // 32, 32, 64
 };
 
+// Cache policy of the persistent kind's weight loads, by format (measured): Q8_0
+// splits (its 544-byte row pieces share only their two end lines); Q4_0's
+// 288-byte pieces share most of their lines, and there streaming every load ran
+// 0.3-4 µs faster than the split on 151,936 x 3,584 and 248,320 x 5,120; BF16's
+// 1 KB pieces share none.
+template <int FMT>
+constexpr int kPersistPolicy = FMT == QG_FMT_Q8_0 ? kSplitPolicy : kStreamPolicy;
+
 // 16-row tile t of the wave's slice into its slot: lane l of load k fetches
 // chunk 64 k + l (row / chunk of the row slice); rows past the range are
 // outside the descriptor and read as zeros.  The matrices this kind serves are
-// beyond the last-level cache: the loads stream, but for the chunks in lines
-// shared with a neighbouring piece (`shm`, kSplitPolicy).
+// beyond the last-level cache: the loads stream (Q8_0: but for the chunks in
+// lines shared with a neighbouring piece, `shm`).
 template <int FMT>
 __device__ __forceinline__ void mxp_issue(const uint8_t* __restrict__ W, int64_t row_bytes, int64_t row_begin,
                                           int64_t row_end, int t, const int (&off)[MxpShape<FMT>::kLoads],
@@ -2067,9 +2075,10 @@ __device__ __forceinline__ void mxp_issue(const uint8_t* __restrict__ W, int64_t
     const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
         (void*)(W + r0 * row_bytes), (short)0, (int)(rows_here * row_bytes), kBufferRsrcWord3);
 #pragma unroll
-    for (int k = 0; k < M::kLoads - 1; ++k) load_w16<kSplitPolicy>(rsrc, slot + 1024 * k, off[k], (shm >> k) & 1u);
+    for (int k = 0; k < M::kLoads - 1; ++k) load_w16<kPersistPolicy<FMT>>(rsrc, slot + 1024 * k, off[k], (shm >> k) & 1u);
     if (M::kLastLanes == 64 || lane < M::kLastLanes)
-        load_w16<kSplitPolicy>(rsrc, slot + 1024 * (M::kLoads - 1), off[M::kLoads - 1], (shm >> (M::kLoads - 1)) & 1u);
+        load_w16<kPersistPolicy<FMT>>(rsrc, slot + 1024 * (M::kLoads - 1), off[M::kLoads - 1],
+                                      (shm >> (M::kLoads - 1)) & 1u);
 }
 
 // The MFMAs of the 16 blocks of one tile, from their bytes: acc += scale *

@@ -178,8 +178,10 @@ def test_tile_query_and_override(lib, monkeypatch):
                            (151936, 3584), (65536, 5120)):
             tiles = [ops.query_tile(fmt, rows, cols, T) for T in (1, 2, 3, 4)]
             assert len({k_split(t, cols) for t in tiles}) == 1, (fmt, rows, cols, tiles)
-            # the vector-ALU kinds share their arithmetic per k slice; the matrix-core kinds do not
-            arith = {(t["mfma"], t["kind"] if t["kind"] in (8, 9, 11) else -1) for t in tiles}
+            # the vector-ALU kinds share their arithmetic per k slice; of the matrix-core
+            # kinds only X and P (the same 512-wide slices) do
+            arith = {(t["mfma"], {8: 8, 9: 11}.get(t["kind"], t["kind"]) if t["kind"] in (8, 9, 11) else -1)
+                     for t in tiles}
             assert len(arith) == 1, (fmt, rows, cols, tiles)
     # the LM head and other Q8_0 matrices of 224 MiB or more with at least seven 512-wide
     # slices, or of 512 MiB or more: the persistent matrix cores on 512-wide slices
@@ -192,7 +194,10 @@ def test_tile_query_and_override(lib, monkeypatch):
     # more than twelve 256-wide slices: the matrix cores on 512-wide slices
     t = ops.query_tile("q8_0", 2560, 6144, 1)
     assert (t["kind"], t["k_slice"], t["waves_per_wg"], t["lanes_per_row"]) == (11, 512, 12, 4), t
-    assert ops.query_tile("q4_0", 248320, 5120, 4)["kind"] != 9
+    # Q4_0 at the LM head's shape: kind X while its rows fit one workgroup per CU (T <= 2),
+    # the persistent kind on the same slices (the same bits) when they do not (T >= 3)
+    assert [ops.query_tile("q4_0", 248320, 5120, T)["kind"] for T in (1, 2, 3, 4)] == [11, 11, 9, 9]
+    assert ops.query_tile("q4_0", 163840, 5120, 4)["kind"] == 11  # 256 workgroups at every T
     monkeypatch.setenv("QGEMV_TILE", "q8_0:2,5,8")
     t = ops.query_tile("q8_0", 10240, 2560, 4)
     assert (t["rows_per_batch"], t["waves_per_wg"], t["rows_per_wg"]) == (2, 5, 8)

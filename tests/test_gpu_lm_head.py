@@ -143,3 +143,29 @@ def test_rows_subset_draft_vocabulary(torch, head, monkeypatch):
         assert np.array_equal(y, full[:T, ids]), T
         err = np.abs(y.astype(np.float64) - head["ref"][:T, ids])
         assert (err <= 1e-4 * head["bound"][:T, ids] + 1e-6).all(), T
+
+
+def test_q4_0_head_kinds_share_bits(torch, orc, monkeypatch):
+    """The head's shape in Q4_0 (715 MB): the default runs the matrix cores on 512-wide
+    slices per workgroup (kind X) while one workgroup per CU holds their partial sums
+    (T <= 2) and the persistent kind on the same slices from T = 3 on.  The two share
+    their arithmetic, so a token's bits must not change with T; every output is checked
+    against the oracle (one T = 4 run serves every T)."""
+    monkeypatch.delenv("QGEMV_TILE", raising=False)
+    rows, cols = 248320, 5120
+    kinds = [ops.query_tile("q4_0", rows, cols, T)["kind"] for T in (1, 2, 3, 4)]
+    assert kinds == [11, 11, 9, 9], kinds
+    say("[q4_0 head] generating 715 MB of packed weights")
+    W = I.weights_chunked(77, I.FMT_Q4_0, rows, cols)
+    x = I.activations(I.rng_for(78), cols)
+    say("[q4_0 head] oracle over all rows at T=4")
+    ref, bound = orc.gemv(I.FMT_Q4_0, rows, cols, W, x)
+    Wd, xd = torch.from_numpy(W).cuda(), torch.from_numpy(x).cuda()
+    ys = {}
+    for T in (4, 3, 2, 1):
+        say(f"[q4_0 head] T={T} kind={kinds[T - 1]}")
+        ys[T] = ops.gemv("q4_0", Wd, xd[:T].contiguous(), rows).cpu().numpy()
+        err = np.abs(ys[T].astype(np.float64) - ref[:T])
+        assert (err <= 1e-4 * bound[:T] + 1e-6).all(), T
+    for T in (1, 2, 3):
+        assert np.array_equal(ys[T], ys[4][:T]), f"a token's bits differ between T={T} and T=4"
