@@ -724,9 +724,10 @@ typedef __attribute__((address_space(3))) void lds_void_t;
 // line, so the lines at its two ends are shared with the neighbouring pieces, which
 // other waves load; those chunks keep the default policy, so that the line stays
 // for its second reader, and every other chunk streams (the bits are the same
-// under any policy).  Measured per kernel kind: the persistent kind splits (the LM
-// head: 225-230 µs at T = 1..4 with the default policy, 214-220 streaming, 203-210
-// split); the dense matrix-core kinds stream for Q4_0 and BF16 only (kDensePolicy);
+// under any policy).  Measured per kernel kind: the persistent kind splits for Q8_0
+// (the LM head: 225-230 µs at T = 1..4 with the default policy, 214-220 streaming,
+// 203-210 split) and streams otherwise (kPersistPolicy); the dense matrix-core kinds
+// stream for Q4_0 and BF16 only (kDensePolicy);
 // the grouped experts, whose experts several tokens share, and the gathered row
 // subset keep the default (streaming cost them 0.4-0.6 and 0.3-0.7 µs).
 constexpr int kDefaultPolicy = 0;
@@ -1682,14 +1683,6 @@ __device__ __forceinline__ void mfma_persist_q8(const uint8_t* __restrict__ W, i
 // A tile is R groups of 16 rows (R = 2: twice the bytes in flight per wave, for
 // the formats with short rows) of a slice of H 256-wide halves (H = 2: 512-wide
 // slices, 16 blocks a wave, for rows of more than twelve 256-wide slices).
-// Cache policy of the dense matrix-core kinds' weight loads, by format (measured:
-// streaming takes 0.1-0.5 µs off the Q4_0 and BF16 8192 x 2560 calls and adds
-// 0.1-0.4 µs to the Q8_0 ones; the split the persistent kind uses adds 0.5-1.2 µs
-// to every one of them, whose few tiles per wave leave no room for twice the load
-// instructions).
-template <int FMT>
-constexpr int kDensePolicy = FMT == QG_FMT_Q8_0 ? kDefaultPolicy : kStreamPolicy;
-
 template <int FMT, int R = 1, int H = 1>
 struct MxShape {
     static constexpr int kChunks = StreamFmt<FMT>::kChunks / 2 * H;      // 16-byte chunks of a row slice
@@ -1700,6 +1693,14 @@ struct MxShape {
     static constexpr int kBlockBytes = FMT == QG_FMT_Q8_0 ? 34 : FMT == QG_FMT_Q4_0 ? 18 : 64;
 };
 
+// Cache policy of the dense matrix-core kinds' weight loads, by format (measured:
+// streaming takes 0.1-0.5 µs off the Q4_0 and BF16 8192 x 2560 calls and adds
+// 0.1-0.4 µs to the Q8_0 ones; the split the persistent kind uses adds 0.5-1.2 µs
+// to every one of them, whose few tiles per wave leave no room for twice the load
+// instructions).
+template <int FMT>
+constexpr int kDensePolicy = FMT == QG_FMT_Q8_0 ? kDefaultPolicy : kStreamPolicy;
+
 // One tile of the wave's slice into its slot: lane l of load k fetches chunk
 // 64 k + l (row / chunk of the slice); lanes past the tile's last chunk do not
 // load, so the slot is exactly the tile's bytes; rows past the range are
@@ -1707,7 +1708,8 @@ struct MxShape {
 template <int FMT, int R = 1, int H = 1, int POLICY = kDefaultPolicy>
 __device__ __forceinline__ void mx_issue(const uint8_t* __restrict__ W, int64_t row_bytes, int64_t row_begin,
                                          int64_t row_end, int ntiles, int t, const int (&off)[MxShape<FMT, R, H>::kLoads],
-                                         uint8_t* slot, int lane, uint32_t shm = 0) {
+                                         uint8_t* slot, int lane) {
+    static_assert(POLICY != kSplitPolicy, "the dense kinds keep one policy per load");
     using M = MxShape<FMT, R, H>;
     const bool live = t < ntiles;
     const int64_t r0 = row_begin + (int64_t)(live ? t : 0) * M::kRows;
@@ -1716,9 +1718,9 @@ __device__ __forceinline__ void mx_issue(const uint8_t* __restrict__ W, int64_t 
     const __amdgpu_buffer_rsrc_t rsrc =
         __builtin_amdgcn_make_buffer_rsrc((void*)(W + r0 * row_bytes), (short)0, num, kBufferRsrcWord3);
 #pragma unroll
-    for (int k = 0; k < M::kLoads - 1; ++k) load_w16<POLICY>(rsrc, slot + 1024 * k, off[k], (shm >> k) & 1u);
+    for (int k = 0; k < M::kLoads - 1; ++k) load_lds16<POLICY>(rsrc, slot + 1024 * k, off[k]);
     if (M::kLastLanes == 64 || lane < M::kLastLanes)
-        load_w16<POLICY>(rsrc, slot + 1024 * (M::kLoads - 1), off[M::kLoads - 1], (shm >> (M::kLoads - 1)) & 1u);
+        load_lds16<POLICY>(rsrc, slot + 1024 * (M::kLoads - 1), off[M::kLoads - 1]);
 }
 
 // Byte q of the 12-byte window w[3] as an fp32 (signed).
@@ -1878,12 +1880,6 @@ __device__ __forceinline__ void mx_rows(const uint8_t* __restrict__ W, int64_t r
         const int r = j / M::kChunks, c = j % M::kChunks;
         off[k] = r < RT ? (GATHER ? 0 : (int)(r * row_bytes)) + s * M::kChunks * 16 + 16 * c : kNoLoad;
     }
-    // tiles lie RT rows apart, a multiple of 128 bytes for rows of whole 256-wide slices
-    uint32_t shm = 0;
-    if constexpr (POLICY == kSplitPolicy && !GATHER)
-        shm = shared_line_mask<L>((uint64_t)(uintptr_t)W + (uint64_t)row_begin * (uint64_t)row_bytes +
-                                      (uint64_t)s * M::kChunks * 16,
-                                  row_bytes, M::kChunks, RT, lane);
     int my_id0 = -1, my_id1 = -1;
     const __amdgpu_buffer_rsrc_t wr =
         __builtin_amdgcn_make_buffer_rsrc((void*)W, (short)0, GATHER ? (int)(wrows * row_bytes) : 0, kBufferRsrcWord3);
@@ -1912,7 +1908,7 @@ __device__ __forceinline__ void mx_rows(const uint8_t* __restrict__ W, int64_t r
                 load_lds16(wr, slot + 1024 * k, live ? (int)(id * row_bytes) + off[k] : kNoLoad);
             }
         } else {
-            mx_issue<FMT, R, H, POLICY>(W, row_bytes, row_begin, row_end, ntiles, t, off, slot, lane, shm);
+            mx_issue<FMT, R, H, POLICY>(W, row_bytes, row_begin, row_end, ntiles, t, off, slot, lane);
         }
     };
     // the wave's first tile, unless PRE has it on its way already (x is older)
